@@ -1,0 +1,263 @@
+/*
+ * qmv_oracle.c -- the oracle for the block-quantized matvec path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: only the tests, the smoke check of __graft_entry__ and the
+ * cpu_baseline leg of bench.py use it.  It shares no code, header, table or
+ * constant with the HIP library.
+ *
+ * Plain, slow, obviously-correct C99 in double precision.  Every function
+ * states the definition it writes out.  Sources are the pages collected on
+ * the subject:
+ *   [NST]  "One Native Stack for Private, Continuously-Learning AI" --
+ *          Sec. "The Unified Quant Core" (Q8_0 = symmetric, 34 bytes per 32
+ *          weights; Q4_0 = symmetric, 18 bytes per 32 weights; one block
+ *          decoder per format dequantizes a stored block to values) and the
+ *          QLoRA Lemma of Sec. "The Central Efficiency Thesis"
+ *          (y_i = sum_j What_ij x_j with What = DEQ(W)).
+ *   [ESP]  "Economical Serving and the hanzo.ai Platform" -- Sec. 2.1 "The
+ *          Roofline that Sets the Price" (a decode token streams the weights
+ *          once) and Sec. 2.2 (per-format block decoder + traits record).
+ *   [ZEN]  "Blue -- porting zen-nano (Qwen3-0.6B) to deterministic on-chain
+ *          inference" -- "Quantization recipe": int8 weights and activations,
+ *          int32 accumulation, per-output-channel requant by
+ *          SaturatingRoundingDoublingHighMul(acc, mult[o]) followed by
+ *          RoundingDivideByPOT(., shift[o]) to int8.
+ * Where the pages leave a step open (byte layout, nibble order, Q4_1, the
+ * bodies of the two gemmlowp functions, the int8 saturation range) this file
+ * takes the plainest reading; each such place says "Reading:".
+ *
+ * Status: every function below is pinned by the CPU tests (hand-computed
+ * blocks, exhaustive fp16 decode, exact-rational brute force, integer
+ * closed forms and an independent big-integer mirror).
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#include <math.h>
+
+enum { QO_Q8_0 = 0, QO_Q4_0 = 1, QO_Q4_1 = 2 };
+enum { QO_OK = 0, QO_EINVAL = 1, QO_ENOMEM = 2, QO_EOVERFLOW = 3 };
+
+/* IEEE 754 binary16 -> double, straight from the format definition:
+ * bit 15 sign, bits 14..10 biased exponent (bias 15), bits 9..0 fraction.
+ * exponent 0: subnormal, value = fraction * 2^-24; exponent 31: inf / NaN;
+ * otherwise value = (1024 + fraction) * 2^(exponent - 25).
+ * Reading: the pages give "fp16 scales" only; IEEE binary16 is the plain
+ * meaning, and subnormals are decoded exactly (no flush). */
+double qo_f16_to_f64(uint16_t h) {
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int f = h & 0x3ff;
+    double v;
+    if (e == 0) {
+        v = ldexp((double)f, -24);
+    } else if (e == 31) {
+        v = (f == 0) ? INFINITY : NAN;
+    } else {
+        v = ldexp((double)(1024 + f), e - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* Bytes per 32-weight block.  [NST] Sec. "The Unified Quant Core": Q8_0 34
+ * bytes, Q4_0 18 bytes.  Q4_1 is not on the pages; reading: fp16 d, fp16 m
+ * and 16 bytes of 4-bit codes = 20 bytes. */
+int64_t qo_block_bytes(int fmt) {
+    switch (fmt) {
+    case QO_Q8_0: return 34;
+    case QO_Q4_0: return 18;
+    case QO_Q4_1: return 20;
+    default: return -1;
+    }
+}
+
+static uint16_t rd16(const uint8_t* p) { return (uint16_t)(p[0] | (p[1] << 8)); }
+
+/* Decode one stored block to 32 exact doubles.
+ * Reading of the layouts (ggml-compatible, little-endian):
+ *   Q8_0: bytes 0-1 d (fp16); bytes 2..33 q_0..q_31 as int8; w_j = d*q_j.
+ *   Q4_0: bytes 0-1 d; bytes 2..17 qs[0..15]; element j (j<16) is the low
+ *         nibble of qs[j], element j+16 the high nibble; w = d*(c-8).
+ *   Q4_1: bytes 0-1 d, bytes 2-3 m (both fp16); bytes 4..19 qs with the
+ *         Q4_0 nibble order; w = d*c + m.
+ * All three are exact in double: d has at most 11 significant bits, the
+ * codes at most 8, and d*c + m spans at most 41 bits. */
+void qo_dequant_block(int fmt, const uint8_t* blk, double out[32]) {
+    int j;
+    if (fmt == QO_Q8_0) {
+        double d = qo_f16_to_f64(rd16(blk));
+        for (j = 0; j < 32; ++j) out[j] = d * (double)(int8_t)blk[2 + j];
+    } else if (fmt == QO_Q4_0) {
+        double d = qo_f16_to_f64(rd16(blk));
+        for (j = 0; j < 16; ++j) {
+            int lo = blk[2 + j] & 0x0f;
+            int hi = blk[2 + j] >> 4;
+            out[j] = d * (double)(lo - 8);
+            out[j + 16] = d * (double)(hi - 8);
+        }
+    } else {
+        double d = qo_f16_to_f64(rd16(blk));
+        double m = qo_f16_to_f64(rd16(blk + 2));
+        for (j = 0; j < 16; ++j) {
+            int lo = blk[4 + j] & 0x0f;
+            int hi = blk[4 + j] >> 4;
+            out[j] = d * (double)lo + m;
+            out[j + 16] = d * (double)hi + m;
+        }
+    }
+}
+
+/* DEQ(W) for one row of K weights (K a multiple of 32). */
+static void dequant_row(int fmt, const uint8_t* row, int64_t K, double* out) {
+    int64_t nb = K / 32, b;
+    int64_t bb = qo_block_bytes(fmt);
+    for (b = 0; b < nb; ++b) qo_dequant_block(fmt, row + b * bb, out + 32 * b);
+}
+
+/* Full dequantization, row-major [N][K]. */
+int qo_dequant(int fmt, const uint8_t* W, int64_t N, int64_t K, double* out) {
+    int64_t i, bb = qo_block_bytes(fmt);
+    if (bb < 0 || N < 0 || K < 0 || K % 32) return QO_EINVAL;
+    for (i = 0; i < N; ++i) dequant_row(fmt, W + i * (K / 32) * bb, K, out + i * K);
+    return QO_OK;
+}
+
+/* Float matvec, dequantize-then-dot ([NST] QLoRA Lemma: y_i = sum_j
+ * What_ij x_j; [ESP] Sec. 2.1: one pass over the weights per token).
+ * For each batch column b and each selected row i:
+ *     y[b][t] = sum_{j<K} What_ij * x[b][j]          (sequential j loop)
+ *     S[b][t] = sum_{j<K} |What_ij * x[b][j]|
+ * where t indexes rows[] (or all rows when rows == NULL).  S is the scale of
+ * the acceptance bound |y_gpu - y| <= 1e-4*S + 1e-6.  x rows are ldx floats
+ * apart; y and S rows are ldo doubles apart. */
+int qo_matvec(int fmt, const uint8_t* W, int64_t N, int64_t K,
+              const float* x, int64_t ldx, int32_t B,
+              const int64_t* rows, int64_t nrows,
+              double* y, double* S, int64_t ldo) {
+    int64_t bb = qo_block_bytes(fmt), t, j;
+    int32_t b;
+    double* w;
+    if (bb < 0 || N < 0 || K < 0 || K % 32 || B < 0 || ldx < K) return QO_EINVAL;
+    if (!rows) nrows = N;
+    w = (double*)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
+    if (!w) return QO_ENOMEM;
+    for (t = 0; t < nrows; ++t) {
+        int64_t i = rows ? rows[t] : t;
+        if (i < 0 || i >= N) { free(w); return QO_EINVAL; }
+        dequant_row(fmt, W + i * (K / 32) * bb, K, w);
+        for (b = 0; b < B; ++b) {
+            const float* xb = x + (int64_t)b * ldx;
+            double acc = 0.0, sabs = 0.0;
+            for (j = 0; j < K; ++j) {
+                double p = w[j] * (double)xb[j];
+                acc += p;
+                sabs += fabs(p);
+            }
+            y[(int64_t)b * ldo + t] = acc;
+            if (S) S[(int64_t)b * ldo + t] = sabs;
+        }
+    }
+    free(w);
+    return QO_OK;
+}
+
+/* floor(n / d) for d > 0, exact in integers. */
+static int64_t floor_div(int64_t n, int64_t d) {
+    int64_t q = n / d;
+    if ((n % d) != 0 && n < 0) q -= 1;
+    return q;
+}
+
+/* SaturatingRoundingDoublingHighMul(a, b) ([ZEN] "Quantization recipe";
+ * the page names the function only, as "int32 multiply-high + rounding
+ * shift").  Reading: the high word of the doubled product 2*a*b, i.e.
+ * a*b / 2^31, rounded to nearest with ties toward +infinity:
+ *     floor((a*b + 2^30) / 2^31),
+ * saturating the single overflowing case a = b = -2^31 to 2^31 - 1. */
+int32_t qo_srdhm(int32_t a, int32_t b) {
+    int64_t p;
+    if (a == INT32_MIN && b == INT32_MIN) return INT32_MAX;
+    p = (int64_t)a * (int64_t)b;
+    return (int32_t)floor_div(p + ((int64_t)1 << 30), (int64_t)1 << 31);
+}
+
+/* RoundingDivideByPOT(x, e) ([ZEN] "Quantization recipe", name only).
+ * Reading: x / 2^e rounded to nearest, ties away from zero, 0 <= e <= 31. */
+int32_t qo_rdbpot(int32_t x, int32_t e) {
+    int64_t p, ax, q;
+    if (e <= 0) return x;            /* e == 0: identity (callers pass 0..31) */
+    p = (int64_t)1 << e;
+    ax = x < 0 ? -(int64_t)x : (int64_t)x;
+    q = floor_div(2 * ax + p, 2 * p); /* floor(|x|/2^e + 1/2) */
+    return (int32_t)(x < 0 ? -q : q);
+}
+
+/* Saturate to the int8 range.  Reading: "-> int8" means [-128, 127]. */
+int32_t qo_sat8(int32_t v) { return v < -128 ? -128 : (v > 127 ? 127 : v); }
+
+/* The per-output-channel requant of one accumulator ([ZEN]). */
+int32_t qo_requant(int32_t acc, int32_t mult, int32_t shift) {
+    return qo_sat8(qo_rdbpot(qo_srdhm(acc, mult), shift));
+}
+
+/* All-integer matvec with per-output-channel requant ([ZEN]):
+ *     acc_i = sum_j Wq_ij * x_j        (exact, int64; must fit int32)
+ *     y_i   = sat8(RDBPOT(SRDHM(acc_i, mult_i), shift_i)).
+ * acc (optional) receives the int64 accumulators, y the int8 outputs, both
+ * indexed [b][t] with row stride ldo.  Returns QO_EOVERFLOW when an
+ * accumulator does not fit int32 (the path accumulates in int32). */
+int qo_matvec_i8(const int8_t* W, int64_t N, int64_t K,
+                 const int8_t* x, int64_t ldx, int32_t B,
+                 const int32_t* mult, const int32_t* shift,
+                 const int64_t* rows, int64_t nrows,
+                 int64_t* acc, int8_t* y, int64_t ldo) {
+    int64_t t, j;
+    int32_t b;
+    int rc = QO_OK;
+    if (N < 0 || K < 0 || B < 0 || ldx < K) return QO_EINVAL;
+    if (!rows) nrows = N;
+    for (t = 0; t < nrows; ++t) {
+        int64_t i = rows ? rows[t] : t;
+        if (i < 0 || i >= N) return QO_EINVAL;
+        if (shift[i] < 0 || shift[i] > 31) return QO_EINVAL;
+        for (b = 0; b < B; ++b) {
+            const int8_t* xb = x + (int64_t)b * ldx;
+            const int8_t* wr = W + i * K;
+            int64_t s = 0;
+            for (j = 0; j < K; ++j) s += (int64_t)wr[j] * (int64_t)xb[j];
+            if (acc) acc[(int64_t)b * ldo + t] = s;
+            if (s < INT32_MIN || s > INT32_MAX) { rc = QO_EOVERFLOW; s = 0; }
+            y[(int64_t)b * ldo + t] = (int8_t)qo_requant((int32_t)s, mult[i], shift[i]);
+        }
+    }
+    return rc;
+}
+
+/* Mixture-of-experts expert matvec, naive form ([NST] Sec. "The Unified
+ * Quant Core": each routed expert goes through the same matvec core).
+ * For every token b < batch and slot s < top_k, with e = ids[b*top_k + s]:
+ *     y[(b*top_k + s)][t] = sum_j DEQ(W_e)_{rows[t], j} * x_{b,s}[j]
+ * where W_e starts expert_stride bytes after W_{e-1} and x_{b,s} sits at
+ * x + b*x_stride_token + s*x_stride_slot.  No grouping: that is only a
+ * schedule.  Ids outside [0, n_experts) are an error here. */
+int qo_moe(int fmt, const uint8_t* W, int64_t expert_stride, int32_t n_experts,
+           int64_t N, int64_t K, const int32_t* ids, int32_t batch, int32_t top_k,
+           const float* x, int64_t x_stride_token, int64_t x_stride_slot,
+           const int64_t* rows, int64_t nrows, double* y, double* S, int64_t ldo) {
+    int32_t b, s;
+    int rc;
+    if (!rows) nrows = N;
+    for (b = 0; b < batch; ++b) {
+        for (s = 0; s < top_k; ++s) {
+            int32_t e = ids[b * top_k + s];
+            int64_t p = (int64_t)b * top_k + s;
+            if (e < 0 || e >= n_experts) return QO_EINVAL;
+            rc = qo_matvec(fmt, W + (int64_t)e * expert_stride, N, K,
+                           x + b * x_stride_token + s * x_stride_slot, K, 1,
+                           rows, nrows, y + p * ldo, S ? S + p * ldo : NULL, ldo);
+            if (rc != QO_OK) return rc;
+        }
+    }
+    return QO_OK;
+}

@@ -1,0 +1,353 @@
+"""Pins of the oracle to facts fixed outside it (CPU only).
+
+Each pin is chosen so that a plausible mistake in the oracle fails it:
+  * fp16 decoding: exhaustive over all 65536 patterns against numpy's
+    IEEE binary16 (library routine);
+  * byte layouts and nibble order: hand-computed blocks;
+  * encoders + decoders together: quantize/dequantize round-trip bounds;
+  * the fp64 dot: exact rational brute force on tiny matrices;
+  * the integer requant: hand cases, closed forms and an independent
+    big-integer mirror on edge and random pairs;
+  * MoE: reduction to single-expert matvecs sliced independently in numpy.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from tests import hand_blocks as hb
+
+FMTS = ["q8_0", "q4_0", "q4_1"]
+
+
+# ------------------------------------------------------------------ fp16
+def test_f16_decode_exhaustive(oracle_lib):
+    o = oracle_lib
+    h = np.arange(65536, dtype=np.uint16)
+    got = o.f16_to_f64(h)
+    ref = h.view(np.float16).astype(np.float64)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # signed zeros and infinities keep their sign
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+# ------------------------------------------------------------------ hand blocks
+@pytest.mark.parametrize("spec", hb.load()["blocks"], ids=lambda s: s["id"])
+def test_hand_block(oracle_lib, spec):
+    o = oracle_lib
+    blk = hb.block_bytes(spec)
+    x = hb.x_vec(spec["x"])
+    y, S = o.matvec(spec["fmt"], blk, 1, 32, x[None, :])
+    assert y[0, 0] == float(spec["y"]), (spec["id"], y[0, 0])
+    # the same block through the full dequantizer
+    w = o.dequant(spec["fmt"], blk, 1, 32)[0]
+    assert float(np.dot(w, x.astype(np.float64))) == float(spec["y"])
+
+
+def test_q4_nibble_order_distinguishes(oracle_lib):
+    """HB12: element j is the low nibble of byte j, element j+16 its high
+    nibble; the interleaved order would give a different value."""
+    spec = [s for s in hb.load()["blocks"] if s["id"] == "HB12"][0]
+    w = oracle_lib.dequant("q4_0", hb.block_bytes(spec), 1, 32)[0]
+    assert np.array_equal(w[:16], np.arange(16) - 8.0)
+    assert np.array_equal(w[16:], np.full(16, -8.0))
+
+
+# ------------------------------------------------------------------ round trip
+def _blocks_f64(Wf):
+    N, K = Wf.shape
+    return Wf.astype(np.float64).reshape(N, K // 32, 32)
+
+
+def _scale_bits(Wq, fmt, N, K, off=0):
+    bb = wl.BLOCK_BYTES[fmt]
+    raw = Wq.reshape(N, K // 32, bb)[..., off:off + 2].copy()
+    return raw.view(np.float16)[..., 0].astype(np.float64)
+
+
+def _test_weights():
+    g = np.random.default_rng(1234)
+    W = g.standard_normal((24, 256)) * 0.02
+    W[0, :32] = 0.0                       # all-zero block
+    W[1, :32] = g.standard_normal(32) * 1e-4   # subnormal (nonzero) fp16 scale
+    W[1, 32:64] = g.standard_normal(32) * 1e-9 # scale underflows to fp16 zero
+    W[2, :32] = 3.0                       # constant block
+    W[3, :32] = -np.linspace(0, 1, 32)    # monotone, negative extreme
+    W[4, 32:64] = np.linspace(-1, 1, 32)  # tie in |w| between ends (first wins)
+    W[5, :32] = g.standard_normal(32) * 100.0
+    return W.astype(np.float32)
+
+
+def test_roundtrip_q8_0(oracle_lib):
+    W = _test_weights()
+    N, K = W.shape
+    Wq = wl.encode_q8_0(W)
+    deq = oracle_lib.dequant("q8_0", Wq, N, K).reshape(N, K // 32, 32)
+    blk = _blocks_f64(W)
+    d = np.abs(_scale_bits(Wq, "q8_0", N, K))[..., None]
+    # every element is within half a step of the stored scale; the subnormal
+    # fp16 scale may be rounded by up to 2^-25 relative to amax/127, which
+    # can move the clipped extreme by at most 127 * 2^-25.
+    slack = 127 * 2.0 ** -25
+    assert np.all(np.abs(blk - deq) <= d / 2 + slack + 1e-300)
+    # the largest-magnitude element maps to +-127 whenever the stored scale is
+    # a normal fp16 number; a zero scale (all-zero block, or amax/127 below half the
+    # smallest fp16 subnormal) stores all-zero codes
+    q = Wq.reshape(N, K // 32, 34)[..., 2:].view(np.int8).astype(np.int64)
+    amax_i = np.abs(blk).argmax(-1)
+    qa = np.take_along_axis(np.abs(q), amax_i[..., None], -1)[..., 0]
+    # (normal fp16 scale: |amax/d - 127| <= 127 * 2^-11 < 1/2)
+    nz = d[..., 0] != 0
+    normal = d[..., 0] >= 2.0 ** -14
+    assert nz[1, 0] and not normal[1, 0] and not nz[1, 1] and not nz[0, 0]
+    assert np.all(qa[normal] == 127)
+    assert np.all(deq[~nz] == 0) and np.all(q[~nz] == 0)
+
+
+def test_roundtrip_q4_0(oracle_lib):
+    W = _test_weights()
+    N, K = W.shape
+    Wq = wl.encode_q4_0(W)
+    deq = oracle_lib.dequant("q4_0", Wq, N, K).reshape(N, K // 32, 32)
+    blk = _blocks_f64(W)
+    d = np.abs(_scale_bits(Wq, "q4_0", N, K))[..., None]
+    qs = Wq.reshape(N, K // 32, 18)[..., 2:]
+    codes = np.concatenate([qs & 15, qs >> 4], axis=-1).astype(np.int64)
+    err = np.abs(blk - deq)
+    clipped = codes == 15
+    normal = d >= 2.0 ** -14
+    # unclipped codes: within half a step; clipped at 15 (w/d >= 7.5): within
+    # one step plus the fp16 rounding slack of d (8 * 2^-11 relative).
+    assert np.all(err[~clipped & np.broadcast_to(normal, err.shape)] <=
+                  (d / 2 * np.ones_like(err))[~clipped & np.broadcast_to(normal, err.shape)] * (1 + 1e-12))
+    bound_clip = d * (1 + 2.0 ** -8)
+    assert np.all((err <= bound_clip * (1 + 1e-12))[np.broadcast_to(normal, err.shape)])
+    # the signed extreme maps to code 0 (w_ext / d = -8)
+    iext = np.abs(blk).argmax(-1)
+    cext = np.take_along_axis(codes, iext[..., None], -1)[..., 0]
+    nz = np.abs(blk).max(-1) > 0
+    assert np.all(cext[nz & normal[..., 0]] == 0)
+    # zero block: d = 0, codes 8, decodes to zeros
+    assert np.all(deq[~nz] == 0)
+
+
+def test_roundtrip_q4_1(oracle_lib):
+    W = _test_weights()
+    N, K = W.shape
+    Wq = wl.encode_q4_1(W)
+    deq = oracle_lib.dequant("q4_1", Wq, N, K).reshape(N, K // 32, 32)
+    blk = _blocks_f64(W)
+    d16 = _scale_bits(Wq, "q4_1", N, K, 0)
+    m16 = _scale_bits(Wq, "q4_1", N, K, 2)
+    mn, mx = blk.min(-1), blk.max(-1)
+    d32 = (mx - mn) / 15.0
+    qs = Wq.reshape(N, K // 32, 20)[..., 4:]
+    codes = np.concatenate([qs & 15, qs >> 4], axis=-1)
+    assert codes.max() <= 15
+    bound = d16 / 2 + np.abs(mn - m16) + 15 * np.abs(d32 - d16)
+    assert np.all(np.abs(blk - deq) <= bound[..., None] * (1 + 1e-9) + 1e-300)
+
+
+# ------------------------------------------------------------------ exact brute force
+def _random_blocks(g, fmt, N, K):
+    """Random stored bytes with finite, varied scales (random codes)."""
+    bb = wl.BLOCK_BYTES[fmt]
+    raw = g.integers(0, 256, size=(N, K // 32, bb), dtype=np.uint8)
+    # finite fp16 scales: exponent field 0..30 (includes subnormals)
+    for off in ([0] if fmt != "q4_1" else [0, 2]):
+        e = g.integers(0, 31, size=(N, K // 32))
+        f = g.integers(0, 1024, size=(N, K // 32))
+        s = g.integers(0, 2, size=(N, K // 32))
+        h = (s << 15) | (e << 10) | f
+        raw[..., off] = h & 0xFF
+        raw[..., off + 1] = h >> 8
+    return raw.reshape(N, -1)
+
+
+def _exact_dequant(fmt, blkbytes):
+    """Exact rational DEQ of one block, written from the layout directly."""
+    def f16(lo, hi):
+        return Fraction(float(np.array([lo | (hi << 8)], dtype=np.uint16).view(np.float16)[0]))
+    b = [int(v) for v in blkbytes]
+    if fmt == "q8_0":
+        d = f16(b[0], b[1])
+        return [d * (v - 256 if v >= 128 else v) for v in b[2:34]]
+    if fmt == "q4_0":
+        d = f16(b[0], b[1])
+        return [d * ((b[2 + j] & 15) - 8) for j in range(16)] + \
+               [d * ((b[2 + j] >> 4) - 8) for j in range(16)]
+    d, m = f16(b[0], b[1]), f16(b[2], b[3])
+    return [d * (b[4 + j] & 15) + m for j in range(16)] + \
+           [d * (b[4 + j] >> 4) + m for j in range(16)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("K", [32, 64])
+def test_matvec_exact_rational(oracle_lib, fmt, K):
+    g = np.random.default_rng(77 + K)
+    N, B = 4, 3
+    Wq = _random_blocks(g, fmt, N, K)
+    x = (g.standard_normal((B, K)) * np.exp(g.uniform(-8, 8, size=(B, K)))).astype(np.float32)
+    y, S = oracle_lib.matvec(fmt, Wq, N, K, x)
+    bb = wl.BLOCK_BYTES[fmt]
+    rows = Wq.reshape(N, K // 32, bb)
+    for i in range(N):
+        w = sum((_exact_dequant(fmt, rows[i, k]) for k in range(K // 32)), [])
+        for b in range(B):
+            exact = sum(wi * Fraction(float(xi)) for wi, xi in zip(w, x[b]))
+            sabs = sum(abs(wi * Fraction(float(xi))) for wi, xi in zip(w, x[b]))
+            err = abs(Fraction(y[b, i]) - exact)
+            assert err <= Fraction(K) * Fraction(2) ** -52 * sabs, (fmt, i, b)
+            assert abs(Fraction(S[b, i]) - sabs) <= Fraction(K) * Fraction(2) ** -52 * sabs
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_one_hot_selects_column(oracle_lib, fmt):
+    g = np.random.default_rng(5)
+    N, K = 6, 96
+    Wq = _random_blocks(g, fmt, N, K)
+    deq = oracle_lib.dequant(fmt, Wq, N, K)
+    x = np.eye(K, dtype=np.float32)[[0, 31, 32, 47, 95]]
+    y, _ = oracle_lib.matvec(fmt, Wq, N, K, x)
+    assert np.array_equal(y, deq[:, [0, 31, 32, 47, 95]].T)
+
+
+def test_row_subset_matches_full(oracle_lib):
+    g = np.random.default_rng(9)
+    N, K = 10, 64
+    Wq = _random_blocks(g, "q4_1", N, K)
+    x = g.standard_normal((2, K)).astype(np.float32)
+    y, S = oracle_lib.matvec("q4_1", Wq, N, K, x)
+    rows = np.array([9, 0, 4])
+    y2, S2 = oracle_lib.matvec("q4_1", Wq, N, K, x, rows=rows)
+    assert np.array_equal(y[:, rows], y2) and np.array_equal(S[:, rows], S2)
+
+
+# ------------------------------------------------------------------ integer path
+from oracle import py_int  # noqa: E402
+
+I32MIN, I32MAX = -(1 << 31), (1 << 31) - 1
+
+
+def test_hand_integer_cases(oracle_lib):
+    o = oracle_lib
+    cases = {c["id"]: c for c in hb.load()["integer"]}
+    c = cases["HB8"]
+    W = np.full((1, c["K"]), c["w"], dtype=np.int8)
+    x = np.full((1, c["K"]), c["x"], dtype=np.int8)
+    acc, y = o.matvec_i8(W, x, [c["mult"]], [c["shift"]])
+    assert acc[0, 0] == c["acc"] and y[0, 0] == c["y"]
+    assert o.srdhm(c["acc"], c["mult"]) == c["srdhm"] == py_int.srdhm(c["acc"], c["mult"])
+    c = cases["HB9"]
+    for a, e in zip(c["a"], c["expect"]):
+        assert o.srdhm(a, c["srdhm_b"]) == e == py_int.srdhm(a, c["srdhm_b"])
+    c = cases["HB10"]
+    for v, e in zip(c["x"], c["expect"]):
+        assert o.rdbpot(v, c["rdbpot_e"]) == e == py_int.rdbpot(v, c["rdbpot_e"])
+    c = cases["HB11"]
+    for a, s, e in zip(c["acc"], c["srdhm"], c["y"]):
+        assert o.srdhm(a, c["mult"]) == s
+        assert o.requant(a, c["mult"], c["shift"]) == e == py_int.requant(a, c["mult"], c["shift"])
+
+
+def test_srdhm_closed_forms(oracle_lib):
+    o = oracle_lib
+    g = np.random.default_rng(3)
+    for a in list(g.integers(I32MIN, I32MAX, size=2000)) + [I32MIN, I32MAX, 0, -1, 1]:
+        a = int(a)
+        # b = 2^30: a/2 rounded, ties up
+        assert o.srdhm(a, 1 << 30) == (a + 1) // 2
+        # b = 2^31 - 1 is the identity on (-2^30, 2^30]
+        if -(1 << 30) < a <= (1 << 30):
+            assert o.srdhm(a, I32MAX) == a
+    assert o.srdhm(-(1 << 30), I32MAX) == -(1 << 30) + 1
+    assert o.srdhm(I32MIN, I32MIN) == I32MAX
+    assert o.srdhm(I32MIN, I32MAX) == I32MIN + 1
+    assert o.srdhm(0, I32MIN) == 0
+
+
+def test_rdbpot_closed_forms(oracle_lib):
+    o = oracle_lib
+    g = np.random.default_rng(4)
+    for v in list(g.integers(I32MIN, I32MAX, size=1000)) + [I32MIN, I32MAX, 0, -1, 1]:
+        v = int(v)
+        assert o.rdbpot(v, 0) == v
+        for e in (1, 7, 20, 31):
+            # exact division when divisible
+            q = o.rdbpot(v, e)
+            assert abs(Fraction(v, 1 << e) - q) <= Fraction(1, 2)
+            if v % (1 << e) == 0:
+                assert q == v >> e
+    # exhaustive small range against the rational definition
+    for v in range(-70, 71):
+        for e in range(0, 6):
+            r = Fraction(v, 1 << e)
+            exp = int(abs(r) + Fraction(1, 2)) * (1 if r >= 0 else -1)
+            assert o.rdbpot(v, e) == exp
+
+
+def test_requant_c_vs_bigint_mirror(oracle_lib):
+    o = oracle_lib
+    g = np.random.default_rng(11)
+    edge = [I32MIN, I32MIN + 1, -(1 << 30) - 1, -(1 << 30), -(1 << 30) + 1, -2, -1, 0, 1, 2,
+            (1 << 30) - 1, 1 << 30, (1 << 30) + 1, I32MAX - 1, I32MAX]
+    for a in edge:
+        for b in edge:
+            assert o.srdhm(a, b) == py_int.srdhm(a, b), (a, b)
+        for e in range(32):
+            assert o.rdbpot(a, e) == py_int.rdbpot(a, e), (a, e)
+    A = g.integers(I32MIN, I32MAX, size=20000, endpoint=True)
+    Bm = g.integers(1 << 30, I32MAX, size=20000, endpoint=True)
+    E = g.integers(0, 32, size=20000)
+    for a, b, e in zip(A.tolist(), Bm.tolist(), E.tolist()):
+        assert o.requant(a, b, e) == py_int.requant(a, b, e)
+        assert o.srdhm(a, -b) == py_int.srdhm(a, -b)
+
+
+def test_matvec_i8_small_vs_mirror(oracle_lib):
+    g = np.random.default_rng(12)
+    N, K, B = 7, 48, 2
+    W = g.integers(-127, 128, size=(N, K), dtype=np.int8)
+    x = g.integers(-128, 128, size=(B, K), dtype=np.int8)
+    mult = g.integers(1 << 30, 1 << 31, size=N).astype(np.int32)
+    shift = g.integers(0, 21, size=N).astype(np.int32)
+    acc, y = oracle_lib.matvec_i8(W, x, mult, shift)
+    for b in range(B):
+        a2, y2 = py_int.matvec_i8(W.tolist(), x[b].tolist(), mult.tolist(), shift.tolist())
+        assert acc[b].tolist() == a2 and y[b].tolist() == y2
+
+
+def test_matvec_i8_overflow_reported(oracle_lib):
+    W = np.full((1, 1 << 18), -128, dtype=np.int8)
+    x = np.full((1, 1 << 18), -128, dtype=np.int8)
+    with pytest.raises(OverflowError):
+        oracle_lib.matvec_i8(W, x, [1 << 30], [0])
+
+
+# ------------------------------------------------------------------ MoE
+def test_moe_reduces_to_single_expert_matvecs(oracle_lib):
+    o = oracle_lib
+    g = np.random.default_rng(21)
+    E, N, K, B, T = 5, 8, 64, 3, 2
+    per = N * (K // 32) * 18
+    stride = per + 36                       # padded experts
+    Wall = g.integers(0, 256, size=E * stride, dtype=np.uint8)
+    for e in range(E):
+        Wall[e * stride:e * stride + per] = _random_blocks(g, "q4_0", N, K).reshape(-1)
+    ids = np.array([[4, 1], [1, 0], [2, 4]], dtype=np.int32)
+    xt = g.standard_normal((B, K)).astype(np.float32)
+    xs = g.standard_normal((B, T, K)).astype(np.float32)
+    y1, _ = o.moe("q4_0", Wall, stride, E, N, K, ids, xt)
+    y2, _ = o.moe("q4_0", Wall, stride, E, N, K, ids, None, x_slots=xs)
+    for b in range(B):
+        for s in range(T):
+            e = ids[b, s]
+            We = Wall[e * stride:e * stride + per]
+            r1, _ = o.matvec("q4_0", We, N, K, xt[b:b + 1])
+            r2, _ = o.matvec("q4_0", We, N, K, xs[b, s][None])
+            assert np.array_equal(y1[b, s], r1[0]) and np.array_equal(y2[b, s], r2[0])
+    with pytest.raises(ValueError):
+        o.moe("q4_0", Wall, stride, E, N, K, np.array([[5, 0]], dtype=np.int32), xt[:1])

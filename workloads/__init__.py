@@ -1,0 +1,184 @@
+"""Seeded synthetic inputs for the block-quantized matvec path.
+
+This module is the one place both sides draw their inputs from: the tests
+feed the same arrays to the oracle and to the HIP library, and bench.py uses
+it for the timed workload.  It holds no part of the matvec arithmetic (no
+decoding, no dot products, no requantization); it only draws random numbers
+and encodes them into the stored block formats, as the input recipe says:
+
+* float weights W ~ N(0, 0.02^2), encoded per 32-weight row block:
+    Q8_0  d = fp16(max|w| / 127),         q = round(w / d) in [-127, 127]
+    Q4_0  d = fp16(w_ext / -8) with w_ext the signed element of largest
+          magnitude (first on ties),      c = clamp(round(w / d) + 8, 0, 15)
+    Q4_1  d = fp16((max - min) / 15), m = fp16(min),
+                                          c = clamp(round((w - m) / d), 0, 15)
+  "round" is round-half-away-from-zero against the stored fp16 scale; the
+  fp16 conversion is numpy's IEEE round-to-nearest-even.
+* activations x ~ N(0, 1) float32;
+* int8 weights / activations uniform in [-127, 127]; per-row requant
+  multipliers uniform in [2^30, 2^31 - 1] and shifts uniform in [0, 20];
+* MoE expert ids: per token, top_k distinct ids uniform without replacement.
+
+Byte layouts (ggml-compatible, little-endian): Q8_0 = [d:fp16][q:int8 x32];
+Q4_0 = [d:fp16][qs:16 bytes], element j<16 in the low nibble of qs[j] and
+element j+16 in its high nibble; Q4_1 = [d:fp16][m:fp16][qs:16 bytes].
+
+Seeds: numpy PCG64 seeded with the first 8 bytes (little-endian) of
+SHA-256("qmv/<tag>").
+"""
+import hashlib
+
+import numpy as np
+
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20}
+
+
+def seed_for(tag: str) -> int:
+    h = hashlib.sha256(("qmv/" + tag).encode()).digest()
+    return int.from_bytes(h[:8], "little")
+
+
+def rng(tag: str) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed_for(tag)))
+
+
+# ---------------------------------------------------------------- draws
+def weights_f32(tag, N, K, std=0.02):
+    return (rng(tag).standard_normal((N, K), dtype=np.float32) * np.float32(std))
+
+
+def activations(tag, B, K):
+    return rng(tag).standard_normal((B, K), dtype=np.float32)
+
+
+def int8_uniform(tag, shape):
+    return rng(tag).integers(-127, 128, size=shape, dtype=np.int8)
+
+
+def requant_params(tag, N, shift_max=20):
+    g = rng(tag)
+    mult = g.integers(1 << 30, (1 << 31), size=N, dtype=np.int64).astype(np.int32)
+    shift = g.integers(0, shift_max + 1, size=N, dtype=np.int32)
+    return mult, shift
+
+
+def moe_ids(tag, batch, top_k, n_experts):
+    g = rng(tag)
+    return np.stack([g.choice(n_experts, size=top_k, replace=False)
+                     for _ in range(batch)]).astype(np.int32)
+
+
+# ---------------------------------------------------------------- encoders
+def _round_half_away(v):
+    return np.sign(v) * np.floor(np.abs(v) + 0.5)
+
+
+def _f16(v):
+    with np.errstate(over="ignore"):
+        return np.asarray(v, dtype=np.float64).astype(np.float16)
+
+
+def _nibbles_to_bytes(c):
+    """c: [..., 32] codes 0..15 -> [..., 16] bytes, low nibble = c[j],
+    high nibble = c[j+16]."""
+    c = c.astype(np.uint8)
+    return (c[..., :16] | (c[..., 16:] << 4)).astype(np.uint8)
+
+
+def encode_q8_0(Wf):
+    """float [N, K] -> uint8 [N, K/32*34]."""
+    Wf = np.asarray(Wf)
+    N, K = Wf.shape
+    assert K % 32 == 0
+    blk = Wf.reshape(N, K // 32, 32).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    d16 = _f16(amax / 127.0)
+    d = d16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(d != 0, np.clip(_round_half_away(blk / d), -127, 127), 0)
+    out = np.empty((N, K // 32, 34), dtype=np.uint8)
+    out[..., 0:2] = d16.view(np.uint8).reshape(N, K // 32, 2)
+    out[..., 2:] = q.astype(np.int8).view(np.uint8)
+    return out.reshape(N, -1)
+
+
+def encode_q4_0(Wf):
+    """float [N, K] -> uint8 [N, K/32*18] (signed-extreme scale)."""
+    Wf = np.asarray(Wf)
+    N, K = Wf.shape
+    assert K % 32 == 0
+    blk = Wf.reshape(N, K // 32, 32).astype(np.float64)
+    idx = np.abs(blk).argmax(axis=-1)[..., None]          # first on ties
+    wext = np.take_along_axis(blk, idx, axis=-1)[..., 0]
+    d16 = _f16(wext / -8.0)
+    d = d16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.where(d != 0, np.clip(_round_half_away(blk / d) + 8, 0, 15), 8)
+    out = np.empty((N, K // 32, 18), dtype=np.uint8)
+    out[..., 0:2] = d16.view(np.uint8).reshape(N, K // 32, 2)
+    out[..., 2:] = _nibbles_to_bytes(c)
+    return out.reshape(N, -1)
+
+
+def encode_q4_1(Wf):
+    """float [N, K] -> uint8 [N, K/32*20] (scale + minimum)."""
+    Wf = np.asarray(Wf)
+    N, K = Wf.shape
+    assert K % 32 == 0
+    blk = Wf.reshape(N, K // 32, 32).astype(np.float64)
+    mn = blk.min(axis=-1)
+    mx = blk.max(axis=-1)
+    d16 = _f16((mx - mn) / 15.0)
+    m16 = _f16(mn)
+    d = d16.astype(np.float64)[..., None]
+    m = m16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        c = np.where(d != 0, np.clip(_round_half_away((blk - m) / d), 0, 15), 0)
+    out = np.empty((N, K // 32, 20), dtype=np.uint8)
+    out[..., 0:2] = d16.view(np.uint8).reshape(N, K // 32, 2)
+    out[..., 2:4] = m16.view(np.uint8).reshape(N, K // 32, 2)
+    out[..., 4:] = _nibbles_to_bytes(c)
+    return out.reshape(N, -1)
+
+
+ENCODERS = {"q8_0": encode_q8_0, "q4_0": encode_q4_0, "q4_1": encode_q4_1}
+
+
+def quant_weights(fmt, tag, N, K, std=0.02, chunk_rows=8192):
+    """Draw W ~ N(0, std^2) [N, K] and encode it; chunked to bound memory.
+
+    The draw is one PCG64 stream, so the bytes do not depend on chunk_rows."""
+    enc = ENCODERS[fmt]
+    g = rng(tag)
+    out = np.empty((N, K // 32 * BLOCK_BYTES[fmt]), dtype=np.uint8)
+    for r0 in range(0, N, chunk_rows):
+        r1 = min(N, r0 + chunk_rows)
+        w = g.standard_normal((r1 - r0, K), dtype=np.float32) * np.float32(std)
+        out[r0:r1] = enc(w)
+    return out
+
+
+# ---------------------------------------------------------------- shapes
+# 8B Llama-shaped layer set: hidden 4096, GQA 32q/8kv x head_dim 128,
+# SwiGLU intermediate 14336; lm_head 128256 x 4096; 32 layers.
+LLAMA8B_LAYER = [("q", 4096, 4096), ("k", 1024, 4096), ("v", 1024, 4096),
+                 ("o", 4096, 4096), ("gate", 14336, 4096), ("up", 14336, 4096),
+                 ("down", 4096, 14336)]
+LLAMA8B_LM_HEAD = ("lm_head", 128256, 4096)
+LLAMA8B_LAYERS = 32
+
+# Qwen3-0.6B-shaped int8 layers (hidden 1024, 16q/8kv x 128, FFN 3072,
+# tied lm_head over vocab 151936); 28 layers.
+QWEN06B_LAYER = [("q", 2048, 1024), ("k", 1024, 1024), ("v", 1024, 1024),
+                 ("o", 1024, 2048), ("gate", 3072, 1024), ("up", 3072, 1024),
+                 ("down", 1024, 3072)]
+QWEN06B_LM_HEAD = ("lm_head", 151936, 1024)
+QWEN06B_LAYERS = 28
+
+# 30B-A3B-style MoE experts: hidden 2048, 128 experts, top-8, expert
+# gate/up 768 x 2048 and down 2048 x 768, 48 layers, Q4_0.
+MOE_HIDDEN, MOE_FFN, MOE_EXPERTS, MOE_TOPK, MOE_LAYERS = 2048, 768, 128, 8, 48
+
+
+def block_bytes(fmt, N, K):
+    return N * (K // 32) * BLOCK_BYTES[fmt]
