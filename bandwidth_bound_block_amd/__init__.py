@@ -1,0 +1,226 @@
+"""Block-quantized matrix x vector products for AMD MI355X (gfx950).
+
+Python binding of ``libqmv.so`` (hand-written HIP, C ABI in
+``include/qmv.h``).  This module only marshals arguments: it checks tensor
+devices, dtypes and shapes, passes raw device pointers and the current HIP
+stream to the library, and turns a non-OK return code into ``QmvError``.
+Every step of the computation runs in the library's kernels; there is no
+fallback of any kind, and importing this package fails loudly when the
+library has not been built.
+
+Entry points (same names as the C ABI):
+  qmv_q8_0 / qmv_q4_0 / qmv_q4_1   float block-quantized matvec, batch 1..8
+  qmv_i8_requant                   int8 matvec + per-channel gemmlowp requant
+  qmv_moe                          grouped MoE expert matvec
+  qmv_dequant                      stored blocks -> fp32 (test/inspection aid)
+"""
+import ctypes
+import os
+
+__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_i8_requant", "qmv_moe",
+           "qmv_dequant", "abi_version", "last_error", "library_path", "lib",
+           "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libqmv.so")
+
+Q8_0, Q4_0, Q4_1 = 0, 1, 2
+FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}
+_ERRORS = {1: "QMV_EINVAL", 2: "QMV_EALIGN", 3: "QMV_EUNSUPPORTED", 4: "QMV_EHIP"}
+
+
+class QmvError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"{_ERRORS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _open():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is not built: run __graft_entry__.build() "
+                          "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(_LIB_PATH)
+    P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    for name in ("qmv_q8_0", "qmv_q4_0", "qmv_q4_1"):
+        f = getattr(L, name)
+        f.argtypes = [P, i64, i64, P, i64, i32, P, i64, P]
+        f.restype = i32
+    L.qmv_i8_requant.argtypes = [P, i64, i64, P, i64, i32, P, P, P, i64, P]
+    L.qmv_i8_requant.restype = i32
+    L.qmv_moe.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P, i64, i64, P, P]
+    L.qmv_moe.restype = i32
+    L.qmv_dequant.argtypes = [ctypes.c_int, P, i64, i64, P, P]
+    L.qmv_dequant.restype = i32
+    L.qmv_last_error.argtypes = []
+    L.qmv_last_error.restype = ctypes.c_char_p
+    L.qmv_abi_version.argtypes = []
+    L.qmv_abi_version.restype = i32
+    return L
+
+
+_lib = _open()
+
+
+def lib():
+    """The raw ctypes handle (C signatures as in include/qmv.h)."""
+    return _lib
+
+
+def last_error():
+    return _lib.qmv_last_error().decode()
+
+
+def abi_version():
+    return int(_lib.qmv_abi_version())
+
+
+def _check(rc):
+    if rc != 0:
+        raise QmvError(rc, last_error())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, name, dtype):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t
+
+
+def _rows2d(t, name, K):
+    """[K] or [B, K] with unit inner stride -> (tensor2d, B, ld)."""
+    t2 = t.unsqueeze(0) if t.dim() == 1 else t
+    if t2.dim() != 2 or t2.shape[1] != K or t2.stride(1) != 1:
+        raise ValueError(f"{name} must be [K] or [B, K] with K={K} and unit inner stride")
+    return t2, t2.shape[0], t2.stride(0) if t2.shape[0] > 1 else K
+
+
+def _fmt(fmt):
+    return FORMATS[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _matvec(cfn, fmt, W, n_rows, n_cols, x, y, stream):
+    torch = _torch()
+    _dev(W, "W", torch.uint8)
+    _dev(x, "x", torch.float32)
+    need = n_rows * (n_cols // 32) * BLOCK_BYTES[fmt]
+    if W.numel() * W.element_size() < need or not W.is_contiguous():
+        raise ValueError(f"W must be contiguous and hold {need} bytes")
+    x2, B, ldx = _rows2d(x, "x", n_cols)
+    if y is None:
+        y = torch.empty((B, n_rows), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    y2, By, ldy = _rows2d(y, "y", n_rows)
+    if By != B:
+        raise ValueError("y must have as many rows as x")
+    _check(cfn(W.data_ptr(), n_rows, n_cols, x2.data_ptr(), ldx, B, y2.data_ptr(), ldy, _stream(stream)))
+    return y
+
+
+def qmv_q8_0(W, n_rows, n_cols, x, y=None, stream=None):
+    """y[b] = DEQ_Q8_0(W) @ x[b]; x float32 [K] or [B, K] (B <= 8)."""
+    return _matvec(_lib.qmv_q8_0, Q8_0, W, n_rows, n_cols, x, y, stream)
+
+
+def qmv_q4_0(W, n_rows, n_cols, x, y=None, stream=None):
+    """y[b] = DEQ_Q4_0(W) @ x[b]; x float32 [K] or [B, K] (B <= 8)."""
+    return _matvec(_lib.qmv_q4_0, Q4_0, W, n_rows, n_cols, x, y, stream)
+
+
+def qmv_q4_1(W, n_rows, n_cols, x, y=None, stream=None):
+    """y[b] = DEQ_Q4_1(W) @ x[b]; x float32 [K] or [B, K] (B <= 8)."""
+    return _matvec(_lib.qmv_q4_1, Q4_1, W, n_rows, n_cols, x, y, stream)
+
+
+def qmv_i8_requant(W, x, mult, shift, y=None, stream=None):
+    """int8 [N, K] weights x int8 [K] or [B, K] activations, per-row requant
+    (mult, shift int32 [N]) -> int8 [B, N]."""
+    torch = _torch()
+    _dev(W, "W", torch.int8)
+    _dev(x, "x", torch.int8)
+    _dev(mult, "mult", torch.int32)
+    _dev(shift, "shift", torch.int32)
+    if W.dim() != 2 or not W.is_contiguous():
+        raise ValueError("W must be a contiguous [N, K] tensor")
+    N, K = W.shape
+    if mult.numel() != N or shift.numel() != N or not mult.is_contiguous() or not shift.is_contiguous():
+        raise ValueError("mult and shift must be contiguous [N]")
+    x2, B, ldx = _rows2d(x, "x", K)
+    if y is None:
+        y = torch.empty((B, N), dtype=torch.int8, device=x.device)
+    _dev(y, "y", torch.int8)
+    y2, By, ldy = _rows2d(y, "y", N)
+    if By != B:
+        raise ValueError("y must have as many rows as x")
+    _check(_lib.qmv_i8_requant(W.data_ptr(), N, K, x2.data_ptr(), ldx, B, mult.data_ptr(), shift.data_ptr(),
+                               y2.data_ptr(), ldy, _stream(stream)))
+    return y
+
+
+def qmv_moe(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, x, y=None,
+            stream=None):
+    """Grouped MoE expert matvec.
+
+    expert_ids: int32 [B, top_k] on the GPU.  x: float32 [B, K] (one input per
+    token, gate/up) or [B, top_k, K] (one input per token and slot, down).
+    Returns y float32 [B, top_k, n_rows]."""
+    torch = _torch()
+    fmt = _fmt(fmt)
+    _dev(W_experts, "W_experts", torch.uint8)
+    _dev(expert_ids, "expert_ids", torch.int32)
+    _dev(x, "x", torch.float32)
+    if not W_experts.is_contiguous() or not expert_ids.is_contiguous() or not x.is_contiguous():
+        raise ValueError("W_experts, expert_ids and x must be contiguous")
+    if expert_ids.dim() != 2:
+        raise ValueError("expert_ids must be [B, top_k]")
+    B, T = expert_ids.shape
+    if x.dim() == 2 and x.shape == (B, n_cols):
+        st_tok, st_slot = n_cols, 0
+    elif x.dim() == 3 and x.shape == (B, T, n_cols):
+        st_tok, st_slot = T * n_cols, n_cols
+    else:
+        raise ValueError("x must be [B, K] or [B, top_k, K]")
+    if W_experts.numel() < (n_experts - 1) * expert_stride_bytes + n_rows * (n_cols // 32) * BLOCK_BYTES.get(fmt, 0):
+        raise ValueError("W_experts is smaller than n_experts expert matrices")
+    if y is None:
+        y = torch.empty((B, T, n_rows), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    if y.shape != (B, T, n_rows) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [B, top_k, n_rows] tensor")
+    _check(_lib.qmv_moe(fmt, W_experts.data_ptr(), expert_stride_bytes, n_experts, n_rows, n_cols,
+                        expert_ids.data_ptr(), B, T, x.data_ptr(), st_tok, st_slot, y.data_ptr(),
+                        _stream(stream)))
+    return y
+
+
+def qmv_dequant(fmt, W, n_rows, n_cols, out=None, stream=None):
+    """fp32 [n_rows, n_cols] values of the stored blocks."""
+    torch = _torch()
+    fmt = _fmt(fmt)
+    _dev(W, "W", torch.uint8)
+    if out is None:
+        out = torch.empty((n_rows, n_cols), dtype=torch.float32, device=W.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != (n_rows, n_cols) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [n_rows, n_cols] tensor")
+    _check(_lib.qmv_dequant(fmt, W.data_ptr(), n_rows, n_cols, out.data_ptr(), _stream(stream)))
+    return out

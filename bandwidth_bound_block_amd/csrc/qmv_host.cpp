@@ -1,0 +1,49 @@
+// Host-side helpers of libqmv.so (see qmv_host.h).
+#include "qmv_host.h"
+
+#include <atomic>
+#include <cstring>
+
+namespace qmv {
+
+namespace {
+thread_local char g_err[512] = {0};
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];
+}  // namespace
+
+int32_t fail(int32_t code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int32_t ok() {
+    g_err[0] = 0;
+    return QMV_OK;
+}
+
+int device_cu_count() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int v = g_cus[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        cus = 256;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+int32_t check_launch(const char* what) {
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QMV_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace qmv
+
+extern "C" const char* qmv_last_error(void) { return qmv::g_err; }
+extern "C" int32_t qmv_abi_version(void) { return QMV_ABI_VERSION; }

@@ -1,0 +1,176 @@
+/*
+ * qmv.h -- block-quantized matrix x vector products for AMD MI355X (gfx950).
+ *
+ * C ABI of libqmv.so.  Every entry point is asynchronous on the given HIP
+ * stream, allocates nothing, keeps no state between calls (apart from a
+ * thread-local error message) and is deterministic: the same inputs give
+ * bitwise-identical outputs (fixed reduction order, no atomics).
+ *
+ * Conventions shared by all entry points
+ *   - Pointers W, x, y, mult, shift, expert_ids and out are DEVICE pointers
+ *     owned by the caller; the library only reads inputs and fully
+ *     overwrites outputs.  Outputs must not alias inputs.
+ *   - stream is a hipStream_t passed as void*; NULL means the null stream.
+ *   - Matrices are row-major.  A block-quantized row of n_cols weights is
+ *     n_cols/32 consecutive 32-weight blocks; rows follow each other with no
+ *     padding.  Block layouts (ggml-compatible, little-endian):
+ *       Q8_0  34 bytes: d (fp16) | q[32] (int8)               w = d*q
+ *       Q4_0  18 bytes: d (fp16) | qs[16]                     w = d*(c-8)
+ *       Q4_1  20 bytes: d (fp16) | m (fp16) | qs[16]          w = d*c + m
+ *     For Q4_0/Q4_1, weight j < 16 of a block is the low nibble of qs[j] and
+ *     weight j + 16 the high nibble of qs[j].  Scales are IEEE binary16 and
+ *     are decoded exactly (subnormals included).
+ *   - The batch width is 1..8: x holds `batch` activation rows, ldx elements
+ *     apart; y holds `batch` output rows, ldy elements apart.  Each batch
+ *     column is computed independently and gives bitwise the same result as
+ *     a batch-1 call on that column alone.
+ *   - Float results are fp32, accumulated in fp32; they agree with the exact
+ *     dequantize-then-dot within |err| <= 1e-4 * sum_j |w_ij x_j| + 1e-6 per
+ *     output (the accuracy contract the tests enforce).
+ *
+ * Return codes: QMV_OK on success, otherwise one of QMV_E*, with a message
+ * from qmv_last_error().  All argument checks happen on the host before any
+ * launch, so a non-OK return means nothing was enqueued (except QMV_EHIP,
+ * which reports a failed launch).  Nothing defaults silently.
+ *
+ * Sources (the pages collected on the subject):
+ *   [NST] "One Native Stack for Private, Continuously-Learning AI", Sec. "The
+ *         Unified Quant Core": Q8_0 symmetric 34 B/32, Q4_0 symmetric
+ *         18 B/32; one templated decode matvec per stage, one block decoder
+ *         per format, the same core driving decode and MoE experts; QLoRA
+ *         Lemma: y_i = sum_j DEQ(W)_ij x_j accumulated in f32.
+ *   [ESP] "Economical Serving and the hanzo.ai Platform", Sec. 2.1 "The
+ *         Roofline that Sets the Price" (a decode token streams the resident
+ *         weights once; t = W/B) and Sec. 2.2 (quant-agnostic core, block
+ *         decoder + traits record, f16/bf16 activation entry points).
+ *   [ZEN] "Blue -- porting zen-nano (Qwen3-0.6B) to deterministic on-chain
+ *         inference", "Quantization recipe": per-output-channel int8 weights,
+ *         int8 activations, int32 accumulation, requant by
+ *         SaturatingRoundingDoublingHighMul(acc, mult[o]) then
+ *         RoundingDivideByPOT(., shift[o]) to int8.
+ *   Q4_1 is not on the pages: its layout above is the ggml-compatible one.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QMV_ABI_VERSION 1
+
+typedef enum { QMV_Q8_0 = 0, QMV_Q4_0 = 1, QMV_Q4_1 = 2 } qmv_fmt;
+
+enum {
+    QMV_OK = 0,
+    QMV_EINVAL = 1,       /* null pointer, bad size, batch/top_k out of range */
+    QMV_EALIGN = 2,       /* pointer or leading dimension misaligned          */
+    QMV_EUNSUPPORTED = 3, /* format not available for this entry point        */
+    QMV_EHIP = 4          /* the HIP runtime reported an error at launch      */
+};
+
+/*
+ * Float block-quantized matvec: y[b][i] = sum_j DEQ(W)[i][j] * x[b][j] for
+ * b < batch, i < n_rows ([NST] QLoRA Lemma; [ESP] Sec. 2.1).
+ *   W       packed blocks of the format named by the function, n_rows rows of
+ *           n_cols/32 blocks; 4-byte aligned.
+ *   n_rows  >= 1.
+ *   n_cols  >= 32 and a multiple of 32.
+ *   x       fp32 [batch][ldx], ldx >= n_cols; 4-byte aligned.
+ *   batch   1..8.
+ *   y       fp32 [batch][ldy], ldy >= n_rows; 4-byte aligned.
+ * Errors: QMV_EINVAL (null pointer, n_rows < 1, n_cols < 32 or not a multiple
+ * of 32, batch outside 1..8, ldx < n_cols, ldy < n_rows, n_rows*n_cols/32
+ * blocks beyond 2^40), QMV_EALIGN (W, x or y not 4-byte aligned), QMV_EHIP.
+ */
+int32_t qmv_q8_0(const void* W, int64_t n_rows, int64_t n_cols,
+                 const float* x, int64_t ldx, int32_t batch,
+                 float* y, int64_t ldy, void* stream);
+int32_t qmv_q4_0(const void* W, int64_t n_rows, int64_t n_cols,
+                 const float* x, int64_t ldx, int32_t batch,
+                 float* y, int64_t ldy, void* stream);
+int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
+                 const float* x, int64_t ldx, int32_t batch,
+                 float* y, int64_t ldy, void* stream);
+
+/*
+ * All-integer matvec with per-output-channel requant ([ZEN]):
+ *   acc[b][i] = sum_j W[i][j] * x[b][j]            (int32, exact)
+ *   y[b][i]   = sat_int8(RDBPOT(SRDHM(acc[b][i], mult[i]), shift[i]))
+ * SRDHM(a, m) = a*m / 2^31 rounded to nearest, ties toward +infinity, with
+ * SRDHM(-2^31, -2^31) = 2^31 - 1; RDBPOT(v, e) = v / 2^e rounded to nearest,
+ * ties away from zero; sat_int8 clamps to [-128, 127].
+ *   W       int8 [n_rows][n_cols]; 16-byte aligned.
+ *   n_cols  >= 16, a multiple of 16, and <= 131056, the largest such value
+ *           with n_cols * 128^2 < 2^31, so acc fits int32 for every input.
+ *   x       int8 [batch][ldx], ldx >= n_cols and a multiple of 16; 16-byte
+ *           aligned.
+ *   mult    int32 [n_rows], any value.
+ *   shift   int32 [n_rows], each in 0..31 (other values give unspecified
+ *           outputs for that row, never an out-of-bounds access).
+ *   y       int8 [batch][ldy], ldy >= n_rows.
+ * Errors: QMV_EINVAL (null pointer, bad sizes, batch outside 1..8),
+ * QMV_EALIGN (W or x not 16-byte aligned, ldx not a multiple of 16), QMV_EHIP.
+ */
+int32_t qmv_i8_requant(const int8_t* W, int64_t n_rows, int64_t n_cols,
+                       const int8_t* x, int64_t ldx, int32_t batch,
+                       const int32_t* mult, const int32_t* shift,
+                       int8_t* y, int64_t ldy, void* stream);
+
+/*
+ * Grouped mixture-of-experts expert matvec ([NST] Sec. "The Unified Quant
+ * Core": each routed expert goes through the same decode matvec core).
+ * For token b < batch and slot s < top_k, with e = expert_ids[b*top_k + s]:
+ *   y[(b*top_k + s)*n_rows + i] = sum_j DEQ(W_e)[i][j] * x_{b,s}[j]
+ * where W_e = (const uint8_t*)W_experts + e*expert_stride_bytes is an
+ * n_rows x n_cols matrix in format fmt, and
+ * x_{b,s} = x + b*x_stride_token + s*x_stride_slot (elements).  Gate/up
+ * projections pass x_stride_slot = 0 (one input per token); the down
+ * projection passes x_stride_slot = n_cols (one input per token and slot).
+ * Each expert that appears in expert_ids is streamed from memory once per
+ * call and applied to every (token, slot) routed to it.
+ *   fmt                 QMV_Q8_0, QMV_Q4_0 or QMV_Q4_1.
+ *   expert_stride_bytes >= the bytes of one expert matrix; a multiple of 4.
+ *   n_experts           >= 1.
+ *   expert_ids          int32 [batch][top_k], device memory.  An id outside
+ *                       [0, n_experts) cannot be reported synchronously: the
+ *                       n_rows outputs of its (token, slot) are written as
+ *                       quiet NaN.
+ *   batch               1..8;  top_k 1..16.
+ *   x                   fp32; x_stride_token >= n_cols (when batch > 1),
+ *                       x_stride_slot 0 or >= n_cols; 4-byte aligned.
+ *   y                   fp32 [batch][top_k][n_rows].
+ * Errors: QMV_EINVAL, QMV_EALIGN, QMV_EUNSUPPORTED (unknown fmt), QMV_EHIP.
+ */
+int32_t qmv_moe(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
+                int32_t n_experts, int64_t n_rows, int64_t n_cols,
+                const int32_t* expert_ids, int32_t batch, int32_t top_k,
+                const float* x, int64_t x_stride_token, int64_t x_stride_slot,
+                float* y, void* stream);
+
+/*
+ * Dequantize a whole matrix to fp32: out[i][j] = DEQ(W)[i][j], exactly (every
+ * Q8_0/Q4_0 value and every Q4_1 value d*c + m whose bits span <= 24 is
+ * representable in fp32; otherwise it is rounded to nearest even).  A test
+ * and inspection aid ([NST] Sec. "The Unified Quant Core": the per-format
+ * block decoder maps a stored block to its values).
+ *   out  fp32 [n_rows][n_cols]; 4-byte aligned.
+ * Errors: as the float matvec, plus QMV_EUNSUPPORTED for an unknown fmt.
+ */
+int32_t qmv_dequant(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols,
+                    float* out, void* stream);
+
+/* Message for the last non-OK return on the calling thread ("" if none). */
+const char* qmv_last_error(void);
+
+/* QMV_ABI_VERSION of the built library. */
+int32_t qmv_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

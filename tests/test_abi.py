@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every declared symbol and rejects bad
+arguments on the host with the documented codes (no GPU needed: every call
+here fails validation before anything is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+EINVAL, EALIGN, EUNSUPPORTED = 1, 2, 3
+A = 0x10000          # a fake, aligned, never dereferenced device address
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_\w+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def qmv():
+    import bandwidth_bound_block_amd as q
+    return q
+
+
+def test_every_declared_symbol_is_exported(qmv):
+    names = declared_functions()
+    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_i8_requant", "qmv_moe", "qmv_dequant",
+            "qmv_last_error", "qmv_abi_version"} <= set(names)
+    raw = ctypes.CDLL(qmv.library_path())
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_abi_version(qmv):
+    assert qmv.abi_version() == 1
+
+
+@pytest.mark.parametrize("name", ["qmv_q8_0", "qmv_q4_0", "qmv_q4_1"])
+def test_float_matvec_argument_errors(qmv, name):
+    f = getattr(qmv.lib(), name)
+    cases = [
+        ((0, 8, 64, A, 64, 1, A, 8, None), EINVAL, "null"),
+        ((A, 0, 64, A, 64, 1, A, 8, None), EINVAL, "n_rows"),
+        ((A, 8, 48, A, 48, 1, A, 8, None), EINVAL, "multiple of 32"),
+        ((A, 8, 0, A, 64, 1, A, 8, None), EINVAL, "multiple of 32"),
+        ((A, 8, 64, A, 64, 0, A, 8, None), EINVAL, "batch"),
+        ((A, 8, 64, A, 64, 9, A, 8, None), EINVAL, "batch"),
+        ((A, 8, 64, A, 63, 1, A, 8, None), EINVAL, "ldx"),
+        ((A, 8, 64, A, 64, 1, A, 7, None), EINVAL, "ldy"),
+        ((A + 2, 8, 64, A, 64, 1, A, 8, None), EALIGN, "aligned"),
+        ((A, 8, 64, A + 1, 64, 1, A, 8, None), EALIGN, "aligned"),
+        ((A, 8, 64, A, 64, 1, A + 2, 8, None), EALIGN, "aligned"),
+        ((A, 8, 64 * 1024 * 1024, A, 64 * 1024 * 1024, 1, A, 8, None), EINVAL, "LDS"),
+    ]
+    for args, code, word in cases:
+        assert f(*args) == code, (args, qmv.last_error())
+        assert word in qmv.last_error(), qmv.last_error()
+
+
+def test_int8_argument_errors(qmv):
+    f = qmv.lib().qmv_i8_requant
+    ok = dict(W=A, N=8, K=64, x=A, ldx=64, B=1, mult=A, shift=A, y=A, ldy=8)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["W"], a["N"], a["K"], a["x"], a["ldx"], a["B"], a["mult"], a["shift"], a["y"], a["ldy"], None)
+
+    assert call(mult=0) == EINVAL
+    assert call(K=40) == EINVAL and "multiple of 16" in qmv.last_error()
+    assert call(K=131072, ldx=131072) == EINVAL
+    assert call(B=9) == EINVAL
+    assert call(ldy=7) == EINVAL
+    assert call(W=A + 4) == EALIGN
+    assert call(x=A + 8) == EALIGN
+    assert call(ldx=72) == EALIGN
+    assert call(shift=A + 2) == EALIGN
+
+
+def test_moe_argument_errors(qmv):
+    f = qmv.lib().qmv_moe
+    per = 16 * 2 * 18   # 16 x 64 Q4_0 expert
+    ok = dict(fmt=1, W=A, stride=per, E=4, N=16, K=64, ids=A, B=2, T=2, x=A, st_tok=64, st_slot=0, y=A)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["fmt"], a["W"], a["stride"], a["E"], a["N"], a["K"], a["ids"], a["B"], a["T"], a["x"],
+                 a["st_tok"], a["st_slot"], a["y"], None)
+
+    assert call(fmt=7) == EUNSUPPORTED
+    assert call(ids=0) == EINVAL
+    assert call(E=0) == EINVAL
+    assert call(T=0) == EINVAL and call(T=17) == EINVAL
+    assert call(B=9) == EINVAL
+    assert call(stride=per - 4) == EINVAL
+    assert call(stride=per + 2) == EINVAL
+    assert call(st_tok=32) == EINVAL
+    assert call(st_slot=32) == EINVAL
+    assert call(y=A + 2) == EALIGN
+
+
+def test_dequant_argument_errors(qmv):
+    f = qmv.lib().qmv_dequant
+    assert f(5, A, 4, 64, A, None) == EUNSUPPORTED
+    assert f(0, 0, 4, 64, A, None) == EINVAL
+    assert f(0, A, 4, 65, A, None) == EINVAL
+
+
+def test_error_message_is_per_call(qmv):
+    f = qmv.lib().qmv_q8_0
+    assert f(A, 0, 64, A, 64, 1, A, 8, None) == EINVAL
+    assert "n_rows" in qmv.last_error()
+    assert f(A, 8, 64, A, 64, 12, A, 8, None) == EINVAL
+    assert "batch" in qmv.last_error()
+
+
+def test_python_binding_rejects_cpu_tensors(qmv):
+    import torch
+    W = torch.zeros(34 * 2, dtype=torch.uint8)
+    x = torch.zeros(64, dtype=torch.float32)
+    with pytest.raises(ValueError):
+        qmv.qmv_q8_0(W, 1, 64, x)

@@ -1,0 +1,366 @@
+"""Parity of the HIP library with the oracle, on an MI355X.
+
+Float paths: |y_gpu - y| <= 1e-4 * S + 1e-6 per output, S = sum_j |w_ij x_j|
+(the accuracy bound of the matvec contract), against the fp64
+dequantize-then-dot oracle.  Dequantized values and the int8 requant path:
+bit-exact.  Inputs come from the seeded generators in workloads/, with the
+shapes and distributions of the five workloads (small cases that span several
+tiles and a ragged tail, then the full sizes, sampled rows where the oracle
+would be slow).  All calls go through the C ABI via the Python binding.
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+from tests import hand_blocks as hb
+
+pytestmark = pytest.mark.gpu
+
+FMTS = ["q8_0", "q4_0", "q4_1"]
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    import bandwidth_bound_block_amd as qmv
+    assert torch.cuda.is_available()
+    return torch, qmv
+
+
+def dev(torch, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to("cuda:0")
+
+
+def gpu_matvec(env, fmt, W, N, K, x):
+    torch, qmv = env
+    f = {"q8_0": qmv.qmv_q8_0, "q4_0": qmv.qmv_q4_0, "q4_1": qmv.qmv_q4_1}[fmt]
+    y = f(dev(torch, W), N, K, dev(torch, x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def assert_tol(y, yr, S, what=""):
+    err = np.abs(y.astype(np.float64) - yr)
+    tol = 1e-4 * S + 1e-6
+    bad = err > tol
+    assert not np.any(bad), (what, int(bad.sum()), float((err / tol).max()))
+    return float((err / tol).max())
+
+
+def random_blocks(seed, fmt, N, K):
+    """Stored bytes with random codes and random finite fp16 scales
+    (subnormals included)."""
+    g = np.random.default_rng(seed)
+    bb = wl.BLOCK_BYTES[fmt]
+    raw = g.integers(0, 256, size=(N, K // 32, bb), dtype=np.uint8)
+    for off in ([0] if fmt != "q4_1" else [0, 2]):
+        e = g.integers(0, 31, size=(N, K // 32))
+        f = g.integers(0, 1024, size=(N, K // 32))
+        s = g.integers(0, 2, size=(N, K // 32))
+        h = (s << 15) | (e << 10) | f
+        raw[..., off] = h & 0xFF
+        raw[..., off + 1] = h >> 8
+    return raw.reshape(N, -1)
+
+
+# ------------------------------------------------------------------ dequant
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("kind", ["encoded", "random_bytes"])
+def test_dequant_bit_exact(env, fmt, kind):
+    torch, qmv = env
+    N, K = 37, 320          # 10 blocks per row: both block parities in every row
+    say(f"dequant {fmt} {kind} {N}x{K}")
+    if kind == "encoded":
+        W = wl.quant_weights(fmt, f"t/deq/{fmt}", N, K)
+    else:
+        W = random_blocks(101, fmt, N, K)
+    ref = oracle.dequant(fmt, W, N, K).astype(np.float32)
+    got = qmv.qmv_dequant(fmt, dev(torch, W), N, K)
+    torch.cuda.synchronize()
+    assert np.array_equal(got.cpu().numpy().view(np.uint32), ref.view(np.uint32))
+
+
+# ------------------------------------------------------------------ hand blocks
+@pytest.mark.parametrize("spec", hb.load()["blocks"], ids=lambda s: s["id"])
+def test_hand_blocks(env, spec):
+    blk = hb.block_bytes(spec)
+    x = hb.x_vec(spec["x"])[None, :]
+    y = gpu_matvec(env, spec["fmt"], blk, 1, 32, x)
+    assert float(y[0, 0]) == float(np.float32(float(spec["y"]))), (spec["id"], y[0, 0])
+
+
+# ------------------------------------------------------------------ small shapes
+SMALL = [(1, 32), (7, 64), (37, 96), (130, 1024), (257, 768), (65, 4096), (5, 14336), (300, 2048),
+         (33, 1056), (9, 35424)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B", [1, 2, 3, 5, 8])
+def test_small_shapes(env, fmt, B):
+    for N, K in SMALL:
+        say(f"small {fmt} B={B} {N}x{K}")
+        W = wl.quant_weights(fmt, f"t/small/{N}x{K}", N, K)
+        x = wl.activations(f"t/small/x/{K}/{B}", B, K)
+        y = gpu_matvec(env, fmt, W, N, K, x)
+        yr, S = oracle.matvec(fmt, W, N, K, x)
+        assert_tol(y, yr, S, (fmt, B, N, K))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_random_byte_blocks(env, fmt):
+    """Arbitrary stored bytes (any codes, any finite scale)."""
+    N, K, B = 41, 1024, 3
+    W = random_blocks(7, fmt, N, K)
+    x = wl.activations("t/rb/x", B, K)
+    y = gpu_matvec(env, fmt, W, N, K, x)
+    yr, S = oracle.matvec(fmt, W, N, K, x)
+    assert_tol(y, yr, S, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_one_hot_columns_exact(env, fmt):
+    """x = e_j gives y_i = DEQ(W)_ij exactly (all other products are 0)."""
+    N, K, B = 50, 1024, 8
+    W = random_blocks(3, fmt, N, K)
+    cols = [0, 1, 31, 32, 33, 511, 1000, 1023]
+    x = np.zeros((B, K), dtype=np.float32)
+    for b, j in enumerate(cols):
+        x[b, j] = 1.0
+    y = gpu_matvec(env, fmt, W, N, K, x)
+    deq = oracle.dequant(fmt, W, N, K).astype(np.float32)
+    for b, j in enumerate(cols):
+        assert np.array_equal(y[b], deq[:, j]), (fmt, j)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_batch_columns_equal_batch1_and_deterministic(env, fmt):
+    N, K = 300, 4096
+    W = wl.quant_weights(fmt, "t/b1/W", N, K)
+    x = wl.activations("t/b1/x", 8, K)
+    y8 = gpu_matvec(env, fmt, W, N, K, x)
+    y8b = gpu_matvec(env, fmt, W, N, K, x)
+    assert np.array_equal(y8.view(np.uint32), y8b.view(np.uint32))
+    for b in range(8):
+        y1 = gpu_matvec(env, fmt, W, N, K, x[b:b + 1])
+        assert np.array_equal(y1[0].view(np.uint32), y8[b].view(np.uint32)), b
+
+
+def test_strided_activations(env):
+    torch, qmv = env
+    N, K, B = 70, 2048, 3
+    W = wl.quant_weights("q4_1", "t/str/W", N, K)
+    xbig = wl.activations("t/str/x", B, K + 40)
+    x = xbig[:, :K]
+    xt = dev(torch, xbig)[:, :K]
+    y = torch.zeros((B, N + 5), dtype=torch.float32, device="cuda:0")
+    qmv.qmv_q4_1(dev(torch, W), N, K, xt, y=y[:, :N])
+    torch.cuda.synchronize()
+    yr, S = oracle.matvec("q4_1", W, N, K, x)
+    assert_tol(y[:, :N].cpu().numpy(), yr, S)
+    assert np.all(y[:, N:].cpu().numpy() == 0)     # nothing written beyond ldy's row
+
+
+# ------------------------------------------------------------------ full sizes
+@functools.lru_cache(maxsize=None)
+def _float_weights(tag, N, K):
+    return wl.weights_f32(tag, N, K)
+
+
+def _encoded(fmt, tag, N, K):
+    return wl.ENCODERS[fmt](_float_weights(tag, N, K))
+
+
+def _sample_rows(N, n, seed):
+    g = np.random.default_rng(seed)
+    r = set(g.choice(N, size=min(n, N), replace=False).tolist()) | {0, N - 1}
+    return np.array(sorted(r), dtype=np.int64)
+
+
+def test_config_q8_0_1024(env):
+    """Q8_0 1024 x 1024, batch 1, all rows."""
+    N = K = 1024
+    W = wl.quant_weights("q8_0", "cfg0/W", N, K)
+    x = wl.activations("cfg0/x", 1, K)
+    y = gpu_matvec(env, "q8_0", W, N, K, x)
+    yr, S = oracle.matvec("q8_0", W, N, K, x)
+    r = assert_tol(y, yr, S)
+    say(f"cfg0 max err/tol {r:.3g}")
+
+
+@pytest.mark.parametrize("fmt,batches", [("q8_0", (1,)), ("q4_0", (1, 2, 4, 8)), ("q4_1", (1, 2, 4, 8))])
+def test_llama8b_layer_set(env, fmt, batches):
+    """One 8B layer set + lm_head at full size (all layers share the shapes)."""
+    torch, qmv = env
+    mats = wl.LLAMA8B_LAYER + [wl.LLAMA8B_LM_HEAD]
+    worst = 0.0
+    for name, N, K in mats:
+        W = _encoded(fmt, f"llama8b/{name}", N, K)
+        Wd = dev(torch, W)
+        for B in batches:
+            say(f"llama8b {fmt} {name} {N}x{K} B={B}")
+            x = wl.activations(f"llama8b/x/{name}/{B}", B, K)
+            f = {"q8_0": qmv.qmv_q8_0, "q4_0": qmv.qmv_q4_0, "q4_1": qmv.qmv_q4_1}[fmt]
+            y = f(Wd, N, K, dev(torch, x))
+            torch.cuda.synchronize()
+            y = y.cpu().numpy()
+            full = (B == 1 and fmt == "q8_0" and name != "lm_head")
+            rows = None if full else _sample_rows(N, 1024, N + B)
+            yr, S = oracle.matvec(fmt, W, N, K, x, rows=rows)
+            yy = y if rows is None else y[:, rows]
+            worst = max(worst, assert_tol(yy, yr, S, (fmt, name, B)))
+        del Wd
+    say(f"llama8b {fmt} max err/tol {worst:.3g}")
+
+
+# ------------------------------------------------------------------ int8 requant
+def gpu_i8(env, W, x, mult, shift):
+    torch, qmv = env
+    y = qmv.qmv_i8_requant(dev(torch, W), dev(torch, x), dev(torch, mult), dev(torch, shift))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+def test_int8_qwen06b_shapes_bit_exact(env):
+    """Every Qwen3-0.6B-shaped matrix, uniform int8 W and x, mult in
+    [2^30, 2^31), shift 0..20; bit-exact."""
+    mats = wl.QWEN06B_LAYER + [wl.QWEN06B_LM_HEAD]
+    for name, N, K in mats:
+        say(f"int8 {name} {N}x{K}")
+        W = wl.int8_uniform(f"qwen/W/{name}", (N, K))
+        x = wl.int8_uniform(f"qwen/x/{name}", (1, K))
+        mult, shift = wl.requant_params(f"qwen/ms/{name}", N)
+        y = gpu_i8(env, W, x, mult, shift)
+        _, yr = oracle.matvec_i8(W, x, mult, shift)
+        assert np.array_equal(y, yr), name
+
+
+def test_int8_calibrated_shift_and_batch(env):
+    """Shifts chosen so outputs do not saturate (exercises the rounding
+    paths), batch 1..8, a ragged row count."""
+    N, K = 1000, 3072
+    W = wl.int8_uniform("qwen/cal/W", (N, K))
+    g = np.random.default_rng(5)
+    mult = g.integers(1 << 30, 1 << 31, size=N).astype(np.int32)
+    sigma = 127 * 127 / np.sqrt(3) * np.sqrt(K) / np.sqrt(3)
+    # smallest e with 3 sigma * mult / 2^31 / 2^e <= 127
+    e = np.ceil(np.log2(3 * sigma * mult.astype(np.float64) / 2 ** 31 / 127)).astype(np.int32)
+    shift = np.clip(e, 0, 31).astype(np.int32)
+    for B in (1, 2, 3, 8):
+        x = wl.int8_uniform(f"qwen/cal/x/{B}", (B, K))
+        y = gpu_i8(env, W, x, mult, shift)
+        _, yr = oracle.matvec_i8(W, x, mult, shift)
+        assert np.array_equal(y, yr), B
+        sat = np.mean((yr == 127) | (yr == -128))
+        assert sat < 0.05
+
+
+def test_int8_edges(env):
+    """x and W at -128, negative and extreme multipliers, shifts 0 and 31,
+    the largest n_cols, tiny shapes."""
+    g = np.random.default_rng(8)
+    for N, K in [(1, 16), (5, 48), (67, 1040), (3, 131056)]:
+        say(f"int8 edge {N}x{K}")
+        W = g.integers(-128, 128, size=(N, K), dtype=np.int8)
+        W[0, :] = -128
+        x = g.integers(-128, 128, size=(2, K), dtype=np.int8)
+        x[0, :] = -128
+        mult = g.integers(-(1 << 31), 1 << 31, size=N, dtype=np.int64).astype(np.int32)
+        mult[0] = -(1 << 31)
+        shift = g.integers(0, 32, size=N).astype(np.int32)
+        shift[0] = 0
+        if N > 1:
+            shift[-1] = 31
+        y = gpu_i8(env, W, x, mult, shift)
+        _, yr = oracle.matvec_i8(W, x, mult, shift)
+        assert np.array_equal(y, yr), (N, K)
+
+
+# ------------------------------------------------------------------ MoE
+@functools.lru_cache(maxsize=None)
+def _moe_experts(kind, N, K, E=wl.MOE_EXPERTS):
+    W = wl.quant_weights("q4_0", f"moe/{kind}", E * N, K)
+    return W.reshape(-1)
+
+
+def gpu_moe(env, fmt, Wall, stride, E, N, K, ids, x):
+    torch, qmv = env
+    y = qmv.qmv_moe(fmt, dev(torch, Wall), stride, E, N, K, dev(torch, ids), dev(torch, x))
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+@pytest.mark.parametrize("B", [1, 2, 3, 4, 8])
+def test_moe_30b_a3b_shapes(env, B):
+    """128 Q4_0 experts, top-8 distinct ids per token; gate/up 768x2048 with
+    one input per token, down 2048x768 with one input per (token, slot)."""
+    E, T = wl.MOE_EXPERTS, wl.MOE_TOPK
+    H, F = wl.MOE_HIDDEN, wl.MOE_FFN
+    ids = wl.moe_ids(f"moe/ids/{B}", B, T, E)
+    for kind, N, K in [("gate", F, H), ("down", H, F)]:
+        say(f"moe {kind} B={B}")
+        Wall = _moe_experts(kind, N, K)
+        stride = wl.block_bytes("q4_0", N, K)
+        if kind == "gate":
+            x = wl.activations(f"moe/x/{kind}/{B}", B, K)
+            yr, S = oracle.moe("q4_0", Wall, stride, E, N, K, ids, x)
+        else:
+            x = wl.activations(f"moe/x/{kind}/{B}", B * T, K).reshape(B, T, K)
+            yr, S = oracle.moe("q4_0", Wall, stride, E, N, K, ids, None, x_slots=x)
+        y = gpu_moe(env, "q4_0", Wall, stride, E, N, K, ids, x)
+        assert_tol(y, yr, S, (kind, B))
+
+
+@pytest.mark.parametrize("case", ["shared", "disjoint", "duplicates", "many_dup"])
+def test_moe_routing_edge_cases(env, case):
+    E, N, K = 16, 96, 512
+    fmt = "q4_0"
+    per = wl.block_bytes(fmt, N, K)
+    stride = per + 64
+    Wq = wl.quant_weights(fmt, "moe/edge/W", E * N, K).reshape(E, per)
+    Wall = np.zeros((E, stride), dtype=np.uint8)
+    Wall[:, :per] = Wq
+    Wall = Wall.reshape(-1)
+    if case == "shared":
+        ids = np.tile(np.array([3, 1, 4, 15], dtype=np.int32), (8, 1))
+    elif case == "disjoint":
+        ids = np.arange(16, dtype=np.int32).reshape(8, 2)
+    elif case == "duplicates":
+        ids = np.array([[2, 2, 5], [5, 2, 2]], dtype=np.int32)
+    else:                      # one expert used by 12 pairs: two groups of <= 8
+        ids = np.full((4, 3), 7, dtype=np.int32)
+    B, T = ids.shape
+    x = wl.activations(f"moe/edge/x/{case}", B * T, K).reshape(B, T, K)
+    y = gpu_moe(env, fmt, Wall, stride, E, N, K, ids, x)
+    yr, S = oracle.moe(fmt, Wall, stride, E, N, K, ids, None, x_slots=x)
+    assert_tol(y, yr, S, case)
+    # each pair equals the plain single-expert matvec of its expert, bitwise
+    torch, qmv = env
+    for b in range(B):
+        for s in range(T):
+            e = int(ids[b, s])
+            y1 = gpu_matvec(env, fmt, Wq[e], N, K, x[b, s][None])
+            assert np.array_equal(y1[0].view(np.uint32), y[b, s].view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_formats_and_invalid_ids(env, fmt):
+    E, N, K = 5, 70, 256
+    per = wl.block_bytes(fmt, N, K)
+    Wall = wl.quant_weights(fmt, f"moe/fmt/{fmt}", E * N, K).reshape(-1)
+    ids = np.array([[0, 4], [9, 1], [4, -1]], dtype=np.int32)
+    x = wl.activations(f"moe/fmt/x/{fmt}", 3, K)
+    y = gpu_moe(env, fmt, Wall, per, E, N, K, ids, x)
+    valid = (ids >= 0) & (ids < E)
+    assert np.all(np.isnan(y[~valid]))
+    ids_ok = np.where(valid, ids, 0).astype(np.int32)
+    yr, S = oracle.moe(fmt, Wall, per, E, N, K, ids_ok, x)
+    assert_tol(y[valid], yr[valid], S[valid], fmt)
