@@ -15,8 +15,10 @@
 //    the row.  Blocks are 34/18/20 bytes, so each lane issues 4-byte-aligned
 //    16-byte loads plus one 2-byte load, chosen so that no byte outside the
 //    block is read (no over-read past the last block), and re-aligns the
-//    codes in registers with v_alignbyte.  Weight loads are non-temporal:
-//    every byte is used once.
+//    codes in registers with v_alignbyte.  Weight loads are ordinary cached
+//    loads: a 64-byte line is shared by neighbouring lanes and by the three
+//    loads of a block, and a non-temporal hint (measured) loses a third of
+//    the bandwidth to refetches.
 //  * The activation vector is the only thing staged in LDS: x[b] once per
 //    workgroup, padded to 36 floats per 32-block so that the 16-byte LDS
 //    reads of neighbouring lanes fall in different banks, plus the per-block
@@ -47,15 +49,9 @@ typedef unsigned int u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
 // --------------------------------------------------------------- loads
 // p is 4-byte aligned; the hardware allows dword-aligned 16-byte loads.
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4_a4*>(p));
-}
-__device__ __forceinline__ uint32_t ld4(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
-__device__ __forceinline__ uint32_t ld2(const uint8_t* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p));
-}
+__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_a4*>(p); }
+__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+__device__ __forceinline__ uint32_t ld2(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
 
 __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(h & 0xffffu)));
@@ -68,53 +64,88 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
 //   Q8_0: c[0..7] = q_0..q_31 (int8, element 4i+k in byte k of c[i])
 //   Q4_0/Q4_1: c[0..3] = qs[0..15] (low nibble of byte k of c[i] is element
 //   4i+k, high nibble element 16+4i+k).
+//
+// fetch() only issues the loads into a Raw record; decode() turns the raw
+// registers into the scale(s) and aligned codes.  Keeping them apart lets a
+// wave have the next blocks in flight while it computes the current ones.
 struct Q8_0 {
     static constexpr int kBytes = 34;
-    __device__ static void load(const uint8_t* W, int64_t g, float& d, float& m, uint32_t (&c)[8]) {
+    static constexpr bool kNeedSx = false;   // the block term needs no sum of x
+    struct Raw {
+        u32x4 a, b;
+        uint32_t u;
+        uint32_t sh;
+    };
+    // 34g = 2g (mod 4): even blocks start 4-aligned (read [o, o+32) and the
+    // last 2 code bytes), odd blocks start at 2 (mod 4) (read d alone, then
+    // the 32 codes from o+2, 4-aligned).  Exactly the block's 34 bytes.
+    __device__ static void fetch(const uint8_t* W, int64_t g, Raw& r) {
         const int64_t o = 34 * g;
-        // 34g = 2g (mod 4): even blocks start 4-aligned (d, then codes at
-        // +2: read [o, o+32) + the last 2 code bytes), odd blocks start at 2
-        // (mod 4) (read d alone, then the 32 codes from o+2, 4-aligned).
         const bool even = (g & 1) == 0;
-        const u32x4 a = ld16(W + o + (even ? 0 : 2));
-        const u32x4 b = ld16(W + o + (even ? 16 : 18));
-        const uint32_t u = ld2(W + o + (even ? 32 : 0));
-        const uint32_t w[9] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w, u};
-        const uint32_t sh = even ? 2u : 0u;
+        r.a = ld16(W + o + (even ? 0 : 2));
+        r.b = ld16(W + o + (even ? 16 : 18));
+        r.u = ld2(W + o + (even ? 32 : 0));
+        r.sh = even ? 2u : 0u;
+    }
+    __device__ static void decode(const Raw& r, float& d, float& m, uint32_t (&c)[8]) {
+        const uint32_t w[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.u};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
-        d = half_bits_to_float(even ? a.x : u);
+        for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r.sh);
+        d = half_bits_to_float(r.sh ? r.a.x : r.u);
         m = 0.f;
     }
 };
 
 struct Q4_0 {
     static constexpr int kBytes = 18;
-    __device__ static void load(const uint8_t* W, int64_t g, float& d, float& m, uint32_t (&c)[8]) {
+    static constexpr bool kNeedSx = true;    // folds the -8 offset
+    struct Raw {
+        u32x4 a;
+        uint32_t u;
+        uint32_t sh;
+    };
+    __device__ static void fetch(const uint8_t* W, int64_t g, Raw& r) {
         const int64_t o = 18 * g;
         const bool even = (g & 1) == 0;    // 18g = 2g (mod 4)
-        const u32x4 a = ld16(W + o + (even ? 0 : 2));
-        const uint32_t u = ld2(W + o + (even ? 16 : 0));
-        const uint32_t w[5] = {a.x, a.y, a.z, a.w, u};
-        const uint32_t sh = even ? 2u : 0u;
+        r.a = ld16(W + o + (even ? 0 : 2));
+        r.u = ld2(W + o + (even ? 16 : 0));
+        r.sh = even ? 2u : 0u;
+    }
+    __device__ static void decode(const Raw& r, float& d, float& m, uint32_t (&c)[8]) {
+        const uint32_t w[5] = {r.a.x, r.a.y, r.a.z, r.a.w, r.u};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
-        d = half_bits_to_float(even ? a.x : u);
+        for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r.sh);
+        d = half_bits_to_float(r.sh ? r.a.x : r.u);
         m = 0.f;
     }
 };
 
 struct Q4_1 {
     static constexpr int kBytes = 20;
-    __device__ static void load(const uint8_t* W, int64_t g, float& d, float& m, uint32_t (&c)[8]) {
+    static constexpr bool kNeedSx = true;    // folds the minimum m
+    struct Raw {
+        uint32_t dm;
+        u32x4 a;
+    };
+    __device__ static void fetch(const uint8_t* W, int64_t g, Raw& r) {
         const int64_t o = 20 * g;          // always 4-aligned
-        const uint32_t dm = ld4(W + o);
-        const u32x4 a = ld16(W + o + 4);
-        c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
-        d = half_bits_to_float(dm);
-        m = half_bits_to_float(dm >> 16);
+        r.dm = ld4(W + o);
+        r.a = ld16(W + o + 4);
+    }
+    __device__ static void decode(const Raw& r, float& d, float& m, uint32_t (&c)[8]) {
+        c[0] = r.a.x; c[1] = r.a.y; c[2] = r.a.z; c[3] = r.a.w;
+        d = half_bits_to_float(r.dm);
+        m = half_bits_to_float(r.dm >> 16);
     }
 };
+
+// fetch + decode in one go (dequant kernel).
+template <class F>
+__device__ __forceinline__ void load_block(const uint8_t* W, int64_t g, float& d, float& m, uint32_t (&c)[8]) {
+    typename F::Raw r;
+    F::fetch(W, g, r);
+    F::decode(r, d, m, c);
+}
 
 __device__ __forceinline__ float sbyte(uint32_t w, int k) {
     return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(w >> (8 * k))));
@@ -212,52 +243,149 @@ __device__ __forceinline__ void dot_cols(const float (&q)[32], const float* __re
     }
 }
 
-// Block term from the code dot s and the block sum sx of x.
+// Adds a block's term to the running sum, from the code dot s and the block
+// sum sx of x.  Written with explicit fused multiply-adds so that every entry
+// point (dense, MoE, any batch width) rounds identically.
 template <class F> struct Term;
 template <> struct Term<Q8_0> {
-    __device__ static float f(float d, float, float s, float) { return d * s; }
+    __device__ static float add(float acc, float d, float, float s, float) { return __builtin_fmaf(d, s, acc); }
 };
 template <> struct Term<Q4_0> {
     // sum_j d*(c_j - 8) x_j = d * (sum_j c_j x_j - 8 sum_j x_j)
-    __device__ static float f(float d, float, float s, float sx) { return d * __builtin_fmaf(-8.f, sx, s); }
+    __device__ static float add(float acc, float d, float, float s, float sx) {
+        return __builtin_fmaf(d, __builtin_fmaf(-8.f, sx, s), acc);
+    }
 };
 template <> struct Term<Q4_1> {
     // sum_j (d*c_j + m) x_j = d * sum_j c_j x_j + m * sum_j x_j
-    __device__ static float f(float d, float m, float s, float sx) { return __builtin_fmaf(d, s, m * sx); }
+    __device__ static float add(float acc, float d, float m, float s, float sx) {
+        return __builtin_fmaf(d, s, __builtin_fmaf(m, sx, acc));
+    }
 };
 
-// Sum over the LPR consecutive lanes of a segment; every lane of the
-// segment ends with the same total.  Fixed butterfly order.
+// Sum over the LPR consecutive lanes of a segment, in a fixed order; the
+// total is valid in the segment's first lane (for LPR <= 16 in every lane of
+// the segment).  Within 16-lane rows the sum uses DPP lane swizzles (a few
+// VALU cycles each): xor 1, xor 2, half-row mirror, row mirror.  Across rows
+// the row totals are read as scalars.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane_val(float v, int l) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 template <int LPR>
 __device__ __forceinline__ float segment_sum(float v) {
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "segment width");
+    v += dpp_mov<0xB1>(v);     // quad_perm [1,0,3,2]: pairs
+    v += dpp_mov<0x4E>(v);     // quad_perm [2,3,0,1]: quads
+    v += dpp_mov<0x141>(v);    // row_half_mirror: 8 lanes
+    if (LPR >= 16) v += dpp_mov<0x140>(v);   // row_mirror: 16 lanes
+    if (LPR == 32) {
+        const float a = lane_val(v, 0) + lane_val(v, 16);
+        const float b = lane_val(v, 32) + lane_val(v, 48);
+        v = (threadIdx.x & 32) ? b : a;
+    } else if (LPR == 64) {
+        v = (lane_val(v, 0) + lane_val(v, 16)) + (lane_val(v, 32) + lane_val(v, 48));
+    }
     return v;
 }
 
-// Stages the B activation columns xcol[b][0..32*nb) into LDS as
-// xs[b][block][36] and the per-block sums into sx[b][block] (sequential sum
-// over the block's 32 elements).  Ends with a barrier.
-template <int B>
-__device__ __forceinline__ void stage_x_cols(const float* const (&xcol)[B], int nb, float* xs, float* sx, int w) {
+// Straight-line staging of one 16-byte-aligned activation column (batch 1):
+// every thread issues XU float4 loads (indices clamped, so the count is a
+// compile-time constant), and only later writes them to LDS.  With no loop
+// the compiler can keep other loads issued in between in flight while it
+// waits for these.
+template <int XU, int NT>
+struct XStage {
+    float4 v[XU];
+    __device__ __forceinline__ void load(const float* __restrict__ x, int K4) {
+        const float4* src = reinterpret_cast<const float4*>(x);
+#pragma unroll
+        for (int u = 0; u < XU; ++u) v[u] = src[min((int)threadIdx.x + u * NT, K4 - 1)];
+    }
+    // Indices past the end are clamped like the loads: such a thread
+    // writes the last chunk's own value to the last chunk's slot.
+    __device__ __forceinline__ void store(float* xs, int K4) const {
+#pragma unroll
+        for (int u = 0; u < XU; ++u) {
+            const int e = 4 * min((int)threadIdx.x + u * NT, K4 - 1);
+            *reinterpret_cast<float4*>(xs + (e >> 5) * kXPad + (e & 31)) = v[u];
+        }
+    }
+};
+
+// Per-block sums of the staged columns (formats that fold an offset).
+template <int NT>
+__device__ __forceinline__ void block_sums(const float* xs, float* sx, int count) {
+    for (int t = threadIdx.x; t < count; t += NT) {
+        const float4* p = reinterpret_cast<const float4*>(xs + t * kXPad);
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 v = p[i];
+            acc += v.x; acc += v.y; acc += v.z; acc += v.w;
+        }
+        sx[t] = acc;
+    }
+}
+
+// Stages the first w of the B activation columns xcol[b][0..32*nb) into
+// LDS as xs[b][block][36] and, when the format needs them, the per-block
+// sums into sx[b][block].  Loads are issued in batches of 4 per thread
+// before any is used, so the staging costs a few memory round trips, not
+// one per element.  vec: every column is 16-byte aligned (float4 loads).
+// Ends with a barrier.
+template <bool kNeedSx, int B, int NT>
+__device__ __forceinline__ void stage_x_cols(const float* const (&xcol)[B], int nb, float* xs, float* sx, int w,
+                                             bool vec) {
     const int K = nb * 32;
+    const int tid = threadIdx.x;
 #pragma unroll
     for (int b = 0; b < B; ++b) {
         if (b < w) {
-            const float* xb = xcol[b];
             float* dst = xs + b * nb * kXPad;
-            for (int e = threadIdx.x; e < K; e += kThreads) dst[(e >> 5) * kXPad + (e & 31)] = xb[e];
+            if (vec) {
+                const float4* src = reinterpret_cast<const float4*>(xcol[b]);
+                const int K4 = K >> 2;
+                auto put = [&](int c, const float4& v) {
+                    const int e = 4 * c;
+                    *reinterpret_cast<float4*>(dst + (e >> 5) * kXPad + (e & 31)) = v;
+                };
+                for (int c0 = tid; c0 < K4; c0 += 4 * NT) {
+                    const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
+                    const float4 v0 = src[c0];
+                    const float4 v1 = src[min(c1, K4 - 1)];
+                    const float4 v2 = src[min(c2, K4 - 1)];
+                    const float4 v3 = src[min(c3, K4 - 1)];
+                    put(c0, v0);
+                    if (c1 < K4) put(c1, v1);
+                    if (c2 < K4) put(c2, v2);
+                    if (c3 < K4) put(c3, v3);
+                }
+            } else {
+                const float* src = xcol[b];
+                auto put = [&](int e, float v) { dst[(e >> 5) * kXPad + (e & 31)] = v; };
+                for (int e0 = tid; e0 < K; e0 += 4 * NT) {
+                    const int e1 = e0 + NT, e2 = e0 + 2 * NT, e3 = e0 + 3 * NT;
+                    const float v0 = src[e0];
+                    const float v1 = src[min(e1, K - 1)];
+                    const float v2 = src[min(e2, K - 1)];
+                    const float v3 = src[min(e3, K - 1)];
+                    put(e0, v0);
+                    if (e1 < K) put(e1, v1);
+                    if (e2 < K) put(e2, v2);
+                    if (e3 < K) put(e3, v3);
+                }
+            }
         }
     }
     __syncthreads();
-    for (int t = threadIdx.x; t < w * nb; t += kThreads) {
-        const float* p = xs + t * kXPad;
-        float acc = 0.f;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) acc += p[e];
-        sx[t] = acc;
+    if (kNeedSx) {
+        block_sums<NT>(xs, sx, w * nb);
+        __syncthreads();
     }
-    __syncthreads();
 }
 
 // ------------------------------------------------------------------ kernels
@@ -288,7 +416,7 @@ __device__ __forceinline__ void tile_rows(const uint8_t* __restrict__ W, int64_t
         float d[RPL], m[RPL];
         uint32_t c[RPL][8];
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) F::load(W, gbase[r] + j, d[r], m[r], c[r]);
+        for (int r = 0; r < RPL; ++r) load_block<F>(W, gbase[r] + j, d[r], m[r], c[r]);
         const float* xj = xs + j * kXPad;
         float sxb[B];
 #pragma unroll
@@ -302,7 +430,7 @@ __device__ __forceinline__ void tile_rows(const uint8_t* __restrict__ W, int64_t
             for (int b = 0; b < B; ++b) s[b] = 0.f;
             dot_cols<B>(q, xj, xb, s, w);
 #pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] += Term<F>::f(d[r], m[r], s[b], sxb[b]);
+            for (int b = 0; b < B; ++b) acc[r][b] = Term<F>::add(acc[r][b], d[r], m[r], s[b], sxb[b]);
         }
     }
 #pragma unroll
@@ -311,40 +439,144 @@ __device__ __forceinline__ void tile_rows(const uint8_t* __restrict__ W, int64_t
         for (int b = 0; b < B; ++b) acc[r][b] = segment_sum<LPR>(acc[r][b]);
 }
 
-// Dense matvec: a persistent grid of workgroups; each wave takes tiles of
-// G*RPL consecutive rows.  LPR lanes per row segment, RPL rows per lane, B
-// batch columns.
-template <class F, int B, int LPR, int RPL>
-__global__ __launch_bounds__(kThreads) void qmv_kernel(const uint8_t* __restrict__ W, int64_t N, int nb,
+// Dense matvec.  A persistent grid (as many workgroups as fit on the GPU at
+// once); wave w of the grid takes row tiles w, w + waves, ... .  A tile is
+// G*RPL rows (G row segments of LPR lanes, RPL rows per lane) and is worked
+// through in T = ceil(nb/LPR) steps; in step t lane li reads block
+// li + LPR*t of each of its RPL rows.  The blocks of the next step are
+// loaded while the current step is computed (two steps in flight per wave),
+// and the first step's loads are issued before the activation staging so
+// that both latencies overlap.
+template <class F, int B, int LPR, int RPL, int XU, int NW>
+__global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict__ W, int64_t N, int nb,
                                                        const float* __restrict__ x, int64_t ldx,
-                                                       float* __restrict__ y, int64_t ldy) {
+                                                       float* __restrict__ y, int64_t ldy, int xvec) {
     extern __shared__ float lds[];
     float* xs = lds;
     float* sx = lds + B * nb * kXPad;
-    const float* xcol[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) xcol[b] = x + b * ldx;
-    stage_x_cols<B>(xcol, nb, xs, sx, B);
 
     constexpr int G = 64 / LPR;
     constexpr int ROWS = G * RPL;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int seg = lane / LPR;
     const int li = lane % LPR;
-    for (int64_t tile = (int64_t)blockIdx.x * kWaves + wave; tile * ROWS < N; tile += (int64_t)gridDim.x * kWaves) {
-        const int64_t row0 = tile * ROWS;
-        float acc[RPL][B];
-        tile_rows<F, B, LPR, RPL>(W, N, nb, row0, xs, sx, acc, B);
-        if (li == 0) {
+    const int T = (nb + LPR - 1) / LPR;
+    const int64_t ntiles = (N + ROWS - 1) / ROWS;
+    const int64_t wstride = (int64_t)gridDim.x * NW;
+
+    // Step (tile, t): lane li handles block li + LPR*t of its RPL rows.
+    using Raw = typename F::Raw;
+    auto load_step = [&](int64_t tile, int t, Raw (&blk)[RPL]) {
+        const int j = min(li + LPR * t, nb - 1);      // clamp: stays in bounds
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-                const int64_t row = row0 + r * G + seg;
-                if (row < N) {
+        for (int r = 0; r < RPL; ++r) {
+            const int64_t row = min(tile * ROWS + r * G + seg, N - 1);
+            F::fetch(W, row * nb + j, blk[r]);
+        }
+    };
+    float acc[RPL][B];
 #pragma unroll
-                    for (int b = 0; b < B; ++b) y[b * ldy + row] = acc[r][b];
+    for (int r = 0; r < RPL; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
+
+    auto compute_step = [&](int64_t tile, int t, const Raw (&blk)[RPL]) {
+        const int j = li + LPR * t;
+        const bool valid = j < nb;
+        const int jc = valid ? j : nb - 1;
+        const float* xj = xs + jc * kXPad;
+        float sxb[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) sxb[b] = F::kNeedSx ? sx[b * nb + jc] : 0.f;
+#pragma unroll
+        for (int r = 0; r < RPL; ++r) {
+            float d, m;
+            uint32_t c[8];
+            F::decode(blk[r], d, m, c);
+            float q[32];
+            codes_to_float<F>(c, q);
+            float sdot[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) sdot[b] = 0.f;
+            dot_cols<B>(q, xj, nb * kXPad, sdot, B);
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float upd = Term<F>::add(acc[r][b], d, m, sdot[b], sxb[b]);
+                acc[r][b] = valid ? upd : acc[r][b];
+            }
+        }
+        if (t == T - 1) {   // tile done: reduce the segments and write
+#pragma unroll
+            for (int r = 0; r < RPL; ++r)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[r][b] = segment_sum<LPR>(acc[r][b]);
+            if (li == 0) {
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) {
+                    const int64_t row = tile * ROWS + r * G + seg;
+                    if (row < N) {
+#pragma unroll
+                        for (int b = 0; b < B; ++b) y[b * ldy + row] = acc[r][b];
+                    }
                 }
             }
+#pragma unroll
+            for (int r = 0; r < RPL; ++r)
+#pragma unroll
+                for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
+        }
+    };
+    auto advance = [&](int64_t& tile, int& t) {
+        if (++t == T) { t = 0; tile += wstride; }
+    };
+
+    // Two register buffers used in turn: the loads of one step are in flight
+    // while the previous step is computed.  Loads are issued without
+    // branches (a wave past its last step re-reads its current blocks, which
+    // are in cache), so the compiler waits only for the buffer in use.
+    int64_t tileA = (int64_t)blockIdx.x * NW + wave;
+    int tA = 0;
+    Raw bufA[RPL], bufB[RPL];
+    const int K4 = nb * 8;
+    if (XU > 0 && xvec) {
+        // batch 1: x loads, then the first weight loads, then x into LDS
+        XStage<XU, 64 * NW> xst;
+        xst.load(x, K4);
+        load_step(min(tileA, ntiles - 1), tA, bufA);
+        __builtin_amdgcn_sched_barrier(0);   // keep both batches of loads issued first
+        xst.store(xs, K4);
+        __syncthreads();
+        if (F::kNeedSx) {
+            block_sums<64 * NW>(xs, sx, nb);
+            __syncthreads();
+        }
+    } else {
+        const float* xcol[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) xcol[b] = x + b * ldx;
+        stage_x_cols<F::kNeedSx, B, 64 * NW>(xcol, nb, xs, sx, B, xvec != 0);
+        load_step(min(tileA, ntiles - 1), tA, bufA);
+    }
+
+    if (tileA < ntiles) {
+        while (true) {
+            int64_t tileB = tileA;
+            int tB = tA;
+            advance(tileB, tB);
+            const bool hasB = tileB < ntiles;
+            load_step(hasB ? tileB : tileA, hasB ? tB : tA, bufB);
+            __builtin_amdgcn_sched_barrier(0);   // issue B's loads before using A
+            compute_step(tileA, tA, bufA);
+            if (!hasB) break;
+            tileA = tileB;
+            tA = tB;
+            advance(tileA, tA);
+            const bool hasA = tileA < ntiles;
+            load_step(hasA ? tileA : tileB, hasA ? tA : tB, bufA);
+            __builtin_amdgcn_sched_barrier(0);   // issue A's loads before using B
+            compute_step(tileB, tB, bufB);
+            if (!hasA) break;
         }
     }
 }
@@ -373,7 +605,7 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
         const int p = b < w ? members[b] : 0;
         xcol[b] = x + (int64_t)(p / top_k) * xs_tok + (int64_t)(p % top_k) * xs_slot;
     }
-    stage_x_cols<B>(xcol, nb, xs, sx, w);
+    stage_x_cols<F::kNeedSx, B, kThreads>(xcol, nb, xs, sx, w, false);
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int seg = lane / LPR;
@@ -468,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
     if (g >= nblocks) return;
     float d, m;
     uint32_t c[8];
-    F::load(W, g, d, m, c);
+    load_block<F>(W, g, d, m, c);
     float v[32];
     block_values<F>(d, m, c, v);
     float* o = out + g * 32;
@@ -477,13 +709,14 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------ host
-constexpr int kRpl = 2;
+constexpr int kRpl = 2;   // MoE rows per lane
 
-template <class F, int B, int LPR>
+template <class F, int B, int LPR, int XU, int NW>
 int32_t launch_b(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
                  hipStream_t st) {
-    auto kern = qmv_kernel<F, B, LPR, kRpl>;
-    const size_t lds = (size_t)B * nb * (kXPad + 1) * sizeof(float);
+    constexpr int RPL = 1;
+    auto kern = qmv_kernel<F, B, LPR, RPL, XU, NW>;
+    const size_t lds = (size_t)B * nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -491,37 +724,59 @@ int32_t launch_b(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ld
             return fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
         attr_set = true;
     }
-    constexpr int rows_per_wg = kWaves * (64 / LPR) * kRpl;
+    constexpr int rows_per_wg = NW * (64 / LPR) * RPL;
     const int64_t tiles = (N + rows_per_wg - 1) / rows_per_wg;
-    const int per_cu = std::max(1, std::min(8, (int)(kLdsMax / std::max<size_t>(lds, 1))));
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int64_t cap = (int64_t)device_cu_count() * per_cu;
-    const int grid = (int)std::min<int64_t>(tiles, cap);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), lds, st, W, N, nb, x, ldx, y, ldy);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, cap));
+    const int xvec = (aligned(x, 16) && ldx % 4 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nb, x, ldx, y, ldy, xvec);
     return check_launch("qmv");
 }
 
-template <class F, int B>
+// Lanes per row: whole waves for long rows, smaller segments for short rows
+// so that lanes are not left idle (e.g. 24 blocks -> 8 lanes x 3).
+template <class F, int B, int XU, int NW>
 int32_t launch_lpr(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
                    hipStream_t st) {
-    // Lanes per row: whole waves for long rows, smaller segments for short
-    // rows so that lanes are not left idle (e.g. 24 blocks -> 8 lanes x 3).
-    if (nb >= 64) return launch_b<F, B, 64>(W, N, nb, x, ldx, y, ldy, st);
-    if (nb >= 32) return launch_b<F, B, 32>(W, N, nb, x, ldx, y, ldy, st);
-    return launch_b<F, B, 8>(W, N, nb, x, ldx, y, ldy, st);
+    if (nb >= 64) return launch_b<F, B, 64, XU, NW>(W, N, nb, x, ldx, y, ldy, st);
+    if (nb >= 32) return launch_b<F, B, 32, XU, NW>(W, N, nb, x, ldx, y, ldy, st);
+    return launch_b<F, B, 8, XU, NW>(W, N, nb, x, ldx, y, ldy, st);
+}
+
+// Batch 1.  Workgroups of 8 waves when the staged activations (> 40 KB)
+// allow few workgroups per CU, else 4 (more, smaller workgroups spread
+// small matrices over every CU).  Activations are staged with straight-line
+// 16-byte loads when 16-byte aligned: XU loads per thread cover
+// K <= 16 * 64 * NW * XU / 4.
+template <class F>
+int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
+                  hipStream_t st) {
+    const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    const bool vec = aligned(x, 16);
+    const int K4 = nb * 8;
+    if (lds > 40 * 1024) {
+        if (vec && K4 <= 2 * 512) return launch_lpr<F, 1, 2, 8>(W, N, nb, x, ldx, y, ldy, st);
+        if (vec && K4 <= 8 * 512) return launch_lpr<F, 1, 8, 8>(W, N, nb, x, ldx, y, ldy, st);
+        return launch_lpr<F, 1, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    }
+    if (vec && K4 <= 4 * 256) return launch_lpr<F, 1, 4, 4>(W, N, nb, x, ldx, y, ldy, st);
+    if (vec && K4 <= 16 * 256) return launch_lpr<F, 1, 16, 4>(W, N, nb, x, ldx, y, ldy, st);
+    return launch_lpr<F, 1, 0, 4>(W, N, nb, x, ldx, y, ldy, st);
 }
 
 template <class F>
 int32_t launch_batch(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B, float* y,
                      int64_t ldy, hipStream_t st) {
     switch (B) {
-    case 1: return launch_lpr<F, 1>(W, N, nb, x, ldx, y, ldy, st);
-    case 2: return launch_lpr<F, 2>(W, N, nb, x, ldx, y, ldy, st);
-    case 3: return launch_lpr<F, 3>(W, N, nb, x, ldx, y, ldy, st);
-    case 4: return launch_lpr<F, 4>(W, N, nb, x, ldx, y, ldy, st);
-    case 5: return launch_lpr<F, 5>(W, N, nb, x, ldx, y, ldy, st);
-    case 6: return launch_lpr<F, 6>(W, N, nb, x, ldx, y, ldy, st);
-    case 7: return launch_lpr<F, 7>(W, N, nb, x, ldx, y, ldy, st);
-    default: return launch_lpr<F, 8>(W, N, nb, x, ldx, y, ldy, st);
+    case 1: return launch_b1<F>(W, N, nb, x, ldx, y, ldy, st);
+    case 2: return launch_lpr<F, 2, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    case 3: return launch_lpr<F, 3, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    case 4: return launch_lpr<F, 4, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    case 5: return launch_lpr<F, 5, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    case 6: return launch_lpr<F, 6, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    case 7: return launch_lpr<F, 7, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    default: return launch_lpr<F, 8, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
     }
 }
 
@@ -548,8 +803,9 @@ int32_t matvec(const char* name, const void* W, int64_t N, int64_t K, const floa
     const int nb = (int)(K / 32);
     // The staged activation block must fit in LDS; wider batches than fit
     // are processed in column groups (each group re-reads W).
-    const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / (nb * (kXPad + 1) * (int)sizeof(float))));
-    if ((size_t)nb * (kXPad + 1) * sizeof(float) > (size_t)kLdsMax)
+    const int per_col = nb * (kXPad + (F::kNeedSx ? 1 : 0)) * (int)sizeof(float);
+    const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / per_col));
+    if (per_col > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
     for (int b0 = 0; b0 < batch; b0 += per_pass) {
         const int bw = std::min(per_pass, batch - b0);

@@ -3,6 +3,9 @@
 
 #include <atomic>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 namespace qmv {
 
@@ -35,6 +38,27 @@ int device_cu_count() {
         cus = 256;
     g_cus[dev].store(cus, std::memory_order_relaxed);
     return cus;
+}
+
+int resident_wgs(const void* kernel, int threads, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, size_t>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_pair(kernel, lds * 64 + (size_t)dev);
+    {
+        std::lock_guard<std::mutex> g(mu);
+        auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1) {
+        (void)hipGetLastError();
+        n = 1;
+    }
+    std::lock_guard<std::mutex> g(mu);
+    cache[key] = n;
+    return n;
 }
 
 int32_t check_launch(const char* what) {

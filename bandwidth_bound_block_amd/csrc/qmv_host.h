@@ -22,6 +22,10 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Workgroups of `kernel` (block threads, dynamic LDS bytes) that fit on one
+// compute unit at once (cached per kernel and LDS size; at least 1).
+int resident_wgs(const void* kernel, int threads, size_t lds);
+
 // Maps the status of the launch just issued to a return code.
 int32_t check_launch(const char* what);
 

@@ -57,10 +57,28 @@ __device__ __forceinline__ int32_t rdbpot(int32_t v, int32_t e) {
 
 __device__ __forceinline__ int8_t sat8(int32_t v) { return (int8_t)(v < -128 ? -128 : (v > 127 ? 127 : v)); }
 
+// Exact int32 sum over the LPR consecutive lanes of a segment; valid in the
+// segment's first lane.  DPP swizzles within 16-lane rows, scalar reads
+// across rows.
+template <int CTRL>
+__device__ __forceinline__ int32_t dpp_mov(int32_t v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, false);
+}
 template <int LPR>
 __device__ __forceinline__ int32_t segment_sum(int32_t v) {
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "segment width");
+    v += dpp_mov<0xB1>(v);     // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);     // quad_perm [2,3,0,1]
+    v += dpp_mov<0x141>(v);    // row_half_mirror
+    if (LPR >= 16) v += dpp_mov<0x140>(v);   // row_mirror
+    if (LPR == 32) {
+        const int32_t a = __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16);
+        const int32_t b = __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+        v = (threadIdx.x & 32) ? b : a;
+    } else if (LPR == 64) {
+        v = __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+            __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+    }
     return v;
 }
 

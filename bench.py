@@ -1,0 +1,411 @@
+#!/usr/bin/env python3
+"""Decode-time quantized matvec benchmark on one MI355X.
+
+A step is one batch-1 decode token of the 8B Llama-shaped layer set in Q8_0:
+32 layers x (q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 14336x4096,
+down 4096x14336) + lm_head 128256x4096 = 225 matvecs, 7,973,699,584 bytes of
+weights, every layer in its own device buffers (the working set is ~31x the
+256 MB last-level cache, so every step streams from HBM).  Weights are drawn
+N(0, 0.02^2) and encoded per 32-weight block; activations N(0, 1).  The step
+is captured once as a HIP graph and replayed.
+
+Printed: one JSON line with the step's achieved GB/s (algorithmic weight +
+activation + output bytes / wall time, whole job), the equivalent decode
+tok/s, a per-kernel roofline object measured with HIP events on the launch
+stream, the oracle's time on the host (cpu_baseline), and the other
+workloads of the path (Q4_0 / Q4_1 at batch 1, 2, 4, 8; the int8 requant
+path on Qwen3-0.6B shapes; the MoE expert path) as extra fields.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweeps all|none|a,b]
+"""
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_GBS = 8000.0
+METRIC = "achieved HBM GB/s (% of MI355X peak) for batch-1 quant matvec; equiv. decode tok/s"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- sweeps
+_FLOAT_CACHE = {}
+_ENC_CACHE = {}
+
+
+def encoded(wl, fmt, tag, N, K):
+    """Seeded weights for (tag, N, K) encoded as fmt; the float draw is
+    shared by the formats (the same draw as workloads.quant_weights)."""
+    key = (fmt, tag, N, K)
+    if key not in _ENC_CACHE:
+        fk = (tag, N, K)
+        if fk not in _FLOAT_CACHE:
+            _FLOAT_CACHE[fk] = wl.weights_f32(tag, N, K)
+        _ENC_CACHE[key] = wl.ENCODERS[fmt](_FLOAT_CACHE[fk])
+    return _ENC_CACHE[key]
+
+
+class Sweep:
+    """A list of independent launches making up one step, with the bytes
+    each launch must move (weights once, activations once, outputs once)."""
+
+    def __init__(self, name, batch):
+        self.name = name
+        self.batch = batch
+        self.launches = []      # (label, cfunc, args_without_stream, bytes)
+        self.keep = []          # device tensors kept alive
+
+    def add(self, label, cfn, args, nbytes):
+        self.launches.append((label, cfn, tuple(args), int(nbytes)))
+
+    @property
+    def bytes_per_step(self):
+        return sum(l[3] for l in self.launches)
+
+    def run(self, stream_ptr):
+        s = ctypes.c_void_p(stream_ptr)
+        for label, cfn, args, _ in self.launches:
+            rc = cfn(*args, s)
+            if rc != 0:
+                import bandwidth_bound_block_amd as qmv
+                raise RuntimeError(f"{self.name}/{label}: rc={rc}: {qmv.last_error()}")
+
+
+def _dense_sweep(torch, qmv, wl, fmt, batch, layers, layer_mats, head, tagbase, name):
+    cfn = {"q8_0": qmv.lib().qmv_q8_0, "q4_0": qmv.lib().qmv_q4_0, "q4_1": qmv.lib().qmv_q4_1}[fmt]
+    sw = Sweep(name, batch)
+    dev = "cuda:0"
+    t0 = time.time()
+    mats = {}
+    for mname, N, K in layer_mats + [head]:
+        W = encoded(wl, fmt, f"{tagbase}/{mname}", N, K)
+        mats[mname] = torch.from_numpy(W).to(dev)
+    log(f"[{name}] encoded weights in {time.time() - t0:.1f}s")
+    xs = {}
+    for layer in range(layers + 1):
+        for K in sorted({m[2] for m in layer_mats + [head]}):
+            xs[(layer, K)] = torch.from_numpy(wl.activations(f"{tagbase}/x/{layer}/{K}/{batch}", batch, K)).to(dev)
+    for layer in range(layers):
+        for mname, N, K in layer_mats:
+            W = mats[mname].clone()          # every layer in its own buffer
+            y = torch.empty((batch, N), dtype=torch.float32, device=dev)
+            x = xs[(layer, K)]
+            sw.keep += [W, y]
+            nbytes = W.numel() + 4 * batch * K + 4 * batch * N
+            sw.add(mname, cfn, (W.data_ptr(), N, K, x.data_ptr(), K, batch, y.data_ptr(), N), nbytes)
+    mname, N, K = head
+    W = mats[mname]
+    y = torch.empty((batch, N), dtype=torch.float32, device=dev)
+    x = xs[(layers, K)]
+    sw.keep += [W, y, xs]
+    sw.add(mname, cfn, (W.data_ptr(), N, K, x.data_ptr(), K, batch, y.data_ptr(), N),
+           W.numel() + 4 * batch * K + 4 * batch * N)
+    sw.keep.append(mats)
+    return sw
+
+
+def build_llama(torch, qmv, wl, fmt, batch):
+    return _dense_sweep(torch, qmv, wl, fmt, batch, wl.LLAMA8B_LAYERS, wl.LLAMA8B_LAYER, wl.LLAMA8B_LM_HEAD,
+                        "llama8b", f"llama8b_{fmt}_b{batch}")
+
+
+def build_int8(torch, qmv, wl):
+    sw = Sweep("qwen06b_int8_b1", 1)
+    dev = "cuda:0"
+    cfn = qmv.lib().qmv_i8_requant
+    mats = {}
+    for mname, N, K in wl.QWEN06B_LAYER + [wl.QWEN06B_LM_HEAD]:
+        W = torch.from_numpy(wl.int8_uniform(f"qwen/W/{mname}", (N, K))).to(dev)
+        mult, shift = wl.requant_params(f"qwen/ms/{mname}", N)
+        mats[mname] = (W, torch.from_numpy(mult).to(dev), torch.from_numpy(shift).to(dev))
+    for layer in range(wl.QWEN06B_LAYERS + 1):
+        mlist = wl.QWEN06B_LAYER if layer < wl.QWEN06B_LAYERS else [wl.QWEN06B_LM_HEAD]
+        for mname, N, K in mlist:
+            W0, mult, shift = mats[mname]
+            W = W0.clone() if layer < wl.QWEN06B_LAYERS else W0
+            x = torch.from_numpy(wl.int8_uniform(f"qwen/x/{layer}/{mname}", (1, K))).to(dev)
+            y = torch.empty((1, N), dtype=torch.int8, device=dev)
+            sw.keep += [W, x, y, mult, shift]
+            sw.add(mname, cfn, (W.data_ptr(), N, K, x.data_ptr(), K, 1, mult.data_ptr(), shift.data_ptr(),
+                                y.data_ptr(), N), N * K + K + 8 * N + N)
+    return sw
+
+
+def build_moe(torch, qmv, wl, batch):
+    """48 MoE layers: per layer one launch for gate||up (each expert's gate
+    and up rows concatenated, 1536 x 2048) and one for down (2048 x 768, one
+    input per token and slot).  Bytes count each distinct routed expert once."""
+    import numpy as np
+    sw = Sweep(f"moe30b_q4_0_b{batch}", batch)
+    dev = "cuda:0"
+    cfn = qmv.lib().qmv_moe
+    E, T, H, F = wl.MOE_EXPERTS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
+    t0 = time.time()
+    if "moe" not in _ENC_CACHE:
+        gate = wl.quant_weights("q4_0", "moe/gate", E * F, H).reshape(E, -1)
+        up = wl.quant_weights("q4_0", "moe/up", E * F, H).reshape(E, -1)
+        _ENC_CACHE["moe"] = (np.concatenate([gate, up], axis=1).reshape(-1),
+                             wl.quant_weights("q4_0", "moe/down", E * H, F).reshape(-1))
+    gu = torch.from_numpy(_ENC_CACHE["moe"][0]).to(dev)
+    down = torch.from_numpy(_ENC_CACHE["moe"][1]).to(dev)
+    log(f"[moe] experts ready in {time.time() - t0:.1f}s")
+    gu_stride = 2 * wl.block_bytes("q4_0", F, H)
+    dn_stride = wl.block_bytes("q4_0", H, F)
+    uniq = []
+    for layer in range(wl.MOE_LAYERS):
+        ids_np = wl.moe_ids(f"moe/ids/{layer}/{batch}", batch, T, E)
+        nu = len(np.unique(ids_np))
+        uniq.append(nu)
+        ids = torch.from_numpy(ids_np).to(dev)
+        Wgu, Wdn = gu.clone(), down.clone()
+        x = torch.from_numpy(wl.activations(f"moe/x/gu/{layer}/{batch}", batch, H)).to(dev)
+        ygu = torch.empty((batch, T, 2 * F), dtype=torch.float32, device=dev)
+        xd = torch.from_numpy(wl.activations(f"moe/x/dn/{layer}/{batch}", batch * T, F)).to(dev)
+        yd = torch.empty((batch, T, H), dtype=torch.float32, device=dev)
+        sw.keep += [ids, Wgu, Wdn, x, ygu, xd, yd]
+        sw.add("gate_up", cfn, (1, Wgu.data_ptr(), gu_stride, E, 2 * F, H, ids.data_ptr(), batch, T,
+                                x.data_ptr(), H, 0, ygu.data_ptr()),
+               nu * gu_stride + 4 * batch * H + 4 * batch * T * 2 * F + 4 * batch * T)
+        sw.add("down", cfn, (1, Wdn.data_ptr(), dn_stride, E, H, F, ids.data_ptr(), batch, T,
+                             xd.data_ptr(), T * F, F, yd.data_ptr()),
+               nu * dn_stride + 4 * batch * T * F + 4 * batch * T * H + 4 * batch * T)
+    sw.mean_unique = float(np.mean(uniq))
+    return sw
+
+
+# ---------------------------------------------------------------- timing
+def time_sweep(torch, sw, steps, warmup, use_graph=True):
+    """Returns dict with wall-clock and per-launch event timings."""
+    stream = torch.cuda.current_stream()
+    for _ in range(max(1, warmup)):
+        sw.run(stream.cuda_stream)
+    torch.cuda.synchronize()
+    graph = None
+    if use_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                sw.run(torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            for _ in range(2):
+                graph.replay()
+            torch.cuda.synchronize()
+        except Exception as e:  # capture unsupported: time eager launches
+            log(f"[{sw.name}] graph capture failed ({e}); timing eager launches")
+            graph = None
+    # timed region: K steps bracketed by synchronize
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            sw.run(stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # per-launch durations: HIP events between consecutive launches on the
+    # launch stream; the queue is pre-filled with graph replays so that the
+    # host stays ahead of the GPU.
+    n = len(sw.launches)
+    reps = max(1, min(steps, 5))
+    dur = [0.0] * n
+    for _ in range(reps):
+        if graph is not None:
+            for _ in range(3):
+                graph.replay()
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        s = ctypes.c_void_p(stream.cuda_stream)
+        evs[0].record(stream)
+        for i, (label, cfn, args, _) in enumerate(sw.launches):
+            rc = cfn(*args, s)
+            if rc != 0:
+                raise RuntimeError(f"{sw.name}/{label}: rc={rc}")
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        for i in range(n):
+            dur[i] += evs[i].elapsed_time(evs[i + 1]) / reps   # ms
+    by_label = {}
+    for (label, _, _, nb), d in zip(sw.launches, dur):
+        e = by_label.setdefault(label, {"launches": 0, "ms": 0.0, "bytes": 0})
+        e["launches"] += 1
+        e["ms"] += d
+        e["bytes"] += nb
+    kernel_ms = sum(dur)
+    ms_step = wall / steps * 1e3
+    bps = sw.bytes_per_step
+    out = {
+        "steps": steps, "graph": graph is not None,
+        "launches_per_step": n, "bytes_per_step": bps,
+        "ms_per_step": ms_step,
+        "gbs_wall": bps / (ms_step * 1e-3) / 1e9,
+        "kernel_ms_per_step": kernel_ms,
+        "gbs_kernel": bps / (kernel_ms * 1e-3) / 1e9,
+        "tok_s_wall": sw.batch / (ms_step * 1e-3),
+        "tok_s_kernel": sw.batch / (kernel_ms * 1e-3),
+        "per_matrix": {k: {"launches": v["launches"], "us_per_launch": v["ms"] / v["launches"] * 1e3,
+                           "gbs": v["bytes"] / (v["ms"] * 1e-3) / 1e9}
+                       for k, v in by_label.items()},
+    }
+    out["pct_peak_wall"] = 100 * out["gbs_wall"] / PEAK_GBS
+    out["pct_peak_kernel"] = 100 * out["gbs_kernel"] / PEAK_GBS
+    return out
+
+
+# ---------------------------------------------------------------- CPU baseline
+def cpu_baseline(wl):
+    """The oracle (single-threaded C, fp64 dequantize-then-dot) on a bounded
+    sample of the headline workload: one full 8B layer set (q, k, v, o,
+    gate, up, down) plus the first 16384 lm_head rows, Q8_0, batch 1."""
+    import numpy as np
+    import oracle
+    mats = wl.LLAMA8B_LAYER + [("lm_head", 16384, 4096)]
+    tot_bytes, tot_s = 0, 0.0
+    for mname, N, K in mats:
+        tag = f"llama8b/{mname}"
+        # the first N rows of the full lm_head draw (one sequential stream)
+        W = wl.quant_weights("q8_0", tag, N, K)
+        x = wl.activations(f"llama8b/x/0/{K}/1", 1, K)
+        t0 = time.perf_counter()
+        oracle.matvec("q8_0", np.ascontiguousarray(W), N, K, x)
+        tot_s += time.perf_counter() - t0
+        tot_bytes += W.size + 4 * K + 4 * N
+    gbs = tot_bytes / tot_s / 1e9
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    full_bytes = 7973699584
+    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one 8B layer set (q,k,v,o,gate,up,down) + lm_head rows 0..16383, Q8_0, batch 1: "
+                      f"{tot_bytes} bytes in {tot_s:.2f} s, single thread",
+            "host_cpus": os.cpu_count(), "cpu_model": model or platform.processor(),
+            "tok_s_equiv": 1.0 / (full_bytes / (gbs * 1e9))}
+
+
+# ---------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--sweeps", default="all",
+                    help="extra workloads: all, none, or a comma list of q4_0,q4_1,int8,moe")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the path runs on one MI355X's share; --gpus {args.gpus} "
+              "is not supported (multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import bandwidth_bound_block_amd as qmv
+    import workloads as wl
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    sw = build_llama(torch, qmv, wl, "q8_0", 1)
+    log(f"[{sw.name}] {len(sw.launches)} launches, {sw.bytes_per_step} bytes/step")
+    head = time_sweep(torch, sw, args.steps, args.warmup, not args.no_graph)
+    log(f"[{sw.name}] {head['ms_per_step']:.3f} ms/step wall, {head['gbs_wall']:.0f} GB/s wall, "
+        f"{head['gbs_kernel']:.0f} GB/s kernel")
+    del sw
+    torch.cuda.empty_cache()
+
+    extra = {}
+    names = [] if args.sweeps == "none" else (
+        ["q4_0", "q4_1", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
+    ksteps = max(5, min(args.steps, 20))
+    for nm in names:
+        if nm in ("q4_0", "q4_1"):
+            for B in (1, 2, 4, 8):
+                s = build_llama(torch, qmv, wl, nm, B)
+                r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+                extra[s.name] = {k: r[k] for k in ("ms_per_step", "gbs_wall", "gbs_kernel", "pct_peak_kernel",
+                                                  "tok_s_wall", "tok_s_kernel", "per_matrix")}
+                log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s kernel, "
+                    f"{r['tok_s_kernel']:.0f} tok/s (kernel)")
+                del s
+                torch.cuda.empty_cache()
+        elif nm == "int8":
+            s = build_int8(torch, qmv, wl)
+            r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+            extra[s.name] = {k: r[k] for k in ("ms_per_step", "gbs_wall", "gbs_kernel", "pct_peak_kernel",
+                                              "tok_s_wall", "tok_s_kernel", "per_matrix")}
+            log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s kernel")
+            del s
+            torch.cuda.empty_cache()
+        elif nm == "moe":
+            for B in (1, 2, 4, 8):
+                s = build_moe(torch, qmv, wl, B)
+                r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+                extra[s.name] = {k: r[k] for k in ("ms_per_step", "gbs_wall", "gbs_kernel", "pct_peak_kernel",
+                                                  "tok_s_wall", "tok_s_kernel", "per_matrix")}
+                extra[s.name]["mean_distinct_experts"] = s.mean_unique
+                log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s kernel, "
+                    f"|U|={s.mean_unique:.1f}")
+                del s
+                torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        t0 = time.time()
+        cpu = cpu_baseline(wl)
+        log(f"[cpu_baseline] {cpu['value']:.3f} GB/s in {time.time() - t0:.1f}s")
+
+    # Roofline of the dominant kernel: every launch of the headline step is
+    # the same kernel instantiation (Q8_0, batch 1, 64 lanes per row), so its
+    # achieved rate is the step's algorithmic bytes over the summed
+    # per-launch event durations.
+    roof = {"bound": "hbm", "achieved": head["gbs_kernel"], "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": head["gbs_kernel"] / PEAK_GBS, "traffic": None,
+            "kernel": "qmv_kernel<Q8_0, B=1, LPR=64, RPL=2>",
+            "us_per_launch": head["kernel_ms_per_step"] * 1e3 / head["launches_per_step"],
+            "bytes_per_launch": head["bytes_per_step"] / head["launches_per_step"]}
+    line = {
+        "metric": METRIC,
+        "value": head["gbs_wall"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama8b_q8_0_decode_sweep_b1", "format": "q8_0", "batch": 1,
+                   "layers": 32, "matvecs_per_step": head["launches_per_step"],
+                   "bytes_per_step": head["bytes_per_step"], "hip_graph": head["graph"]},
+        "pct_of_peak": head["pct_peak_wall"],
+        "tok_s_equiv": head["tok_s_wall"],
+        "kernel_time": {"gbs": head["gbs_kernel"], "pct_of_peak": head["pct_peak_kernel"],
+                        "tok_s_equiv": head["tok_s_kernel"], "ms_per_step": head["kernel_ms_per_step"],
+                        "per_matrix": head["per_matrix"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "sweeps": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
