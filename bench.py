@@ -31,6 +31,26 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_GBS = 8000.0
+
+# HBM traffic of the dominant kernel from rocprofv3 FETCH_SIZE + WRITE_SIZE
+# runs (copy-calibrated: FETCH x2.0, WRITE x1.0), per launch, recorded for
+# the kernel source with this SHA-256; reported as null once the source
+# differs (the kernel changed since the counters were taken).
+TRAFFIC_RECORD = {
+    "source": "bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
+    "sha256": "b63f2677e21f4f9992eed2a72c693897960efb17571f5144989ed37c8ab8f4f9",
+    "bytes_per_launch": 31237716,
+}
+
+
+def recorded_traffic():
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, TRAFFIC_RECORD["source"]), "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except OSError:
+        return None
+    return TRAFFIC_RECORD["bytes_per_launch"] if h == TRAFFIC_RECORD["sha256"] else None
 METRIC = "achieved HBM GB/s (% of MI355X peak) for batch-1 quant matvec; equiv. decode tok/s"
 
 
@@ -81,15 +101,36 @@ class Sweep:
                 raise RuntimeError(f"{self.name}/{label}: rc={rc}: {qmv.last_error()}")
 
 
-def _dense_sweep(torch, qmv, wl, fmt, batch, layers, layer_mats, head, tagbase, name):
+def _dense_sweep(torch, qmv, wl, fmt, batch, layers, layer_mats, head, tagbase, name, fuse=None):
+    """fuse: optional list of (fused_name, [member names]) whose rows are
+    stored concatenated (same input vector), e.g. q||k||v and gate||up."""
+    import numpy as np
     cfn = {"q8_0": qmv.lib().qmv_q8_0, "q4_0": qmv.lib().qmv_q4_0, "q4_1": qmv.lib().qmv_q4_1}[fmt]
     sw = Sweep(name, batch)
     dev = "cuda:0"
     t0 = time.time()
     mats = {}
+    enc = {m: encoded(wl, fmt, f"{tagbase}/{m}", N, K) for m, N, K in layer_mats + [head]}
+    shapes = {m: (N, K) for m, N, K in layer_mats}
+    if fuse:
+        merged = []
+        used = set()
+        for fname, members in fuse:
+            N = sum(shapes[m][0] for m in members)
+            K = shapes[members[0]][1]
+            enc[fname] = np.concatenate([enc[m] for m in members], axis=0)   # rows of an encoded matrix are independent
+            merged.append((fname, N, K))
+            used |= set(members)
+        layer_mats = []
+        for m, N, K in wl.LLAMA8B_LAYER if tagbase == "llama8b" else []:
+            if m not in used:
+                layer_mats.append((m, N, K))
+            else:
+                for fname, members in fuse:
+                    if members[0] == m:
+                        layer_mats.append([t for t in merged if t[0] == fname][0])
     for mname, N, K in layer_mats + [head]:
-        W = encoded(wl, fmt, f"{tagbase}/{mname}", N, K)
-        mats[mname] = torch.from_numpy(W).to(dev)
+        mats[mname] = torch.from_numpy(enc[mname]).to(dev)
     log(f"[{name}] encoded weights in {time.time() - t0:.1f}s")
     xs = {}
     for layer in range(layers + 1):
@@ -114,9 +155,13 @@ def _dense_sweep(torch, qmv, wl, fmt, batch, layers, layer_mats, head, tagbase, 
     return sw
 
 
-def build_llama(torch, qmv, wl, fmt, batch):
+FUSED_8B = [("qkv", ["q", "k", "v"]), ("gate_up", ["gate", "up"])]
+
+
+def build_llama(torch, qmv, wl, fmt, batch, fused=False):
     return _dense_sweep(torch, qmv, wl, fmt, batch, wl.LLAMA8B_LAYERS, wl.LLAMA8B_LAYER, wl.LLAMA8B_LM_HEAD,
-                        "llama8b", f"llama8b_{fmt}_b{batch}")
+                        "llama8b", f"llama8b_{fmt}{'_fused' if fused else ''}_b{batch}",
+                        FUSED_8B if fused else None)
 
 
 def build_int8(torch, qmv, wl):
@@ -185,7 +230,13 @@ def build_moe(torch, qmv, wl, batch):
 
 # ---------------------------------------------------------------- timing
 def time_sweep(torch, sw, steps, warmup, use_graph=True):
-    """Returns dict with wall-clock and per-launch event timings."""
+    """Wall clock and HIP-event timings of a sweep.
+
+    Timed region: `steps` replays of the step's HIP graph (or eager launches)
+    bracketed by synchronize, with events on the launch stream around them.
+    Per matrix: every launch of that matrix (the per-layer copies, so each is
+    cache-cold) back to back between two events on the launch stream, three
+    times; the per-launch average includes the gaps between launches."""
     stream = torch.cuda.current_stream()
     for _ in range(max(1, warmup)):
         sw.run(stream.cuda_stream)
@@ -203,58 +254,58 @@ def time_sweep(torch, sw, steps, warmup, use_graph=True):
         except Exception as e:  # capture unsupported: time eager launches
             log(f"[{sw.name}] graph capture failed ({e}); timing eager launches")
             graph = None
-    # timed region: K steps bracketed by synchronize
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record(stream)
     for _ in range(steps):
         if graph is not None:
             graph.replay()
         else:
             sw.run(stream.cuda_stream)
+    e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # per-launch durations: HIP events between consecutive launches on the
-    # launch stream; the queue is pre-filled with graph replays so that the
-    # host stays ahead of the GPU.
-    n = len(sw.launches)
-    reps = max(1, min(steps, 5))
-    dur = [0.0] * n
-    for _ in range(reps):
-        if graph is not None:
-            for _ in range(3):
-                graph.replay()
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
-        s = ctypes.c_void_p(stream.cuda_stream)
-        evs[0].record(stream)
-        for i, (label, cfn, args, _) in enumerate(sw.launches):
-            rc = cfn(*args, s)
-            if rc != 0:
-                raise RuntimeError(f"{sw.name}/{label}: rc={rc}")
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        for i in range(n):
-            dur[i] += evs[i].elapsed_time(evs[i + 1]) / reps   # ms
+    gpu_ms = e0.elapsed_time(e1) / steps
+
     by_label = {}
-    for (label, _, _, nb), d in zip(sw.launches, dur):
-        e = by_label.setdefault(label, {"launches": 0, "ms": 0.0, "bytes": 0})
-        e["launches"] += 1
-        e["ms"] += d
+    for label, cfn, args, nb in sw.launches:
+        e = by_label.setdefault(label, {"launches": [], "bytes": 0})
+        e["launches"].append((cfn, args))
         e["bytes"] += nb
-    kernel_ms = sum(dur)
+    s = ctypes.c_void_p(stream.cuda_stream)
+    per = {}
+    for label, e in by_label.items():
+        best = None
+        for _ in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for cfn, args in e["launches"]:
+                cfn(*args, s)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        n = len(e["launches"])
+        per[label] = {"launches": n, "us_per_launch": best / n * 1e3, "bytes_per_launch": e["bytes"] // n,
+                      "gbs": e["bytes"] / (best * 1e-3) / 1e9}
+    kernel_ms = sum(v["us_per_launch"] * v["launches"] for v in per.values()) / 1e3
     ms_step = wall / steps * 1e3
     bps = sw.bytes_per_step
     out = {
         "steps": steps, "graph": graph is not None,
-        "launches_per_step": n, "bytes_per_step": bps,
+        "launches_per_step": len(sw.launches), "bytes_per_step": bps,
         "ms_per_step": ms_step,
+        "gpu_ms_per_step": gpu_ms,
         "gbs_wall": bps / (ms_step * 1e-3) / 1e9,
+        "gbs_gpu": bps / (gpu_ms * 1e-3) / 1e9,
         "kernel_ms_per_step": kernel_ms,
         "gbs_kernel": bps / (kernel_ms * 1e-3) / 1e9,
         "tok_s_wall": sw.batch / (ms_step * 1e-3),
         "tok_s_kernel": sw.batch / (kernel_ms * 1e-3),
-        "per_matrix": {k: {"launches": v["launches"], "us_per_launch": v["ms"] / v["launches"] * 1e3,
-                           "gbs": v["bytes"] / (v["ms"] * 1e-3) / 1e9}
-                       for k, v in by_label.items()},
+        "per_matrix": per,
     }
     out["pct_peak_wall"] = 100 * out["gbs_wall"] / PEAK_GBS
     out["pct_peak_kernel"] = 100 * out["gbs_kernel"] / PEAK_GBS
@@ -263,23 +314,27 @@ def time_sweep(torch, sw, steps, warmup, use_graph=True):
 
 # ---------------------------------------------------------------- CPU baseline
 def cpu_baseline(wl):
-    """The oracle (single-threaded C, fp64 dequantize-then-dot) on a bounded
-    sample of the headline workload: one full 8B layer set (q, k, v, o,
-    gate, up, down) plus the first 16384 lm_head rows, Q8_0, batch 1."""
-    import numpy as np
+    """The oracle (single-threaded C, fp64 dequantize-then-dot) on one full
+    token of the headline workload: the 8B layer set's 7 matrices 32 times
+    over (the oracle's time does not depend on the values, so one layer's
+    weights stand for all 32) plus the full lm_head, Q8_0, batch 1."""
     import oracle
-    mats = wl.LLAMA8B_LAYER + [("lm_head", 16384, 4096)]
     tot_bytes, tot_s = 0, 0.0
-    for mname, N, K in mats:
-        tag = f"llama8b/{mname}"
-        # the first N rows of the full lm_head draw (one sequential stream)
-        W = wl.quant_weights("q8_0", tag, N, K)
+    for mname, N, K in wl.LLAMA8B_LAYER:
+        W = encoded(wl, "q8_0", f"llama8b/{mname}", N, K)
         x = wl.activations(f"llama8b/x/0/{K}/1", 1, K)
         t0 = time.perf_counter()
-        oracle.matvec("q8_0", np.ascontiguousarray(W), N, K, x)
+        for _ in range(wl.LLAMA8B_LAYERS):
+            oracle.matvec("q8_0", W, N, K, x)
         tot_s += time.perf_counter() - t0
-        tot_bytes += W.size + 4 * K + 4 * N
-    gbs = tot_bytes / tot_s / 1e9
+        tot_bytes += wl.LLAMA8B_LAYERS * (W.size + 4 * K + 4 * N)
+    mname, N, K = wl.LLAMA8B_LM_HEAD
+    W = encoded(wl, "q8_0", f"llama8b/{mname}", N, K)
+    x = wl.activations(f"llama8b/x/{wl.LLAMA8B_LAYERS}/{K}/1", 1, K)
+    t0 = time.perf_counter()
+    oracle.matvec("q8_0", W, N, K, x)
+    tot_s += time.perf_counter() - t0
+    tot_bytes += W.size + 4 * K + 4 * N
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -289,12 +344,11 @@ def cpu_baseline(wl):
                     break
     except OSError:
         pass
-    full_bytes = 7973699584
-    return {"value": gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one 8B layer set (q,k,v,o,gate,up,down) + lm_head rows 0..16383, Q8_0, batch 1: "
-                      f"{tot_bytes} bytes in {tot_s:.2f} s, single thread",
+    return {"value": tot_bytes / tot_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full batch-1 Q8_0 token: 225 matvecs (the layer set's 7 matrices x32 + lm_head), "
+                      f"{tot_bytes} bytes in {tot_s:.2f} s on one thread",
             "host_cpus": os.cpu_count(), "cpu_model": model or platform.processor(),
-            "tok_s_equiv": 1.0 / (full_bytes / (gbs * 1e9))}
+            "tok_s_equiv": 1.0 / tot_s}
 
 
 # ---------------------------------------------------------------- main
@@ -307,6 +361,8 @@ def main():
                     help="extra workloads: all, none, or a comma list of q4_0,q4_1,int8,moe")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (scale for HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the path runs on one MI355X's share; --gpus {args.gpus} "
@@ -321,46 +377,60 @@ def main():
         sys.exit(1)
     torch.cuda.set_device(0)
 
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
+        return
+
     sw = build_llama(torch, qmv, wl, "q8_0", 1)
     log(f"[{sw.name}] {len(sw.launches)} launches, {sw.bytes_per_step} bytes/step")
     head = time_sweep(torch, sw, args.steps, args.warmup, not args.no_graph)
     log(f"[{sw.name}] {head['ms_per_step']:.3f} ms/step wall, {head['gbs_wall']:.0f} GB/s wall, "
-        f"{head['gbs_kernel']:.0f} GB/s kernel")
+        f"{head['gbs_gpu']:.0f} GB/s events, {head['gbs_kernel']:.0f} GB/s per-matrix sum")
     del sw
     torch.cuda.empty_cache()
 
+    keys = ("ms_per_step", "gpu_ms_per_step", "gbs_wall", "gbs_gpu", "gbs_kernel", "pct_peak_wall",
+            "pct_peak_kernel", "tok_s_wall", "tok_s_kernel", "launches_per_step", "bytes_per_step", "per_matrix")
     extra = {}
+
+    def record(s, r):
+        extra[s.name] = {k: r[k] for k in keys}
+        log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s per-matrix sum, "
+            f"{r['tok_s_wall']:.0f} tok/s (wall)")
+
     names = [] if args.sweeps == "none" else (
-        ["q4_0", "q4_1", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
+        ["q8_0", "q4_0", "q4_1", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
-        if nm in ("q4_0", "q4_1"):
-            for B in (1, 2, 4, 8):
-                s = build_llama(torch, qmv, wl, nm, B)
-                r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
-                extra[s.name] = {k: r[k] for k in ("ms_per_step", "gbs_wall", "gbs_kernel", "pct_peak_kernel",
-                                                  "tok_s_wall", "tok_s_kernel", "per_matrix")}
-                log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s kernel, "
-                    f"{r['tok_s_kernel']:.0f} tok/s (kernel)")
+        if nm == "q8_0":
+            s = build_llama(torch, qmv, wl, "q8_0", 1, fused=True)
+            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+            del s
+            torch.cuda.empty_cache()
+        elif nm in ("q4_0", "q4_1"):
+            for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
+                s = build_llama(torch, qmv, wl, nm, B, fused=fused)
+                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
                 del s
                 torch.cuda.empty_cache()
         elif nm == "int8":
             s = build_int8(torch, qmv, wl)
-            r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
-            extra[s.name] = {k: r[k] for k in ("ms_per_step", "gbs_wall", "gbs_kernel", "pct_peak_kernel",
-                                              "tok_s_wall", "tok_s_kernel", "per_matrix")}
-            log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s kernel")
+            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
             del s
             torch.cuda.empty_cache()
         elif nm == "moe":
             for B in (1, 2, 4, 8):
                 s = build_moe(torch, qmv, wl, B)
                 r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
-                extra[s.name] = {k: r[k] for k in ("ms_per_step", "gbs_wall", "gbs_kernel", "pct_peak_kernel",
-                                                  "tok_s_wall", "tok_s_kernel", "per_matrix")}
+                record(s, r)
                 extra[s.name]["mean_distinct_experts"] = s.mean_unique
-                log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s kernel, "
-                    f"|U|={s.mean_unique:.1f}")
                 del s
                 torch.cuda.empty_cache()
 
@@ -370,15 +440,22 @@ def main():
         cpu = cpu_baseline(wl)
         log(f"[cpu_baseline] {cpu['value']:.3f} GB/s in {time.time() - t0:.1f}s")
 
-    # Roofline of the dominant kernel: every launch of the headline step is
-    # the same kernel instantiation (Q8_0, batch 1, 64 lanes per row), so its
-    # achieved rate is the step's algorithmic bytes over the summed
-    # per-launch event durations.
-    roof = {"bound": "hbm", "achieved": head["gbs_kernel"], "peak": PEAK_GBS, "unit": "GB/s",
-            "frac": head["gbs_kernel"] / PEAK_GBS, "traffic": None,
-            "kernel": "qmv_kernel<Q8_0, B=1, LPR=64, RPL=2>",
-            "us_per_launch": head["kernel_ms_per_step"] * 1e3 / head["launches_per_step"],
-            "bytes_per_launch": head["bytes_per_step"] / head["launches_per_step"]}
+    # Roofline of the dominant kernel.  Every K = 4096 launch of the step
+    # (q, k, v, o, gate, up, lm_head: 193 of 225) runs one instantiation,
+    # qmv_kernel<Q8_0, B=1, 64 lanes/row, 1 row/lane, XU=4, 4 waves>; down
+    # (K = 14336) runs the 8-wave one.  achieved = that kernel's algorithmic
+    # bytes over its summed per-launch event times.
+    dom = [k for k in ("q", "k", "v", "o", "gate", "up", "lm_head") if k in head["per_matrix"]]
+    pm = head["per_matrix"]
+    dom_bytes = sum(pm[k]["bytes_per_launch"] * pm[k]["launches"] for k in dom)
+    dom_us = sum(pm[k]["us_per_launch"] * pm[k]["launches"] for k in dom)
+    dom_n = sum(pm[k]["launches"] for k in dom)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(),
+            "kernel": "qmv_kernel<Q8_0, 1, 64, 1, 4, 4>",
+            "launches_per_step": dom_n, "us_per_launch": dom_us / dom_n,
+            "bytes_per_launch": dom_bytes / dom_n}
     line = {
         "metric": METRIC,
         "value": head["gbs_wall"],
@@ -397,6 +474,7 @@ def main():
                    "bytes_per_step": head["bytes_per_step"], "hip_graph": head["graph"]},
         "pct_of_peak": head["pct_peak_wall"],
         "tok_s_equiv": head["tok_s_wall"],
+        "gpu_time": {"gbs": head["gbs_gpu"], "ms_per_step": head["gpu_ms_per_step"]},
         "kernel_time": {"gbs": head["gbs_kernel"], "pct_of_peak": head["pct_peak_kernel"],
                         "tok_s_equiv": head["tok_s_kernel"], "ms_per_step": head["kernel_ms_per_step"],
                         "per_matrix": head["per_matrix"]},
