@@ -18,8 +18,8 @@ import ctypes
 import os
 
 __all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_i8_requant", "qmv_moe",
-           "qmv_dequant", "abi_version", "last_error", "library_path", "lib",
-           "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
+           "qmv_dequant", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
+           "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqmv.so")
@@ -28,6 +28,14 @@ Q8_0, Q4_0, Q4_1 = 0, 1, 2
 FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1}
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}
 _ERRORS = {1: "QMV_EINVAL", 2: "QMV_EALIGN", 3: "QMV_EUNSUPPORTED", 4: "QMV_EHIP"}
+CHAIN_WORKSPACE_BYTES = 40960
+
+
+class ChainStage(ctypes.Structure):
+    """qmv_chain_stage of include/qmv.h."""
+    _fields_ = [("W", ctypes.c_void_p), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p),
+                ("n_rows", ctypes.c_int64), ("n_cols", ctypes.c_int64),
+                ("wait", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class QmvError(RuntimeError):
@@ -56,6 +64,8 @@ def _open():
     L.qmv_moe.restype = i32
     L.qmv_dequant.argtypes = [ctypes.c_int, P, i64, i64, P, P]
     L.qmv_dequant.restype = i32
+    L.qmv_chain.argtypes = [ctypes.c_int, P, i32, P, ctypes.c_size_t, P]
+    L.qmv_chain.restype = i32
     L.qmv_last_error.argtypes = []
     L.qmv_last_error.restype = ctypes.c_char_p
     L.qmv_abi_version.argtypes = []
@@ -224,3 +234,30 @@ def qmv_dequant(fmt, W, n_rows, n_cols, out=None, stream=None):
         raise ValueError("out must be a contiguous [n_rows, n_cols] tensor")
     _check(_lib.qmv_dequant(fmt, W.data_ptr(), n_rows, n_cols, out.data_ptr(), _stream(stream)))
     return out
+
+
+def chain_stages(stages):
+    """[(W, n_rows, n_cols, x, y, wait), ...] of GPU tensors -> ctypes array."""
+    torch = _torch()
+    arr = (ChainStage * len(stages))()
+    for i, (W, n_rows, n_cols, x, y, wait) in enumerate(stages):
+        _dev(W, "W", torch.uint8)
+        _dev(x, "x", torch.float32)
+        _dev(y, "y", torch.float32)
+        if x.numel() < n_cols or y.numel() < n_rows or not x.is_contiguous() or not y.is_contiguous():
+            raise ValueError(f"stage {i}: x must hold n_cols and y n_rows contiguous floats")
+        arr[i] = ChainStage(W.data_ptr(), x.data_ptr(), y.data_ptr(), n_rows, n_cols, 1 if wait else 0, 0)
+    return arr
+
+
+def qmv_chain(fmt, stages, workspace, stream=None):
+    """Runs batch-1 matvec stages in one persistent launch (see qmv.h).
+
+    stages: list of (W, n_rows, n_cols, x, y, wait) with GPU tensors, or a
+    ctypes array from chain_stages().  workspace: uint8 GPU tensor of at
+    least CHAIN_WORKSPACE_BYTES, zero-filled before its first use."""
+    torch = _torch()
+    _dev(workspace, "workspace", torch.uint8)
+    arr = stages if isinstance(stages, ctypes.Array) else chain_stages(stages)
+    _check(_lib.qmv_chain(_fmt(fmt), ctypes.cast(arr, ctypes.c_void_p), len(arr), workspace.data_ptr(),
+                          workspace.numel(), _stream(stream)))

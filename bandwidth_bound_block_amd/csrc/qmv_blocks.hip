@@ -28,365 +28,10 @@
 //    reduces across its LPR lanes with cross-lane shuffles in a fixed order
 //    (deterministic, no atomics).
 //  * No MFMA: at batch 1..8 this is a GEMV, bound by HBM bandwidth.
-#include <hip/hip_runtime.h>
-#include <hip/hip_fp16.h>
-
-#include <algorithm>
-#include <cstdint>
-
-#include "qmv_host.h"
+#include "qmv_block_decode.h"
 
 namespace qmv {
 namespace {
-
-constexpr int kWaves = 4;               // waves per workgroup
-constexpr int kThreads = 64 * kWaves;   // workgroup size
-constexpr int kXPad = 36;               // floats per staged 32-block of x
-constexpr int kLdsMax = 160 * 1024;     // LDS per workgroup on gfx950
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
-
-// --------------------------------------------------------------- loads
-// p is 4-byte aligned; the hardware allows dword-aligned 16-byte loads.
-__device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_a4*>(p); }
-__device__ __forceinline__ uint32_t ld4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
-__device__ __forceinline__ uint32_t ld2(const uint8_t* p) { return *reinterpret_cast<const uint16_t*>(p); }
-
-__device__ __forceinline__ float half_bits_to_float(uint32_t h) {
-    return __half2float(__ushort_as_half(static_cast<unsigned short>(h & 0xffffu)));
-}
-
-// --------------------------------------------------------------- formats
-// Traits + decoder per format.  load() fetches block g (global block index,
-// row * blocks_per_row + column block) and leaves the scale(s) as floats and
-// the code bytes 4-byte aligned in c[]:
-//   Q8_0: c[0..7] = q_0..q_31 (int8, element 4i+k in byte k of c[i])
-//   Q4_0/Q4_1: c[0..3] = qs[0..15] (low nibble of byte k of c[i] is element
-//   4i+k, high nibble element 16+4i+k).
-//
-// fetch() only issues the loads into a Raw record; decode() turns the raw
-// registers into the scale(s) and aligned codes.  Keeping them apart lets a
-// wave have the next blocks in flight while it computes the current ones.
-struct Q8_0 {
-    static constexpr int kBytes = 34;
-    static constexpr bool kNeedSx = false;   // the block term needs no sum of x
-    struct Raw {
-        u32x4 a, b;
-        uint32_t u;
-        uint32_t sh;
-    };
-    // 34g = 2g (mod 4): even blocks start 4-aligned (read [o, o+32) and the
-    // last 2 code bytes), odd blocks start at 2 (mod 4) (read d alone, then
-    // the 32 codes from o+2, 4-aligned).  Exactly the block's 34 bytes.
-    __device__ static void fetch(const uint8_t* W, int64_t g, Raw& r) {
-        const int64_t o = 34 * g;
-        const bool even = (g & 1) == 0;
-        r.a = ld16(W + o + (even ? 0 : 2));
-        r.b = ld16(W + o + (even ? 16 : 18));
-        r.u = ld2(W + o + (even ? 32 : 0));
-        r.sh = even ? 2u : 0u;
-    }
-    __device__ static void decode(const Raw& r, float& d, float& m, uint32_t (&c)[8]) {
-        const uint32_t w[9] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w, r.u};
-#pragma unroll
-        for (int i = 0; i < 8; ++i) c[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r.sh);
-        d = half_bits_to_float(r.sh ? r.a.x : r.u);
-        m = 0.f;
-    }
-};
-
-struct Q4_0 {
-    static constexpr int kBytes = 18;
-    static constexpr bool kNeedSx = true;    // folds the -8 offset
-    struct Raw {
-        u32x4 a;
-        uint32_t u;
-        uint32_t sh;
-    };
-    __device__ static void fetch(const uint8_t* W, int64_t g, Raw& r) {
-        const int64_t o = 18 * g;
-        const bool even = (g & 1) == 0;    // 18g = 2g (mod 4)
-        r.a = ld16(W + o + (even ? 0 : 2));
-        r.u = ld2(W + o + (even ? 16 : 0));
-        r.sh = even ? 2u : 0u;
-    }
-    __device__ static void decode(const Raw& r, float& d, float& m, uint32_t (&c)[8]) {
-        const uint32_t w[5] = {r.a.x, r.a.y, r.a.z, r.a.w, r.u};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r.sh);
-        d = half_bits_to_float(r.sh ? r.a.x : r.u);
-        m = 0.f;
-    }
-};
-
-struct Q4_1 {
-    static constexpr int kBytes = 20;
-    static constexpr bool kNeedSx = true;    // folds the minimum m
-    struct Raw {
-        uint32_t dm;
-        u32x4 a;
-    };
-    __device__ static void fetch(const uint8_t* W, int64_t g, Raw& r) {
-        const int64_t o = 20 * g;          // always 4-aligned
-        r.dm = ld4(W + o);
-        r.a = ld16(W + o + 4);
-    }
-    __device__ static void decode(const Raw& r, float& d, float& m, uint32_t (&c)[8]) {
-        c[0] = r.a.x; c[1] = r.a.y; c[2] = r.a.z; c[3] = r.a.w;
-        d = half_bits_to_float(r.dm);
-        m = half_bits_to_float(r.dm >> 16);
-    }
-};
-
-// fetch + decode in one go (dequant kernel).
-template <class F>
-__device__ __forceinline__ void load_block(const uint8_t* W, int64_t g, float& d, float& m, uint32_t (&c)[8]) {
-    typename F::Raw r;
-    F::fetch(W, g, r);
-    F::decode(r, d, m, c);
-}
-
-__device__ __forceinline__ float sbyte(uint32_t w, int k) {
-    return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(w >> (8 * k))));
-}
-__device__ __forceinline__ float ubyte(uint32_t w, int k) {
-    return static_cast<float>((w >> (8 * k)) & 0xffu);
-}
-
-// Decoded element e of a block as float (the codes, before the scale).
-// Used by the dequant kernel; the matvec kernel inlines the same steps.
-template <class F>
-__device__ __forceinline__ void block_values(const float d, const float m, const uint32_t (&c)[8], float (&v)[32]);
-
-template <>
-__device__ __forceinline__ void block_values<Q8_0>(const float d, const float, const uint32_t (&c)[8], float (&v)[32]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) v[4 * i + k] = d * sbyte(c[i], k);
-}
-template <>
-__device__ __forceinline__ void block_values<Q4_0>(const float d, const float, const uint32_t (&c)[8], float (&v)[32]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = c[i] & 0x0f0f0f0fu, hi = (c[i] >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[4 * i + k] = d * (ubyte(lo, k) - 8.f);
-            v[16 + 4 * i + k] = d * (ubyte(hi, k) - 8.f);
-        }
-    }
-}
-template <>
-__device__ __forceinline__ void block_values<Q4_1>(const float d, const float m, const uint32_t (&c)[8], float (&v)[32]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = c[i] & 0x0f0f0f0fu, hi = (c[i] >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[4 * i + k] = __builtin_fmaf(d, ubyte(lo, k), m);
-            v[16 + 4 * i + k] = __builtin_fmaf(d, ubyte(hi, k), m);
-        }
-    }
-}
-
-// The block's 32 codes as floats in element order: Q8_0 the signed bytes,
-// Q4_0/Q4_1 the unsigned nibbles (offset and minimum are applied per block).
-template <class F>
-__device__ __forceinline__ void codes_to_float(const uint32_t (&c)[8], float (&q)[32]);
-
-template <>
-__device__ __forceinline__ void codes_to_float<Q8_0>(const uint32_t (&c)[8], float (&q)[32]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) q[4 * i + k] = sbyte(c[i], k);
-}
-__device__ __forceinline__ void nibbles_to_float(const uint32_t (&c)[8], float (&q)[32]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = c[i] & 0x0f0f0f0fu, hi = (c[i] >> 4) & 0x0f0f0f0fu;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            q[4 * i + k] = ubyte(lo, k);
-            q[16 + 4 * i + k] = ubyte(hi, k);
-        }
-    }
-}
-template <>
-__device__ __forceinline__ void codes_to_float<Q4_0>(const uint32_t (&c)[8], float (&q)[32]) { nibbles_to_float(c, q); }
-template <>
-__device__ __forceinline__ void codes_to_float<Q4_1>(const uint32_t (&c)[8], float (&q)[32]) { nibbles_to_float(c, q); }
-
-// s[b] = sum_{e<32} q[e] * x_b[e] for the first w of B columns (w is
-// wave-uniform: inactive columns are skipped by a scalar branch).  xs points
-// at the block's 32 staged floats of column 0; column b is xstride_b after.
-template <int B>
-__device__ __forceinline__ void dot_cols(const float (&q)[32], const float* __restrict__ xs, int xstride_b,
-                                         float (&s)[B], int w) {
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        if (b < w) {
-            const float* xp = xs + b * xstride_b;
-            float a = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float4 xv = *reinterpret_cast<const float4*>(xp + 4 * i);
-                a = __builtin_fmaf(q[4 * i + 0], xv.x, a);
-                a = __builtin_fmaf(q[4 * i + 1], xv.y, a);
-                a = __builtin_fmaf(q[4 * i + 2], xv.z, a);
-                a = __builtin_fmaf(q[4 * i + 3], xv.w, a);
-            }
-            s[b] = a;
-        }
-    }
-}
-
-// Adds a block's term to the running sum, from the code dot s and the block
-// sum sx of x.  Written with explicit fused multiply-adds so that every entry
-// point (dense, MoE, any batch width) rounds identically.
-template <class F> struct Term;
-template <> struct Term<Q8_0> {
-    __device__ static float add(float acc, float d, float, float s, float) { return __builtin_fmaf(d, s, acc); }
-};
-template <> struct Term<Q4_0> {
-    // sum_j d*(c_j - 8) x_j = d * (sum_j c_j x_j - 8 sum_j x_j)
-    __device__ static float add(float acc, float d, float, float s, float sx) {
-        return __builtin_fmaf(d, __builtin_fmaf(-8.f, sx, s), acc);
-    }
-};
-template <> struct Term<Q4_1> {
-    // sum_j (d*c_j + m) x_j = d * sum_j c_j x_j + m * sum_j x_j
-    __device__ static float add(float acc, float d, float m, float s, float sx) {
-        return __builtin_fmaf(d, s, __builtin_fmaf(m, sx, acc));
-    }
-};
-
-// Sum over the LPR consecutive lanes of a segment, in a fixed order; the
-// total is valid in the segment's first lane (for LPR <= 16 in every lane of
-// the segment).  Within 16-lane rows the sum uses DPP lane swizzles (a few
-// VALU cycles each): xor 1, xor 2, half-row mirror, row mirror.  Across rows
-// the row totals are read as scalars.
-template <int CTRL>
-__device__ __forceinline__ float dpp_mov(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane_val(float v, int l) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
-}
-template <int LPR>
-__device__ __forceinline__ float segment_sum(float v) {
-    static_assert(LPR == 8 || LPR == 16 || LPR == 32 || LPR == 64, "segment width");
-    v += dpp_mov<0xB1>(v);     // quad_perm [1,0,3,2]: pairs
-    v += dpp_mov<0x4E>(v);     // quad_perm [2,3,0,1]: quads
-    v += dpp_mov<0x141>(v);    // row_half_mirror: 8 lanes
-    if (LPR >= 16) v += dpp_mov<0x140>(v);   // row_mirror: 16 lanes
-    if (LPR == 32) {
-        const float a = lane_val(v, 0) + lane_val(v, 16);
-        const float b = lane_val(v, 32) + lane_val(v, 48);
-        v = (threadIdx.x & 32) ? b : a;
-    } else if (LPR == 64) {
-        v = (lane_val(v, 0) + lane_val(v, 16)) + (lane_val(v, 32) + lane_val(v, 48));
-    }
-    return v;
-}
-
-// Straight-line staging of one 16-byte-aligned activation column (batch 1):
-// every thread issues XU float4 loads (indices clamped, so the count is a
-// compile-time constant), and only later writes them to LDS.  With no loop
-// the compiler can keep other loads issued in between in flight while it
-// waits for these.
-template <int XU, int NT>
-struct XStage {
-    float4 v[XU];
-    __device__ __forceinline__ void load(const float* __restrict__ x, int K4) {
-        const float4* src = reinterpret_cast<const float4*>(x);
-#pragma unroll
-        for (int u = 0; u < XU; ++u) v[u] = src[min((int)threadIdx.x + u * NT, K4 - 1)];
-    }
-    // Indices past the end are clamped like the loads: such a thread
-    // writes the last chunk's own value to the last chunk's slot.
-    __device__ __forceinline__ void store(float* xs, int K4) const {
-#pragma unroll
-        for (int u = 0; u < XU; ++u) {
-            const int e = 4 * min((int)threadIdx.x + u * NT, K4 - 1);
-            *reinterpret_cast<float4*>(xs + (e >> 5) * kXPad + (e & 31)) = v[u];
-        }
-    }
-};
-
-// Per-block sums of the staged columns (formats that fold an offset).
-template <int NT>
-__device__ __forceinline__ void block_sums(const float* xs, float* sx, int count) {
-    for (int t = threadIdx.x; t < count; t += NT) {
-        const float4* p = reinterpret_cast<const float4*>(xs + t * kXPad);
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 v = p[i];
-            acc += v.x; acc += v.y; acc += v.z; acc += v.w;
-        }
-        sx[t] = acc;
-    }
-}
-
-// Stages the first w of the B activation columns xcol[b][0..32*nb) into
-// LDS as xs[b][block][36] and, when the format needs them, the per-block
-// sums into sx[b][block].  Loads are issued in batches of 4 per thread
-// before any is used, so the staging costs a few memory round trips, not
-// one per element.  vec: every column is 16-byte aligned (float4 loads).
-// Ends with a barrier.
-template <bool kNeedSx, int B, int NT>
-__device__ __forceinline__ void stage_x_cols(const float* const (&xcol)[B], int nb, float* xs, float* sx, int w,
-                                             bool vec) {
-    const int K = nb * 32;
-    const int tid = threadIdx.x;
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        if (b < w) {
-            float* dst = xs + b * nb * kXPad;
-            if (vec) {
-                const float4* src = reinterpret_cast<const float4*>(xcol[b]);
-                const int K4 = K >> 2;
-                auto put = [&](int c, const float4& v) {
-                    const int e = 4 * c;
-                    *reinterpret_cast<float4*>(dst + (e >> 5) * kXPad + (e & 31)) = v;
-                };
-                for (int c0 = tid; c0 < K4; c0 += 4 * NT) {
-                    const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
-                    const float4 v0 = src[c0];
-                    const float4 v1 = src[min(c1, K4 - 1)];
-                    const float4 v2 = src[min(c2, K4 - 1)];
-                    const float4 v3 = src[min(c3, K4 - 1)];
-                    put(c0, v0);
-                    if (c1 < K4) put(c1, v1);
-                    if (c2 < K4) put(c2, v2);
-                    if (c3 < K4) put(c3, v3);
-                }
-            } else {
-                const float* src = xcol[b];
-                auto put = [&](int e, float v) { dst[(e >> 5) * kXPad + (e & 31)] = v; };
-                for (int e0 = tid; e0 < K; e0 += 4 * NT) {
-                    const int e1 = e0 + NT, e2 = e0 + 2 * NT, e3 = e0 + 3 * NT;
-                    const float v0 = src[e0];
-                    const float v1 = src[min(e1, K - 1)];
-                    const float v2 = src[min(e2, K - 1)];
-                    const float v3 = src[min(e3, K - 1)];
-                    put(e0, v0);
-                    if (e1 < K) put(e1, v1);
-                    if (e2 < K) put(e2, v2);
-                    if (e3 < K) put(e3, v3);
-                }
-            }
-        }
-    }
-    __syncthreads();
-    if (kNeedSx) {
-        block_sums<NT>(xs, sx, w * nb);
-        __syncthreads();
-    }
-}
 
 // ------------------------------------------------------------------ kernels
 // Computes, for the rows row0 + r*G + seg (r < RPL) of an N-row matrix with
@@ -447,7 +92,7 @@ __device__ __forceinline__ void tile_rows(const uint8_t* __restrict__ W, int64_t
 // loaded while the current step is computed (two steps in flight per wave),
 // and the first step's loads are issued before the activation staging so
 // that both latencies overlap.
-template <class F, int B, int LPR, int RPL, int XU, int NW>
+template <class F, int B, int LPR, int RPL, int XU, int NW, int PD = 2>
 __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict__ W, int64_t N, int nb,
                                                        const float* __restrict__ x, int64_t ldx,
                                                        float* __restrict__ y, int64_t ldy, int xvec) {
@@ -531,19 +176,26 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
         if (++t == T) { t = 0; tile += wstride; }
     };
 
-    // Two register buffers used in turn: the loads of one step are in flight
-    // while the previous step is computed.  Loads are issued without
-    // branches (a wave past its last step re-reads its current blocks, which
-    // are in cache), so the compiler waits only for the buffer in use.
-    int64_t tileA = (int64_t)blockIdx.x * NW + wave;
-    int tA = 0;
-    Raw bufA[RPL], bufB[RPL];
+    // PD register buffers used in turn: while one step is computed the loads
+    // of the next PD-1 steps are in flight.  Loads are issued without
+    // branches (a wave past its last step re-reads its last blocks, which are
+    // in cache), so the compiler waits only for the buffer in use.
+    Raw buf[PD][RPL];
+    int64_t ltile = (int64_t)blockIdx.x * NW + wave;   // next step to load
+    int lt = 0;
+    int64_t ctile = ltile;                             // next step to compute
+    int ct = 0;
     const int K4 = nb * 8;
+    auto load_next = [&](Raw (&b)[RPL]) {
+        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, b);
+        if (ltile < ntiles) advance(ltile, lt);
+    };
     if (XU > 0 && xvec) {
         // batch 1: x loads, then the first weight loads, then x into LDS
         XStage<XU, 64 * NW> xst;
         xst.load(x, K4);
-        load_step(min(tileA, ntiles - 1), tA, bufA);
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
         __builtin_amdgcn_sched_barrier(0);   // keep both batches of loads issued first
         xst.store(xs, K4);
         __syncthreads();
@@ -556,29 +208,30 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 #pragma unroll
         for (int b = 0; b < B; ++b) xcol[b] = x + b * ldx;
         stage_x_cols<F::kNeedSx, B, 64 * NW>(xcol, nb, xs, sx, B, xvec != 0);
-        load_step(min(tileA, ntiles - 1), tA, bufA);
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
 
-    if (tileA < ntiles) {
+    // One pipeline step: load a step PD-1 ahead into the buffer freed last,
+    // then compute buffer P.  Exits the loop after the wave's last step.
+#define QMV_PIPE_STEP(P)                                                   \
+    {                                                                      \
+        load_next(buf[((P) + PD - 1) % PD]);                               \
+        __builtin_amdgcn_sched_barrier(0); /* loads before using buf[P] */ \
+        compute_step(ctile, ct, buf[(P)]);                                 \
+        advance(ctile, ct);                                                \
+        if (ctile >= ntiles) break;                                        \
+    }
+    static_assert(PD >= 2 && PD <= 4, "pipeline depth");
+    if (ctile < ntiles) {
         while (true) {
-            int64_t tileB = tileA;
-            int tB = tA;
-            advance(tileB, tB);
-            const bool hasB = tileB < ntiles;
-            load_step(hasB ? tileB : tileA, hasB ? tB : tA, bufB);
-            __builtin_amdgcn_sched_barrier(0);   // issue B's loads before using A
-            compute_step(tileA, tA, bufA);
-            if (!hasB) break;
-            tileA = tileB;
-            tA = tB;
-            advance(tileA, tA);
-            const bool hasA = tileA < ntiles;
-            load_step(hasA ? tileA : tileB, hasA ? tA : tB, bufA);
-            __builtin_amdgcn_sched_barrier(0);   // issue A's loads before using B
-            compute_step(tileB, tB, bufB);
-            if (!hasA) break;
+            QMV_PIPE_STEP(0)
+            QMV_PIPE_STEP(1)
+            if constexpr (PD >= 3) QMV_PIPE_STEP(2)
+            if constexpr (PD >= 4) QMV_PIPE_STEP(3)
         }
     }
+#undef QMV_PIPE_STEP
 }
 
 // Grouped MoE expert matvec.  blockIdx.y = u selects the u-th distinct

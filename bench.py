@@ -164,6 +164,33 @@ def build_llama(torch, qmv, wl, fmt, batch, fused=False):
                         FUSED_8B if fused else None)
 
 
+# Stages that read outputs of earlier stages in a decode step (the others
+# share their input with the stage before them).
+DECODE_WAITS = {"q": 1, "k": 0, "v": 0, "qkv": 1, "o": 1, "gate": 1, "up": 0, "gate_up": 1, "down": 1,
+                "lm_head": 1}
+
+
+def build_llama_chain(torch, qmv, wl, fmt, fused=False):
+    """The batch-1 8B decode step as one qmv_chain call: the same matrices,
+    buffers and order as build_llama, with a stage barrier wherever a decode
+    step has a data dependency (q/qkv, o, gate/gate_up, down, lm_head)."""
+    dense = build_llama(torch, qmv, wl, fmt, 1, fused=fused)
+    sw = Sweep(dense.name.replace("_b1", "_chain_b1"), 1)
+    sw.keep = dense.keep
+    arr = (qmv.ChainStage * len(dense.launches))()
+    total = 0
+    for i, (label, _, args, nb) in enumerate(dense.launches):
+        Wp, N, K, xp, _, _, yp, _ = args
+        arr[i] = qmv.ChainStage(Wp, xp, yp, N, K, DECODE_WAITS[label], 0)
+        total += nb
+    ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    sw.keep += [arr, ws]
+    sw.add("chain", qmv.lib().qmv_chain,
+           (qmv.FORMATS[fmt], ctypes.cast(arr, ctypes.c_void_p), len(arr), ws.data_ptr(), ws.numel()), total)
+    sw.workspace = ws
+    return sw
+
+
 def build_int8(torch, qmv, wl):
     sw = Sweep("qwen06b_int8_b1", 1)
     dev = "cuda:0"
@@ -414,6 +441,12 @@ def main():
             record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
             del s
             torch.cuda.empty_cache()
+            for fused in (False, True):
+                s = build_llama_chain(torch, qmv, wl, "q8_0", fused=fused)
+                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+                extra[s.name]["barrier_error_flag"] = int(s.workspace.view(torch.int32)[2].item())
+                del s
+                torch.cuda.empty_cache()
         elif nm in ("q4_0", "q4_1"):
             for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
                 s = build_llama(torch, qmv, wl, nm, B, fused=fused)

@@ -152,6 +152,46 @@ int32_t qmv_moe(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                 float* y, void* stream);
 
 /*
+ * A chain of batch-1 float matvecs in one persistent launch.  Decode is a
+ * sequence of matvecs, each streaming its weights once ("Economical Serving
+ * and the hanzo.ai Platform", Sec. 2.1); at batch 1 most of them take a few
+ * microseconds, about as long as a kernel launch.  Stage s computes
+ *   stages[s].y[i] = sum_j DEQ(stages[s].W)[i][j] * stages[s].x[j]
+ * for i < n_rows, in format fmt, exactly as the batch-1 entry point of that
+ * format (bitwise the same result when n_cols >= 2048; within the accuracy
+ * bound otherwise).  A stage with wait != 0 may read outputs of earlier
+ * stages of the same call: it starts reading x only after every earlier
+ * stage is complete and its outputs are visible.  A stage with wait == 0
+ * may read only outputs that were already visible to the last earlier
+ * stage with wait != 0 (e.g. it shares that stage's input), not outputs
+ * of stages after it.  Weight loads of a stage may begin before earlier
+ * stages finish.
+ *   stages        host array of n_stages entries (copied into the launch).
+ *   n_rows        1..2^30;  n_cols a multiple of 32 in 32..35424.
+ *   W, x, y       device pointers, 4-byte aligned, as for qmv_q8_0.
+ *   workspace     device memory of >= QMV_CHAIN_WORKSPACE_BYTES, 4-byte
+ *                 aligned, zero-filled once before its first use; the
+ *                 library leaves it ready for the next call.  Calls that
+ *                 share a workspace must not run concurrently.  Word 2 is
+ *                 an error flag: nonzero means a stage barrier timed out
+ *                 (outputs undefined; zero the workspace again).
+ * Errors: QMV_EINVAL, QMV_EALIGN, QMV_EUNSUPPORTED (unknown fmt), QMV_EHIP.
+ */
+#define QMV_CHAIN_WORKSPACE_BYTES 40960
+typedef struct {
+    const void* W;
+    const float* x;
+    float* y;
+    int64_t n_rows;
+    int64_t n_cols;
+    int32_t wait;
+    int32_t reserved;
+} qmv_chain_stage;
+
+int32_t qmv_chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/*
  * Dequantize a whole matrix to fp32: out[i][j] = DEQ(W)[i][j], exactly (every
  * Q8_0/Q4_0 value and every Q4_1 value d*c + m whose bits span <= 24 is
  * representable in fp32; otherwise it is rounded to nearest even).  A test

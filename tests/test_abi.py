@@ -29,10 +29,16 @@ def qmv():
 def test_every_declared_symbol_is_exported(qmv):
     names = declared_functions()
     assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_i8_requant", "qmv_moe", "qmv_dequant",
-            "qmv_last_error", "qmv_abi_version"} <= set(names)
+            "qmv_chain", "qmv_last_error", "qmv_abi_version"} <= set(names)
     raw = ctypes.CDLL(qmv.library_path())
     for n in names:
         assert hasattr(raw, n), n
+
+
+def test_header_constants_match_binding(qmv):
+    src = open(HEADER).read()
+    m = re.search(r"#define\s+QMV_CHAIN_WORKSPACE_BYTES\s+(\d+)", src)
+    assert m and int(m.group(1)) == qmv.CHAIN_WORKSPACE_BYTES
 
 
 def test_abi_version(qmv):
@@ -123,3 +129,25 @@ def test_python_binding_rejects_cpu_tensors(qmv):
     x = torch.zeros(64, dtype=torch.float32)
     with pytest.raises(ValueError):
         qmv.qmv_q8_0(W, 1, 64, x)
+
+
+def test_chain_argument_errors(qmv):
+    import ctypes
+    f = qmv.lib().qmv_chain
+
+    def call(stages, ws=A, ws_bytes=qmv.CHAIN_WORKSPACE_BYTES, fmt=0):
+        arr = (qmv.ChainStage * len(stages))(*stages)
+        return f(fmt, ctypes.cast(arr, ctypes.c_void_p), len(stages), ws, ws_bytes, None)
+
+    good = qmv.ChainStage(A, A, A, 16, 4096, 0, 0)
+    assert call([good], fmt=9) == EUNSUPPORTED
+    assert call([good], ws=0) == EINVAL
+    assert call([good], ws_bytes=qmv.CHAIN_WORKSPACE_BYTES - 4) == EINVAL and "workspace" in qmv.last_error()
+    assert call([good], ws=A + 2) == EALIGN
+    assert call([qmv.ChainStage(A, A, A, 0, 4096, 0, 0)]) == EINVAL
+    assert call([good, qmv.ChainStage(A, A, A, 16, 4100, 1, 0)]) == EINVAL and "stage 1" in qmv.last_error()
+    assert call([qmv.ChainStage(A, A, A, 16, 65536, 0, 0)]) == EINVAL
+    assert call([qmv.ChainStage(A, A + 2, A, 16, 4096, 0, 0)]) == EALIGN
+    assert f(0, None, 1, A, qmv.CHAIN_WORKSPACE_BYTES, None) == EINVAL
+    arr = (qmv.ChainStage * 1)(good)
+    assert f(0, ctypes.cast(arr, ctypes.c_void_p), 0, A, qmv.CHAIN_WORKSPACE_BYTES, None) == EINVAL

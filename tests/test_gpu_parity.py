@@ -364,3 +364,104 @@ def test_moe_formats_and_invalid_ids(env, fmt):
     ids_ok = np.where(valid, ids, 0).astype(np.int32)
     yr, S = oracle.moe(fmt, Wall, per, E, N, K, ids_ok, x)
     assert_tol(y[valid], yr[valid], S[valid], fmt)
+
+
+# ------------------------------------------------------------------ chain
+def _chain_fn(qmv, fmt):
+    return {"q8_0": qmv.qmv_q8_0, "q4_0": qmv.qmv_q4_0, "q4_1": qmv.qmv_q4_1}[fmt]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_chain_independent_stages(env, fmt):
+    """Stages that do not wait: each equals the batch-1 entry point bitwise
+    (>= 64 blocks per row) or the oracle within the bound (shorter rows)."""
+    torch, qmv = env
+    shapes = [(300, 4096), (1024, 2048), (77, 14336), (130, 1024), (40, 768), (2000, 4096)]
+    ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    stages, keep = [], []
+    for i, (N, K) in enumerate(shapes):
+        W = wl.quant_weights(fmt, f"t/chain/{N}x{K}", N, K)
+        x = wl.activations(f"t/chain/x/{i}", 1, K)
+        Wd, xd = dev(torch, W), dev(torch, x)
+        yd = torch.full((N,), float("nan"), device="cuda:0")
+        stages.append((Wd, N, K, xd[0], yd, 0))
+        keep.append((W, x, N, K))
+    qmv.qmv_chain(fmt, stages, ws)
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[2].item()) == 0
+    for (Wd, N, K, xd, yd, _), (W, x, _, _) in zip(stages, keep):
+        y = yd.cpu().numpy()
+        if K >= 2048:
+            ref = _chain_fn(qmv, fmt)(Wd, N, K, xd)
+            torch.cuda.synchronize()
+            assert np.array_equal(y.view(np.uint32), ref.cpu().numpy()[0].view(np.uint32)), (N, K)
+        yr, S = oracle.matvec(fmt, W, N, K, x)
+        assert_tol(y[None], yr, S, (fmt, N, K))
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_1"])
+def test_chain_dependent_stages(env, fmt):
+    """x of stage s+1 is y of stage s (square 2048 x 2048 layers, more stages
+    than one launch holds): equals sequential batch-1 calls bitwise, and the
+    workspace stays consistent over repeated calls."""
+    torch, qmv = env
+    N = K = 2048
+    n_stages = 70
+    Ws = [dev(torch, wl.quant_weights(fmt, f"t/chain/dep/{i % 5}", N, K)) for i in range(n_stages)]
+    x0 = dev(torch, wl.activations("t/chain/dep/x", 1, K))[0]
+    ys = [torch.empty(N, device="cuda:0") for _ in range(n_stages)]
+    stages = [(Ws[i], N, K, x0 if i == 0 else ys[i - 1], ys[i], 1) for i in range(n_stages)]
+    ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    ref = []
+    cur = x0
+    for i in range(n_stages):
+        cur = _chain_fn(qmv, fmt)(Ws[i], N, K, cur)[0]
+        ref.append(cur)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for y in ys:
+            y.fill_(float("nan"))
+        qmv.qmv_chain(fmt, stages, ws)
+        torch.cuda.synchronize()
+        assert int(ws.view(torch.int32)[2].item()) == 0
+        for i in range(n_stages):
+            assert torch.equal(ys[i].view(torch.int32), ref[i].view(torch.int32)), (rep, i)
+    last = ref[-1].cpu().numpy()
+    assert np.isfinite(last).all() and np.abs(last).max() > 1e-3   # the chain did not decay or blow up
+
+
+@pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
+def test_chain_decode_pattern(env, fmt):
+    """Decode-shaped dependencies over 12 layers (72 stages, two launches):
+    q and k read the layer input, o reads q, gate and up read o, down reads
+    up and is the next layer's input.  k and up do not wait: they read an
+    output of the chain that the barrier of the stage before them (q, gate)
+    already made visible.  Every output equals the sequential batch-1 calls
+    bitwise."""
+    torch, qmv = env
+    H, F = 2048, 5632
+    mats = {"q": (H, H), "k": (512, H), "o": (H, H), "gate": (F, H), "up": (F, H), "down": (H, F)}
+    Wd = {(m, v): dev(torch, wl.quant_weights(fmt, f"t/chain/dec/{m}/{v}", N, K))
+          for m, (N, K) in mats.items() for v in range(2)}
+    h0 = dev(torch, wl.activations("t/chain/dec/h", 1, H))[0]
+    stages, outs = [], []
+    h = h0
+    for layer in range(12):
+        y = {m: torch.full((N,), float("nan"), device="cuda:0") for m, (N, _) in mats.items()}
+        W = {m: Wd[(m, layer % 2)] for m in mats}
+        stages += [(W["q"], H, H, h, y["q"], 1), (W["k"], 512, H, h, y["k"], 0),
+                   (W["o"], H, H, y["q"], y["o"], 1), (W["gate"], F, H, y["o"], y["gate"], 1),
+                   (W["up"], F, H, y["o"], y["up"], 0), (W["down"], H, F, y["up"], y["down"], 1)]
+        outs.append(y)
+        h = y["down"]
+    ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    qmv.qmv_chain(fmt, stages, ws)
+    torch.cuda.synchronize()
+    assert int(ws.view(torch.int32)[2].item()) == 0
+    f = _chain_fn(qmv, fmt)
+    for i, (W, N, K, x, y, _) in enumerate(stages):
+        ref = f(W, N, K, x)[0]        # x as the chain computed it: checks each stage on its own input
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), i
+    last = outs[-1]["down"].cpu().numpy()
+    assert np.isfinite(last).all() and np.abs(last).max() > 1e-3
