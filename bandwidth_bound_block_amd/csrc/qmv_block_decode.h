@@ -69,6 +69,17 @@ struct Q8_0 {
         d = half_bits_to_float(r.sh ? r.a.x : r.u);
         m = 0.f;
     }
+    // Block l of a step of 64 blocks copied to LDS at s (16-byte aligned):
+    // the same registers fetch() leaves for a block of the same parity.
+    __device__ static void from_lds(const uint8_t* s, int l, Raw& r) {
+        const int o = 34 * l;
+        const bool even = (l & 1) == 0;
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(s + o + (even ? 0 : 2));
+        r.a = u32x4{a[0], a[1], a[2], a[3]};
+        r.b = u32x4{a[4], a[5], a[6], a[7]};
+        r.u = *reinterpret_cast<const uint32_t*>(s + (even ? o + 32 : o - 2)) >> (even ? 0 : 16);
+        r.sh = even ? 2u : 0u;
+    }
 };
 
 struct Q4_0 {
@@ -93,6 +104,14 @@ struct Q4_0 {
         d = half_bits_to_float(r.sh ? r.a.x : r.u);
         m = 0.f;
     }
+    __device__ static void from_lds(const uint8_t* s, int l, Raw& r) {
+        const int o = 18 * l;
+        const bool even = (l & 1) == 0;
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(s + o + (even ? 0 : 2));
+        r.a = u32x4{a[0], a[1], a[2], a[3]};
+        r.u = *reinterpret_cast<const uint32_t*>(s + (even ? o + 16 : o - 2)) >> (even ? 0 : 16);
+        r.sh = even ? 2u : 0u;
+    }
 };
 
 struct Q4_1 {
@@ -111,6 +130,42 @@ struct Q4_1 {
         c[0] = r.a.x; c[1] = r.a.y; c[2] = r.a.z; c[3] = r.a.w;
         d = half_bits_to_float(r.dm);
         m = half_bits_to_float(r.dm >> 16);
+    }
+    __device__ static void from_lds(const uint8_t* s, int l, Raw& r) {
+        const uint32_t* a = reinterpret_cast<const uint32_t*>(s + 20 * l);
+        r.dm = a[0];
+        r.a = u32x4{a[1], a[2], a[3], a[4]};
+    }
+};
+
+// A step of 64 consecutive blocks read as whole 16-byte chunks: lane l
+// loads chunks l, 64 + l, ... (lanes past the last chunk re-read it, so
+// every load is in bounds and branch-free).  Each load instruction covers
+// whole cache lines, which lets the weights stream with non-temporal loads.
+template <class F>
+struct Contig {
+    static constexpr int kStepBytes = 64 * F::kBytes;        // 2176 / 1152 / 1280
+    static constexpr int kChunks = kStepBytes / 16;          // 136 / 72 / 80
+    static constexpr int kLoads = (kChunks + 63) / 64;       // 3 / 2 / 2
+    static_assert(kStepBytes % 16 == 0, "whole chunks");
+    struct Chunks {
+        u32x4 v[kLoads];
+    };
+    // step points at the step's first byte, 16-byte aligned
+    __device__ static void fetch(const uint8_t* step, int lane, Chunks& c) {
+        const u32x4* p = reinterpret_cast<const u32x4*>(step);
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) c.v[k] = __builtin_nontemporal_load(p + min(64 * k + lane, kChunks - 1));
+    }
+    // Copies the chunks to the wave's LDS scratch (kStepBytes, 16-byte aligned)
+    // and reads block `lane` back.  LDS operations of one wave complete in
+    // order, so the next step's copy cannot overtake these reads.
+    __device__ static void to_block(const Chunks& c, uint8_t* scratch, int lane, typename F::Raw& r) {
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k)
+            if (64 * k + 64 <= kChunks || 64 * k + lane < kChunks)
+                *reinterpret_cast<u32x4*>(scratch + 16 * (64 * k + lane)) = c.v[k];
+        F::from_lds(scratch, lane, r);
     }
 };
 

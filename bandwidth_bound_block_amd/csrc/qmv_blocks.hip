@@ -234,6 +234,99 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 #undef QMV_PIPE_STEP
 }
 
+// Batch 1, rows of whole 64-block steps (nb % 64 == 0), W 16-byte aligned:
+// the same lane-to-block mapping, arithmetic and reduction order as
+// qmv_kernel<F, 1, 64, 1, ...> (bitwise the same y), but each step's 64
+// blocks arrive as whole 16-byte chunks with non-temporal loads and are
+// re-read block-aligned from a per-wave LDS scratch.  One row per wave at
+// a time; rows are taken wave, wave + grid waves, ...
+template <class F, int XU, int NW, int PD = 2>
+__global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const uint8_t* __restrict__ W, int64_t N, int nb,
+                                                         const float* __restrict__ x, float* __restrict__ y) {
+    using C = Contig<F>;
+    extern __shared__ float lds[];
+    float* xs = lds;
+    float* sx = lds + nb * kXPad;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint8_t* scratch = reinterpret_cast<uint8_t*>(lds + nb * (kXPad + (F::kNeedSx ? 1 : 0))) + wave * C::kStepBytes;
+    const int T = nb / 64;
+    const int64_t wstride = (int64_t)gridDim.x * NW;
+
+    typename C::Chunks buf[PD];
+    int64_t lrow = (int64_t)blockIdx.x * NW + wave;   // next step to load
+    int lt = 0;
+    int64_t crow = lrow;                              // next step to compute
+    int ct = 0;
+    auto advance = [&](int64_t& row, int& t) {
+        if (++t == T) { t = 0; row += wstride; }
+    };
+    auto load_next = [&](typename C::Chunks& c) {
+        const int64_t row = min(lrow, N - 1);          // past the end: re-read a loaded step
+        const int t = lrow < N ? lt : 0;
+        C::fetch(W + (row * nb + 64 * t) * F::kBytes, lane, c);
+        if (lrow < N) advance(lrow, lt);
+    };
+    float acc = 0.f;
+    auto compute_step = [&](int t, const typename C::Chunks& c) {
+        typename F::Raw r;
+        C::to_block(c, scratch, lane, r);
+        const int j = lane + 64 * t;
+        float d, m;
+        uint32_t cd[8];
+        F::decode(r, d, m, cd);
+        float q[32];
+        codes_to_float<F>(cd, q);
+        float sdot[1] = {0.f};
+        dot_cols<1>(q, xs + j * kXPad, nb * kXPad, sdot, 1);
+        acc = Term<F>::add(acc, d, m, sdot[0], F::kNeedSx ? sx[j] : 0.f);
+        if (t == T - 1) {
+            const float tot = segment_sum<64>(acc);
+            if (lane == 0) y[crow] = tot;
+            acc = 0.f;
+        }
+    };
+
+    const int K4 = nb * 8;
+    if (XU > 0) {
+        XStage<XU, 64 * NW> xst;
+        xst.load(x, K4);
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
+        __builtin_amdgcn_sched_barrier(0);
+        xst.store(xs, K4);
+        __syncthreads();
+        if (F::kNeedSx) {
+            block_sums<64 * NW>(xs, sx, nb);
+            __syncthreads();
+        }
+    } else {
+        const float* xcol[1] = {x};
+        stage_x_cols<F::kNeedSx, 1, 64 * NW>(xcol, nb, xs, sx, 1, true);
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
+    }
+
+#define QMV_PIPE_STEP(P)                                   \
+    {                                                      \
+        load_next(buf[((P) + PD - 1) % PD]);               \
+        __builtin_amdgcn_sched_barrier(0);                 \
+        compute_step(ct, buf[(P)]);                        \
+        advance(crow, ct);                                 \
+        if (crow >= N) break;                              \
+    }
+    static_assert(PD >= 2 && PD <= 4, "pipeline depth");
+    if (crow < N) {
+        while (true) {
+            QMV_PIPE_STEP(0)
+            QMV_PIPE_STEP(1)
+            if constexpr (PD >= 3) QMV_PIPE_STEP(2)
+            if constexpr (PD >= 4) QMV_PIPE_STEP(3)
+        }
+    }
+#undef QMV_PIPE_STEP
+}
+
 // Grouped MoE expert matvec.  blockIdx.y = u selects the u-th distinct
 // expert id in first-occurrence order of ids[0..P); the workgroup streams
 // rows [blockIdx.x*ROWS_WG, +ROWS_WG) of that expert once per group of up
@@ -397,6 +490,61 @@ int32_t launch_lpr(const uint8_t* W, int64_t N, int nb, const float* x, int64_t 
     return launch_b<F, B, 8, XU, NW>(W, N, nb, x, ldx, y, ldy, st);
 }
 
+template <class F, int XU, int NW>
+int32_t launch_c(const uint8_t* W, int64_t N, int nb, const float* x, float* y, hipStream_t st) {
+    auto kern = qmv_kernel_c<F, XU, NW>;
+    const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float) + NW * Contig<F>::kStepBytes;
+    static bool attr_set = false;   // benign race: every thread sets the same value
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kLdsMax) != hipSuccess)
+            return fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
+        attr_set = true;
+    }
+    const int64_t tiles = (N + NW - 1) / NW;
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nb, x, y);
+    return check_launch("qmv");
+}
+
+// XU 16-byte activation loads per thread stage K4 = K / 4 chunks with a
+// workgroup of NW waves; past 8 per thread the staging loops instead.
+template <class F, int NW>
+int32_t launch_c_xu(const uint8_t* W, int64_t N, int nb, const float* x, float* y, hipStream_t st) {
+    const int per = (nb * 8 + 64 * NW - 1) / (64 * NW);
+    if (per <= 1) return launch_c<F, 1, NW>(W, N, nb, x, y, st);
+    if (per <= 2) return launch_c<F, 2, NW>(W, N, nb, x, y, st);
+    if (per <= 4) return launch_c<F, 4, NW>(W, N, nb, x, y, st);
+    if (per <= 8) return launch_c<F, 8, NW>(W, N, nb, x, y, st);
+    return launch_c<F, 0, NW>(W, N, nb, x, y, st);
+}
+
+// Batch 1 with whole 64-block steps and 16-byte aligned W and x: the
+// contiguous-chunk kernel where it streams faster than per-block loads
+// (measured on the 8B decode shapes, cache-cold):
+//   Q8_0: matrices of >= 8192 rows or >= 256 blocks per row;
+//   Q4_0/Q4_1 (closer to the VALU bound, where the LDS copy costs more):
+//   2048..32768 rows, or >= 256 blocks per row.
+// 16 waves per workgroup for long rows (one activation copy per CU) and
+// for Q4 matrices of <= 4096 rows, else 8; fewer if the LDS does not fit.
+template <class F>
+bool try_launch_c(const uint8_t* W, int64_t N, int nb, const float* x, float* y, hipStream_t st, int32_t* rc) {
+    if (nb % 64 || !aligned(W, 16) || !aligned(x, 16)) return false;
+    const bool q8 = !F::kNeedSx;
+    const bool long_rows = nb >= 256;
+    if (q8 ? !(N >= 8192 || long_rows) : !((N >= 2048 && N <= 32768) || long_rows)) return false;
+    const size_t lds_x = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    int nw = (long_rows || (!q8 && N <= 4096)) ? 16 : 8;
+    while (nw >= 4 && lds_x + (size_t)nw * Contig<F>::kStepBytes > (size_t)kLdsMax) nw /= 2;
+    switch (nw) {
+    case 16: *rc = launch_c_xu<F, 16>(W, N, nb, x, y, st); return true;
+    case 8: *rc = launch_c_xu<F, 8>(W, N, nb, x, y, st); return true;
+    case 4: *rc = launch_c_xu<F, 4>(W, N, nb, x, y, st); return true;
+    default: return false;
+    }
+}
+
 // Batch 1.  Workgroups of 8 waves when the staged activations (> 40 KB)
 // allow few workgroups per CU, else 4 (more, smaller workgroups spread
 // small matrices over every CU).  Activations are staged with straight-line
@@ -405,6 +553,8 @@ int32_t launch_lpr(const uint8_t* W, int64_t N, int nb, const float* x, int64_t 
 template <class F>
 int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
                   hipStream_t st) {
+    int32_t rc;
+    if (try_launch_c<F>(W, N, nb, x, y, st, &rc)) return rc;
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     const bool vec = aligned(x, 16);
     const int K4 = nb * 8;

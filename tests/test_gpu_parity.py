@@ -127,6 +127,33 @@ def test_random_byte_blocks(env, fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_contiguous_path_equals_per_block_path(env, fmt):
+    """Rows of whole 64-block steps with 16-byte aligned W take the
+    contiguous-chunk kernel; the same bytes at a 4-byte offset take the
+    per-block kernel.  Same lane mapping and arithmetic: bitwise equal, and
+    both within the bound of the oracle.  The shapes reach each launch
+    choice of the contiguous kernel: >= 8192 rows (Q8_0, 8 waves), Q4 with
+    2048..4096 rows (16 waves), >= 256 blocks per row (16 waves), the LDS
+    fallbacks to 8 waves (30720 columns, loop staging) and 4 waves (32768
+    columns), and ragged row counts."""
+    torch, qmv = env
+    f = _chain_fn(qmv, fmt)
+    for N, K in [(8193, 2048), (2100, 4096), (5, 8192), (129, 14336), (3, 30720), (2, 32768), (40000, 2048)]:
+        W = wl.quant_weights(fmt, f"t/contig/{N}x{K}", N, K)
+        x = wl.activations(f"t/contig/x/{K}", 1, K)
+        Wd, xd = dev(torch, W), dev(torch, x)
+        buf = torch.zeros(W.size + 16, dtype=torch.uint8, device="cuda:0")
+        Wo = buf[4:4 + W.size]
+        Wo.copy_(Wd.reshape(-1))
+        assert Wd.data_ptr() % 16 == 0 and Wo.data_ptr() % 16 == 4
+        y_c = f(Wd, N, K, xd[0])
+        y_b = f(Wo, N, K, xd[0])
+        torch.cuda.synchronize()
+        assert torch.equal(y_c.view(torch.int32), y_b.view(torch.int32)), (N, K)
+        yr, S = oracle.matvec(fmt, W, N, K, x)
+        assert_tol(y_c.cpu().numpy(), yr, S, (fmt, N, K))
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_one_hot_columns_exact(env, fmt):
     """x = e_j gives y_i = DEQ(W)_ij exactly (all other products are 0)."""
     N, K, B = 50, 1024, 8
