@@ -236,12 +236,18 @@ def qmv_dequant(fmt, W, n_rows, n_cols, out=None, stream=None):
     return out
 
 
-def chain_stages(stages):
-    """[(W, n_rows, n_cols, x, y, wait), ...] of GPU tensors -> ctypes array."""
+def chain_stages(stages, fmt=None):
+    """[(W, n_rows, n_cols, x, y, wait), ...] of GPU tensors -> ctypes array.
+    With fmt, each W is checked to hold its n_rows x n_cols blocks."""
     torch = _torch()
     arr = (ChainStage * len(stages))()
     for i, (W, n_rows, n_cols, x, y, wait) in enumerate(stages):
         _dev(W, "W", torch.uint8)
+        bb = BLOCK_BYTES.get(_fmt(fmt)) if fmt is not None else None   # unknown fmt: the library rejects it
+        if bb is not None:
+            need = n_rows * (n_cols // 32) * bb
+            if W.numel() < need or not W.is_contiguous():
+                raise ValueError(f"stage {i}: W must be contiguous and hold {need} bytes")
         _dev(x, "x", torch.float32)
         _dev(y, "y", torch.float32)
         if x.numel() < n_cols or y.numel() < n_rows or not x.is_contiguous() or not y.is_contiguous():
@@ -258,6 +264,6 @@ def qmv_chain(fmt, stages, workspace, stream=None):
     least CHAIN_WORKSPACE_BYTES, zero-filled before its first use."""
     torch = _torch()
     _dev(workspace, "workspace", torch.uint8)
-    arr = stages if isinstance(stages, ctypes.Array) else chain_stages(stages)
+    arr = stages if isinstance(stages, ctypes.Array) else chain_stages(stages, fmt)
     _check(_lib.qmv_chain(_fmt(fmt), ctypes.cast(arr, ctypes.c_void_p), len(arr), workspace.data_ptr(),
                           workspace.numel(), _stream(stream)))

@@ -239,10 +239,11 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 // qmv_kernel<F, 1, 64, 1, ...> (bitwise the same y), but each step's 64
 // blocks arrive as whole 16-byte chunks with non-temporal loads and are
 // re-read block-aligned from a per-wave LDS scratch.  One row per wave at
-// a time; rows are taken wave, wave + grid waves, ...
+// a time; rows are taken wave, wave + grid waves, ...  The rows are those
+// of up to kMaxSegs matrices sharing x, concatenated (a wave-uniform
+// lookup finds a row's matrix).
 template <class F, int XU, int NW, int PD = 2>
-__global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const uint8_t* __restrict__ W, int64_t N, int nb,
-                                                         const float* __restrict__ x, float* __restrict__ y) {
+__global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int nb, const float* __restrict__ x) {
     using C = Contig<F>;
     extern __shared__ float lds[];
     float* xs = lds;
@@ -252,6 +253,13 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const uint8_t* __restric
     uint8_t* scratch = reinterpret_cast<uint8_t*>(lds + nb * (kXPad + (F::kNeedSx ? 1 : 0))) + wave * C::kStepBytes;
     const int T = nb / 64;
     const int64_t wstride = (int64_t)gridDim.x * NW;
+    const int64_t N = segs.end[segs.n - 1];
+    auto seg_of = [&](int64_t g) {
+        int i = 0;
+#pragma unroll
+        for (int k = 0; k + 1 < kMaxSegs; ++k) i += (k + 1 < segs.n && g >= segs.end[k]) ? 1 : 0;
+        return i;
+    };
 
     typename C::Chunks buf[PD];
     int64_t lrow = (int64_t)blockIdx.x * NW + wave;   // next step to load
@@ -264,7 +272,9 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const uint8_t* __restric
     auto load_next = [&](typename C::Chunks& c) {
         const int64_t row = min(lrow, N - 1);          // past the end: re-read a loaded step
         const int t = lrow < N ? lt : 0;
-        C::fetch(W + (row * nb + 64 * t) * F::kBytes, lane, c);
+        const int i = seg_of(row);
+        const int64_t r = row - (i ? segs.end[i - 1] : 0);
+        C::fetch(segs.W[i] + (r * nb + 64 * t) * F::kBytes, lane, c);
         if (lrow < N) advance(lrow, lt);
     };
     float acc = 0.f;
@@ -282,7 +292,10 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const uint8_t* __restric
         acc = Term<F>::add(acc, d, m, sdot[0], F::kNeedSx ? sx[j] : 0.f);
         if (t == T - 1) {
             const float tot = segment_sum<64>(acc);
-            if (lane == 0) y[crow] = tot;
+            if (lane == 0) {
+                const int i = seg_of(crow);
+                segs.y[i][crow - (i ? segs.end[i - 1] : 0)] = tot;
+            }
             acc = 0.f;
         }
     };
@@ -491,7 +504,7 @@ int32_t launch_lpr(const uint8_t* W, int64_t N, int nb, const float* x, int64_t 
 }
 
 template <class F, int XU, int NW>
-int32_t launch_c(const uint8_t* W, int64_t N, int nb, const float* x, float* y, hipStream_t st) {
+int32_t launch_c(const RowSegs& segs, int nb, const float* x, hipStream_t st) {
     auto kern = qmv_kernel_c<F, XU, NW>;
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float) + NW * Contig<F>::kStepBytes;
     static bool attr_set = false;   // benign race: every thread sets the same value
@@ -501,23 +514,23 @@ int32_t launch_c(const uint8_t* W, int64_t N, int nb, const float* x, float* y, 
             return fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
         attr_set = true;
     }
-    const int64_t tiles = (N + NW - 1) / NW;
+    const int64_t tiles = (segs.end[segs.n - 1] + NW - 1) / NW;
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nb, x, y);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, segs, nb, x);
     return check_launch("qmv");
 }
 
 // XU 16-byte activation loads per thread stage K4 = K / 4 chunks with a
 // workgroup of NW waves; past 8 per thread the staging loops instead.
 template <class F, int NW>
-int32_t launch_c_xu(const uint8_t* W, int64_t N, int nb, const float* x, float* y, hipStream_t st) {
+int32_t launch_c_xu(const RowSegs& segs, int nb, const float* x, hipStream_t st) {
     const int per = (nb * 8 + 64 * NW - 1) / (64 * NW);
-    if (per <= 1) return launch_c<F, 1, NW>(W, N, nb, x, y, st);
-    if (per <= 2) return launch_c<F, 2, NW>(W, N, nb, x, y, st);
-    if (per <= 4) return launch_c<F, 4, NW>(W, N, nb, x, y, st);
-    if (per <= 8) return launch_c<F, 8, NW>(W, N, nb, x, y, st);
-    return launch_c<F, 0, NW>(W, N, nb, x, y, st);
+    if (per <= 1) return launch_c<F, 1, NW>(segs, nb, x, st);
+    if (per <= 2) return launch_c<F, 2, NW>(segs, nb, x, st);
+    if (per <= 4) return launch_c<F, 4, NW>(segs, nb, x, st);
+    if (per <= 8) return launch_c<F, 8, NW>(segs, nb, x, st);
+    return launch_c<F, 0, NW>(segs, nb, x, st);
 }
 
 // Batch 1 with whole 64-block steps and 16-byte aligned W and x: the
@@ -529,18 +542,21 @@ int32_t launch_c_xu(const uint8_t* W, int64_t N, int nb, const float* x, float* 
 // 16 waves per workgroup for long rows (one activation copy per CU) and
 // for Q4 matrices of <= 4096 rows, else 8; fewer if the LDS does not fit.
 template <class F>
-bool try_launch_c(const uint8_t* W, int64_t N, int nb, const float* x, float* y, hipStream_t st, int32_t* rc) {
-    if (nb % 64 || !aligned(W, 16) || !aligned(x, 16)) return false;
+bool try_launch_c(const RowSegs& segs, int nb, const float* x, hipStream_t st, bool force, int32_t* rc) {
+    if (nb % 64 || !aligned(x, 16) || segs.n < 1 || segs.n > kMaxSegs) return false;
+    for (int i = 0; i < segs.n; ++i)
+        if (!aligned(segs.W[i], 16)) return false;
+    const int64_t N = segs.end[segs.n - 1];
     const bool q8 = !F::kNeedSx;
     const bool long_rows = nb >= 256;
-    if (q8 ? !(N >= 8192 || long_rows) : !((N >= 2048 && N <= 32768) || long_rows)) return false;
+    if (!force && (q8 ? !(N >= 8192 || long_rows) : !((N >= 2048 && N <= 32768) || long_rows))) return false;
     const size_t lds_x = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     int nw = (long_rows || (!q8 && N <= 4096)) ? 16 : 8;
     while (nw >= 4 && lds_x + (size_t)nw * Contig<F>::kStepBytes > (size_t)kLdsMax) nw /= 2;
     switch (nw) {
-    case 16: *rc = launch_c_xu<F, 16>(W, N, nb, x, y, st); return true;
-    case 8: *rc = launch_c_xu<F, 8>(W, N, nb, x, y, st); return true;
-    case 4: *rc = launch_c_xu<F, 4>(W, N, nb, x, y, st); return true;
+    case 16: *rc = launch_c_xu<F, 16>(segs, nb, x, st); return true;
+    case 8: *rc = launch_c_xu<F, 8>(segs, nb, x, st); return true;
+    case 4: *rc = launch_c_xu<F, 4>(segs, nb, x, st); return true;
     default: return false;
     }
 }
@@ -554,7 +570,12 @@ template <class F>
 int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
                   hipStream_t st) {
     int32_t rc;
-    if (try_launch_c<F>(W, N, nb, x, y, st, &rc)) return rc;
+    RowSegs one = {};
+    one.W[0] = W;
+    one.y[0] = y;
+    one.end[0] = N;
+    one.n = 1;
+    if (try_launch_c<F>(one, nb, x, st, false, &rc)) return rc;
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     const bool vec = aligned(x, 16);
     const int K4 = nb * 8;
@@ -684,6 +705,17 @@ int32_t moe(const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64
 }
 
 }  // namespace
+
+bool group_matvec_contig(qmv_fmt fmt, const RowSegs& segs, int nb, const float* x, hipStream_t st, bool force,
+                         int32_t* rc) {
+    switch (fmt) {
+    case QMV_Q8_0: return try_launch_c<Q8_0>(segs, nb, x, st, force, rc);
+    case QMV_Q4_0: return try_launch_c<Q4_0>(segs, nb, x, st, force, rc);
+    case QMV_Q4_1: return try_launch_c<Q4_1>(segs, nb, x, st, force, rc);
+    default: return false;
+    }
+}
+
 }  // namespace qmv
 
 extern "C" int32_t qmv_q8_0(const void* W, int64_t n_rows, int64_t n_cols, const float* x, int64_t ldx, int32_t batch,

@@ -17,6 +17,8 @@
 // segment, fixed reduction order), so each stage's output equals a
 // qmv_q8_0 / qmv_q4_0 / qmv_q4_1 call on a matrix of >= 64 blocks per row
 // bitwise.
+#include <type_traits>
+
 #include "qmv_block_decode.h"
 
 namespace qmv {
@@ -24,7 +26,7 @@ namespace {
 
 constexpr int kChainMaxStages = 64;
 
-struct ChainStage {        // 32 bytes in the kernel arguments
+struct ChainStage {        // 40 bytes in the kernel arguments
     const uint8_t* W;
     const float* x;
     float* y;
@@ -32,6 +34,7 @@ struct ChainStage {        // 32 bytes in the kernel arguments
     int16_t nb;
     int8_t wait;
     int8_t xvec;           // x is 16-byte aligned
+    int32_t off;           // wave (of the grid's waves) that takes row 0
 };
 
 struct ChainArgs {
@@ -39,6 +42,7 @@ struct ChainArgs {
     unsigned* bar;         // barrier words (top at [0], groups 4 KB apart), [2] error flag
     int32_t n;
     int32_t nwg;
+    int32_t xfloats;       // LDS floats of staged activations; the weight copies follow
 };
 
 constexpr int kSc1 = 16;                     // buffer cache-policy operand: device-scope coherent
@@ -146,7 +150,11 @@ __device__ __forceinline__ void stage_x_coherent(const float* x, int nb, float* 
     }
 }
 
-template <class F, int NW>
+// CONTIG: every stage has whole 64-block steps and 16-byte aligned W, and
+// its weights arrive as whole 16-byte chunks (non-temporal) copied through
+// a per-wave LDS scratch, as in the contiguous dense kernel.  Otherwise
+// each lane loads its own block.
+template <class F, int NW, bool CONTIG>
 __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
     constexpr int LPR = 64;
     constexpr int RPL = 1;
@@ -155,21 +163,30 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
     float* sx = lds;   // set per stage: after the stage's staged x
     const int li = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t w0 = (int64_t)blockIdx.x * NW + wave;
-    const int64_t wstride = (int64_t)gridDim.x * NW;
+    const int w0 = (int)blockIdx.x * NW + wave;        // rows < 2^30, waves < 2^16: int
+    const int wstride = (int)gridDim.x * NW;
     const int n = args.n;
-    using Raw = typename F::Raw;
+    using C = Contig<F>;
+    using Raw = typename std::conditional<CONTIG, typename C::Chunks, typename F::Raw>::type;
+    uint8_t* scratch = reinterpret_cast<uint8_t*>(lds + args.xfloats) + wave * C::kStepBytes;
 
     // The load cursor runs one step ahead of the compute cursor, across
     // stage boundaries.  A step is (stage, row, t): lane li handles block
-    // li + 64 t of the row.  Rows of a stage are taken w0, w0 + wstride, ...
+    // li + 64 t of the row.  Row r of stage s goes to wave (off_s + r) mod
+    // wstride: the stages' rows continue one round-robin, so short stages
+    // do not all land on the first waves.
+    auto first_row = [&](int s) -> int { return (w0 - args.st[s].off + wstride) % wstride; };
     int ls = 0;
-    int64_t lrow = w0;
+    int lrow = first_row(0);
     int lt = 0;
-    auto skip_empty = [&](int& s, int64_t& row, int& t) {
-        while (s < n && row >= args.st[s].N) { ++s; row = w0; t = 0; }
+    auto skip_empty = [&](int& s, int& row, int& t) {
+        while (s < n && row >= args.st[s].N) {
+            ++s;
+            if (s < n) row = first_row(s);
+            t = 0;
+        }
     };
-    auto advance = [&](int& s, int64_t& row, int& t) {
+    auto advance = [&](int& s, int& row, int& t) {
         const int T = (args.st[s].nb + LPR - 1) / LPR;
         if (++t == T) { t = 0; row += wstride; }
         skip_empty(s, row, t);
@@ -178,9 +195,14 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
         // past the last step: re-read a block already loaded (in cache)
         const int s = ls < n ? ls : n - 1;
         const ChainStage& st = args.st[s];
-        const int64_t row = ls < n ? lrow : min(w0, (int64_t)st.N - 1);
-        const int j = min(li + LPR * (ls < n ? lt : 0), (int)st.nb - 1);
-        F::fetch(st.W, row * st.nb + j, r);
+        const int64_t row = ls < n ? lrow : min(w0, st.N - 1);
+        const int t = ls < n ? lt : 0;
+        if constexpr (CONTIG) {
+            C::fetch(st.W + (row * st.nb + 64 * t) * F::kBytes, li, r);
+        } else {
+            const int j = min(li + LPR * t, (int)st.nb - 1);
+            F::fetch(st.W, row * st.nb + j, r);
+        }
         if (ls < n) advance(ls, lrow, lt);
     };
     auto stage_x = [&](int s) {
@@ -189,7 +211,7 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
         stage_x_coherent<F::kNeedSx, 64 * NW>(st.x, st.nb, xs, sx, st.xvec != 0);
     };
     float acc = 0.f;
-    auto compute = [&](int s, int64_t row, int t, const Raw& r) {
+    auto compute = [&](int s, int row, int t, const Raw& r) {
         const ChainStage& st = args.st[s];
         const int nb = st.nb;
         const int j = li + LPR * t;
@@ -197,7 +219,13 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
         const int jc = valid ? j : nb - 1;
         float d, m;
         uint32_t c[8];
-        F::decode(r, d, m, c);
+        if constexpr (CONTIG) {
+            typename F::Raw blk;
+            C::to_block(r, scratch, li, blk);
+            F::decode(blk, d, m, c);
+        } else {
+            F::decode(r, d, m, c);
+        }
         float q[32];
         codes_to_float<F>(c, q);
         float sdot[1] = {0.f};
@@ -213,7 +241,7 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
     };
 
     int cs = 0;
-    int64_t crow = w0;
+    int crow = first_row(0);
     int ct = 0;
     skip_empty(ls, lrow, lt);
     skip_empty(cs, crow, ct);
@@ -276,9 +304,14 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
     }
 }
 
-template <class F, int NW>
-int32_t launch_chain(const ChainArgs& a, size_t lds, hipStream_t st, int* grid_out) {
-    auto kern = chain_kernel<F, NW>;
+// Launches one batch of stages.  lds_x: bytes of staged activations (the
+// largest stage's); the per-wave weight copies follow them in CONTIG mode.
+// The grid is what stays resident (the stage barriers need every
+// workgroup running), and no larger than the rows of all stages need.
+template <class F, int NW, bool CONTIG>
+int32_t launch_chain(ChainArgs& a, size_t lds_x, hipStream_t st) {
+    auto kern = chain_kernel<F, NW, CONTIG>;
+    const size_t lds = lds_x + (CONTIG ? (size_t)NW * Contig<F>::kStepBytes : 0);
     static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
     if (!dyn_max) {
         hipFuncAttributes fa;
@@ -293,18 +326,24 @@ int32_t launch_chain(const ChainArgs& a, size_t lds, hipStream_t st, int* grid_o
     if (lds > dyn_max) return fail(QMV_EINVAL, "qmv_chain: %zu bytes of staged activations exceed the LDS", lds);
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     int64_t rows = 0;
-    for (int s = 0; s < a.n; ++s) rows = std::max<int64_t>(rows, a.st[s].N);
+    for (int s = 0; s < a.n; ++s) rows += a.st[s].N;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>((rows + NW - 1) / NW,
                                                                  (int64_t)device_cu_count() * per_cu));
-    ChainArgs args = a;
-    args.nwg = grid;
-    *grid_out = grid;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, args);
+    a.nwg = grid;
+    a.xfloats = (int32_t)(lds_x / sizeof(float));
+    const int64_t waves = (int64_t)grid * NW;
+    int64_t before = 0;
+    for (int s = 0; s < a.n; ++s) {
+        a.st[s].off = (int32_t)(before % waves);
+        before += a.st[s].N;
+    }
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, a);
     return check_launch("qmv_chain");
 }
 
 template <class F>
-int32_t chain(const qmv_chain_stage* stages, int32_t n_stages, void* workspace, size_t ws_bytes, void* stream) {
+int32_t chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void* workspace, size_t ws_bytes,
+              void* stream) {
     const char* name = "qmv_chain";
     if (!stages || !workspace) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (n_stages < 1) return fail(QMV_EINVAL, "%s: n_stages must be >= 1", name);
@@ -312,6 +351,7 @@ int32_t chain(const qmv_chain_stage* stages, int32_t n_stages, void* workspace, 
         return fail(QMV_EINVAL, "%s: workspace of %zu bytes < %d", name, ws_bytes, QMV_CHAIN_WORKSPACE_BYTES);
     if (!aligned(workspace, 4)) return fail(QMV_EALIGN, "%s: workspace must be 4-byte aligned", name);
     int max_nb = 0;
+    bool contig = true;   // every stage: whole 64-block steps, 16-byte aligned W
     for (int s = 0; s < n_stages; ++s) {
         const qmv_chain_stage& q = stages[s];
         if (!q.W || !q.x || !q.y) return fail(QMV_EINVAL, "%s: stage %d: null pointer", name, s);
@@ -322,9 +362,33 @@ int32_t chain(const qmv_chain_stage* stages, int32_t n_stages, void* workspace, 
         if (!aligned(q.W, 4) || !aligned(q.x, 4) || !aligned(q.y, 4))
             return fail(QMV_EALIGN, "%s: stage %d: W, x and y must be 4-byte aligned", name, s);
         max_nb = std::max(max_nb, (int)(q.n_cols / 32));
+        contig = contig && (q.n_cols / 32) % 64 == 0 && aligned(q.W, 16);
     }
-    const size_t lds = (size_t)max_nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     hipStream_t st = as_stream(stream);
+    // One group of matvecs on one input (no stage waits, same x and width):
+    // the dense contiguous kernel over the stages' concatenated rows, one
+    // launch and no stage boundaries (bitwise the same outputs).
+    bool group = n_stages <= kMaxSegs;
+    for (int s = 1; s < n_stages && group; ++s)
+        group = !stages[s].wait && stages[s].x == stages[0].x && stages[s].n_cols == stages[0].n_cols;
+    if (group) {
+        RowSegs segs = {};
+        segs.n = n_stages;
+        int64_t rows = 0;
+        for (int s = 0; s < n_stages; ++s) {
+            segs.W[s] = static_cast<const uint8_t*>(stages[s].W);
+            segs.y[s] = stages[s].y;
+            rows += stages[s].n_rows;
+            segs.end[s] = rows;
+        }
+        int32_t rc;
+        if (group_matvec_contig(fmt, segs, (int)(stages[0].n_cols / 32), stages[0].x, st, true, &rc))
+            return rc == QMV_OK ? ok() : rc;
+    }
+    const size_t lds_x = (size_t)max_nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    const size_t step = Contig<F>::kStepBytes;
+    const int contig_nw = !contig ? 0 : lds_x + 8 * step <= (size_t)kLdsMax ? 8
+                                      : lds_x + 4 * step <= (size_t)kLdsMax ? 4 : 0;
     for (int s0 = 0; s0 < n_stages; s0 += kChainMaxStages) {
         ChainArgs a = {};
         a.n = std::min(kChainMaxStages, n_stages - s0);
@@ -339,8 +403,11 @@ int32_t chain(const qmv_chain_stage* stages, int32_t n_stages, void* workspace, 
             a.st[i].wait = (i > 0 && q.wait) ? 1 : 0;   // the first stage of a launch follows a kernel boundary
             a.st[i].xvec = aligned(q.x, 16) ? 1 : 0;
         }
-        int grid = 0;
-        const int32_t rc = lds > 40 * 1024 ? launch_chain<F, 8>(a, lds, st, &grid) : launch_chain<F, 4>(a, lds, st, &grid);
+        int32_t rc;
+        if (contig_nw == 8) rc = launch_chain<F, 8, true>(a, lds_x, st);
+        else if (contig_nw == 4) rc = launch_chain<F, 4, true>(a, lds_x, st);
+        else if (lds_x > 40 * 1024) rc = launch_chain<F, 8, false>(a, lds_x, st);
+        else rc = launch_chain<F, 4, false>(a, lds_x, st);
         if (rc != QMV_OK) return rc;
     }
     return ok();
@@ -352,9 +419,9 @@ int32_t chain(const qmv_chain_stage* stages, int32_t n_stages, void* workspace, 
 extern "C" int32_t qmv_chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void* workspace,
                              size_t workspace_bytes, void* stream) {
     switch (fmt) {
-    case QMV_Q8_0: return qmv::chain<qmv::Q8_0>(stages, n_stages, workspace, workspace_bytes, stream);
-    case QMV_Q4_0: return qmv::chain<qmv::Q4_0>(stages, n_stages, workspace, workspace_bytes, stream);
-    case QMV_Q4_1: return qmv::chain<qmv::Q4_1>(stages, n_stages, workspace, workspace_bytes, stream);
+    case QMV_Q8_0: return qmv::chain<qmv::Q8_0>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
+    case QMV_Q4_0: return qmv::chain<qmv::Q4_0>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
+    case QMV_Q4_1: return qmv::chain<qmv::Q4_1>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
     default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_chain: unknown format %d", (int)fmt);
     }
 }

@@ -31,4 +31,22 @@ int32_t check_launch(const char* what);
 
 inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
+// Up to kMaxSegs matrices with the same number of columns that read one
+// activation vector, run as one batch-1 matvec over their concatenated
+// rows (each matrix's blocks and outputs stay in its own buffers).
+constexpr int kMaxSegs = 4;
+struct RowSegs {
+    const uint8_t* W[kMaxSegs];
+    float* y[kMaxSegs];
+    int64_t end[kMaxSegs];   // cumulative row counts: rows of matrix i are [end[i-1], end[i])
+    int32_t n;
+};
+
+// Runs segs with the contiguous-chunk batch-1 kernel of format fmt when it
+// applies (whole 64-block steps, W and x 16-byte aligned): returns true and
+// the launch status in *rc, else false and launches nothing.  Without
+// force, only where that kernel measured faster than per-block loads.
+bool group_matvec_contig(qmv_fmt fmt, const RowSegs& segs, int nb, const float* x, hipStream_t st, bool force,
+                         int32_t* rc);
+
 }  // namespace qmv

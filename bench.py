@@ -4,10 +4,14 @@
 A step is one batch-1 decode token of the 8B Llama-shaped layer set in Q8_0:
 32 layers x (q 4096x4096, k/v 1024x4096, o 4096x4096, gate/up 14336x4096,
 down 4096x14336) + lm_head 128256x4096 = 225 matvecs, 7,973,699,584 bytes of
-weights, every layer in its own device buffers (the working set is ~31x the
+weights, every matrix in its own device buffer (the working set is ~31x the
 256 MB last-level cache, so every step streams from HBM).  Weights are drawn
-N(0, 0.02^2) and encoded per 32-weight block; activations N(0, 1).  The step
-is captured once as a HIP graph and replayed.
+N(0, 0.02^2) and encoded per 32-weight block; activations N(0, 1).  The
+matvecs run in decode dependency order, one launch per dependency level:
+q, k, v (one input) in one qmv_chain call, o, gate and up (one input) in
+one call, down, then lm_head (129 launches).  The step is captured once as
+a HIP graph and replayed.  The same matrices launched one matvec at a time
+(225 launches) are reported as the sweep llama8b_q8_0_b1.
 
 Printed: one JSON line with the step's achieved GB/s (algorithmic weight +
 activation + output bytes / wall time, whole job), the equivalent decode
@@ -34,20 +38,30 @@ PEAK_GBS = 8000.0
 
 # HBM traffic of the dominant kernel from rocprofv3 FETCH_SIZE + WRITE_SIZE
 # runs (copy-calibrated: FETCH x2.0, WRITE x1.0), per launch, recorded for
-# the kernel source with this SHA-256; reported as null once the source
-# differs (the kernel changed since the counters were taken).
+# the kernel sources with this SHA-256 (of the files in order); reported as
+# null once a source differs (the kernel changed since the counters were
+# taken).
 TRAFFIC_RECORD = {
-    "source": "bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
-    "sha256": "b63f2677e21f4f9992eed2a72c693897960efb17571f5144989ed37c8ab8f4f9",
-    "bytes_per_launch": 31237716,
+    "sources": ["bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
+                "bandwidth_bound_block_amd/csrc/qmv_block_decode.h",
+                "bandwidth_bound_block_amd/csrc/qmv_host.h"],
+    "sha256": "5a06f277d8a9f7688a3409f7a41e6844ece692f21be5129ebaa81eb0b5e5e9d3",
+    "bytes_per_launch": 83478652,
 }
 
 
-def recorded_traffic():
+def sources_sha256(paths):
     import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
     try:
-        with open(os.path.join(ROOT, TRAFFIC_RECORD["source"]), "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()
+        h = sources_sha256(TRAFFIC_RECORD["sources"])
     except OSError:
         return None
     return TRAFFIC_RECORD["bytes_per_launch"] if h == TRAFFIC_RECORD["sha256"] else None
@@ -188,6 +202,49 @@ def build_llama_chain(torch, qmv, wl, fmt, fused=False):
     sw.add("chain", qmv.lib().qmv_chain,
            (qmv.FORMATS[fmt], ctypes.cast(arr, ctypes.c_void_p), len(arr), ws.data_ptr(), ws.numel()), total)
     sw.workspace = ws
+    return sw
+
+
+# Matvecs of a decode step that share their input and do not depend on one
+# another: one qmv_chain call each (no stage waits inside a group).
+DECODE_GROUPS = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "up")), ("down", ("down",))]
+
+
+def build_llama_grouped(torch, qmv, wl, fmt):
+    """The batch-1 8B decode step with the separate matrices and buffers of
+    build_llama, launched in dependency order with one launch per
+    dependency level: q, k, v (same input) in one qmv_chain call, o, gate
+    and up (same input) in one call, down; then lm_head."""
+    dense = build_llama(torch, qmv, wl, fmt, 1, fused=False)
+    sw = Sweep(dense.name.replace("_b1", "_grouped_b1"), 1)
+    sw.keep = dense.keep
+    ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    sw.keep.append(ws)
+    sw.workspace = ws
+    by_label = {}
+    per_layer = [l for l in dense.launches if l[0] != "lm_head"]
+    order = [m for _, ms in DECODE_GROUPS for m in ms]
+    nl = len(per_layer) // len(order)
+    for layer in range(nl):
+        mats = {l[0]: l for l in per_layer[layer * len(order):(layer + 1) * len(order)]}
+        for gname, members in DECODE_GROUPS:
+            if len(members) == 1:
+                label, cfn, args, nb = mats[members[0]]
+                sw.add(label, cfn, args, nb)
+                continue
+            arr = (qmv.ChainStage * len(members))()
+            total = 0
+            for i, m in enumerate(members):
+                _, _, (Wp, N, K, xp, _, _, yp, _), nb = mats[m]
+                arr[i] = qmv.ChainStage(Wp, xp, yp, N, K, 0, 0)
+                total += nb
+            sw.keep.append(arr)
+            sw.add(gname, qmv.lib().qmv_chain,
+                   (qmv.FORMATS[fmt], ctypes.cast(arr, ctypes.c_void_p), len(members), ws.data_ptr(), ws.numel()),
+                   total)
+    for l in dense.launches:
+        if l[0] == "lm_head":
+            sw.add(*l)
     return sw
 
 
@@ -415,7 +472,7 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
         return
 
-    sw = build_llama(torch, qmv, wl, "q8_0", 1)
+    sw = build_llama_grouped(torch, qmv, wl, "q8_0")
     log(f"[{sw.name}] {len(sw.launches)} launches, {sw.bytes_per_step} bytes/step")
     head = time_sweep(torch, sw, args.steps, args.warmup, not args.no_graph)
     log(f"[{sw.name}] {head['ms_per_step']:.3f} ms/step wall, {head['gbs_wall']:.0f} GB/s wall, "
@@ -437,10 +494,11 @@ def main():
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
         if nm == "q8_0":
-            s = build_llama(torch, qmv, wl, "q8_0", 1, fused=True)
-            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
-            del s
-            torch.cuda.empty_cache()
+            for fused in (False, True):
+                s = build_llama(torch, qmv, wl, "q8_0", 1, fused=fused)
+                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+                del s
+                torch.cuda.empty_cache()
             for fused in (False, True):
                 s = build_llama_chain(torch, qmv, wl, "q8_0", fused=fused)
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
@@ -448,6 +506,10 @@ def main():
                 del s
                 torch.cuda.empty_cache()
         elif nm in ("q4_0", "q4_1"):
+            s = build_llama_grouped(torch, qmv, wl, nm)
+            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+            del s
+            torch.cuda.empty_cache()
             for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
                 s = build_llama(torch, qmv, wl, nm, B, fused=fused)
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
@@ -473,12 +535,14 @@ def main():
         cpu = cpu_baseline(wl)
         log(f"[cpu_baseline] {cpu['value']:.3f} GB/s in {time.time() - t0:.1f}s")
 
-    # Roofline of the dominant kernel.  Every K = 4096 launch of the step
-    # (q, k, v, o, gate, up, lm_head: 193 of 225) runs one instantiation,
-    # qmv_kernel<Q8_0, B=1, 64 lanes/row, 1 row/lane, XU=4, 4 waves>; down
-    # (K = 14336) runs the 8-wave one.  achieved = that kernel's algorithmic
-    # bytes over its summed per-launch event times.
-    dom = [k for k in ("q", "k", "v", "o", "gate", "up", "lm_head") if k in head["per_matrix"]]
+    # Roofline of the dominant kernel.  The q||k||v (6144 rows), gate||up
+    # (28672 rows) and lm_head (128256 rows) launches, 65 of the step's 129
+    # and ~60% of its time, run one instantiation: the contiguous-chunk
+    # kernel qmv_kernel_c<Q8_0, XU=2, 8 waves, PD=2>; down (K = 14336) runs
+    # the 16-wave one and o (4096 rows) the per-block kernel.  achieved =
+    # that kernel's algorithmic bytes over its summed per-launch event
+    # times (each launch of a label back to back on the launch stream).
+    dom = [k for k in ("qkv", "gate_up", "lm_head") if k in head["per_matrix"]]
     pm = head["per_matrix"]
     dom_bytes = sum(pm[k]["bytes_per_launch"] * pm[k]["launches"] for k in dom)
     dom_us = sum(pm[k]["us_per_launch"] * pm[k]["launches"] for k in dom)
@@ -486,7 +550,7 @@ def main():
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(),
-            "kernel": "qmv_kernel<Q8_0, 1, 64, 1, 4, 4>",
+            "kernel": "qmv_kernel_c<Q8_0, 2, 8, 2>",
             "launches_per_step": dom_n, "us_per_launch": dom_us / dom_n,
             "bytes_per_launch": dom_bytes / dom_n}
     line = {
@@ -503,7 +567,8 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": "llama8b_q8_0_decode_sweep_b1", "format": "q8_0", "batch": 1,
-                   "layers": 32, "matvecs_per_step": head["launches_per_step"],
+                   "layers": 32, "matvecs_per_step": 225, "launches_per_step": head["launches_per_step"],
+                   "launch": "one per dependency level: qkv, o, gate_up, down; lm_head",
                    "bytes_per_step": head["bytes_per_step"], "hip_graph": head["graph"]},
         "pct_of_peak": head["pct_peak_wall"],
         "tok_s_equiv": head["tok_s_wall"],

@@ -165,7 +165,9 @@ int32_t qmv_moe(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
  * may read only outputs that were already visible to the last earlier
  * stage with wait != 0 (e.g. it shares that stage's input), not outputs
  * of stages after it.  Weight loads of a stage may begin before earlier
- * stages finish.
+ * stages finish.  A call of at most 4 stages that all read one x with the
+ * same n_cols and do not wait (e.g. the q, k and v projections of a decode
+ * step) runs as a single matvec over their concatenated rows.
  *   stages        host array of n_stages entries (copied into the launch).
  *   n_rows        1..2^30;  n_cols a multiple of 32 in 32..35424.
  *   W, x, y       device pointers, 4-byte aligned, as for qmv_q8_0.

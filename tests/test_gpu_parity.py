@@ -492,3 +492,40 @@ def test_chain_decode_pattern(env, fmt):
         assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), i
     last = outs[-1]["down"].cpu().numpy()
     assert np.isfinite(last).all() and np.abs(last).max() > 1e-3
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_chain_shared_input_groups(env, fmt):
+    """Stages that read one x and do not wait: up to 4 run as one matvec over
+    their concatenated rows, more (or with a misaligned W) through the
+    persistent chain kernel.  Every output equals the batch-1 entry point
+    on its own matrix bitwise (>= 64 blocks per row)."""
+    torch, qmv = env
+    f = _chain_fn(qmv, fmt)
+    ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
+    groups = {
+        "qkv": [(4096, 4096), (1024, 4096), (1024, 4096)],
+        "gate_up": [(3000, 2048), (3000, 2048)],
+        "five": [(300, 2048), (77, 2048), (1, 2048), (513, 2048), (64, 2048)],
+        "misaligned": [(700, 2048), (129, 2048)],
+    }
+    for gname, shapes in groups.items():
+        K = shapes[0][1]
+        x = dev(torch, wl.activations(f"t/chain/grp/{gname}/x", 1, K))[0]
+        stages, mats = [], []
+        for i, (N, _) in enumerate(shapes):
+            W = dev(torch, wl.quant_weights(fmt, f"t/chain/grp/{gname}/{i}", N, K)).reshape(-1)
+            if gname == "misaligned" and i == 1:
+                buf = torch.zeros(W.numel() + 16, dtype=torch.uint8, device="cuda:0")
+                buf[4:4 + W.numel()].copy_(W)
+                W = buf[4:4 + W.numel()]
+            y = torch.full((N,), float("nan"), device="cuda:0")
+            stages.append((W, N, K, x, y, 0))
+            mats.append((W, N))
+        qmv.qmv_chain(fmt, stages, ws)
+        torch.cuda.synchronize()
+        assert int(ws.view(torch.int32)[2].item()) == 0
+        for (W, N), st in zip(mats, stages):
+            ref = f(W, N, K, x)[0]
+            torch.cuda.synchronize()
+            assert torch.equal(st[4].view(torch.int32), ref.view(torch.int32)), (gname, N)
