@@ -273,6 +273,58 @@ __device__ __forceinline__ void dot_cols(const float (&q)[32], const float* __re
     }
 }
 
+// Codes of elements 4i..4i+3 of a block as floats (the same values
+// codes_to_float puts at q[4i..4i+3]).
+template <class F>
+__device__ __forceinline__ void chunk_codes(const uint32_t (&c)[8], int i, float (&q)[4]);
+template <>
+__device__ __forceinline__ void chunk_codes<Q8_0>(const uint32_t (&c)[8], int i, float (&q)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = sbyte(c[i], k);
+}
+__device__ __forceinline__ void chunk_nibbles(const uint32_t (&c)[8], int i, float (&q)[4]) {
+    const uint32_t v = i < 4 ? (c[i] & 0x0f0f0f0fu) : ((c[i - 4] >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = ubyte(v, k);
+}
+template <>
+__device__ __forceinline__ void chunk_codes<Q4_0>(const uint32_t (&c)[8], int i, float (&q)[4]) { chunk_nibbles(c, i, q); }
+template <>
+__device__ __forceinline__ void chunk_codes<Q4_1>(const uint32_t (&c)[8], int i, float (&q)[4]) { chunk_nibbles(c, i, q); }
+
+// s[r][b] = sum_{e<32} code_r[e] * x_b[e] for R blocks (rows) of the same
+// block column and the first w of B columns.  Chunk-outer: each 16-byte
+// read of x from LDS serves all R rows, so LDS traffic per weight falls by
+// R.  Each s[r][b] accumulates e = 0..31 in order, with the operations of
+// dot_cols: the same bits.
+template <class F, int R, int B>
+__device__ __forceinline__ void dot_multi(const uint32_t (&c)[R][8], const float* __restrict__ xs, int xstride_b,
+                                          float (&s)[R][B], int w) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int b = 0; b < B; ++b) s[r][b] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float q[R][4];
+#pragma unroll
+        for (int r = 0; r < R; ++r) chunk_codes<F>(c[r], i, q[r]);
+#pragma unroll
+        for (int b = 0; b < B; ++b) {
+            if (b < w) {
+                const float4 xv = *reinterpret_cast<const float4*>(xs + b * xstride_b + 4 * i);
+#pragma unroll
+                for (int r = 0; r < R; ++r) {
+                    s[r][b] = __builtin_fmaf(q[r][0], xv.x, s[r][b]);
+                    s[r][b] = __builtin_fmaf(q[r][1], xv.y, s[r][b]);
+                    s[r][b] = __builtin_fmaf(q[r][2], xv.z, s[r][b]);
+                    s[r][b] = __builtin_fmaf(q[r][3], xv.w, s[r][b]);
+                }
+            }
+        }
+    }
+}
+
 // Adds a block's term to the running sum, from the code dot s and the block
 // sum sx of x.  Written with explicit fused multiply-adds so that every entry
 // point (dense, MoE, any batch width) rounds identically.

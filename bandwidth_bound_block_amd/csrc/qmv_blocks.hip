@@ -34,55 +34,16 @@ namespace qmv {
 namespace {
 
 // ------------------------------------------------------------------ kernels
-// Computes, for the rows row0 + r*G + seg (r < RPL) of an N-row matrix with
-// nb blocks per row, the B dot products with the staged activations, and
-// leaves the segment totals in acc (identical in all LPR lanes).
-template <class F, int B, int LPR, int RPL>
-__device__ __forceinline__ void tile_rows(const uint8_t* __restrict__ W, int64_t N, int nb, int64_t row0,
-                                          const float* __restrict__ xs, const float* __restrict__ sx,
-                                          float (&acc)[RPL][B], int w) {
-    constexpr int G = 64 / LPR;
-    const int lane = threadIdx.x & 63;
-    const int seg = lane / LPR;
-    const int li = lane % LPR;
-    const int xb = nb * kXPad;
-    int64_t gbase[RPL];
-#pragma unroll
-    for (int r = 0; r < RPL; ++r) {
-        const int64_t row = row0 + r * G + seg;
-        gbase[r] = (row < N ? row : N - 1) * nb;   // clamp: loads stay in bounds
-    }
-#pragma unroll
-    for (int r = 0; r < RPL; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[r][b] = 0.f;
-
-    for (int j = li; j < nb; j += LPR) {
-        float d[RPL], m[RPL];
-        uint32_t c[RPL][8];
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) load_block<F>(W, gbase[r] + j, d[r], m[r], c[r]);
-        const float* xj = xs + j * kXPad;
-        float sxb[B];
-#pragma unroll
-        for (int b = 0; b < B; ++b) sxb[b] = b < w ? sx[b * nb + j] : 0.f;
-#pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-            float q[32];
-            codes_to_float<F>(c[r], q);
-            float s[B];
-#pragma unroll
-            for (int b = 0; b < B; ++b) s[b] = 0.f;
-            dot_cols<B>(q, xj, xb, s, w);
-#pragma unroll
-            for (int b = 0; b < B; ++b) acc[r][b] = Term<F>::add(acc[r][b], d[r], m[r], s[b], sxb[b]);
-        }
-    }
-#pragma unroll
-    for (int r = 0; r < RPL; ++r)
-#pragma unroll
-        for (int b = 0; b < B; ++b) acc[r][b] = segment_sum<LPR>(acc[r][b]);
-}
+// Routing of the dense kernel (ROUTE = true): grid row p (blockIdx.y)
+// computes pair p of a single token's expert list, with expert ids[p]
+// (weights at ids[p] * estride), activations at p * xs_slot and outputs at
+// p * ldy.  An id outside [0, n_experts) makes that pair's outputs quiet NaN.
+struct PairRoute {
+    const int32_t* ids;
+    int64_t estride;
+    int64_t xs_slot;
+    int32_t n_experts;
+};
 
 // Dense matvec.  A persistent grid (as many workgroups as fit on the GPU at
 // once); wave w of the grid takes row tiles w, w + waves, ... .  A tile is
@@ -92,11 +53,12 @@ __device__ __forceinline__ void tile_rows(const uint8_t* __restrict__ W, int64_t
 // loaded while the current step is computed (two steps in flight per wave),
 // and the first step's loads are issued before the activation staging so
 // that both latencies overlap.
-template <class F, int B, int LPR, int RPL, int XU, int NW, int PD = 2>
+template <class F, int B, int LPR, int RPL, int XU, int NW, int PD = 2, bool ROUTE = false>
 __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict__ W, int64_t N, int nb,
                                                        const float* __restrict__ x, int64_t ldx,
-                                                       float* __restrict__ y, int64_t ldy, int xvec) {
-    extern __shared__ float lds[];
+                                                       float* __restrict__ y, int64_t ldy, int xvec,
+                                                       const PairRoute route) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
     float* xs = lds;
     float* sx = lds + B * nb * kXPad;
 
@@ -109,6 +71,17 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
     const int T = (nb + LPR - 1) / LPR;
     const int64_t ntiles = (N + ROWS - 1) / ROWS;
     const int64_t wstride = (int64_t)gridDim.x * NW;
+    bool bad = false;   // routed pair with an invalid id: outputs become NaN
+    if constexpr (ROUTE) {
+        // No branch: an invalid id streams expert 0 (valid memory) and its
+        // outputs are replaced, so the prologue below stays straight-line.
+        const int p = blockIdx.y;
+        const int e = route.ids[p];          // uniform: one scalar load
+        bad = e < 0 || e >= route.n_experts;
+        W += (int64_t)(bad ? 0 : e) * route.estride;
+        x += (int64_t)p * route.xs_slot;
+        y += (int64_t)p * ldy;
+    }
 
     // Step (tile, t): lane li handles block li + LPR*t of its RPL rows.
     using Raw = typename F::Raw;
@@ -134,23 +107,19 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
         float sxb[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) sxb[b] = F::kNeedSx ? sx[b * nb + jc] : 0.f;
+        float d[RPL], m[RPL];
+        uint32_t c[RPL][8];
 #pragma unroll
-        for (int r = 0; r < RPL; ++r) {
-            float d, m;
-            uint32_t c[8];
-            F::decode(blk[r], d, m, c);
-            float q[32];
-            codes_to_float<F>(c, q);
-            float sdot[B];
+        for (int r = 0; r < RPL; ++r) F::decode(blk[r], d[r], m[r], c[r]);
+        float sdot[RPL][B];
+        dot_multi<F, RPL, B>(c, xj, nb * kXPad, sdot, B);
 #pragma unroll
-            for (int b = 0; b < B; ++b) sdot[b] = 0.f;
-            dot_cols<B>(q, xj, nb * kXPad, sdot, B);
+        for (int r = 0; r < RPL; ++r)
 #pragma unroll
             for (int b = 0; b < B; ++b) {
-                const float upd = Term<F>::add(acc[r][b], d, m, sdot[b], sxb[b]);
+                const float upd = Term<F>::add(acc[r][b], d[r], m[r], sdot[r][b], sxb[b]);
                 acc[r][b] = valid ? upd : acc[r][b];
             }
-        }
         if (t == T - 1) {   // tile done: reduce the segments and write
 #pragma unroll
             for (int r = 0; r < RPL; ++r)
@@ -162,7 +131,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
                     const int64_t row = tile * ROWS + r * G + seg;
                     if (row < N) {
 #pragma unroll
-                        for (int b = 0; b < B; ++b) y[b * ldy + row] = acc[r][b];
+                        for (int b = 0; b < B; ++b) y[b * ldy + row] = bad ? __builtin_nanf("") : acc[r][b];
                     }
                 }
             }
@@ -245,7 +214,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 template <class F, int XU, int NW, int PD = 2>
 __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int nb, const float* __restrict__ x) {
     using C = Contig<F>;
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
     float* xs = lds;
     float* sx = lds + nb * kXPad;
     const int lane = threadIdx.x & 63;
@@ -348,57 +317,133 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
 constexpr int kMoeMaxPairs = 128;
 constexpr int kMoeStaticLds = 4096;  // s_ids/s_first/s_members/scalars, rounded up
 
-// One group of w <= 8 member pairs: stage their activations, then the
-// wave's rows of the expert, written to each member's output rows.
-template <class F, int LPR, int RPL>
-__device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_t N, int nb, int64_t wg_row0,
-                                          const float* __restrict__ x, int64_t xs_tok, int64_t xs_slot, int top_k,
-                                          const int* __restrict__ members, int w, float* __restrict__ y, float* xs,
+// One chunk of up to BC member pairs of expert We: stage their activations
+// and stream the workgroup's row tiles [tb, te) once, writing each member's
+// output rows.  XU > 0 (the activations fit in XU 16-byte loads per thread
+// and are 16-byte aligned): the activation loads are issued first, then the
+// first weight loads, and only then are the activations stored to LDS, so
+// the two latencies overlap (loads complete in order).  XU == 0: staged by
+// the looping stager, then the weights.  Ends with a barrier.
+template <class F, int BC, int LPR, int NW, int XU, int PD = 2>
+__device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_t N, int nb, int64_t tb, int64_t te,
+                                          const float* const (&xcol)[BC], int w, bool xvec,
+                                          const int* __restrict__ members, float* __restrict__ y, float* xs,
                                           float* sx) {
-    constexpr int B = 8;
     constexpr int G = 64 / LPR;
-    constexpr int ROWS = G * RPL;
-    const float* xcol[B];
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        const int p = b < w ? members[b] : 0;
-        xcol[b] = x + (int64_t)(p / top_k) * xs_tok + (int64_t)(p % top_k) * xs_slot;
-    }
-    stage_x_cols<F::kNeedSx, B, kThreads>(xcol, nb, xs, sx, w, false);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int seg = lane / LPR;
     const int li = lane % LPR;
-    const int64_t row0 = wg_row0 + (int64_t)wave * ROWS;
-    if (row0 < N) {
-        float acc[RPL][B];
-        tile_rows<F, B, LPR, RPL>(We, N, nb, row0, xs, sx, acc, w);
-        if (li == 0) {
+    const int T = (nb + LPR - 1) / LPR;
+    using Raw = typename F::Raw;
+    int64_t ltile = tb + wave, ctile = ltile;
+    int lt = 0, ct = 0;
+    auto advance = [&](int64_t& tile, int& st) {
+        if (++st == T) { st = 0; tile += NW; }
+    };
+    auto load_next = [&](Raw& r) {
+        const int64_t tile = min(ltile, te - 1);       // past the range: re-read a loaded block
+        const int j = min(li + LPR * (ltile < te ? lt : 0), nb - 1);
+        const int64_t row = min(tile * G + seg, N - 1);
+        F::fetch(We, row * nb + j, r);
+        if (ltile < te) advance(ltile, lt);
+    };
+    float acc[BC];
 #pragma unroll
-            for (int r = 0; r < RPL; ++r) {
-                const int64_t row = row0 + r * G + seg;
-                if (row < N) {
+    for (int b = 0; b < BC; ++b) acc[b] = 0.f;
+    auto compute_step = [&](int64_t tile, int st, const Raw& r) {
+        const int j = li + LPR * st;
+        const bool valid = j < nb;
+        const int jc = valid ? j : nb - 1;
+        float d[1], m[1];
+        uint32_t c[1][8];
+        F::decode(r, d[0], m[0], c[0]);
+        float s[1][BC];
+        dot_multi<F, 1, BC>(c, xs + jc * kXPad, nb * kXPad, s, w);
 #pragma unroll
-                    for (int b = 0; b < B; ++b)
-                        if (b < w) y[(int64_t)members[b] * N + row] = acc[r][b];
-                }
+        for (int b = 0; b < BC; ++b) {
+            if (b < w) {
+                const float sxb = F::kNeedSx ? sx[b * nb + jc] : 0.f;
+                const float upd = Term<F>::add(acc[b], d[0], m[0], s[0][b], sxb);
+                acc[b] = valid ? upd : acc[b];
             }
         }
+        if (st == T - 1) {
+            const int64_t row = tile * G + seg;
+#pragma unroll
+            for (int b = 0; b < BC; ++b) {
+                if (b < w) {
+                    const float tot = segment_sum<LPR>(acc[b]);
+                    if (li == 0 && row < N) y[(int64_t)members[b] * N + row] = tot;
+                }
+                acc[b] = 0.f;
+            }
+        }
+    };
+
+    Raw buf[PD];
+    const int K4 = nb * 8;
+    if constexpr (XU > 0) {
+        // every column slot is loaded and stored (inactive ones repeat
+        // column 0): straight-line code, so no branch merges the waits
+        XStage<XU, 64 * NW> xst[BC];
+#pragma unroll
+        for (int b = 0; b < BC; ++b) xst[b].load(xcol[b], K4);
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int b = 0; b < BC; ++b) xst[b].store(xs + b * nb * kXPad, K4);
+        __syncthreads();
+        if (F::kNeedSx) {
+            block_sums<64 * NW>(xs, sx, BC * nb);
+            __syncthreads();
+        }
+    } else {
+        stage_x_cols<F::kNeedSx, BC, 64 * NW>(xcol, nb, xs, sx, w, xvec);
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
-    __syncthreads();   // xs is restaged by the next group
+
+#define QMV_MOE_STEP(P)                                    \
+    {                                                      \
+        load_next(buf[((P) + PD - 1) % PD]);               \
+        __builtin_amdgcn_sched_barrier(0);                 \
+        compute_step(ctile, ct, buf[(P)]);                 \
+        advance(ctile, ct);                                \
+        if (ctile >= te) break;                            \
+    }
+    static_assert(PD == 2, "pipeline depth");
+    if (ctile < te) {
+        while (true) {
+            QMV_MOE_STEP(0)
+            QMV_MOE_STEP(1)
+        }
+    }
+#undef QMV_MOE_STEP
+    __syncthreads();   // xs is restaged by the next chunk
 }
 
-template <class F, int LPR, int RPL>
-__global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
+// Grouped expert matvec.  Workgroup (bx, u) serves the u-th distinct id
+// of the (token, slot) pairs, in first-occurrence order, and the bx-th
+// range of that expert's row tiles: it groups the pairs itself (O(P) per
+// thread for P <= 128 pairs; no prologue kernel, no workspace), then runs
+// moe_chunk for up to BC member pairs at a time.  Per (row, pair) the
+// arithmetic is the dense kernel's, so each output equals a single-expert
+// dense call bitwise.
+template <class F, int BC, int LPR, int NW, int XU>
+__global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
                                                        int n_experts, int64_t N, int nb,
                                                        const int32_t* __restrict__ ids, int P, int top_k,
                                                        const float* __restrict__ x, int64_t xs_tok,
-                                                       int64_t xs_slot, float* __restrict__ y, int max_cols) {
+                                                       int64_t xs_slot, float* __restrict__ y, int xvec) {
+    static_assert(64 * NW >= kMoeMaxPairs, "one thread per pair");
     __shared__ int s_ids[kMoeMaxPairs];
     __shared__ int s_first[kMoeMaxPairs];
     __shared__ int s_members[kMoeMaxPairs];
     __shared__ int s_expert, s_has, s_nmem;
-    extern __shared__ float lds[];
+    extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
     const int t = threadIdx.x;
     const int u = blockIdx.y;
     if (t < P) s_ids[t] = ids[t];
@@ -431,23 +476,37 @@ __global__ __launch_bounds__(kThreads) void moe_kernel(const uint8_t* __restrict
     }
     __syncthreads();
     const int nmem = s_nmem;
-    constexpr int ROWS_WG = kWaves * (64 / LPR) * RPL;
-    const int64_t wg_row0 = (int64_t)blockIdx.x * ROWS_WG;
+
+    constexpr int G = 64 / LPR;
+    const int64_t ntiles = (N + G - 1) / G;
+    const int64_t per_wg = (ntiles + gridDim.x - 1) / gridDim.x;
+    const int64_t tb = (int64_t)blockIdx.x * per_wg;
+    const int64_t te = min(ntiles, tb + per_wg);
+    if (tb >= te) return;
     if (e < 0 || e >= n_experts) {
         // An id outside [0, n_experts) cannot be reported to the host:
         // its outputs become quiet NaN.
         const float qnan = __builtin_nanf("");
         for (int k = 0; k < nmem; ++k)
-            for (int64_t row = wg_row0 + t; row < wg_row0 + ROWS_WG && row < N; row += kThreads)
+            for (int64_t row = tb * G + t; row < te * G && row < N; row += 64 * NW)
                 y[(int64_t)s_members[k] * N + row] = qnan;
         return;
     }
-    const uint8_t* We = Wx + (int64_t)e * estride;
+    const uint8_t* __restrict__ We = Wx + (int64_t)e * estride;
     float* xs = lds;
-    float* sx = lds + max_cols * nb * kXPad;
-    for (int c0 = 0; c0 < nmem; c0 += max_cols) {
-        const int w = min(max_cols, nmem - c0);
-        moe_chunk<F, LPR, RPL>(We, N, nb, wg_row0, x, xs_tok, xs_slot, top_k, s_members + c0, w, y, xs, sx);
+    float* sx = lds + BC * nb * kXPad;
+    for (int c0 = 0; c0 < nmem; c0 += BC) {
+        const int w = min(BC, nmem - c0);
+        const float* xcol[BC];
+#pragma unroll
+        for (int b = 0; b < BC; ++b) {
+            const int pr = s_members[c0 + (b < w ? b : 0)];
+            xcol[b] = x + (int64_t)(pr / top_k) * xs_tok + (int64_t)(pr % top_k) * xs_slot;
+        }
+        if (c0 == 0 && XU > 0 && xvec)
+            moe_chunk<F, BC, LPR, NW, XU>(We, N, nb, tb, te, xcol, w, true, s_members + c0, y, xs, sx);
+        else
+            moe_chunk<F, BC, LPR, NW, 0>(We, N, nb, tb, te, xcol, w, xvec != 0, s_members + c0, y, xs, sx);
     }
 }
 
@@ -468,7 +527,6 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 }
 
 // ------------------------------------------------------------------ host
-constexpr int kRpl = 2;   // MoE rows per lane
 
 template <class F, int B, int LPR, int XU, int NW>
 int32_t launch_b(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
@@ -489,7 +547,7 @@ int32_t launch_b(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ld
     const int64_t cap = (int64_t)device_cu_count() * per_cu;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, cap));
     const int xvec = (aligned(x, 16) && ldx % 4 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nb, x, ldx, y, ldy, xvec);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nb, x, ldx, y, ldy, xvec, PairRoute{});
     return check_launch("qmv");
 }
 
@@ -597,10 +655,12 @@ int32_t launch_batch(const uint8_t* W, int64_t N, int nb, const float* x, int64_
     case 2: return launch_lpr<F, 2, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
     case 3: return launch_lpr<F, 3, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
     case 4: return launch_lpr<F, 4, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
-    case 5: return launch_lpr<F, 5, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
-    case 6: return launch_lpr<F, 6, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
-    case 7: return launch_lpr<F, 7, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
-    default: return launch_lpr<F, 8, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    // 5..8 columns: the staged activations fill most of the LDS, so one
+    // workgroup per CU; 16 waves share them (measured +13..26% at 8).
+    case 5: return launch_lpr<F, 5, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
+    case 6: return launch_lpr<F, 6, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
+    case 7: return launch_lpr<F, 7, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
+    default: return launch_lpr<F, 8, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
     }
 }
 
@@ -651,24 +711,95 @@ int32_t dequant(const void* W, int64_t N, int64_t K, float* out, void* stream) {
     return check_launch("qmv_dequant");
 }
 
-template <class F, int LPR>
-int32_t launch_moe_lpr(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
-                       int P, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int max_cols,
-                       hipStream_t st) {
-    auto kern = moe_kernel<F, LPR, kRpl>;
+// The grid is (range, group): group u serves the u-th distinct routed id
+// (at most P = batch * top_k groups; the extra ones exit at once), and the
+// ranges split each expert's row tiles so that ranges x expected groups
+// fill the GPU once.
+template <class F, int BC, int LPR, int XU>
+int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
+                   int P, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
+                   hipStream_t st) {
+    constexpr int NW = 4;
+    auto kern = moe_kernel<F, BC, LPR, NW, XU>;
+    static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
+    if (!dyn_max) {
+        hipFuncAttributes fa;
+        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) != hipSuccess)
+            return fail(QMV_EHIP, "qmv_moe: cannot query the kernel: %s", hipGetErrorString(hipGetLastError()));
+        const size_t m = kLdsMax - fa.sharedSizeBytes;
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)m) != hipSuccess)
+            return fail(QMV_EHIP, "qmv_moe: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
+        dyn_max = m;
+    }
+    const size_t lds = (size_t)BC * nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    if (lds > dyn_max)
+        return fail(QMV_EINVAL, "qmv_moe: n_cols %d too large for one activation row in LDS", nb * 32);
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
+    const int64_t ntiles = (N + 64 / LPR - 1) / (64 / LPR);
+    const int64_t groups = std::max(1, std::min(P, n_experts));
+    const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(ntiles, (int64_t)device_cu_count() * per_cu / groups));
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)P), dim3(64 * NW), lds, st, Wx, estride, n_experts, N, nb,
+                       ids, P, top_k, x, xs_tok, xs_slot, y, xvec);
+    return check_launch("qmv_moe");
+}
+
+// Member columns per pass: one token routes to an expert once, so batch 1
+// needs one column; at batches 2..8 a routed expert of 128 has about 1.4
+// members on average, and 2 columns per pass (more passes when an expert
+// has more) measured fastest: the staged rows stay small, so more
+// workgroups fit.  Activations staged straight-line (XU 16-byte loads per
+// thread) up to K = 8192.
+template <class F, int LPR, int XU>
+int32_t launch_moe_bc(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
+                      int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
+                      hipStream_t st) {
+    const int P = batch * top_k;
+    const size_t per_col = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    if (batch > 1 && 2 * per_col + kMoeStaticLds <= (size_t)kLdsMax)
+        return launch_moe<F, 2, LPR, XU>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec, st);
+    return launch_moe<F, 1, LPR, XU>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec, st);
+}
+
+// Batch 1: the pairs of one token need no grouping (a duplicated id only
+// streams that expert twice), so grid row p runs the dense kernel on
+// expert ids[p] with no prologue at all.
+template <class F, int LPR, int XU>
+int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
+                         int top_k, const float* x, int64_t xs_slot, float* y, hipStream_t st) {
+    constexpr int NW = 4;
+    auto kern = qmv_kernel<F, 1, LPR, 1, XU, NW, 2, true>;
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsMax - kMoeStaticLds) != hipSuccess)
+                                kLdsMax) != hipSuccess)
             return fail(QMV_EHIP, "qmv_moe: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
         attr_set = true;
     }
-    constexpr int rows_per_wg = kWaves * (64 / LPR) * kRpl;
-    const size_t lds = (size_t)max_cols * nb * (kXPad + 1) * sizeof(float);
-    const dim3 grid((unsigned)((N + rows_per_wg - 1) / rows_per_wg), (unsigned)P);
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), lds, st, Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok,
-                       xs_slot, y, max_cols);
+    const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
+    const int64_t tiles = (N + NW * (64 / LPR) - 1) / (NW * (64 / LPR));
+    const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu / top_k));
+    const PairRoute route{ids, estride, xs_slot, n_experts};
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)top_k), dim3(64 * NW), lds, st, Wx, N, nb, x, (int64_t)nb * 32,
+                       y, N, 1, route);
     return check_launch("qmv_moe");
+}
+
+template <class F, int LPR>
+int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
+                      int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
+                      hipStream_t st) {
+    const int K4 = nb * 8;   // 16-byte chunks of one activation row; 256 threads
+    if (batch == 1 && xvec && K4 <= 4 * 256)
+        return launch_moe_pairs<F, LPR, 4>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
+    if (batch == 1 && xvec && K4 <= 16 * 256)
+        return launch_moe_pairs<F, LPR, 16>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
+    if (K4 <= 2 * 256)
+        return launch_moe_bc<F, LPR, 2>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
+    if (K4 <= 8 * 256)
+        return launch_moe_bc<F, LPR, 8>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
+    return launch_moe_bc<F, LPR, 0>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
 }
 
 template <class F>
@@ -693,15 +824,15 @@ int32_t moe(const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64
     if (xs_slot < 0) return fail(QMV_EINVAL, "%s: x_stride_slot must be >= 0", name);
     if (!aligned(Wx, 4) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ids, 4))
         return fail(QMV_EALIGN, "%s: W_experts, x, y and expert_ids must be 4-byte aligned", name);
-    const int64_t per_col = nb * (kXPad + 1) * (int64_t)sizeof(float);
-    const int max_cols = (int)std::min<int64_t>(8, (kLdsMax - kMoeStaticLds) / per_col);
-    if (max_cols < 1) return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
-    const int P = batch * top_k;
+    const int64_t per_col = nb * (kXPad + (F::kNeedSx ? 1 : 0)) * (int64_t)sizeof(float);
+    if (per_col + kMoeStaticLds > kLdsMax)
+        return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
     const uint8_t* W8 = static_cast<const uint8_t*>(Wx);
     hipStream_t st = as_stream(stream);
-    if (nb >= 64) return launch_moe_lpr<F, 64>(W8, estride, n_experts, N, (int)nb, ids, P, top_k, x, xs_tok, xs_slot, y, max_cols, st);
-    if (nb >= 32) return launch_moe_lpr<F, 32>(W8, estride, n_experts, N, (int)nb, ids, P, top_k, x, xs_tok, xs_slot, y, max_cols, st);
-    return launch_moe_lpr<F, 8>(W8, estride, n_experts, N, (int)nb, ids, P, top_k, x, xs_tok, xs_slot, y, max_cols, st);
+    const int xvec = (aligned(x, 16) && xs_tok % 4 == 0 && xs_slot % 4 == 0) ? 1 : 0;
+    if (nb >= 64) return launch_moe_xu<F, 64>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
+    if (nb >= 32) return launch_moe_xu<F, 32>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
+    return launch_moe_xu<F, 8>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
 }
 
 }  // namespace
