@@ -378,6 +378,51 @@ def test_moe_routing_edge_cases(env, case):
             assert np.array_equal(y1[0].view(np.uint32), y[b, s].view(np.uint32))
 
 
+@pytest.mark.parametrize("case", ["dup_invalid", "long_rows", "unaligned_slots"])
+def test_moe_batch1_paths(env, case):
+    """One token: its pairs run as separate grid rows of the dense kernel
+    (no grouping; a duplicated id streams that expert twice), or, when the
+    activations cannot be staged straight-line (rows of > 16384 columns, or
+    slot strides that break 16-byte alignment), through the grouping
+    kernel.  Either way each valid pair equals the single-expert dense call
+    bitwise, invalid ids give NaN, and the result is within the bound."""
+    torch, qmv = env
+    fmt = "q4_1"
+    E = 5
+    if case == "dup_invalid":
+        N, K, ids, slot_pad = 200, 2048, np.array([[3, 3, 9, -1, 0, 3]], dtype=np.int32), 0
+    elif case == "long_rows":
+        N, K, ids, slot_pad = 40, 16416, np.array([[1, 4, 1]], dtype=np.int32), 0
+    else:
+        N, K, ids, slot_pad = 64, 768, np.array([[2, 0, 2, 4]], dtype=np.int32), 1
+    per = wl.block_bytes(fmt, N, K)
+    Wq = wl.quant_weights(fmt, f"moe/b1/{case}", E * N, K).reshape(E, per)
+    Wall = Wq.reshape(-1)
+    T = ids.shape[1]
+    xs = wl.activations(f"moe/b1/x/{case}", T, K)
+    ld = K + slot_pad                     # slot stride in floats
+    xbuf = np.zeros((T, ld), dtype=np.float32)
+    xbuf[:, :K] = xs
+    xd = torch.from_numpy(xbuf.reshape(-1)).to("cuda:0")
+    Wd, idsd = dev(torch, Wall), dev(torch, ids)
+    yd = torch.full((T * N,), float("nan"), device="cuda:0")
+    rc = qmv.lib().qmv_moe(qmv.FORMATS[fmt], Wd.data_ptr(), per, E, N, K, idsd.data_ptr(), 1, T, xd.data_ptr(),
+                           T * ld, ld, yd.data_ptr(), None)
+    assert rc == 0, qmv.last_error()
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy().reshape(1, T, N)
+    valid = (ids >= 0) & (ids < E)
+    assert np.all(np.isnan(y[~valid]))
+    for s in range(T):
+        if not valid[0, s]:
+            continue
+        e = int(ids[0, s])
+        y1 = gpu_matvec(env, fmt, Wq[e], N, K, xs[s][None])
+        assert np.array_equal(y1[0].view(np.uint32), y[0, s].view(np.uint32)), (case, s)
+        yr, S = oracle.matvec(fmt, Wq[e], N, K, xs[s][None])
+        assert_tol(y[0, s][None], yr, S, (case, s))
+
+
 @pytest.mark.parametrize("fmt", FMTS)
 def test_moe_formats_and_invalid_ids(env, fmt):
     E, N, K = 5, 70, 256
