@@ -45,8 +45,8 @@ TRAFFIC_RECORD = {
     "sources": ["bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
                 "bandwidth_bound_block_amd/csrc/qmv_block_decode.h",
                 "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-    "sha256": "5a06f277d8a9f7688a3409f7a41e6844ece692f21be5129ebaa81eb0b5e5e9d3",
-    "bytes_per_launch": 83478652,
+    "sha256": "59e378609dd9c1e4c295a2b3cb0541673973b4e8899e8ae7e1fed6b976a73ad5",
+    "bytes_per_launch": 83476489,
 }
 
 
