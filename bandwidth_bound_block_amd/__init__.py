@@ -10,6 +10,8 @@ library has not been built.
 
 Entry points (same names as the C ABI):
   qmv_q8_0 / qmv_q4_0 / qmv_q4_1   float block-quantized matvec, batch 1..8
+  qmv_matvec_path                  the same with the kernel family chosen
+                                   (PATH_AUTO / PATH_FMA / PATH_MFMA)
   qmv_i8_requant                   int8 matvec + per-channel gemmlowp requant
   qmv_moe                          grouped MoE expert matvec
   qmv_dequant                      stored blocks -> fp32 (test/inspection aid)
@@ -17,7 +19,8 @@ Entry points (same names as the C ABI):
 import ctypes
 import os
 
-__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_i8_requant", "qmv_moe",
+__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "PATH_AUTO", "PATH_FMA",
+           "PATH_MFMA", "qmv_i8_requant", "qmv_moe",
            "qmv_dequant", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
            "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
 
@@ -27,6 +30,7 @@ _LIB_PATH = os.path.join(_HERE, "libqmv.so")
 Q8_0, Q4_0, Q4_1 = 0, 1, 2
 FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1}
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}
+PATH_AUTO, PATH_FMA, PATH_MFMA = 0, 1, 2
 _ERRORS = {1: "QMV_EINVAL", 2: "QMV_EALIGN", 3: "QMV_EUNSUPPORTED", 4: "QMV_EHIP"}
 CHAIN_WORKSPACE_BYTES = 40960
 
@@ -58,6 +62,8 @@ def _open():
         f = getattr(L, name)
         f.argtypes = [P, i64, i64, P, i64, i32, P, i64, P]
         f.restype = i32
+    L.qmv_matvec_path.argtypes = [ctypes.c_int, P, i64, i64, P, i64, i32, P, i64, i32, P]
+    L.qmv_matvec_path.restype = i32
     L.qmv_i8_requant.argtypes = [P, i64, i64, P, i64, i32, P, P, P, i64, P]
     L.qmv_i8_requant.restype = i32
     L.qmv_moe.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P, i64, i64, P, P]
@@ -159,6 +165,18 @@ def qmv_q4_0(W, n_rows, n_cols, x, y=None, stream=None):
 def qmv_q4_1(W, n_rows, n_cols, x, y=None, stream=None):
     """y[b] = DEQ_Q4_1(W) @ x[b]; x float32 [K] or [B, K] (B <= 8)."""
     return _matvec(_lib.qmv_q4_1, Q4_1, W, n_rows, n_cols, x, y, stream)
+
+
+def qmv_matvec_path(fmt, W, n_rows, n_cols, x, path, y=None, stream=None):
+    """As qmv_q8_0/q4_0/q4_1 for format fmt (Q8_0, Q4_0, Q4_1 or its name)
+    with the kernel family `path` (PATH_AUTO, PATH_FMA or PATH_MFMA)."""
+    f = FORMATS.get(fmt, fmt)
+    if f not in BLOCK_BYTES:
+        raise ValueError(f"unknown format {fmt!r}")
+
+    def cfn(*a):
+        return _lib.qmv_matvec_path(f, *a[:-1], path, a[-1])
+    return _matvec(cfn, f, W, n_rows, n_cols, x, y, stream)
 
 
 def qmv_i8_requant(W, x, mult, shift, y=None, stream=None):

@@ -680,11 +680,27 @@ int32_t check_common(const char* name, const void* W, int64_t N, int64_t K, cons
 }
 
 template <class F>
+constexpr qmv_fmt fmt_of() {
+    return F::kBytes == 34 ? QMV_Q8_0 : (F::kBytes == 18 ? QMV_Q4_0 : QMV_Q4_1);
+}
+
+// path: QMV_PATH_AUTO, QMV_PATH_FMA (the FMA kernels) or QMV_PATH_MFMA (the
+// matrix-core kernel; QMV_EUNSUPPORTED where it does not apply).
+template <class F>
 int32_t matvec(const char* name, const void* W, int64_t N, int64_t K, const float* x, int64_t ldx, int32_t batch,
-               float* y, int64_t ldy, void* stream) {
+               float* y, int64_t ldy, void* stream, int32_t path = QMV_PATH_AUTO) {
     int32_t rc = check_common(name, W, N, K, x, ldx, batch, y, ldy);
     if (rc != QMV_OK) return rc;
     const int nb = (int)(K / 32);
+    if (path == QMV_PATH_MFMA || (path == QMV_PATH_AUTO && use_mfma(fmt_of<F>(), N, nb, batch))) {
+        if (batch_matvec_mma(fmt_of<F>(), static_cast<const uint8_t*>(W), N, nb, x, ldx, batch, y, ldy,
+                             as_stream(stream), 0, &rc))
+            return rc == QMV_OK ? ok() : rc;
+        if (path == QMV_PATH_MFMA)
+            return fail(QMV_EUNSUPPORTED,
+                        "%s: the matrix-core path needs batch 2..8, n_cols a multiple of 256, W and x 16-byte "
+                        "aligned and ldx a multiple of 4", name);
+    }
     // The staged activation block must fit in LDS; wider batches than fit
     // are processed in column groups (each group re-reads W).
     const int per_col = nb * (kXPad + (F::kNeedSx ? 1 : 0)) * (int)sizeof(float);
@@ -860,6 +876,17 @@ extern "C" int32_t qmv_q4_0(const void* W, int64_t n_rows, int64_t n_cols, const
 extern "C" int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols, const float* x, int64_t ldx, int32_t batch,
                             float* y, int64_t ldy, void* stream) {
     return qmv::matvec<qmv::Q4_1>("qmv_q4_1", W, n_rows, n_cols, x, ldx, batch, y, ldy, stream);
+}
+extern "C" int32_t qmv_matvec_path(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols, const float* x,
+                                   int64_t ldx, int32_t batch, float* y, int64_t ldy, int32_t path, void* stream) {
+    if (path != QMV_PATH_AUTO && path != QMV_PATH_FMA && path != QMV_PATH_MFMA)
+        return qmv::fail(QMV_EINVAL, "qmv_matvec_path: unknown path %d", (int)path);
+    switch (fmt) {
+    case QMV_Q8_0: return qmv::matvec<qmv::Q8_0>("qmv_matvec_path", W, n_rows, n_cols, x, ldx, batch, y, ldy, stream, path);
+    case QMV_Q4_0: return qmv::matvec<qmv::Q4_0>("qmv_matvec_path", W, n_rows, n_cols, x, ldx, batch, y, ldy, stream, path);
+    case QMV_Q4_1: return qmv::matvec<qmv::Q4_1>("qmv_matvec_path", W, n_rows, n_cols, x, ldx, batch, y, ldy, stream, path);
+    default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_matvec_path: unknown format %d", (int)fmt);
+    }
 }
 extern "C" int32_t qmv_dequant(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols, float* out, void* stream) {
     switch (fmt) {

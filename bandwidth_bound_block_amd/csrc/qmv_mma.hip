@@ -1,0 +1,462 @@
+// Batch 2..8 block-quantized matvec on the matrix cores (gfx950).
+//
+// The block dot of the quantized-matvec pages (dequantize in registers, dot
+// in f32, per-block scale) turns compute-bound once several activation
+// columns share each weight: the FMA kernels spend B multiply-adds per
+// weight.  Here one v_mfma_f32_16x16x32_bf16 computes, for one 32-weight
+// block column, the code dots of 16 rows against 16 activation columns, and
+// the per-block scale is applied to its four results per lane afterwards.
+//
+// Exactness of the operands:
+//  * codes (Q8_0 int8, Q4_x nibbles 0..15) have at most 8 significant bits:
+//    exact in bf16;
+//  * each activation x is split into two bf16 pieces, hi = RN(x) and
+//    lo = RN(x - hi) (x - hi is exact in f32), so |x - hi - lo| <= 2^-16 |x|;
+//  * bf16 products are exact in f32 and the matrix core sums in f32.
+// So each row's result differs from the exact dequantize-then-dot value by at
+// most 2^-16 of sum_j |w_j x_j| plus f32 summation error.
+//
+// MFMA roles: A (16 x 32) = activation pieces, row bp = p*B + b for piece p
+// of batch column b (rows past 2B are ignored); B (32 x 16) = codes of 16 weight
+// rows.  Lane l supplies A row l%16 and B column l%16 for k-group l/16, and
+// holds D[4*(l/16)+i][l%16], i = 0..3: weight row l%16, so the lane scales
+// its four results by the fp16 scale of the block of its own row.  Which
+// element of the block sits in which k-slot is free as long as A and B agree;
+// Mma<F> fixes it per format (x0/x1 below).
+//
+// Work split: 16-row tiles; a workgroup of NW waves handles NW/KP tiles at a
+// time (a tile group) and the KP waves of a tile take interleaved steps of 8
+// blocks along the row; their partial sums are combined through LDS in a
+// fixed order.  The activation pieces of up to KC blocks are staged in LDS
+// (re-staged per tile group when the row needs several chunks).  Each wave
+// streams a step (16 rows x 8 blocks) as whole 16-byte chunks into its LDS
+// slot, with the next step's loads in flight in registers.
+#include <type_traits>
+
+#include "qmv_block_decode.h"
+
+namespace qmv {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Calls fn(std::integral_constant<int, J>{}) for J = 0..N-1 in order.
+template <class Fn, int... Js>
+__device__ __forceinline__ void static_for(std::integer_sequence<int, Js...>, Fn&& fn) {
+    (fn(std::integral_constant<int, Js>{}), ...);
+}
+
+// Keeps the compiler from folding a nibble mask into per-element bit-field
+// extracts (one v_cvt_f32_ubyte<k> per element instead of two instructions).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
+// bf16 pair {a, b} (a in the low half) from two floats that are exact in bf16.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    return __builtin_amdgcn_perm(fbits(b), fbits(a), 0x07060302u);
+}
+__device__ __forceinline__ uint32_t lds4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
+
+__device__ __forceinline__ void nibble_operand(uint32_t c, uint32_t (&b)[4]) {
+    const uint32_t lo = opaque(c & 0x0f0f0f0fu), hi = opaque((c >> 4) & 0x0f0f0f0fu);
+    b[0] = pack_bf16(ubyte(lo, 0), ubyte(lo, 1));
+    b[1] = pack_bf16(ubyte(lo, 2), ubyte(lo, 3));
+    b[2] = pack_bf16(ubyte(hi, 0), ubyte(hi, 1));
+    b[3] = pack_bf16(ubyte(hi, 2), ubyte(hi, 3));
+}
+
+// Per-format B operand: lane group g (0..3) of weight row r gets 8 codes of
+// block J of the row's step (the step's bytes at `row`, in LDS, 16-byte
+// aligned), as packed bf16, plus the block's scale (and minimum).
+// x0(g), x1(g): the block elements of those 8 codes, as two runs of 4.
+template <class F> struct Mma;
+
+template <> struct Mma<Q8_0> {
+    static constexpr bool kSums = false;     // the term needs no activation sums
+    static constexpr float kOutScale = 1.f;
+    __device__ static constexpr int x0(int g) { return 8 * g; }
+    __device__ static constexpr int x1(int g) { return 8 * g + 4; }
+    // codes q[8g..8g+7] = bytes 2+8g..9+8g of the block; 34j = 2j (mod 4)
+    template <int J>
+    __device__ static void operand(const uint8_t* row, int g, uint32_t (&b)[4], float& d, float&) {
+        const uint8_t* blk = row + 34 * J;
+        uint32_t c0, c1;
+        if constexpr ((J & 1) == 0) {
+            const uint8_t* p = blk + 8 * g;     // 4-aligned; codes start 2 bytes in
+            const uint32_t w0 = lds4(p), w1 = lds4(p + 4), w2 = lds4(p + 8);
+            c0 = __builtin_amdgcn_alignbyte(w1, w0, 2);
+            c1 = __builtin_amdgcn_alignbyte(w2, w1, 2);
+        } else {
+            const uint8_t* p = blk + 2 + 8 * g;  // 4-aligned
+            c0 = lds4(p);
+            c1 = lds4(p + 4);
+        }
+        d = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk));
+        b[0] = pack_bf16(sbyte(c0, 0), sbyte(c0, 1));
+        b[1] = pack_bf16(sbyte(c0, 2), sbyte(c0, 3));
+        b[2] = pack_bf16(sbyte(c1, 0), sbyte(c1, 1));
+        b[3] = pack_bf16(sbyte(c1, 2), sbyte(c1, 3));
+    }
+    __device__ static float term(float acc, float d, float, float dot, float) { return __builtin_fmaf(d, dot, acc); }
+};
+
+template <> struct Mma<Q4_0> {
+    static constexpr bool kSums = false;
+    static constexpr float kOutScale = 0.0625f;   // the operand carries the codes times 16
+    __device__ static constexpr int x0(int g) { return 4 * g; }
+    __device__ static constexpr int x1(int g) { return 16 + 4 * g; }
+    // qs[4g..4g+3] = bytes 2+4g..5+4g of the block: elements 4g..4g+3 (low
+    // nibbles) and 16+4g..19+4g (high nibbles); 18j = 2j (mod 4).  A nibble c
+    // placed in the top half of a byte with its top bit flipped reads as the
+    // signed byte 16 (c - 8), so one sign-extending convert per code gives
+    // the offset code times 16 (exact in bf16; the 16 is taken out once per
+    // output, exactly).
+    template <int J>
+    __device__ static void operand(const uint8_t* row, int g, uint32_t (&b)[4], float& d, float&) {
+        const uint8_t* blk = row + 18 * J;
+        uint32_t c;
+        if constexpr ((J & 1) == 0) {
+            const uint8_t* p = blk + 4 * g;
+            c = __builtin_amdgcn_alignbyte(lds4(p + 4), lds4(p), 2);
+        } else {
+            c = lds4(blk + 2 + 4 * g);
+        }
+        d = half_bits_to_float(*reinterpret_cast<const uint16_t*>(blk));
+        const uint32_t lo = ((c << 4) & 0xf0f0f0f0u) ^ 0x80808080u, hi = (c & 0xf0f0f0f0u) ^ 0x80808080u;
+        b[0] = pack_bf16(sbyte(lo, 0), sbyte(lo, 1));
+        b[1] = pack_bf16(sbyte(lo, 2), sbyte(lo, 3));
+        b[2] = pack_bf16(sbyte(hi, 0), sbyte(hi, 1));
+        b[3] = pack_bf16(sbyte(hi, 2), sbyte(hi, 3));
+    }
+    // d * 16 * sum_e (c_e - 8) x_e
+    __device__ static float term(float acc, float d, float, float dot, float) { return __builtin_fmaf(d, dot, acc); }
+};
+
+template <> struct Mma<Q4_1> {
+    static constexpr bool kSums = true;      // the minimum multiplies the block sum of x
+    static constexpr float kOutScale = 1.f;
+    __device__ static constexpr int x0(int g) { return 4 * g; }
+    __device__ static constexpr int x1(int g) { return 16 + 4 * g; }
+    template <int J>
+    __device__ static void operand(const uint8_t* row, int g, uint32_t (&b)[4], float& d, float& m) {
+        const uint8_t* blk = row + 20 * J;   // always 4-aligned
+        const uint32_t dm = lds4(blk);
+        d = half_bits_to_float(dm);
+        m = half_bits_to_float(dm >> 16);
+        nibble_operand(lds4(blk + 4 + 4 * g), b);
+    }
+    // d * sum_e c_e x_e + m * sum_e x_e
+    __device__ static float term(float acc, float d, float m, float dot, float sx) {
+        return __builtin_fmaf(m, sx, __builtin_fmaf(d, dot, acc));
+    }
+};
+
+// A wave step: 16 rows x SB blocks, read as whole 16-byte chunks.
+template <class F, int SB>
+struct MmaStep {
+    static constexpr int kRowStep = SB * F::kBytes;
+    static constexpr int kChunksPerRow = kRowStep / 16;
+    static constexpr int kChunks = 16 * kChunksPerRow;
+    static constexpr int kLoads = (kChunks + 63) / 64;
+    static constexpr int kSlot = 16 * kRowStep;                 // LDS bytes per wave
+    static_assert(kRowStep % 16 == 0, "whole chunks per row step");
+    static_assert(kSlot >= 1024, "the slot also holds a wave's 16 x 16 partial sums");
+    struct Buf {
+        u32x4 v[kLoads];
+    };
+};
+
+// Splits x into bf16 pieces for blocks [b0, b0 + nbc) of every batch column
+// and stores them in the A-operand layout: row q = g*2B + bp (k-group g,
+// piece row bp) holds the 16-byte operand of each block of the chunk, kcp
+// entries apart (kcp odd: the 16 lanes of a k-group hit distinct banks).
+// For Q4_1 also the block sums of each piece row, as rows g of four floats
+// (piece rows 4g..4g+3).  Threads take (block, column, k-group) with the
+// group fastest, so the four groups of a block are neighbouring lanes.
+template <class F, int NT>
+__device__ __forceinline__ void stage_pieces(const float* __restrict__ x, int64_t ldx, int B, int b0, int nbc,
+                                             int kcp, uint8_t* xs, float* sxs) {
+    using M = Mma<F>;
+    const int n = nbc * B * 4;
+    for (int e = threadIdx.x; e < n; e += NT) {   // n and NT are multiples of 4: whole groups
+        const int g = e & 3, q = e >> 2, b = q % B, blk = q / B;
+        const float* src = x + b * ldx + 32 * (b0 + blk);
+        const float4 u = *reinterpret_cast<const float4*>(src + M::x0(g));
+        const float4 w = *reinterpret_cast<const float4*>(src + M::x1(g));
+        const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+        uint32_t hp[4], lp[4];
+        float sh = 0.f, sl = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const __bf16 h0 = static_cast<__bf16>(v[2 * k]), h1 = static_cast<__bf16>(v[2 * k + 1]);
+            const float f0 = static_cast<float>(h0), f1 = static_cast<float>(h1);
+            const __bf16 l0 = static_cast<__bf16>(v[2 * k] - f0), l1 = static_cast<__bf16>(v[2 * k + 1] - f1);
+            hp[k] = __builtin_bit_cast(uint16_t, h0) | (uint32_t)__builtin_bit_cast(uint16_t, h1) << 16;
+            lp[k] = __builtin_bit_cast(uint16_t, l0) | (uint32_t)__builtin_bit_cast(uint16_t, l1) << 16;
+            if constexpr (M::kSums) {
+                sh += f0;
+                sh += f1;
+                sl += static_cast<float>(l0);
+                sl += static_cast<float>(l1);
+            }
+        }
+        const int qh = g * 2 * B + b;   // hi piece row b, lo piece row B + b
+        *reinterpret_cast<u32x4*>(xs + (qh * kcp + blk) * 16) = u32x4{hp[0], hp[1], hp[2], hp[3]};
+        *reinterpret_cast<u32x4*>(xs + ((qh + B) * kcp + blk) * 16) = u32x4{lp[0], lp[1], lp[2], lp[3]};
+        if constexpr (M::kSums) {
+            // (s0 + s1) + (s2 + s3) in every lane of the group (addition commutes)
+            sh += __shfl_xor(sh, 1);
+            sh += __shfl_xor(sh, 2);
+            sl += __shfl_xor(sl, 1);
+            sl += __shfl_xor(sl, 2);
+            if (g == 0) {
+                sxs[((b >> 2) * kcp + blk) * 4 + (b & 3)] = sh;
+                sxs[(((B + b) >> 2) * kcp + blk) * 4 + ((B + b) & 3)] = sl;
+            }
+        }
+    }
+}
+
+template <class F, int NW, int SB, int PD>
+__global__ __launch_bounds__(64 * NW) void qmv_mma_kernel(const uint8_t* __restrict__ W, int N, int nb,
+                                                          const float* __restrict__ x, int64_t ldx, int B,
+                                                          float* __restrict__ y, int64_t ldy, int KP, int KC) {
+    using M = Mma<F>;
+    using S = MmaStep<F, SB>;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int TPI = NW / KP, ts = wave / KP, kp = wave % KP;
+    const int nsteps = nb / SB;
+    const int tiles = (N + 15) >> 4;
+    const int ngroups = (tiles + TPI - 1) / TPI;
+    const int CS = KC / SB;                             // steps per chunk (a multiple of KP)
+    const int nchunks = (nsteps + CS - 1) / CS;
+    const int ipg = nsteps / KP;                        // items (steps) per wave per tile group
+    const int ipc = CS / KP;                            // items per wave per full chunk
+    const int kcp = KC | 1;                             // entries per piece row (odd)
+    const int64_t pitch = (int64_t)nb * F::kBytes;
+
+    uint8_t* xs = lds;                                            // [4 * 2B][kcp] x 16 B
+    float* sxs = reinterpret_cast<float*>(xs + 128 * B * kcp);    // [ceil(2B/4)][kcp] x 4 floats (Q4_1)
+    uint8_t* slots = reinterpret_cast<uint8_t*>(sxs) + (M::kSums ? 16 * ((2 * B + 3) / 4) * kcp : 0);
+    uint8_t* slot = slots + wave * S::kSlot;
+
+    // A operand: piece row bp = lane % 16, k-group lane / 16.  Lanes past the
+    // 2B piece rows read a valid row too; their results are never used.
+    const int g = lane >> 4, r = lane & 15;
+    const uint8_t* a_base = xs + (g * 2 * B + r % (2 * B)) * kcp * 16;
+    // block sums for the lane's result rows bp = 4g..4g+3 (rows past 2B unused)
+    const uint8_t* s_base = reinterpret_cast<const uint8_t*>(sxs) + (4 * g < 2 * B ? g : 0) * kcp * 16;
+
+    // Chunk k of a step: row k / kChunksPerRow, 16-byte column k % kChunksPerRow.
+    int roff[S::kLoads], coff[S::kLoads];
+#pragma unroll
+    for (int k = 0; k < S::kLoads; ++k) {
+        const int i = min(64 * k + lane, S::kChunks - 1);
+        roff[k] = i / S::kChunksPerRow;
+        coff[k] = 16 * (i % S::kChunksPerRow);
+    }
+    const int my_groups = (ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int total = my_groups > 0 ? my_groups * ipg : 0;
+
+    // Loads step n (past the last one: the last one again, so that every
+    // pipeline slot issues its loads unconditionally and the waits before
+    // each LDS copy count exactly the loads issued after it).
+    auto load = [&](int n, typename S::Buf& buf) __attribute__((always_inline)) {
+        n = min(n, total - 1);
+        const int it = blockIdx.x + (n / ipg) * gridDim.x;
+        const int s = kp + KP * (n % ipg);
+        const int row0 = 16 * (it * TPI + ts);
+        const uint8_t* base = W + (int64_t)s * S::kRowStep;
+#pragma unroll
+        for (int k = 0; k < S::kLoads; ++k) {
+            const int64_t row = min(row0 + roff[k], N - 1);   // rows past the end re-read the last row
+            buf.v[k] = *reinterpret_cast<const u32x4*>(base + row * pitch + coff[k]);
+        }
+    };
+    auto to_slot = [&](const typename S::Buf& buf) __attribute__((always_inline)) {
+#pragma unroll
+        for (int k = 0; k < S::kLoads; ++k)
+            if (64 * k + 64 <= S::kChunks || 64 * k + lane < S::kChunks)
+                *reinterpret_cast<u32x4*>(slot + 16 * (64 * k + lane)) = buf.v[k];
+    };
+
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    struct Dot {
+        f32x4 dot, sx;
+        float d, m;
+    };
+    // Operands of block J of the step and its MFMA; the scaling follows one
+    // block later, so the matrix core's latency is covered.
+    auto issue = [&](auto jc, int cb) __attribute__((always_inline)) {
+        constexpr int J = decltype(jc)::value;
+        Dot o;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(a_base + cb * 16);
+        o.sx = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (M::kSums) o.sx = *reinterpret_cast<const f32x4*>(s_base + cb * 16);
+        uint32_t bw[4];
+        o.m = 0.f;
+        M::template operand<J>(slot + r * S::kRowStep, g, bw, o.d, o.m);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        o.dot = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bw), z, 0, 0, 0);
+        return o;
+    };
+    auto finish = [&](const Dot& o) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = M::term(acc[i], o.d, o.m, o.dot[i], o.sx[i]);
+    };
+
+    auto item = [&](int n) __attribute__((always_inline)) {
+        const int nig = n % ipg;
+        const int c = nig / ipc;
+        if (nig % ipc == 0 && (nchunks > 1 || n == 0)) {
+            const int b0 = c * KC;
+            __syncthreads();
+            stage_pieces<F, 64 * NW>(x, ldx, B, b0, min(KC, nb - b0), kcp, xs, sxs);
+            __syncthreads();
+        }
+        const int cb = (kp + KP * nig) * SB - c * KC;   // first block of the step in the chunk
+        Dot dots[SB];
+        static_for(std::make_integer_sequence<int, SB>{}, [&](auto jc) __attribute__((always_inline)) {
+            constexpr int J = decltype(jc)::value;
+            dots[J] = issue(jc, cb + J);
+            if constexpr (J > 0) finish(dots[J - 1]);
+        });
+        finish(dots[SB - 1]);
+        if (nig == ipg - 1) {
+            // tile group done: partials of every wave through the slots
+            const int it = blockIdx.x + (n / ipg) * gridDim.x;
+            __syncthreads();
+            *reinterpret_cast<f32x4*>(slot + (r * 16 + 4 * g) * 4) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            __syncthreads();
+            const int outs = TPI * 16 * B;
+            for (int t = tid; t < outs; t += 64 * NW) {
+                const int tsl = t / (16 * B), rem = t % (16 * B), b = rem >> 4, rr = rem & 15;
+                const int row = 16 * (it * TPI + tsl) + rr;
+                float v = 0.f;
+                for (int q = 0; q < KP; ++q) {
+                    const float* pw = reinterpret_cast<const float*>(slots + (tsl * KP + q) * S::kSlot) + rr * 16;
+                    v += pw[b];
+                    v += pw[B + b];
+                }
+                if (row < N) y[b * ldy + row] = v * M::kOutScale;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = 0.f;
+        }
+    };
+
+    // PD register buffers: the loads of the next PD - 1 steps are in flight
+    // while a step is computed.
+    if (total == 0) return;
+    typename S::Buf buf[PD];
+    static_for(std::make_integer_sequence<int, PD - 1>{}, [&](auto pc) __attribute__((always_inline)) {
+        load(decltype(pc)::value, buf[decltype(pc)::value]);
+    });
+    for (int n = 0; n < total; n += PD) {
+        bool done = false;
+        static_for(std::make_integer_sequence<int, PD>{}, [&](auto pc) __attribute__((always_inline)) {
+            constexpr int P = decltype(pc)::value;
+            if (done || n + P >= total) {
+                done = true;
+                return;
+            }
+            load(n + P + PD - 1, buf[(P + PD - 1) % PD]);
+            __builtin_amdgcn_sched_barrier(0);
+            to_slot(buf[P]);
+            item(n + P);
+        });
+    }
+}
+
+template <class F, int NW, int SB, int PD>
+bool launch_mma(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B, float* y, int64_t ldy,
+                hipStream_t st, int kp_force, int32_t* rc) {
+    using S = MmaStep<F, SB>;
+    if (nb % SB) return false;
+    const int nsteps = nb / SB;
+    const size_t fixed = (size_t)NW * S::kSlot;
+    // LDS per staged block (plus one block of padding per chunk)
+    const size_t per_blk = 128 * (size_t)B + (Mma<F>::kSums ? 16 * (size_t)((2 * B + 3) / 4) : 0);
+    if (fixed + (SB + 1) * per_blk > (size_t)kLdsMax) return false;
+    const int64_t tiles = (N + 15) / 16;
+    const int cus = device_cu_count();
+    int KP = 1;
+    if (kp_force > 0) {
+        KP = kp_force;
+        if (NW % KP || nsteps % KP) return false;
+    } else {
+        while (KP < NW && nsteps % (2 * KP) == 0 && (tiles + NW / KP - 1) / (NW / KP) < cus) KP *= 2;
+    }
+    // steps per chunk: a multiple of KP (fewer waves per tile if KP steps do not fit)
+    int cs_max = 0;
+    for (;; KP /= 2) {
+        cs_max = (int)((kLdsMax - fixed) / per_blk - 1) / SB / KP * KP;
+        if (cs_max >= KP) break;
+        if (KP == 1) return false;
+    }
+    const int nchunks = (nsteps + cs_max - 1) / cs_max;
+    const int cs = ((nsteps + nchunks - 1) / nchunks + KP - 1) / KP * KP;
+    const int KC = cs * SB;
+    const size_t lds = fixed + (size_t)(KC | 1) * per_blk;
+
+    auto kern = qmv_mma_kernel<F, NW, SB, PD>;
+    static bool attr_set = false;   // benign race: every thread sets the same value
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                kLdsMax) != hipSuccess) {
+            *rc = fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
+            return true;
+        }
+        attr_set = true;
+    }
+    const int64_t ngroups = (tiles + NW / KP - 1) / (NW / KP);
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ngroups, (int64_t)cus * per_cu));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, (int)N, nb, x, ldx, B, y, ldy, KP, KC);
+    *rc = check_launch("qmv");
+    return true;
+}
+
+}  // namespace
+
+// Measured on the 8B decode shapes (4096..128256 rows, 4096 and 14336
+// columns, cache-cold): the matrix-core kernel is faster from batch 3 on
+// for every format, and at batch 2 for Q4_0 (at batch 2 the FMA kernels
+// still win most Q8_0 and Q4_1 shapes).
+bool use_mfma(qmv_fmt fmt, int64_t, int, int B) { return B >= 3 || (B == 2 && fmt == QMV_Q4_0); }
+
+namespace {
+// 16 waves per workgroup pay off on many tiles at batch 3..4 (the staged
+// activations leave room for 16 slots) and on very many tiles above that;
+// otherwise 8 (more tile groups than compute units, one activation chunk).
+template <class F>
+bool launch_mma_auto(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B, float* y,
+                     int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
+    const int64_t tiles = (N + 15) / 16;
+    int nw = variant >> 8;
+    if (nw == 0) nw = ((B >= 3 && B <= 4 && tiles >= 1024) || (B >= 5 && tiles >= 4096)) ? 16 : 8;
+    const int kp = variant & 0xff;
+    return nw == 16 ? launch_mma<F, 16, 8, 2>(W, N, nb, x, ldx, B, y, ldy, st, kp, rc)
+                    : launch_mma<F, 8, 8, 2>(W, N, nb, x, ldx, B, y, ldy, st, kp, rc);
+}
+}  // namespace
+
+bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B,
+                      float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
+    if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || !aligned(W, 16) || !aligned(x, 16) || ldx % 4) return false;
+    switch (fmt) {
+    case QMV_Q8_0: return launch_mma_auto<Q8_0>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
+    case QMV_Q4_0: return launch_mma_auto<Q4_0>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
+    case QMV_Q4_1: return launch_mma_auto<Q4_1>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
+    }
+    return false;
+}
+
+}  // namespace qmv

@@ -22,11 +22,17 @@
  *     are decoded exactly (subnormals included).
  *   - The batch width is 1..8: x holds `batch` activation rows, ldx elements
  *     apart; y holds `batch` output rows, ldy elements apart.  Each batch
- *     column is computed independently and gives bitwise the same result as
- *     a batch-1 call on that column alone.
+ *     column is computed independently of the others.  The FMA kernels give
+ *     a column bitwise the same result as a batch-1 call on it alone; the
+ *     matrix-core kernel (batch 2..8, see qmv_matvec_path) gives a column
+ *     bitwise the same result at every batch width 2..8 and position, and
+ *     agrees with the batch-1 result within the accuracy contract.
  *   - Float results are fp32, accumulated in fp32; they agree with the exact
  *     dequantize-then-dot within |err| <= 1e-4 * sum_j |w_ij x_j| + 1e-6 per
- *     output (the accuracy contract the tests enforce).
+ *     output (the accuracy contract the tests enforce).  The matrix-core
+ *     kernel multiplies the codes (exact in bf16) by the activations split
+ *     into two bf16 pieces, hi = RN(x) and lo = RN(x - hi), which represent
+ *     x to within 2^-16 |x|; the products are exact and summed in fp32.
  *
  * Return codes: QMV_OK on success, otherwise one of QMV_E*, with a message
  * from qmv_last_error().  All argument checks happen on the host before any
@@ -95,6 +101,25 @@ int32_t qmv_q4_0(const void* W, int64_t n_rows, int64_t n_cols,
 int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
                  float* y, int64_t ldy, void* stream);
+
+/*
+ * The float matvec above with the kernel family chosen by the caller (a test
+ * and tuning aid; the format entry points use QMV_PATH_AUTO):
+ *   QMV_PATH_AUTO  the entry point's own choice by shape and batch;
+ *   QMV_PATH_FMA   the FMA kernels (one fp32 multiply-add per weight and
+ *                  batch column, activations staged in LDS);
+ *   QMV_PATH_MFMA  the matrix-core kernel: 16 rows x one 32-weight block x
+ *                  up to 8 batch columns per v_mfma_f32_16x16x32_bf16 (the
+ *                  block scale applied to its results), for batch 2..8, n_cols
+ *                  a multiple of 256, W and x 16-byte aligned and ldx a
+ *                  multiple of 4; otherwise QMV_EUNSUPPORTED.
+ * Arguments and other errors as the format entry points; QMV_EINVAL for an
+ * unknown path, QMV_EUNSUPPORTED for an unknown fmt.
+ */
+enum { QMV_PATH_AUTO = 0, QMV_PATH_FMA = 1, QMV_PATH_MFMA = 2 };
+int32_t qmv_matvec_path(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols,
+                        const float* x, int64_t ldx, int32_t batch,
+                        float* y, int64_t ldy, int32_t path, void* stream);
 
 /*
  * All-integer matvec with per-output-channel requant ([ZEN]):

@@ -28,7 +28,7 @@ def qmv():
 
 def test_every_declared_symbol_is_exported(qmv):
     names = declared_functions()
-    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_i8_requant", "qmv_moe", "qmv_dequant",
+    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_i8_requant", "qmv_moe", "qmv_dequant",
             "qmv_chain", "qmv_last_error", "qmv_abi_version"} <= set(names)
     raw = ctypes.CDLL(qmv.library_path())
     for n in names:
@@ -65,6 +65,24 @@ def test_float_matvec_argument_errors(qmv, name):
     for args, code, word in cases:
         assert f(*args) == code, (args, qmv.last_error())
         assert word in qmv.last_error(), qmv.last_error()
+
+
+def test_matvec_path_argument_errors(qmv):
+    f = qmv.lib().qmv_matvec_path
+    ok = (A, 8, 256, A, 256, 2, A, 8)
+    assert f(qmv.Q4_0, *ok, 7, None) == EINVAL and "unknown path" in qmv.last_error()
+    assert f(9, *ok, qmv.PATH_AUTO, None) == EUNSUPPORTED
+    # the common checks come first, whatever the path
+    assert f(qmv.Q4_0, A, 8, 256, A, 256, 9, A, 8, qmv.PATH_MFMA, None) == EINVAL and "batch" in qmv.last_error()
+    assert f(qmv.Q8_0, A + 2, 8, 256, A, 256, 2, A, 8, qmv.PATH_FMA, None) == EALIGN
+    # shapes the matrix-core kernel does not take (no launch happens)
+    for args in [(A, 8, 256, A, 256, 1, A, 8),          # batch 1
+                 (A, 8, 224, A, 224, 2, A, 8),          # 7 blocks per row
+                 (A + 4, 8, 256, A, 256, 2, A, 8),      # W not 16-byte aligned
+                 (A, 8, 256, A + 4, 256, 2, A, 8),      # x not 16-byte aligned
+                 (A, 8, 256, A, 258, 2, A, 8)]:         # ldx not a multiple of 4
+        assert f(qmv.Q4_1, *args, qmv.PATH_MFMA, None) == EUNSUPPORTED, args
+        assert "matrix-core" in qmv.last_error()
 
 
 def test_int8_argument_errors(qmv):

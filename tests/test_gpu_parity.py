@@ -170,15 +170,24 @@ def test_one_hot_columns_exact(env, fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_batch_columns_equal_batch1_and_deterministic(env, fmt):
+    """The FMA kernels give every batch column bitwise the batch-1 result;
+    the entry point's own choice (the matrix-core kernel at this batch) is
+    deterministic and within the bound."""
+    torch, qmv = env
     N, K = 300, 4096
     W = wl.quant_weights(fmt, "t/b1/W", N, K)
     x = wl.activations("t/b1/x", 8, K)
-    y8 = gpu_matvec(env, fmt, W, N, K, x)
-    y8b = gpu_matvec(env, fmt, W, N, K, x)
-    assert np.array_equal(y8.view(np.uint32), y8b.view(np.uint32))
+    Wd, xd = dev(torch, W), dev(torch, x)
+    y8 = qmv.qmv_matvec_path(fmt, Wd, N, K, xd, qmv.PATH_FMA)
     for b in range(8):
-        y1 = gpu_matvec(env, fmt, W, N, K, x[b:b + 1])
-        assert np.array_equal(y1[0].view(np.uint32), y8[b].view(np.uint32)), b
+        y1 = qmv.qmv_matvec_path(fmt, Wd, N, K, xd[b:b + 1], qmv.PATH_FMA)
+        assert torch.equal(y1[0].view(torch.int32), y8[b].view(torch.int32)), b
+    ya = gpu_matvec(env, fmt, W, N, K, x)
+    yb = gpu_matvec(env, fmt, W, N, K, x)
+    assert np.array_equal(ya.view(np.uint32), yb.view(np.uint32))
+    yr, S = oracle.matvec(fmt, W, N, K, x)
+    assert_tol(ya, yr, S, fmt)
+    assert_tol(y8.cpu().numpy(), yr, S, fmt)
 
 
 def test_strided_activations(env):
@@ -194,6 +203,103 @@ def test_strided_activations(env):
     yr, S = oracle.matvec("q4_1", W, N, K, x)
     assert_tol(y[:, :N].cpu().numpy(), yr, S)
     assert np.all(y[:, N:].cpu().numpy() == 0)     # nothing written beyond ldy's row
+
+
+# ------------------------------------------------------------------ matrix-core path
+# n_cols multiples of 256 (whole 8-block steps); row counts with ragged
+# 16-row tiles; 8192 and 30720 columns need several activation chunks in
+# LDS at batch 8 (and 30720 at every width).
+MFMA_SHAPES = [(1, 256), (7, 512), (37, 768), (130, 1024), (65, 4096), (5, 14336), (300, 2048),
+               (17, 2304), (33, 8192), (3, 30720), (1000, 4096)]
+
+
+def mfma_matvec(env, fmt, Wd, N, K, xd, path=2):
+    torch, qmv = env
+    y = qmv.qmv_matvec_path(fmt, Wd, N, K, xd, path)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("B", [2, 3, 4, 7, 8])
+def test_mfma_path_small_shapes(env, fmt, B):
+    torch, qmv = env
+    for N, K in MFMA_SHAPES:
+        say(f"mfma {fmt} B={B} {N}x{K}")
+        W = wl.quant_weights(fmt, f"t/small/{N}x{K}", N, K)
+        x = wl.activations(f"t/small/x/{K}/{B}", B, K)
+        y = mfma_matvec(env, fmt, dev(torch, W), N, K, dev(torch, x)).cpu().numpy()
+        yr, S = oracle.matvec(fmt, W, N, K, x)
+        assert_tol(y, yr, S, (fmt, B, N, K))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_path_random_bytes_and_scales(env, fmt):
+    """Arbitrary codes and finite fp16 scales (subnormal to 65504), and
+    activations over many binades: the split into two bf16 pieces keeps the
+    bound."""
+    torch, _ = env
+    N, K, B = 45, 2048, 8
+    W = random_blocks(17, fmt, N, K)
+    g = np.random.default_rng(5)
+    x = (g.standard_normal((B, K)) * np.exp2(g.integers(-30, 30, size=(B, K)))).astype(np.float32)
+    y = mfma_matvec(env, fmt, dev(torch, W), N, K, dev(torch, x)).cpu().numpy()
+    yr, S = oracle.matvec(fmt, W, N, K, x)
+    assert_tol(y, yr, S, fmt)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_path_one_hot_exact(env, fmt):
+    """x = e_j: hi = 1, lo = 0, one code times 1 in the dot, so y_i = DEQ(W)_ij
+    exactly."""
+    torch, _ = env
+    N, K, B = 50, 1024, 8
+    W = random_blocks(3, fmt, N, K)
+    cols = [0, 1, 31, 32, 33, 511, 1000, 1023]
+    x = np.zeros((B, K), dtype=np.float32)
+    for b, j in enumerate(cols):
+        x[b, j] = 1.0
+    y = mfma_matvec(env, fmt, dev(torch, W), N, K, dev(torch, x)).cpu().numpy()
+    deq = oracle.dequant(fmt, W, N, K).astype(np.float32)
+    for b, j in enumerate(cols):
+        assert np.array_equal(y[b], deq[:, j]), (fmt, j)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_mfma_path_columns_independent_and_deterministic(env, fmt):
+    """A column's result depends on its own activations only: bitwise the same
+    at any batch width 2..8 and position, and run to run."""
+    torch, _ = env
+    N, K = 300, 4096
+    W = wl.quant_weights(fmt, "t/b1/W", N, K)
+    Wd = dev(torch, W)
+    x = wl.activations("t/b1/x", 8, K)
+    xd = dev(torch, x)
+    y8 = mfma_matvec(env, fmt, Wd, N, K, xd)
+    y8b = mfma_matvec(env, fmt, Wd, N, K, xd)
+    assert torch.equal(y8.view(torch.int32), y8b.view(torch.int32))
+    for b in range(8):
+        pair = dev(torch, np.stack([x[(b + 3) % 8], x[b]]))
+        y2 = mfma_matvec(env, fmt, Wd, N, K, pair)
+        assert torch.equal(y2[1].view(torch.int32), y8[b].view(torch.int32)), b
+    y5 = mfma_matvec(env, fmt, Wd, N, K, xd[3:8])
+    assert torch.equal(y5.view(torch.int32), y8[3:8].view(torch.int32))
+    yr, S = oracle.matvec(fmt, W, N, K, x)
+    assert_tol(y8.cpu().numpy(), yr, S, fmt)
+
+
+def test_mfma_path_strided(env):
+    torch, qmv = env
+    N, K, B = 70, 2048, 3
+    W = wl.quant_weights("q4_0", "t/str/W0", N, K)
+    xbig = wl.activations("t/str/x", B, K + 40)
+    xt = dev(torch, xbig)[:, :K]
+    y = torch.zeros((B, N + 5), dtype=torch.float32, device="cuda:0")
+    qmv.qmv_matvec_path("q4_0", dev(torch, W), N, K, xt, qmv.PATH_MFMA, y=y[:, :N])
+    torch.cuda.synchronize()
+    yr, S = oracle.matvec("q4_0", W, N, K, xbig[:, :K])
+    assert_tol(y[:, :N].cpu().numpy(), yr, S)
+    assert np.all(y[:, N:].cpu().numpy() == 0)
 
 
 # ------------------------------------------------------------------ full sizes
