@@ -39,7 +39,9 @@ namespace qmv {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Calls fn(std::integral_constant<int, J>{}) for J = 0..N-1 in order.
 template <class Fn, int... Js>
@@ -163,7 +165,7 @@ struct MmaStep {
     static constexpr int kLoads = (kChunks + 63) / 64;
     static constexpr int kSlot = 16 * kRowStep;                 // LDS bytes per wave
     static_assert(kRowStep % 16 == 0, "whole chunks per row step");
-    static_assert(kSlot >= 1024, "the slot also holds a wave's 16 x 16 partial sums");
+    static_assert(kSlot >= 16 * 20 * 4, "the slot also holds a wave's 16 x 16 partial sums (rows of 20)");
     struct Buf {
         u32x4 v[kLoads];
     };
@@ -174,48 +176,50 @@ struct MmaStep {
 // piece row bp) holds the 16-byte operand of each block of the chunk, kcp
 // entries apart (kcp odd: the 16 lanes of a k-group hit distinct banks).
 // For Q4_1 also the block sums of each piece row, as rows g of four floats
-// (piece rows 4g..4g+3).  Threads take (block, column, k-group) with the
-// group fastest, so the four groups of a block are neighbouring lanes.
+// (piece rows 4g..4g+3).  One thread per (column, block) with blocks
+// fastest: it does all four k-groups (the sums need no cross-lane step), and
+// neighbouring lanes write neighbouring 16-byte entries of a row.
 template <class F, int NT>
 __device__ __forceinline__ void stage_pieces(const float* __restrict__ x, int64_t ldx, int B, int b0, int nbc,
                                              int kcp, uint8_t* xs, float* sxs) {
     using M = Mma<F>;
-    const int n = nbc * B * 4;
-    for (int e = threadIdx.x; e < n; e += NT) {   // n and NT are multiples of 4: whole groups
-        const int g = e & 3, q = e >> 2, b = q % B, blk = q / B;
+    for (int idx = threadIdx.x; idx < nbc * B; idx += NT) {
+        const int b = idx / nbc, blk = idx - b * nbc;
         const float* src = x + b * ldx + 32 * (b0 + blk);
-        const float4 u = *reinterpret_cast<const float4*>(src + M::x0(g));
-        const float4 w = *reinterpret_cast<const float4*>(src + M::x1(g));
-        const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
-        uint32_t hp[4], lp[4];
-        float sh = 0.f, sl = 0.f;
+        float sums[2][4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const __bf16 h0 = static_cast<__bf16>(v[2 * k]), h1 = static_cast<__bf16>(v[2 * k + 1]);
-            const float f0 = static_cast<float>(h0), f1 = static_cast<float>(h1);
-            const __bf16 l0 = static_cast<__bf16>(v[2 * k] - f0), l1 = static_cast<__bf16>(v[2 * k + 1] - f1);
-            hp[k] = __builtin_bit_cast(uint16_t, h0) | (uint32_t)__builtin_bit_cast(uint16_t, h1) << 16;
-            lp[k] = __builtin_bit_cast(uint16_t, l0) | (uint32_t)__builtin_bit_cast(uint16_t, l1) << 16;
-            if constexpr (M::kSums) {
-                sh += f0;
-                sh += f1;
-                sl += static_cast<float>(l0);
-                sl += static_cast<float>(l1);
+        for (int g = 0; g < 4; ++g) {
+            const float4 u = *reinterpret_cast<const float4*>(src + M::x0(g));
+            const float4 w = *reinterpret_cast<const float4*>(src + M::x1(g));
+            const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
+            uint32_t hp[4], lp[4];
+            float sh = 0.f, sl = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // one packed convert per pair: hi = RN(x), then lo = RN(x - hi)
+                const float a = v[2 * k], c = v[2 * k + 1];
+                hp[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, c}, bf16x2));
+                const float ha = __builtin_bit_cast(float, hp[k] << 16);
+                const float hc = __builtin_bit_cast(float, hp[k] & 0xffff0000u);
+                lp[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, c - hc}, bf16x2));
+                if constexpr (M::kSums) {
+                    sh += ha;
+                    sh += hc;
+                    sl += __builtin_bit_cast(float, lp[k] << 16);
+                    sl += __builtin_bit_cast(float, lp[k] & 0xffff0000u);
+                }
             }
+            const int qh = g * 2 * B + b;   // hi piece row b, lo piece row B + b
+            *reinterpret_cast<u32x4*>(xs + (qh * kcp + blk) * 16) = u32x4{hp[0], hp[1], hp[2], hp[3]};
+            *reinterpret_cast<u32x4*>(xs + ((qh + B) * kcp + blk) * 16) = u32x4{lp[0], lp[1], lp[2], lp[3]};
+            sums[0][g] = sh;
+            sums[1][g] = sl;
         }
-        const int qh = g * 2 * B + b;   // hi piece row b, lo piece row B + b
-        *reinterpret_cast<u32x4*>(xs + (qh * kcp + blk) * 16) = u32x4{hp[0], hp[1], hp[2], hp[3]};
-        *reinterpret_cast<u32x4*>(xs + ((qh + B) * kcp + blk) * 16) = u32x4{lp[0], lp[1], lp[2], lp[3]};
         if constexpr (M::kSums) {
-            // (s0 + s1) + (s2 + s3) in every lane of the group (addition commutes)
-            sh += __shfl_xor(sh, 1);
-            sh += __shfl_xor(sh, 2);
-            sl += __shfl_xor(sl, 1);
-            sl += __shfl_xor(sl, 2);
-            if (g == 0) {
-                sxs[((b >> 2) * kcp + blk) * 4 + (b & 3)] = sh;
-                sxs[(((B + b) >> 2) * kcp + blk) * 4 + ((B + b) & 3)] = sl;
-            }
+            const float sh = (sums[0][0] + sums[0][1]) + (sums[0][2] + sums[0][3]);
+            const float sl = (sums[1][0] + sums[1][1]) + (sums[1][2] + sums[1][3]);
+            sxs[((b >> 2) * kcp + blk) * 4 + (b & 3)] = sh;
+            sxs[(((B + b) >> 2) * kcp + blk) * 4 + ((B + b) & 3)] = sl;
         }
     }
 }
@@ -266,17 +270,20 @@ __global__ __launch_bounds__(64 * NW) void qmv_mma_kernel(const uint8_t* __restr
 
     // Loads step n (past the last one: the last one again, so that every
     // pipeline slot issues its loads unconditionally and the waits before
-    // each LDS copy count exactly the loads issued after it).
+    // each LDS copy count exactly the loads issued after it).  pitch < 2^24.
     auto load = [&](int n, typename S::Buf& buf) __attribute__((always_inline)) {
         n = min(n, total - 1);
         const int it = blockIdx.x + (n / ipg) * gridDim.x;
         const int s = kp + KP * (n % ipg);
-        const int row0 = 16 * (it * TPI + ts);
-        const uint8_t* base = W + (int64_t)s * S::kRowStep;
+        // wave-uniform base row (clamped) and 32-bit lane offsets from it:
+        // rows past the end re-read the last row
+        const int brow = min(16 * (it * TPI + ts), N - 1);
+        const int lim = N - 1 - brow;
+        const uint8_t* base = W + (int64_t)brow * pitch + (int64_t)s * S::kRowStep;
 #pragma unroll
         for (int k = 0; k < S::kLoads; ++k) {
-            const int64_t row = min(row0 + roff[k], N - 1);   // rows past the end re-read the last row
-            buf.v[k] = *reinterpret_cast<const u32x4*>(base + row * pitch + coff[k]);
+            const uint32_t o = __umul24((uint32_t)min(roff[k], lim), (uint32_t)pitch) + (uint32_t)coff[k];
+            buf.v[k] = *reinterpret_cast<const u32x4*>(base + o);
         }
     };
     auto to_slot = [&](const typename S::Buf& buf) __attribute__((always_inline)) {
@@ -332,7 +339,8 @@ __global__ __launch_bounds__(64 * NW) void qmv_mma_kernel(const uint8_t* __restr
             // tile group done: partials of every wave through the slots
             const int it = blockIdx.x + (n / ipg) * gridDim.x;
             __syncthreads();
-            *reinterpret_cast<f32x4*>(slot + (r * 16 + 4 * g) * 4) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            // rows of 20 floats: the 16-byte stores and the reads below hit distinct banks
+            *reinterpret_cast<f32x4*>(slot + (r * 20 + 4 * g) * 4) = f32x4{acc[0], acc[1], acc[2], acc[3]};
             __syncthreads();
             const int outs = TPI * 16 * B;
             for (int t = tid; t < outs; t += 64 * NW) {
@@ -340,7 +348,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_mma_kernel(const uint8_t* __restr
                 const int row = 16 * (it * TPI + tsl) + rr;
                 float v = 0.f;
                 for (int q = 0; q < KP; ++q) {
-                    const float* pw = reinterpret_cast<const float*>(slots + (tsl * KP + q) * S::kSlot) + rr * 16;
+                    const float* pw = reinterpret_cast<const float*>(slots + (tsl * KP + q) * S::kSlot) + rr * 20;
                     v += pw[b];
                     v += pw[B + b];
                 }
@@ -450,7 +458,10 @@ bool launch_mma_auto(const uint8_t* W, int64_t N, int nb, const float* x, int64_
 
 bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B,
                       float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
-    if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || !aligned(W, 16) || !aligned(x, 16) || ldx % 4) return false;
+    const int64_t pitch = (int64_t)nb * (fmt == QMV_Q8_0 ? 34 : (fmt == QMV_Q4_0 ? 18 : 20));
+    if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || pitch >= (1 << 24) || !aligned(W, 16) || !aligned(x, 16) ||
+        ldx % 4)
+        return false;
     switch (fmt) {
     case QMV_Q8_0: return launch_mma_auto<Q8_0>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
     case QMV_Q4_0: return launch_mma_auto<Q4_0>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
