@@ -442,7 +442,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--sweeps", default="all",
-                    help="extra workloads: all, none, or a comma list of q4_0,q4_1,int8,moe")
+                    help="extra workloads: all, none, or a comma list of q8_0,q4_0,q4_1,int8,moe, or of "
+                         "FMT@B / FMT@Bf (one 8B sweep of format FMT at batch B, f: row-fused layout)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -493,7 +494,13 @@ def main():
         ["q8_0", "q4_0", "q4_1", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
-        if nm == "q8_0":
+        if "@" in nm:
+            fmt, spec = nm.split("@")
+            s = build_llama(torch, qmv, wl, fmt, int(spec.rstrip("f")), fused=spec.endswith("f"))
+            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+            del s
+            torch.cuda.empty_cache()
+        elif nm == "q8_0":
             for fused in (False, True):
                 s = build_llama(torch, qmv, wl, "q8_0", 1, fused=fused)
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
@@ -510,7 +517,8 @@ def main():
             record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
             del s
             torch.cuda.empty_cache()
-            for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
+            for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False), (2, True), (4, True),
+                             (8, True)):
                 s = build_llama(torch, qmv, wl, nm, B, fused=fused)
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
                 del s
