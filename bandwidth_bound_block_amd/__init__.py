@@ -12,6 +12,7 @@ Entry points (same names as the C ABI):
   qmv_q8_0 / qmv_q4_0 / qmv_q4_1   float block-quantized matvec, batch 1..8
   qmv_matvec_path                  the same with the kernel family chosen
                                    (PATH_AUTO / PATH_FMA / PATH_MFMA)
+  qmv_matvec_xt                    the same with fp32, fp16 or bf16 activations
   qmv_i8_requant                   int8 matvec + per-channel gemmlowp requant
   qmv_moe                          grouped MoE expert matvec
   qmv_dequant                      stored blocks -> fp32 (test/inspection aid)
@@ -19,8 +20,8 @@ Entry points (same names as the C ABI):
 import ctypes
 import os
 
-__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "PATH_AUTO", "PATH_FMA",
-           "PATH_MFMA", "qmv_i8_requant", "qmv_moe",
+__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
+           "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_moe",
            "qmv_dequant", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
            "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
 
@@ -31,6 +32,7 @@ Q8_0, Q4_0, Q4_1 = 0, 1, 2
 FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1}
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}
 PATH_AUTO, PATH_FMA, PATH_MFMA = 0, 1, 2
+X_F32, X_F16, X_BF16 = 0, 1, 2
 _ERRORS = {1: "QMV_EINVAL", 2: "QMV_EALIGN", 3: "QMV_EUNSUPPORTED", 4: "QMV_EHIP"}
 CHAIN_WORKSPACE_BYTES = 40960
 
@@ -64,6 +66,8 @@ def _open():
         f.restype = i32
     L.qmv_matvec_path.argtypes = [ctypes.c_int, P, i64, i64, P, i64, i32, P, i64, i32, P]
     L.qmv_matvec_path.restype = i32
+    L.qmv_matvec_xt.argtypes = [ctypes.c_int, P, i64, i64, P, i32, i64, i32, P, i64, i32, P]
+    L.qmv_matvec_xt.restype = i32
     L.qmv_i8_requant.argtypes = [P, i64, i64, P, i64, i32, P, P, P, i64, P]
     L.qmv_i8_requant.restype = i32
     L.qmv_moe.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P, i64, i64, P, P]
@@ -177,6 +181,33 @@ def qmv_matvec_path(fmt, W, n_rows, n_cols, x, path, y=None, stream=None):
     def cfn(*a):
         return _lib.qmv_matvec_path(f, *a[:-1], path, a[-1])
     return _matvec(cfn, f, W, n_rows, n_cols, x, y, stream)
+
+
+def qmv_matvec_xt(fmt, W, n_rows, n_cols, x, path=PATH_AUTO, y=None, stream=None):
+    """As qmv_matvec_path with x float32, float16 or bfloat16 [K] or [B, K]
+    (widened to fp32 exactly); y is float32."""
+    torch = _torch()
+    f = FORMATS.get(fmt, fmt)
+    if f not in BLOCK_BYTES:
+        raise ValueError(f"unknown format {fmt!r}")
+    xt = {torch.float32: X_F32, torch.float16: X_F16, torch.bfloat16: X_BF16}.get(x.dtype)
+    if xt is None:
+        raise ValueError(f"x must be float32, float16 or bfloat16 (got {x.dtype})")
+    _dev(W, "W", torch.uint8)
+    _dev(x, "x", x.dtype)
+    need = n_rows * (n_cols // 32) * BLOCK_BYTES[f]
+    if W.numel() * W.element_size() < need or not W.is_contiguous():
+        raise ValueError(f"W must be contiguous and hold {need} bytes")
+    x2, B, ldx = _rows2d(x, "x", n_cols)
+    if y is None:
+        y = torch.empty((B, n_rows), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    y2, By, ldy = _rows2d(y, "y", n_rows)
+    if By != B:
+        raise ValueError("y must have as many rows as x")
+    _check(_lib.qmv_matvec_xt(f, W.data_ptr(), n_rows, n_cols, x2.data_ptr(), xt, ldx, B, y2.data_ptr(), ldy, path,
+                              _stream(stream)))
+    return y
 
 
 def qmv_i8_requant(W, x, mult, shift, y=None, stream=None):

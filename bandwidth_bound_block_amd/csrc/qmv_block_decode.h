@@ -32,6 +32,40 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t h) {
     return __half2float(__ushort_as_half(static_cast<unsigned short>(h & 0xffffu)));
 }
 
+// --------------------------------------------------------------- activations
+// Activation element types: fp32, fp16 (_Float16) and bf16 (__bf16).  Staging
+// widens 16-bit activations to fp32 exactly, so every kernel computes on the
+// same fp32 values an fp32 call with the widened activations would.
+// load4: elements p[0..3] (p aligned to kVecAlign); load1: p[0].
+template <class XT> struct XIn;
+template <> struct XIn<float> {
+    static constexpr int kVecAlign = 16;
+    __device__ static float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+    __device__ static float load1(const float* p) { return *p; }
+};
+template <> struct XIn<_Float16> {
+    static constexpr int kVecAlign = 8;
+    __device__ static float4 load4(const _Float16* p) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        return float4{half_bits_to_float(w.x), half_bits_to_float(w.x >> 16), half_bits_to_float(w.y),
+                      half_bits_to_float(w.y >> 16)};
+    }
+    __device__ static float load1(const _Float16* p) {
+        return half_bits_to_float(*reinterpret_cast<const uint16_t*>(p));
+    }
+};
+template <> struct XIn<__bf16> {
+    static constexpr int kVecAlign = 8;
+    __device__ static float bits(uint32_t hi16) { return __builtin_bit_cast(float, hi16); }
+    __device__ static float4 load4(const __bf16* p) {
+        const uint2 w = *reinterpret_cast<const uint2*>(p);
+        return float4{bits(w.x << 16), bits(w.x & 0xffff0000u), bits(w.y << 16), bits(w.y & 0xffff0000u)};
+    }
+    __device__ static float load1(const __bf16* p) {
+        return bits((uint32_t)*reinterpret_cast<const uint16_t*>(p) << 16);
+    }
+};
+
 // --------------------------------------------------------------- formats
 // Traits + decoder per format.  load() fetches block g (global block index,
 // row * blocks_per_row + column block) and leaves the scale(s) as floats and
@@ -379,13 +413,12 @@ __device__ __forceinline__ float segment_sum(float v) {
 // compile-time constant), and only later writes them to LDS.  With no loop
 // the compiler can keep other loads issued in between in flight while it
 // waits for these.
-template <int XU, int NT>
+template <int XU, int NT, class XT = float>
 struct XStage {
     float4 v[XU];
-    __device__ __forceinline__ void load(const float* __restrict__ x, int K4) {
-        const float4* src = reinterpret_cast<const float4*>(x);
+    __device__ __forceinline__ void load(const XT* __restrict__ x, int K4) {
 #pragma unroll
-        for (int u = 0; u < XU; ++u) v[u] = src[min((int)threadIdx.x + u * NT, K4 - 1)];
+        for (int u = 0; u < XU; ++u) v[u] = XIn<XT>::load4(x + 4 * min((int)threadIdx.x + u * NT, K4 - 1));
     }
     // Indices past the end are clamped like the loads: such a thread
     // writes the last chunk's own value to the last chunk's slot.
@@ -417,10 +450,10 @@ __device__ __forceinline__ void block_sums(const float* xs, float* sx, int count
 // LDS as xs[b][block][36] and, when the format needs them, the per-block
 // sums into sx[b][block].  Loads are issued in batches of 4 per thread
 // before any is used, so the staging costs a few memory round trips, not
-// one per element.  vec: every column is 16-byte aligned (float4 loads).
+// one per element.  vec: every column is aligned for 4-element loads.
 // Ends with a barrier.
-template <bool kNeedSx, int B, int NT>
-__device__ __forceinline__ void stage_x_cols(const float* const (&xcol)[B], int nb, float* xs, float* sx, int w,
+template <bool kNeedSx, int B, int NT, class XT = float>
+__device__ __forceinline__ void stage_x_cols(const XT* const (&xcol)[B], int nb, float* xs, float* sx, int w,
                                              bool vec) {
     const int K = nb * 32;
     const int tid = threadIdx.x;
@@ -429,7 +462,7 @@ __device__ __forceinline__ void stage_x_cols(const float* const (&xcol)[B], int 
         if (b < w) {
             float* dst = xs + b * nb * kXPad;
             if (vec) {
-                const float4* src = reinterpret_cast<const float4*>(xcol[b]);
+                const XT* src = xcol[b];
                 const int K4 = K >> 2;
                 auto put = [&](int c, const float4& v) {
                     const int e = 4 * c;
@@ -437,24 +470,24 @@ __device__ __forceinline__ void stage_x_cols(const float* const (&xcol)[B], int 
                 };
                 for (int c0 = tid; c0 < K4; c0 += 4 * NT) {
                     const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
-                    const float4 v0 = src[c0];
-                    const float4 v1 = src[min(c1, K4 - 1)];
-                    const float4 v2 = src[min(c2, K4 - 1)];
-                    const float4 v3 = src[min(c3, K4 - 1)];
+                    const float4 v0 = XIn<XT>::load4(src + 4 * c0);
+                    const float4 v1 = XIn<XT>::load4(src + 4 * min(c1, K4 - 1));
+                    const float4 v2 = XIn<XT>::load4(src + 4 * min(c2, K4 - 1));
+                    const float4 v3 = XIn<XT>::load4(src + 4 * min(c3, K4 - 1));
                     put(c0, v0);
                     if (c1 < K4) put(c1, v1);
                     if (c2 < K4) put(c2, v2);
                     if (c3 < K4) put(c3, v3);
                 }
             } else {
-                const float* src = xcol[b];
+                const XT* src = xcol[b];
                 auto put = [&](int e, float v) { dst[(e >> 5) * kXPad + (e & 31)] = v; };
                 for (int e0 = tid; e0 < K; e0 += 4 * NT) {
                     const int e1 = e0 + NT, e2 = e0 + 2 * NT, e3 = e0 + 3 * NT;
-                    const float v0 = src[e0];
-                    const float v1 = src[min(e1, K - 1)];
-                    const float v2 = src[min(e2, K - 1)];
-                    const float v3 = src[min(e3, K - 1)];
+                    const float v0 = XIn<XT>::load1(src + e0);
+                    const float v1 = XIn<XT>::load1(src + min(e1, K - 1));
+                    const float v2 = XIn<XT>::load1(src + min(e2, K - 1));
+                    const float v3 = XIn<XT>::load1(src + min(e3, K - 1));
                     put(e0, v0);
                     if (e1 < K) put(e1, v1);
                     if (e2 < K) put(e2, v2);

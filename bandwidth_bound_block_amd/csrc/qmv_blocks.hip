@@ -28,6 +28,8 @@
 //    reduces across its LPR lanes with cross-lane shuffles in a fixed order
 //    (deterministic, no atomics).
 //  * No MFMA: at batch 1..8 this is a GEMV, bound by HBM bandwidth.
+#include <type_traits>
+
 #include "qmv_block_decode.h"
 
 namespace qmv {
@@ -53,9 +55,9 @@ struct PairRoute {
 // loaded while the current step is computed (two steps in flight per wave),
 // and the first step's loads are issued before the activation staging so
 // that both latencies overlap.
-template <class F, int B, int LPR, int RPL, int XU, int NW, int PD = 2, bool ROUTE = false>
+template <class F, int B, int LPR, int RPL, int XU, int NW, int PD = 2, bool ROUTE = false, class XT = float>
 __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict__ W, int64_t N, int nb,
-                                                       const float* __restrict__ x, int64_t ldx,
+                                                       const XT* __restrict__ x, int64_t ldx,
                                                        float* __restrict__ y, int64_t ldy, int xvec,
                                                        const PairRoute route) {
     extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
     };
     if (XU > 0 && xvec) {
         // batch 1: x loads, then the first weight loads, then x into LDS
-        XStage<XU, 64 * NW> xst;
+        XStage<XU, 64 * NW, XT> xst;
         xst.load(x, K4);
 #pragma unroll
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
@@ -173,10 +175,10 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
             __syncthreads();
         }
     } else {
-        const float* xcol[B];
+        const XT* xcol[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) xcol[b] = x + b * ldx;
-        stage_x_cols<F::kNeedSx, B, 64 * NW>(xcol, nb, xs, sx, B, xvec != 0);
+        stage_x_cols<F::kNeedSx, B, 64 * NW, XT>(xcol, nb, xs, sx, B, xvec != 0);
 #pragma unroll
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
@@ -211,8 +213,8 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 // a time; rows are taken wave, wave + grid waves, ...  The rows are those
 // of up to kMaxSegs matrices sharing x, concatenated (a wave-uniform
 // lookup finds a row's matrix).
-template <class F, int XU, int NW, int PD = 2>
-__global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int nb, const float* __restrict__ x) {
+template <class F, int XU, int NW, int PD = 2, class XT = float>
+__global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int nb, const XT* __restrict__ x) {
     using C = Contig<F>;
     extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
     float* xs = lds;
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
 
     const int K4 = nb * 8;
     if (XU > 0) {
-        XStage<XU, 64 * NW> xst;
+        XStage<XU, 64 * NW, XT> xst;
         xst.load(x, K4);
 #pragma unroll
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
@@ -283,8 +285,8 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
             __syncthreads();
         }
     } else {
-        const float* xcol[1] = {x};
-        stage_x_cols<F::kNeedSx, 1, 64 * NW>(xcol, nb, xs, sx, 1, true);
+        const XT* xcol[1] = {x};
+        stage_x_cols<F::kNeedSx, 1, 64 * NW, XT>(xcol, nb, xs, sx, 1, true);
 #pragma unroll
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
@@ -528,11 +530,11 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 
 // ------------------------------------------------------------------ host
 
-template <class F, int B, int LPR, int XU, int NW>
-int32_t launch_b(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
+template <class F, int B, int LPR, int XU, int NW, class XT = float>
+int32_t launch_b(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                  hipStream_t st) {
     constexpr int RPL = 1;
-    auto kern = qmv_kernel<F, B, LPR, RPL, XU, NW>;
+    auto kern = qmv_kernel<F, B, LPR, RPL, XU, NW, 2, false, XT>;
     const size_t lds = (size_t)B * nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
@@ -546,24 +548,24 @@ int32_t launch_b(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ld
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int64_t cap = (int64_t)device_cu_count() * per_cu;
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, cap));
-    const int xvec = (aligned(x, 16) && ldx % 4 == 0) ? 1 : 0;
+    const int xvec = (aligned(x, XIn<XT>::kVecAlign) && ldx % 4 == 0) ? 1 : 0;
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nb, x, ldx, y, ldy, xvec, PairRoute{});
     return check_launch("qmv");
 }
 
 // Lanes per row: whole waves for long rows, smaller segments for short rows
 // so that lanes are not left idle (e.g. 24 blocks -> 8 lanes x 3).
-template <class F, int B, int XU, int NW>
-int32_t launch_lpr(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
+template <class F, int B, int XU, int NW, class XT = float>
+int32_t launch_lpr(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                    hipStream_t st) {
-    if (nb >= 64) return launch_b<F, B, 64, XU, NW>(W, N, nb, x, ldx, y, ldy, st);
-    if (nb >= 32) return launch_b<F, B, 32, XU, NW>(W, N, nb, x, ldx, y, ldy, st);
-    return launch_b<F, B, 8, XU, NW>(W, N, nb, x, ldx, y, ldy, st);
+    if (nb >= 64) return launch_b<F, B, 64, XU, NW, XT>(W, N, nb, x, ldx, y, ldy, st);
+    if (nb >= 32) return launch_b<F, B, 32, XU, NW, XT>(W, N, nb, x, ldx, y, ldy, st);
+    return launch_b<F, B, 8, XU, NW, XT>(W, N, nb, x, ldx, y, ldy, st);
 }
 
-template <class F, int XU, int NW>
-int32_t launch_c(const RowSegs& segs, int nb, const float* x, hipStream_t st) {
-    auto kern = qmv_kernel_c<F, XU, NW>;
+template <class F, int XU, int NW, class XT = float>
+int32_t launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
+    auto kern = qmv_kernel_c<F, XU, NW, 2, XT>;
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float) + NW * Contig<F>::kStepBytes;
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
@@ -581,14 +583,14 @@ int32_t launch_c(const RowSegs& segs, int nb, const float* x, hipStream_t st) {
 
 // XU 16-byte activation loads per thread stage K4 = K / 4 chunks with a
 // workgroup of NW waves; past 8 per thread the staging loops instead.
-template <class F, int NW>
-int32_t launch_c_xu(const RowSegs& segs, int nb, const float* x, hipStream_t st) {
+template <class F, int NW, class XT = float>
+int32_t launch_c_xu(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
     const int per = (nb * 8 + 64 * NW - 1) / (64 * NW);
-    if (per <= 1) return launch_c<F, 1, NW>(segs, nb, x, st);
-    if (per <= 2) return launch_c<F, 2, NW>(segs, nb, x, st);
-    if (per <= 4) return launch_c<F, 4, NW>(segs, nb, x, st);
-    if (per <= 8) return launch_c<F, 8, NW>(segs, nb, x, st);
-    return launch_c<F, 0, NW>(segs, nb, x, st);
+    if (per <= 1) return launch_c<F, 1, NW, XT>(segs, nb, x, st);
+    if (per <= 2) return launch_c<F, 2, NW, XT>(segs, nb, x, st);
+    if (per <= 4) return launch_c<F, 4, NW, XT>(segs, nb, x, st);
+    if (per <= 8) return launch_c<F, 8, NW, XT>(segs, nb, x, st);
+    return launch_c<F, 0, NW, XT>(segs, nb, x, st);
 }
 
 // Batch 1 with whole 64-block steps and 16-byte aligned W and x: the
@@ -599,9 +601,9 @@ int32_t launch_c_xu(const RowSegs& segs, int nb, const float* x, hipStream_t st)
 //   2048..32768 rows, or >= 256 blocks per row.
 // 16 waves per workgroup for long rows (one activation copy per CU) and
 // for Q4 matrices of <= 4096 rows, else 8; fewer if the LDS does not fit.
-template <class F>
-bool try_launch_c(const RowSegs& segs, int nb, const float* x, hipStream_t st, bool force, int32_t* rc) {
-    if (nb % 64 || !aligned(x, 16) || segs.n < 1 || segs.n > kMaxSegs) return false;
+template <class F, class XT = float>
+bool try_launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st, bool force, int32_t* rc) {
+    if (nb % 64 || !aligned(x, XIn<XT>::kVecAlign) || segs.n < 1 || segs.n > kMaxSegs) return false;
     for (int i = 0; i < segs.n; ++i)
         if (!aligned(segs.W[i], 16)) return false;
     const int64_t N = segs.end[segs.n - 1];
@@ -612,9 +614,9 @@ bool try_launch_c(const RowSegs& segs, int nb, const float* x, hipStream_t st, b
     int nw = (long_rows || (!q8 && N <= 4096)) ? 16 : 8;
     while (nw >= 4 && lds_x + (size_t)nw * Contig<F>::kStepBytes > (size_t)kLdsMax) nw /= 2;
     switch (nw) {
-    case 16: *rc = launch_c_xu<F, 16>(segs, nb, x, st); return true;
-    case 8: *rc = launch_c_xu<F, 8>(segs, nb, x, st); return true;
-    case 4: *rc = launch_c_xu<F, 4>(segs, nb, x, st); return true;
+    case 16: *rc = launch_c_xu<F, 16, XT>(segs, nb, x, st); return true;
+    case 8: *rc = launch_c_xu<F, 8, XT>(segs, nb, x, st); return true;
+    case 4: *rc = launch_c_xu<F, 4, XT>(segs, nb, x, st); return true;
     default: return false;
     }
 }
@@ -624,8 +626,8 @@ bool try_launch_c(const RowSegs& segs, int nb, const float* x, hipStream_t st, b
 // small matrices over every CU).  Activations are staged with straight-line
 // 16-byte loads when 16-byte aligned: XU loads per thread cover
 // K <= 16 * 64 * NW * XU / 4.
-template <class F>
-int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, float* y, int64_t ldy,
+template <class F, class XT = float>
+int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                   hipStream_t st) {
     int32_t rc;
     RowSegs one = {};
@@ -633,18 +635,18 @@ int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const float* x, int64_t l
     one.y[0] = y;
     one.end[0] = N;
     one.n = 1;
-    if (try_launch_c<F>(one, nb, x, st, false, &rc)) return rc;
+    if (try_launch_c<F, XT>(one, nb, x, st, false, &rc)) return rc;
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
-    const bool vec = aligned(x, 16);
+    const bool vec = aligned(x, XIn<XT>::kVecAlign);
     const int K4 = nb * 8;
     if (lds > 40 * 1024) {
-        if (vec && K4 <= 2 * 512) return launch_lpr<F, 1, 2, 8>(W, N, nb, x, ldx, y, ldy, st);
-        if (vec && K4 <= 8 * 512) return launch_lpr<F, 1, 8, 8>(W, N, nb, x, ldx, y, ldy, st);
-        return launch_lpr<F, 1, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+        if (vec && K4 <= 2 * 512) return launch_lpr<F, 1, 2, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
+        if (vec && K4 <= 8 * 512) return launch_lpr<F, 1, 8, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
+        return launch_lpr<F, 1, 0, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
     }
-    if (vec && K4 <= 4 * 256) return launch_lpr<F, 1, 4, 4>(W, N, nb, x, ldx, y, ldy, st);
-    if (vec && K4 <= 16 * 256) return launch_lpr<F, 1, 16, 4>(W, N, nb, x, ldx, y, ldy, st);
-    return launch_lpr<F, 1, 0, 4>(W, N, nb, x, ldx, y, ldy, st);
+    if (vec && K4 <= 4 * 256) return launch_lpr<F, 1, 4, 4, XT>(W, N, nb, x, ldx, y, ldy, st);
+    if (vec && K4 <= 16 * 256) return launch_lpr<F, 1, 16, 4, XT>(W, N, nb, x, ldx, y, ldy, st);
+    return launch_lpr<F, 1, 0, 4, XT>(W, N, nb, x, ldx, y, ldy, st);
 }
 
 template <class F>
@@ -665,7 +667,7 @@ int32_t launch_batch(const uint8_t* W, int64_t N, int nb, const float* x, int64_
 }
 
 int32_t check_common(const char* name, const void* W, int64_t N, int64_t K, const void* x, int64_t ldx,
-                     int32_t batch, const void* y, int64_t ldy) {
+                     int32_t batch, const void* y, int64_t ldy, int x_align = 4) {
     if (!W || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
     if (K < 32 || K % 32) return fail(QMV_EINVAL, "%s: n_cols must be a positive multiple of 32 (got %lld)", name, (long long)K);
@@ -674,8 +676,10 @@ int32_t check_common(const char* name, const void* W, int64_t N, int64_t K, cons
     if (ldy < N) return fail(QMV_EINVAL, "%s: ldy (%lld) < n_rows (%lld)", name, (long long)ldy, (long long)N);
     if (K / 32 > (1 << 26) || N > ((int64_t)1 << 40) / (K / 32))
         return fail(QMV_EINVAL, "%s: matrix too large (%lld x %lld)", name, (long long)N, (long long)K);
-    if (!aligned(W, 4) || !aligned(x, 4) || !aligned(y, 4))
-        return fail(QMV_EALIGN, "%s: W, x and y must be 4-byte aligned", name);
+    if (!aligned(W, 4) || !aligned(y, 4))
+        return fail(QMV_EALIGN, "%s: W and y must be 4-byte aligned", name);
+    if (!aligned(x, x_align))
+        return fail(QMV_EALIGN, "%s: x must be %d-byte aligned (its element size)", name, x_align);
     return QMV_OK;
 }
 
@@ -684,22 +688,28 @@ constexpr qmv_fmt fmt_of() {
     return F::kBytes == 34 ? QMV_Q8_0 : (F::kBytes == 18 ? QMV_Q4_0 : QMV_Q4_1);
 }
 
+template <class XT> constexpr int32_t xtype_of();
+template <> constexpr int32_t xtype_of<float>() { return QMV_X_F32; }
+template <> constexpr int32_t xtype_of<_Float16>() { return QMV_X_F16; }
+template <> constexpr int32_t xtype_of<__bf16>() { return QMV_X_BF16; }
+
 // path: QMV_PATH_AUTO, QMV_PATH_FMA (the FMA kernels) or QMV_PATH_MFMA (the
-// matrix-core kernel; QMV_EUNSUPPORTED where it does not apply).
-template <class F>
-int32_t matvec(const char* name, const void* W, int64_t N, int64_t K, const float* x, int64_t ldx, int32_t batch,
+// matrix-core kernel; QMV_EUNSUPPORTED where it does not apply).  XT: the
+// activation element type (fp32, fp16 or bf16).
+template <class F, class XT = float>
+int32_t matvec(const char* name, const void* W, int64_t N, int64_t K, const XT* x, int64_t ldx, int32_t batch,
                float* y, int64_t ldy, void* stream, int32_t path = QMV_PATH_AUTO) {
-    int32_t rc = check_common(name, W, N, K, x, ldx, batch, y, ldy);
+    int32_t rc = check_common(name, W, N, K, x, ldx, batch, y, ldy, (int)sizeof(XT));
     if (rc != QMV_OK) return rc;
     const int nb = (int)(K / 32);
     if (path == QMV_PATH_MFMA || (path == QMV_PATH_AUTO && use_mfma(fmt_of<F>(), N, nb, batch))) {
-        if (batch_matvec_mma(fmt_of<F>(), static_cast<const uint8_t*>(W), N, nb, x, ldx, batch, y, ldy,
-                             as_stream(stream), 0, &rc))
+        if (batch_matvec_mma(fmt_of<F>(), static_cast<const uint8_t*>(W), N, nb, x, xtype_of<XT>(), ldx, batch, y,
+                             ldy, as_stream(stream), 0, &rc))
             return rc == QMV_OK ? ok() : rc;
         if (path == QMV_PATH_MFMA)
             return fail(QMV_EUNSUPPORTED,
-                        "%s: the matrix-core path needs batch 2..8, n_cols a multiple of 256, W and x 16-byte "
-                        "aligned and ldx a multiple of 4", name);
+                        "%s: the matrix-core path needs batch 2..8, n_cols a multiple of 256, W 16-byte aligned, "
+                        "x aligned to 4 elements (16 bytes for fp32) and ldx a multiple of 4", name);
     }
     // The staged activation block must fit in LDS; wider batches than fit
     // are processed in column groups (each group re-reads W).
@@ -707,11 +717,20 @@ int32_t matvec(const char* name, const void* W, int64_t N, int64_t K, const floa
     const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / per_col));
     if (per_col > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
-    for (int b0 = 0; b0 < batch; b0 += per_pass) {
-        const int bw = std::min(per_pass, batch - b0);
-        rc = launch_batch<F>(static_cast<const uint8_t*>(W), N, nb, x + b0 * ldx, ldx, bw, y + b0 * ldy, ldy,
-                             as_stream(stream));
-        if (rc != QMV_OK) return rc;
+    if constexpr (std::is_same<XT, float>::value) {
+        for (int b0 = 0; b0 < batch; b0 += per_pass) {
+            const int bw = std::min(per_pass, batch - b0);
+            rc = launch_batch<F>(static_cast<const uint8_t*>(W), N, nb, x + b0 * ldx, ldx, bw, y + b0 * ldy, ldy,
+                                 as_stream(stream));
+            if (rc != QMV_OK) return rc;
+        }
+    } else {
+        // 16-bit activations on the FMA kernels: one batch-1 launch per column
+        for (int b = 0; b < batch; ++b) {
+            rc = launch_b1<F, XT>(static_cast<const uint8_t*>(W), N, nb, x + b * ldx, ldx, y + b * ldy, ldy,
+                                  as_stream(stream));
+            if (rc != QMV_OK) return rc;
+        }
     }
     return ok();
 }
@@ -876,6 +895,30 @@ extern "C" int32_t qmv_q4_0(const void* W, int64_t n_rows, int64_t n_cols, const
 extern "C" int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols, const float* x, int64_t ldx, int32_t batch,
                             float* y, int64_t ldy, void* stream) {
     return qmv::matvec<qmv::Q4_1>("qmv_q4_1", W, n_rows, n_cols, x, ldx, batch, y, ldy, stream);
+}
+extern "C" int32_t qmv_matvec_xt(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols, const void* x,
+                                 int32_t x_type, int64_t ldx, int32_t batch, float* y, int64_t ldy, int32_t path,
+                                 void* stream) {
+    const char* name = "qmv_matvec_xt";
+    if (path != QMV_PATH_AUTO && path != QMV_PATH_FMA && path != QMV_PATH_MFMA)
+        return qmv::fail(QMV_EINVAL, "%s: unknown path %d", name, (int)path);
+    if (fmt != QMV_Q8_0 && fmt != QMV_Q4_0 && fmt != QMV_Q4_1)
+        return qmv::fail(QMV_EUNSUPPORTED, "%s: unknown format %d", name, (int)fmt);
+    auto run = [&](auto xt) -> int32_t {
+        using XT = decltype(xt);
+        const XT* xp = static_cast<const XT*>(x);
+        switch (fmt) {
+        case QMV_Q8_0: return qmv::matvec<qmv::Q8_0, XT>(name, W, n_rows, n_cols, xp, ldx, batch, y, ldy, stream, path);
+        case QMV_Q4_0: return qmv::matvec<qmv::Q4_0, XT>(name, W, n_rows, n_cols, xp, ldx, batch, y, ldy, stream, path);
+        default: return qmv::matvec<qmv::Q4_1, XT>(name, W, n_rows, n_cols, xp, ldx, batch, y, ldy, stream, path);
+        }
+    };
+    switch (x_type) {
+    case QMV_X_F32: return run(float{});
+    case QMV_X_F16: return run(_Float16{});
+    case QMV_X_BF16: return run(__bf16{});
+    default: return qmv::fail(QMV_EINVAL, "%s: unknown activation type %d", name, (int)x_type);
+    }
 }
 extern "C" int32_t qmv_matvec_path(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols, const float* x,
                                    int64_t ldx, int32_t batch, float* y, int64_t ldy, int32_t path, void* stream) {

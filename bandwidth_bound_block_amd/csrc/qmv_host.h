@@ -50,12 +50,13 @@ bool group_matvec_contig(qmv_fmt fmt, const RowSegs& segs, int nb, const float* 
                          int32_t* rc);
 
 // Batch 2..8 on the matrix cores (bf16 MFMA with the activations split into
-// two bf16 pieces).  Applies when n_cols is a multiple of 256, W and x are
-// 16-byte aligned and ldx is a multiple of 4: then returns true and the
+// two bf16 pieces).  Applies when n_cols is a multiple of 256, W is 16-byte
+// aligned, x is aligned to 4 elements and ldx is a multiple of 4: then returns true and the
 // launch status in *rc; else false and launches nothing.  variant: 0 for
 // the default workgroup shape, else (waves << 8) | waves-per-tile (tuning).
-bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B,
-                      float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc);
+// x_type: QMV_X_F32 / QMV_X_F16 / QMV_X_BF16 (x holds that element type).
+bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const void* x, int32_t x_type, int64_t ldx,
+                      int B, float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc);
 // Whether QMV_PATH_AUTO takes the matrix-core kernel for this shape.
 bool use_mfma(qmv_fmt fmt, int64_t N, int nb, int B);
 

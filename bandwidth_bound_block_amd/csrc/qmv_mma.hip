@@ -179,18 +179,18 @@ struct MmaStep {
 // (piece rows 4g..4g+3).  One thread per (column, block) with blocks
 // fastest: it does all four k-groups (the sums need no cross-lane step), and
 // neighbouring lanes write neighbouring 16-byte entries of a row.
-template <class F, int NT>
-__device__ __forceinline__ void stage_pieces(const float* __restrict__ x, int64_t ldx, int B, int b0, int nbc,
+template <class F, int NT, class XT>
+__device__ __forceinline__ void stage_pieces(const XT* __restrict__ x, int64_t ldx, int B, int b0, int nbc,
                                              int kcp, uint8_t* xs, float* sxs) {
     using M = Mma<F>;
     for (int idx = threadIdx.x; idx < nbc * B; idx += NT) {
         const int b = idx / nbc, blk = idx - b * nbc;
-        const float* src = x + b * ldx + 32 * (b0 + blk);
+        const XT* src = x + b * ldx + 32 * (b0 + blk);
         float sums[2][4];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const float4 u = *reinterpret_cast<const float4*>(src + M::x0(g));
-            const float4 w = *reinterpret_cast<const float4*>(src + M::x1(g));
+            const float4 u = XIn<XT>::load4(src + M::x0(g));
+            const float4 w = XIn<XT>::load4(src + M::x1(g));
             const float v[8] = {u.x, u.y, u.z, u.w, w.x, w.y, w.z, w.w};
             uint32_t hp[4], lp[4];
             float sh = 0.f, sl = 0.f;
@@ -224,9 +224,9 @@ __device__ __forceinline__ void stage_pieces(const float* __restrict__ x, int64_
     }
 }
 
-template <class F, int NW, int SB, int PD>
+template <class F, int NW, int SB, int PD, class XT = float>
 __global__ __launch_bounds__(64 * NW) void qmv_mma_kernel(const uint8_t* __restrict__ W, int N, int nb,
-                                                          const float* __restrict__ x, int64_t ldx, int B,
+                                                          const XT* __restrict__ x, int64_t ldx, int B,
                                                           float* __restrict__ y, int64_t ldy, int KP, int KC) {
     using M = Mma<F>;
     using S = MmaStep<F, SB>;
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_mma_kernel(const uint8_t* __restr
         if (nig % ipc == 0 && (nchunks > 1 || n == 0)) {
             const int b0 = c * KC;
             __syncthreads();
-            stage_pieces<F, 64 * NW>(x, ldx, B, b0, min(KC, nb - b0), kcp, xs, sxs);
+            stage_pieces<F, 64 * NW, XT>(x, ldx, B, b0, min(KC, nb - b0), kcp, xs, sxs);
             __syncthreads();
         }
         const int cb = (kp + KP * nig) * SB - c * KC;   // first block of the step in the chunk
@@ -383,8 +383,8 @@ __global__ __launch_bounds__(64 * NW) void qmv_mma_kernel(const uint8_t* __restr
     }
 }
 
-template <class F, int NW, int SB, int PD>
-bool launch_mma(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B, float* y, int64_t ldy,
+template <class F, int NW, int SB, int PD, class XT = float>
+bool launch_mma(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, int B, float* y, int64_t ldy,
                 hipStream_t st, int kp_force, int32_t* rc) {
     using S = MmaStep<F, SB>;
     if (nb % SB) return false;
@@ -414,7 +414,7 @@ bool launch_mma(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx
     const int KC = cs * SB;
     const size_t lds = fixed + (size_t)(KC | 1) * per_blk;
 
-    auto kern = qmv_mma_kernel<F, NW, SB, PD>;
+    auto kern = qmv_mma_kernel<F, NW, SB, PD, XT>;
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -444,28 +444,42 @@ namespace {
 // 16 waves per workgroup pay off on many tiles at batch 3..4 (the staged
 // activations leave room for 16 slots) and on very many tiles above that;
 // otherwise 8 (more tile groups than compute units, one activation chunk).
-template <class F>
-bool launch_mma_auto(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B, float* y,
+template <class F, class XT>
+bool launch_mma_auto(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, int B, float* y,
                      int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
+    if (!aligned(x, XIn<XT>::kVecAlign)) return false;
     const int64_t tiles = (N + 15) / 16;
     int nw = variant >> 8;
     if (nw == 0) nw = ((B >= 3 && B <= 4 && tiles >= 1024) || (B >= 5 && tiles >= 4096)) ? 16 : 8;
     const int kp = variant & 0xff;
-    return nw == 16 ? launch_mma<F, 16, 8, 2>(W, N, nb, x, ldx, B, y, ldy, st, kp, rc)
-                    : launch_mma<F, 8, 8, 2>(W, N, nb, x, ldx, B, y, ldy, st, kp, rc);
+    return nw == 16 ? launch_mma<F, 16, 8, 2, XT>(W, N, nb, x, ldx, B, y, ldy, st, kp, rc)
+                    : launch_mma<F, 8, 8, 2, XT>(W, N, nb, x, ldx, B, y, ldy, st, kp, rc);
+}
+
+template <class F>
+bool launch_mma_x(const uint8_t* W, int64_t N, int nb, const void* x, int32_t x_type, int64_t ldx, int B, float* y,
+                  int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
+    switch (x_type) {
+    case QMV_X_F32:
+        return launch_mma_auto<F, float>(W, N, nb, static_cast<const float*>(x), ldx, B, y, ldy, st, variant, rc);
+    case QMV_X_F16:
+        return launch_mma_auto<F, _Float16>(W, N, nb, static_cast<const _Float16*>(x), ldx, B, y, ldy, st, variant,
+                                            rc);
+    case QMV_X_BF16:
+        return launch_mma_auto<F, __bf16>(W, N, nb, static_cast<const __bf16*>(x), ldx, B, y, ldy, st, variant, rc);
+    }
+    return false;
 }
 }  // namespace
 
-bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B,
-                      float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
+bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const void* x, int32_t x_type, int64_t ldx,
+                      int B, float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
     const int64_t pitch = (int64_t)nb * (fmt == QMV_Q8_0 ? 34 : (fmt == QMV_Q4_0 ? 18 : 20));
-    if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || pitch >= (1 << 24) || !aligned(W, 16) || !aligned(x, 16) ||
-        ldx % 4)
-        return false;
+    if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || pitch >= (1 << 24) || !aligned(W, 16) || ldx % 4) return false;
     switch (fmt) {
-    case QMV_Q8_0: return launch_mma_auto<Q8_0>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
-    case QMV_Q4_0: return launch_mma_auto<Q4_0>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
-    case QMV_Q4_1: return launch_mma_auto<Q4_1>(W, N, nb, x, ldx, B, y, ldy, st, variant, rc);
+    case QMV_Q8_0: return launch_mma_x<Q8_0>(W, N, nb, x, x_type, ldx, B, y, ldy, st, variant, rc);
+    case QMV_Q4_0: return launch_mma_x<Q4_0>(W, N, nb, x, x_type, ldx, B, y, ldy, st, variant, rc);
+    case QMV_Q4_1: return launch_mma_x<Q4_1>(W, N, nb, x, x_type, ldx, B, y, ldy, st, variant, rc);
     }
     return false;
 }

@@ -111,8 +111,9 @@ int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
  *   QMV_PATH_MFMA  the matrix-core kernel: 16 rows x one 32-weight block x
  *                  up to 8 batch columns per v_mfma_f32_16x16x32_bf16 (the
  *                  block scale applied to its results), for batch 2..8, n_cols
- *                  a multiple of 256, W and x 16-byte aligned and ldx a
- *                  multiple of 4; otherwise QMV_EUNSUPPORTED.
+ *                  a multiple of 256, W 16-byte aligned, x 16-byte aligned
+ *                  (8-byte for 16-bit activations) and ldx a multiple of 4;
+ *                  otherwise QMV_EUNSUPPORTED.
  * Arguments and other errors as the format entry points; QMV_EINVAL for an
  * unknown path, QMV_EUNSUPPORTED for an unknown fmt.
  */
@@ -120,6 +121,28 @@ enum { QMV_PATH_AUTO = 0, QMV_PATH_FMA = 1, QMV_PATH_MFMA = 2 };
 int32_t qmv_matvec_path(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols,
                         const float* x, int64_t ldx, int32_t batch,
                         float* y, int64_t ldy, int32_t path, void* stream);
+
+/*
+ * The float matvec with 16-bit activations ([ESP] Sec. 2.2: the core is
+ * templated on the activation type as well as the weight format, with f16
+ * and bf16 entry points).  x holds `batch` rows of x_type elements, ldx
+ * elements apart:
+ *   QMV_X_F32   fp32 (the same as qmv_matvec_path);
+ *   QMV_X_F16   IEEE binary16;
+ *   QMV_X_BF16  bfloat16 (the upper half of an fp32).
+ * Activations are widened to fp32 exactly and y is fp32, accumulated in fp32:
+ * the result equals, bitwise, the fp32 call on the widened activations with
+ * the same path.  x must be aligned to its element size; the vectorized
+ * staging needs 4-element (8-byte) alignment and ldx a multiple of 4, and is
+ * skipped otherwise.  On the FMA kernels 16-bit activations at batch > 1 run
+ * one column per launch.  path as qmv_matvec_path.
+ * Errors: as qmv_matvec_path; QMV_EINVAL for an unknown x_type, QMV_EALIGN
+ * for x not aligned to its element size.
+ */
+enum { QMV_X_F32 = 0, QMV_X_F16 = 1, QMV_X_BF16 = 2 };
+int32_t qmv_matvec_xt(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols,
+                      const void* x, int32_t x_type, int64_t ldx, int32_t batch,
+                      float* y, int64_t ldy, int32_t path, void* stream);
 
 /*
  * All-integer matvec with per-output-channel requant ([ZEN]):

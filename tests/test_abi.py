@@ -28,7 +28,8 @@ def qmv():
 
 def test_every_declared_symbol_is_exported(qmv):
     names = declared_functions()
-    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_i8_requant", "qmv_moe", "qmv_dequant",
+    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "qmv_i8_requant", "qmv_moe",
+            "qmv_dequant",
             "qmv_chain", "qmv_last_error", "qmv_abi_version"} <= set(names)
     raw = ctypes.CDLL(qmv.library_path())
     for n in names:
@@ -83,6 +84,22 @@ def test_matvec_path_argument_errors(qmv):
                  (A, 8, 256, A, 258, 2, A, 8)]:         # ldx not a multiple of 4
         assert f(qmv.Q4_1, *args, qmv.PATH_MFMA, None) == EUNSUPPORTED, args
         assert "matrix-core" in qmv.last_error()
+
+
+def test_matvec_xt_argument_errors(qmv):
+    f = qmv.lib().qmv_matvec_xt
+    ok = (A, 8, 256)
+    tail = (256, 2, A, 8)
+    assert f(qmv.Q4_0, *ok, A, 7, *tail, qmv.PATH_AUTO, None) == EINVAL and "activation type" in qmv.last_error()
+    assert f(qmv.Q4_0, *ok, A, qmv.X_F16, *tail, 5, None) == EINVAL and "unknown path" in qmv.last_error()
+    assert f(11, *ok, A, qmv.X_BF16, *tail, qmv.PATH_AUTO, None) == EUNSUPPORTED
+    # x aligned to its element size: 2 bytes for 16-bit activations, 4 for fp32
+    assert f(qmv.Q8_0, *ok, A + 1, qmv.X_F16, *tail, qmv.PATH_AUTO, None) == EALIGN
+    assert "2-byte" in qmv.last_error()
+    assert f(qmv.Q8_0, *ok, A + 2, qmv.X_F32, *tail, qmv.PATH_AUTO, None) == EALIGN
+    # 8-byte vector alignment is only needed by the matrix-core path
+    assert f(qmv.Q4_0, *ok, A + 2, qmv.X_BF16, *tail, qmv.PATH_MFMA, None) == EUNSUPPORTED
+    assert f(qmv.Q4_0, A, 8, 256, A, qmv.X_F16, 255, 2, A, 8, qmv.PATH_FMA, None) == EINVAL   # ldx < n_cols
 
 
 def test_int8_argument_errors(qmv):

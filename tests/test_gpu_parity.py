@@ -302,6 +302,75 @@ def test_mfma_path_strided(env):
     assert np.all(y[:, N:].cpu().numpy() == 0)
 
 
+# ------------------------------------------------------------------ 16-bit activations
+def _x16(torch, x, kind):
+    """x (float32 numpy) rounded to fp16 / bf16 on the device, and the exact
+    fp32 widening of those values."""
+    t = dev(torch, x).to(torch.float16 if kind == "f16" else torch.bfloat16)
+    return t, t.float()
+
+
+X16_SHAPES = [(1, 32), (37, 96), (130, 1024), (65, 4096), (5, 14336), (300, 2048), (33, 1056), (2100, 4096)]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_x16_activations_equal_widened_fp32(env, fmt, kind):
+    """16-bit activations give bitwise the result of the fp32 call on the
+    exactly widened activations, on every kernel family, and are within the
+    bound of the oracle run on those widened values."""
+    torch, qmv = env
+    for N, K in X16_SHAPES:
+        W = wl.quant_weights(fmt, f"t/small/{N}x{K}", N, K)
+        Wd = dev(torch, W)
+        for B in (1, 2, 3, 8):
+            say(f"x16 {fmt} {kind} B={B} {N}x{K}")
+            x = wl.activations(f"t/x16/{K}/{B}", B, K)
+            xh, xw = _x16(torch, x, kind)
+            for path in (qmv.PATH_AUTO, qmv.PATH_FMA, qmv.PATH_MFMA):
+                if path == qmv.PATH_MFMA and (B == 1 or K % 256):
+                    continue
+                y16 = qmv.qmv_matvec_xt(fmt, Wd, N, K, xh, path)
+                y32 = qmv.qmv_matvec_path(fmt, Wd, N, K, xw, path)
+                torch.cuda.synchronize()
+                assert torch.equal(y16.view(torch.int32), y32.view(torch.int32)), (N, K, B, path)
+            yr, S = oracle.matvec(fmt, W, N, K, xw.cpu().numpy())
+            assert_tol(y16.cpu().numpy(), yr, S, (fmt, kind, N, K, B))
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_x16_unaligned_and_strided(env, kind):
+    """x at a 2-byte offset (element-wise staging, no matrix cores) and an
+    odd row stride; fp16 subnormals and extreme values survive widening."""
+    torch, qmv = env
+    N, K, B = 70, 2048, 3
+    W = wl.quant_weights("q4_1", "t/str/W", N, K)
+    Wd = dev(torch, W)
+    x = wl.activations("t/x16s/x", B, K + 7)
+    # fp16: subnormal, smallest normal and largest values; bf16: far outside
+    # the fp16 range (the block dot sum_j c_j x_j must stay finite in fp32)
+    x[0, :5] = [6.0e-8, -6.1e-5, 65504.0, -3.0e30 if kind == "bf16" else -60000.0, 1e-30 if kind == "bf16" else 1e-7]
+    dt = torch.float16 if kind == "f16" else torch.bfloat16
+    big = torch.zeros(B * (K + 7) + 1, dtype=dt, device="cuda:0")
+    xv = big[1:].view(B, K + 7)[:, :K]                  # 2-byte aligned only, ldx = K + 7
+    xv.copy_(dev(torch, x[:, :K]).to(dt))
+    assert xv.data_ptr() % 4 == 2
+    # the fp32 reference with the same layout (4-byte offset, ldx = K + 7):
+    # neither takes the matrix-core kernel
+    big32 = torch.zeros(B * (K + 7) + 1, dtype=torch.float32, device="cuda:0")
+    xw = big32[1:].view(B, K + 7)[:, :K]
+    xw.copy_(xv.float())
+    for path in (qmv.PATH_AUTO, qmv.PATH_FMA):
+        y16 = qmv.qmv_matvec_xt("q4_1", Wd, N, K, xv, path)
+        y32 = qmv.qmv_matvec_path("q4_1", Wd, N, K, xw, path)
+        torch.cuda.synchronize()
+        assert torch.equal(y16.view(torch.int32), y32.view(torch.int32)), path
+    yr, S = oracle.matvec("q4_1", W, N, K, xv.float().cpu().numpy())
+    assert_tol(y16.cpu().numpy(), yr, S)
+    with pytest.raises(qmv.QmvError):
+        qmv.qmv_matvec_xt("q4_1", Wd, N, K, xv, qmv.PATH_MFMA)
+
+
 # ------------------------------------------------------------------ full sizes
 @functools.lru_cache(maxsize=None)
 def _float_weights(tag, N, K):
