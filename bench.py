@@ -248,8 +248,15 @@ def build_llama_grouped(torch, qmv, wl, fmt):
     return sw
 
 
-def build_int8(torch, qmv, wl):
-    sw = Sweep("qwen06b_int8_b1", 1)
+FUSED_QWEN = [("qkv", ["q", "k", "v"]), ("gate_up", ["gate", "up"])]
+
+
+def build_int8(torch, qmv, wl, fused=False):
+    """28 Qwen3-0.6B-shaped int8 layers + the tied lm_head at batch 1.  With
+    fused, q||k||v and gate||up are stored row-concatenated (weights and
+    per-row mult/shift) and run as one launch each: 113 launches instead of
+    197 (a caller layout choice; the kernel and ABI are the same)."""
+    sw = Sweep(f"qwen06b_int8{'_fused' if fused else ''}_b1", 1)
     dev = "cuda:0"
     cfn = qmv.lib().qmv_i8_requant
     mats = {}
@@ -257,8 +264,23 @@ def build_int8(torch, qmv, wl):
         W = torch.from_numpy(wl.int8_uniform(f"qwen/W/{mname}", (N, K))).to(dev)
         mult, shift = wl.requant_params(f"qwen/ms/{mname}", N)
         mats[mname] = (W, torch.from_numpy(mult).to(dev), torch.from_numpy(shift).to(dev))
+    layer_list = list(wl.QWEN06B_LAYER)
+    if fused:
+        shapes = {m: (N, K) for m, N, K in wl.QWEN06B_LAYER}
+        layer_list = []
+        groups = {g: members for g, members in FUSED_QWEN}
+        done = set()
+        for mname, N, K in wl.QWEN06B_LAYER:
+            g = next((g for g, mem in FUSED_QWEN if mname in mem), None)
+            if g is None:
+                layer_list.append((mname, N, K))
+            elif g not in done:
+                mem = groups[g]
+                mats[g] = tuple(torch.cat([mats[m][i] for m in mem]) for i in range(3))
+                layer_list.append((g, sum(shapes[m][0] for m in mem), K))
+                done.add(g)
     for layer in range(wl.QWEN06B_LAYERS + 1):
-        mlist = wl.QWEN06B_LAYER if layer < wl.QWEN06B_LAYERS else [wl.QWEN06B_LM_HEAD]
+        mlist = layer_list if layer < wl.QWEN06B_LAYERS else [wl.QWEN06B_LM_HEAD]
         for mname, N, K in mlist:
             W0, mult, shift = mats[mname]
             W = W0.clone() if layer < wl.QWEN06B_LAYERS else W0
@@ -524,10 +546,11 @@ def main():
                 del s
                 torch.cuda.empty_cache()
         elif nm == "int8":
-            s = build_int8(torch, qmv, wl)
-            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
-            del s
-            torch.cuda.empty_cache()
+            for fused in (False, True):
+                s = build_int8(torch, qmv, wl, fused=fused)
+                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+                del s
+                torch.cuda.empty_cache()
         elif nm == "moe":
             for B in (1, 2, 4, 8):
                 s = build_moe(torch, qmv, wl, B)
