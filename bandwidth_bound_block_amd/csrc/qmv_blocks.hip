@@ -28,6 +28,7 @@
 //    reduces across its LPR lanes with cross-lane shuffles in a fixed order
 //    (deterministic, no atomics).
 //  * No MFMA: at batch 1..8 this is a GEMV, bound by HBM bandwidth.
+#include <cmath>
 #include <type_traits>
 
 #include "qmv_block_decode.h"
@@ -416,11 +417,13 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
         advance(ctile, ct);                                \
         if (ctile >= te) break;                            \
     }
-    static_assert(PD == 2, "pipeline depth");
+    static_assert(PD >= 2 && PD <= 4, "pipeline depth");
     if (ctile < te) {
         while (true) {
             QMV_MOE_STEP(0)
             QMV_MOE_STEP(1)
+            if constexpr (PD >= 3) QMV_MOE_STEP(2)
+            if constexpr (PD >= 4) QMV_MOE_STEP(3)
         }
     }
 #undef QMV_MOE_STEP
@@ -434,7 +437,7 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
 // moe_chunk for up to BC member pairs at a time.  Per (row, pair) the
 // arithmetic is the dense kernel's, so each output equals a single-expert
 // dense call bitwise.
-template <class F, int BC, int LPR, int NW, int XU>
+template <class F, int BC, int LPR, int NW, int XU, int PD>
 __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
                                                        int n_experts, int64_t N, int nb,
                                                        const int32_t* __restrict__ ids, int P, int top_k,
@@ -506,9 +509,9 @@ __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict_
             xcol[b] = x + (int64_t)(pr / top_k) * xs_tok + (int64_t)(pr % top_k) * xs_slot;
         }
         if (c0 == 0 && XU > 0 && xvec)
-            moe_chunk<F, BC, LPR, NW, XU>(We, N, nb, tb, te, xcol, w, true, s_members + c0, y, xs, sx);
+            moe_chunk<F, BC, LPR, NW, XU, PD>(We, N, nb, tb, te, xcol, w, true, s_members + c0, y, xs, sx);
         else
-            moe_chunk<F, BC, LPR, NW, 0>(We, N, nb, tb, te, xcol, w, xvec != 0, s_members + c0, y, xs, sx);
+            moe_chunk<F, BC, LPR, NW, 0, PD>(We, N, nb, tb, te, xcol, w, xvec != 0, s_members + c0, y, xs, sx);
     }
 }
 
@@ -749,13 +752,14 @@ int32_t dequant(const void* W, int64_t N, int64_t K, float* out, void* stream) {
 // The grid is (range, group): group u serves the u-th distinct routed id
 // (at most P = batch * top_k groups; the extra ones exit at once), and the
 // ranges split each expert's row tiles so that ranges x expected groups
-// fill the GPU once.
-template <class F, int BC, int LPR, int XU>
+// fill the GPU once.  Expected groups: all P (spread), or the distinct ids
+// that P uniformly routed pairs reach on average, E (1 - (1 - 1/E)^P).
+template <class F, int BC, int LPR, int XU, int PD>
 int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                    int P, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
-                   hipStream_t st) {
+                   bool spread, hipStream_t st) {
     constexpr int NW = 4;
-    auto kern = moe_kernel<F, BC, LPR, NW, XU>;
+    auto kern = moe_kernel<F, BC, LPR, NW, XU, PD>;
     static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
     if (!dyn_max) {
         hipFuncAttributes fa;
@@ -772,28 +776,37 @@ int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N,
         return fail(QMV_EINVAL, "qmv_moe: n_cols %d too large for one activation row in LDS", nb * 32);
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int64_t ntiles = (N + 64 / LPR - 1) / (64 / LPR);
-    const int64_t groups = std::max(1, std::min(P, n_experts));
+    const double e = n_experts;
+    const int64_t groups = std::max<int64_t>(
+        1, std::min<int64_t>(std::min(P, n_experts),
+                             spread ? P : (int64_t)std::ceil(e * (1.0 - std::pow(1.0 - 1.0 / e, (double)P)))));
     const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(ntiles, (int64_t)device_cu_count() * per_cu / groups));
     hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)P), dim3(64 * NW), lds, st, Wx, estride, n_experts, N, nb,
                        ids, P, top_k, x, xs_tok, xs_slot, y, xvec);
     return check_launch("qmv_moe");
 }
 
-// Member columns per pass: one token routes to an expert once, so batch 1
-// needs one column; at batches 2..8 a routed expert of 128 has about 1.4
-// members on average, and 2 columns per pass (more passes when an expert
-// has more) measured fastest: the staged rows stay small, so more
-// workgroups fit.  Activations staged straight-line (XU 16-byte loads per
-// thread) up to K = 8192.
+// Member columns per pass.  One token routes to an expert once, so batch 1
+// needs one column.  At batches 2..8 a routed expert of 128 has 1.0 to 1.3
+// members on average.  Measured on the 30B-A3B expert shapes (cache-cold):
+// one column per pass, three steps in flight and a grid sized for the
+// expected distinct experts win where the rows are long (2048 columns) or
+// the batch is 8 (about 70 VGPRs: 7 waves per SIMD; an expert with two members
+// streams twice, mostly from L2); on short rows at batch 2..4 there is
+// too little work per workgroup for that, and two columns per pass over a
+// grid sized for every pair measured faster.  Activations staged
+// straight-line (XU 16-byte loads per thread) up to K = 8192.
 template <class F, int LPR, int XU>
 int32_t launch_moe_bc(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                       int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
     const int P = batch * top_k;
     const size_t per_col = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
-    if (batch > 1 && 2 * per_col + kMoeStaticLds <= (size_t)kLdsMax)
-        return launch_moe<F, 2, LPR, XU>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec, st);
-    return launch_moe<F, 1, LPR, XU>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec, st);
+    if (batch > 1 && batch < 8 && nb < 64 && 2 * per_col + kMoeStaticLds <= (size_t)kLdsMax)
+        return launch_moe<F, 2, LPR, XU, 2>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec,
+                                            true, st);
+    return launch_moe<F, 1, LPR, XU, 3>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec,
+                                        batch == 1, st);
 }
 
 // Batch 1: the pairs of one token need no grouping (a duplicated id only
