@@ -69,7 +69,15 @@ def _load():
         lib.qo_matvec_i8.argtypes = [P, i64, i64, P, i64, i32, P, P, P, i64, P, P, i64]
         lib.qo_moe.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P,
                                i64, i64, P, i64, P, P, i64]
-        for f in ("qo_dequant", "qo_matvec", "qo_matvec_i8", "qo_moe"):
+        lib.qo_matvec_i8_lut.argtypes = [P, i64, i64, P, i64, i32, P, P, P, P, i64, P, P, i64]
+        lib.qo_silu.argtypes = [ctypes.c_double]
+        lib.qo_silu.restype = ctypes.c_double
+        lib.qo_moe_swiglu.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P,
+                                      i64, i64, P, i64, P, P, P, P, P, i64]
+        lib.qo_moe_combine.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, P, i32, i32, P,
+                                       i64, i64, P, i64, P, P, i64]
+        for f in ("qo_dequant", "qo_matvec", "qo_matvec_i8", "qo_moe", "qo_matvec_i8_lut",
+                  "qo_moe_swiglu", "qo_moe_combine"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -209,3 +217,96 @@ def moe(fmt, W_experts, expert_stride, n_experts, N, K, ids, x_tokens, x_slots=N
                       batch, top_k, _ptr(xs), st_tok, st_slot, _ptr(rows), n,
                       _ptr(y), _ptr(S), n), "moe")
     return y, S
+
+
+def matvec_i8_lut(W, x, mult, shift, lut, rows=None):
+    """matvec_i8 with the requantized outputs mapped through a frozen table:
+    y = lut[y_requant + 128].  lut: int8 [256].  Returns (acc, y) like
+    matvec_i8."""
+    lib = _load()
+    W = np.ascontiguousarray(W, dtype=np.int8)
+    x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.int8)
+    mult = np.ascontiguousarray(mult, dtype=np.int32)
+    shift = np.ascontiguousarray(shift, dtype=np.int32)
+    lut = np.ascontiguousarray(lut, dtype=np.int8)
+    assert lut.shape == (256,)
+    N, K = W.shape
+    B = x.shape[0]
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+    else:
+        n = N
+    acc = np.empty((B, n), dtype=np.int64)
+    y = np.empty((B, n), dtype=np.int8)
+    rc = lib.qo_matvec_i8_lut(_ptr(W), N, K, _ptr(x), K, B, _ptr(mult), _ptr(shift), _ptr(lut),
+                              _ptr(rows), n, _ptr(acc), _ptr(y), n)
+    if rc == 3:
+        raise OverflowError("int8 accumulator does not fit int32")
+    _check(rc, "matvec_i8_lut")
+    return acc, y
+
+
+def silu(z):
+    """SiLU(z) = z / (1 + e^-z), fp64 (C oracle)."""
+    return float(_load().qo_silu(float(z)))
+
+
+def _moe_x(x_tokens, x_slots, batch, top_k, K):
+    if x_slots is not None:
+        xs = np.ascontiguousarray(x_slots, dtype=np.float32)
+        assert xs.shape == (batch, top_k, K)
+        return xs, top_k * K, K
+    xs = np.ascontiguousarray(x_tokens, dtype=np.float32)
+    assert xs.shape == (batch, K)
+    return xs, K, 0
+
+
+def moe_swiglu(fmt, W_experts, expert_stride, n_experts, F, K, ids, x_tokens, x_slots=None, rows=None):
+    """MoE gate/up with SwiGLU: every expert holds 2F rows (gate rows, then up
+    rows); h[b, s, i] = SiLU(g) * u with g, u the gate and up rows' matvecs.
+
+    Returns (h, g, u, Sg, Su), float64 [batch, top_k, n_rows]."""
+    lib = _load()
+    fmt = _fmt(fmt)
+    W_experts = np.ascontiguousarray(W_experts, dtype=np.uint8)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    batch, top_k = ids.shape
+    xs, st_tok, st_slot = _moe_x(x_tokens, x_slots, batch, top_k, K)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+    else:
+        n = F
+    out = [np.empty((batch, top_k, n), dtype=np.float64) for _ in range(5)]
+    _check(lib.qo_moe_swiglu(fmt, _ptr(W_experts), expert_stride, n_experts, F, K, _ptr(ids), batch, top_k,
+                             _ptr(xs), st_tok, st_slot, _ptr(rows), n, *[_ptr(a) for a in out], n), "moe_swiglu")
+    return tuple(out)
+
+
+def moe_combine(fmt, W_experts, expert_stride, n_experts, N, K, ids, weights, x_tokens=None, x_slots=None,
+                rows=None):
+    """MoE down projection with the router-weighted combine:
+    out[b, i] = sum_s w[b, s] * (DEQ(W_{ids[b,s]}) x_{b,s})_i.
+
+    weights: float32 [batch, top_k].  Returns (out, S), float64 [batch, n_rows],
+    S[b, i] = sum_s |w[b, s]| * sum_j |DEQ(W)_ij x_j|."""
+    lib = _load()
+    fmt = _fmt(fmt)
+    W_experts = np.ascontiguousarray(W_experts, dtype=np.uint8)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    batch, top_k = ids.shape
+    w = np.ascontiguousarray(weights, dtype=np.float32)
+    assert w.shape == (batch, top_k)
+    xs, st_tok, st_slot = _moe_x(x_tokens, x_slots, batch, top_k, K)
+    if rows is not None:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+    else:
+        n = N
+    out = np.empty((batch, n), dtype=np.float64)
+    S = np.empty((batch, n), dtype=np.float64)
+    _check(lib.qo_moe_combine(fmt, _ptr(W_experts), expert_stride, n_experts, N, K, _ptr(ids), _ptr(w), batch,
+                              top_k, _ptr(xs), st_tok, st_slot, _ptr(rows), n, _ptr(out), _ptr(S), n),
+           "moe_combine")
+    return out, S

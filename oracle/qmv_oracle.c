@@ -261,3 +261,124 @@ int qo_moe(int fmt, const uint8_t* W, int64_t expert_stride, int32_t n_experts,
     }
     return QO_OK;
 }
+
+/* ------------------------------------------------------------------ the
+ * steps on either side of the matvec (fused on the GPU, separate here). */
+
+/* The requantized int8 output mapped through a frozen lookup table.  [ZEN]
+ * "Quantization recipe": the integer engine's activation ops run as frozen
+ * tables (SiLU among them).  Reading: a table is 256 int8 entries and value
+ * v in [-128, 127] maps to lut[v + 128]; the table's contents belong to the
+ * caller (a SiLU table folds the activation scales into its entries).
+ *     y_i = lut[sat8(RDBPOT(SRDHM(acc_i, mult_i), shift_i)) + 128] */
+int qo_matvec_i8_lut(const int8_t* W, int64_t N, int64_t K,
+                     const int8_t* x, int64_t ldx, int32_t B,
+                     const int32_t* mult, const int32_t* shift, const int8_t* lut,
+                     const int64_t* rows, int64_t nrows,
+                     int64_t* acc, int8_t* y, int64_t ldo) {
+    int64_t t;
+    int32_t b;
+    int rc = qo_matvec_i8(W, N, K, x, ldx, B, mult, shift, rows, nrows, acc, y, ldo);
+    if (rc != QO_OK && rc != QO_EOVERFLOW) return rc;
+    if (!rows) nrows = N;
+    for (b = 0; b < B; ++b)
+        for (t = 0; t < nrows; ++t) {
+            int8_t* p = y + (int64_t)b * ldo + t;
+            *p = lut[(int)*p + 128];
+        }
+    return rc;
+}
+
+/* SiLU(z) = z * sigmoid(z) = z / (1 + e^-z).  [ZEN] "Architecture": the MLP
+ * is SwiGLU(gate, up, down); the page names it only.  Reading: the standard
+ * SwiGLU MLP, h = SiLU(gate x) * (up x), then down h. */
+double qo_silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* MoE gate/up with the SwiGLU step ([NST] Sec. "The Unified Quant Core": the
+ * MoE path runs each routed expert through the matvec core).  Every expert
+ * matrix holds 2F rows: the gate rows 0..F-1, then the up rows F..2F-1 (the
+ * caller stores the two row-concatenated).  For pair p = (b, s) with expert
+ * e = ids[p] and row i = rows[t]:
+ *     g = sum_j DEQ(W_e)_{i, j} x_p[j],   u = sum_j DEQ(W_e)_{F+i, j} x_p[j],
+ *     h[p][t] = SiLU(g) * u,
+ * with g, u (and their |.| sums Sg, Su) returned as well, all [p][t] with row
+ * stride ldo. */
+int qo_moe_swiglu(int fmt, const uint8_t* W, int64_t expert_stride, int32_t n_experts,
+                  int64_t F, int64_t K, const int32_t* ids, int32_t batch, int32_t top_k,
+                  const float* x, int64_t x_stride_token, int64_t x_stride_slot,
+                  const int64_t* rows, int64_t nrows,
+                  double* h, double* g, double* u, double* Sg, double* Su, int64_t ldo) {
+    int32_t b, s;
+    int64_t t;
+    int rc;
+    if (F < 1) return QO_EINVAL;
+    if (!rows) nrows = F;
+    for (b = 0; b < batch; ++b) {
+        for (s = 0; s < top_k; ++s) {
+            int32_t e = ids[b * top_k + s];
+            int64_t p = (int64_t)b * top_k + s;
+            const float* xp = x + b * x_stride_token + s * x_stride_slot;
+            if (e < 0 || e >= n_experts) return QO_EINVAL;
+            for (t = 0; t < nrows; ++t) {
+                int64_t i = rows ? rows[t] : t, ri[2];
+                double yv[2], sv[2];
+                if (i < 0 || i >= F) return QO_EINVAL;
+                ri[0] = i;
+                ri[1] = F + i;
+                rc = qo_matvec(fmt, W + (int64_t)e * expert_stride, 2 * F, K, xp, K, 1, ri, 1, &yv[0], &sv[0], 1);
+                if (rc != QO_OK) return rc;
+                rc = qo_matvec(fmt, W + (int64_t)e * expert_stride, 2 * F, K, xp, K, 1, ri + 1, 1, &yv[1], &sv[1], 1);
+                if (rc != QO_OK) return rc;
+                g[p * ldo + t] = yv[0];
+                u[p * ldo + t] = yv[1];
+                Sg[p * ldo + t] = sv[0];
+                Su[p * ldo + t] = sv[1];
+                h[p * ldo + t] = qo_silu(yv[0]) * yv[1];
+            }
+        }
+    }
+    return QO_OK;
+}
+
+/* MoE down projection with the router-weighted combine of a token's top_k
+ * expert outputs (the MoE block's last step).  For token b and row
+ * i = rows[t]:
+ *     out[b][t] = sum_{s<top_k} w[b][s] * y[b][s][t],
+ *     y[b][s][t] = sum_j DEQ(W_{ids[b][s]})_{i, j} x_{b,s}[j],
+ *     S[b][t] = sum_s |w[b][s]| * sum_j |DEQ(W_{ids[b][s]})_{i, j} x_{b,s}[j]|.
+ * Reading: the router weights are given (the router and its normalization
+ * are not part of this step). */
+int qo_moe_combine(int fmt, const uint8_t* W, int64_t expert_stride, int32_t n_experts,
+                   int64_t N, int64_t K, const int32_t* ids, const float* w, int32_t batch, int32_t top_k,
+                   const float* x, int64_t x_stride_token, int64_t x_stride_slot,
+                   const int64_t* rows, int64_t nrows, double* out, double* S, int64_t ldo) {
+    int32_t b, s;
+    int64_t t;
+    int rc;
+    double *y, *sy;
+    if (!rows) nrows = N;
+    y = (double*)malloc((size_t)(nrows > 0 ? nrows : 1) * sizeof(double));
+    sy = (double*)malloc((size_t)(nrows > 0 ? nrows : 1) * sizeof(double));
+    if (!y || !sy) { free(y); free(sy); return QO_ENOMEM; }
+    for (b = 0; b < batch; ++b) {
+        for (t = 0; t < nrows; ++t) {
+            out[(int64_t)b * ldo + t] = 0.0;
+            S[(int64_t)b * ldo + t] = 0.0;
+        }
+        for (s = 0; s < top_k; ++s) {
+            int32_t e = ids[b * top_k + s];
+            double ws = (double)w[b * top_k + s];
+            if (e < 0 || e >= n_experts) { free(y); free(sy); return QO_EINVAL; }
+            rc = qo_matvec(fmt, W + (int64_t)e * expert_stride, N, K,
+                           x + b * x_stride_token + s * x_stride_slot, K, 1, rows, nrows, y, sy, nrows);
+            if (rc != QO_OK) { free(y); free(sy); return rc; }
+            for (t = 0; t < nrows; ++t) {
+                out[(int64_t)b * ldo + t] += ws * y[t];
+                S[(int64_t)b * ldo + t] += fabs(ws) * sy[t];
+            }
+        }
+    }
+    free(y);
+    free(sy);
+    return QO_OK;
+}

@@ -8,7 +8,12 @@ Each pin is chosen so that a plausible mistake in the oracle fails it:
   * the fp64 dot: exact rational brute force on tiny matrices;
   * the integer requant: hand cases, closed forms and an independent
     big-integer mirror on edge and random pairs;
-  * MoE: reduction to single-expert matvecs sliced independently in numpy.
+  * MoE: reduction to single-expert matvecs sliced independently in numpy;
+  * the fused steps: the int8 table lookup against numpy indexing (identity
+    and permutation tables), SiLU against scipy's logistic function and its
+    odd-part identity, SwiGLU against the plain MoE oracle on the gate and
+    up rows (a swapped gate/up or a row offset fails), the weighted combine
+    against one-hot weights and numpy's einsum.
 """
 from fractions import Fraction
 
@@ -351,3 +356,107 @@ def test_moe_reduces_to_single_expert_matvecs(oracle_lib):
             assert np.array_equal(y1[b, s], r1[0]) and np.array_equal(y2[b, s], r2[0])
     with pytest.raises(ValueError):
         o.moe("q4_0", Wall, stride, E, N, K, np.array([[5, 0]], dtype=np.int32), xt[:1])
+
+
+# ------------------------------------------------------------------ fused steps
+def test_matvec_i8_lut_identity_and_permutation(oracle_lib):
+    o = oracle_lib
+    g = np.random.default_rng(31)
+    N, K, B = 9, 64, 3
+    W = g.integers(-127, 128, size=(N, K), dtype=np.int8)
+    x = g.integers(-127, 128, size=(B, K), dtype=np.int8)
+    mult = g.integers(1 << 30, 1 << 31, size=N).astype(np.int32)
+    shift = g.integers(8, 16, size=N).astype(np.int32)
+    acc, y = o.matvec_i8(W, x, mult, shift)
+    ident = (np.arange(256) - 128).astype(np.int8)
+    acc2, y2 = o.matvec_i8_lut(W, x, mult, shift, ident)
+    assert np.array_equal(acc, acc2) and np.array_equal(y, y2)
+    perm = g.permutation(256).astype(np.int64) - 128
+    perm = perm.astype(np.int8)
+    _, y3 = o.matvec_i8_lut(W, x, mult, shift, perm)
+    assert np.array_equal(y3, perm[y.astype(np.int64) + 128])
+    assert len(np.unique(y)) > 3          # the case spans several table entries
+
+
+def test_silu_library_and_identities(oracle_lib):
+    from scipy.special import expit
+    o = oracle_lib
+    assert o.silu(0.0) == 0.0
+    for z in [-30.0, -5.5, -1.0, -0.125, 0.3, 1.0, 2.0, 7.25, 40.0]:
+        assert abs(o.silu(z) - z * expit(z)) <= 4e-16 * max(1.0, abs(z)), z
+        # silu(z) - silu(-z) = z (sigma(z) + sigma(-z) = 1)
+        assert abs((o.silu(z) - o.silu(-z)) - z) <= 4e-16 * max(1.0, abs(z)), z
+    assert o.silu(800.0) == 800.0 and o.silu(-800.0) == 0.0
+
+
+def _moe_case(g, fmt, E, rows, K, pad=0):
+    per = wl.block_bytes(fmt, rows, K)
+    stride = per + pad
+    Wall = np.zeros(E * stride, dtype=np.uint8)
+    for e in range(E):
+        Wall[e * stride:e * stride + per] = _random_blocks(g, fmt, rows, K).reshape(-1)
+    return Wall, per, stride
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_swiglu_reduces_to_gate_and_up_matvecs(oracle_lib, fmt):
+    from scipy.special import expit
+    o = oracle_lib
+    g = np.random.default_rng(41)
+    E, F, K = 4, 6, 64
+    Wall, per, stride = _moe_case(g, fmt, E, 2 * F, K, pad=20)
+    ids = np.array([[3, 1], [1, 2]], dtype=np.int32)
+    x = g.standard_normal((2, K)).astype(np.float32)
+    h, gg, uu, Sg, Su = o.moe_swiglu(fmt, Wall, stride, E, F, K, ids, x)
+    y, S = o.moe(fmt, Wall, stride, E, 2 * F, K, ids, x)
+    assert np.array_equal(gg, y[:, :, :F]) and np.array_equal(uu, y[:, :, F:])
+    assert np.array_equal(Sg, S[:, :, :F]) and np.array_equal(Su, S[:, :, F:])
+    ref = y[:, :, :F] * expit(y[:, :, :F]) * y[:, :, F:]
+    assert np.allclose(h, ref, rtol=1e-14, atol=1e-300)
+    swapped = y[:, :, F:] * expit(y[:, :, F:]) * y[:, :, :F]
+    assert not np.allclose(h, swapped, rtol=1e-6)
+    rows = np.array([5, 0, 2], dtype=np.int64)
+    hr = o.moe_swiglu(fmt, Wall, stride, E, F, K, ids, x, rows=rows)[0]
+    assert np.array_equal(hr, h[:, :, rows])
+
+
+def test_moe_swiglu_hand_case(oracle_lib):
+    """One Q8_0 expert, F = 1, K = 32: gate row q_0 = 3, up row q_1 = -2,
+    d = 1, so g = 3 x_0 and u = -2 x_1 exactly."""
+    from scipy.special import expit
+    o = oracle_lib
+    blk = np.zeros((2, 34), dtype=np.uint8)
+    blk[:, 1] = 0x3C                      # d = 1.0 (fp16 0x3C00)
+    blk[0, 2] = 3
+    blk[1, 3] = np.uint8(256 - 2)
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, 0], x[0, 1] = 0.75, 1.5
+    h, gg, uu, _, _ = o.moe_swiglu("q8_0", blk.reshape(-1), 68, 1, 1, 32, np.zeros((1, 1), np.int32), x)
+    assert gg[0, 0, 0] == 2.25 and uu[0, 0, 0] == -3.0
+    assert abs(h[0, 0, 0] - 2.25 * expit(2.25) * -3.0) <= 1e-15
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_moe_combine_one_hot_and_einsum(oracle_lib, fmt):
+    o = oracle_lib
+    g = np.random.default_rng(51)
+    E, N, K, B, T = 5, 7, 96, 3, 4
+    Wall, per, stride = _moe_case(g, fmt, E, N, K)
+    ids = np.array([[0, 4, 2, 1], [3, 3, 0, 4], [2, 1, 0, 3]], dtype=np.int32)
+    xs = g.standard_normal((B, T, K)).astype(np.float32)
+    y, S = o.moe(fmt, Wall, stride, E, N, K, ids, None, x_slots=xs)
+    for s in range(T):
+        w = np.zeros((B, T), dtype=np.float32)
+        w[:, s] = 1.0
+        out, So = o.moe_combine(fmt, Wall, stride, E, N, K, ids, w, x_slots=xs)
+        assert np.array_equal(out, y[:, s]) and np.array_equal(So, S[:, s])
+    w = g.random((B, T)).astype(np.float32)
+    w[1, 2] = -0.5                        # a negative weight counts by magnitude in S
+    out, So = o.moe_combine(fmt, Wall, stride, E, N, K, ids, w, x_slots=xs)
+    w64 = w.astype(np.float64)
+    assert np.allclose(out, np.einsum("bs,bsn->bn", w64, y), rtol=1e-13, atol=1e-13)
+    assert np.allclose(So, np.einsum("bs,bsn->bn", np.abs(w64), S), rtol=1e-13)
+    xt = g.standard_normal((B, K)).astype(np.float32)
+    out_t, _ = o.moe_combine(fmt, Wall, stride, E, N, K, ids, w, x_tokens=xt)
+    yt, _ = o.moe(fmt, Wall, stride, E, N, K, ids, xt)
+    assert np.allclose(out_t, np.einsum("bs,bsn->bn", w64, yt), rtol=1e-13, atol=1e-13)
