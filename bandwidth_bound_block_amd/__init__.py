@@ -14,14 +14,18 @@ Entry points (same names as the C ABI):
                                    (PATH_AUTO / PATH_FMA / PATH_MFMA)
   qmv_matvec_xt                    the same with fp32, fp16 or bf16 activations
   qmv_i8_requant                   int8 matvec + per-channel gemmlowp requant
+  qmv_i8_requant_lut               the same through a frozen int8 lookup table
   qmv_moe                          grouped MoE expert matvec
+  qmv_moe_swiglu                   MoE gate||up with the SwiGLU step fused
+  qmv_moe_combine                  MoE down with the router-weighted combine
   qmv_dequant                      stored blocks -> fp32 (test/inspection aid)
 """
 import ctypes
 import os
 
 __all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
-           "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_moe",
+           "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_i8_requant_lut",
+           "qmv_moe", "qmv_moe_swiglu", "qmv_moe_combine",
            "qmv_dequant", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
            "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
 
@@ -70,8 +74,14 @@ def _open():
     L.qmv_matvec_xt.restype = i32
     L.qmv_i8_requant.argtypes = [P, i64, i64, P, i64, i32, P, P, P, i64, P]
     L.qmv_i8_requant.restype = i32
+    L.qmv_i8_requant_lut.argtypes = [P, i64, i64, P, i64, i32, P, P, P, P, i64, P]
+    L.qmv_i8_requant_lut.restype = i32
     L.qmv_moe.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P, i64, i64, P, P]
     L.qmv_moe.restype = i32
+    L.qmv_moe_swiglu.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P, i64, i64, P, P]
+    L.qmv_moe_swiglu.restype = i32
+    L.qmv_moe_combine.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, P, i32, i32, P, i64, i64, P, P]
+    L.qmv_moe_combine.restype = i32
     L.qmv_dequant.argtypes = [ctypes.c_int, P, i64, i64, P, P]
     L.qmv_dequant.restype = i32
     L.qmv_chain.argtypes = [ctypes.c_int, P, i32, P, ctypes.c_size_t, P]
@@ -213,6 +223,16 @@ def qmv_matvec_xt(fmt, W, n_rows, n_cols, x, path=PATH_AUTO, y=None, stream=None
 def qmv_i8_requant(W, x, mult, shift, y=None, stream=None):
     """int8 [N, K] weights x int8 [K] or [B, K] activations, per-row requant
     (mult, shift int32 [N]) -> int8 [B, N]."""
+    return _i8(W, x, mult, shift, None, y, stream)
+
+
+def qmv_i8_requant_lut(W, x, mult, shift, lut, y=None, stream=None):
+    """qmv_i8_requant with the outputs mapped through a frozen table:
+    y = lut[y_requant + 128]; lut int8 [256] on the GPU."""
+    return _i8(W, x, mult, shift, lut, y, stream)
+
+
+def _i8(W, x, mult, shift, lut, y, stream):
     torch = _torch()
     _dev(W, "W", torch.int8)
     _dev(x, "x", torch.int8)
@@ -230,18 +250,19 @@ def qmv_i8_requant(W, x, mult, shift, y=None, stream=None):
     y2, By, ldy = _rows2d(y, "y", N)
     if By != B:
         raise ValueError("y must have as many rows as x")
-    _check(_lib.qmv_i8_requant(W.data_ptr(), N, K, x2.data_ptr(), ldx, B, mult.data_ptr(), shift.data_ptr(),
-                               y2.data_ptr(), ldy, _stream(stream)))
+    if lut is None:
+        _check(_lib.qmv_i8_requant(W.data_ptr(), N, K, x2.data_ptr(), ldx, B, mult.data_ptr(), shift.data_ptr(),
+                                   y2.data_ptr(), ldy, _stream(stream)))
+    else:
+        _dev(lut, "lut", torch.int8)
+        if lut.numel() != 256 or not lut.is_contiguous():
+            raise ValueError("lut must be a contiguous int8 [256] tensor")
+        _check(_lib.qmv_i8_requant_lut(W.data_ptr(), N, K, x2.data_ptr(), ldx, B, mult.data_ptr(), shift.data_ptr(),
+                                       lut.data_ptr(), y2.data_ptr(), ldy, _stream(stream)))
     return y
 
 
-def qmv_moe(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, x, y=None,
-            stream=None):
-    """Grouped MoE expert matvec.
-
-    expert_ids: int32 [B, top_k] on the GPU.  x: float32 [B, K] (one input per
-    token, gate/up) or [B, top_k, K] (one input per token and slot, down).
-    Returns y float32 [B, top_k, n_rows]."""
+def _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, rows, n_cols, expert_ids, x):
     torch = _torch()
     fmt = _fmt(fmt)
     _dev(W_experts, "W_experts", torch.uint8)
@@ -258,8 +279,59 @@ def qmv_moe(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expe
         st_tok, st_slot = T * n_cols, n_cols
     else:
         raise ValueError("x must be [B, K] or [B, top_k, K]")
-    if W_experts.numel() < (n_experts - 1) * expert_stride_bytes + n_rows * (n_cols // 32) * BLOCK_BYTES.get(fmt, 0):
+    if W_experts.numel() < (n_experts - 1) * expert_stride_bytes + rows * (n_cols // 32) * BLOCK_BYTES.get(fmt, 0):
         raise ValueError("W_experts is smaller than n_experts expert matrices")
+    return torch, fmt, B, T, st_tok, st_slot
+
+
+def qmv_moe_swiglu(fmt, W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, x, h=None,
+                   stream=None):
+    """MoE gate||up with SwiGLU: every expert holds 2*n_ff rows (gate rows,
+    then up rows); returns h float32 [B, top_k, n_ff] = SiLU(gate x) * (up x).
+    x as qmv_moe."""
+    torch, fmt, B, T, st_tok, st_slot = _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, 2 * n_ff, n_cols,
+                                                  expert_ids, x)
+    if h is None:
+        h = torch.empty((B, T, n_ff), dtype=torch.float32, device=x.device)
+    _dev(h, "h", torch.float32)
+    if h.shape != (B, T, n_ff) or not h.is_contiguous():
+        raise ValueError("h must be a contiguous [B, top_k, n_ff] tensor")
+    _check(_lib.qmv_moe_swiglu(fmt, W_experts.data_ptr(), expert_stride_bytes, n_experts, n_ff, n_cols,
+                               expert_ids.data_ptr(), B, T, x.data_ptr(), st_tok, st_slot, h.data_ptr(),
+                               _stream(stream)))
+    return h
+
+
+def qmv_moe_combine(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, weights, x,
+                    out=None, stream=None):
+    """MoE down with the router-weighted combine: out float32 [B, n_rows] =
+    sum_s weights[b, s] * DEQ(W_{ids[b,s]}) x_{b,s}.  weights float32
+    [B, top_k] on the GPU; x as qmv_moe."""
+    torch, fmt, B, T, st_tok, st_slot = _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols,
+                                                  expert_ids, x)
+    _dev(weights, "weights", torch.float32)
+    if weights.shape != (B, T) or not weights.is_contiguous():
+        raise ValueError("weights must be a contiguous [B, top_k] tensor")
+    if out is None:
+        out = torch.empty((B, n_rows), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    if out.shape != (B, n_rows) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, n_rows] tensor")
+    _check(_lib.qmv_moe_combine(fmt, W_experts.data_ptr(), expert_stride_bytes, n_experts, n_rows, n_cols,
+                                expert_ids.data_ptr(), weights.data_ptr(), B, T, x.data_ptr(), st_tok, st_slot,
+                                out.data_ptr(), _stream(stream)))
+    return out
+
+
+def qmv_moe(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, x, y=None,
+            stream=None):
+    """Grouped MoE expert matvec.
+
+    expert_ids: int32 [B, top_k] on the GPU.  x: float32 [B, K] (one input per
+    token, gate/up) or [B, top_k, K] (one input per token and slot, down).
+    Returns y float32 [B, top_k, n_rows]."""
+    torch, fmt, B, T, st_tok, st_slot = _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols,
+                                                  expert_ids, x)
     if y is None:
         y = torch.empty((B, T, n_rows), dtype=torch.float32, device=x.device)
     _dev(y, "y", torch.float32)

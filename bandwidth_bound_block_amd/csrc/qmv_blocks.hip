@@ -318,20 +318,24 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
 // to 8 (token, slot) pairs routed to it (one group in the usual case of
 // distinct ids per token), in pair order.
 constexpr int kMoeMaxPairs = 128;
+constexpr int kMoeMaxSlots = 16;     // top_k
 constexpr int kMoeStaticLds = 4096;  // s_ids/s_first/s_members/scalars, rounded up
 
 // One chunk of up to BC member pairs of expert We: stage their activations
-// and stream the workgroup's row tiles [tb, te) once, writing each member's
-// output rows.  XU > 0 (the activations fit in XU 16-byte loads per thread
-// and are 16-byte aligned): the activation loads are issued first, then the
-// first weight loads, and only then are the activations stored to LDS, so
-// the two latencies overlap (loads complete in order).  XU == 0: staged by
-// the looping stager, then the weights.  Ends with a barrier.
-template <class F, int BC, int LPR, int NW, int XU, int PD = 2>
+// and stream the workgroup's row tiles [tb, te) once.  A row tile holds G
+// output rows; output row i reads matrix row i, and with RS = 2 also row
+// N + i (the up row paired with gate row i of a row-concatenated gate||up
+// expert).  When a row is done, emit(b, row, t0, t1) receives member b's
+// sums of the row (t1: of row N + row when RS = 2) in the row's first lane.
+// XU > 0 (the activations fit in XU 16-byte loads per thread and are
+// 16-byte aligned): the activation loads are issued first, then the first
+// weight loads, and only then are the activations stored to LDS, so the two
+// latencies overlap (loads complete in order).  XU == 0: staged by the
+// looping stager, then the weights.  Ends with a barrier.
+template <class F, int BC, int LPR, int NW, int XU, int PD, int RS, class Emit>
 __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_t N, int nb, int64_t tb, int64_t te,
-                                          const float* const (&xcol)[BC], int w, bool xvec,
-                                          const int* __restrict__ members, float* __restrict__ y, float* xs,
-                                          float* sx) {
+                                          const float* const (&xcol)[BC], int w, bool xvec, float* xs, float* sx,
+                                          Emit&& emit) {
     constexpr int G = 64 / LPR;
     const int t = threadIdx.x;
     const int lane = t & 63;
@@ -345,31 +349,38 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
     auto advance = [&](int64_t& tile, int& st) {
         if (++st == T) { st = 0; tile += NW; }
     };
-    auto load_next = [&](Raw& r) {
+    auto load_next = [&](Raw (&r)[RS]) {
         const int64_t tile = min(ltile, te - 1);       // past the range: re-read a loaded block
         const int j = min(li + LPR * (ltile < te ? lt : 0), nb - 1);
         const int64_t row = min(tile * G + seg, N - 1);
-        F::fetch(We, row * nb + j, r);
+#pragma unroll
+        for (int k = 0; k < RS; ++k) F::fetch(We, (row + k * N) * nb + j, r[k]);
         if (ltile < te) advance(ltile, lt);
     };
-    float acc[BC];
+    float acc[RS][BC];
 #pragma unroll
-    for (int b = 0; b < BC; ++b) acc[b] = 0.f;
-    auto compute_step = [&](int64_t tile, int st, const Raw& r) {
+    for (int k = 0; k < RS; ++k)
+#pragma unroll
+        for (int b = 0; b < BC; ++b) acc[k][b] = 0.f;
+    auto compute_step = [&](int64_t tile, int st, const Raw (&r)[RS]) {
         const int j = li + LPR * st;
         const bool valid = j < nb;
         const int jc = valid ? j : nb - 1;
-        float d[1], m[1];
-        uint32_t c[1][8];
-        F::decode(r, d[0], m[0], c[0]);
-        float s[1][BC];
-        dot_multi<F, 1, BC>(c, xs + jc * kXPad, nb * kXPad, s, w);
+        float d[RS], m[RS];
+        uint32_t c[RS][8];
+#pragma unroll
+        for (int k = 0; k < RS; ++k) F::decode(r[k], d[k], m[k], c[k]);
+        float s[RS][BC];
+        dot_multi<F, RS, BC>(c, xs + jc * kXPad, nb * kXPad, s, w);
 #pragma unroll
         for (int b = 0; b < BC; ++b) {
             if (b < w) {
                 const float sxb = F::kNeedSx ? sx[b * nb + jc] : 0.f;
-                const float upd = Term<F>::add(acc[b], d[0], m[0], s[0][b], sxb);
-                acc[b] = valid ? upd : acc[b];
+#pragma unroll
+                for (int k = 0; k < RS; ++k) {
+                    const float upd = Term<F>::add(acc[k][b], d[k], m[k], s[k][b], sxb);
+                    acc[k][b] = valid ? upd : acc[k][b];
+                }
             }
         }
         if (st == T - 1) {
@@ -377,15 +388,17 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
 #pragma unroll
             for (int b = 0; b < BC; ++b) {
                 if (b < w) {
-                    const float tot = segment_sum<LPR>(acc[b]);
-                    if (li == 0 && row < N) y[(int64_t)members[b] * N + row] = tot;
+                    const float t0 = segment_sum<LPR>(acc[0][b]);
+                    const float t1 = RS > 1 ? segment_sum<LPR>(acc[RS - 1][b]) : 0.f;
+                    if (li == 0 && row < N) emit(b, row, t0, t1);
                 }
-                acc[b] = 0.f;
+#pragma unroll
+                for (int k = 0; k < RS; ++k) acc[k][b] = 0.f;
             }
         }
     };
 
-    Raw buf[PD];
+    Raw buf[PD][RS];
     const int K4 = nb * 8;
     if constexpr (XU > 0) {
         // every column slot is loaded and stored (inactive ones repeat
@@ -430,14 +443,20 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
     __syncthreads();   // xs is restaged by the next chunk
 }
 
+// SiLU(g) = g / (1 + e^-g), in fp32 on the device (expf of the device
+// library); g = -inf or +inf give -0 and +inf, NaN stays NaN.
+__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+
 // Grouped expert matvec.  Workgroup (bx, u) serves the u-th distinct id
 // of the (token, slot) pairs, in first-occurrence order, and the bx-th
 // range of that expert's row tiles: it groups the pairs itself (O(P) per
 // thread for P <= 128 pairs; no prologue kernel, no workspace), then runs
 // moe_chunk for up to BC member pairs at a time.  Per (row, pair) the
 // arithmetic is the dense kernel's, so each output equals a single-expert
-// dense call bitwise.
-template <class F, int BC, int LPR, int NW, int XU, int PD>
+// dense call bitwise.  SW (SwiGLU): every expert holds 2N rows, gate rows
+// then up rows, and output row i is SiLU(gate_i x) * (up_i x), both sums
+// again the dense kernel's.
+template <class F, int BC, int LPR, int NW, int XU, int PD, bool SW = false>
 __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
                                                        int n_experts, int64_t N, int nb,
                                                        const int32_t* __restrict__ ids, int P, int top_k,
@@ -508,11 +527,196 @@ __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict_
             const int pr = s_members[c0 + (b < w ? b : 0)];
             xcol[b] = x + (int64_t)(pr / top_k) * xs_tok + (int64_t)(pr % top_k) * xs_slot;
         }
+        const int* mem = s_members + c0;
+        auto emit = [&](int b, int64_t row, float t0, float t1) {
+            y[(int64_t)mem[b] * N + row] = SW ? silu(t0) * t1 : t0;
+        };
+        constexpr int RS = SW ? 2 : 1;
         if (c0 == 0 && XU > 0 && xvec)
-            moe_chunk<F, BC, LPR, NW, XU, PD>(We, N, nb, tb, te, xcol, w, true, s_members + c0, y, xs, sx);
+            moe_chunk<F, BC, LPR, NW, XU, PD, RS>(We, N, nb, tb, te, xcol, w, true, xs, sx, emit);
         else
-            moe_chunk<F, BC, LPR, NW, 0, PD>(We, N, nb, tb, te, xcol, w, xvec != 0, s_members + c0, y, xs, sx);
+            moe_chunk<F, BC, LPR, NW, 0, PD, RS>(We, N, nb, tb, te, xcol, w, xvec != 0, xs, sx, emit);
     }
+}
+
+// MoE down projection with the router-weighted combine, token-major:
+// workgroup (bx, b) computes rows of out[b] = sum_s w[b][s] * DEQ(W_{e_s}) x_{b,s}
+// over the top_k slots of token b, in slot order.  The slots' activation
+// vectors are staged together (in chunks of SC slots when they do not all
+// fit the LDS); each wave then streams its row tiles slot after slot with one
+// pipeline running across the slots, and the first lane of each row keeps
+// the row's running sum in LDS (the same lane owns the row in every slot).
+// Each slot's row sum is the dense kernel's (bitwise the qmv_moe output),
+// and the combine is fma(w_s, y_s, acc) from s = 0 up.  Every (token, slot)
+// streams its expert: experts shared by several tokens are read once per
+// token, which is what keeps the combine free of atomics and workspace.
+template <class F, int LPR, int NW, int PD>
+__global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
+                                                               int n_experts, int64_t N, int nb,
+                                                               const int32_t* __restrict__ ids,
+                                                               const float* __restrict__ wts, int top_k,
+                                                               const float* __restrict__ x, int64_t xs_tok,
+                                                               int64_t xs_slot, float* __restrict__ out, int xvec,
+                                                               int SC, int rows_wg) {
+    __shared__ const uint8_t* s_base[kMoeMaxSlots];
+    __shared__ float s_w[kMoeMaxSlots];
+    __shared__ int s_bad;
+    extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after the static LDS
+    constexpr int G = 64 / LPR;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int seg = lane / LPR, li = lane % LPR;
+    const int T = (nb + LPR - 1) / LPR;
+    const int b = blockIdx.y;
+    const int64_t ntiles = (N + G - 1) / G;
+    const int64_t per_wg = rows_wg / G;
+    const int64_t tb = (int64_t)blockIdx.x * per_wg;
+    const int64_t te = min(ntiles, tb + per_wg);
+    if (tb >= te) return;
+    const int per_col = nb * (kXPad + (F::kNeedSx ? 1 : 0));
+    float* xs = lds;                          // [SC][nb][kXPad]
+    float* sx = lds + SC * nb * kXPad;        // [SC][nb]
+    float* oacc = lds + SC * per_col;         // running sums of rows tb*G ...
+    const int64_t r0 = tb * G;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    if (tid < top_k) {
+        const int e = ids[b * top_k + tid];
+        const bool eb = e < 0 || e >= n_experts;
+        if (eb) s_bad = 1;
+        s_base[tid] = Wx + (int64_t)(eb ? 0 : e) * estride;
+        s_w[tid] = wts[b * top_k + tid];
+    }
+    using Raw = typename F::Raw;
+    const int64_t wtiles = te - tb;
+    for (int s0 = 0; s0 < top_k; s0 += SC) {
+        const int sc = min(SC, top_k - s0);
+        // the chunk's activation vectors (previous chunk's reads are done:
+        // the loop below ends every wave's use of xs before this barrier)
+        __syncthreads();
+        {
+            // chunk i of the sc concatenated vectors, four loads in flight per thread
+            const float* xb = x + (int64_t)b * xs_tok + (int64_t)s0 * xs_slot;
+            const int per = xvec ? nb * 8 : nb * 32;          // float4 chunks or floats per vector
+            const int total = sc * per;
+            for (int i0 = tid; i0 < total; i0 += 4 * 64 * NW) {
+                int k4[4], c4[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int i = min(i0 + u * 64 * NW, total - 1);
+                    k4[u] = i / per;
+                    c4[u] = i - k4[u] * per;
+                }
+                if (xvec) {
+                    float4 v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        v[u] = *reinterpret_cast<const float4*>(xb + (int64_t)k4[u] * xs_slot + 4 * c4[u]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = 4 * c4[u];
+                        if (i0 + u * 64 * NW < total)
+                            *reinterpret_cast<float4*>(xs + k4[u] * nb * kXPad + (e >> 5) * kXPad + (e & 31)) = v[u];
+                    }
+                } else {
+                    float v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) v[u] = xb[(int64_t)k4[u] * xs_slot + c4[u]];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = c4[u];
+                        if (i0 + u * 64 * NW < total) xs[k4[u] * nb * kXPad + (e >> 5) * kXPad + (e & 31)] = v[u];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (F::kNeedSx) {
+            block_sums<64 * NW>(xs, sx, sc * nb);
+            __syncthreads();
+        }
+        // this wave's steps: slots of the chunk (outer), its row tiles
+        // tb + wave, + NW, ... (middle), the row's T steps (inner)
+        const int64_t my_tiles = wave < wtiles ? (wtiles - wave + NW - 1) / NW : 0;
+        const int64_t nsteps = my_tiles * T * sc;
+        if (nsteps == 0) continue;
+        struct Cur {
+            int s, t;
+            int64_t tile;
+        };
+        Cur lc{0, 0, tb + wave}, cc = lc;
+        auto advance = [&](Cur& k) {
+            if (++k.t < T) return;
+            k.t = 0;
+            k.tile += NW;
+            if (k.tile >= te) {
+                k.tile = tb + wave;
+                ++k.s;
+            }
+        };
+        int64_t lrem = nsteps;
+        const uint8_t* lW = s_base[s0];
+        auto load_next = [&](Raw& r) {
+            const int64_t row = min(lc.tile * G + seg, N - 1);
+            const int j = min(li + LPR * lc.t, nb - 1);
+            F::fetch(lW, row * nb + j, r);
+            if (lrem > 1) {   // past the last step: re-read it (in cache)
+                --lrem;
+                const int so = lc.s;
+                advance(lc);
+                if (lc.s != so) lW = s_base[s0 + lc.s];
+            }
+        };
+        float acc = 0.f;
+        auto compute = [&](const Raw& r) {
+            const int j = li + LPR * cc.t;
+            const bool valid = j < nb;
+            const int jc = valid ? j : nb - 1;
+            float d, m;
+            uint32_t c[1][8];
+            F::decode(r, d, m, c[0]);
+            float sd[1][1];
+            dot_multi<F, 1, 1>(c, xs + cc.s * nb * kXPad + jc * kXPad, 0, sd, 1);
+            const float sxb = F::kNeedSx ? sx[cc.s * nb + jc] : 0.f;
+            const float upd = Term<F>::add(acc, d, m, sd[0][0], sxb);
+            acc = valid ? upd : acc;
+            if (cc.t == T - 1) {
+                const float tot = segment_sum<LPR>(acc);
+                const int64_t row = cc.tile * G + seg;
+                if (li == 0 && row < N) {
+                    float* p = oacc + (row - r0);
+                    const float ws = s_w[s0 + cc.s];
+                    *p = (s0 + cc.s == 0) ? ws * tot : __builtin_fmaf(ws, tot, *p);
+                }
+                acc = 0.f;
+            }
+        };
+        Raw buf[PD];
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
+        int64_t crem = nsteps;
+#define QMV_MOEC_STEP(P)                                   \
+    {                                                      \
+        load_next(buf[((P) + PD - 1) % PD]);               \
+        __builtin_amdgcn_sched_barrier(0);                 \
+        compute(buf[(P)]);                                 \
+        if (--crem == 0) break;                            \
+        advance(cc);                                       \
+    }
+        static_assert(PD >= 2 && PD <= 4, "pipeline depth");
+        while (true) {
+            QMV_MOEC_STEP(0)
+            QMV_MOEC_STEP(1)
+            if constexpr (PD >= 3) QMV_MOEC_STEP(2)
+            if constexpr (PD >= 4) QMV_MOEC_STEP(3)
+        }
+#undef QMV_MOEC_STEP
+    }
+    __syncthreads();
+    const float qnan = __builtin_nanf("");
+    const int64_t r1 = min(te * G, N);
+    for (int64_t row = r0 + tid; row < r1; row += 64 * NW) out[(int64_t)b * N + row] = s_bad ? qnan : oacc[row - r0];
 }
 
 // One thread per block: out[g*32 + e] = value e of block g.
@@ -754,12 +958,12 @@ int32_t dequant(const void* W, int64_t N, int64_t K, float* out, void* stream) {
 // ranges split each expert's row tiles so that ranges x expected groups
 // fill the GPU once.  Expected groups: all P (spread), or the distinct ids
 // that P uniformly routed pairs reach on average, E (1 - (1 - 1/E)^P).
-template <class F, int BC, int LPR, int XU, int PD>
+template <class F, int BC, int LPR, int XU, int PD, bool SW>
 int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                    int P, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                    bool spread, hipStream_t st) {
     constexpr int NW = 4;
-    auto kern = moe_kernel<F, BC, LPR, NW, XU, PD>;
+    auto kern = moe_kernel<F, BC, LPR, NW, XU, PD, SW>;
     static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
     if (!dyn_max) {
         hipFuncAttributes fa;
@@ -796,17 +1000,17 @@ int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N,
 // too little work per workgroup for that, and two columns per pass over a
 // grid sized for every pair measured faster.  Activations staged
 // straight-line (XU 16-byte loads per thread) up to K = 8192.
-template <class F, int LPR, int XU>
+template <class F, int LPR, int XU, bool SW>
 int32_t launch_moe_bc(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                       int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
     const int P = batch * top_k;
     const size_t per_col = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     if (batch > 1 && batch < 8 && nb < 64 && 2 * per_col + kMoeStaticLds <= (size_t)kLdsMax)
-        return launch_moe<F, 2, LPR, XU, 2>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec,
-                                            true, st);
-    return launch_moe<F, 1, LPR, XU, 3>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec,
-                                        batch == 1, st);
+        return launch_moe<F, 2, LPR, XU, 2, SW>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y,
+                                                xvec, true, st);
+    return launch_moe<F, 1, LPR, XU, 3, SW>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec,
+                                            batch == 1, st);
 }
 
 // Batch 1: the pairs of one token need no grouping (a duplicated id only
@@ -834,34 +1038,83 @@ int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int6
     return check_launch("qmv_moe");
 }
 
-template <class F, int LPR>
+// SW: the SwiGLU form takes the grouping kernel at every batch.
+template <class F, int LPR, bool SW>
 int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                       int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
     const int K4 = nb * 8;   // 16-byte chunks of one activation row; 256 threads
-    if (batch == 1 && xvec && K4 <= 4 * 256)
+    if (!SW && batch == 1 && xvec && K4 <= 4 * 256)
         return launch_moe_pairs<F, LPR, 4>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
-    if (batch == 1 && xvec && K4 <= 16 * 256)
+    if (!SW && batch == 1 && xvec && K4 <= 16 * 256)
         return launch_moe_pairs<F, LPR, 16>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
     if (K4 <= 2 * 256)
-        return launch_moe_bc<F, LPR, 2>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
+        return launch_moe_bc<F, LPR, 2, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                            xvec, st);
     if (K4 <= 8 * 256)
-        return launch_moe_bc<F, LPR, 8>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
-    return launch_moe_bc<F, LPR, 0>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
+        return launch_moe_bc<F, LPR, 8, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                            xvec, st);
+    return launch_moe_bc<F, LPR, 0, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec,
+                                        st);
 }
 
+// The combine kernel's grid: (row ranges, tokens).  Ranges x tokens fill
+// the GPU once; a range holds at most kCombineRows rows (their running sums
+// sit in LDS beside SC staged slot vectors).
+constexpr int kCombineRows = 4096;
+
+template <class F, int LPR>
+int32_t launch_combine(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
+                       const float* wts, int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot,
+                       float* out, int xvec, hipStream_t st) {
+    constexpr int NW = 4, PD = 3;
+    constexpr int G = 64 / LPR;
+    auto kern = moe_combine_kernel<F, LPR, NW, PD>;
+    static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
+    if (!dyn_max) {
+        hipFuncAttributes fa;
+        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) != hipSuccess)
+            return fail(QMV_EHIP, "qmv_moe_combine: cannot query the kernel: %s", hipGetErrorString(hipGetLastError()));
+        const size_t m = kLdsMax - fa.sharedSizeBytes;
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)m) != hipSuccess)
+            return fail(QMV_EHIP, "qmv_moe_combine: cannot raise the LDS limit: %s",
+                        hipGetErrorString(hipGetLastError()));
+        dyn_max = m;
+    }
+    const size_t per_col = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    const size_t sums_max = (size_t)(kCombineRows + 64) * sizeof(float);   // a range rounds up to whole tiles
+    if (per_col + sums_max > dyn_max)
+        return fail(QMV_EINVAL, "qmv_moe_combine: n_cols %d too large for one activation row in LDS", nb * 32);
+    const int SC = (int)std::min<size_t>((size_t)top_k, (dyn_max - sums_max) / per_col);
+    const int64_t ntiles = (N + G - 1) / G;
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, SC * per_col + sums_max);
+    const int64_t min_ranges = (ntiles * G + kCombineRows - 1) / kCombineRows;
+    const int64_t gx = std::max<int64_t>(
+        min_ranges, std::min<int64_t>(ntiles, std::max<int64_t>(1, (int64_t)device_cu_count() * per_cu / batch)));
+    const int64_t per_wg = (ntiles + gx - 1) / gx;
+    const int rows_wg = (int)(per_wg * G);
+    const size_t lds = SC * per_col + (size_t)rows_wg * sizeof(float);
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)batch), dim3(64 * NW), lds, st, Wx, estride, n_experts, N, nb,
+                       ids, wts, top_k, x, xs_tok, xs_slot, out, xvec, SC, rows_wg);
+    return check_launch("qmv_moe_combine");
+}
+
+// Argument checks shared by the MoE entry points.  rows: rows of one
+// expert matrix; n_out: rows of one output vector.
 template <class F>
-int32_t moe(const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64_t K, const int32_t* ids,
-            int32_t batch, int32_t top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, void* stream) {
-    const char* name = "qmv_moe";
+int32_t moe_check(const char* name, const void* Wx, int64_t estride, int32_t n_experts, int64_t rows, int64_t K,
+                  const int32_t* ids, int32_t batch, int32_t top_k, const float* x, int64_t xs_tok, int64_t xs_slot,
+                  const float* y) {
     if (!Wx || !ids || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (n_experts < 1) return fail(QMV_EINVAL, "%s: n_experts must be >= 1", name);
-    if (N < 1 || K < 32 || K % 32) return fail(QMV_EINVAL, "%s: bad matrix shape %lld x %lld", name, (long long)N, (long long)K);
+    if (rows < 1 || K < 32 || K % 32)
+        return fail(QMV_EINVAL, "%s: bad matrix shape %lld x %lld", name, (long long)rows, (long long)K);
     if (batch < 1 || batch > 8) return fail(QMV_EINVAL, "%s: batch must be in 1..8 (got %d)", name, batch);
     if (top_k < 1 || top_k > 16) return fail(QMV_EINVAL, "%s: top_k must be in 1..16 (got %d)", name, top_k);
     const int64_t nb = K / 32;
-    if (nb > (1 << 26) || N > ((int64_t)1 << 40) / nb) return fail(QMV_EINVAL, "%s: matrix too large", name);
-    const int64_t mbytes = N * nb * F::kBytes;
+    if (nb > (1 << 26) || rows > ((int64_t)1 << 40) / nb) return fail(QMV_EINVAL, "%s: matrix too large", name);
+    const int64_t mbytes = rows * nb * F::kBytes;
     if (estride < mbytes || estride % 4)
         return fail(QMV_EINVAL, "%s: expert_stride_bytes (%lld) must be >= %lld and a multiple of 4", name,
                     (long long)estride, (long long)mbytes);
@@ -871,16 +1124,62 @@ int32_t moe(const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64
     if (top_k > 1 && xs_slot != 0 && xs_slot < K) return fail(QMV_EINVAL, "%s: x_stride_slot must be 0 or >= n_cols", name);
     if (xs_slot < 0) return fail(QMV_EINVAL, "%s: x_stride_slot must be >= 0", name);
     if (!aligned(Wx, 4) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ids, 4))
-        return fail(QMV_EALIGN, "%s: W_experts, x, y and expert_ids must be 4-byte aligned", name);
+        return fail(QMV_EALIGN, "%s: W_experts, x, the output and expert_ids must be 4-byte aligned", name);
     const int64_t per_col = nb * (kXPad + (F::kNeedSx ? 1 : 0)) * (int64_t)sizeof(float);
     if (per_col + kMoeStaticLds > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
+    return QMV_OK;
+}
+
+inline int moe_xvec(const float* x, int64_t xs_tok, int64_t xs_slot) {
+    return (aligned(x, 16) && xs_tok % 4 == 0 && xs_slot % 4 == 0) ? 1 : 0;
+}
+
+// SW = false: y[p][i] = DEQ(W_e)[i] x_p (N rows per expert).  SW = true:
+// every expert holds 2N rows and y[p][i] = SiLU(gate_i x_p) * (up_i x_p).
+template <class F, bool SW>
+int32_t moe(const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64_t K, const int32_t* ids,
+            int32_t batch, int32_t top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, void* stream) {
+    const char* name = SW ? "qmv_moe_swiglu" : "qmv_moe";
+    if (SW && N > ((int64_t)1 << 39)) return fail(QMV_EINVAL, "%s: n_ff too large", name);
+    const int32_t rc = moe_check<F>(name, Wx, estride, n_experts, SW ? 2 * N : N, K, ids, batch, top_k, x, xs_tok,
+                                    xs_slot, y);
+    if (rc != QMV_OK) return rc;
+    const int64_t nb = K / 32;
     const uint8_t* W8 = static_cast<const uint8_t*>(Wx);
     hipStream_t st = as_stream(stream);
-    const int xvec = (aligned(x, 16) && xs_tok % 4 == 0 && xs_slot % 4 == 0) ? 1 : 0;
-    if (nb >= 64) return launch_moe_xu<F, 64>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
-    if (nb >= 32) return launch_moe_xu<F, 32>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
-    return launch_moe_xu<F, 8>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec, st);
+    const int xvec = moe_xvec(x, xs_tok, xs_slot);
+    if (nb >= 64)
+        return launch_moe_xu<F, 64, SW>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                        xvec, st);
+    if (nb >= 32)
+        return launch_moe_xu<F, 32, SW>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                        xvec, st);
+    return launch_moe_xu<F, 8, SW>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec,
+                                   st);
+}
+
+template <class F>
+int32_t moe_combine(const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64_t K, const int32_t* ids,
+                    const float* wts, int32_t batch, int32_t top_k, const float* x, int64_t xs_tok, int64_t xs_slot,
+                    float* out, void* stream) {
+    const char* name = "qmv_moe_combine";
+    if (!wts) return fail(QMV_EINVAL, "%s: null pointer", name);
+    if (!aligned(wts, 4)) return fail(QMV_EALIGN, "%s: weights must be 4-byte aligned", name);
+    const int32_t rc = moe_check<F>(name, Wx, estride, n_experts, N, K, ids, batch, top_k, x, xs_tok, xs_slot, out);
+    if (rc != QMV_OK) return rc;
+    const int64_t nb = K / 32;
+    const uint8_t* W8 = static_cast<const uint8_t*>(Wx);
+    hipStream_t st = as_stream(stream);
+    const int xvec = moe_xvec(x, xs_tok, xs_slot);
+    if (nb >= 64)
+        return launch_combine<F, 64>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok, xs_slot, out,
+                                     xvec, st);
+    if (nb >= 32)
+        return launch_combine<F, 32>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok, xs_slot, out,
+                                     xvec, st);
+    return launch_combine<F, 8>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok, xs_slot, out,
+                                xvec, st);
 }
 
 }  // namespace
@@ -957,14 +1256,50 @@ extern "C" int32_t qmv_moe(qmv_fmt fmt, const void* W_experts, int64_t expert_st
                            const float* x, int64_t x_stride_token, int64_t x_stride_slot, float* y, void* stream) {
     switch (fmt) {
     case QMV_Q8_0:
-        return qmv::moe<qmv::Q8_0>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch, top_k,
-                                   x, x_stride_token, x_stride_slot, y, stream);
+        return qmv::moe<qmv::Q8_0, false>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch,
+                                          top_k, x, x_stride_token, x_stride_slot, y, stream);
     case QMV_Q4_0:
-        return qmv::moe<qmv::Q4_0>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch, top_k,
-                                   x, x_stride_token, x_stride_slot, y, stream);
+        return qmv::moe<qmv::Q4_0, false>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch,
+                                          top_k, x, x_stride_token, x_stride_slot, y, stream);
     case QMV_Q4_1:
-        return qmv::moe<qmv::Q4_1>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch, top_k,
-                                   x, x_stride_token, x_stride_slot, y, stream);
+        return qmv::moe<qmv::Q4_1, false>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch,
+                                          top_k, x, x_stride_token, x_stride_slot, y, stream);
     default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_moe: unknown format %d", (int)fmt);
+    }
+}
+
+extern "C" int32_t qmv_moe_swiglu(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes, int32_t n_experts,
+                                  int64_t n_ff, int64_t n_cols, const int32_t* expert_ids, int32_t batch,
+                                  int32_t top_k, const float* x, int64_t x_stride_token, int64_t x_stride_slot,
+                                  float* h, void* stream) {
+    switch (fmt) {
+    case QMV_Q8_0:
+        return qmv::moe<qmv::Q8_0, true>(W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, batch,
+                                         top_k, x, x_stride_token, x_stride_slot, h, stream);
+    case QMV_Q4_0:
+        return qmv::moe<qmv::Q4_0, true>(W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, batch,
+                                         top_k, x, x_stride_token, x_stride_slot, h, stream);
+    case QMV_Q4_1:
+        return qmv::moe<qmv::Q4_1, true>(W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, batch,
+                                         top_k, x, x_stride_token, x_stride_slot, h, stream);
+    default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_moe_swiglu: unknown format %d", (int)fmt);
+    }
+}
+
+extern "C" int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes, int32_t n_experts,
+                                   int64_t n_rows, int64_t n_cols, const int32_t* expert_ids, const float* weights,
+                                   int32_t batch, int32_t top_k, const float* x, int64_t x_stride_token,
+                                   int64_t x_stride_slot, float* out, void* stream) {
+    switch (fmt) {
+    case QMV_Q8_0:
+        return qmv::moe_combine<qmv::Q8_0>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids,
+                                           weights, batch, top_k, x, x_stride_token, x_stride_slot, out, stream);
+    case QMV_Q4_0:
+        return qmv::moe_combine<qmv::Q4_0>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids,
+                                           weights, batch, top_k, x, x_stride_token, x_stride_slot, out, stream);
+    case QMV_Q4_1:
+        return qmv::moe_combine<qmv::Q4_1>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids,
+                                           weights, batch, top_k, x, x_stride_token, x_stride_slot, out, stream);
+    default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_moe_combine: unknown format %d", (int)fmt);
     }
 }

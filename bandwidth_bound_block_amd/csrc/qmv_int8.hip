@@ -11,6 +11,10 @@
 // +infinity (saturating the single overflow case -2^31 * -2^31), and
 // RDBPOT(v, e) = v / 2^e rounded to nearest with ties away from zero.
 //
+// The same page's integer engine runs its activation functions (SiLU among
+// them) as frozen lookup tables; qmv_i8_requant_lut applies such a table to
+// the requantized output in the epilogue: y = lut[y + 128].
+//
 // Mapping: rows are split into segments of LPR lanes; each lane reads
 // 16 consecutive weight bytes per step (one 16-byte load; a segment reads
 // 16*LPR contiguous bytes), multiplies them with the matching 16 activation
@@ -86,7 +90,8 @@ template <int B, int LPR, int RPL>
 __global__ __launch_bounds__(kThreads) void i8_kernel(const int8_t* __restrict__ W, int64_t N, int nc,
                                                       const int8_t* __restrict__ x, int64_t ldx,
                                                       const int32_t* __restrict__ mult,
-                                                      const int32_t* __restrict__ shift, int8_t* __restrict__ y,
+                                                      const int32_t* __restrict__ shift,
+                                                      const int8_t* __restrict__ lut, int8_t* __restrict__ y,
                                                       int64_t ldy) {
     constexpr int G = 64 / LPR;
     constexpr int ROWS = G * RPL;
@@ -139,7 +144,10 @@ __global__ __launch_bounds__(kThreads) void i8_kernel(const int8_t* __restrict__
                 if (row < N) {
                     const int32_t mu = mult[row], sh = shift[row];
 #pragma unroll
-                    for (int b = 0; b < B; ++b) y[b * ldy + row] = sat8(rdbpot(srdhm(acc[r][b], mu), sh));
+                    for (int b = 0; b < B; ++b) {
+                        const int8_t v = sat8(rdbpot(srdhm(acc[r][b], mu), sh));
+                        y[b * ldy + row] = lut ? lut[v + 128] : v;   // lut: a kernel argument, uniform
+                    }
                 }
             }
         }
@@ -150,31 +158,26 @@ constexpr int kRpl = 2;
 
 template <int B, int LPR>
 int32_t launch_b(const int8_t* W, int64_t N, int nc, const int8_t* x, int64_t ldx, const int32_t* mult,
-                 const int32_t* shift, int8_t* y, int64_t ldy, hipStream_t st) {
+                 const int32_t* shift, const int8_t* lut, int8_t* y, int64_t ldy, hipStream_t st) {
     constexpr int rows_per_wg = kWaves * (64 / LPR) * kRpl;
     const int64_t tiles = (N + rows_per_wg - 1) / rows_per_wg;
     const int grid = (int)std::min<int64_t>(tiles, (int64_t)device_cu_count() * 8);
     hipLaunchKernelGGL((i8_kernel<B, LPR, kRpl>), dim3(grid), dim3(kThreads), 0, st, W, N, nc, x, ldx, mult, shift,
-                       y, ldy);
+                       lut, y, ldy);
     return check_launch("qmv_i8_requant");
 }
 
 template <int B>
 int32_t launch_lpr(const int8_t* W, int64_t N, int nc, const int8_t* x, int64_t ldx, const int32_t* mult,
-                   const int32_t* shift, int8_t* y, int64_t ldy, hipStream_t st) {
-    if (nc >= 64) return launch_b<B, 64>(W, N, nc, x, ldx, mult, shift, y, ldy, st);
-    if (nc >= 32) return launch_b<B, 32>(W, N, nc, x, ldx, mult, shift, y, ldy, st);
-    return launch_b<B, 8>(W, N, nc, x, ldx, mult, shift, y, ldy, st);
+                   const int32_t* shift, const int8_t* lut, int8_t* y, int64_t ldy, hipStream_t st) {
+    if (nc >= 64) return launch_b<B, 64>(W, N, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    if (nc >= 32) return launch_b<B, 32>(W, N, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    return launch_b<B, 8>(W, N, nc, x, ldx, mult, shift, lut, y, ldy, st);
 }
 
-}  // namespace
-}  // namespace qmv
-
-extern "C" int32_t qmv_i8_requant(const int8_t* W, int64_t n_rows, int64_t n_cols, const int8_t* x, int64_t ldx,
-                                  int32_t batch, const int32_t* mult, const int32_t* shift, int8_t* y, int64_t ldy,
-                                  void* stream) {
-    using namespace qmv;
-    const char* name = "qmv_i8_requant";
+int32_t i8_requant(const char* name, const int8_t* W, int64_t n_rows, int64_t n_cols, const int8_t* x, int64_t ldx,
+                   int32_t batch, const int32_t* mult, const int32_t* shift, const int8_t* lut, int8_t* y,
+                   int64_t ldy, void* stream) {
     if (!W || !x || !mult || !shift || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (n_rows < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)n_rows);
     if (n_cols < 16 || n_cols % 16 || n_cols > 131056)
@@ -190,13 +193,29 @@ extern "C" int32_t qmv_i8_requant(const int8_t* W, int64_t n_rows, int64_t n_col
     const int nc = (int)(n_cols / 16);
     hipStream_t st = as_stream(stream);
     switch (batch) {
-    case 1: return launch_lpr<1>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
-    case 2: return launch_lpr<2>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
-    case 3: return launch_lpr<3>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
-    case 4: return launch_lpr<4>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
-    case 5: return launch_lpr<5>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
-    case 6: return launch_lpr<6>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
-    case 7: return launch_lpr<7>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
-    default: return launch_lpr<8>(W, n_rows, nc, x, ldx, mult, shift, y, ldy, st);
+    case 1: return launch_lpr<1>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    case 2: return launch_lpr<2>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    case 3: return launch_lpr<3>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    case 4: return launch_lpr<4>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    case 5: return launch_lpr<5>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    case 6: return launch_lpr<6>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    case 7: return launch_lpr<7>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
+    default: return launch_lpr<8>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
     }
+}
+
+}  // namespace
+}  // namespace qmv
+
+extern "C" int32_t qmv_i8_requant(const int8_t* W, int64_t n_rows, int64_t n_cols, const int8_t* x, int64_t ldx,
+                                  int32_t batch, const int32_t* mult, const int32_t* shift, int8_t* y, int64_t ldy,
+                                  void* stream) {
+    return qmv::i8_requant("qmv_i8_requant", W, n_rows, n_cols, x, ldx, batch, mult, shift, nullptr, y, ldy, stream);
+}
+
+extern "C" int32_t qmv_i8_requant_lut(const int8_t* W, int64_t n_rows, int64_t n_cols, const int8_t* x, int64_t ldx,
+                                      int32_t batch, const int32_t* mult, const int32_t* shift, const int8_t* lut,
+                                      int8_t* y, int64_t ldy, void* stream) {
+    if (!lut) return qmv::fail(QMV_EINVAL, "qmv_i8_requant_lut: null table");
+    return qmv::i8_requant("qmv_i8_requant_lut", W, n_rows, n_cols, x, ldx, batch, mult, shift, lut, y, ldy, stream);
 }

@@ -169,6 +169,21 @@ int32_t qmv_i8_requant(const int8_t* W, int64_t n_rows, int64_t n_cols,
                        int8_t* y, int64_t ldy, void* stream);
 
 /*
+ * qmv_i8_requant with the requantized outputs mapped through a frozen
+ * lookup table, the form in which [ZEN]'s integer engine applies its
+ * activation functions (SiLU among them, "Quantization recipe"):
+ *   y[b][i] = lut[sat_int8(RDBPOT(SRDHM(acc[b][i], mult[i]), shift[i])) + 128]
+ *   lut  int8 [256], device memory, read-only; entry v + 128 is the output
+ *        for requantized value v.  Its contents are the caller's (a SiLU
+ *        table folds the input and output scales into its entries).
+ * Other arguments and errors as qmv_i8_requant; QMV_EINVAL for a null lut.
+ */
+int32_t qmv_i8_requant_lut(const int8_t* W, int64_t n_rows, int64_t n_cols,
+                           const int8_t* x, int64_t ldx, int32_t batch,
+                           const int32_t* mult, const int32_t* shift, const int8_t* lut,
+                           int8_t* y, int64_t ldy, void* stream);
+
+/*
  * Grouped mixture-of-experts expert matvec ([NST] Sec. "The Unified Quant
  * Core": each routed expert goes through the same decode matvec core).
  * For token b < batch and slot s < top_k, with e = expert_ids[b*top_k + s]:
@@ -198,6 +213,52 @@ int32_t qmv_moe(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                 const int32_t* expert_ids, int32_t batch, int32_t top_k,
                 const float* x, int64_t x_stride_token, int64_t x_stride_slot,
                 float* y, void* stream);
+
+/*
+ * MoE gate/up projection with the SwiGLU step fused ([ZEN] "Architecture":
+ * the MLP is SwiGLU(gate, up, down); [NST] Sec. "The Unified Quant Core":
+ * each routed expert goes through the same matvec core).  Every expert
+ * matrix holds 2*n_ff rows of n_cols: its gate rows 0..n_ff-1, then its up
+ * rows n_ff..2*n_ff-1 (the two row-concatenated by the caller).  For token
+ * b, slot s, expert e = expert_ids[b*top_k + s] and i < n_ff:
+ *   g = sum_j DEQ(W_e)[i][j] * x_{b,s}[j],  u = sum_j DEQ(W_e)[n_ff + i][j] * x_{b,s}[j],
+ *   h[(b*top_k + s)*n_ff + i] = SiLU(g) * u,   SiLU(g) = g / (1 + e^-g),
+ * with g and u the sums qmv_moe produces for those rows (bitwise), and
+ * SiLU and the product in fp32.  Every routed expert is streamed once per
+ * call.  Arguments as qmv_moe, with expert_stride_bytes >= the bytes of
+ * 2*n_ff rows; h is fp32 [batch][top_k][n_ff], 4-byte aligned.  Invalid
+ * ids give quiet NaN rows, as in qmv_moe.
+ * Errors: as qmv_moe.
+ */
+int32_t qmv_moe_swiglu(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
+                       int32_t n_experts, int64_t n_ff, int64_t n_cols,
+                       const int32_t* expert_ids, int32_t batch, int32_t top_k,
+                       const float* x, int64_t x_stride_token, int64_t x_stride_slot,
+                       float* h, void* stream);
+
+/*
+ * MoE down projection with the router-weighted combine of each token's
+ * top_k expert outputs fused (the last step of the MoE block):
+ *   out[b*n_rows + i] = sum_{s < top_k} weights[b*top_k + s] * y_{b,s}[i],
+ *   y_{b,s}[i] = sum_j DEQ(W_{expert_ids[b*top_k + s]})[i][j] * x_{b,s}[j],
+ * with every y_{b,s}[i] the sum qmv_moe produces (bitwise) and the combine
+ * an fp32 fused multiply-add chain in slot order s = 0, 1, ...  The router
+ * (top-k choice and weight normalization) is the caller's.  Each (token,
+ * slot) streams its expert: an expert routed from several tokens is read
+ * once per token (no cross-token reduction, so no atomics and no
+ * workspace).
+ *   weights  fp32 [batch][top_k], device memory, 4-byte aligned.
+ *   out      fp32 [batch][n_rows], 4-byte aligned; fully overwritten.
+ * Other arguments as qmv_moe.  A token with an invalid id gets quiet NaN
+ * for all its n_rows outputs.
+ * Errors: as qmv_moe; QMV_EINVAL for null weights, QMV_EALIGN for
+ * misaligned weights.
+ */
+int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
+                        int32_t n_experts, int64_t n_rows, int64_t n_cols,
+                        const int32_t* expert_ids, const float* weights, int32_t batch, int32_t top_k,
+                        const float* x, int64_t x_stride_token, int64_t x_stride_slot,
+                        float* out, void* stream);
 
 /*
  * A chain of batch-1 float matvecs in one persistent launch.  Decode is a

@@ -28,8 +28,8 @@ def qmv():
 
 def test_every_declared_symbol_is_exported(qmv):
     names = declared_functions()
-    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "qmv_i8_requant", "qmv_moe",
-            "qmv_dequant",
+    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "qmv_i8_requant",
+            "qmv_i8_requant_lut", "qmv_moe", "qmv_moe_swiglu", "qmv_moe_combine", "qmv_dequant",
             "qmv_chain", "qmv_last_error", "qmv_abi_version"} <= set(names)
     raw = ctypes.CDLL(qmv.library_path())
     for n in names:
@@ -119,6 +119,29 @@ def test_int8_argument_errors(qmv):
     assert call(x=A + 8) == EALIGN
     assert call(ldx=72) == EALIGN
     assert call(shift=A + 2) == EALIGN
+
+
+def test_int8_lut_argument_errors(qmv):
+    f = qmv.lib().qmv_i8_requant_lut
+    assert f(A, 8, 64, A, 64, 1, A, A, 0, A, 8, None) == EINVAL and "table" in qmv.last_error()
+    assert f(A, 8, 40, A, 64, 1, A, A, A, A, 8, None) == EINVAL and "multiple of 16" in qmv.last_error()
+    assert f(A, 8, 64, A + 8, 64, 1, A, A, A, A, 8, None) == EALIGN
+
+
+def test_moe_swiglu_and_combine_argument_errors(qmv):
+    sw = qmv.lib().qmv_moe_swiglu
+    per = 2 * 16 * 2 * 18   # 2 x 16 rows of a 64-column Q4_0 expert
+    assert sw(7, A, per, 4, 16, 64, A, 2, 2, A, 64, 0, A, None) == EUNSUPPORTED
+    assert sw(1, A, per - 4, 4, 16, 64, A, 2, 2, A, 64, 0, A, None) == EINVAL and "expert_stride" in qmv.last_error()
+    assert sw(1, A, per, 4, 16, 64, A, 9, 2, A, 64, 0, A, None) == EINVAL
+    assert sw(1, A, per, 4, 16, 64, A, 2, 2, A, 64, 0, A + 2, None) == EALIGN
+    cb = qmv.lib().qmv_moe_combine
+    per = 16 * 2 * 18
+    assert cb(7, A, per, 4, 16, 64, A, A, 2, 2, A, 128, 64, A, None) == EUNSUPPORTED
+    assert cb(1, A, per, 4, 16, 64, A, 0, 2, 2, A, 128, 64, A, None) == EINVAL and "null" in qmv.last_error()
+    assert cb(1, A, per, 4, 16, 64, A, A + 2, 2, 2, A, 128, 64, A, None) == EALIGN
+    assert cb(1, A, per, 4, 16, 64, A, A, 2, 17, A, 128, 64, A, None) == EINVAL and "top_k" in qmv.last_error()
+    assert cb(1, A, per, 4, 16, 64, A, A, 2, 2, A, 128, 32, A, None) == EINVAL
 
 
 def test_moe_argument_errors(qmv):

@@ -749,3 +749,213 @@ def test_chain_shared_input_groups(env, fmt):
             ref = f(W, N, K, x)[0]
             torch.cuda.synchronize()
             assert torch.equal(st[4].view(torch.int32), ref.view(torch.int32)), (gname, N)
+
+
+# ------------------------------------------------------------------ fused steps
+def silu_table(s_in, s_out):
+    """An int8 SiLU table of the frozen-table kind, written out here from the
+    closed form (example data for the table step, which itself only looks
+    entries up): entry v + 128 = clamp(round(SiLU(v s_in) / s_out))."""
+    v = np.arange(-128, 128, dtype=np.float64) * s_in
+    r = v / (1.0 + np.exp(-v)) / s_out
+    return np.clip(np.sign(r) * np.floor(np.abs(r) + 0.5), -128, 127).astype(np.int8)
+
+
+def test_int8_lut_bit_exact(env):
+    """The requant output through a frozen table: a SiLU table, a random
+    table and the identity (which must equal qmv_i8_requant); Qwen3-0.6B
+    gate shape, batch 1..8, a ragged shape; bit-exact."""
+    torch, qmv = env
+    tables = {"silu": silu_table(1 / 16, 1 / 16), "random": wl.int8_table("lut/random"),
+              "identity": (np.arange(256) - 128).astype(np.int8)}
+    assert tables["silu"][128 + 16] == 12 and tables["silu"][128 - 16] == -4 and tables["silu"][128] == 0
+    for (N, K), B in [((3072, 1024), 1), ((3072, 1024), 8), ((77, 1040), 3)]:
+        W = wl.int8_uniform(f"lut/W/{N}", (N, K))
+        x = wl.int8_uniform(f"lut/x/{N}/{B}", (B, K))
+        g = np.random.default_rng(N)
+        mult = g.integers(1 << 30, 1 << 31, size=N).astype(np.int32)
+        sigma = 127 * 127 / 3 * np.sqrt(K)
+        shift = np.clip(np.ceil(np.log2(3 * sigma * mult / 2 ** 31 / 127)), 0, 31).astype(np.int32)
+        Wd, xd, md, sd = dev(torch, W), dev(torch, x), dev(torch, mult), dev(torch, shift)
+        plain = qmv.qmv_i8_requant(Wd, xd, md, sd)
+        for name, lut in tables.items():
+            say(f"int8 lut {name} {N}x{K} B={B}")
+            y = qmv.qmv_i8_requant_lut(Wd, xd, md, sd, dev(torch, lut))
+            torch.cuda.synchronize()
+            _, yr = oracle.matvec_i8_lut(W, x, mult, shift, lut)
+            assert np.array_equal(y.cpu().numpy(), yr), (name, N, B)
+            if name == "identity":
+                assert torch.equal(y, plain)
+
+
+def swiglu_bound(h, g, u, Sg, Su):
+    """|h_gpu - h| for h = SiLU(g) u from fp32 g, u within the matvec bound
+    (tg, tu): |SiLU'| <= 1.1, so |dh| <= 1.1 tg (|u| + tu) + (|SiLU(g)| +
+    1.1 tg) tu, plus the fp32 epilogue (a few ulps of h)."""
+    tg, tu = 1e-4 * Sg + 1e-6, 1e-4 * Su + 1e-6
+    sg = np.abs(g / (1.0 + np.exp(-g)))
+    return 1.1 * tg * (np.abs(u) + tu) + (sg + 1.1 * tg) * tu + 2.0 ** -20 * np.abs(h) + 1e-30
+
+
+def gpu_swiglu(env, fmt, Wall, stride, E, F, K, ids, x):
+    torch, qmv = env
+    h = qmv.qmv_moe_swiglu(fmt, dev(torch, Wall), stride, E, F, K, dev(torch, ids), dev(torch, x))
+    torch.cuda.synchronize()
+    return h.cpu().numpy()
+
+
+@pytest.mark.parametrize("B", [1, 2, 8])
+def test_moe_swiglu_30b_a3b(env, B):
+    """128 Q4_0 experts of gate||up 1536 x 2048, top-8 per token: h against
+    the fp64 oracle within the propagated bound, and the gate and up sums
+    bitwise those of qmv_moe on the same experts."""
+    torch, qmv = env
+    E, T, H, F = wl.MOE_EXPERTS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
+    gate = wl.quant_weights("q4_0", "moe/gate", E * F, H).reshape(E, -1)
+    up = wl.quant_weights("q4_0", "moe/up", E * F, H).reshape(E, -1)
+    Wall = np.concatenate([gate, up], axis=1).reshape(-1)
+    stride = 2 * wl.block_bytes("q4_0", F, H)
+    ids = wl.moe_ids(f"moe/swiglu/ids/{B}", B, T, E)
+    x = wl.activations(f"moe/swiglu/x/{B}", B, H)
+    say(f"moe swiglu B={B}")
+    h = gpu_swiglu(env, "q4_0", Wall, stride, E, F, H, ids, x)
+    rows = np.sort(np.random.default_rng(B).choice(F, size=96, replace=False))
+    hr, g, u, Sg, Su = oracle.moe_swiglu("q4_0", Wall, stride, E, F, H, ids, x, rows=rows)
+    err = np.abs(h[:, :, rows].astype(np.float64) - hr)
+    assert np.all(err <= swiglu_bound(hr, g, u, Sg, Su)), float((err / swiglu_bound(hr, g, u, Sg, Su)).max())
+    # the gate and up sums are qmv_moe's: h == SiLU(g32) * u32 up to the epilogue's rounding
+    y = gpu_moe(env, "q4_0", Wall, stride, E, 2 * F, H, ids, x).astype(np.float64)
+    g32, u32 = y[:, :, :F], y[:, :, F:]
+    href = g32 / (1.0 + np.exp(-g32)) * u32
+    assert np.all(np.abs(h - href) <= 2.0 ** -21 * np.abs(href) + 1e-37)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", ["dup_invalid", "strided", "long_rows"])
+def test_moe_swiglu_edges(env, fmt, case):
+    """Duplicated and invalid ids (NaN rows), per-slot inputs with an odd
+    stride, rows of 16416 columns (looping stager); all rows against the
+    oracle."""
+    torch, qmv = env
+    E = 5
+    if case == "dup_invalid":
+        F, K, ids, pad = 40, 1024, np.array([[3, 3, 9], [0, -1, 3]], dtype=np.int32), 0
+    elif case == "strided":
+        F, K, ids, pad = 72, 768, np.array([[2, 0, 4, 1], [4, 4, 1, 0]], dtype=np.int32), 1
+    else:
+        F, K, ids, pad = 24, 16416, np.array([[1, 4]], dtype=np.int32), 0
+    B, T = ids.shape
+    per = wl.block_bytes(fmt, 2 * F, K)
+    Wall = wl.quant_weights(fmt, f"moe/swiglu/{case}", E * 2 * F, K).reshape(-1)
+    say(f"moe swiglu edge {fmt} {case}")
+    if case == "strided":
+        ld = K + pad
+        xs = wl.activations(f"moe/swiglu/x/{case}", B * T, K).reshape(B, T, K)
+        buf = np.zeros((B * T, ld), dtype=np.float32)
+        buf[:, :K] = xs.reshape(B * T, K)
+        hd = torch.empty((B, T, F), dtype=torch.float32, device="cuda:0")
+        Wd, idsd, xd = dev(torch, Wall), dev(torch, ids), dev(torch, buf.reshape(-1))   # alive across the call
+        rc = qmv.lib().qmv_moe_swiglu(qmv.FORMATS[fmt], Wd.data_ptr(), per, E, F, K, idsd.data_ptr(), B, T,
+                                      xd.data_ptr(), T * ld, ld, hd.data_ptr(), None)
+        assert rc == 0, qmv.last_error()
+        torch.cuda.synchronize()
+        h = hd.cpu().numpy()
+        hr, g, u, Sg, Su = oracle.moe_swiglu(fmt, Wall, per, E, F, K, ids, None, x_slots=xs)
+    else:
+        x = wl.activations(f"moe/swiglu/x/{case}", B, K)
+        h = gpu_swiglu(env, fmt, Wall, per, E, F, K, ids, x)
+        valid = (ids >= 0) & (ids < E)
+        assert np.all(np.isnan(h[~valid]))
+        ids_ok = np.where(valid, ids, 0).astype(np.int32)
+        hr, g, u, Sg, Su = oracle.moe_swiglu(fmt, Wall, per, E, F, K, ids_ok, x)
+        h, hr, g, u, Sg, Su = (a[valid] for a in (h, hr, g, u, Sg, Su))
+    err = np.abs(h.astype(np.float64) - hr)
+    assert np.all(err <= swiglu_bound(hr, g, u, Sg, Su)), (case, float((err / swiglu_bound(hr, g, u, Sg, Su)).max()))
+
+
+def combine_bound(S, w):
+    """The combine's bound: the weighted matvec bounds plus the fp32
+    multiply-add chain over at most 16 slots."""
+    return (1e-4 + 16 * 2.0 ** -24) * S + 1e-6 * np.abs(w).sum(axis=1, keepdims=True) + 1e-30
+
+
+def gpu_combine(env, fmt, Wall, stride, E, N, K, ids, w, x):
+    torch, qmv = env
+    out = qmv.qmv_moe_combine(fmt, dev(torch, Wall), stride, E, N, K, dev(torch, ids), dev(torch, w), dev(torch, x))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B", [1, 2, 8])
+def test_moe_combine_30b_a3b(env, B):
+    """128 Q4_0 down experts 2048 x 768, one input per (token, slot), router
+    weights summing to 1: against the fp64 oracle, and against the
+    weighted sum of qmv_moe's per-slot outputs (the same per-slot sums)."""
+    torch, qmv = env
+    E, T, H, F = wl.MOE_EXPERTS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
+    Wall = _moe_experts("down", H, F)
+    stride = wl.block_bytes("q4_0", H, F)
+    ids = wl.moe_ids(f"moe/combine/ids/{B}", B, T, E)
+    w = wl.router_weights(f"moe/combine/w/{B}", B, T)
+    x = wl.activations(f"moe/combine/x/{B}", B * T, F).reshape(B, T, F)
+    say(f"moe combine B={B}")
+    out = gpu_combine(env, "q4_0", Wall, stride, E, H, F, ids, w, x)
+    ref, S = oracle.moe_combine("q4_0", Wall, stride, E, H, F, ids, w, x_slots=x)
+    err = np.abs(out.astype(np.float64) - ref)
+    assert np.all(err <= combine_bound(S, w)), float((err / combine_bound(S, w)).max())
+    y = gpu_moe(env, "q4_0", Wall, stride, E, H, F, ids, x).astype(np.float64)
+    mix = np.einsum("bs,bsn->bn", w.astype(np.float64), y)
+    assert np.all(np.abs(out - mix) <= T * 2.0 ** -24 * np.einsum("bs,bsn->bn", np.abs(w), np.abs(y)) + 1e-37)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("case", ["one_hot_dup", "invalid", "chunked_slots", "token_inputs"])
+def test_moe_combine_edges(env, fmt, case):
+    """One-hot weights (out equals one slot's qmv_moe output bitwise),
+    duplicated ids, an invalid id (the token's row becomes NaN), top_k 16 on
+    rows of 16384 columns (slot vectors staged in several chunks, rows in
+    several ranges), one input per token."""
+    torch, qmv = env
+    E = 6
+    if case == "one_hot_dup":
+        N, K, ids = 300, 1024, np.array([[2, 5, 2], [0, 0, 1]], dtype=np.int32)
+    elif case == "invalid":
+        N, K, ids = 96, 512, np.array([[1, 3], [7, 2], [4, 4]], dtype=np.int32)
+    elif case == "chunked_slots":
+        N, K, ids = 4200, 16384, np.array([[i % E for i in range(16)]], dtype=np.int32)
+    else:
+        N, K, ids = 128, 2048, np.array([[5, 1, 0, 3], [2, 2, 4, 1]], dtype=np.int32)
+    B, T = ids.shape
+    per = wl.block_bytes(fmt, N, K)
+    Wall = wl.quant_weights(fmt, f"moe/combine/{case}", E * N, K).reshape(-1)
+    w = wl.router_weights(f"moe/combine/w/{case}", B, T)
+    say(f"moe combine edge {fmt} {case}")
+    if case == "token_inputs":
+        x = wl.activations(f"moe/combine/x/{case}", B, K)
+        out = gpu_combine(env, fmt, Wall, per, E, N, K, ids, w, x)
+        ref, S = oracle.moe_combine(fmt, Wall, per, E, N, K, ids, w, x_tokens=x)
+    else:
+        x = wl.activations(f"moe/combine/x/{case}", B * T, K).reshape(B, T, K)
+        if case == "one_hot_dup":
+            w = np.zeros((B, T), dtype=np.float32)
+            w[0, 2] = 1.0
+            w[1, 1] = 1.0
+        out = gpu_combine(env, fmt, Wall, per, E, N, K, ids, w, x)
+        if case == "invalid":
+            valid = np.all((ids >= 0) & (ids < E), axis=1)
+            assert np.all(np.isnan(out[~valid])) and not np.any(np.isnan(out[valid]))
+            ids_ok = np.where((ids >= 0) & (ids < E), ids, 0).astype(np.int32)
+            ref, S = oracle.moe_combine(fmt, Wall, per, E, N, K, ids_ok, w, x_slots=x)
+            out, ref, S, w = out[valid], ref[valid], S[valid], w[valid]
+        elif case == "chunked_slots":
+            rows = np.sort(np.random.default_rng(3).choice(N, size=64, replace=False))
+            rows[-1] = N - 1
+            ref, S = oracle.moe_combine(fmt, Wall, per, E, N, K, ids, w, x_slots=x, rows=rows)
+            out = out[:, rows]
+        else:
+            ref, S = oracle.moe_combine(fmt, Wall, per, E, N, K, ids, w, x_slots=x)
+            y = gpu_moe(env, fmt, Wall, per, E, N, K, ids, x)
+            assert np.array_equal(out[0].view(np.uint32), y[0, 2].view(np.uint32))
+            assert np.array_equal(out[1].view(np.uint32), y[1, 1].view(np.uint32))
+    err = np.abs(out.astype(np.float64) - ref)
+    assert np.all(err <= combine_bound(S, w)), (case, float((err / combine_bound(S, w)).max()))

@@ -17,7 +17,10 @@ and encodes them into the stored block formats, as the input recipe says:
 * activations x ~ N(0, 1) float32;
 * int8 weights / activations uniform in [-127, 127]; per-row requant
   multipliers uniform in [2^30, 2^31 - 1] and shifts uniform in [0, 20];
-* MoE expert ids: per token, top_k distinct ids uniform without replacement.
+* MoE expert ids: per token, top_k distinct ids uniform without replacement;
+  router weights per token drawn from a flat Dirichlet (positive, summing
+  to 1 over the token's top_k slots);
+* an int8 lookup table: 256 entries uniform in [-128, 127].
 
 Byte layouts (ggml-compatible, little-endian): Q8_0 = [d:fp16][q:int8 x32];
 Q4_0 = [d:fp16][qs:16 bytes], element j<16 in the low nibble of qs[j] and
@@ -66,6 +69,14 @@ def moe_ids(tag, batch, top_k, n_experts):
     g = rng(tag)
     return np.stack([g.choice(n_experts, size=top_k, replace=False)
                      for _ in range(batch)]).astype(np.int32)
+
+
+def router_weights(tag, batch, top_k):
+    return rng(tag).dirichlet(np.ones(top_k), size=batch).astype(np.float32)
+
+
+def int8_table(tag):
+    return rng(tag).integers(-128, 128, size=256, dtype=np.int8)
 
 
 # ---------------------------------------------------------------- encoders
