@@ -541,15 +541,15 @@ __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict_
 
 // MoE down projection with the router-weighted combine, token-major:
 // workgroup (bx, b) computes rows of out[b] = sum_s w[b][s] * DEQ(W_{e_s}) x_{b,s}
-// over the top_k slots of token b, in slot order.  The slots' activation
-// vectors are staged together (in chunks of SC slots when they do not all
-// fit the LDS); each wave then streams its row tiles slot after slot with one
-// pipeline running across the slots, and the first lane of each row keeps
-// the row's running sum in LDS (the same lane owns the row in every slot).
-// Each slot's row sum is the dense kernel's (bitwise the qmv_moe output),
-// and the combine is fma(w_s, y_s, acc) from s = 0 up.  Every (token, slot)
-// streams its expert: experts shared by several tokens are read once per
-// token, which is what keeps the combine free of atomics and workspace.
+// over the top_k slots of token b.  The slots' activation vectors are
+// staged together (in chunks of SC slots when they do not all fit the LDS).
+// The work is the units (slot, row tile); wave w takes units w, w + NW,
+// ... with one pipeline running across them, and each unit's row sums (the
+// dense kernel's, bitwise the qmv_moe outputs) go to LDS.  Then one thread
+// per row adds them in slot order: fma(w_s, y_s, acc) from s = 0 up.  Every
+// (token, slot) streams its expert: experts shared by several tokens are
+// read once per token, which is what keeps the combine free of atomics and
+// workspace.
 template <class F, int LPR, int NW, int PD>
 __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
                                                                int n_experts, int64_t N, int nb,
@@ -570,14 +570,15 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
     const int T = (nb + LPR - 1) / LPR;
     const int b = blockIdx.y;
     const int64_t ntiles = (N + G - 1) / G;
-    const int64_t per_wg = rows_wg / G;
+    const int per_wg = rows_wg / G;
     const int64_t tb = (int64_t)blockIdx.x * per_wg;
     const int64_t te = min(ntiles, tb + per_wg);
     if (tb >= te) return;
+    const int wtiles = (int)(te - tb);
     const int per_col = nb * (kXPad + (F::kNeedSx ? 1 : 0));
     float* xs = lds;                          // [SC][nb][kXPad]
     float* sx = lds + SC * nb * kXPad;        // [SC][nb]
-    float* oacc = lds + SC * per_col;         // running sums of rows tb*G ...
+    float* ybuf = lds + SC * per_col;         // [top_k][rows_wg]: row sums per slot
     const int64_t r0 = tb * G;
     if (tid == 0) s_bad = 0;
     __syncthreads();
@@ -589,11 +590,10 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
         s_w[tid] = wts[b * top_k + tid];
     }
     using Raw = typename F::Raw;
-    const int64_t wtiles = te - tb;
     for (int s0 = 0; s0 < top_k; s0 += SC) {
         const int sc = min(SC, top_k - s0);
-        // the chunk's activation vectors (previous chunk's reads are done:
-        // the loop below ends every wave's use of xs before this barrier)
+        // the chunk's activation vectors (every wave is done with the
+        // previous chunk's: its units all ended before this barrier)
         __syncthreads();
         {
             // chunk i of the sc concatenated vectors, four loads in flight per thread
@@ -636,40 +636,45 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
             block_sums<64 * NW>(xs, sx, sc * nb);
             __syncthreads();
         }
-        // this wave's steps: slots of the chunk (outer), its row tiles
-        // tb + wave, + NW, ... (middle), the row's T steps (inner)
-        const int64_t my_tiles = wave < wtiles ? (wtiles - wave + NW - 1) / NW : 0;
-        const int64_t nsteps = my_tiles * T * sc;
+        // this wave's units q = wave, wave + NW, ... of the chunk's
+        // sc * wtiles (slot-major), T steps each
+        const int units = sc * wtiles;
+        const int my_units = wave < units ? (units - wave + NW - 1) / NW : 0;
+        const int64_t nsteps = (int64_t)my_units * T;
         if (nsteps == 0) continue;
         struct Cur {
-            int s, t;
-            int64_t tile;
+            int q, t;
         };
-        Cur lc{0, 0, tb + wave}, cc = lc;
+        Cur lc{wave, 0}, cc = lc;
         auto advance = [&](Cur& k) {
-            if (++k.t < T) return;
-            k.t = 0;
-            k.tile += NW;
-            if (k.tile >= te) {
-                k.tile = tb + wave;
-                ++k.s;
+            if (++k.t == T) {
+                k.t = 0;
+                k.q += NW;
             }
         };
         int64_t lrem = nsteps;
-        const uint8_t* lW = s_base[s0];
+        int lslot = lc.q / wtiles;
+        const uint8_t* lW = s_base[s0 + lslot];
         auto load_next = [&](Raw& r) {
-            const int64_t row = min(lc.tile * G + seg, N - 1);
+            const int slot = lc.q / wtiles;
+            const int64_t tile = tb + (lc.q - slot * wtiles);
+            const int64_t row = min(tile * G + seg, N - 1);
             const int j = min(li + LPR * lc.t, nb - 1);
             F::fetch(lW, row * nb + j, r);
             if (lrem > 1) {   // past the last step: re-read it (in cache)
                 --lrem;
-                const int so = lc.s;
                 advance(lc);
-                if (lc.s != so) lW = s_base[s0 + lc.s];
+                const int ns = lc.q / wtiles;
+                if (ns != lslot) {
+                    lslot = ns;
+                    lW = s_base[s0 + ns];
+                }
             }
         };
         float acc = 0.f;
         auto compute = [&](const Raw& r) {
+            const int slot = cc.q / wtiles;
+            const int64_t tile = tb + (cc.q - slot * wtiles);
             const int j = li + LPR * cc.t;
             const bool valid = j < nb;
             const int jc = valid ? j : nb - 1;
@@ -677,18 +682,14 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
             uint32_t c[1][8];
             F::decode(r, d, m, c[0]);
             float sd[1][1];
-            dot_multi<F, 1, 1>(c, xs + cc.s * nb * kXPad + jc * kXPad, 0, sd, 1);
-            const float sxb = F::kNeedSx ? sx[cc.s * nb + jc] : 0.f;
+            dot_multi<F, 1, 1>(c, xs + slot * nb * kXPad + jc * kXPad, 0, sd, 1);
+            const float sxb = F::kNeedSx ? sx[slot * nb + jc] : 0.f;
             const float upd = Term<F>::add(acc, d, m, sd[0][0], sxb);
             acc = valid ? upd : acc;
             if (cc.t == T - 1) {
                 const float tot = segment_sum<LPR>(acc);
-                const int64_t row = cc.tile * G + seg;
-                if (li == 0 && row < N) {
-                    float* p = oacc + (row - r0);
-                    const float ws = s_w[s0 + cc.s];
-                    *p = (s0 + cc.s == 0) ? ws * tot : __builtin_fmaf(ws, tot, *p);
-                }
+                const int64_t row = tile * G + seg;
+                if (li == 0 && row < N) ybuf[(s0 + slot) * rows_wg + (row - r0)] = tot;
                 acc = 0.f;
             }
         };
@@ -716,7 +717,12 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
     __syncthreads();
     const float qnan = __builtin_nanf("");
     const int64_t r1 = min(te * G, N);
-    for (int64_t row = r0 + tid; row < r1; row += 64 * NW) out[(int64_t)b * N + row] = s_bad ? qnan : oacc[row - r0];
+    for (int64_t row = r0 + tid; row < r1; row += 64 * NW) {
+        const float* yr = ybuf + (row - r0);
+        float v = s_w[0] * yr[0];
+        for (int s = 1; s < top_k; ++s) v = __builtin_fmaf(s_w[s], yr[s * rows_wg], v);
+        out[(int64_t)b * N + row] = s_bad ? qnan : v;
+    }
 }
 
 // One thread per block: out[g*32 + e] = value e of block g.
@@ -1059,9 +1065,9 @@ int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t
 }
 
 // The combine kernel's grid: (row ranges, tokens).  Ranges x tokens fill
-// the GPU once; a range holds at most kCombineRows rows (their running sums
-// sit in LDS beside SC staged slot vectors).
-constexpr int kCombineRows = 4096;
+// the GPU once; a range holds at most kCombineRows rows (the row sums of
+// all slots sit in LDS beside SC staged slot vectors).
+constexpr int kCombineRows = 1024;
 
 template <class F, int LPR>
 int32_t launch_combine(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
@@ -1083,18 +1089,20 @@ int32_t launch_combine(const uint8_t* Wx, int64_t estride, int n_experts, int64_
         dyn_max = m;
     }
     const size_t per_col = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
-    const size_t sums_max = (size_t)(kCombineRows + 64) * sizeof(float);   // a range rounds up to whole tiles
+    const size_t sums_max = (size_t)top_k * (kCombineRows + 64) * sizeof(float);   // ranges round up to whole tiles
     if (per_col + sums_max > dyn_max)
         return fail(QMV_EINVAL, "qmv_moe_combine: n_cols %d too large for one activation row in LDS", nb * 32);
     const int SC = (int)std::min<size_t>((size_t)top_k, (dyn_max - sums_max) / per_col);
     const int64_t ntiles = (N + G - 1) / G;
-    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, SC * per_col + sums_max);
+    // residency for ranges of a few tiles (the row sums then take little LDS)
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW,
+                                    SC * per_col + (size_t)top_k * NW * G * sizeof(float));
     const int64_t min_ranges = (ntiles * G + kCombineRows - 1) / kCombineRows;
     const int64_t gx = std::max<int64_t>(
         min_ranges, std::min<int64_t>(ntiles, std::max<int64_t>(1, (int64_t)device_cu_count() * per_cu / batch)));
     const int64_t per_wg = (ntiles + gx - 1) / gx;
     const int rows_wg = (int)(per_wg * G);
-    const size_t lds = SC * per_col + (size_t)rows_wg * sizeof(float);
+    const size_t lds = SC * per_col + (size_t)top_k * rows_wg * sizeof(float);
     hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)batch), dim3(64 * NW), lds, st, Wx, estride, n_experts, N, nb,
                        ids, wts, top_k, x, xs_tok, xs_slot, out, xvec, SC, rows_wg);
     return check_launch("qmv_moe_combine");

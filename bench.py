@@ -279,6 +279,11 @@ def build_int8(torch, qmv, wl, fused=False):
                 mats[g] = tuple(torch.cat([mats[m][i] for m in mem]) for i in range(3))
                 layer_list.append((g, sum(shapes[m][0] for m in mem), K))
                 done.add(g)
+    # the gate projection's output goes through a frozen SiLU table (the
+    # page's integer engine applies SiLU that way); in the row-fused layout
+    # gate and up share one launch, so there the table step is not applied
+    lut = torch.from_numpy(wl.int8_table("qwen/silu_table")).to(dev)
+    sw.keep.append(lut)
     for layer in range(wl.QWEN06B_LAYERS + 1):
         mlist = layer_list if layer < wl.QWEN06B_LAYERS else [wl.QWEN06B_LM_HEAD]
         for mname, N, K in mlist:
@@ -287,8 +292,13 @@ def build_int8(torch, qmv, wl, fused=False):
             x = torch.from_numpy(wl.int8_uniform(f"qwen/x/{layer}/{mname}", (1, K))).to(dev)
             y = torch.empty((1, N), dtype=torch.int8, device=dev)
             sw.keep += [W, x, y, mult, shift]
-            sw.add(mname, cfn, (W.data_ptr(), N, K, x.data_ptr(), K, 1, mult.data_ptr(), shift.data_ptr(),
-                                y.data_ptr(), N), N * K + K + 8 * N + N)
+            if mname == "gate":
+                sw.add(mname, qmv.lib().qmv_i8_requant_lut,
+                       (W.data_ptr(), N, K, x.data_ptr(), K, 1, mult.data_ptr(), shift.data_ptr(), lut.data_ptr(),
+                        y.data_ptr(), N), N * K + K + 8 * N + N)
+            else:
+                sw.add(mname, cfn, (W.data_ptr(), N, K, x.data_ptr(), K, 1, mult.data_ptr(), shift.data_ptr(),
+                                    y.data_ptr(), N), N * K + K + 8 * N + N)
     return sw
 
 
@@ -330,6 +340,49 @@ def build_moe(torch, qmv, wl, batch):
         sw.add("down", cfn, (1, Wdn.data_ptr(), dn_stride, E, H, F, ids.data_ptr(), batch, T,
                              xd.data_ptr(), T * F, F, yd.data_ptr()),
                nu * dn_stride + 4 * batch * T * F + 4 * batch * T * H + 4 * batch * T)
+    sw.mean_unique = float(np.mean(uniq))
+    return sw
+
+
+def build_moe_block(torch, qmv, wl, batch):
+    """48 MoE blocks with the steps around the expert matvecs fused: per
+    layer qmv_moe_swiglu over gate||up (h = SiLU(gate x) * (up x), 768 per
+    slot) and qmv_moe_combine over down (out = sum_s w_s * down_s h_s),
+    the second reading the first's output.  Bytes count each distinct
+    routed expert once (the method's bytes); the combine kernel reads an
+    expert once per token routed to it."""
+    import numpy as np
+    sw = Sweep(f"moe30b_block_q4_0_b{batch}", batch)
+    dev = "cuda:0"
+    E, T, H, F = wl.MOE_EXPERTS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
+    if "moe" not in _ENC_CACHE:
+        gate = wl.quant_weights("q4_0", "moe/gate", E * F, H).reshape(E, -1)
+        up = wl.quant_weights("q4_0", "moe/up", E * F, H).reshape(E, -1)
+        _ENC_CACHE["moe"] = (np.concatenate([gate, up], axis=1).reshape(-1),
+                             wl.quant_weights("q4_0", "moe/down", E * H, F).reshape(-1))
+    gu = torch.from_numpy(_ENC_CACHE["moe"][0]).to(dev)
+    down = torch.from_numpy(_ENC_CACHE["moe"][1]).to(dev)
+    gu_stride = 2 * wl.block_bytes("q4_0", F, H)
+    dn_stride = wl.block_bytes("q4_0", H, F)
+    uniq = []
+    for layer in range(wl.MOE_LAYERS):
+        ids_np = wl.moe_ids(f"moe/ids/{layer}/{batch}", batch, T, E)
+        nu = len(np.unique(ids_np))
+        uniq.append(nu)
+        ids = torch.from_numpy(ids_np).to(dev)
+        w = torch.from_numpy(wl.router_weights(f"moe/w/{layer}/{batch}", batch, T)).to(dev)
+        Wgu, Wdn = gu.clone(), down.clone()
+        x = torch.from_numpy(wl.activations(f"moe/x/gu/{layer}/{batch}", batch, H)).to(dev)
+        h = torch.empty((batch, T, F), dtype=torch.float32, device=dev)
+        out = torch.empty((batch, H), dtype=torch.float32, device=dev)
+        sw.keep += [ids, w, Wgu, Wdn, x, h, out]
+        sw.add("swiglu", qmv.lib().qmv_moe_swiglu,
+               (1, Wgu.data_ptr(), gu_stride, E, F, H, ids.data_ptr(), batch, T, x.data_ptr(), H, 0, h.data_ptr()),
+               nu * gu_stride + 4 * batch * H + 4 * batch * T * F + 4 * batch * T)
+        sw.add("combine", qmv.lib().qmv_moe_combine,
+               (1, Wdn.data_ptr(), dn_stride, E, H, F, ids.data_ptr(), w.data_ptr(), batch, T, h.data_ptr(), T * F, F,
+                out.data_ptr()),
+               nu * dn_stride + 4 * batch * T * F + 4 * batch * H + 8 * batch * T)
     sw.mean_unique = float(np.mean(uniq))
     return sw
 
@@ -553,12 +606,13 @@ def main():
                 torch.cuda.empty_cache()
         elif nm == "moe":
             for B in (1, 2, 4, 8):
-                s = build_moe(torch, qmv, wl, B)
-                r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
-                record(s, r)
-                extra[s.name]["mean_distinct_experts"] = s.mean_unique
-                del s
-                torch.cuda.empty_cache()
+                for build in (build_moe, build_moe_block):
+                    s = build(torch, qmv, wl, B)
+                    r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+                    record(s, r)
+                    extra[s.name]["mean_distinct_experts"] = s.mean_unique
+                    del s
+                    torch.cuda.empty_cache()
 
     cpu = None
     if not args.no_cpu_baseline:
