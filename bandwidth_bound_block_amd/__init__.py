@@ -16,7 +16,9 @@ Entry points (same names as the C ABI):
   qmv_i8_requant                   int8 matvec + per-channel gemmlowp requant
   qmv_i8_requant_lut               the same through a frozen int8 lookup table
   qmv_moe                          grouped MoE expert matvec
+  qmv_moe_xt                       the same with fp32, fp16 or bf16 activations
   qmv_moe_swiglu                   MoE gate||up with the SwiGLU step fused
+  qmv_moe_swiglu_xt                the same with fp32, fp16 or bf16 activations
   qmv_moe_combine                  MoE down with the router-weighted combine
   qmv_dequant                      stored blocks -> fp32 (test/inspection aid)
 """
@@ -25,7 +27,7 @@ import os
 
 __all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
            "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_i8_requant_lut",
-           "qmv_moe", "qmv_moe_swiglu", "qmv_moe_combine",
+           "qmv_moe", "qmv_moe_xt", "qmv_moe_swiglu", "qmv_moe_swiglu_xt", "qmv_moe_combine",
            "qmv_dequant", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
            "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
 
@@ -80,6 +82,10 @@ def _open():
     L.qmv_moe.restype = i32
     L.qmv_moe_swiglu.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P, i64, i64, P, P]
     L.qmv_moe_swiglu.restype = i32
+    for name in ("qmv_moe_xt", "qmv_moe_swiglu_xt"):
+        f = getattr(L, name)
+        f.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, i32, i32, P, i32, i64, i64, P, P]
+        f.restype = i32
     L.qmv_moe_combine.argtypes = [ctypes.c_int, P, i64, i32, i64, i64, P, P, i32, i32, P, i64, i64, P, P]
     L.qmv_moe_combine.restype = i32
     L.qmv_dequant.argtypes = [ctypes.c_int, P, i64, i64, P, P]
@@ -262,12 +268,17 @@ def _i8(W, x, mult, shift, lut, y, stream):
     return y
 
 
-def _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, rows, n_cols, expert_ids, x):
+def _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, rows, n_cols, expert_ids, x, x_types=None):
     torch = _torch()
     fmt = _fmt(fmt)
     _dev(W_experts, "W_experts", torch.uint8)
     _dev(expert_ids, "expert_ids", torch.int32)
-    _dev(x, "x", torch.float32)
+    if x_types is None:
+        _dev(x, "x", torch.float32)
+    else:
+        _dev(x, "x", x.dtype)
+        if x.dtype not in x_types:
+            raise ValueError("x must be float32, float16 or bfloat16")
     if not W_experts.is_contiguous() or not expert_ids.is_contiguous() or not x.is_contiguous():
         raise ValueError("W_experts, expert_ids and x must be contiguous")
     if expert_ids.dim() != 2:
@@ -282,6 +293,45 @@ def _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, rows, n_cols, expe
     if W_experts.numel() < (n_experts - 1) * expert_stride_bytes + rows * (n_cols // 32) * BLOCK_BYTES.get(fmt, 0):
         raise ValueError("W_experts is smaller than n_experts expert matrices")
     return torch, fmt, B, T, st_tok, st_slot
+
+
+def _x_types(torch):
+    return {torch.float32: X_F32, torch.float16: X_F16, torch.bfloat16: X_BF16}
+
+
+def qmv_moe_xt(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, x, y=None, stream=None):
+    """qmv_moe with x float32, float16 or bfloat16 ([B, K] or [B, top_k, K])."""
+    torch = _torch()
+    xt = _x_types(torch)
+    torch, fmt, B, T, st_tok, st_slot = _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols,
+                                                  expert_ids, x, xt)
+    if y is None:
+        y = torch.empty((B, T, n_rows), dtype=torch.float32, device=x.device)
+    _dev(y, "y", torch.float32)
+    if y.shape != (B, T, n_rows) or not y.is_contiguous():
+        raise ValueError("y must be a contiguous [B, top_k, n_rows] tensor")
+    _check(_lib.qmv_moe_xt(fmt, W_experts.data_ptr(), expert_stride_bytes, n_experts, n_rows, n_cols,
+                           expert_ids.data_ptr(), B, T, x.data_ptr(), xt[x.dtype], st_tok, st_slot, y.data_ptr(),
+                           _stream(stream)))
+    return y
+
+
+def qmv_moe_swiglu_xt(fmt, W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, x, h=None,
+                      stream=None):
+    """qmv_moe_swiglu with x float32, float16 or bfloat16."""
+    torch = _torch()
+    xt = _x_types(torch)
+    torch, fmt, B, T, st_tok, st_slot = _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, 2 * n_ff, n_cols,
+                                                  expert_ids, x, xt)
+    if h is None:
+        h = torch.empty((B, T, n_ff), dtype=torch.float32, device=x.device)
+    _dev(h, "h", torch.float32)
+    if h.shape != (B, T, n_ff) or not h.is_contiguous():
+        raise ValueError("h must be a contiguous [B, top_k, n_ff] tensor")
+    _check(_lib.qmv_moe_swiglu_xt(fmt, W_experts.data_ptr(), expert_stride_bytes, n_experts, n_ff, n_cols,
+                                  expert_ids.data_ptr(), B, T, x.data_ptr(), xt[x.dtype], st_tok, st_slot,
+                                  h.data_ptr(), _stream(stream)))
+    return h
 
 
 def qmv_moe_swiglu(fmt, W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, x, h=None,

@@ -332,9 +332,9 @@ constexpr int kMoeStaticLds = 4096;  // s_ids/s_first/s_members/scalars, rounded
 // weight loads, and only then are the activations stored to LDS, so the two
 // latencies overlap (loads complete in order).  XU == 0: staged by the
 // looping stager, then the weights.  Ends with a barrier.
-template <class F, int BC, int LPR, int NW, int XU, int PD, int RS, class Emit>
+template <class F, int BC, int LPR, int NW, int XU, int PD, int RS, class XT, class Emit>
 __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_t N, int nb, int64_t tb, int64_t te,
-                                          const float* const (&xcol)[BC], int w, bool xvec, float* xs, float* sx,
+                                          const XT* const (&xcol)[BC], int w, bool xvec, float* xs, float* sx,
                                           Emit&& emit) {
     constexpr int G = 64 / LPR;
     const int t = threadIdx.x;
@@ -403,7 +403,7 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
     if constexpr (XU > 0) {
         // every column slot is loaded and stored (inactive ones repeat
         // column 0): straight-line code, so no branch merges the waits
-        XStage<XU, 64 * NW> xst[BC];
+        XStage<XU, 64 * NW, XT> xst[BC];
 #pragma unroll
         for (int b = 0; b < BC; ++b) xst[b].load(xcol[b], K4);
 #pragma unroll
@@ -417,7 +417,7 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
             __syncthreads();
         }
     } else {
-        stage_x_cols<F::kNeedSx, BC, 64 * NW>(xcol, nb, xs, sx, w, xvec);
+        stage_x_cols<F::kNeedSx, BC, 64 * NW, XT>(xcol, nb, xs, sx, w, xvec);
 #pragma unroll
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
@@ -456,11 +456,11 @@ __device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
 // dense call bitwise.  SW (SwiGLU): every expert holds 2N rows, gate rows
 // then up rows, and output row i is SiLU(gate_i x) * (up_i x), both sums
 // again the dense kernel's.
-template <class F, int BC, int LPR, int NW, int XU, int PD, bool SW = false>
+template <class F, int BC, int LPR, int NW, int XU, int PD, bool SW = false, class XT = float>
 __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
                                                        int n_experts, int64_t N, int nb,
                                                        const int32_t* __restrict__ ids, int P, int top_k,
-                                                       const float* __restrict__ x, int64_t xs_tok,
+                                                       const XT* __restrict__ x, int64_t xs_tok,
                                                        int64_t xs_slot, float* __restrict__ y, int xvec) {
     static_assert(64 * NW >= kMoeMaxPairs, "one thread per pair");
     __shared__ int s_ids[kMoeMaxPairs];
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict_
     float* sx = lds + BC * nb * kXPad;
     for (int c0 = 0; c0 < nmem; c0 += BC) {
         const int w = min(BC, nmem - c0);
-        const float* xcol[BC];
+        const XT* xcol[BC];
 #pragma unroll
         for (int b = 0; b < BC; ++b) {
             const int pr = s_members[c0 + (b < w ? b : 0)];
@@ -533,9 +533,9 @@ __global__ __launch_bounds__(64 * NW) void moe_kernel(const uint8_t* __restrict_
         };
         constexpr int RS = SW ? 2 : 1;
         if (c0 == 0 && XU > 0 && xvec)
-            moe_chunk<F, BC, LPR, NW, XU, PD, RS>(We, N, nb, tb, te, xcol, w, true, xs, sx, emit);
+            moe_chunk<F, BC, LPR, NW, XU, PD, RS, XT>(We, N, nb, tb, te, xcol, w, true, xs, sx, emit);
         else
-            moe_chunk<F, BC, LPR, NW, 0, PD, RS>(We, N, nb, tb, te, xcol, w, xvec != 0, xs, sx, emit);
+            moe_chunk<F, BC, LPR, NW, 0, PD, RS, XT>(We, N, nb, tb, te, xcol, w, xvec != 0, xs, sx, emit);
     }
 }
 
@@ -964,12 +964,12 @@ int32_t dequant(const void* W, int64_t N, int64_t K, float* out, void* stream) {
 // ranges split each expert's row tiles so that ranges x expected groups
 // fill the GPU once.  Expected groups: all P (spread), or the distinct ids
 // that P uniformly routed pairs reach on average, E (1 - (1 - 1/E)^P).
-template <class F, int BC, int LPR, int XU, int PD, bool SW>
+template <class F, int BC, int LPR, int XU, int PD, bool SW, class XT>
 int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
-                   int P, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
+                   int P, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                    bool spread, hipStream_t st) {
     constexpr int NW = 4;
-    auto kern = moe_kernel<F, BC, LPR, NW, XU, PD, SW>;
+    auto kern = moe_kernel<F, BC, LPR, NW, XU, PD, SW, XT>;
     static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
     if (!dyn_max) {
         hipFuncAttributes fa;
@@ -1006,27 +1006,27 @@ int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N,
 // too little work per workgroup for that, and two columns per pass over a
 // grid sized for every pair measured faster.  Activations staged
 // straight-line (XU 16-byte loads per thread) up to K = 8192.
-template <class F, int LPR, int XU, bool SW>
+template <class F, int LPR, int XU, bool SW, class XT>
 int32_t launch_moe_bc(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
-                      int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
+                      int batch, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
     const int P = batch * top_k;
     const size_t per_col = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     if (batch > 1 && batch < 8 && nb < 64 && 2 * per_col + kMoeStaticLds <= (size_t)kLdsMax)
-        return launch_moe<F, 2, LPR, XU, 2, SW>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y,
-                                                xvec, true, st);
-    return launch_moe<F, 1, LPR, XU, 3, SW>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y, xvec,
-                                            batch == 1, st);
+        return launch_moe<F, 2, LPR, XU, 2, SW, XT>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot,
+                                                    y, xvec, true, st);
+    return launch_moe<F, 1, LPR, XU, 3, SW, XT>(Wx, estride, n_experts, N, nb, ids, P, top_k, x, xs_tok, xs_slot, y,
+                                                xvec, batch == 1, st);
 }
 
 // Batch 1: the pairs of one token need no grouping (a duplicated id only
 // streams that expert twice), so grid row p runs the dense kernel on
 // expert ids[p] with no prologue at all.
-template <class F, int LPR, int XU>
+template <class F, int LPR, int XU, class XT>
 int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
-                         int top_k, const float* x, int64_t xs_slot, float* y, hipStream_t st) {
+                         int top_k, const XT* x, int64_t xs_slot, float* y, hipStream_t st) {
     constexpr int NW = 4;
-    auto kern = qmv_kernel<F, 1, LPR, 1, XU, NW, 2, true>;
+    auto kern = qmv_kernel<F, 1, LPR, 1, XU, NW, 2, true, XT>;
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1045,23 +1045,23 @@ int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int6
 }
 
 // SW: the SwiGLU form takes the grouping kernel at every batch.
-template <class F, int LPR, bool SW>
+template <class F, int LPR, bool SW, class XT>
 int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
-                      int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
+                      int batch, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
-    const int K4 = nb * 8;   // 16-byte chunks of one activation row; 256 threads
+    const int K4 = nb * 8;   // 4-element chunks of one activation row; 256 threads
     if (!SW && batch == 1 && xvec && K4 <= 4 * 256)
-        return launch_moe_pairs<F, LPR, 4>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
+        return launch_moe_pairs<F, LPR, 4, XT>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
     if (!SW && batch == 1 && xvec && K4 <= 16 * 256)
-        return launch_moe_pairs<F, LPR, 16>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
+        return launch_moe_pairs<F, LPR, 16, XT>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
     if (K4 <= 2 * 256)
-        return launch_moe_bc<F, LPR, 2, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
-                                            xvec, st);
+        return launch_moe_bc<F, LPR, 2, SW, XT>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                                xvec, st);
     if (K4 <= 8 * 256)
-        return launch_moe_bc<F, LPR, 8, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+        return launch_moe_bc<F, LPR, 8, SW, XT>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                                xvec, st);
+    return launch_moe_bc<F, LPR, 0, SW, XT>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
                                             xvec, st);
-    return launch_moe_bc<F, LPR, 0, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec,
-                                        st);
 }
 
 // The combine kernel's grid: (row ranges, tokens).  Ranges x tokens fill
@@ -1112,8 +1112,8 @@ int32_t launch_combine(const uint8_t* Wx, int64_t estride, int n_experts, int64_
 // expert matrix; n_out: rows of one output vector.
 template <class F>
 int32_t moe_check(const char* name, const void* Wx, int64_t estride, int32_t n_experts, int64_t rows, int64_t K,
-                  const int32_t* ids, int32_t batch, int32_t top_k, const float* x, int64_t xs_tok, int64_t xs_slot,
-                  const float* y) {
+                  const int32_t* ids, int32_t batch, int32_t top_k, const void* x, size_t x_elem, int64_t xs_tok,
+                  int64_t xs_slot, const float* y) {
     if (!Wx || !ids || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (n_experts < 1) return fail(QMV_EINVAL, "%s: n_experts must be >= 1", name);
     if (rows < 1 || K < 32 || K % 32)
@@ -1131,40 +1131,42 @@ int32_t moe_check(const char* name, const void* Wx, int64_t estride, int32_t n_e
     if (xs_tok < 0) return fail(QMV_EINVAL, "%s: x_stride_token must be >= 0", name);
     if (top_k > 1 && xs_slot != 0 && xs_slot < K) return fail(QMV_EINVAL, "%s: x_stride_slot must be 0 or >= n_cols", name);
     if (xs_slot < 0) return fail(QMV_EINVAL, "%s: x_stride_slot must be >= 0", name);
-    if (!aligned(Wx, 4) || !aligned(x, 4) || !aligned(y, 4) || !aligned(ids, 4))
-        return fail(QMV_EALIGN, "%s: W_experts, x, the output and expert_ids must be 4-byte aligned", name);
+    if (!aligned(Wx, 4) || !aligned(y, 4) || !aligned(ids, 4))
+        return fail(QMV_EALIGN, "%s: W_experts, the output and expert_ids must be 4-byte aligned", name);
+    if (!aligned(x, x_elem)) return fail(QMV_EALIGN, "%s: x must be aligned to its %zu-byte elements", name, x_elem);
     const int64_t per_col = nb * (kXPad + (F::kNeedSx ? 1 : 0)) * (int64_t)sizeof(float);
     if (per_col + kMoeStaticLds > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
     return QMV_OK;
 }
 
-inline int moe_xvec(const float* x, int64_t xs_tok, int64_t xs_slot) {
-    return (aligned(x, 16) && xs_tok % 4 == 0 && xs_slot % 4 == 0) ? 1 : 0;
+template <class XT>
+int moe_xvec(const XT* x, int64_t xs_tok, int64_t xs_slot) {
+    return (aligned(x, XIn<XT>::kVecAlign) && xs_tok % 4 == 0 && xs_slot % 4 == 0) ? 1 : 0;
 }
 
 // SW = false: y[p][i] = DEQ(W_e)[i] x_p (N rows per expert).  SW = true:
 // every expert holds 2N rows and y[p][i] = SiLU(gate_i x_p) * (up_i x_p).
-template <class F, bool SW>
-int32_t moe(const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64_t K, const int32_t* ids,
-            int32_t batch, int32_t top_k, const float* x, int64_t xs_tok, int64_t xs_slot, float* y, void* stream) {
-    const char* name = SW ? "qmv_moe_swiglu" : "qmv_moe";
+template <class F, bool SW, class XT = float>
+int32_t moe(const char* name, const void* Wx, int64_t estride, int32_t n_experts, int64_t N, int64_t K,
+            const int32_t* ids, int32_t batch, int32_t top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y,
+            void* stream) {
     if (SW && N > ((int64_t)1 << 39)) return fail(QMV_EINVAL, "%s: n_ff too large", name);
-    const int32_t rc = moe_check<F>(name, Wx, estride, n_experts, SW ? 2 * N : N, K, ids, batch, top_k, x, xs_tok,
-                                    xs_slot, y);
+    const int32_t rc = moe_check<F>(name, Wx, estride, n_experts, SW ? 2 * N : N, K, ids, batch, top_k, x, sizeof(XT),
+                                    xs_tok, xs_slot, y);
     if (rc != QMV_OK) return rc;
     const int64_t nb = K / 32;
     const uint8_t* W8 = static_cast<const uint8_t*>(Wx);
     hipStream_t st = as_stream(stream);
     const int xvec = moe_xvec(x, xs_tok, xs_slot);
     if (nb >= 64)
-        return launch_moe_xu<F, 64, SW>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
-                                        xvec, st);
+        return launch_moe_xu<F, 64, SW, XT>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                            xvec, st);
     if (nb >= 32)
-        return launch_moe_xu<F, 32, SW>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
-                                        xvec, st);
-    return launch_moe_xu<F, 8, SW>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y, xvec,
-                                   st);
+        return launch_moe_xu<F, 32, SW, XT>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                            xvec, st);
+    return launch_moe_xu<F, 8, SW, XT>(W8, estride, n_experts, N, (int)nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
+                                       xvec, st);
 }
 
 template <class F>
@@ -1174,7 +1176,8 @@ int32_t moe_combine(const void* Wx, int64_t estride, int32_t n_experts, int64_t 
     const char* name = "qmv_moe_combine";
     if (!wts) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (!aligned(wts, 4)) return fail(QMV_EALIGN, "%s: weights must be 4-byte aligned", name);
-    const int32_t rc = moe_check<F>(name, Wx, estride, n_experts, N, K, ids, batch, top_k, x, xs_tok, xs_slot, out);
+    const int32_t rc = moe_check<F>(name, Wx, estride, n_experts, N, K, ids, batch, top_k, x, sizeof(float), xs_tok,
+                                    xs_slot, out);
     if (rc != QMV_OK) return rc;
     const int64_t nb = K / 32;
     const uint8_t* W8 = static_cast<const uint8_t*>(Wx);
@@ -1259,39 +1262,63 @@ extern "C" int32_t qmv_dequant(qmv_fmt fmt, const void* W, int64_t n_rows, int64
     default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_dequant: unknown format %d", (int)fmt);
     }
 }
+namespace qmv {
+namespace {
+// The plain and SwiGLU MoE entry points for activation type x_type.
+template <bool SW>
+int32_t moe_entry(const char* name, qmv_fmt fmt, const void* W, int64_t estride, int32_t E, int64_t N, int64_t K,
+                  const int32_t* ids, int32_t batch, int32_t top_k, const void* x, int32_t x_type, int64_t xs_tok,
+                  int64_t xs_slot, float* y, void* stream) {
+    if (fmt != QMV_Q8_0 && fmt != QMV_Q4_0 && fmt != QMV_Q4_1)
+        return fail(QMV_EUNSUPPORTED, "%s: unknown format %d", name, (int)fmt);
+    auto run = [&](auto xt) -> int32_t {
+        using XT = decltype(xt);
+        const XT* xp = static_cast<const XT*>(x);
+        switch (fmt) {
+        case QMV_Q8_0: return moe<Q8_0, SW, XT>(name, W, estride, E, N, K, ids, batch, top_k, xp, xs_tok, xs_slot, y, stream);
+        case QMV_Q4_0: return moe<Q4_0, SW, XT>(name, W, estride, E, N, K, ids, batch, top_k, xp, xs_tok, xs_slot, y, stream);
+        default: return moe<Q4_1, SW, XT>(name, W, estride, E, N, K, ids, batch, top_k, xp, xs_tok, xs_slot, y, stream);
+        }
+    };
+    switch (x_type) {
+    case QMV_X_F32: return run(float{});
+    case QMV_X_F16: return run(_Float16{});
+    case QMV_X_BF16: return run(__bf16{});
+    default: return fail(QMV_EINVAL, "%s: unknown activation type %d", name, (int)x_type);
+    }
+}
+}  // namespace
+}  // namespace qmv
+
 extern "C" int32_t qmv_moe(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes, int32_t n_experts,
                            int64_t n_rows, int64_t n_cols, const int32_t* expert_ids, int32_t batch, int32_t top_k,
                            const float* x, int64_t x_stride_token, int64_t x_stride_slot, float* y, void* stream) {
-    switch (fmt) {
-    case QMV_Q8_0:
-        return qmv::moe<qmv::Q8_0, false>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch,
-                                          top_k, x, x_stride_token, x_stride_slot, y, stream);
-    case QMV_Q4_0:
-        return qmv::moe<qmv::Q4_0, false>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch,
-                                          top_k, x, x_stride_token, x_stride_slot, y, stream);
-    case QMV_Q4_1:
-        return qmv::moe<qmv::Q4_1, false>(W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids, batch,
-                                          top_k, x, x_stride_token, x_stride_slot, y, stream);
-    default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_moe: unknown format %d", (int)fmt);
-    }
+    return qmv::moe_entry<false>("qmv_moe", fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols, expert_ids,
+                                 batch, top_k, x, QMV_X_F32, x_stride_token, x_stride_slot, y, stream);
+}
+
+extern "C" int32_t qmv_moe_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes, int32_t n_experts,
+                              int64_t n_rows, int64_t n_cols, const int32_t* expert_ids, int32_t batch, int32_t top_k,
+                              const void* x, int32_t x_type, int64_t x_stride_token, int64_t x_stride_slot, float* y,
+                              void* stream) {
+    return qmv::moe_entry<false>("qmv_moe_xt", fmt, W_experts, expert_stride_bytes, n_experts, n_rows, n_cols,
+                                 expert_ids, batch, top_k, x, x_type, x_stride_token, x_stride_slot, y, stream);
 }
 
 extern "C" int32_t qmv_moe_swiglu(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes, int32_t n_experts,
                                   int64_t n_ff, int64_t n_cols, const int32_t* expert_ids, int32_t batch,
                                   int32_t top_k, const float* x, int64_t x_stride_token, int64_t x_stride_slot,
                                   float* h, void* stream) {
-    switch (fmt) {
-    case QMV_Q8_0:
-        return qmv::moe<qmv::Q8_0, true>(W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, batch,
-                                         top_k, x, x_stride_token, x_stride_slot, h, stream);
-    case QMV_Q4_0:
-        return qmv::moe<qmv::Q4_0, true>(W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, batch,
-                                         top_k, x, x_stride_token, x_stride_slot, h, stream);
-    case QMV_Q4_1:
-        return qmv::moe<qmv::Q4_1, true>(W_experts, expert_stride_bytes, n_experts, n_ff, n_cols, expert_ids, batch,
-                                         top_k, x, x_stride_token, x_stride_slot, h, stream);
-    default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_moe_swiglu: unknown format %d", (int)fmt);
-    }
+    return qmv::moe_entry<true>("qmv_moe_swiglu", fmt, W_experts, expert_stride_bytes, n_experts, n_ff, n_cols,
+                                expert_ids, batch, top_k, x, QMV_X_F32, x_stride_token, x_stride_slot, h, stream);
+}
+
+extern "C" int32_t qmv_moe_swiglu_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
+                                     int32_t n_experts, int64_t n_ff, int64_t n_cols, const int32_t* expert_ids,
+                                     int32_t batch, int32_t top_k, const void* x, int32_t x_type,
+                                     int64_t x_stride_token, int64_t x_stride_slot, float* h, void* stream) {
+    return qmv::moe_entry<true>("qmv_moe_swiglu_xt", fmt, W_experts, expert_stride_bytes, n_experts, n_ff, n_cols,
+                                expert_ids, batch, top_k, x, x_type, x_stride_token, x_stride_slot, h, stream);
 }
 
 extern "C" int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes, int32_t n_experts,

@@ -215,6 +215,21 @@ int32_t qmv_moe(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                 float* y, void* stream);
 
 /*
+ * qmv_moe with fp32, fp16 or bf16 activations ([ESP] Sec. 2.2: f16 and bf16
+ * activation entry points of the one core).  x holds elements of x_type
+ * (QMV_X_F32 / QMV_X_F16 / QMV_X_BF16), aligned to the element size; the
+ * strides count elements.  Activations are widened to fp32 exactly when
+ * staged, so the result equals, bitwise, qmv_moe on the widened values.
+ * Errors: as qmv_moe; QMV_EINVAL for an unknown x_type, QMV_EALIGN for x
+ * not aligned to its element size.
+ */
+int32_t qmv_moe_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
+                   int32_t n_experts, int64_t n_rows, int64_t n_cols,
+                   const int32_t* expert_ids, int32_t batch, int32_t top_k,
+                   const void* x, int32_t x_type, int64_t x_stride_token, int64_t x_stride_slot,
+                   float* y, void* stream);
+
+/*
  * MoE gate/up projection with the SwiGLU step fused ([ZEN] "Architecture":
  * the MLP is SwiGLU(gate, up, down); [NST] Sec. "The Unified Quant Core":
  * each routed expert goes through the same matvec core).  Every expert
@@ -235,6 +250,13 @@ int32_t qmv_moe_swiglu(qmv_fmt fmt, const void* W_experts, int64_t expert_stride
                        const int32_t* expert_ids, int32_t batch, int32_t top_k,
                        const float* x, int64_t x_stride_token, int64_t x_stride_slot,
                        float* h, void* stream);
+
+/* qmv_moe_swiglu with x of x_type, as qmv_moe_xt (h stays fp32). */
+int32_t qmv_moe_swiglu_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
+                          int32_t n_experts, int64_t n_ff, int64_t n_cols,
+                          const int32_t* expert_ids, int32_t batch, int32_t top_k,
+                          const void* x, int32_t x_type, int64_t x_stride_token, int64_t x_stride_slot,
+                          float* h, void* stream);
 
 /*
  * MoE down projection with the router-weighted combine of each token's

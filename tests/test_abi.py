@@ -29,7 +29,8 @@ def qmv():
 def test_every_declared_symbol_is_exported(qmv):
     names = declared_functions()
     assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "qmv_i8_requant",
-            "qmv_i8_requant_lut", "qmv_moe", "qmv_moe_swiglu", "qmv_moe_combine", "qmv_dequant",
+            "qmv_i8_requant_lut", "qmv_moe", "qmv_moe_xt", "qmv_moe_swiglu", "qmv_moe_swiglu_xt", "qmv_moe_combine",
+            "qmv_dequant",
             "qmv_chain", "qmv_last_error", "qmv_abi_version"} <= set(names)
     raw = ctypes.CDLL(qmv.library_path())
     for n in names:
@@ -142,6 +143,18 @@ def test_moe_swiglu_and_combine_argument_errors(qmv):
     assert cb(1, A, per, 4, 16, 64, A, A + 2, 2, 2, A, 128, 64, A, None) == EALIGN
     assert cb(1, A, per, 4, 16, 64, A, A, 2, 17, A, 128, 64, A, None) == EINVAL and "top_k" in qmv.last_error()
     assert cb(1, A, per, 4, 16, 64, A, A, 2, 2, A, 128, 32, A, None) == EINVAL
+
+
+def test_moe_xt_argument_errors(qmv):
+    per = 16 * 2 * 18
+    for name in ("qmv_moe_xt", "qmv_moe_swiglu_xt"):
+        f = getattr(qmv.lib(), name)
+        p = per * (2 if "swiglu" in name else 1)
+        assert f(1, A, p, 4, 16, 64, A, 2, 2, A, 7, 64, 0, A, None) == EINVAL and "activation type" in qmv.last_error()
+        assert f(1, A, p, 4, 16, 64, A, 2, 2, A + 1, qmv.X_F16, 64, 0, A, None) == EALIGN
+        assert "2-byte" in qmv.last_error()
+        assert f(1, A, p, 4, 16, 64, A, 2, 2, A + 2, qmv.X_F32, 64, 0, A, None) == EALIGN
+        assert f(9, A, p, 4, 16, 64, A, 2, 2, A, qmv.X_BF16, 64, 0, A, None) == EUNSUPPORTED
 
 
 def test_moe_argument_errors(qmv):

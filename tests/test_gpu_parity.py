@@ -959,3 +959,48 @@ def test_moe_combine_edges(env, fmt, case):
             assert np.array_equal(out[1].view(np.uint32), y[1, 1].view(np.uint32))
     err = np.abs(out.astype(np.float64) - ref)
     assert np.all(err <= combine_bound(S, w)), (case, float((err / combine_bound(S, w)).max()))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+def test_moe_x16_equals_widened_fp32(env, fmt, kind):
+    """qmv_moe_xt and qmv_moe_swiglu_xt with 16-bit activations equal, bitwise,
+    qmv_moe / qmv_moe_swiglu on the exactly widened activations: batch 1
+    (per-pair route) and 2..8 (grouping kernel), per-token and per-slot
+    inputs, duplicated ids, rows needing the looping stager, and x at a
+    2-byte offset; within the bound of the oracle on the widened values."""
+    torch, qmv = env
+    E = 6
+    cases = [("b1_tok", 1, 256, 2048, [[4, 1, 4, 0]], False, 0),
+             ("b8_tok", 8, 96, 1024, None, False, 0),
+             ("b3_slot", 3, 64, 768, [[0, 5, 2], [2, 2, 1], [5, 0, 3]], True, 0),
+             ("b2_long", 2, 40, 16416, [[1, 3], [3, 5]], False, 0),
+             ("b2_offset", 2, 72, 512, [[2, 0], [1, 2]], True, 1)]
+    for name, B, N, K, ids, per_slot, off in cases:
+        say(f"moe x16 {fmt} {kind} {name}")
+        T = 4 if ids is None else len(ids[0])
+        ids_np = wl.moe_ids(f"moe/x16/ids/{name}", B, T, E) if ids is None else np.array(ids, dtype=np.int32)
+        Wall = wl.quant_weights(fmt, f"moe/x16/W/{name}", E * 2 * N, K).reshape(-1)
+        per = wl.block_bytes(fmt, 2 * N, K)
+        shape = (B, T, K) if per_slot else (B, K)
+        x = wl.activations(f"moe/x16/x/{name}", int(np.prod(shape[:-1])), K).reshape(shape)
+        xh, xw = _x16(torch, x, kind)
+        if off:
+            # the same values one element into a larger buffer: 2-byte aligned only
+            buf = torch.zeros(xh.numel() + 1, dtype=xh.dtype, device="cuda:0")
+            buf[1:] = xh.reshape(-1)
+            xh = buf[1:].view(shape)
+        Wd, idsd = dev(torch, Wall), dev(torch, ids_np)
+        y16 = qmv.qmv_moe_xt(fmt, Wd, per, E, 2 * N, K, idsd, xh)
+        y32 = qmv.qmv_moe(fmt, Wd, per, E, 2 * N, K, idsd, xw)
+        h16 = qmv.qmv_moe_swiglu_xt(fmt, Wd, per, E, N, K, idsd, xh)
+        h32 = qmv.qmv_moe_swiglu(fmt, Wd, per, E, N, K, idsd, xw)
+        torch.cuda.synchronize()
+        assert torch.equal(y16.view(torch.int32), y32.view(torch.int32)), name
+        assert torch.equal(h16.view(torch.int32), h32.view(torch.int32)), name
+        xw_np = xw.cpu().numpy()
+        if per_slot:
+            yr, S = oracle.moe(fmt, Wall, per, E, 2 * N, K, ids_np, None, x_slots=xw_np)
+        else:
+            yr, S = oracle.moe(fmt, Wall, per, E, 2 * N, K, ids_np, xw_np)
+        assert_tol(y16.cpu().numpy(), yr, S, (fmt, kind, name))
