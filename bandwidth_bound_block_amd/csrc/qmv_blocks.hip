@@ -210,11 +210,12 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 // the same lane-to-block mapping, arithmetic and reduction order as
 // qmv_kernel<F, 1, 64, 1, ...> (bitwise the same y), but each step's 64
 // blocks arrive as whole 16-byte chunks with non-temporal loads and are
-// re-read block-aligned from a per-wave LDS scratch.  One row per wave at
-// a time; rows are taken wave, wave + grid waves, ...  The rows are those
-// of up to kMaxSegs matrices sharing x, concatenated (a wave-uniform
-// lookup finds a row's matrix).
-template <class F, int XU, int NW, int PD = 2, class XT = float>
+// re-read block-aligned from a per-wave LDS scratch.  A wave works on RR
+// rows at a time (rows RR*p .. RR*p + RR - 1 for p = wave, wave + grid
+// waves, ...), so a step moves RR * 64 blocks.  The rows are those of up to
+// kMaxSegs matrices sharing x, concatenated (a wave-uniform lookup finds a
+// row's matrix).
+template <class F, int XU, int NW, int PD = 2, class XT = float, int RR = 1>
 __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int nb, const XT* __restrict__ x) {
     using C = Contig<F>;
     extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
@@ -222,10 +223,12 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
     float* sx = lds + nb * kXPad;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    uint8_t* scratch = reinterpret_cast<uint8_t*>(lds + nb * (kXPad + (F::kNeedSx ? 1 : 0))) + wave * C::kStepBytes;
+    uint8_t* scratch =
+        reinterpret_cast<uint8_t*>(lds + nb * (kXPad + (F::kNeedSx ? 1 : 0))) + wave * RR * C::kStepBytes;
     const int T = nb / 64;
     const int64_t wstride = (int64_t)gridDim.x * NW;
     const int64_t N = segs.end[segs.n - 1];
+    const int64_t NP = (N + RR - 1) / RR;          // row groups
     auto seg_of = [&](int64_t g) {
         int i = 0;
 #pragma unroll
@@ -233,42 +236,63 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
         return i;
     };
 
-    typename C::Chunks buf[PD];
-    int64_t lrow = (int64_t)blockIdx.x * NW + wave;   // next step to load
+    typename C::Chunks buf[PD][RR];
+    int64_t lrow = (int64_t)blockIdx.x * NW + wave;   // next step to load (row group)
     int lt = 0;
     int64_t crow = lrow;                              // next step to compute
     int ct = 0;
     auto advance = [&](int64_t& row, int& t) {
         if (++t == T) { t = 0; row += wstride; }
     };
-    auto load_next = [&](typename C::Chunks& c) {
-        const int64_t row = min(lrow, N - 1);          // past the end: re-read a loaded step
-        const int t = lrow < N ? lt : 0;
-        const int i = seg_of(row);
-        const int64_t r = row - (i ? segs.end[i - 1] : 0);
-        C::fetch(segs.W[i] + (r * nb + 64 * t) * F::kBytes, lane, c);
-        if (lrow < N) advance(lrow, lt);
+    auto load_next = [&](typename C::Chunks (&c)[RR]) {
+        const int64_t p = min(lrow, NP - 1);           // past the end: re-read a loaded step
+        const int t = lrow < NP ? lt : 0;
+#pragma unroll
+        for (int k = 0; k < RR; ++k) {
+            const int64_t row = min(RR * p + k, N - 1);
+            const int i = seg_of(row);
+            const int64_t r = row - (i ? segs.end[i - 1] : 0);
+            C::fetch(segs.W[i] + (r * nb + 64 * t) * F::kBytes, lane, c[k]);
+        }
+        if (lrow < NP) advance(lrow, lt);
     };
-    float acc = 0.f;
-    auto compute_step = [&](int t, const typename C::Chunks& c) {
-        typename F::Raw r;
-        C::to_block(c, scratch, lane, r);
+    float acc[RR];
+#pragma unroll
+    for (int k = 0; k < RR; ++k) acc[k] = 0.f;
+    auto compute_step = [&](int t, const typename C::Chunks (&c)[RR]) {
         const int j = lane + 64 * t;
-        float d, m;
-        uint32_t cd[8];
-        F::decode(r, d, m, cd);
-        float q[32];
-        codes_to_float<F>(cd, q);
-        float sdot[1] = {0.f};
-        dot_cols<1>(q, xs + j * kXPad, nb * kXPad, sdot, 1);
-        acc = Term<F>::add(acc, d, m, sdot[0], F::kNeedSx ? sx[j] : 0.f);
+        float d[RR], m[RR];
+        uint32_t cd[RR][8];
+#pragma unroll
+        for (int k = 0; k < RR; ++k) {
+            typename F::Raw r;
+            C::to_block(c[k], scratch + k * C::kStepBytes, lane, r);
+            F::decode(r, d[k], m[k], cd[k]);
+        }
+        float sdot[RR][1];
+        if constexpr (RR == 1) {
+            float q[32];
+            codes_to_float<F>(cd[0], q);
+            float s1[1] = {0.f};
+            dot_cols<1>(q, xs + j * kXPad, nb * kXPad, s1, 1);
+            sdot[0][0] = s1[0];
+        } else {
+            dot_multi<F, RR, 1>(cd, xs + j * kXPad, nb * kXPad, sdot, 1);
+        }
+        const float sxj = F::kNeedSx ? sx[j] : 0.f;
+#pragma unroll
+        for (int k = 0; k < RR; ++k) acc[k] = Term<F>::add(acc[k], d[k], m[k], sdot[k][0], sxj);
         if (t == T - 1) {
-            const float tot = segment_sum<64>(acc);
-            if (lane == 0) {
-                const int i = seg_of(crow);
-                segs.y[i][crow - (i ? segs.end[i - 1] : 0)] = tot;
+#pragma unroll
+            for (int k = 0; k < RR; ++k) {
+                const float tot = segment_sum<64>(acc[k]);
+                const int64_t row = RR * crow + k;
+                if (lane == 0 && row < N) {
+                    const int i = seg_of(row);
+                    segs.y[i][row - (i ? segs.end[i - 1] : 0)] = tot;
+                }
+                acc[k] = 0.f;
             }
-            acc = 0.f;
         }
     };
 
@@ -298,10 +322,11 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
         __builtin_amdgcn_sched_barrier(0);                 \
         compute_step(ct, buf[(P)]);                        \
         advance(crow, ct);                                 \
-        if (crow >= N) break;                              \
+        if (crow >= NP) break;                             \
     }
     static_assert(PD >= 2 && PD <= 4, "pipeline depth");
-    if (crow < N) {
+    static_assert(RR == 1 || RR == 2, "rows per step");
+    if (crow < NP) {
         while (true) {
             QMV_PIPE_STEP(0)
             QMV_PIPE_STEP(1)
@@ -743,10 +768,9 @@ __global__ __launch_bounds__(kThreads) void dequant_kernel(const uint8_t* __rest
 
 // ------------------------------------------------------------------ host
 
-template <class F, int B, int LPR, int XU, int NW, class XT = float>
+template <class F, int B, int LPR, int XU, int NW, class XT = float, int RPL = 1>
 int32_t launch_b(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                  hipStream_t st) {
-    constexpr int RPL = 1;
     auto kern = qmv_kernel<F, B, LPR, RPL, XU, NW, 2, false, XT>;
     const size_t lds = (size_t)B * nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     static bool attr_set = false;   // benign race: every thread sets the same value
@@ -768,18 +792,19 @@ int32_t launch_b(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, 
 
 // Lanes per row: whole waves for long rows, smaller segments for short rows
 // so that lanes are not left idle (e.g. 24 blocks -> 8 lanes x 3).
-template <class F, int B, int XU, int NW, class XT = float>
+template <class F, int B, int XU, int NW, class XT = float, int RPL = 1>
 int32_t launch_lpr(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                    hipStream_t st) {
-    if (nb >= 64) return launch_b<F, B, 64, XU, NW, XT>(W, N, nb, x, ldx, y, ldy, st);
-    if (nb >= 32) return launch_b<F, B, 32, XU, NW, XT>(W, N, nb, x, ldx, y, ldy, st);
-    return launch_b<F, B, 8, XU, NW, XT>(W, N, nb, x, ldx, y, ldy, st);
+    if (nb >= 64) return launch_b<F, B, 64, XU, NW, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
+    if (nb >= 32) return launch_b<F, B, 32, XU, NW, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
+    return launch_b<F, B, 8, XU, NW, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
 }
 
-template <class F, int XU, int NW, class XT = float>
+template <class F, int XU, int NW, class XT = float, int RR = 1>
 int32_t launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
-    auto kern = qmv_kernel_c<F, XU, NW, 2, XT>;
-    const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float) + NW * Contig<F>::kStepBytes;
+    auto kern = qmv_kernel_c<F, XU, NW, 2, XT, RR>;
+    const size_t lds =
+        (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float) + (size_t)NW * RR * Contig<F>::kStepBytes;
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -787,7 +812,7 @@ int32_t launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
             return fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
         attr_set = true;
     }
-    const int64_t tiles = (segs.end[segs.n - 1] + NW - 1) / NW;
+    const int64_t tiles = ((segs.end[segs.n - 1] + RR - 1) / RR + NW - 1) / NW;
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
     hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, segs, nb, x);
@@ -796,14 +821,14 @@ int32_t launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
 
 // XU 16-byte activation loads per thread stage K4 = K / 4 chunks with a
 // workgroup of NW waves; past 8 per thread the staging loops instead.
-template <class F, int NW, class XT = float>
+template <class F, int NW, class XT = float, int RR = 1>
 int32_t launch_c_xu(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
     const int per = (nb * 8 + 64 * NW - 1) / (64 * NW);
-    if (per <= 1) return launch_c<F, 1, NW, XT>(segs, nb, x, st);
-    if (per <= 2) return launch_c<F, 2, NW, XT>(segs, nb, x, st);
-    if (per <= 4) return launch_c<F, 4, NW, XT>(segs, nb, x, st);
-    if (per <= 8) return launch_c<F, 8, NW, XT>(segs, nb, x, st);
-    return launch_c<F, 0, NW, XT>(segs, nb, x, st);
+    if (per <= 1) return launch_c<F, 1, NW, XT, RR>(segs, nb, x, st);
+    if (per <= 2) return launch_c<F, 2, NW, XT, RR>(segs, nb, x, st);
+    if (per <= 4) return launch_c<F, 4, NW, XT, RR>(segs, nb, x, st);
+    if (per <= 8) return launch_c<F, 8, NW, XT, RR>(segs, nb, x, st);
+    return launch_c<F, 0, NW, XT, RR>(segs, nb, x, st);
 }
 
 // Batch 1 with whole 64-block steps and 16-byte aligned W and x: the
@@ -822,8 +847,16 @@ bool try_launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st, bool
     const int64_t N = segs.end[segs.n - 1];
     const bool q8 = !F::kNeedSx;
     const bool long_rows = nb >= 256;
-    if (!force && (q8 ? !(N >= 8192 || long_rows) : !((N >= 2048 && N <= 32768) || long_rows))) return false;
+    // Measured (8B shapes, cache-cold): Q8_0 gains from this kernel on >= 8192
+    // rows or long rows; Q4_x only on long rows (down) as a single matrix
+    // (the per-block kernel with two rows per lane is faster elsewhere),
+    // and on row groups of > 8192 rows two rows per wave step (4 waves).
+    if (!force && (q8 ? !(N >= 8192 || long_rows) : !long_rows)) return false;
     const size_t lds_x = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    if (!q8 && !long_rows && N > 8192 && lds_x + 4 * 2 * (size_t)Contig<F>::kStepBytes <= (size_t)kLdsMax) {
+        *rc = launch_c_xu<F, 4, XT, 2>(segs, nb, x, st);
+        return true;
+    }
     int nw = (long_rows || (!q8 && N <= 4096)) ? 16 : 8;
     while (nw >= 4 && lds_x + (size_t)nw * Contig<F>::kStepBytes > (size_t)kLdsMax) nw /= 2;
     switch (nw) {
@@ -852,14 +885,16 @@ int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx,
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     const bool vec = aligned(x, XIn<XT>::kVecAlign);
     const int K4 = nb * 8;
+    // Q4_x: two rows per lane (measured faster on every 8B shape it takes)
+    constexpr int RPL = F::kNeedSx ? 2 : 1;
     if (lds > 40 * 1024) {
-        if (vec && K4 <= 2 * 512) return launch_lpr<F, 1, 2, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
-        if (vec && K4 <= 8 * 512) return launch_lpr<F, 1, 8, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
-        return launch_lpr<F, 1, 0, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
+        if (vec && K4 <= 2 * 512) return launch_lpr<F, 1, 2, 8, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
+        if (vec && K4 <= 8 * 512) return launch_lpr<F, 1, 8, 8, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
+        return launch_lpr<F, 1, 0, 8, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
     }
-    if (vec && K4 <= 4 * 256) return launch_lpr<F, 1, 4, 4, XT>(W, N, nb, x, ldx, y, ldy, st);
-    if (vec && K4 <= 16 * 256) return launch_lpr<F, 1, 16, 4, XT>(W, N, nb, x, ldx, y, ldy, st);
-    return launch_lpr<F, 1, 0, 4, XT>(W, N, nb, x, ldx, y, ldy, st);
+    if (vec && K4 <= 4 * 256) return launch_lpr<F, 1, 4, 4, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
+    if (vec && K4 <= 16 * 256) return launch_lpr<F, 1, 16, 4, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
+    return launch_lpr<F, 1, 0, 4, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
 }
 
 template <class F>

@@ -129,13 +129,14 @@ def test_random_byte_blocks(env, fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_contiguous_path_equals_per_block_path(env, fmt):
     """Rows of whole 64-block steps with 16-byte aligned W take the
-    contiguous-chunk kernel; the same bytes at a 4-byte offset take the
-    per-block kernel.  Same lane mapping and arithmetic: bitwise equal, and
-    both within the bound of the oracle.  The shapes reach each launch
-    choice of the contiguous kernel: >= 8192 rows (Q8_0, 8 waves), Q4 with
-    2048..4096 rows (16 waves), >= 256 blocks per row (16 waves), the LDS
-    fallbacks to 8 waves (30720 columns, loop staging) and 4 waves (32768
-    columns), and ragged row counts."""
+    contiguous-chunk kernel where it is chosen; the same bytes at a 4-byte
+    offset take the per-block kernel.  Same lane mapping and arithmetic:
+    bitwise equal, and both within the bound of the oracle.  The shapes
+    reach each launch choice: >= 8192 rows (Q8_0, 8 waves), >= 256 blocks
+    per row (16 waves), the LDS fallbacks to 8 waves (30720 columns, loop
+    staging) and 4 waves (32768 columns), Q4 rows of < 256 blocks (the
+    per-block kernel with two rows per lane, aligned or not), and ragged
+    row counts."""
     torch, qmv = env
     f = _chain_fn(qmv, fmt)
     for N, K in [(8193, 2048), (2100, 4096), (5, 8192), (129, 14336), (3, 30720), (2, 32768), (40000, 2048)]:
@@ -728,6 +729,9 @@ def test_chain_shared_input_groups(env, fmt):
         "gate_up": [(3000, 2048), (3000, 2048)],
         "five": [(300, 2048), (77, 2048), (1, 2048), (513, 2048), (64, 2048)],
         "misaligned": [(700, 2048), (129, 2048)],
+        # > 8192 rows: Q4 takes two rows per wave step; a row pair straddles
+        # the two matrices and the last pair has one row
+        "big_odd": [(5001, 2048), (4000, 2048)],
     }
     for gname, shapes in groups.items():
         K = shapes[0][1]
