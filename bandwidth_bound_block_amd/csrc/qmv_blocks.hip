@@ -1061,7 +1061,8 @@ template <class F, int LPR, int XU, class XT>
 int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                          int top_k, const XT* x, int64_t xs_slot, float* y, hipStream_t st) {
     constexpr int NW = 4;
-    auto kern = qmv_kernel<F, 1, LPR, 1, XU, NW, 2, true, XT>;
+    constexpr int RPL = F::kNeedSx ? 2 : 1;   // Q4_x: two rows per lane, as the dense batch-1 kernel
+    auto kern = qmv_kernel<F, 1, LPR, RPL, XU, NW, 2, true, XT>;
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1071,7 +1072,7 @@ int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int6
     }
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
-    const int64_t tiles = (N + NW * (64 / LPR) - 1) / (NW * (64 / LPR));
+    const int64_t tiles = (N + NW * (64 / LPR) * RPL - 1) / (NW * (64 / LPR) * RPL);
     const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu / top_k));
     const PairRoute route{ids, estride, xs_slot, n_experts};
     hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)top_k), dim3(64 * NW), lds, st, Wx, N, nb, x, (int64_t)nb * 32,
