@@ -48,6 +48,10 @@ struct PairRoute {
     int32_t n_experts;
 };
 
+// SiLU(g) = g / (1 + e^-g), in fp32 on the device (expf of the device
+// library); g = -inf or +inf give -0 and +inf, NaN stays NaN.
+__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+
 // Dense matvec.  A persistent grid (as many workgroups as fit on the GPU at
 // once); wave w of the grid takes row tiles w, w + waves, ... .  A tile is
 // G*RPL rows (G row segments of LPR lanes, RPL rows per lane) and is worked
@@ -55,18 +59,22 @@ struct PairRoute {
 // li + LPR*t of each of its RPL rows.  The blocks of the next step are
 // loaded while the current step is computed (two steps in flight per wave),
 // and the first step's loads are issued before the activation staging so
-// that both latencies overlap.
-template <class F, int B, int LPR, int RPL, int XU, int NW, int PD = 2, bool ROUTE = false, class XT = float>
+// that both latencies overlap.  SWG (routed, RPL = 2): the expert holds 2N
+// rows, gate rows then up rows; output row i pairs gate row i with up row
+// N + i in the same lanes and writes SiLU(gate) * up.
+template <class F, int B, int LPR, int RPL, int XU, int NW, int PD = 2, bool ROUTE = false, class XT = float,
+          bool SWG = false>
 __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict__ W, int64_t N, int nb,
                                                        const XT* __restrict__ x, int64_t ldx,
                                                        float* __restrict__ y, int64_t ldy, int xvec,
                                                        const PairRoute route) {
+    static_assert(!SWG || (RPL == 2 && B == 1), "paired gate/up rows: two rows per lane, one column");
     extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
     float* xs = lds;
     float* sx = lds + B * nb * kXPad;
 
     constexpr int G = 64 / LPR;
-    constexpr int ROWS = G * RPL;
+    constexpr int ROWS = SWG ? G : G * RPL;   // output rows per tile
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
     const int seg = lane / LPR;
@@ -92,7 +100,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
         const int j = min(li + LPR * t, nb - 1);      // clamp: stays in bounds
 #pragma unroll
         for (int r = 0; r < RPL; ++r) {
-            const int64_t row = min(tile * ROWS + r * G + seg, N - 1);
+            const int64_t row = SWG ? min(tile * G + seg, N - 1) + r * N : min(tile * ROWS + r * G + seg, N - 1);
             F::fetch(W, row * nb + j, blk[r]);
         }
     };
@@ -129,12 +137,17 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 #pragma unroll
                 for (int b = 0; b < B; ++b) acc[r][b] = segment_sum<LPR>(acc[r][b]);
             if (li == 0) {
+                if constexpr (SWG) {
+                    const int64_t row = tile * G + seg;
+                    if (row < N) y[row] = bad ? __builtin_nanf("") : silu(acc[0][0]) * acc[1][0];
+                } else {
 #pragma unroll
-                for (int r = 0; r < RPL; ++r) {
-                    const int64_t row = tile * ROWS + r * G + seg;
-                    if (row < N) {
+                    for (int r = 0; r < RPL; ++r) {
+                        const int64_t row = tile * ROWS + r * G + seg;
+                        if (row < N) {
 #pragma unroll
-                        for (int b = 0; b < B; ++b) y[b * ldy + row] = bad ? __builtin_nanf("") : acc[r][b];
+                            for (int b = 0; b < B; ++b) y[b * ldy + row] = bad ? __builtin_nanf("") : acc[r][b];
+                        }
                     }
                 }
             }
@@ -467,10 +480,6 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
 #undef QMV_MOE_STEP
     __syncthreads();   // xs is restaged by the next chunk
 }
-
-// SiLU(g) = g / (1 + e^-g), in fp32 on the device (expf of the device
-// library); g = -inf or +inf give -0 and +inf, NaN stays NaN.
-__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
 
 // Grouped expert matvec.  Workgroup (bx, u) serves the u-th distinct id
 // of the (token, slot) pairs, in first-occurrence order, and the bx-th
@@ -1057,12 +1066,15 @@ int32_t launch_moe_bc(const uint8_t* Wx, int64_t estride, int n_experts, int64_t
 // Batch 1: the pairs of one token need no grouping (a duplicated id only
 // streams that expert twice), so grid row p runs the dense kernel on
 // expert ids[p] with no prologue at all.
-template <class F, int LPR, int XU, class XT>
+template <class F, int LPR, int XU, class XT, bool SW>
 int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                          int top_k, const XT* x, int64_t xs_slot, float* y, hipStream_t st) {
     constexpr int NW = 4;
-    constexpr int RPL = F::kNeedSx ? 2 : 1;   // Q4_x: two rows per lane, as the dense batch-1 kernel
-    auto kern = qmv_kernel<F, 1, LPR, RPL, XU, NW, 2, true, XT>;
+    // Q4_x: two rows per lane, as the dense batch-1 kernel; SwiGLU: the
+    // gate and up rows of an output row
+    constexpr int RPL = (SW || F::kNeedSx) ? 2 : 1;
+    constexpr int OUT_RPL = SW ? 1 : RPL;      // output rows per lane
+    auto kern = qmv_kernel<F, 1, LPR, RPL, XU, NW, 2, true, XT, SW>;
     static bool attr_set = false;   // benign race: every thread sets the same value
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1072,7 +1084,7 @@ int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int6
     }
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
-    const int64_t tiles = (N + NW * (64 / LPR) * RPL - 1) / (NW * (64 / LPR) * RPL);
+    const int64_t tiles = (N + NW * (64 / LPR) * OUT_RPL - 1) / (NW * (64 / LPR) * OUT_RPL);
     const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu / top_k));
     const PairRoute route{ids, estride, xs_slot, n_experts};
     hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)top_k), dim3(64 * NW), lds, st, Wx, N, nb, x, (int64_t)nb * 32,
@@ -1080,16 +1092,15 @@ int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int6
     return check_launch("qmv_moe");
 }
 
-// SW: the SwiGLU form takes the grouping kernel at every batch.
 template <class F, int LPR, bool SW, class XT>
 int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                       int batch, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
     const int K4 = nb * 8;   // 4-element chunks of one activation row; 256 threads
-    if (!SW && batch == 1 && xvec && K4 <= 4 * 256)
-        return launch_moe_pairs<F, LPR, 4, XT>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
-    if (!SW && batch == 1 && xvec && K4 <= 16 * 256)
-        return launch_moe_pairs<F, LPR, 16, XT>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
+    if (batch == 1 && xvec && K4 <= 4 * 256)
+        return launch_moe_pairs<F, LPR, 4, XT, SW>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
+    if (batch == 1 && xvec && K4 <= 16 * 256)
+        return launch_moe_pairs<F, LPR, 16, XT, SW>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
     if (K4 <= 2 * 256)
         return launch_moe_bc<F, LPR, 2, SW, XT>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
                                                 xvec, st);
