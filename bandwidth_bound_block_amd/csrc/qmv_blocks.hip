@@ -624,8 +624,48 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
         s_w[tid] = wts[b * top_k + tid];
     }
     using Raw = typename F::Raw;
+    __syncthreads();   // s_base, s_w
     for (int s0 = 0; s0 < top_k; s0 += SC) {
         const int sc = min(SC, top_k - s0);
+        // this wave's units q = wave, wave + NW, ... of the chunk's
+        // sc * wtiles (slot-major), T steps each
+        const int units = sc * wtiles;
+        const int my_units = wave < units ? (units - wave + NW - 1) / NW : 0;
+        const int64_t nsteps = (int64_t)my_units * T;
+        struct Cur {
+            int q, t;
+        };
+        Cur lc{wave, 0}, cc = lc;
+        auto advance = [&](Cur& k) {
+            if (++k.t == T) {
+                k.t = 0;
+                k.q += NW;
+            }
+        };
+        int64_t lrem = nsteps;
+        int lslot = min(lc.q, units - 1) / wtiles;
+        const uint8_t* lW = s_base[s0 + lslot];
+        auto load_next = [&](Raw& r) {
+            const int q = min(lc.q, units - 1);            // a wave without units re-reads a valid block
+            const int slot = q / wtiles;
+            const int64_t tile = tb + (q - slot * wtiles);
+            const int64_t row = min(tile * G + seg, N - 1);
+            const int j = min(li + LPR * lc.t, nb - 1);
+            F::fetch(lW, row * nb + j, r);
+            if (lrem > 1) {   // past the last step: re-read it (in cache)
+                --lrem;
+                advance(lc);
+                const int ns = lc.q / wtiles;
+                if (ns != lslot) {
+                    lslot = ns;
+                    lW = s_base[s0 + ns];
+                }
+            }
+        };
+        // the first weight loads go out before the activations are staged
+        Raw buf[PD];
+#pragma unroll
+        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
         // the chunk's activation vectors (every wave is done with the
         // previous chunk's: its units all ended before this barrier)
         __syncthreads();
@@ -670,41 +710,7 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
             block_sums<64 * NW>(xs, sx, sc * nb);
             __syncthreads();
         }
-        // this wave's units q = wave, wave + NW, ... of the chunk's
-        // sc * wtiles (slot-major), T steps each
-        const int units = sc * wtiles;
-        const int my_units = wave < units ? (units - wave + NW - 1) / NW : 0;
-        const int64_t nsteps = (int64_t)my_units * T;
         if (nsteps == 0) continue;
-        struct Cur {
-            int q, t;
-        };
-        Cur lc{wave, 0}, cc = lc;
-        auto advance = [&](Cur& k) {
-            if (++k.t == T) {
-                k.t = 0;
-                k.q += NW;
-            }
-        };
-        int64_t lrem = nsteps;
-        int lslot = lc.q / wtiles;
-        const uint8_t* lW = s_base[s0 + lslot];
-        auto load_next = [&](Raw& r) {
-            const int slot = lc.q / wtiles;
-            const int64_t tile = tb + (lc.q - slot * wtiles);
-            const int64_t row = min(tile * G + seg, N - 1);
-            const int j = min(li + LPR * lc.t, nb - 1);
-            F::fetch(lW, row * nb + j, r);
-            if (lrem > 1) {   // past the last step: re-read it (in cache)
-                --lrem;
-                advance(lc);
-                const int ns = lc.q / wtiles;
-                if (ns != lslot) {
-                    lslot = ns;
-                    lW = s_base[s0 + ns];
-                }
-            }
-        };
         float acc = 0.f;
         auto compute = [&](const Raw& r) {
             const int slot = cc.q / wtiles;
@@ -727,9 +733,6 @@ __global__ __launch_bounds__(64 * NW) void moe_combine_kernel(const uint8_t* __r
                 acc = 0.f;
             }
         };
-        Raw buf[PD];
-#pragma unroll
-        for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
         int64_t crem = nsteps;
 #define QMV_MOEC_STEP(P)                                   \
     {                                                      \
