@@ -45,8 +45,8 @@ TRAFFIC_RECORD = {
     "sources": ["bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
                 "bandwidth_bound_block_amd/csrc/qmv_block_decode.h",
                 "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-    "sha256": "59e378609dd9c1e4c295a2b3cb0541673973b4e8899e8ae7e1fed6b976a73ad5",
-    "bytes_per_launch": 83476489,
+    "sha256": "26333c88596049f0d96537e667ae06e7ff450dcbeb9479100fdde9946d22dbf0",
+    "bytes_per_launch": 83479530,
 }
 
 
@@ -635,7 +635,7 @@ def main():
     achieved = dom_bytes / (dom_us * 1e-6) / 1e9
     roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
             "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(),
-            "kernel": "qmv_kernel_c<Q8_0, 2, 8, 2>",
+            "kernel": "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>",
             "launches_per_step": dom_n, "us_per_launch": dom_us / dom_n,
             "bytes_per_launch": dom_bytes / dom_n}
     line = {
