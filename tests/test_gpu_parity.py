@@ -1008,3 +1008,31 @@ def test_moe_x16_equals_widened_fp32(env, fmt, kind):
         else:
             yr, S = oracle.moe(fmt, Wall, per, E, 2 * N, K, ids_np, xw_np)
         assert_tol(y16.cpu().numpy(), yr, S, (fmt, kind, name))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_fused_steps_degenerate_shapes(env, fmt):
+    """The smallest shapes of the fused steps: one output row of one block
+    (n_ff = 1 for SwiGLU, n_rows = 1 for the combine), top_k 1 and batch 1
+    and 8; the one-slot combine is the weight times qmv_moe's output."""
+    torch, qmv = env
+    E, K = 3, 32
+    for B, T in [(1, 1), (8, 1), (2, 3)]:
+        say(f"fused degenerate {fmt} B={B} T={T}")
+        ids = np.array([[(b + s) % E for s in range(T)] for b in range(B)], dtype=np.int32)
+        Wsw = wl.quant_weights(fmt, f"deg/sw/{B}/{T}", E * 2, K).reshape(-1)
+        per_sw = wl.block_bytes(fmt, 2, K)
+        x = wl.activations(f"deg/x/{B}/{T}", B, K)
+        h = gpu_swiglu(env, fmt, Wsw, per_sw, E, 1, K, ids, x)
+        hr, g, u, Sg, Su = oracle.moe_swiglu(fmt, Wsw, per_sw, E, 1, K, ids, x)
+        assert np.all(np.abs(h.astype(np.float64) - hr) <= swiglu_bound(hr, g, u, Sg, Su)), (B, T)
+        Wdn = wl.quant_weights(fmt, f"deg/dn/{B}/{T}", E, K).reshape(-1)
+        per_dn = wl.block_bytes(fmt, 1, K)
+        xs = wl.activations(f"deg/xs/{B}/{T}", B * T, K).reshape(B, T, K)
+        w = wl.router_weights(f"deg/w/{B}/{T}", B, T)
+        out = gpu_combine(env, fmt, Wdn, per_dn, E, 1, K, ids, w, xs)
+        ref, S = oracle.moe_combine(fmt, Wdn, per_dn, E, 1, K, ids, w, x_slots=xs)
+        assert np.all(np.abs(out.astype(np.float64) - ref) <= combine_bound(S, w)), (B, T)
+        if T == 1:
+            y = gpu_moe(env, fmt, Wdn, per_dn, E, 1, K, ids, xs)
+            assert np.array_equal(out.view(np.uint32), (w * y[:, :, 0]).astype(np.float32).view(np.uint32))
