@@ -1026,8 +1026,12 @@ def test_fused_steps_degenerate_shapes(env, fmt):
         h = gpu_swiglu(env, fmt, Wsw, per_sw, E, 1, K, ids, x)
         hr, g, u, Sg, Su = oracle.moe_swiglu(fmt, Wsw, per_sw, E, 1, K, ids, x)
         assert np.all(np.abs(h.astype(np.float64) - hr) <= swiglu_bound(hr, g, u, Sg, Su)), (B, T)
-        Wdn = wl.quant_weights(fmt, f"deg/dn/{B}/{T}", E, K).reshape(-1)
-        per_dn = wl.block_bytes(fmt, 1, K)
+        # one-block experts at a stride rounded up to the ABI's 4-byte multiple
+        per = wl.block_bytes(fmt, 1, K)
+        per_dn = (per + 3) // 4 * 4
+        Wdn = np.zeros((E, per_dn), dtype=np.uint8)
+        Wdn[:, :per] = wl.quant_weights(fmt, f"deg/dn/{B}/{T}", E, K).reshape(E, per)
+        Wdn = Wdn.reshape(-1)
         xs = wl.activations(f"deg/xs/{B}/{T}", B * T, K).reshape(B, T, K)
         w = wl.router_weights(f"deg/w/{B}/{T}", B, T)
         out = gpu_combine(env, fmt, Wdn, per_dn, E, 1, K, ids, w, xs)
