@@ -1119,11 +1119,11 @@ int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t
 // all slots sit in LDS beside SC staged slot vectors).
 constexpr int kCombineRows = 1024;
 
-template <class F, int LPR>
+template <class F, int LPR, int NW>
 int32_t launch_combine(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                        const float* wts, int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot,
                        float* out, int xvec, hipStream_t st) {
-    constexpr int NW = 4, PD = 3;
+    constexpr int PD = 3;
     constexpr int G = 64 / LPR;
     auto kern = moe_combine_kernel<F, LPR, NW, PD>;
     static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
@@ -1233,14 +1233,19 @@ int32_t moe_combine(const void* Wx, int64_t estride, int32_t n_experts, int64_t 
     const uint8_t* W8 = static_cast<const uint8_t*>(Wx);
     hipStream_t st = as_stream(stream);
     const int xvec = moe_xvec(x, xs_tok, xs_slot);
-    if (nb >= 64)
-        return launch_combine<F, 64>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok, xs_slot, out,
-                                     xvec, st);
-    if (nb >= 32)
-        return launch_combine<F, 32>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok, xs_slot, out,
-                                     xvec, st);
-    return launch_combine<F, 8>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok, xs_slot, out,
-                                xvec, st);
+    // at batch 1..2 the grid holds one row tile per workgroup: 8 waves give
+    // each wave one (slot, tile) unit of a token's 8 slots
+    const bool wide = batch <= 2;
+    auto go = [&](auto lpr) {
+        constexpr int L = decltype(lpr)::value;
+        return wide ? launch_combine<F, L, 8>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok,
+                                              xs_slot, out, xvec, st)
+                    : launch_combine<F, L, 4>(W8, estride, n_experts, N, (int)nb, ids, wts, batch, top_k, x, xs_tok,
+                                              xs_slot, out, xvec, st);
+    };
+    if (nb >= 64) return go(std::integral_constant<int, 64>{});
+    if (nb >= 32) return go(std::integral_constant<int, 32>{});
+    return go(std::integral_constant<int, 8>{});
 }
 
 }  // namespace

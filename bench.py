@@ -45,8 +45,8 @@ TRAFFIC_RECORD = {
     "sources": ["bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
                 "bandwidth_bound_block_amd/csrc/qmv_block_decode.h",
                 "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-    "sha256": "26333c88596049f0d96537e667ae06e7ff450dcbeb9479100fdde9946d22dbf0",
-    "bytes_per_launch": 83479530,
+    "sha256": "7d7ed9c5fc0060aa4832a24d4d802c0f582d1ecf2e6feca92a03ac8b551f65eb",
+    "bytes_per_launch": 83479342,
 }
 
 
