@@ -283,15 +283,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
             F::decode(r, d[k], m[k], cd[k]);
         }
         float sdot[RR][1];
-        if constexpr (RR == 1) {
-            float q[32];
-            codes_to_float<F>(cd[0], q);
-            float s1[1] = {0.f};
-            dot_cols<1>(q, xs + j * kXPad, nb * kXPad, s1, 1);
-            sdot[0][0] = s1[0];
-        } else {
-            dot_multi<F, RR, 1>(cd, xs + j * kXPad, nb * kXPad, sdot, 1);
-        }
+        dot_multi<F, RR, 1>(cd, xs + j * kXPad, nb * kXPad, sdot, 1);
         const float sxj = F::kNeedSx ? sx[j] : 0.f;
 #pragma unroll
         for (int k = 0; k < RR; ++k) acc[k] = Term<F>::add(acc[k], d[k], m[k], sdot[k][0], sxj);
@@ -785,13 +777,9 @@ int32_t launch_b(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, 
                  hipStream_t st) {
     auto kern = qmv_kernel<F, B, LPR, RPL, XU, NW, 2, false, XT>;
     const size_t lds = (size_t)B * nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
-    static bool attr_set = false;   // benign race: every thread sets the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsMax) != hipSuccess)
-            return fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
-        attr_set = true;
-    }
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv", &dyn_max)) return e;
+    if (lds > dyn_max) return fail(QMV_EINVAL, "qmv: %zu bytes of staged activations exceed the LDS", lds);
     constexpr int rows_per_wg = NW * (64 / LPR) * RPL;
     const int64_t tiles = (N + rows_per_wg - 1) / rows_per_wg;
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
@@ -817,13 +805,9 @@ int32_t launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
     auto kern = qmv_kernel_c<F, XU, NW, 2, XT, RR>;
     const size_t lds =
         (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float) + (size_t)NW * RR * Contig<F>::kStepBytes;
-    static bool attr_set = false;   // benign race: every thread sets the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsMax) != hipSuccess)
-            return fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
-        attr_set = true;
-    }
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv", &dyn_max)) return e;
+    if (lds > dyn_max) return fail(QMV_EINVAL, "qmv: %zu bytes of staged activations exceed the LDS", lds);
     const int64_t tiles = ((segs.end[segs.n - 1] + RR - 1) / RR + NW - 1) / NW;
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
@@ -1017,17 +1001,8 @@ int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N,
                    bool spread, hipStream_t st) {
     constexpr int NW = 4;
     auto kern = moe_kernel<F, BC, LPR, NW, XU, PD, SW, XT>;
-    static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
-    if (!dyn_max) {
-        hipFuncAttributes fa;
-        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) != hipSuccess)
-            return fail(QMV_EHIP, "qmv_moe: cannot query the kernel: %s", hipGetErrorString(hipGetLastError()));
-        const size_t m = kLdsMax - fa.sharedSizeBytes;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)m) != hipSuccess)
-            return fail(QMV_EHIP, "qmv_moe: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
-        dyn_max = m;
-    }
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv_moe", &dyn_max)) return e;
     const size_t lds = (size_t)BC * nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     if (lds > dyn_max)
         return fail(QMV_EINVAL, "qmv_moe: n_cols %d too large for one activation row in LDS", nb * 32);
@@ -1078,14 +1053,10 @@ int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int6
     constexpr int RPL = (SW || F::kNeedSx) ? 2 : 1;
     constexpr int OUT_RPL = SW ? 1 : RPL;      // output rows per lane
     auto kern = qmv_kernel<F, 1, LPR, RPL, XU, NW, 2, true, XT, SW>;
-    static bool attr_set = false;   // benign race: every thread sets the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsMax) != hipSuccess)
-            return fail(QMV_EHIP, "qmv_moe: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
-        attr_set = true;
-    }
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv_moe", &dyn_max)) return e;
     const size_t lds = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    if (lds > dyn_max) return fail(QMV_EINVAL, "qmv_moe: %zu bytes of staged activations exceed the LDS", lds);
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int64_t tiles = (N + NW * (64 / LPR) * OUT_RPL - 1) / (NW * (64 / LPR) * OUT_RPL);
     const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu / top_k));
@@ -1126,18 +1097,8 @@ int32_t launch_combine(const uint8_t* Wx, int64_t estride, int n_experts, int64_
     constexpr int PD = 3;
     constexpr int G = 64 / LPR;
     auto kern = moe_combine_kernel<F, LPR, NW, PD>;
-    static size_t dyn_max = 0;   // benign race: every thread computes and sets the same value
-    if (!dyn_max) {
-        hipFuncAttributes fa;
-        if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern)) != hipSuccess)
-            return fail(QMV_EHIP, "qmv_moe_combine: cannot query the kernel: %s", hipGetErrorString(hipGetLastError()));
-        const size_t m = kLdsMax - fa.sharedSizeBytes;
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)m) != hipSuccess)
-            return fail(QMV_EHIP, "qmv_moe_combine: cannot raise the LDS limit: %s",
-                        hipGetErrorString(hipGetLastError()));
-        dyn_max = m;
-    }
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv_moe_combine", &dyn_max)) return e;
     const size_t per_col = (size_t)nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
     const size_t sums_max = (size_t)top_k * (kCombineRows + 64) * sizeof(float);   // ranges round up to whole tiles
     if (per_col + sums_max > dyn_max)

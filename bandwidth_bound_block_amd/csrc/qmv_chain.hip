@@ -157,7 +157,6 @@ __device__ __forceinline__ void stage_x_coherent(const float* x, int nb, float* 
 template <class F, int NW, bool CONTIG>
 __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
     constexpr int LPR = 64;
-    constexpr int RPL = 1;
     extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
     float* xs = lds;
     float* sx = lds;   // set per stage: after the stage's staged x

@@ -61,6 +61,31 @@ int resident_wgs(const void* kernel, int threads, size_t lds) {
     return n;
 }
 
+int32_t lds_limit(const void* kernel, size_t lds_total, const char* what, size_t* dyn_max) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, size_t> done;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return fail(QMV_EHIP, "%s: no current device: %s", what, hipGetErrorString(hipGetLastError()));
+    const auto key = std::make_pair(kernel, dev);
+    std::lock_guard<std::mutex> g(mu);
+    auto it = done.find(key);
+    if (it != done.end()) {
+        *dyn_max = it->second;
+        return QMV_OK;
+    }
+    hipFuncAttributes fa;
+    if (hipFuncGetAttributes(&fa, kernel) != hipSuccess)
+        return fail(QMV_EHIP, "%s: cannot query the kernel: %s", what, hipGetErrorString(hipGetLastError()));
+    if (fa.sharedSizeBytes >= lds_total) return fail(QMV_EHIP, "%s: the kernel's static LDS fills the workgroup", what);
+    const size_t m = lds_total - fa.sharedSizeBytes;
+    if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)m) != hipSuccess)
+        return fail(QMV_EHIP, "%s: cannot raise the LDS limit: %s", what, hipGetErrorString(hipGetLastError()));
+    done[key] = m;
+    *dyn_max = m;
+    return QMV_OK;
+}
+
 int32_t check_launch(const char* what) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QMV_EHIP, "%s: launch failed: %s", what, hipGetErrorString(e));

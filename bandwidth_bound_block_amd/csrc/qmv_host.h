@@ -26,6 +26,12 @@ int device_cu_count();
 // compute unit at once (cached per kernel and LDS size; at least 1).
 int resident_wgs(const void* kernel, int threads, size_t lds);
 
+// Raises the dynamic LDS limit of `kernel` to what a workgroup of lds_total
+// bytes leaves beside the kernel's static LDS, once per kernel and device
+// (thread-safe).  Returns QMV_OK with that limit in *dyn_max, else QMV_EHIP
+// with the message set (prefixed by `what`).
+int32_t lds_limit(const void* kernel, size_t lds_total, const char* what, size_t* dyn_max);
+
 // Maps the status of the launch just issued to a return code.
 int32_t check_launch(const char* what);
 

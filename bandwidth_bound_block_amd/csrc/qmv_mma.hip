@@ -415,14 +415,14 @@ bool launch_mma(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, i
     const size_t lds = fixed + (size_t)(KC | 1) * per_blk;
 
     auto kern = qmv_mma_kernel<F, NW, SB, PD, XT>;
-    static bool attr_set = false;   // benign race: every thread sets the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
-                                kLdsMax) != hipSuccess) {
-            *rc = fail(QMV_EHIP, "qmv: cannot raise the LDS limit: %s", hipGetErrorString(hipGetLastError()));
-            return true;
-        }
-        attr_set = true;
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv", &dyn_max)) {
+        *rc = e;
+        return true;
+    }
+    if (lds > dyn_max) {
+        *rc = fail(QMV_EINVAL, "qmv: %zu bytes of staged activations exceed the LDS", lds);
+        return true;
     }
     const int64_t ngroups = (tiles + NW / KP - 1) / (NW / KP);
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);

@@ -45,8 +45,8 @@ TRAFFIC_RECORD = {
     "sources": ["bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
                 "bandwidth_bound_block_amd/csrc/qmv_block_decode.h",
                 "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-    "sha256": "7d7ed9c5fc0060aa4832a24d4d802c0f582d1ecf2e6feca92a03ac8b551f65eb",
-    "bytes_per_launch": 83479342,
+    "sha256": "de5109bbf562eb59653af45d1c9a7b2812e8ae2135a7142ee189a72c8a9dda02",
+    "bytes_per_launch": 83478418,
 }
 
 
