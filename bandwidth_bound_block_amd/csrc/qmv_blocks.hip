@@ -163,8 +163,10 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
 
     // PD register buffers used in turn: while one step is computed the loads
     // of the next PD-1 steps are in flight.  Loads are issued without
-    // branches (a wave past its last step re-reads its last blocks, which are
-    // in cache), so the compiler waits only for the buffer in use.
+    // branches, so the compiler waits only for the buffer in use: a wave past
+    // its last step re-reads the first step of the last tile (its data is
+    // never used).  Measured alternatives (the wave's own last step, a window
+    // of x) were no faster.
     Raw buf[PD][RPL];
     int64_t ltile = (int64_t)blockIdx.x * NW + wave;   // next step to load
     int lt = 0;
@@ -258,7 +260,11 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
         if (++t == T) { t = 0; row += wstride; }
     };
     auto load_next = [&](typename C::Chunks (&c)[RR]) {
-        const int64_t p = min(lrow, NP - 1);           // past the end: re-read a loaded step
+        // Past the end: the last row group's first step (data never used).
+        // Re-reading the wave's own last step instead was faster on 4-6k-row
+        // Q8_0 matrices but went back to HBM (non-temporal loads, +5% traffic
+        // on gate+up); a window of the staged x was slower everywhere.
+        const int64_t p = min(lrow, NP - 1);
         const int t = lrow < NP ? lt : 0;
 #pragma unroll
         for (int k = 0; k < RR; ++k) {
@@ -883,7 +889,9 @@ int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx,
     const int K4 = nb * 8;
     // Q4_x: two rows per lane (measured faster on every 8B shape it takes)
     constexpr int RPL = F::kNeedSx ? 2 : 1;
-    if (lds > 40 * 1024) {
+    // 8 waves where x is large, and for Q8_0 (o, 4096 x 4096: 6.0 -> 5.6 us);
+    // Q4_x keeps 4 (q+k+v and lm_head were slower with 8)
+    if (lds > 40 * 1024 || !F::kNeedSx) {
         if (vec && K4 <= 2 * 512) return launch_lpr<F, 1, 2, 8, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
         if (vec && K4 <= 8 * 512) return launch_lpr<F, 1, 8, 8, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
         return launch_lpr<F, 1, 0, 8, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);

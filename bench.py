@@ -45,8 +45,8 @@ TRAFFIC_RECORD = {
     "sources": ["bandwidth_bound_block_amd/csrc/qmv_blocks.hip",
                 "bandwidth_bound_block_amd/csrc/qmv_block_decode.h",
                 "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-    "sha256": "de5109bbf562eb59653af45d1c9a7b2812e8ae2135a7142ee189a72c8a9dda02",
-    "bytes_per_launch": 83478418,
+    "sha256": "9a78417f3be0e9df161458139e8d4b81b205017ab01db33a116a123f86f7431e",
+    "bytes_per_launch": 83478263,
 }
 
 
