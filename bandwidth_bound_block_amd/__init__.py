@@ -21,6 +21,7 @@ Entry points (same names as the C ABI):
   qmv_moe_swiglu_xt                the same with fp32, fp16 or bf16 activations
   qmv_moe_combine                  MoE down with the router-weighted combine
   qmv_dequant                      stored blocks -> fp32 (test/inspection aid)
+  qmv_stream_read                  stream-read ceiling of the device (measurement aid)
 """
 import ctypes
 import os
@@ -28,7 +29,7 @@ import os
 __all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
            "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_i8_requant_lut",
            "qmv_moe", "qmv_moe_xt", "qmv_moe_swiglu", "qmv_moe_swiglu_xt", "qmv_moe_combine",
-           "qmv_dequant", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
+           "qmv_dequant", "qmv_stream_read", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
            "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -90,6 +91,8 @@ def _open():
     L.qmv_moe_combine.restype = i32
     L.qmv_dequant.argtypes = [ctypes.c_int, P, i64, i64, P, P]
     L.qmv_dequant.restype = i32
+    L.qmv_stream_read.argtypes = [P, ctypes.c_size_t, P, ctypes.c_size_t, P]
+    L.qmv_stream_read.restype = i32
     L.qmv_chain.argtypes = [ctypes.c_int, P, i32, P, ctypes.c_size_t, P]
     L.qmv_chain.restype = i32
     L.qmv_last_error.argtypes = []
@@ -404,6 +407,19 @@ def qmv_dequant(fmt, W, n_rows, n_cols, out=None, stream=None):
     if out.shape != (n_rows, n_cols) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [n_rows, n_cols] tensor")
     _check(_lib.qmv_dequant(fmt, W.data_ptr(), n_rows, n_cols, out.data_ptr(), _stream(stream)))
+    return out
+
+
+def qmv_stream_read(buf, out, stream=None):
+    """Reads the uint8 GPU tensor buf once (16-byte non-temporal loads); each
+    launched thread writes the XOR of the words it read into out (uint32,
+    >= 256 words).  A measurement aid: the device's stream-read ceiling."""
+    torch = _torch()
+    _dev(buf, "buf", torch.uint8)
+    _dev(out, "out", torch.int32)
+    if not buf.is_contiguous() or not out.is_contiguous():
+        raise ValueError("buf and out must be contiguous")
+    _check(_lib.qmv_stream_read(buf.data_ptr(), buf.numel(), out.data_ptr(), out.numel(), _stream(stream)))
     return out
 
 

@@ -472,6 +472,32 @@ def time_sweep(torch, sw, steps, warmup, use_graph=True):
 
 
 # ---------------------------------------------------------------- CPU baseline
+def read_ceiling(torch, qmv, nbytes=4 << 30, reps=7):
+    """The device's stream-read ceiling: qmv_stream_read over a 4 GiB buffer
+    (16-byte non-temporal loads, the load form of the whole-line matvec
+    kernel), each launch timed with HIP events on the launch stream.  A
+    measured denominator reported beside the 8 TB/s spec."""
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    out = torch.empty(1 << 20, dtype=torch.int32, device="cuda:0")
+    st = torch.cuda.current_stream()
+    for _ in range(2):
+        qmv.qmv_stream_read(buf, out, st)
+    secs = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        qmv.qmv_stream_read(buf, out, st)
+        e1.record(st)
+        e1.synchronize()
+        secs.append(e0.elapsed_time(e1) * 1e-3)
+    del buf, out
+    torch.cuda.empty_cache()
+    med = sorted(secs)[len(secs) // 2]
+    return {"value": nbytes / med / 1e9, "best": nbytes / min(secs) / 1e9, "unit": "GB/s", "bytes": nbytes,
+            "frac_of_peak": nbytes / med / 1e9 / PEAK_GBS, "launches": reps, "statistic": "median",
+            "kernel": "stream_read_kernel (qmv_stream_read)"}
+
+
 def cpu_baseline(wl):
     """The oracle (single-threaded C, fp64 dequantize-then-dot) on one full
     token of the headline workload: the 8B layer set's 7 matrices 32 times
@@ -614,6 +640,10 @@ def main():
                     del s
                     torch.cuda.empty_cache()
 
+    ceiling = read_ceiling(torch, qmv)
+    log(f"[read_ceiling] {ceiling['value']:.0f} GB/s median, {ceiling['best']:.0f} best "
+        f"({100 * ceiling['frac_of_peak']:.1f}% of {PEAK_GBS:.0f})")
+
     cpu = None
     if not args.no_cpu_baseline:
         t0 = time.time()
@@ -637,7 +667,7 @@ def main():
             "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(),
             "kernel": "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>",
             "launches_per_step": dom_n, "us_per_launch": dom_us / dom_n,
-            "bytes_per_launch": dom_bytes / dom_n}
+            "bytes_per_launch": dom_bytes / dom_n, "frac_of_read_ceiling": achieved / ceiling["value"]}
     line = {
         "metric": METRIC,
         "value": head["gbs_wall"],
@@ -662,6 +692,7 @@ def main():
                         "tok_s_equiv": head["tok_s_kernel"], "ms_per_step": head["kernel_ms_per_step"],
                         "per_matrix": head["per_matrix"]},
         "roofline": roof,
+        "read_ceiling": ceiling,
         "cpu_baseline": cpu,
         "sweeps": extra,
     }

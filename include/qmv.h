@@ -336,6 +336,25 @@ int32_t qmv_chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, 
 int32_t qmv_dequant(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_cols,
                     float* out, void* stream);
 
+/* Stream-read ceiling (a measurement aid, not a step of the matvec):
+ * reads buf[0..bytes) once with 16-byte non-temporal loads, the load form of
+ * the whole-line matvec kernel, so that achieved matvec bandwidth can be
+ * stated against a read ceiling measured on the same device as well as
+ * against the spec ("Economical Serving and the hanzo.ai Platform",
+ * Sec. 2.1: spec versus measured achievable read bandwidth; "One Native
+ * Stack for Private, Continuously-Learning AI", "Honest Risks": which
+ * denominator a figure uses).
+ *   buf   device, 16-byte aligned; bytes a positive multiple of 16.
+ *   out   device uint32 [out_words], out_words >= 256, 4-byte aligned.
+ *         Each of the launch's threads (at most out_words) writes one word,
+ *         the XOR of every 32-bit word it read, so the XOR of the written
+ *         words equals the XOR of the whole buffer.  Words past the
+ *         launch's threads are not written.
+ * Errors: QMV_EINVAL (null pointer, bad bytes or out_words), QMV_EALIGN,
+ * QMV_EHIP (launch).  Asynchronous on `stream`; the caller owns both buffers.
+ */
+int32_t qmv_stream_read(const void* buf, size_t bytes, uint32_t* out, size_t out_words, void* stream);
+
 /* Message for the last non-OK return on the calling thread ("" if none). */
 const char* qmv_last_error(void);
 

@@ -222,3 +222,19 @@ def test_chain_argument_errors(qmv):
     assert f(0, None, 1, A, qmv.CHAIN_WORKSPACE_BYTES, None) == EINVAL
     arr = (qmv.ChainStage * 1)(good)
     assert f(0, ctypes.cast(arr, ctypes.c_void_p), 0, A, qmv.CHAIN_WORKSPACE_BYTES, None) == EINVAL
+
+
+def test_stream_read_argument_errors(qmv):
+    f = qmv.lib().qmv_stream_read
+    cases = [
+        ((0, 4096, A, 256, None), EINVAL, "null"),
+        ((A, 4096, 0, 256, None), EINVAL, "null"),
+        ((A, 0, A, 256, None), EINVAL, "multiple of 16"),
+        ((A, 4100, A, 256, None), EINVAL, "multiple of 16"),
+        ((A, 4096, A, 255, None), EINVAL, "out_words"),
+        ((A + 8, 4096, A, 256, None), EALIGN, "aligned"),
+        ((A, 4096, A + 2, 256, None), EALIGN, "aligned"),
+    ]
+    for args, code, msg in cases:
+        assert f(*args) == code, args
+        assert msg in qmv.last_error(), (args, qmv.last_error())

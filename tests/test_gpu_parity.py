@@ -1040,3 +1040,19 @@ def test_fused_steps_degenerate_shapes(env, fmt):
         if T == 1:
             y = gpu_moe(env, fmt, Wdn, per_dn, E, 1, K, ids, xs)
             assert np.array_equal(out.view(np.uint32), (w * y[:, :, 0]).astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("nbytes,out_words", [(16, 256), (1 << 20, 256), ((1 << 20) + 48, 8 * 256 * 300),
+                                              (64 << 20, 1 << 20)])
+def test_stream_read_xor(env, nbytes, out_words):
+    """The stream-read ceiling kernel reads every word exactly once: the XOR
+    of what its threads write equals the XOR of the buffer (a word skipped
+    or read twice changes it).  Unwritten output words stay zero."""
+    torch, qmv = env
+    say(f"stream_read {nbytes} bytes, {out_words} output words")
+    buf = np.random.default_rng(nbytes % 1009).integers(0, 256, size=nbytes, dtype=np.uint8)
+    out = torch.zeros(out_words, dtype=torch.int32, device="cuda:0")
+    qmv.qmv_stream_read(dev(torch, buf), out)
+    torch.cuda.synchronize()
+    got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(buf.view(np.uint32))
