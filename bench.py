@@ -552,7 +552,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the path runs on one MI355X's share; --gpus {args.gpus} "
-              "is not supported (multi-GPU sharding is described in DESIGN.md, not run).", file=sys.stderr)
+              "is not supported (the path runs on one GPU; sharding across GPUs is a design note, not run).", file=sys.stderr)
         sys.exit(2)
 
     import torch
