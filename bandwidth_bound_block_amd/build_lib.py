@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmv.so")
-SOURCES = ["qmv_host.cpp", "qmv_blocks.hip", "qmv_int8.hip", "qmv_chain.hip", "qmv_mma.hip", "qmv_stream.hip"]
+SOURCES = ["qmv_host.cpp", "qmv_blocks.hip", "qmv_fmt_q8_0.hip", "qmv_fmt_q4_0.hip", "qmv_fmt_q4_1.hip", "qmv_int8.hip", "qmv_chain.hip", "qmv_mma.hip", "qmv_stream.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.
@@ -28,10 +28,7 @@ def hipcc():
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose=False, extra=()):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra) + ["-o", tmp] + srcs
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,7 +39,30 @@ def build(verbose=False, extra=()):
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
+
+
+def build(verbose=False, extra=(), jobs=None):
+    """Compiles every source to an object (in parallel, one hipcc per
+    source), then links libqmv.so.  Objects go to a scratch folder beside
+    the sources and are removed afterwards."""
+    import concurrent.futures
+    import shutil
+    import tempfile
+    srcs = [os.path.join(CSRC, s) for s in SOURCES]
+    objdir = tempfile.mkdtemp(prefix="_build_", dir=HERE)
+    try:
+        compile_flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra)
+        objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in srcs]
+        cmds = [[hipcc()] + compile_flags + ["-c", s, "-o", o] for s, o in zip(srcs, objs)]
+        jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+            for f in [ex.submit(_run, c, verbose) for c in cmds]:
+                f.result()
+        tmp = LIB + ".tmp"
+        _run([hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc", "-o", tmp] + objs, verbose)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(objdir, ignore_errors=True)
     return LIB
 
 

@@ -2,6 +2,13 @@
 // block fetch/decode, code conversion, the block dot product and term, the
 // segment reduction and the activation staging.  Included by each kernel
 // translation unit (everything is in an anonymous namespace).
+//
+// Accuracy: every block term is formed so that its rounding error is
+// relative to sum_j |w_j x_j| of the block, whatever the codes: Q8_0 and
+// Q4_0 dot signed codes (c - 8 for Q4_0) with x and scale the block dot by
+// d; Q4_1 dequantizes each weight (d*c + m, exact in fp32 for stored
+// blocks whose value bits span <= 24) before the dot.  No term subtracts
+// two sums of |x| size, which would cancel on rows of zero weights.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <hip/hip_fp16.h>
@@ -79,7 +86,7 @@ template <> struct XIn<__bf16> {
 // wave have the next blocks in flight while it computes the current ones.
 struct Q8_0 {
     static constexpr int kBytes = 34;
-    static constexpr bool kNeedSx = false;   // the block term needs no sum of x
+    static constexpr bool kNibbles = false;  // 8-bit codes
     struct Raw {
         u32x4 a, b;
         uint32_t u;
@@ -118,7 +125,7 @@ struct Q8_0 {
 
 struct Q4_0 {
     static constexpr int kBytes = 18;
-    static constexpr bool kNeedSx = true;    // folds the -8 offset
+    static constexpr bool kNibbles = true;   // 4-bit codes
     struct Raw {
         u32x4 a;
         uint32_t u;
@@ -150,7 +157,7 @@ struct Q4_0 {
 
 struct Q4_1 {
     static constexpr int kBytes = 20;
-    static constexpr bool kNeedSx = true;    // folds the minimum m
+    static constexpr bool kNibbles = true;   // 4-bit codes
     struct Raw {
         uint32_t dm;
         u32x4 a;
@@ -255,33 +262,55 @@ __device__ __forceinline__ void block_values<Q4_1>(const float d, const float m,
     }
 }
 
-// The block's 32 codes as floats in element order: Q8_0 the signed bytes,
-// Q4_0/Q4_1 the unsigned nibbles (offset and minimum are applied per block).
-template <class F>
-__device__ __forceinline__ void codes_to_float(const uint32_t (&c)[8], float (&q)[32]);
-
-template <>
-__device__ __forceinline__ void codes_to_float<Q8_0>(const uint32_t (&c)[8], float (&q)[32]) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) q[4 * i + k] = sbyte(c[i], k);
+// The per-element factors the block dot multiplies with x, in element
+// order: Q8_0 the signed codes q; Q4_0 the offset codes times 16, 16 (c - 8);
+// Q4_1 the dequantized weights d*c + m (one rounding at most; exact for
+// every stored block whose value bits span <= 24).  Term<F> then applies
+// the rest of the scale: d, d/16 (exact) or nothing.
+//
+// Q4_0: a nibble moved to the top half of a byte with its top bit flipped
+// reads as the signed byte 16 (c - 8), so one sign-extending convert per
+// element gives the offset code, with no sum of x to fold in afterwards.
+__device__ __forceinline__ void signed_nibbles(uint32_t c, uint32_t& lo, uint32_t& hi) {
+    const uint32_t f = c ^ 0x88888888u;    // flips bit 3 of every nibble
+    lo = (f << 4) & 0xf0f0f0f0u;           // elements 4i..4i+3
+    hi = f & 0xf0f0f0f0u;                  // elements 16+4i..16+4i+3
 }
-__device__ __forceinline__ void nibbles_to_float(const uint32_t (&c)[8], float (&q)[32]) {
+
+// Factors of elements 4i..4i+3 of a block (i = 0..7).
+template <class F>
+__device__ __forceinline__ void chunk_codes(const uint32_t (&c)[8], int i, float d, float m, float (&q)[4]);
+template <>
+__device__ __forceinline__ void chunk_codes<Q8_0>(const uint32_t (&c)[8], int i, float, float, float (&q)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t lo = c[i] & 0x0f0f0f0fu, hi = (c[i] >> 4) & 0x0f0f0f0fu;
+    for (int k = 0; k < 4; ++k) q[k] = sbyte(c[i], k);
+}
+template <>
+__device__ __forceinline__ void chunk_codes<Q4_0>(const uint32_t (&c)[8], int i, float, float, float (&q)[4]) {
+    uint32_t lo, hi;
+    signed_nibbles(c[i & 3], lo, hi);
+    const uint32_t v = i < 4 ? lo : hi;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            q[4 * i + k] = ubyte(lo, k);
-            q[16 + 4 * i + k] = ubyte(hi, k);
-        }
+    for (int k = 0; k < 4; ++k) q[k] = sbyte(v, k);
+}
+template <>
+__device__ __forceinline__ void chunk_codes<Q4_1>(const uint32_t (&c)[8], int i, float d, float m, float (&q)[4]) {
+    const uint32_t v = i < 4 ? (c[i] & 0x0f0f0f0fu) : ((c[i - 4] >> 4) & 0x0f0f0f0fu);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) q[k] = __builtin_fmaf(d, ubyte(v, k), m);
+}
+
+// All 32 factors of a block (the values chunk_codes gives, in element order).
+template <class F>
+__device__ __forceinline__ void codes_to_float(const uint32_t (&c)[8], float d, float m, float (&q)[32]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float v[4];
+        chunk_codes<F>(c, i, d, m, v);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) q[4 * i + k] = v[k];
     }
 }
-template <>
-__device__ __forceinline__ void codes_to_float<Q4_0>(const uint32_t (&c)[8], float (&q)[32]) { nibbles_to_float(c, q); }
-template <>
-__device__ __forceinline__ void codes_to_float<Q4_1>(const uint32_t (&c)[8], float (&q)[32]) { nibbles_to_float(c, q); }
 
 // s[b] = sum_{e<32} q[e] * x_b[e] for the first w of B columns (w is
 // wave-uniform: inactive columns are skipped by a scalar branch).  xs points
@@ -307,33 +336,14 @@ __device__ __forceinline__ void dot_cols(const float (&q)[32], const float* __re
     }
 }
 
-// Codes of elements 4i..4i+3 of a block as floats (the same values
-// codes_to_float puts at q[4i..4i+3]).
-template <class F>
-__device__ __forceinline__ void chunk_codes(const uint32_t (&c)[8], int i, float (&q)[4]);
-template <>
-__device__ __forceinline__ void chunk_codes<Q8_0>(const uint32_t (&c)[8], int i, float (&q)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = sbyte(c[i], k);
-}
-__device__ __forceinline__ void chunk_nibbles(const uint32_t (&c)[8], int i, float (&q)[4]) {
-    const uint32_t v = i < 4 ? (c[i] & 0x0f0f0f0fu) : ((c[i - 4] >> 4) & 0x0f0f0f0fu);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = ubyte(v, k);
-}
-template <>
-__device__ __forceinline__ void chunk_codes<Q4_0>(const uint32_t (&c)[8], int i, float (&q)[4]) { chunk_nibbles(c, i, q); }
-template <>
-__device__ __forceinline__ void chunk_codes<Q4_1>(const uint32_t (&c)[8], int i, float (&q)[4]) { chunk_nibbles(c, i, q); }
-
-// s[r][b] = sum_{e<32} code_r[e] * x_b[e] for R blocks (rows) of the same
+// s[r][b] = sum_{e<32} factor_r[e] * x_b[e] for R blocks (rows) of the same
 // block column and the first w of B columns.  Chunk-outer: each 16-byte
 // read of x from LDS serves all R rows, so LDS traffic per weight falls by
 // R.  Each s[r][b] accumulates e = 0..31 in order, with the operations of
 // dot_cols: the same bits.
 template <class F, int R, int B>
-__device__ __forceinline__ void dot_multi(const uint32_t (&c)[R][8], const float* __restrict__ xs, int xstride_b,
-                                          float (&s)[R][B], int w) {
+__device__ __forceinline__ void dot_multi(const uint32_t (&c)[R][8], const float (&d)[R], const float (&m)[R],
+                                          const float* __restrict__ xs, int xstride_b, float (&s)[R][B], int w) {
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -342,7 +352,7 @@ __device__ __forceinline__ void dot_multi(const uint32_t (&c)[R][8], const float
     for (int i = 0; i < 8; ++i) {
         float q[R][4];
 #pragma unroll
-        for (int r = 0; r < R; ++r) chunk_codes<F>(c[r], i, q[r]);
+        for (int r = 0; r < R; ++r) chunk_codes<F>(c[r], i, d[r], m[r], q[r]);
 #pragma unroll
         for (int b = 0; b < B; ++b) {
             if (b < w) {
@@ -359,24 +369,21 @@ __device__ __forceinline__ void dot_multi(const uint32_t (&c)[R][8], const float
     }
 }
 
-// Adds a block's term to the running sum, from the code dot s and the block
-// sum sx of x.  Written with explicit fused multiply-adds so that every entry
-// point (dense, MoE, any batch width) rounds identically.
+// Adds a block's term to the running sum, from the block dot s of the
+// factors above with x.  Written with explicit operations so that every
+// entry point (dense, MoE, any batch width) rounds identically.
 template <class F> struct Term;
 template <> struct Term<Q8_0> {
-    __device__ static float add(float acc, float d, float, float s, float) { return __builtin_fmaf(d, s, acc); }
+    // sum_j d q_j x_j = d * s
+    __device__ static float add(float acc, float d, float, float s) { return __builtin_fmaf(d, s, acc); }
 };
 template <> struct Term<Q4_0> {
-    // sum_j d*(c_j - 8) x_j = d * (sum_j c_j x_j - 8 sum_j x_j)
-    __device__ static float add(float acc, float d, float, float s, float sx) {
-        return __builtin_fmaf(d, __builtin_fmaf(-8.f, sx, s), acc);
-    }
+    // sum_j d (c_j - 8) x_j = (d / 16) * sum_j 16 (c_j - 8) x_j; d / 16 is exact
+    __device__ static float add(float acc, float d, float, float s) { return __builtin_fmaf(d * 0.0625f, s, acc); }
 };
 template <> struct Term<Q4_1> {
-    // sum_j (d*c_j + m) x_j = d * sum_j c_j x_j + m * sum_j x_j
-    __device__ static float add(float acc, float d, float m, float s, float sx) {
-        return __builtin_fmaf(d, s, __builtin_fmaf(m, sx, acc));
-    }
+    // sum_j (d c_j + m) x_j = s
+    __device__ static float add(float acc, float, float, float s) { return acc + s; }
 };
 
 // Sum over the LPR consecutive lanes of a segment, in a fixed order; the
@@ -431,30 +438,13 @@ struct XStage {
     }
 };
 
-// Per-block sums of the staged columns (formats that fold an offset).
-template <int NT>
-__device__ __forceinline__ void block_sums(const float* xs, float* sx, int count) {
-    for (int t = threadIdx.x; t < count; t += NT) {
-        const float4* p = reinterpret_cast<const float4*>(xs + t * kXPad);
-        float acc = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 v = p[i];
-            acc += v.x; acc += v.y; acc += v.z; acc += v.w;
-        }
-        sx[t] = acc;
-    }
-}
-
 // Stages the first w of the B activation columns xcol[b][0..32*nb) into
-// LDS as xs[b][block][36] and, when the format needs them, the per-block
-// sums into sx[b][block].  Loads are issued in batches of 4 per thread
+// LDS as xs[b][block][36].  Loads are issued in batches of 4 per thread
 // before any is used, so the staging costs a few memory round trips, not
 // one per element.  vec: every column is aligned for 4-element loads.
 // Ends with a barrier.
-template <bool kNeedSx, int B, int NT, class XT = float>
-__device__ __forceinline__ void stage_x_cols(const XT* const (&xcol)[B], int nb, float* xs, float* sx, int w,
-                                             bool vec) {
+template <int B, int NT, class XT = float>
+__device__ __forceinline__ void stage_x_cols(const XT* const (&xcol)[B], int nb, float* xs, int w, bool vec) {
     const int K = nb * 32;
     const int tid = threadIdx.x;
 #pragma unroll
@@ -497,10 +487,6 @@ __device__ __forceinline__ void stage_x_cols(const XT* const (&xcol)[B], int nb,
         }
     }
     __syncthreads();
-    if (kNeedSx) {
-        block_sums<NT>(xs, sx, w * nb);
-        __syncthreads();
-    }
 }
 
 }  // namespace

@@ -103,13 +103,12 @@ __device__ __forceinline__ bool grid_barrier_thread0(unsigned* bar, unsigned nwg
     return true;
 }
 
-// Stages one activation vector x[0..32 nb) into LDS as xs[block][36] (and
-// the per-block sums into sx when the format needs them), reading it with
-// device-coherent loads: x may have been written by other workgroups
+// Stages one activation vector x[0..32 nb) into LDS as xs[block][36],
+// reading it with device-coherent loads: x may have been written by other workgroups
 // earlier in the same launch.  Same layout and batching as the dense
 // kernel's staging; loads past the end of x read 0 and are not stored.
-template <bool kNeedSx, int NT>
-__device__ __forceinline__ void stage_x_coherent(const float* x, int nb, float* xs, float* sx, bool vec) {
+template <int NT>
+__device__ __forceinline__ void stage_x_coherent(const float* x, int nb, float* xs, bool vec) {
     const int K = nb * 32;
     const int tid = threadIdx.x;
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)x, 0, K * 4, 0x00020000);
@@ -144,10 +143,6 @@ __device__ __forceinline__ void stage_x_coherent(const float* x, int nb, float* 
         }
     }
     __syncthreads();
-    if (kNeedSx) {
-        block_sums<NT>(xs, sx, nb);
-        __syncthreads();
-    }
 }
 
 // CONTIG: every stage has whole 64-block steps and 16-byte aligned W, and
@@ -159,7 +154,6 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
     constexpr int LPR = 64;
     extern __shared__ __attribute__((aligned(16))) float lds[];   // 16-byte aligned after any static LDS
     float* xs = lds;
-    float* sx = lds;   // set per stage: after the stage's staged x
     const int li = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int w0 = (int)blockIdx.x * NW + wave;        // rows < 2^30, waves < 2^16: int
@@ -206,8 +200,7 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
     };
     auto stage_x = [&](int s) {
         const ChainStage& st = args.st[s];
-        sx = lds + st.nb * kXPad;
-        stage_x_coherent<F::kNeedSx, 64 * NW>(st.x, st.nb, xs, sx, st.xvec != 0);
+        stage_x_coherent<64 * NW>(st.x, st.nb, xs, st.xvec != 0);
     };
     float acc = 0.f;
     auto compute = [&](int s, int row, int t, const Raw& r) {
@@ -226,11 +219,10 @@ __global__ __launch_bounds__(64 * NW) void chain_kernel(const ChainArgs args) {
             F::decode(r, d, m, c);
         }
         float q[32];
-        codes_to_float<F>(c, q);
+        codes_to_float<F>(c, d, m, q);
         float sdot[1] = {0.f};
         dot_cols<1>(q, xs + jc * kXPad, nb * kXPad, sdot, 1);
-        const float sxv = F::kNeedSx ? sx[jc] : 0.f;
-        const float upd = Term<F>::add(acc, d, m, sdot[0], sxv);
+        const float upd = Term<F>::add(acc, d, m, sdot[0]);
         acc = valid ? upd : acc;
         if (t == (nb + LPR - 1) / LPR - 1) {
             const float tot = segment_sum<LPR>(acc);
@@ -384,7 +376,7 @@ int32_t chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void
         if (group_matvec_contig(fmt, segs, (int)(stages[0].n_cols / 32), stages[0].x, st, true, &rc))
             return rc == QMV_OK ? ok() : rc;
     }
-    const size_t lds_x = (size_t)max_nb * (kXPad + (F::kNeedSx ? 1 : 0)) * sizeof(float);
+    const size_t lds_x = (size_t)max_nb * kXPad * sizeof(float);
     const size_t step = Contig<F>::kStepBytes;
     const int contig_nw = !contig ? 0 : lds_x + 8 * step <= (size_t)kLdsMax ? 8
                                       : lds_x + 4 * step <= (size_t)kLdsMax ? 4 : 0;

@@ -55,6 +55,27 @@ struct RowSegs {
 bool group_matvec_contig(qmv_fmt fmt, const RowSegs& segs, int nb, const float* x, hipStream_t st, bool force,
                          int32_t* rc);
 
+// The entry points of one block format (its kernels are compiled in a
+// translation unit of their own).  x_type: QMV_X_F32 / QMV_X_F16 /
+// QMV_X_BF16; path: QMV_PATH_*; swiglu: the MoE gate||up variant.
+struct FormatOps {
+    int32_t (*matvec)(const char* name, const void* W, int64_t N, int64_t K, const void* x, int32_t x_type,
+                      int64_t ldx, int32_t batch, float* y, int64_t ldy, void* stream, int32_t path);
+    int32_t (*dequant)(const void* W, int64_t N, int64_t K, float* out, void* stream);
+    int32_t (*moe)(const char* name, bool swiglu, const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K,
+                   const int32_t* ids, int32_t batch, int32_t top_k, const void* x, int32_t x_type, int64_t xs_tok,
+                   int64_t xs_slot, float* y, void* stream);
+    int32_t (*moe_combine)(const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K, const int32_t* ids,
+                           const float* wts, int32_t batch, int32_t top_k, const float* x, int64_t xs_tok,
+                           int64_t xs_slot, float* out, void* stream);
+    bool (*group_contig)(const RowSegs& segs, int nb, const float* x, hipStream_t st, bool force, int32_t* rc);
+};
+const FormatOps& ops_q8_0();
+const FormatOps& ops_q4_0();
+const FormatOps& ops_q4_1();
+// The table of fmt, or nullptr for an unknown format.
+const FormatOps* format_ops(qmv_fmt fmt);
+
 // Batch 2..8 on the matrix cores (bf16 MFMA with the activations split into
 // two bf16 pieces).  Applies when n_cols is a multiple of 256, W is 16-byte
 // aligned, x is aligned to 4 elements and ldx is a multiple of 4: then returns true and the

@@ -62,14 +62,6 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
 }
 __device__ __forceinline__ uint32_t lds4(const uint8_t* p) { return *reinterpret_cast<const uint32_t*>(p); }
 
-__device__ __forceinline__ void nibble_operand(uint32_t c, uint32_t (&b)[4]) {
-    const uint32_t lo = opaque(c & 0x0f0f0f0fu), hi = opaque((c >> 4) & 0x0f0f0f0fu);
-    b[0] = pack_bf16(ubyte(lo, 0), ubyte(lo, 1));
-    b[1] = pack_bf16(ubyte(lo, 2), ubyte(lo, 3));
-    b[2] = pack_bf16(ubyte(hi, 0), ubyte(hi, 1));
-    b[3] = pack_bf16(ubyte(hi, 2), ubyte(hi, 3));
-}
-
 // Per-format B operand: lane group g (0..3) of weight row r gets 8 codes of
 // block J of the row's step (the step's bytes at `row`, in LDS, 16-byte
 // aligned), as packed bf16, plus the block's scale (and minimum).
@@ -137,22 +129,41 @@ template <> struct Mma<Q4_0> {
     __device__ static float term(float acc, float d, float, float dot, float) { return __builtin_fmaf(d, dot, acc); }
 };
 
+// Q4_1 weights d c + m are not exact in bf16, so the operand carries codes
+// relative to a pivot code k of the block, the code nearest the zero of
+// d c + m (k = clamp(rint(-m/d), 0, 15)):
+//   sum_e (d c_e + m) x_e = d sum_e (c_e - k) x_e + mu sum_e x_e,  mu = m + d k.
+// c - k is exact in bf16, and both terms stay bounded by the block's
+// sum_e |w_e x_e|: where c_e != k, |mu| <= |d|/2 (unless k was clamped, when
+// every weight has the sign of mu and |mu| <= |w_e|) and so
+// |d (c_e - k)| <= 2 |w_e|; where c_e = k, w_e = mu.  So a block of mostly
+// zero weights (d c + m = 0) adds no large cancelling terms.  Any k in
+// 0..15 gives the same exact value; the reciprocal only picks it.
 template <> struct Mma<Q4_1> {
-    static constexpr bool kSums = true;      // the minimum multiplies the block sum of x
+    static constexpr bool kSums = true;      // mu multiplies the block sum of x
     static constexpr float kOutScale = 1.f;
     __device__ static constexpr int x0(int g) { return 4 * g; }
     __device__ static constexpr int x1(int g) { return 16 + 4 * g; }
+    // d: the block's scale; m: returns mu = m + d k
     template <int J>
     __device__ static void operand(const uint8_t* row, int g, uint32_t (&b)[4], float& d, float& m) {
         const uint8_t* blk = row + 20 * J;   // always 4-aligned
         const uint32_t dm = lds4(blk);
         d = half_bits_to_float(dm);
-        m = half_bits_to_float(dm >> 16);
-        nibble_operand(lds4(blk + 4 + 4 * g), b);
+        const float mn = half_bits_to_float(dm >> 16);
+        // fmax/fmin return the number for a NaN operand (d = m = 0): k = 0
+        const float k = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(-mn * __builtin_amdgcn_rcpf(d)), 0.f), 15.f);
+        m = __builtin_fmaf(d, k, mn);
+        const uint32_t c = lds4(blk + 4 + 4 * g);
+        const uint32_t lo = opaque(c & 0x0f0f0f0fu), hi = opaque((c >> 4) & 0x0f0f0f0fu);
+        b[0] = pack_bf16(ubyte(lo, 0) - k, ubyte(lo, 1) - k);
+        b[1] = pack_bf16(ubyte(lo, 2) - k, ubyte(lo, 3) - k);
+        b[2] = pack_bf16(ubyte(hi, 0) - k, ubyte(hi, 1) - k);
+        b[3] = pack_bf16(ubyte(hi, 2) - k, ubyte(hi, 3) - k);
     }
-    // d * sum_e c_e x_e + m * sum_e x_e
-    __device__ static float term(float acc, float d, float m, float dot, float sx) {
-        return __builtin_fmaf(m, sx, __builtin_fmaf(d, dot, acc));
+    // d * sum_e (c_e - k) x_e + mu * sum_e x_e
+    __device__ static float term(float acc, float d, float mu, float dot, float sx) {
+        return __builtin_fmaf(mu, sx, __builtin_fmaf(d, dot, acc));
     }
 };
 

@@ -8,19 +8,25 @@ weights, every matrix in its own device buffer (the working set is ~31x the
 256 MB last-level cache, so every step streams from HBM).  Weights are drawn
 N(0, 0.02^2) and encoded per 32-weight block; activations N(0, 1).  The
 matvecs run in decode dependency order, one launch per dependency level:
-q, k, v (one input) in one qmv_chain call, o, gate and up (one input) in
-one call, down, then lm_head (129 launches).  The step is captured once as
-a HIP graph and replayed.  The same matrices launched one matvec at a time
-(225 launches) are reported as the sweep llama8b_q8_0_b1.
+q||k||v (one input) in one qmv_chain call, then o, gate||up (one input) in
+one call, down, and lm_head (129 launches).  The step is captured once as a
+HIP graph and replayed.
 
-Printed: one JSON line with the step's achieved GB/s (algorithmic weight +
+Output: one JSON line per extra workload ("sweep") on stdout as it finishes,
+each with the oracle's time on the host for the same workload; the full
+per-matrix tables on stderr (and in --detail FILE); and, last, one compact
+JSON line with the headline: the step's achieved GB/s (algorithmic weight +
 activation + output bytes / wall time, whole job), the equivalent decode
-tok/s, a per-kernel roofline object measured with HIP events on the launch
-stream, the oracle's time on the host (cpu_baseline), and the other
-workloads of the path (Q4_0 / Q4_1 at batch 1, 2, 4, 8; the int8 requant
-path on Qwen3-0.6B shapes; the MoE expert path) as extra fields.
+tok/s, a roofline object for the dominant kernel measured with HIP events
+on the launch stream, the measured stream-read ceiling, the oracle's time
+on the host (cpu_baseline) and a one-number summary per sweep.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweeps all|none|a,b]
+Extra workloads: the Q8_0 1024 x 1024 matvec over 480 rotated copies (so
+every call reads HBM), Q4_0 / Q4_1 at batch 1, 2, 4, 8, the int8 requant path
+on Qwen3-0.6B shapes and the MoE expert path (plain and fused) at batch
+1, 2, 4, 8.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweeps all|none|a,b] [--detail FILE]
 """
 import argparse
 import ctypes
@@ -245,6 +251,27 @@ def build_llama_grouped(torch, qmv, wl, fmt):
     for l in dense.launches:
         if l[0] == "lm_head":
             sw.add(*l)
+    return sw
+
+
+C1_COPIES = 480      # 480 x 1,114,112 B = 535 MB, over twice the 256 MB last-level cache
+
+
+def build_c1(torch, qmv, wl):
+    """The Q8_0 1024 x 1024 batch-1 matvec, one launch per distinct copy of
+    the matrix (480 copies, so every launch reads its weights from HBM)."""
+    N = K = 1024
+    sw = Sweep("q8_0_1024_b1", 1)
+    dev = "cuda:0"
+    W0 = torch.from_numpy(wl.quant_weights("q8_0", "c1/W", N, K)).to(dev)
+    x = torch.from_numpy(wl.activations("c1/x", 1, K)).to(dev)
+    cfn = qmv.lib().qmv_q8_0
+    for _ in range(C1_COPIES):
+        W = W0.clone()
+        y = torch.empty((1, N), dtype=torch.float32, device=dev)
+        sw.keep += [W, y]
+        sw.add("q8_0_1024", cfn, (W.data_ptr(), N, K, x.data_ptr(), K, 1, y.data_ptr(), N), W.numel() + 4 * K + 4 * N)
+    sw.keep.append(x)
     return sw
 
 
@@ -498,55 +525,178 @@ def read_ceiling(torch, qmv, nbytes=4 << 30, reps=7):
             "kernel": "stream_read_kernel (qmv_stream_read)"}
 
 
-def cpu_baseline(wl):
-    """The oracle (single-threaded C, fp64 dequantize-then-dot) on one full
-    token of the headline workload: the 8B layer set's 7 matrices 32 times
-    over (the oracle's time does not depend on the values, so one layer's
-    weights stand for all 32) plus the full lm_head, Q8_0, batch 1."""
-    import oracle
-    tot_bytes, tot_s = 0, 0.0
-    for mname, N, K in wl.LLAMA8B_LAYER:
-        W = encoded(wl, "q8_0", f"llama8b/{mname}", N, K)
-        x = wl.activations(f"llama8b/x/0/{K}/1", 1, K)
-        t0 = time.perf_counter()
-        for _ in range(wl.LLAMA8B_LAYERS):
-            oracle.matvec("q8_0", W, N, K, x)
-        tot_s += time.perf_counter() - t0
-        tot_bytes += wl.LLAMA8B_LAYERS * (W.size + 4 * K + 4 * N)
-    mname, N, K = wl.LLAMA8B_LM_HEAD
-    W = encoded(wl, "q8_0", f"llama8b/{mname}", N, K)
-    x = wl.activations(f"llama8b/x/{wl.LLAMA8B_LAYERS}/{K}/1", 1, K)
-    t0 = time.perf_counter()
-    oracle.matvec("q8_0", W, N, K, x)
-    tot_s += time.perf_counter() - t0
-    tot_bytes += W.size + 4 * K + 4 * N
-    model = ""
+def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
             for ln in f:
                 if ln.startswith("model name"):
-                    model = ln.split(":", 1)[1].strip()
-                    break
+                    return ln.split(":", 1)[1].strip()
     except OSError:
         pass
-    return {"value": tot_bytes / tot_s / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"one full batch-1 Q8_0 token: 225 matvecs (the layer set's 7 matrices x32 + lm_head), "
-                      f"{tot_bytes} bytes in {tot_s:.2f} s on one thread",
-            "host_cpus": os.cpu_count(), "cpu_model": model or platform.processor(),
-            "tok_s_equiv": 1.0 / tot_s}
+    return platform.processor()
+
+
+def _timed(fn):
+    t0 = time.perf_counter()
+    fn()
+    return time.perf_counter() - t0
+
+
+def oracle_dense(wl, fmt, batch=1, layers_timed=None):
+    """The oracle (single-threaded C, fp64 dequantize-then-dot) on one full
+    batch-`batch` token of the 8B layer set in fmt: the 7 matrices of a layer
+    timed once each and counted 32 times (the oracle's time does not depend
+    on the values) plus the full lm_head.  Returns (seconds per token,
+    bytes per token)."""
+    import oracle
+    secs, nbytes = 0.0, 0
+    for mname, N, K in wl.LLAMA8B_LAYER:
+        W = encoded(wl, fmt, f"llama8b/{mname}", N, K)
+        x = wl.activations(f"llama8b/x/0/{K}/{batch}", batch, K)
+        secs += wl.LLAMA8B_LAYERS * _timed(lambda: oracle.matvec(fmt, W, N, K, x))
+        nbytes += wl.LLAMA8B_LAYERS * (W.size + 4 * batch * (K + N))
+    mname, N, K = wl.LLAMA8B_LM_HEAD
+    W = encoded(wl, fmt, f"llama8b/{mname}", N, K)
+    x = wl.activations(f"llama8b/x/{wl.LLAMA8B_LAYERS}/{K}/{batch}", batch, K)
+    secs += _timed(lambda: oracle.matvec(fmt, W, N, K, x))
+    nbytes += W.size + 4 * batch * (K + N)
+    return secs, nbytes
+
+
+def oracle_c1(wl):
+    import oracle
+    N = K = 1024
+    W = wl.quant_weights("q8_0", "c1/W", N, K)
+    x = wl.activations("c1/x", 1, K)
+    reps = 20
+    secs = _timed(lambda: [oracle.matvec("q8_0", W, N, K, x) for _ in range(reps)]) / reps
+    return secs, W.size + 8 * K
+
+
+def oracle_int8(wl):
+    """One int8 token: 28 layers (one layer's matrices timed, counted 28
+    times) plus the tied lm_head, with requant."""
+    import oracle
+    secs, nbytes = 0.0, 0
+    for mname, N, K in wl.QWEN06B_LAYER:
+        W = wl.int8_uniform(f"qwen/W/{mname}", (N, K))
+        mult, shift = wl.requant_params(f"qwen/ms/{mname}", N)
+        x = wl.int8_uniform(f"qwen/x/0/{mname}", (1, K))
+        secs += wl.QWEN06B_LAYERS * _timed(lambda: oracle.matvec_i8(W, x, mult, shift))
+        nbytes += wl.QWEN06B_LAYERS * (N * K + K + 9 * N)
+    mname, N, K = wl.QWEN06B_LM_HEAD
+    W = wl.int8_uniform(f"qwen/W/{mname}", (N, K))
+    mult, shift = wl.requant_params(f"qwen/ms/{mname}", N)
+    x = wl.int8_uniform(f"qwen/x/{wl.QWEN06B_LAYERS}/{mname}", (1, K))
+    secs += _timed(lambda: oracle.matvec_i8(W, x, mult, shift))
+    nbytes += N * K + K + 9 * N
+    return secs, nbytes
+
+
+def oracle_moe(wl, batch):
+    """One MoE step at `batch` tokens: one layer's gate||up and down calls
+    (128 Q4_0 experts, top-8) timed and counted 48 times.  The oracle loops
+    over (token, slot) pairs, so it reads an expert once per pair."""
+    import numpy as np
+    import oracle
+    E, T, H, F = wl.MOE_EXPERTS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
+    gate = wl.quant_weights("q4_0", "moe/gate", E * F, H).reshape(E, -1)
+    up = wl.quant_weights("q4_0", "moe/up", E * F, H).reshape(E, -1)
+    gu = np.concatenate([gate, up], axis=1).reshape(-1)
+    dn = wl.quant_weights("q4_0", "moe/down", E * H, F).reshape(-1)
+    ids = wl.moe_ids(f"moe/ids/0/{batch}", batch, T, E)
+    x = wl.activations(f"moe/x/gu/0/{batch}", batch, H)
+    xd = wl.activations(f"moe/x/dn/0/{batch}", batch * T, F).reshape(batch, T, F)
+    gus, dns = 2 * wl.block_bytes("q4_0", F, H), wl.block_bytes("q4_0", H, F)
+    secs = _timed(lambda: oracle.moe("q4_0", gu, gus, E, 2 * F, H, ids, x))
+    secs += _timed(lambda: oracle.moe("q4_0", dn, dns, E, H, F, ids, None, x_slots=xd))
+    nu = len(np.unique(ids))
+    return wl.MOE_LAYERS * secs, wl.MOE_LAYERS * nu * (gus + dns)
+
+
+def oracle_entry(secs, nbytes, tokens, sample):
+    return {"kind": "oracle", "cores": 1, "s_per_token": secs / tokens, "gbs": nbytes / secs / 1e9,
+            "tok_s": tokens / secs, "sample": sample}
+
+
+def cpu_baseline(wl):
+    """The oracle on one full token of the headline workload (Q8_0, batch
+    1), single-threaded, on this host."""
+    secs, nbytes = oracle_dense(wl, "q8_0")
+    return {"value": nbytes / secs / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"one full batch-1 Q8_0 token of the 8B layer set: 225 matvecs (a layer's 7 matrices "
+                      f"timed once, x32, + lm_head), {nbytes} bytes in {secs:.2f} s on one thread",
+            "host_cpus": os.cpu_count(), "cpu_model": _cpu_model(), "tok_s_equiv": 1.0 / secs}
 
 
 # ---------------------------------------------------------------- main
+def final_line(head, ceiling, cpu, summary, steps, warmup):
+    """The compact last stdout line: the headline step, the dominant
+    kernel's roofline, the read ceiling, the oracle baseline and one
+    [GB/s, tok/s] pair per extra workload (kept well under 4 KB)."""
+    # Roofline of the dominant kernel.  The q||k||v (6144 rows), gate||up
+    # (28672 rows) and lm_head (128256 rows) launches, 65 of the step's 129
+    # and ~60% of its time, run one instantiation: the contiguous-chunk
+    # kernel qmv_kernel_c<Q8_0, XU=2, 8 waves, PD=2>; down (K = 14336) runs
+    # the 16-wave one and o (4096 rows) the per-block kernel.  achieved =
+    # that kernel's algorithmic bytes over its summed per-launch event
+    # times (each launch of a label back to back on the launch stream).
+    dom = [k for k in ("qkv", "gate_up", "lm_head") if k in head["per_matrix"]]
+    pm = head["per_matrix"]
+    dom_bytes = sum(pm[k]["bytes_per_launch"] * pm[k]["launches"] for k in dom)
+    dom_us = sum(pm[k]["us_per_launch"] * pm[k]["launches"] for k in dom)
+    dom_n = sum(pm[k]["launches"] for k in dom)
+    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
+    roof = {"bound": "hbm", "achieved": _r(achieved), "peak": PEAK_GBS, "unit": "GB/s",
+            "frac": _r(achieved / PEAK_GBS, 4), "traffic": recorded_traffic(),
+            "kernel": "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>",
+            "basis": "HIP events on the launch stream around each label's 32 cache-cold launches back to back",
+            "launches_per_step": dom_n, "us_per_launch": _r(dom_us / dom_n, 3),
+            "bytes_per_launch": int(dom_bytes / dom_n), "frac_of_read_ceiling": _r(achieved / ceiling["value"], 4)}
+    line = {
+        "metric": METRIC,
+        "value": _r(head["gbs_wall"]),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": _r(head["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "llama8b_q8_0_decode_sweep_b1", "format": "q8_0", "batch": 1,
+                   "layers": 32, "matvecs_per_step": 225, "launches_per_step": head["launches_per_step"],
+                   "launch": "one per dependency level: qkv, o, gate_up, down; lm_head",
+                   "bytes_per_step": head["bytes_per_step"], "hip_graph": head["graph"]},
+        "pct_of_peak": _r(head["pct_peak_wall"], 2),
+        "tok_s_equiv": _r(head["tok_s_wall"]),
+        "gpu_time": {"gbs": _r(head["gbs_gpu"]), "ms_per_step": _r(head["gpu_ms_per_step"], 4)},
+        "kernel_time": {"gbs": _r(head["gbs_kernel"]), "ms_per_step": _r(head["kernel_ms_per_step"], 4)},
+        "roofline": roof,
+        "read_ceiling": {k: (_r(v, 4) if isinstance(v, float) else v) for k, v in ceiling.items()},
+        "cpu_baseline": None if cpu is None else {k: (_r(v, 4) if isinstance(v, float) else v) for k, v in cpu.items()},
+        "sweeps_gbs_toks": summary,
+    }
+    return line
+
+
+def _r(v, nd=1):
+    return None if v is None else round(float(v), nd)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--sweeps", default="all",
-                    help="extra workloads: all, none, or a comma list of q8_0,q4_0,q4_1,int8,moe, or of "
+                    help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,int8,moe, or of "
                          "FMT@B / FMT@Bf (one 8B sweep of format FMT at batch B, f: row-fused layout)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--detail", default=None, help="write the full per-matrix tables of every workload here (JSON)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (scale for HBM counters)")
     args = ap.parse_args()
@@ -574,31 +724,68 @@ def main():
         print(json.dumps({"calibrate_copy_bytes": n, "copies": 5}), flush=True)
         return
 
+    detail = {}
     sw = build_llama_grouped(torch, qmv, wl, "q8_0")
     log(f"[{sw.name}] {len(sw.launches)} launches, {sw.bytes_per_step} bytes/step")
     head = time_sweep(torch, sw, args.steps, args.warmup, not args.no_graph)
+    detail[sw.name] = head
     log(f"[{sw.name}] {head['ms_per_step']:.3f} ms/step wall, {head['gbs_wall']:.0f} GB/s wall, "
         f"{head['gbs_gpu']:.0f} GB/s events, {head['gbs_kernel']:.0f} GB/s per-matrix sum")
+    log(f"[{sw.name}] per matrix: " + json.dumps(head["per_matrix"]))
     del sw
     torch.cuda.empty_cache()
 
-    keys = ("ms_per_step", "gpu_ms_per_step", "gbs_wall", "gbs_gpu", "gbs_kernel", "pct_peak_wall",
-            "pct_peak_kernel", "tok_s_wall", "tok_s_kernel", "launches_per_step", "bytes_per_step", "per_matrix")
-    extra = {}
+    summary = {}          # sweep name -> [GB/s wall, tok/s wall] (the compact last line)
+    oracles = {}          # memoized oracle timings per workload kind
 
-    def record(s, r):
-        extra[s.name] = {k: r[k] for k in keys}
+    def oracle_for(key, fn):
+        if args.no_cpu_baseline:
+            return None
+        if key not in oracles:
+            t0 = time.time()
+            oracles[key] = fn()
+            log(f"[oracle] {key}: {oracles[key]['s_per_token']:.3f} s per token ({time.time() - t0:.1f} s)")
+        return oracles[key]
+
+    def record(s, r, oracle_info=None, **more):
+        detail[s.name] = r
+        line = {"sweep": s.name, "batch": s.batch, "gbs": _r(r["gbs_wall"]), "pct_of_peak": _r(r["pct_peak_wall"], 2),
+                "tok_s": _r(r["tok_s_wall"]), "ms_per_step": _r(r["ms_per_step"], 4),
+                "gbs_kernel_sum": _r(r["gbs_kernel"]), "launches_per_step": r["launches_per_step"],
+                "bytes_per_step": r["bytes_per_step"]}
+        line.update(more)
+        if oracle_info is not None:
+            line["oracle"] = {k: (_r(v, 4) if isinstance(v, float) else v) for k, v in oracle_info.items()}
+            line["speedup_vs_oracle"] = _r(r["tok_s_wall"] / s.batch / oracle_info["tok_s"], 0)
+        print(json.dumps(line), flush=True)
         log(f"[{s.name}] {r['gbs_wall']:.0f} GB/s wall, {r['gbs_kernel']:.0f} GB/s per-matrix sum, "
-            f"{r['tok_s_wall']:.0f} tok/s (wall)")
+            f"{r['tok_s_wall']:.0f} tok/s (wall); per matrix: " + json.dumps(r["per_matrix"]))
+        summary[s.name] = [_r(r["gbs_wall"], 0), _r(r["tok_s_wall"], 0)]
+
+    def dense_oracle(fmt):
+        secs, nb = oracle_dense(wl, fmt)
+        return oracle_entry(secs, nb, 1, f"one batch-1 {fmt} token of the 8B layer set (a layer's 7 matrices "
+                                          f"timed once, x32, + lm_head); per column at batch B: B times this")
 
     names = [] if args.sweeps == "none" else (
-        ["q8_0", "q4_0", "q4_1", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
+        ["c1", "q8_0", "q4_0", "q4_1", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
         if "@" in nm:
             fmt, spec = nm.split("@")
             s = build_llama(torch, qmv, wl, fmt, int(spec.rstrip("f")), fused=spec.endswith("f"))
             record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+            del s
+            torch.cuda.empty_cache()
+        elif nm == "c1":
+            s = build_c1(torch, qmv, wl)
+            r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+            pm = r["per_matrix"]["q8_0_1024"]
+            o = oracle_for("c1", lambda: oracle_entry(*oracle_c1(wl), 1, "one 1024x1024 Q8_0 matvec, mean of 20"))
+            record(s, r, o, us_per_matvec_wall=_r(r["ms_per_step"] * 1e3 / C1_COPIES, 3),
+                   us_per_matvec_events=_r(pm["us_per_launch"], 3), copies=C1_COPIES,
+                   matvecs_per_s=_r(C1_COPIES / (r["ms_per_step"] * 1e-3), 0),
+                   note="a step is one call on each of the 480 copies; tok_s counts steps")
             del s
             torch.cuda.empty_cache()
         elif nm == "q8_0":
@@ -609,13 +796,14 @@ def main():
                 torch.cuda.empty_cache()
             for fused in (False, True):
                 s = build_llama_chain(torch, qmv, wl, "q8_0", fused=fused)
-                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
-                extra[s.name]["barrier_error_flag"] = int(s.workspace.view(torch.int32)[2].item())
+                r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+                record(s, r, barrier_error_flag=int(s.workspace.view(torch.int32)[2].item()))
                 del s
                 torch.cuda.empty_cache()
         elif nm in ("q4_0", "q4_1"):
             s = build_llama_grouped(torch, qmv, wl, nm)
-            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+            o = oracle_for(nm, lambda: dense_oracle(nm))
+            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph), o)
             del s
             torch.cuda.empty_cache()
             for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False), (2, True), (4, True),
@@ -625,18 +813,21 @@ def main():
                 del s
                 torch.cuda.empty_cache()
         elif nm == "int8":
+            o = oracle_for("int8", lambda: oracle_entry(*oracle_int8(wl), 1, "one int8 token: a layer's 7 matrices "
+                                                                           "timed once, x28, + lm_head"))
             for fused in (False, True):
                 s = build_int8(torch, qmv, wl, fused=fused)
-                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph), o)
                 del s
                 torch.cuda.empty_cache()
         elif nm == "moe":
             for B in (1, 2, 4, 8):
+                o = oracle_for(f"moe{B}", lambda: oracle_entry(*oracle_moe(wl, B), B,
+                                                               f"one MoE layer at batch {B} timed once, x48"))
                 for build in (build_moe, build_moe_block):
                     s = build(torch, qmv, wl, B)
                     r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
-                    record(s, r)
-                    extra[s.name]["mean_distinct_experts"] = s.mean_unique
+                    record(s, r, o, mean_distinct_experts=_r(s.mean_unique, 2))
                     del s
                     torch.cuda.empty_cache()
 
@@ -650,52 +841,10 @@ def main():
         cpu = cpu_baseline(wl)
         log(f"[cpu_baseline] {cpu['value']:.3f} GB/s in {time.time() - t0:.1f}s")
 
-    # Roofline of the dominant kernel.  The q||k||v (6144 rows), gate||up
-    # (28672 rows) and lm_head (128256 rows) launches, 65 of the step's 129
-    # and ~60% of its time, run one instantiation: the contiguous-chunk
-    # kernel qmv_kernel_c<Q8_0, XU=2, 8 waves, PD=2>; down (K = 14336) runs
-    # the 16-wave one and o (4096 rows) the per-block kernel.  achieved =
-    # that kernel's algorithmic bytes over its summed per-launch event
-    # times (each launch of a label back to back on the launch stream).
-    dom = [k for k in ("qkv", "gate_up", "lm_head") if k in head["per_matrix"]]
-    pm = head["per_matrix"]
-    dom_bytes = sum(pm[k]["bytes_per_launch"] * pm[k]["launches"] for k in dom)
-    dom_us = sum(pm[k]["us_per_launch"] * pm[k]["launches"] for k in dom)
-    dom_n = sum(pm[k]["launches"] for k in dom)
-    achieved = dom_bytes / (dom_us * 1e-6) / 1e9
-    roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
-            "frac": achieved / PEAK_GBS, "traffic": recorded_traffic(),
-            "kernel": "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>",
-            "launches_per_step": dom_n, "us_per_launch": dom_us / dom_n,
-            "bytes_per_launch": dom_bytes / dom_n, "frac_of_read_ceiling": achieved / ceiling["value"]}
-    line = {
-        "metric": METRIC,
-        "value": head["gbs_wall"],
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": head["ms_per_step"],
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic",
-        "config": {"workload": "llama8b_q8_0_decode_sweep_b1", "format": "q8_0", "batch": 1,
-                   "layers": 32, "matvecs_per_step": 225, "launches_per_step": head["launches_per_step"],
-                   "launch": "one per dependency level: qkv, o, gate_up, down; lm_head",
-                   "bytes_per_step": head["bytes_per_step"], "hip_graph": head["graph"]},
-        "pct_of_peak": head["pct_peak_wall"],
-        "tok_s_equiv": head["tok_s_wall"],
-        "gpu_time": {"gbs": head["gbs_gpu"], "ms_per_step": head["gpu_ms_per_step"]},
-        "kernel_time": {"gbs": head["gbs_kernel"], "pct_of_peak": head["pct_peak_kernel"],
-                        "tok_s_equiv": head["tok_s_kernel"], "ms_per_step": head["kernel_ms_per_step"],
-                        "per_matrix": head["per_matrix"]},
-        "roofline": roof,
-        "read_ceiling": ceiling,
-        "cpu_baseline": cpu,
-        "sweeps": extra,
-    }
+    line = final_line(head, ceiling, cpu, summary, args.steps, args.warmup)
+    if args.detail:
+        with open(args.detail, "w") as f:
+            json.dump({"headline": line, "detail": detail}, f)
     print(json.dumps(line), flush=True)
 
 

@@ -29,7 +29,13 @@
  *     agrees with the batch-1 result within the accuracy contract.
  *   - Float results are fp32, accumulated in fp32; they agree with the exact
  *     dequantize-then-dot within |err| <= 1e-4 * sum_j |w_ij x_j| + 1e-6 per
- *     output (the accuracy contract the tests enforce).  The matrix-core
+ *     output (the accuracy contract the tests enforce), for every stored
+ *     block and every finite activation vector with 128 * 32 * max|x| below
+ *     the fp32 maximum (|x| < 8e34), rows of mostly zero weights included:
+ *     no kernel forms a block term as a difference of two sums of size
+ *     sum_j |x_j| (Q4_0 dots the signed codes c - 8; Q4_1 dequantizes each
+ *     weight, d*c + m, on the FMA kernels, and dots the codes relative to
+ *     the block's zero-crossing code on the matrix cores).  The matrix-core
  *     kernel multiplies the codes (exact in bf16) by the activations split
  *     into two bf16 pieces, hi = RN(x) and lo = RN(x - hi), which represent
  *     x to within 2^-16 |x|; the products are exact and summed in fp32.
@@ -84,13 +90,19 @@ enum {
  *   W       packed blocks of the format named by the function, n_rows rows of
  *           n_cols/32 blocks; 4-byte aligned.
  *   n_rows  >= 1.
- *   n_cols  >= 32 and a multiple of 32.
+ *   n_cols  >= 32 and a multiple of 32; at most 36384 where the FMA kernels
+ *           run (batch 1, and batch 2 for Q8_0 / Q4_1): they stage one
+ *           activation row in LDS, 144 bytes per 32 columns, within the
+ *           160 KB of a workgroup.  The matrix-core kernel (batch >= 3, and
+ *           Q4_0 at batch 2, n_cols a multiple of 256) stages it in chunks
+ *           and has no such limit.
  *   x       fp32 [batch][ldx], ldx >= n_cols; 4-byte aligned.
  *   batch   1..8.
  *   y       fp32 [batch][ldy], ldy >= n_rows; 4-byte aligned.
  * Errors: QMV_EINVAL (null pointer, n_rows < 1, n_cols < 32 or not a multiple
  * of 32, batch outside 1..8, ldx < n_cols, ldy < n_rows, n_rows*n_cols/32
- * blocks beyond 2^40), QMV_EALIGN (W, x or y not 4-byte aligned), QMV_EHIP.
+ * blocks beyond 2^40, n_cols above the LDS limit on the FMA kernels),
+ * QMV_EALIGN (W, x or y not 4-byte aligned), QMV_EHIP.
  */
 int32_t qmv_q8_0(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
@@ -196,6 +208,9 @@ int32_t qmv_i8_requant_lut(const int8_t* W, int64_t n_rows, int64_t n_cols,
  * Each expert that appears in expert_ids is streamed from memory once per
  * call and applied to every (token, slot) routed to it.
  *   fmt                 QMV_Q8_0, QMV_Q4_0 or QMV_Q4_1.
+ *   n_cols              a multiple of 32, at most 35488 (one activation row,
+ *                       144 bytes per 32 columns, plus 4 KB of routing
+ *                       tables fit the 160 KB LDS of a workgroup).
  *   expert_stride_bytes >= the bytes of one expert matrix; a multiple of 4.
  *   n_experts           >= 1.
  *   expert_ids          int32 [batch][top_k], device memory.  An id outside
@@ -271,6 +286,9 @@ int32_t qmv_moe_swiglu_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_str
  * workspace).
  *   weights  fp32 [batch][top_k], device memory, 4-byte aligned.
  *   out      fp32 [batch][n_rows], 4-byte aligned; fully overwritten.
+ *   n_cols   144 bytes per 32 columns (one staged slot vector) plus
+ *            top_k * 4352 bytes of row sums must fit the 160 KB LDS of a
+ *            workgroup (n_cols <= 28608 at top_k = 8).
  * Other arguments as qmv_moe.  A token with an invalid id gets quiet NaN
  * for all its n_rows outputs.
  * Errors: as qmv_moe; QMV_EINVAL for null weights, QMV_EALIGN for

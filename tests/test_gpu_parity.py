@@ -156,17 +156,23 @@ def test_contiguous_path_equals_per_block_path(env, fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_one_hot_columns_exact(env, fmt):
-    """x = e_j gives y_i = DEQ(W)_ij exactly (all other products are 0)."""
+    """FMA kernels: x = e_j gives y_i = DEQ(W)_ij exactly (all other products
+    are 0; Q4_1 weights are dequantized with one rounding, d*c + m, before
+    the dot), at batch 8 and batch 1, on random bytes and scales."""
+    torch, qmv = env
     N, K, B = 50, 1024, 8
     W = random_blocks(3, fmt, N, K)
     cols = [0, 1, 31, 32, 33, 511, 1000, 1023]
     x = np.zeros((B, K), dtype=np.float32)
     for b, j in enumerate(cols):
         x[b, j] = 1.0
-    y = gpu_matvec(env, fmt, W, N, K, x)
+    Wd, xd = dev(torch, W), dev(torch, x)
+    y = qmv.qmv_matvec_path(fmt, Wd, N, K, xd, qmv.PATH_FMA).cpu().numpy()
+    y1 = gpu_matvec(env, fmt, W, N, K, x[:1])
     deq = oracle.dequant(fmt, W, N, K).astype(np.float32)
     for b, j in enumerate(cols):
         assert np.array_equal(y[b], deq[:, j]), (fmt, j)
+    assert np.array_equal(y1[0], deq[:, cols[0]])
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -261,9 +267,20 @@ def test_mfma_path_one_hot_exact(env, fmt):
     for b, j in enumerate(cols):
         x[b, j] = 1.0
     y = mfma_matvec(env, fmt, dev(torch, W), N, K, dev(torch, x)).cpu().numpy()
-    deq = oracle.dequant(fmt, W, N, K).astype(np.float32)
+    deq64 = oracle.dequant(fmt, W, N, K)
+    deq = deq64.astype(np.float32)
+    exact = deq.astype(np.float64) == deq64
     for b, j in enumerate(cols):
-        assert np.array_equal(y[b], deq[:, j]), (fmt, j)
+        if fmt != "q4_1":
+            assert np.array_equal(y[b], deq[:, j]), (fmt, j)
+        else:
+            # d (c - k) + mu with mu = m + d k rounded once: exact wherever
+            # d c + m is exact in fp32 (every stored block whose value bits
+            # span <= 24), else within one ulp of it (random scales here)
+            e = exact[:, j]
+            assert np.array_equal(y[b][e], deq[e, j]), (fmt, j)
+            ulp = np.spacing(np.abs(deq[~e, j]))
+            assert np.all(np.abs(y[b][~e].astype(np.float64) - deq64[~e, j]) <= ulp), (fmt, j)
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -674,6 +691,11 @@ def test_chain_dependent_stages(env, fmt):
         assert int(ws.view(torch.int32)[2].item()) == 0
         for i in range(n_stages):
             assert torch.equal(ys[i].view(torch.int32), ref[i].view(torch.int32)), (rep, i)
+    # the oracle on each of the last stages' own inputs (as the chain computed them)
+    for i in range(n_stages - 4, n_stages):
+        xin = (x0 if i == 0 else ys[i - 1]).cpu().numpy()[None]
+        yr, S = oracle.matvec(fmt, Ws[i].cpu().numpy(), N, K, xin)
+        assert_tol(ys[i].cpu().numpy()[None], yr, S, (fmt, i))
     last = ref[-1].cpu().numpy()
     assert np.isfinite(last).all() and np.abs(last).max() > 1e-3   # the chain did not decay or blow up
 
@@ -711,6 +733,11 @@ def test_chain_decode_pattern(env, fmt):
         ref = f(W, N, K, x)[0]        # x as the chain computed it: checks each stage on its own input
         torch.cuda.synchronize()
         assert torch.equal(y.view(torch.int32), ref.view(torch.int32)), i
+    # the oracle on the last layer's six stages, each on its own input
+    for i in range(len(stages) - 6, len(stages)):
+        W, N, K, x, y, _ = stages[i]
+        yr, S = oracle.matvec(fmt, W.cpu().numpy(), N, K, x.cpu().numpy()[None])
+        assert_tol(y.cpu().numpy()[None], yr, S, (fmt, i))
     last = outs[-1]["down"].cpu().numpy()
     assert np.isfinite(last).all() and np.abs(last).max() > 1e-3
 
@@ -718,14 +745,19 @@ def test_chain_decode_pattern(env, fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_chain_shared_input_groups(env, fmt):
     """Stages that read one x and do not wait: up to 4 run as one matvec over
-    their concatenated rows, more (or with a misaligned W) through the
-    persistent chain kernel.  Every output equals the batch-1 entry point
-    on its own matrix bitwise (>= 64 blocks per row)."""
+    their concatenated rows (the launch the batch-1 decode step times for
+    q||k||v and gate||up), more (or with a misaligned W) through the
+    persistent chain kernel.  Every output is checked against the oracle
+    within the bound (all rows, or 1024 sampled rows plus both ends of each
+    matrix of the 8B gate||up group) and equals the batch-1 entry point on
+    its own matrix bitwise (>= 64 blocks per row)."""
     torch, qmv = env
     f = _chain_fn(qmv, fmt)
     ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
     groups = {
-        "qkv": [(4096, 4096), (1024, 4096), (1024, 4096)],
+        # the 8B decode groups: q||k||v and gate||up at 4096 columns
+        "qkv_8b": [(4096, 4096), (1024, 4096), (1024, 4096)],
+        "gate_up_8b": [(14336, 4096), (14336, 4096)],
         "gate_up": [(3000, 2048), (3000, 2048)],
         "five": [(300, 2048), (77, 2048), (1, 2048), (513, 2048), (64, 2048)],
         "misaligned": [(700, 2048), (129, 2048)],
@@ -734,22 +766,34 @@ def test_chain_shared_input_groups(env, fmt):
         "big_odd": [(5001, 2048), (4000, 2048)],
     }
     for gname, shapes in groups.items():
+        say(f"chain group {fmt} {gname}")
         K = shapes[0][1]
-        x = dev(torch, wl.activations(f"t/chain/grp/{gname}/x", 1, K))[0]
+        xh = wl.activations(f"t/chain/grp/{gname}/x", 1, K)
+        x = dev(torch, xh)[0]
         stages, mats = [], []
         for i, (N, _) in enumerate(shapes):
-            W = dev(torch, wl.quant_weights(fmt, f"t/chain/grp/{gname}/{i}", N, K)).reshape(-1)
+            Wh = wl.quant_weights(fmt, f"t/chain/grp/{gname}/{i}", N, K)
+            W = dev(torch, Wh).reshape(-1)
             if gname == "misaligned" and i == 1:
                 buf = torch.zeros(W.numel() + 16, dtype=torch.uint8, device="cuda:0")
                 buf[4:4 + W.numel()].copy_(W)
                 W = buf[4:4 + W.numel()]
             y = torch.full((N,), float("nan"), device="cuda:0")
             stages.append((W, N, K, x, y, 0))
-            mats.append((W, N))
+            mats.append((W, N, Wh))
         qmv.qmv_chain(fmt, stages, ws)
         torch.cuda.synchronize()
         assert int(ws.view(torch.int32)[2].item()) == 0
-        for (W, N), st in zip(mats, stages):
+        for (W, N, Wh), st in zip(mats, stages):
+            got = st[4].cpu().numpy()
+            if N > 4096:
+                rows = np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N),
+                                                 np.random.default_rng(N).choice(N, size=1024, replace=False)]))
+                yr, S = oracle.matvec(fmt, Wh, N, K, xh, rows=rows)
+                assert_tol(got[rows][None], yr, S, (gname, N))
+            else:
+                yr, S = oracle.matvec(fmt, Wh, N, K, xh)
+                assert_tol(got[None], yr, S, (gname, N))
             ref = f(W, N, K, x)[0]
             torch.cuda.synchronize()
             assert torch.equal(st[4].view(torch.int32), ref.view(torch.int32)), (gname, N)

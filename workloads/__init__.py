@@ -20,7 +20,13 @@ and encodes them into the stored block formats, as the input recipe says:
 * MoE expert ids: per token, top_k distinct ids uniform without replacement;
   router weights per token drawn from a flat Dirichlet (positive, summing
   to 1 over the token's top_k slots);
-* an int8 lookup table: 256 entries uniform in [-128, 127].
+* an int8 lookup table: 256 entries uniform in [-128, 127];
+* "zero-heavy" rows (an edge case of the stored formats, not a workload):
+  blocks whose weights are exactly zero except on a sparse set of columns,
+  with activations of magnitude ~1e3 on the zero weights and ~1e-3 on the
+  others, so that sum_j |w_j x_j| is tiny next to sum_j |x_j|.  Q8_0 codes
+  0, Q4_0 codes 8, Q4_1 codes k with d*k + m = 0 exactly (d with few
+  significant bits and m = -d*k, both exact in fp16).
 
 Byte layouts (ggml-compatible, little-endian): Q8_0 = [d:fp16][q:int8 x32];
 Q4_0 = [d:fp16][qs:16 bytes], element j<16 in the low nibble of qs[j] and
@@ -193,3 +199,45 @@ MOE_HIDDEN, MOE_FFN, MOE_EXPERTS, MOE_TOPK, MOE_LAYERS = 2048, 768, 128, 8, 48
 
 def block_bytes(fmt, N, K):
     return N * (K // 32) * BLOCK_BYTES[fmt]
+
+
+def zero_heavy(fmt, tag, N, K, B=1, every=16):
+    """Stored bytes [N][K/32 * block bytes] and activations [B][K] float32
+    of the zero-heavy kind (module docstring): column j carries nonzero
+    codes only when j % every == every - 1 (the "small" columns)."""
+    g = rng(tag)
+    nb = K // 32
+    small = (np.arange(K) % every) == every - 1
+    x = g.standard_normal((B, K)).astype(np.float32)
+    x *= np.where(small, np.float32(1e-3), np.float32(1e3))
+    e = g.integers(-10, 3, size=(N, nb))
+    frac = g.integers(0, 8, size=(N, nb))
+    mag = np.ldexp(1.0 + frac / 8.0, e)                     # <= 4 significant bits
+    if fmt == "q8_0":
+        codes = np.zeros((N, K), dtype=np.int64)
+        codes[:, small] = g.integers(-127, 128, size=(N, int(small.sum())))
+        d = (mag * np.where(g.integers(0, 2, size=(N, nb)) == 1, -1.0, 1.0)).astype(np.float16)
+        out = np.zeros((N, nb, 34), dtype=np.uint8)
+        out[:, :, 0:2] = d.view(np.uint8).reshape(N, nb, 2)
+        out[:, :, 2:] = codes.astype(np.int8).view(np.uint8).reshape(N, nb, 32)
+        return out.reshape(N, nb * 34), x
+    if fmt == "q4_0":
+        codes = np.full((N, K), 8, dtype=np.int64)
+        codes[:, small] = g.integers(0, 16, size=(N, int(small.sum())))
+        d = (mag * np.where(g.integers(0, 2, size=(N, nb)) == 1, -1.0, 1.0)).astype(np.float16)
+        hdr = d.view(np.uint8).reshape(N, nb, 2)
+        bb = 18
+    else:
+        k = g.integers(0, 16, size=(N, nb))
+        codes = np.repeat(k, 32, axis=1)
+        codes[:, small] = g.integers(0, 16, size=(N, int(small.sum())))
+        d = mag.astype(np.float16)
+        m = (-(mag * k)).astype(np.float16)                # exact: <= 8 significant bits
+        assert np.all(m.astype(np.float64) == -(mag * k))
+        hdr = np.concatenate([d.view(np.uint8).reshape(N, nb, 2), m.view(np.uint8).reshape(N, nb, 2)], axis=2)
+        bb = 20
+    c = codes.reshape(N, nb, 32).astype(np.uint8)
+    qs = (c[:, :, :16] | (c[:, :, 16:] << 4)).astype(np.uint8)
+    out = np.concatenate([hdr, qs], axis=2)
+    assert out.shape[2] == bb
+    return out.reshape(N, nb * bb), x
