@@ -22,6 +22,8 @@ Entry points (same names as the C ABI):
   qmv_moe_combine                  MoE down with the router-weighted combine
   qmv_dequant                      stored blocks -> fp32 (test/inspection aid)
   qmv_stream_read                  stream-read ceiling of the device (measurement aid)
+  qmv_chain                        batch-1 matvec stages in one persistent launch
+  qmv_chain_noalloc                the same with library-held barrier words (no workspace)
 """
 import ctypes
 import os
@@ -29,7 +31,7 @@ import os
 __all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
            "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_i8_requant_lut",
            "qmv_moe", "qmv_moe_xt", "qmv_moe_swiglu", "qmv_moe_swiglu_xt", "qmv_moe_combine",
-           "qmv_dequant", "qmv_stream_read", "qmv_chain", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
+           "qmv_dequant", "qmv_stream_read", "qmv_chain", "qmv_chain_noalloc", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
            "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -95,6 +97,8 @@ def _open():
     L.qmv_stream_read.restype = i32
     L.qmv_chain.argtypes = [ctypes.c_int, P, i32, P, ctypes.c_size_t, P]
     L.qmv_chain.restype = i32
+    L.qmv_chain_noalloc.argtypes = [ctypes.c_int, P, i32, P]
+    L.qmv_chain_noalloc.restype = i32
     L.qmv_last_error.argtypes = []
     L.qmv_last_error.restype = ctypes.c_char_p
     L.qmv_abi_version.argtypes = []
@@ -454,3 +458,10 @@ def qmv_chain(fmt, stages, workspace, stream=None):
     arr = stages if isinstance(stages, ctypes.Array) else chain_stages(stages, fmt)
     _check(_lib.qmv_chain(_fmt(fmt), ctypes.cast(arr, ctypes.c_void_p), len(arr), workspace.data_ptr(),
                           workspace.numel(), _stream(stream)))
+
+
+def qmv_chain_noalloc(fmt, stages, stream=None):
+    """qmv_chain with the barrier words held by the library (no workspace
+    argument, nothing allocated; see qmv.h).  stages as for qmv_chain."""
+    arr = stages if isinstance(stages, ctypes.Array) else chain_stages(stages, fmt)
+    _check(_lib.qmv_chain_noalloc(_fmt(fmt), ctypes.cast(arr, ctypes.c_void_p), len(arr), _stream(stream)))

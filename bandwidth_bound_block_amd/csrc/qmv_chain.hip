@@ -17,9 +17,18 @@
 // segment, fixed reduction order), so each stage's output equals a
 // qmv_q8_0 / qmv_q4_0 / qmv_q4_1 call on a matrix of >= 64 blocks per row
 // bitwise.
+#include <mutex>
 #include <type_traits>
 
 #include "qmv_block_decode.h"
+
+// The barrier words of qmv_chain_noalloc, held by the library: a file-scope
+// device array, so every GPU the library runs on holds one copy (at its own
+// address) until the process ends.  Host code never passes this name to a
+// kernel or a copy (in host code it is only a stand-in for the symbol): it
+// looks the device address up with hipGetSymbolAddress once per device and
+// uses that pointer.
+static __device__ __align__(256) unsigned scratch[QMV_CHAIN_WORKSPACE_BYTES / 4];
 
 namespace qmv {
 namespace {
@@ -332,10 +341,19 @@ int32_t launch_chain(ChainArgs& a, size_t lds_x, hipStream_t st) {
     return check_launch("qmv_chain");
 }
 
+// Zeroes n words (the chain's barrier words before a call that does not
+// rely on an earlier one); a kernel, not a memset, so that it records as a
+// kernel node under graph capture.
+__global__ __launch_bounds__(256) void zero_words_kernel(unsigned* p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// clear: zero the workspace on the stream before the first launch that
+// uses its barrier words (qmv_chain_noalloc's library-held copy).
 template <class F>
 int32_t chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void* workspace, size_t ws_bytes,
-              void* stream) {
-    const char* name = "qmv_chain";
+              void* stream, bool clear = false, const char* name = "qmv_chain") {
     if (!stages || !workspace) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (n_stages < 1) return fail(QMV_EINVAL, "%s: n_stages must be >= 1", name);
     if (ws_bytes < QMV_CHAIN_WORKSPACE_BYTES)
@@ -376,6 +394,12 @@ int32_t chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void
         if (group_matvec_contig(fmt, segs, (int)(stages[0].n_cols / 32), stages[0].x, st, true, &rc))
             return rc == QMV_OK ? ok() : rc;
     }
+    if (clear) {
+        constexpr int words = QMV_CHAIN_WORKSPACE_BYTES / 4;
+        hipLaunchKernelGGL(zero_words_kernel, dim3((words + 255) / 256), dim3(256), 0, st,
+                           static_cast<unsigned*>(workspace), words);
+        if (const int32_t rc = check_launch(name)) return rc;
+    }
     const size_t lds_x = (size_t)max_nb * kXPad * sizeof(float);
     const size_t step = Contig<F>::kStepBytes;
     const int contig_nw = !contig ? 0 : lds_x + 8 * step <= (size_t)kLdsMax ? 8
@@ -404,6 +428,28 @@ int32_t chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void
     return ok();
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (thread-safe).  QMV_EHIP with a message when the lookup fails.
+int32_t scratch_address(void** out) {
+    constexpr int kMaxDev = 64;
+    static std::mutex mu;
+    static void* addr[kMaxDev] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev)
+        return fail(QMV_EHIP, "qmv_chain_noalloc: no usable current device");
+    std::lock_guard<std::mutex> g(mu);
+    if (!addr[dev]) {
+        void* p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(QMV_EHIP, "qmv_chain_noalloc: cannot find the library's barrier words: %s",
+                        hipGetErrorString(e));
+        addr[dev] = p;
+    }
+    *out = addr[dev];
+    return QMV_OK;
+}
+
 }  // namespace
 }  // namespace qmv
 
@@ -414,5 +460,20 @@ extern "C" int32_t qmv_chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t
     case QMV_Q4_0: return qmv::chain<qmv::Q4_0>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
     case QMV_Q4_1: return qmv::chain<qmv::Q4_1>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
     default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_chain: unknown format %d", (int)fmt);
+    }
+}
+
+extern "C" int32_t qmv_chain_noalloc(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void* stream) {
+    const char* name = "qmv_chain_noalloc";
+    void* ws = nullptr;
+    if (fmt != QMV_Q8_0 && fmt != QMV_Q4_0 && fmt != QMV_Q4_1)
+        return qmv::fail(QMV_EUNSUPPORTED, "%s: unknown format %d", name, (int)fmt);
+    if (!stages) return qmv::fail(QMV_EINVAL, "%s: null pointer", name);
+    if (n_stages < 1) return qmv::fail(QMV_EINVAL, "%s: n_stages must be >= 1", name);
+    if (const int32_t rc = qmv::scratch_address(&ws)) return rc;
+    switch (fmt) {
+    case QMV_Q8_0: return qmv::chain<qmv::Q8_0>(fmt, stages, n_stages, ws, QMV_CHAIN_WORKSPACE_BYTES, stream, true, name);
+    case QMV_Q4_0: return qmv::chain<qmv::Q4_0>(fmt, stages, n_stages, ws, QMV_CHAIN_WORKSPACE_BYTES, stream, true, name);
+    default: return qmv::chain<qmv::Q4_1>(fmt, stages, n_stages, ws, QMV_CHAIN_WORKSPACE_BYTES, stream, true, name);
     }
 }

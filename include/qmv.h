@@ -343,6 +343,28 @@ int32_t qmv_chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, 
                   size_t workspace_bytes, void* stream);
 
 /*
+ * qmv_chain for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * same stages, kernels and outputs as qmv_chain (bitwise), with the chain's
+ * barrier words in a library-held device array instead of a caller
+ * workspace; the call allocates nothing.
+ *   - The array is QMV_CHAIN_WORKSPACE_BYTES (40 KB), a static device
+ *     variable of libqmv.so: every GPU the library runs on holds one copy
+ *     until the process ends.  Its address is looked up once per device.
+ *   - The chain needs the same fixed 40 KB of barrier words for every stage
+ *     list, so no list qmv_chain accepts exceeds the array.
+ *   - Every call that launches the persistent chain kernel first clears the
+ *     array on `stream` with a small kernel (no memset), so a call never
+ *     depends on an earlier one, an interrupted one included.
+ *   - All calls on one GPU share the array: calls that overlap in time on
+ *     one GPU (other streams or threads) race and give undefined outputs;
+ *     the caller serializes them.
+ * Arguments, outputs and errors as qmv_chain without the workspace, plus
+ * QMV_EHIP if the array's address cannot be found.
+ */
+int32_t qmv_chain_noalloc(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void* stream);
+
+/*
  * Dequantize a whole matrix to fp32: out[i][j] = DEQ(W)[i][j], exactly (every
  * Q8_0/Q4_0 value and every Q4_1 value d*c + m whose bits span <= 24 is
  * representable in fp32; otherwise it is rounded to nearest even).  A test

@@ -224,6 +224,16 @@ def test_chain_argument_errors(qmv):
     assert f(0, ctypes.cast(arr, ctypes.c_void_p), 0, A, qmv.CHAIN_WORKSPACE_BYTES, None) == EINVAL
 
 
+def test_chain_noalloc_argument_errors(qmv):
+    """Checked before the library looks up its barrier words (no GPU here)."""
+    import ctypes
+    f = qmv.lib().qmv_chain_noalloc
+    arr = (qmv.ChainStage * 1)(qmv.ChainStage(A, A, A, 16, 4096, 0, 0))
+    assert f(9, ctypes.cast(arr, ctypes.c_void_p), 1, None) == EUNSUPPORTED
+    assert f(0, None, 1, None) == EINVAL and "null" in qmv.last_error()
+    assert f(0, ctypes.cast(arr, ctypes.c_void_p), 0, None) == EINVAL and "n_stages" in qmv.last_error()
+
+
 def test_stream_read_argument_errors(qmv):
     f = qmv.lib().qmv_stream_read
     cases = [
