@@ -400,6 +400,12 @@ int32_t chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void
                            static_cast<unsigned*>(workspace), words);
         if (const int32_t rc = check_launch(name)) return rc;
     }
+    {
+        // whole 2048-column windows: one weight stream across the levels
+        int32_t rc;
+        if (decode_chain(fmt, stages, n_stages, static_cast<unsigned*>(workspace), st, &rc))
+            return rc == QMV_OK ? ok() : rc;
+    }
     const size_t lds_x = (size_t)max_nb * kXPad * sizeof(float);
     const size_t step = Contig<F>::kStepBytes;
     const int contig_nw = !contig ? 0 : lds_x + 8 * step <= (size_t)kLdsMax ? 8

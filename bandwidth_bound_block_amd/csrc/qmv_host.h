@@ -76,6 +76,15 @@ const FormatOps& ops_q4_1();
 // The table of fmt, or nullptr for an unknown format.
 const FormatOps* format_ops(qmv_fmt fmt);
 
+// The batch-1 chain of qmv_chain as one weight stream across dependency
+// levels (qmv_decode.hip).  Applies when every stage has n_cols a multiple
+// of 2048 and 16-byte aligned W and x, and the staged x, partial sums and
+// load ring fit the LDS: then returns true and the launch status in *rc;
+// else false and launches nothing.  ws: the 40 KB workspace (flag words
+// 9216.. and the error word 2).
+bool decode_chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, unsigned* ws, hipStream_t st,
+                  int32_t* rc);
+
 // Batch 2..8 on the matrix cores (bf16 MFMA with the activations split into
 // two bf16 pieces).  Applies when n_cols is a multiple of 256, W is 16-byte
 // aligned, x is aligned to 4 elements and ldx is a multiple of 4: then returns true and the

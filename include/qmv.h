@@ -301,22 +301,30 @@ int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_strid
                         float* out, void* stream);
 
 /*
- * A chain of batch-1 float matvecs in one persistent launch.  Decode is a
- * sequence of matvecs, each streaming its weights once ("Economical Serving
- * and the hanzo.ai Platform", Sec. 2.1); at batch 1 most of them take a few
+ * A chain of batch-1 float matvecs in one call.  Decode is a sequence of
+ * matvecs, each streaming its weights once ("Economical Serving and the
+ * hanzo.ai Platform", Sec. 2.1); at batch 1 most of them take a few
  * microseconds, about as long as a kernel launch.  Stage s computes
  *   stages[s].y[i] = sum_j DEQ(stages[s].W)[i][j] * stages[s].x[j]
- * for i < n_rows, in format fmt, exactly as the batch-1 entry point of that
- * format (bitwise the same result when n_cols >= 2048; within the accuracy
- * bound otherwise).  A stage with wait != 0 may read outputs of earlier
- * stages of the same call: it starts reading x only after every earlier
- * stage is complete and its outputs are visible.  A stage with wait == 0
- * may read only outputs that were already visible to the last earlier
- * stage with wait != 0 (e.g. it shares that stage's input), not outputs
- * of stages after it.  Weight loads of a stage may begin before earlier
- * stages finish.  A call of at most 4 stages that all read one x with the
- * same n_cols and do not wait (e.g. the q, k and v projections of a decode
- * step) runs as a single matvec over their concatenated rows.
+ * for i < n_rows, in format fmt, within the accuracy contract above and
+ * deterministically (bitwise the same outputs for the same inputs).  A
+ * stage with wait != 0 may read outputs of earlier stages of the same call:
+ * it starts reading x only after every earlier stage is complete and its
+ * outputs are visible.  A stage with wait == 0 may read only outputs that
+ * were already visible to the last earlier stage with wait != 0 (e.g. it
+ * shares that stage's input), not outputs of stages after it.  Weight loads
+ * of a stage may begin before earlier stages finish.  How it runs:
+ *   - at most 4 stages that all read one x with the same n_cols and do not
+ *     wait (e.g. the q, k and v projections of a decode step): one matvec
+ *     over their concatenated rows, each output bitwise the batch-1 entry
+ *     point's for n_cols >= 2048 and a multiple of 2048;
+ *   - otherwise, every stage with n_cols a multiple of 2048 and 16-byte
+ *     aligned W and x: one persistent launch (per 36 dependency levels)
+ *     that streams the weights through LDS and sums each row's 2048-column
+ *     window partials in window order (within the bound; not bitwise the
+ *     entry points, which accumulate across windows before reducing);
+ *   - otherwise one persistent launch of per-stage cursors, each output
+ *     bitwise the batch-1 entry point's when n_cols >= 2048.
  *   stages        host array of n_stages entries (copied into the launch).
  *   n_rows        1..2^30;  n_cols a multiple of 32 in 32..35424.
  *   W, x, y       device pointers, 4-byte aligned, as for qmv_q8_0.

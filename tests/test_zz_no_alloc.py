@@ -3,8 +3,9 @@ against qmv_chain with a caller workspace, called through the C ABI: the
 same outputs bitwise (the same kernels) and within the accuracy bound of the
 oracle, on two calls in a row, the second with a smaller stage list.  The
 stages are decode-shaped and dependent (stage barriers inside the
-persistent chain kernel use the barrier words), and the first list holds
-more stages than one launch, so it also crosses a launch boundary."""
+persistent kernels use the barrier words), and the first list holds more
+stages than one launch, so it also crosses a launch boundary; both
+persistent kernels of qmv_chain are reached."""
 import ctypes
 
 import numpy as np
@@ -16,10 +17,10 @@ import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def _decode_stages(torch, qmv, fmt, layers, tag):
+def _decode_stages(torch, qmv, fmt, layers, tag, F):
     """q reads the layer input, k too (no wait), o reads q, gate and up read
     o (up does not wait), down reads up and is the next layer's input."""
-    H, F = 2048, 5632
+    H = 2048
     mats = {"q": (H, H), "k": (512, H), "o": (H, H), "gate": (F, H), "up": (F, H), "down": (H, F)}
     Wd = {m: torch.from_numpy(wl.quant_weights(fmt, f"t/noalloc/{tag}/{m}", N, K)).to("cuda:0")
           for m, (N, K) in mats.items()}
@@ -35,16 +36,19 @@ def _decode_stages(torch, qmv, fmt, layers, tag):
     return stages, outs
 
 
+# F = 5632: the per-stage chain kernel (two-level atomic barrier words);
+# F = 6144: whole 2048-column windows, the streaming kernel (flag words)
+@pytest.mark.parametrize("F", [5632, 6144])
 @pytest.mark.parametrize("fmt", ["q8_0", "q4_0"])
-def test_chain_noalloc_equals_chain(fmt):
+def test_chain_noalloc_equals_chain(fmt, F):
     import torch
     import bandwidth_bound_block_amd as qmv
     lib = qmv.lib()
     ws = torch.zeros(qmv.CHAIN_WORKSPACE_BYTES, dtype=torch.uint8, device="cuda:0")
     stream = torch.cuda.current_stream().cuda_stream
     for call, layers in enumerate((12, 2)):          # 72 stages (two launches), then 12
-        print(f"noalloc {fmt} call {call}: {layers} layers", flush=True)
-        stages, outs = _decode_stages(torch, qmv, fmt, layers, f"{fmt}/{call}")
+        print(f"noalloc {fmt} F={F} call {call}: {layers} layers", flush=True)
+        stages, outs = _decode_stages(torch, qmv, fmt, layers, f"{fmt}/{F}/{call}", F)
         arr = qmv.chain_stages(stages, fmt)
         rc = lib.qmv_chain(qmv.FORMATS[fmt], ctypes.cast(arr, ctypes.c_void_p), len(arr), ws.data_ptr(), ws.numel(),
                            ctypes.c_void_p(stream))
