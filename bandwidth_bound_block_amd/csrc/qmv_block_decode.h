@@ -29,6 +29,14 @@ constexpr int kLdsMax = 160 * 1024;     // LDS per workgroup on gfx950
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
 
+constexpr int kPolicyNT = 2;               // buffer-load cache policy: non-temporal
+constexpr int kRawBufferFlags = 0x00020000;   // descriptor word 3 of a raw (untyped) buffer
+
+// A raw buffer descriptor over [p, p + bytes), bytes < 2^32.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, kRawBufferFlags);
+}
+
 // --------------------------------------------------------------- loads
 // p is 4-byte aligned; the hardware allows dword-aligned 16-byte loads.
 __device__ __forceinline__ u32x4 ld16(const uint8_t* p) { return *reinterpret_cast<const u32x4_a4*>(p); }
@@ -197,6 +205,22 @@ struct Contig {
         const u32x4* p = reinterpret_cast<const u32x4*>(step);
 #pragma unroll
         for (int k = 0; k < kLoads; ++k) c.v[k] = __builtin_nontemporal_load(p + min(64 * k + lane, kChunks - 1));
+    }
+    // The same loads through a buffer descriptor: the step starts soff bytes
+    // into the buffer of rs, and voff[k] = 16 * min(64 k + lane, kChunks - 1)
+    // (lane_offsets) is the lane's chunk within it.  The address arithmetic
+    // is scalar (soff) and per-lane constant (voff), so no vector
+    // instructions go to it; offsets past the buffer's range read 0.
+    __device__ static void lane_offsets(int lane, int (&voff)[kLoads]) {
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) voff[k] = 16 * min(64 * k + lane, kChunks - 1);
+    }
+    __device__ static void fetch(__amdgpu_buffer_rsrc_t rs, int soff, const int (&voff)[kLoads], Chunks& c) {
+#pragma unroll
+        for (int k = 0; k < kLoads; ++k) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff[k], soff, kPolicyNT);
+            c.v[k] = u32x4{v[0], v[1], v[2], v[3]};
+        }
     }
     // Copies the chunks to the wave's LDS scratch (kStepBytes, 16-byte aligned)
     // and reads block `lane` back.  LDS operations of one wave complete in

@@ -235,39 +235,55 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
     uint8_t* scratch = reinterpret_cast<uint8_t*>(lds + nb * kXPad) + wave * RR * C::kStepBytes;
     const int T = nb / 64;
     const int64_t wstride = (int64_t)gridDim.x * NW;
-    const int64_t N = segs.end[segs.n - 1];
-    const int64_t NP = (N + RR - 1) / RR;          // row groups
-    auto seg_of = [&](int64_t g) {
-        int i = 0;
-#pragma unroll
-        for (int k = 0; k + 1 < kMaxSegs; ++k) i += (k + 1 < segs.n && g >= segs.end[k]) ? 1 : 0;
-        return i;
-    };
+    // rows < 2^31 (checked by the launcher): 32-bit row arithmetic is scalar
+    const int N = (int)segs.end[segs.n - 1];
+    const int NP = (N + RR - 1) / RR;               // row groups
+    const int wstride32 = (int)wstride;
+    const uint32_t pitch = (uint32_t)nb * F::kBytes;  // bytes per row (< 2^32, checked)
 
     typename C::Chunks buf[PD][RR];
-    int64_t lrow = (int64_t)blockIdx.x * NW + wave;   // next step to load (row group)
+    int lrow = (int)blockIdx.x * NW + wave;          // next step to load (row group)
     int lt = 0;
-    int64_t crow = lrow;                              // next step to compute
+    int crow = lrow;                                 // next step to compute
     int ct = 0;
-    auto advance = [&](int64_t& row, int& t) {
-        if (++t == T) { t = 0; row += wstride; }
+    auto advance = [&](int& row, int& t) {
+        if (++t == T) { t = 0; row += wstride32; }
     };
+    // The load cursor keeps a buffer descriptor over each row of its row
+    // group (wave-uniform, in scalar registers): the matrix lookup runs once
+    // per row group (rows only increase, so it starts from the last matrix
+    // found), and a step's loads are the descriptor, a scalar step offset
+    // and a per-lane constant offset.
+    __amdgpu_buffer_rsrc_t lrs[RR];
+    int lseg = 0;
+    int voff[C::kLoads];
+    C::lane_offsets(lane, voff);
+    auto set_rows = [&](int p) {
+        int i = lseg;
+#pragma unroll
+        for (int k = 0; k < RR; ++k) {
+            const int row = min(RR * p + k, N - 1);
+            while (i + 1 < segs.n && row >= segs.end[i]) ++i;
+            if (k == 0) lseg = i;
+            lrs[k] = raw_buffer(segs.W[i] + (int64_t)(row - (i ? (int)segs.end[i - 1] : 0)) * pitch, pitch);
+        }
+    };
+    set_rows(min(lrow, NP - 1));
     auto load_next = [&](typename C::Chunks (&c)[RR]) {
         // Past the end: the last row group's first step (data never used).
         // Re-reading the wave's own last step instead was faster on 4-6k-row
         // Q8_0 matrices but went back to HBM (non-temporal loads, +5% traffic
         // on gate+up); a window of the staged x was slower everywhere.
-        const int64_t p = min(lrow, NP - 1);
-        const int t = lrow < NP ? lt : 0;
+        const int soff = (lrow < NP ? lt : 0) * C::kStepBytes;
 #pragma unroll
-        for (int k = 0; k < RR; ++k) {
-            const int64_t row = min(RR * p + k, N - 1);
-            const int i = seg_of(row);
-            const int64_t r = row - (i ? segs.end[i - 1] : 0);
-            C::fetch(segs.W[i] + (r * nb + 64 * t) * F::kBytes, lane, c[k]);
+        for (int k = 0; k < RR; ++k) C::fetch(lrs[k], soff, voff, c[k]);
+        if (lrow < NP && ++lt == T) {
+            lt = 0;
+            lrow += wstride32;
+            set_rows(min(lrow, NP - 1));
         }
-        if (lrow < NP) advance(lrow, lt);
     };
+    int cseg = 0;   // matrix of the compute cursor's rows (rows only increase)
     float acc[RR];
 #pragma unroll
     for (int k = 0; k < RR; ++k) acc[k] = 0.f;
@@ -289,10 +305,10 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
 #pragma unroll
             for (int k = 0; k < RR; ++k) {
                 const float tot = segment_sum<64>(acc[k]);
-                const int64_t row = RR * crow + k;
-                if (lane == 0 && row < N) {
-                    const int i = seg_of(row);
-                    segs.y[i][row - (i ? segs.end[i - 1] : 0)] = tot;
+                const int row = RR * crow + k;
+                if (row < N) {
+                    while (cseg + 1 < segs.n && row >= segs.end[cseg]) ++cseg;
+                    if (lane == 0) segs.y[cseg][row - (cseg ? segs.end[cseg - 1] : 0)] = tot;
                 }
                 acc[k] = 0.f;
             }
@@ -820,6 +836,8 @@ int32_t launch_c_xu(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
 template <class F, class XT = float>
 bool try_launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st, bool force, int32_t* rc) {
     if (nb % 64 || !aligned(x, XIn<XT>::kVecAlign) || segs.n < 1 || segs.n > kMaxSegs) return false;
+    // 32-bit row indices and per-row buffer descriptors
+    if (segs.end[segs.n - 1] >= ((int64_t)1 << 31) || (int64_t)nb * F::kBytes >= ((int64_t)1 << 31)) return false;
     for (int i = 0; i < segs.n; ++i)
         if (!aligned(segs.W[i], 16)) return false;
     const int64_t N = segs.end[segs.n - 1];

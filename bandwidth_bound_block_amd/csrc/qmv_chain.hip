@@ -10,8 +10,11 @@
 // previous stage is still being computed.  A stage marked `wait` reads
 // outputs of earlier stages: before it stages its activations every
 // workgroup meets at a grid barrier (all earlier outputs written through to
-// device-coherent memory), while the weight loads already issued stay in
-// flight.  Stages without `wait` start as soon as each workgroup is done.
+// device-coherent memory).  The wave's wait before it arrives covers every
+// outstanding memory operation, so the weight loads it issued for the
+// stage's first step land before the barrier (they are in registers when
+// it ends) rather than overlapping it: only their issue is early.  Stages
+// without `wait` start as soon as each workgroup is done.
 //
 // The per-stage arithmetic is the batch-1 dense kernel's (64 lanes per row
 // segment, fixed reduction order), so each stage's output equals a

@@ -219,8 +219,8 @@ DECODE_GROUPS = [("qkv", ("q", "k", "v")), ("o", ("o",)), ("gate_up", ("gate", "
 def build_llama_grouped(torch, qmv, wl, fmt):
     """The batch-1 8B decode step with the separate matrices and buffers of
     build_llama, launched in dependency order with one launch per
-    dependency level: q, k, v (same input) in one qmv_chain call, o, gate
-    and up (same input) in one call, down; then lm_head."""
+    dependency level: q, k and v (one input) in one qmv_chain call; o;
+    gate and up (one input, o's output) in one call; down; then lm_head."""
     dense = build_llama(torch, qmv, wl, fmt, 1, fused=False)
     sw = Sweep(dense.name.replace("_b1", "_grouped_b1"), 1)
     sw.keep = dense.keep
@@ -686,6 +686,21 @@ def _r(v, nd=1):
     return None if v is None else round(float(v), nd)
 
 
+def run_headline(torch, qmv, wl, args, detail):
+    """The headline step: the 8B Q8_0 batch-1 decode token, one launch per
+    dependency level, timed as a replayed HIP graph."""
+    sw = build_llama_grouped(torch, qmv, wl, "q8_0")
+    log(f"[{sw.name}] {len(sw.launches)} launches, {sw.bytes_per_step} bytes/step")
+    head = time_sweep(torch, sw, args.steps, args.warmup, not args.no_graph)
+    detail[sw.name] = head
+    log(f"[{sw.name}] {head['ms_per_step']:.3f} ms/step wall, {head['gbs_wall']:.0f} GB/s wall, "
+        f"{head['gbs_gpu']:.0f} GB/s events, {head['gbs_kernel']:.0f} GB/s per-matrix sum")
+    log(f"[{sw.name}] per matrix: " + json.dumps(head["per_matrix"]))
+    del sw
+    torch.cuda.empty_cache()
+    return head
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -693,8 +708,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--sweeps", default="all",
                     help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,int8,moe, or of "
-                         "FMT@B / FMT@Bf (one 8B sweep of format FMT at batch B, f: row-fused layout)")
+                         "FMT@B / FMT@Bf / FMT@1g (one 8B sweep of format FMT at batch B, f: row-fused layout, "
+                         "1g: batch 1 with one launch per dependency level)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing")
+    ap.add_argument("--no-headline", action="store_true",
+                    help="skip the headline step (profiling runs of single sweeps); no final line is printed")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--detail", default=None, help="write the full per-matrix tables of every workload here (JSON)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -725,15 +743,11 @@ def main():
         return
 
     detail = {}
-    sw = build_llama_grouped(torch, qmv, wl, "q8_0")
-    log(f"[{sw.name}] {len(sw.launches)} launches, {sw.bytes_per_step} bytes/step")
-    head = time_sweep(torch, sw, args.steps, args.warmup, not args.no_graph)
-    detail[sw.name] = head
-    log(f"[{sw.name}] {head['ms_per_step']:.3f} ms/step wall, {head['gbs_wall']:.0f} GB/s wall, "
-        f"{head['gbs_gpu']:.0f} GB/s events, {head['gbs_kernel']:.0f} GB/s per-matrix sum")
-    log(f"[{sw.name}] per matrix: " + json.dumps(head["per_matrix"]))
-    del sw
-    torch.cuda.empty_cache()
+    if args.no_headline:
+        head = None
+    else:
+        head = run_headline(torch, qmv, wl, args, detail)
+
 
     summary = {}          # sweep name -> [GB/s wall, tok/s wall] (the compact last line)
     oracles = {}          # memoized oracle timings per workload kind
@@ -773,7 +787,10 @@ def main():
     for nm in names:
         if "@" in nm:
             fmt, spec = nm.split("@")
-            s = build_llama(torch, qmv, wl, fmt, int(spec.rstrip("f")), fused=spec.endswith("f"))
+            if spec == "1g":
+                s = build_llama_grouped(torch, qmv, wl, fmt)
+            else:
+                s = build_llama(torch, qmv, wl, fmt, int(spec.rstrip("f")), fused=spec.endswith("f"))
             record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
             del s
             torch.cuda.empty_cache()
@@ -831,6 +848,8 @@ def main():
                     del s
                     torch.cuda.empty_cache()
 
+    if head is None:
+        return
     ceiling = read_ceiling(torch, qmv)
     log(f"[read_ceiling] {ceiling['value']:.0f} GB/s median, {ceiling['best']:.0f} best "
         f"({100 * ceiling['frac_of_peak']:.1f}% of {PEAK_GBS:.0f})")
