@@ -269,11 +269,9 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
         }
     };
     set_rows(min(lrow, NP - 1));
+    // Called while the load cursor is inside the wave's rows, and once at
+    // the start by waves without rows (clamped to the last row group).
     auto load_next = [&](typename C::Chunks (&c)[RR]) {
-        // Past the end: the last row group's first step (data never used).
-        // Re-reading the wave's own last step instead was faster on 4-6k-row
-        // Q8_0 matrices but went back to HBM (non-temporal loads, +5% traffic
-        // on gate+up); a window of the staged x was slower everywhere.
         const int soff = (lrow < NP ? lt : 0) * C::kStepBytes;
 #pragma unroll
         for (int k = 0; k < RR; ++k) C::fetch(lrs[k], soff, voff, c[k]);
@@ -331,25 +329,32 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
 
-#define QMV_PIPE_STEP(P)                                   \
-    {                                                      \
-        load_next(buf[((P) + PD - 1) % PD]);               \
-        __builtin_amdgcn_sched_barrier(0);                 \
-        compute_step(ct, buf[(P)]);                        \
-        advance(crow, ct);                                 \
-        if (crow >= NP) break;                             \
-    }
-    static_assert(PD >= 2 && PD <= 4, "pipeline depth");
+    // The load cursor runs one step ahead; once it is past the wave's last
+    // step, the step in hand is the last one and nothing more is loaded (no
+    // loads past the end: with every idle wave re-reading one place they
+    // queued on a few L2 channels).
+    static_assert(PD == 2, "pipeline depth");
     static_assert(RR == 1 || RR == 2, "rows per step");
     if (crow < NP) {
         while (true) {
-            QMV_PIPE_STEP(0)
-            QMV_PIPE_STEP(1)
-            if constexpr (PD >= 3) QMV_PIPE_STEP(2)
-            if constexpr (PD >= 4) QMV_PIPE_STEP(3)
+            if (lrow >= NP) {
+                compute_step(ct, buf[0]);
+                break;
+            }
+            load_next(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ct, buf[0]);
+            advance(crow, ct);
+            if (lrow >= NP) {
+                compute_step(ct, buf[1]);
+                break;
+            }
+            load_next(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ct, buf[1]);
+            advance(crow, ct);
         }
     }
-#undef QMV_PIPE_STEP
 }
 
 // Grouped MoE expert matvec.  blockIdx.y = u selects the u-th distinct

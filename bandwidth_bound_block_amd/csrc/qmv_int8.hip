@@ -154,6 +154,229 @@ __global__ __launch_bounds__(kThreads) void i8_kernel(const int8_t* __restrict__
     }
 }
 
+// ---------------------------------------------------------------- pipelined form
+// Rows of whole 1024-byte steps (n_cols a multiple of 1024, as every
+// Qwen3-0.6B shape): a wave streams row groups of RR rows with the next
+// pipeline slot's loads in flight while one is computed, across row
+// groups.  Lane l loads bytes 16 l .. 16 l + 15 of each 1024-byte step
+// through a per-row buffer descriptor (scalar row base, lane-constant
+// offset).  Activations either sit in registers for the whole launch (TX >
+// 0: rows of TX steps at batch B with B TX <= 8; a slot then holds all TX
+// steps of the group's rows) or are staged once per workgroup in LDS (TX ==
+// 0: a slot holds one step of each row).  Each slot also carries the mult
+// and shift of the lane's epilogue row, read with the weights through
+// buffer descriptors (rows past the end read 0 and are not stored), so the
+// epilogue waits on no memory access of its own.  The table of the _lut
+// form sits in registers (lane l holds entries 4 l .. 4 l + 3) and is
+// looked up across lanes.  The epilogue of a row group runs in RR x B lanes
+// at once (lane k + RR b: row k of the group, column b).  Sums are exact
+// int32, so every output equals i8_kernel's.
+constexpr int kI8Step = 1024;
+constexpr int kBufNT = 2;   // buffer-load cache policy: non-temporal
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t i8_buffer(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, (int)bytes, 0x00020000);   // raw buffer
+}
+
+template <int RR, int SW>
+struct I8Slot {
+    i32x4 w[RR][SW];
+    int32_t m, s;
+};
+
+template <int B, int RR, int NW, int TX>
+__global__ __launch_bounds__(64 * NW) void i8_stream_kernel(const int8_t* __restrict__ W, int N, int T_arg,
+                                                             const int8_t* __restrict__ x, int64_t ldx,
+                                                             const int32_t* __restrict__ mult,
+                                                             const int32_t* __restrict__ shift,
+                                                             const int8_t* __restrict__ lut, int8_t* __restrict__ y,
+                                                             int64_t ldy) {
+    static_assert(RR * B <= 64 && (RR & (RR - 1)) == 0, "epilogue lanes");
+    static_assert(TX == 0 || B * TX <= 8, "activations held in registers");
+    constexpr int SW = TX > 0 ? TX : 1;             // steps of a row per slot
+    extern __shared__ __attribute__((aligned(16))) i32x4 xs[];   // TX == 0: [B][T * 64] chunks of 16 bytes
+    const int T = TX > 0 ? TX : T_arg;              // steps per row
+    const int TS = TX > 0 ? 1 : T;                  // slots per row group
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const uint32_t K = (uint32_t)T * kI8Step;
+    const int NP = (N + RR - 1) / RR;
+    const int wstride = (int)gridDim.x * NW;
+    const int ek = lane % RR, eb = lane / RR;
+    const __amdgpu_buffer_rsrc_t mrs = i8_buffer(mult, 4u * (uint32_t)N);
+    const __amdgpu_buffer_rsrc_t srs = i8_buffer(shift, 4u * (uint32_t)N);
+
+    int32_t lutw = 0;
+    if (lut)
+        lutw = (int32_t)((uint32_t)(uint8_t)lut[4 * lane] | (uint32_t)(uint8_t)lut[4 * lane + 1] << 8 |
+                         (uint32_t)(uint8_t)lut[4 * lane + 2] << 16 | (uint32_t)(uint8_t)lut[4 * lane + 3] << 24);
+
+    int lrow = (int)blockIdx.x * NW + wave, lt = 0;   // load cursor: row group, slot
+    int crow = lrow, ct = 0;                          // compute cursor
+    __amdgpu_buffer_rsrc_t lrs[RR];
+    auto set_rows = [&](int p) {
+#pragma unroll
+        for (int k = 0; k < RR; ++k) lrs[k] = i8_buffer(W + (int64_t)min(RR * p + k, N - 1) * K, K);
+    };
+    set_rows(min(lrow, NP - 1));
+    // Called while the load cursor is inside the wave's rows, and once at
+    // the start by waves without rows (their loads stay inside W through the
+    // clamped descriptors, and mult / shift past the end read 0).
+    auto load_next = [&](I8Slot<RR, SW>& sl) {
+        const int t = lt;
+        const int g = lrow;
+#pragma unroll
+        for (int k = 0; k < RR; ++k)
+#pragma unroll
+            for (int u = 0; u < SW; ++u) {
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(lrs[k], 16 * lane, (t * SW + u) * kI8Step, kBufNT);
+                sl.w[k][u] = i32x4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+            }
+        const int goff = (int)(4u * RR * (uint32_t)g);   // < 2^32 bytes: a byte offset into mult / shift
+        sl.m = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(mrs, 4 * ek, goff, 0);
+        sl.s = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(srs, 4 * ek, goff, 0);
+        if (++lt == TS) {
+            lt = 0;
+            lrow += wstride;
+            set_rows(min(lrow, NP - 1));
+        }
+    };
+    i32x4 xr[B][SW];   // TX > 0: the lane's activation chunks
+    int32_t acc[RR][B];
+#pragma unroll
+    for (int k = 0; k < RR; ++k)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[k][b] = 0;
+    auto compute = [&](const I8Slot<RR, SW>& sl, int t) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int u = 0; u < SW; ++u) {
+                const i32x4 xv = TX > 0 ? xr[b][u] : xs[(b * T + t) * 64 + lane];
+#pragma unroll
+                for (int k = 0; k < RR; ++k) {
+                    int32_t a = acc[k][b];
+                    a = __builtin_amdgcn_sdot4(sl.w[k][u].x, xv.x, a, false);
+                    a = __builtin_amdgcn_sdot4(sl.w[k][u].y, xv.y, a, false);
+                    a = __builtin_amdgcn_sdot4(sl.w[k][u].z, xv.z, a, false);
+                    a = __builtin_amdgcn_sdot4(sl.w[k][u].w, xv.w, a, false);
+                    acc[k][b] = a;
+                }
+            }
+        if (t == TS - 1) {
+            int32_t mine = 0;
+#pragma unroll
+            for (int k = 0; k < RR; ++k)
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const int32_t tot = segment_sum<64>(acc[k][b]);
+                    if (k == ek && b == eb) mine = tot;
+                    acc[k][b] = 0;
+                }
+            int32_t v = sat8(rdbpot(srdhm(mine, sl.m), sl.s));
+            if (lut) {   // every lane takes part in the cross-lane read
+                const int idx = v + 128;
+                const int32_t wv = __builtin_amdgcn_ds_bpermute((idx >> 2) << 2, lutw);
+                v = (int8_t)(wv >> (8 * (idx & 3)));
+            }
+            const int row = RR * crow + ek;
+            if (eb < B && row < N) y[eb * ldy + row] = (int8_t)v;
+        }
+    };
+
+    // Activation loads go out before the first weight loads; with staging
+    // of one chunk per thread the store then waits for that chunk only
+    // (loads complete in order).
+    I8Slot<RR, SW> s0, s1;
+    const int nch = B * T * 64;
+    if constexpr (TX > 0) {
+#pragma unroll
+        for (int b = 0; b < B; ++b)
+#pragma unroll
+            for (int u = 0; u < TX; ++u) xr[b][u] = ld16(x + b * ldx + u * kI8Step + 16 * lane);
+        load_next(s0);
+    } else {
+        if (nch <= 64 * NW) {
+            const int i = threadIdx.x;
+            i32x4 xv = {0, 0, 0, 0};
+            if (i < nch) xv = ld16(x + (i / (T * 64)) * ldx + 16 * (i % (T * 64)));
+            load_next(s0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (i < nch) xs[i] = xv;
+        } else {
+            for (int i = threadIdx.x; i < nch; i += 64 * NW)
+                xs[i] = ld16(x + (i / (T * 64)) * ldx + 16 * (i % (T * 64)));
+            load_next(s0);
+        }
+        __syncthreads();
+    }
+
+    auto advance = [&]() {
+        if (++ct == TS) {
+            ct = 0;
+            crow += wstride;
+        }
+    };
+    // The load cursor runs one slot ahead; once it is past the wave's last
+    // slot, the slot in hand is the last one and nothing more is loaded.
+    if (crow < NP) {
+        while (true) {
+            if (lrow >= NP) {
+                compute(s0, ct);
+                break;
+            }
+            load_next(s1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(s0, ct);
+            advance();
+            if (lrow >= NP) {
+                compute(s1, ct);
+                break;
+            }
+            load_next(s0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(s1, ct);
+            advance();
+        }
+    }
+}
+
+// Largest activation block (batch x n_cols bytes) the pipelined form stages.
+constexpr int64_t kI8StreamLds = 32768;
+
+template <int B, int RR, int NW, int TX = 0>
+int32_t launch_stream(const int8_t* W, int64_t N, int64_t K, const int8_t* x, int64_t ldx, const int32_t* mult,
+                      const int32_t* shift, const int8_t* lut, int8_t* y, int64_t ldy, hipStream_t st) {
+    auto kern = i8_stream_kernel<B, RR, NW, TX>;
+    const size_t lds = TX > 0 ? 0 : (size_t)B * (size_t)K;
+    const int64_t tiles = ((N + RR - 1) / RR + NW - 1) / NW;
+    const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, (int)N, (int)(K / kI8Step), x, ldx, mult, shift,
+                       lut, y, ldy);
+    return check_launch("qmv_i8_requant");
+}
+
+// Four rows per group and 8 waves on tall matrices (the lm_head).  Shorter
+// ones at batch 1 with rows of up to 4 steps keep the activations in
+// registers (no staging, no barrier: these launches are latency-bound),
+// two rows per group; otherwise one row per group and 4 waves.
+template <int B>
+int32_t launch_stream_rows(const int8_t* W, int64_t N, int64_t K, const int8_t* x, int64_t ldx, const int32_t* mult,
+                           const int32_t* shift, const int8_t* lut, int8_t* y, int64_t ldy, hipStream_t st) {
+    if (N >= 16384) return launch_stream<B, 4, 8>(W, N, K, x, ldx, mult, shift, lut, y, ldy, st);
+    if constexpr (B == 1) {
+        switch (K / kI8Step) {
+        case 1: return launch_stream<1, 2, 4, 1>(W, N, K, x, ldx, mult, shift, lut, y, ldy, st);
+        case 2: return launch_stream<1, 2, 4, 2>(W, N, K, x, ldx, mult, shift, lut, y, ldy, st);
+        case 3: return launch_stream<1, 2, 4, 3>(W, N, K, x, ldx, mult, shift, lut, y, ldy, st);
+        case 4: return launch_stream<1, 2, 4, 4>(W, N, K, x, ldx, mult, shift, lut, y, ldy, st);
+        default: break;
+        }
+    }
+    return launch_stream<B, 1, 4>(W, N, K, x, ldx, mult, shift, lut, y, ldy, st);
+}
+
 constexpr int kRpl = 2;
 
 template <int B, int LPR>
@@ -192,6 +415,18 @@ int32_t i8_requant(const char* name, const int8_t* W, int64_t n_rows, int64_t n_
     if (!aligned(mult, 4) || !aligned(shift, 4)) return fail(QMV_EALIGN, "%s: mult/shift must be 4-byte aligned", name);
     const int nc = (int)(n_cols / 16);
     hipStream_t st = as_stream(stream);
+    if (n_cols % kI8Step == 0 && batch * n_cols <= kI8StreamLds) {
+        switch (batch) {
+        case 1: return launch_stream_rows<1>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        case 2: return launch_stream_rows<2>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        case 3: return launch_stream_rows<3>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        case 4: return launch_stream_rows<4>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        case 5: return launch_stream_rows<5>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        case 6: return launch_stream_rows<6>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        case 7: return launch_stream_rows<7>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        default: return launch_stream_rows<8>(W, n_rows, n_cols, x, ldx, mult, shift, lut, y, ldy, st);
+        }
+    }
     switch (batch) {
     case 1: return launch_lpr<1>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);
     case 2: return launch_lpr<2>(W, n_rows, nc, x, ldx, mult, shift, lut, y, ldy, st);

@@ -504,6 +504,35 @@ def test_int8_edges(env):
         assert np.array_equal(y, yr), (N, K)
 
 
+def test_int8_pipelined_shapes(env):
+    """The pipelined int8 form (n_cols a multiple of 1024, batch x n_cols <=
+    32 KB) on what the Qwen3-0.6B shapes do not reach: tall ragged matrices
+    (four rows per group, N % 4 != 0) at batch 1, 3 and 8 with and without
+    a table, long rows (32 steps per row), single rows, odd row counts with
+    two rows per group and the activations in registers (batch 1, 1..4
+    steps per row), batch 1 at 5 steps (staged activations), and the sizes
+    on either side of the LDS limit (batch 8 at 4096 columns: pipelined; at
+    5120: the per-segment kernel); bit-exact against the oracle."""
+    torch, qmv = env
+    g = np.random.default_rng(21)
+    lut = wl.int8_table("lut/random")
+    for N, K, B in [(16387, 1024, 1), (16387, 1024, 3), (20001, 2048, 8), (513, 32768, 1), (1, 1024, 2),
+                    (1, 1024, 1), (5, 2048, 1), (3, 3072, 1), (777, 4096, 1), (16383, 1024, 1), (77, 5120, 1),
+                    (777, 4096, 8), (777, 5120, 8)]:
+        say(f"int8 pipelined {N}x{K} B={B}")
+        W = g.integers(-128, 128, size=(N, K), dtype=np.int8)
+        x = g.integers(-128, 128, size=(B, K), dtype=np.int8)
+        mult = g.integers(-(1 << 31), 1 << 31, size=N, dtype=np.int64).astype(np.int32)
+        shift = g.integers(0, 32, size=N).astype(np.int32)
+        Wd, xd, md, sd = dev(torch, W), dev(torch, x), dev(torch, mult), dev(torch, shift)
+        y = qmv.qmv_i8_requant(Wd, xd, md, sd)
+        yl = qmv.qmv_i8_requant_lut(Wd, xd, md, sd, dev(torch, lut))
+        torch.cuda.synchronize()
+        _, yr = oracle.matvec_i8(W, x, mult, shift)
+        assert np.array_equal(y.cpu().numpy(), yr), (N, K, B)
+        assert np.array_equal(yl.cpu().numpy(), lut[yr.astype(np.int64) + 128]), (N, K, B, "lut")
+
+
 # ------------------------------------------------------------------ MoE
 @functools.lru_cache(maxsize=None)
 def _moe_experts(kind, N, K, E=wl.MOE_EXPERTS):
