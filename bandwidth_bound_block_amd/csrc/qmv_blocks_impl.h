@@ -336,17 +336,14 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
     static_assert(PD == 2, "pipeline depth");
     static_assert(RR == 1 || RR == 2, "rows per step");
     if (crow < NP) {
-        while (true) {
-            if (lrow >= NP) {
-                compute_step(ct, buf[0]);
-                break;
-            }
+        while (lrow < NP) {
             load_next(buf[1]);
             __builtin_amdgcn_sched_barrier(0);
             compute_step(ct, buf[0]);
             advance(crow, ct);
-            if (lrow >= NP) {
-                compute_step(ct, buf[1]);
+            if (lrow >= NP) {   // the last step is in buf[1]: one drain site below
+#pragma unroll
+                for (int k = 0; k < RR; ++k) buf[0][k] = buf[1][k];
                 break;
             }
             load_next(buf[0]);
@@ -354,6 +351,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
             compute_step(ct, buf[1]);
             advance(crow, ct);
         }
+        compute_step(ct, buf[0]);
     }
 }
 
