@@ -160,12 +160,11 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
         if (++t == T) { t = 0; tile += wstride; }
     };
 
-    // PD register buffers used in turn: while one step is computed the loads
-    // of the next PD-1 steps are in flight.  Loads are issued without
-    // branches, so the compiler waits only for the buffer in use: a wave past
-    // its last step re-reads the first step of the last tile (its data is
-    // never used).  Measured alternatives (the wave's own last step, a window
-    // of x) were no faster.
+    // Two register buffers used in turn: while one step is computed the
+    // loads of the next are in flight.  Once the load cursor is past the
+    // wave's last step, the step in hand is the last one: it is computed
+    // after the loop and nothing more is loaded.  (A wave without any step
+    // loads the last tile's first step once, clamped in bounds, unused.)
     Raw buf[PD][RPL];
     int64_t ltile = (int64_t)blockIdx.x * NW + wave;   // next step to load
     int lt = 0;
@@ -194,26 +193,25 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
 
-    // One pipeline step: load a step PD-1 ahead into the buffer freed last,
-    // then compute buffer P.  Exits the loop after the wave's last step.
-#define QMV_PIPE_STEP(P)                                                   \
-    {                                                                      \
-        load_next(buf[((P) + PD - 1) % PD]);                               \
-        __builtin_amdgcn_sched_barrier(0); /* loads before using buf[P] */ \
-        compute_step(ctile, ct, buf[(P)]);                                 \
-        advance(ctile, ct);                                                \
-        if (ctile >= ntiles) break;                                        \
-    }
-    static_assert(PD >= 2 && PD <= 4, "pipeline depth");
+    static_assert(PD == 2, "pipeline depth");
     if (ctile < ntiles) {
-        while (true) {
-            QMV_PIPE_STEP(0)
-            QMV_PIPE_STEP(1)
-            if constexpr (PD >= 3) QMV_PIPE_STEP(2)
-            if constexpr (PD >= 4) QMV_PIPE_STEP(3)
+        while (ltile < ntiles) {
+            load_next(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);   // loads before using buf[0]
+            compute_step(ctile, ct, buf[0]);
+            advance(ctile, ct);
+            if (ltile >= ntiles) {   // the last step is in buf[1]: one drain site below
+#pragma unroll
+                for (int r = 0; r < RPL; ++r) buf[0][r] = buf[1][r];
+                break;
+            }
+            load_next(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[1]);
+            advance(ctile, ct);
         }
+        compute_step(ctile, ct, buf[0]);
     }
-#undef QMV_PIPE_STEP
 }
 
 // Batch 1, rows of whole 64-block steps (nb % 64 == 0), W 16-byte aligned:
