@@ -390,7 +390,7 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
         if (++st == T) { st = 0; tile += NW; }
     };
     auto load_next = [&](Raw (&r)[RS]) {
-        const int64_t tile = min(ltile, te - 1);       // past the range: re-read a loaded block
+        const int64_t tile = min(ltile, te - 1);       // past the range (prologue only): a block in range
         const int j = min(li + LPR * (ltile < te ? lt : 0), nb - 1);
         const int64_t row = min(tile * G + seg, N - 1);
 #pragma unroll
@@ -457,21 +457,56 @@ __device__ __forceinline__ void moe_chunk(const uint8_t* __restrict__ We, int64_
         for (int p = 0; p < PD - 1; ++p) load_next(buf[p]);
     }
 
+    // The load cursor runs PD - 1 steps ahead.  Once it is past the range,
+    // the steps still in flight (buffer P first, then the next) are moved to
+    // buf[0], buf[1] in order and computed at one site after the loop, so no
+    // load goes past the wave's last step (idle re-reads of one place queued
+    // on a few L2 channels).
+    static_assert(PD == 2 || PD == 3, "pipeline depth");
+    auto rotate_to_front = [&](int P) {
+        if (PD == 2) {
+            if (P == 1)
+#pragma unroll
+                for (int k = 0; k < RS; ++k) buf[0][k] = buf[1][k];
+        } else if (P == 1) {
+#pragma unroll
+            for (int k = 0; k < RS; ++k) {
+                buf[0][k] = buf[1][k];
+                buf[1][k] = buf[PD - 1][k];
+            }
+        } else if (P == 2) {
+#pragma unroll
+            for (int k = 0; k < RS; ++k) {
+                const Raw tmp = buf[0][k];
+                buf[0][k] = buf[PD - 1][k];
+                buf[1][k] = tmp;
+            }
+        }
+    };
 #define QMV_MOE_STEP(P)                                    \
     {                                                      \
+        if (ltile >= te) {                                 \
+            rotate_to_front(P);                            \
+            break;                                         \
+        }                                                  \
         load_next(buf[((P) + PD - 1) % PD]);               \
         __builtin_amdgcn_sched_barrier(0);                 \
         compute_step(ctile, ct, buf[(P)]);                 \
         advance(ctile, ct);                                \
-        if (ctile >= te) break;                            \
     }
-    static_assert(PD >= 2 && PD <= 4, "pipeline depth");
     if (ctile < te) {
         while (true) {
             QMV_MOE_STEP(0)
             QMV_MOE_STEP(1)
             if constexpr (PD >= 3) QMV_MOE_STEP(2)
-            if constexpr (PD >= 4) QMV_MOE_STEP(3)
+        }
+#pragma unroll 1
+        for (int i = 0; i < PD - 1 && ctile < te; ++i) {
+            compute_step(ctile, ct, buf[0]);
+            advance(ctile, ct);
+            if (PD > 2)
+#pragma unroll
+                for (int k = 0; k < RS; ++k) buf[0][k] = buf[1][k];
         }
     }
 #undef QMV_MOE_STEP
