@@ -21,11 +21,11 @@ def test_final_line_is_compact_and_complete():
     ceiling = {"value": 6784.2, "best": 6811.0, "unit": "GB/s", "bytes": 4 << 30, "frac_of_peak": 0.848,
                "launches": 7, "statistic": "median", "kernel": "stream_read_kernel (qmv_stream_read)"}
     cpu = {"value": 1.288, "unit": "GB/s", "cores": 1, "kind": "oracle",
-           "sample": "one full batch-1 Q8_0 token of the 8B layer set: 225 matvecs (a layer's 7 matrices timed "
-                     "once, x32, + lm_head), 7984714752 bytes in 6.20 s on one thread",
+           "sample": "one batch-1 Q8_0 8B token: a layer's 7 matrices timed once x32 + lm_head, "
+                     "7984714752 B in 6.20 s, 1 thread",
            "host_cpus": 16, "cpu_model": "AMD EPYC 9575F 64-Core Processor", "tok_s_equiv": 0.1613}
     # more sweeps, with longer names, than a default run produces
-    summary = {f"llama8b_q4_1_fused_grouped_chain_b{i}": [12345.0, 123456.0] for i in range(40)}
+    summary = {f"llama8b_q4_1_fused_grouped_chain_b{i}": [12345, 123456] for i in range(40)}
     line = bench.final_line(_head(), ceiling, cpu, summary, 50, 3)
     text = json.dumps(line)
     assert len(text) < 4096, len(text)
