@@ -931,20 +931,20 @@ int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx,
     return launch_lpr<F, 1, 0, 4, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);
 }
 
-template <class F>
-int32_t launch_batch(const uint8_t* W, int64_t N, int nb, const float* x, int64_t ldx, int B, float* y,
+template <class F, class XT = float>
+int32_t launch_batch(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, int B, float* y,
                      int64_t ldy, hipStream_t st) {
     switch (B) {
-    case 1: return launch_b1<F>(W, N, nb, x, ldx, y, ldy, st);
-    case 2: return launch_lpr<F, 2, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
-    case 3: return launch_lpr<F, 3, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
-    case 4: return launch_lpr<F, 4, 0, 8>(W, N, nb, x, ldx, y, ldy, st);
+    case 1: return launch_b1<F, XT>(W, N, nb, x, ldx, y, ldy, st);
+    case 2: return launch_lpr<F, 2, 0, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
+    case 3: return launch_lpr<F, 3, 0, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
+    case 4: return launch_lpr<F, 4, 0, 8, XT>(W, N, nb, x, ldx, y, ldy, st);
     // 5..8 columns: the staged activations fill most of the LDS, so one
     // workgroup per CU; 16 waves share them (measured +13..26% at 8).
-    case 5: return launch_lpr<F, 5, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
-    case 6: return launch_lpr<F, 6, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
-    case 7: return launch_lpr<F, 7, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
-    default: return launch_lpr<F, 8, 0, 16>(W, N, nb, x, ldx, y, ldy, st);
+    case 5: return launch_lpr<F, 5, 0, 16, XT>(W, N, nb, x, ldx, y, ldy, st);
+    case 6: return launch_lpr<F, 6, 0, 16, XT>(W, N, nb, x, ldx, y, ldy, st);
+    case 7: return launch_lpr<F, 7, 0, 16, XT>(W, N, nb, x, ldx, y, ldy, st);
+    default: return launch_lpr<F, 8, 0, 16, XT>(W, N, nb, x, ldx, y, ldy, st);
     }
 }
 
@@ -993,26 +993,19 @@ int32_t matvec(const char* name, const void* W, int64_t N, int64_t K, const XT* 
                         "%s: the matrix-core path needs batch 2..8, n_cols a multiple of 256, W 16-byte aligned, "
                         "x aligned to 4 elements (16 bytes for fp32) and ldx a multiple of 4", name);
     }
-    // The staged activation block must fit in LDS; wider batches than fit
-    // are processed in column groups (each group re-reads W).
+    // The staged activation block (widened to fp32) must fit in LDS; wider
+    // batches than fit are processed in column groups (each group re-reads
+    // W).  16-bit activations take the same multi-column kernels: W is
+    // streamed once per column group, not once per column.
     const int per_col = nb * kXPad * (int)sizeof(float);
     const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / per_col));
     if (per_col > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
-    if constexpr (std::is_same<XT, float>::value) {
-        for (int b0 = 0; b0 < batch; b0 += per_pass) {
-            const int bw = std::min(per_pass, batch - b0);
-            rc = launch_batch<F>(static_cast<const uint8_t*>(W), N, nb, x + b0 * ldx, ldx, bw, y + b0 * ldy, ldy,
+    for (int b0 = 0; b0 < batch; b0 += per_pass) {
+        const int bw = std::min(per_pass, batch - b0);
+        rc = launch_batch<F, XT>(static_cast<const uint8_t*>(W), N, nb, x + b0 * ldx, ldx, bw, y + b0 * ldy, ldy,
                                  as_stream(stream));
-            if (rc != QMV_OK) return rc;
-        }
-    } else {
-        // 16-bit activations on the FMA kernels: one batch-1 launch per column
-        for (int b = 0; b < batch; ++b) {
-            rc = launch_b1<F, XT>(static_cast<const uint8_t*>(W), N, nb, x + b * ldx, ldx, y + b * ldy, ldy,
-                                  as_stream(stream));
-            if (rc != QMV_OK) return rc;
-        }
+        if (rc != QMV_OK) return rc;
     }
     return ok();
 }

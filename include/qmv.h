@@ -146,8 +146,8 @@ int32_t qmv_matvec_path(qmv_fmt fmt, const void* W, int64_t n_rows, int64_t n_co
  * the result equals, bitwise, the fp32 call on the widened activations with
  * the same path.  x must be aligned to its element size; the vectorized
  * staging needs 4-element (8-byte) alignment and ldx a multiple of 4, and is
- * skipped otherwise.  On the FMA kernels 16-bit activations at batch > 1 run
- * one column per launch.  path as qmv_matvec_path.
+ * skipped otherwise.  All columns of a call share one pass over W (per
+ * column group that fits the LDS, as for fp32).  path as qmv_matvec_path.
  * Errors: as qmv_matvec_path; QMV_EINVAL for an unknown x_type, QMV_EALIGN
  * for x not aligned to its element size.
  */
