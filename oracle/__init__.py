@@ -9,8 +9,9 @@ the integer semantics).
 
 Sources (the pages collected on the subject):
   * "One Native Stack for Private, Continuously-Learning AI", Sec. "The
-    Unified Quant Core" (formats Q8_0 34 B/32, Q4_0 18 B/32; one decoder per
-    format) and the QLoRA Lemma (y_i = sum_j DEQ(W)_ij x_j).
+    Unified Quant Core" (formats Q8_0 34 B/32, Q4_0 18 B/32, Q4_K named
+    without its layout; one decoder per format) and the QLoRA Lemma
+    (y_i = sum_j DEQ(W)_ij x_j).
   * "Economical Serving and the hanzo.ai Platform", Sec. 2.1 (one stream of
     the weights per token) and Sec. 2.2 (block decoder + traits record).
   * "Blue -- porting zen-nano (Qwen3-0.6B) to deterministic on-chain
@@ -28,9 +29,21 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _SRC_PATH = os.path.join(_HERE, "qmv_oracle.c")
 
-Q8_0, Q4_0, Q4_1 = 0, 1, 2
-FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}
+Q8_0, Q4_0, Q4_1, Q4_K = 0, 1, 2, 3
+FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q4_k": Q4_K}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}      # per 32 weights
+SUPER_BLOCK = {Q4_K: (256, 144)}                   # (weights, bytes) per super-block
+
+
+def row_bytes(fmt, K):
+    """Stored bytes of one row of K weights."""
+    fmt = _fmt(fmt)
+    if fmt in SUPER_BLOCK:
+        w, b = SUPER_BLOCK[fmt]
+        assert K % w == 0
+        return K // w * b
+    assert K % 32 == 0
+    return K // 32 * BLOCK_BYTES[fmt]
 
 _lib = None
 
@@ -112,7 +125,7 @@ def dequant(fmt, W, N, K):
     lib = _load()
     W = np.ascontiguousarray(W, dtype=np.uint8)
     fmt = _fmt(fmt)
-    assert W.size == N * (K // 32) * BLOCK_BYTES[fmt]
+    assert W.size == N * row_bytes(fmt, K)
     out = np.empty((N, K), dtype=np.float64)
     _check(lib.qo_dequant(fmt, _ptr(W), N, K, _ptr(out)), "dequant")
     return out
@@ -129,7 +142,7 @@ def matvec(fmt, W, N, K, x, rows=None):
     W = np.ascontiguousarray(W, dtype=np.uint8)
     x = np.ascontiguousarray(np.atleast_2d(x), dtype=np.float32)
     B = x.shape[0]
-    assert x.shape[1] == K and W.size == N * (K // 32) * BLOCK_BYTES[fmt]
+    assert x.shape[1] == K and W.size == N * row_bytes(fmt, K)
     if rows is not None:
         rows = np.ascontiguousarray(rows, dtype=np.int64)
         n = rows.size

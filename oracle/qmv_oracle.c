@@ -24,19 +24,22 @@
  *          SaturatingRoundingDoublingHighMul(acc, mult[o]) followed by
  *          RoundingDivideByPOT(., shift[o]) to int8.
  * Where the pages leave a step open (byte layout, nibble order, Q4_1, the
- * bodies of the two gemmlowp functions, the int8 saturation range) this file
- * takes the plainest reading; each such place says "Reading:".
+ * Q4_K super-block layout, the bodies of the two gemmlowp functions, the
+ * int8 saturation range) this file takes the plainest reading; each such
+ * place says "Reading:".
  *
  * Status: every function below is pinned by the CPU tests (hand-computed
- * blocks, exhaustive fp16 decode, exact-rational brute force, integer
- * closed forms and an independent big-integer mirror).
+ * blocks and super-blocks, exhaustive fp16 decode, exact-rational brute
+ * force, integer closed forms and an independent big-integer mirror).  The
+ * Q4_K layout itself is a reading: agreement with ggml's Q4_K files is
+ * parity unpinned (no ggml file or output is available to compare with).
  */
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 #include <math.h>
 
-enum { QO_Q8_0 = 0, QO_Q4_0 = 1, QO_Q4_1 = 2 };
+enum { QO_Q8_0 = 0, QO_Q4_0 = 1, QO_Q4_1 = 2, QO_Q4_K = 3 };
 enum { QO_OK = 0, QO_EINVAL = 1, QO_ENOMEM = 2, QO_EOVERFLOW = 3 };
 
 /* IEEE 754 binary16 -> double, straight from the format definition:
@@ -108,18 +111,74 @@ void qo_dequant_block(int fmt, const uint8_t* blk, double out[32]) {
     }
 }
 
-/* DEQ(W) for one row of K weights (K a multiple of 32). */
+/* Q4_K: 256-weight super-blocks of 144 bytes.  [NST] Sec. "The Unified
+ * Quant Core" lists Q4_K beside Q8_0 and Q4_0 without its layout.
+ * Reading: the ggml-compatible layout (agreement with ggml itself is
+ * parity unpinned):
+ *   bytes 0-1  d    (fp16)   scale of the sub-block scales
+ *   bytes 2-3  dmin (fp16)   scale of the sub-block minimums
+ *   bytes 4-15 b[0..11]      eight 6-bit scales sc_s and eight 6-bit
+ *                            minimums mn_s, s = 0..7:
+ *                              s < 4:  sc_s = b[s] & 63,  mn_s = b[s+4] & 63
+ *                              s >= 4: sc_s = (b[s+4] & 15) + 16*(b[s-4] >> 6)
+ *                                      mn_s = (b[s+4] >> 4) + 16*(b[s] >> 6)
+ *   bytes 16-143 q[0..127]   4-bit codes: weight 32s + i (i < 32) is the low
+ *                            nibble of q[32*(s/2) + i] for even s, the high
+ *                            nibble for odd s
+ *   w_{32s+i} = d*sc_s*c - dmin*mn_s.
+ * d*sc_s*c (at most 21 significant bits) and dmin*mn_s (at most 17) are
+ * exact in double; their difference is exact whenever its bit span is at
+ * most 53 (scale exponents within 2^32 of each other), else rounded once. */
+static void q4k_scale_min(const uint8_t b[12], int s, int* sc, int* mn) {
+    if (s < 4) {
+        *sc = b[s] & 63;
+        *mn = b[s + 4] & 63;
+    } else {
+        *sc = (b[s + 4] & 15) + 16 * (b[s - 4] >> 6);
+        *mn = (b[s + 4] >> 4) + 16 * (b[s] >> 6);
+    }
+}
+
+void qo_dequant_superblock_q4k(const uint8_t* sb, double out[256]) {
+    double d = qo_f16_to_f64(rd16(sb));
+    double dmin = qo_f16_to_f64(rd16(sb + 2));
+    const uint8_t* b = sb + 4;
+    const uint8_t* q = sb + 16;
+    int s, i;
+    for (s = 0; s < 8; ++s) {
+        int sc, mn;
+        q4k_scale_min(b, s, &sc, &mn);
+        for (i = 0; i < 32; ++i) {
+            int byte = q[32 * (s / 2) + i];
+            int c = (s % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
+            out[32 * s + i] = d * (double)sc * (double)c - dmin * (double)mn;
+        }
+    }
+}
+
+/* Bytes of one row of K weights; K must be a multiple of the format's
+ * block (32, or 256 for Q4_K). */
+int64_t qo_row_bytes(int fmt, int64_t K) {
+    if (fmt == QO_Q4_K) return (K % 256) ? -1 : K / 256 * 144;
+    if (qo_block_bytes(fmt) < 0 || K % 32) return -1;
+    return K / 32 * qo_block_bytes(fmt);
+}
+
+/* DEQ(W) for one row of K weights. */
 static void dequant_row(int fmt, const uint8_t* row, int64_t K, double* out) {
-    int64_t nb = K / 32, b;
-    int64_t bb = qo_block_bytes(fmt);
-    for (b = 0; b < nb; ++b) qo_dequant_block(fmt, row + b * bb, out + 32 * b);
+    int64_t b;
+    if (fmt == QO_Q4_K) {
+        for (b = 0; b < K / 256; ++b) qo_dequant_superblock_q4k(row + 144 * b, out + 256 * b);
+        return;
+    }
+    for (b = 0; b < K / 32; ++b) qo_dequant_block(fmt, row + b * qo_block_bytes(fmt), out + 32 * b);
 }
 
 /* Full dequantization, row-major [N][K]. */
 int qo_dequant(int fmt, const uint8_t* W, int64_t N, int64_t K, double* out) {
-    int64_t i, bb = qo_block_bytes(fmt);
-    if (bb < 0 || N < 0 || K < 0 || K % 32) return QO_EINVAL;
-    for (i = 0; i < N; ++i) dequant_row(fmt, W + i * (K / 32) * bb, K, out + i * K);
+    int64_t i, rb = qo_row_bytes(fmt, K);
+    if (rb < 0 || N < 0 || K < 0) return QO_EINVAL;
+    for (i = 0; i < N; ++i) dequant_row(fmt, W + i * rb, K, out + i * K);
     return QO_OK;
 }
 
@@ -135,17 +194,17 @@ int qo_matvec(int fmt, const uint8_t* W, int64_t N, int64_t K,
               const float* x, int64_t ldx, int32_t B,
               const int64_t* rows, int64_t nrows,
               double* y, double* S, int64_t ldo) {
-    int64_t bb = qo_block_bytes(fmt), t, j;
+    int64_t rb = qo_row_bytes(fmt, K), t, j;
     int32_t b;
     double* w;
-    if (bb < 0 || N < 0 || K < 0 || K % 32 || B < 0 || ldx < K) return QO_EINVAL;
+    if (rb < 0 || N < 0 || K < 0 || B < 0 || ldx < K) return QO_EINVAL;
     if (!rows) nrows = N;
     w = (double*)malloc((size_t)(K > 0 ? K : 1) * sizeof(double));
     if (!w) return QO_ENOMEM;
     for (t = 0; t < nrows; ++t) {
         int64_t i = rows ? rows[t] : t;
         if (i < 0 || i >= N) { free(w); return QO_EINVAL; }
-        dequant_row(fmt, W + i * (K / 32) * bb, K, w);
+        dequant_row(fmt, W + i * rb, K, w);
         for (b = 0; b < B; ++b) {
             const float* xb = x + (int64_t)b * ldx;
             double acc = 0.0, sabs = 0.0;

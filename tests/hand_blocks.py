@@ -56,3 +56,25 @@ def x_vec(kind):
         x[0] = 1
         return x
     raise ValueError(kind)
+
+
+def super_block_bytes(spec):
+    """The 144 stored bytes of a Q4_K super-block spec."""
+    q = spec["q"]
+    if q.startswith("all:"):
+        qs = [int(q[4:], 16)] * 128
+    elif q == "k":
+        qs = list(range(128))
+    else:
+        raise ValueError(q)
+    out = _u16(spec["d"]) + _u16(spec["dmin"]) + list(spec["b"]) + qs
+    assert len(out) == 144
+    return np.array(out, dtype=np.uint8)
+
+
+def x_vec256(kind):
+    if kind == "ones":
+        return np.ones(256, dtype=np.float32)
+    if kind == "ramp":
+        return np.arange(256, dtype=np.float32)
+    raise ValueError(kind)

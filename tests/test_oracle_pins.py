@@ -61,6 +61,53 @@ def test_q4_nibble_order_distinguishes(oracle_lib):
     assert np.array_equal(w[16:], np.full(16, -8.0))
 
 
+@pytest.mark.parametrize("spec", hb.load()["super_blocks"], ids=lambda s: s["id"])
+def test_hand_super_block_q4k(oracle_lib, spec):
+    """Q4_K super-blocks worked by hand (HB13-HB15): y of the oracle's
+    matvec and of its dequantizer, and HB14's per-sub-block weights and
+    6-bit fields."""
+    o = oracle_lib
+    blk = hb.super_block_bytes(spec)
+    x = hb.x_vec256(spec["x"])
+    y, S = o.matvec("q4_k", blk, 1, 256, x[None, :])
+    assert y[0, 0] == float(spec["y"]), (spec["id"], y[0, 0])
+    w = o.dequant("q4_k", blk, 1, 256)[0]
+    assert float(np.dot(w, x.astype(np.float64))) == float(spec["y"])
+    if "w" in spec:
+        for s in range(8):
+            assert np.all(w[32 * s:32 * s + 32] == float(spec["w"][s])), (spec["id"], s)
+
+
+def test_q4k_nibble_order_distinguishes(oracle_lib):
+    """HB15: sub-block 2p takes the low nibbles of bytes 32p..32p+31 and
+    sub-block 2p+1 their high nibbles; element by element."""
+    spec = [s for s in hb.load()["super_blocks"] if s["id"] == "HB15"][0]
+    w = oracle_lib.dequant("q4_k", hb.super_block_bytes(spec), 1, 256)[0]
+    for p in range(4):
+        i = np.arange(32)
+        assert np.array_equal(w[64 * p:64 * p + 32], ((32 * p + i) & 15).astype(np.float64))
+        assert np.array_equal(w[64 * p + 32:64 * p + 64], ((32 * p + i) >> 4).astype(np.float64))
+
+
+def test_q4k_rows_and_one_hot(oracle_lib):
+    """Two-super-block rows of HB13 and HB14 in either order (row pitch 288
+    bytes), one-hot x picks single weights, and a row subset equals the
+    full run."""
+    o = oracle_lib
+    sbs = {s["id"]: hb.super_block_bytes(s) for s in hb.load()["super_blocks"]}
+    W = np.stack([np.concatenate([sbs["HB13"], sbs["HB14"]]), np.concatenate([sbs["HB14"], sbs["HB13"]])])
+    for j, want in [(0, [1.0, 94.25]), (256 + 32 * 7 + 5, [460.75, 16.0]), (256 + 64, [-15.5, 3.0])]:
+        x = np.zeros((1, 512), dtype=np.float32)
+        x[0, j] = 1
+        y, _ = o.matvec("q4_k", W, 2, 512, x)
+        assert list(y[0]) == want, (j, y)
+    x = np.ones((1, 512), dtype=np.float32)
+    y, _ = o.matvec("q4_k", W, 2, 512, x)
+    assert list(y[0]) == [1792.0 + 33728.0] * 2
+    y1, _ = o.matvec("q4_k", W, 2, 512, x, rows=np.array([1]))
+    assert y1[0, 0] == y[0, 1]
+
+
 # ------------------------------------------------------------------ round trip
 def _blocks_f64(Wf):
     N, K = Wf.shape
