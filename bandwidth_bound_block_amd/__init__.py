@@ -10,6 +10,7 @@ library has not been built.
 
 Entry points (same names as the C ABI):
   qmv_q8_0 / qmv_q4_0 / qmv_q4_1   float block-quantized matvec, batch 1..8
+  qmv_q4_k                         the same for Q4_K super-blocks (256 weights, 144 bytes)
   qmv_matvec_path                  the same with the kernel family chosen
                                    (PATH_AUTO / PATH_FMA / PATH_MFMA)
   qmv_matvec_xt                    the same with fp32, fp16 or bf16 activations
@@ -28,18 +29,28 @@ Entry points (same names as the C ABI):
 import ctypes
 import os
 
-__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
+__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
            "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_i8_requant_lut",
            "qmv_moe", "qmv_moe_xt", "qmv_moe_swiglu", "qmv_moe_swiglu_xt", "qmv_moe_combine",
            "qmv_dequant", "qmv_stream_read", "qmv_chain", "qmv_chain_noalloc", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
-           "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "FORMATS", "BLOCK_BYTES"]
+           "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "Q4_K", "FORMATS", "BLOCK_BYTES", "row_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqmv.so")
 
-Q8_0, Q4_0, Q4_1 = 0, 1, 2
-FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1}
-BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}
+Q8_0, Q4_0, Q4_1, Q4_K = 0, 1, 2, 3
+FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q4_k": Q4_K}
+BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}      # per 32 weights
+SUPER_BLOCK = {Q4_K: (256, 144)}                   # (weights, bytes) per super-block
+
+
+def row_bytes(fmt, n_cols):
+    """Stored bytes of one row of n_cols weights (0 for an unknown format)."""
+    f = FORMATS.get(fmt, fmt)
+    if f in SUPER_BLOCK:
+        w, b = SUPER_BLOCK[f]
+        return n_cols // w * b
+    return n_cols // 32 * BLOCK_BYTES.get(f, 0)
 PATH_AUTO, PATH_FMA, PATH_MFMA = 0, 1, 2
 X_F32, X_F16, X_BF16 = 0, 1, 2
 _ERRORS = {1: "QMV_EINVAL", 2: "QMV_EALIGN", 3: "QMV_EUNSUPPORTED", 4: "QMV_EHIP"}
@@ -69,7 +80,7 @@ def _open():
                           "(hipcc --offload-arch=gfx950) first")
     L = ctypes.CDLL(_LIB_PATH)
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-    for name in ("qmv_q8_0", "qmv_q4_0", "qmv_q4_1"):
+    for name in ("qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k"):
         f = getattr(L, name)
         f.argtypes = [P, i64, i64, P, i64, i32, P, i64, P]
         f.restype = i32
@@ -165,7 +176,7 @@ def _matvec(cfn, fmt, W, n_rows, n_cols, x, y, stream):
     torch = _torch()
     _dev(W, "W", torch.uint8)
     _dev(x, "x", torch.float32)
-    need = n_rows * (n_cols // 32) * BLOCK_BYTES[fmt]
+    need = n_rows * row_bytes(fmt, n_cols)
     if W.numel() * W.element_size() < need or not W.is_contiguous():
         raise ValueError(f"W must be contiguous and hold {need} bytes")
     x2, B, ldx = _rows2d(x, "x", n_cols)
@@ -194,11 +205,18 @@ def qmv_q4_1(W, n_rows, n_cols, x, y=None, stream=None):
     return _matvec(_lib.qmv_q4_1, Q4_1, W, n_rows, n_cols, x, y, stream)
 
 
+def qmv_q4_k(W, n_rows, n_cols, x, y=None, stream=None):
+    """y[b] = DEQ_Q4_K(W) @ x[b]; x float32 [K] or [B, K] (B <= 8), K a
+    multiple of 256."""
+    return _matvec(_lib.qmv_q4_k, Q4_K, W, n_rows, n_cols, x, y, stream)
+
+
 def qmv_matvec_path(fmt, W, n_rows, n_cols, x, path, y=None, stream=None):
-    """As qmv_q8_0/q4_0/q4_1 for format fmt (Q8_0, Q4_0, Q4_1 or its name)
-    with the kernel family `path` (PATH_AUTO, PATH_FMA or PATH_MFMA)."""
+    """As qmv_q8_0/q4_0/q4_1/q4_k for format fmt (Q8_0, Q4_0, Q4_1, Q4_K or
+    its name) with the kernel family `path` (PATH_AUTO, PATH_FMA or
+    PATH_MFMA)."""
     f = FORMATS.get(fmt, fmt)
-    if f not in BLOCK_BYTES:
+    if f not in FORMATS.values():
         raise ValueError(f"unknown format {fmt!r}")
 
     def cfn(*a):
@@ -211,14 +229,14 @@ def qmv_matvec_xt(fmt, W, n_rows, n_cols, x, path=PATH_AUTO, y=None, stream=None
     (widened to fp32 exactly); y is float32."""
     torch = _torch()
     f = FORMATS.get(fmt, fmt)
-    if f not in BLOCK_BYTES:
+    if f not in FORMATS.values():
         raise ValueError(f"unknown format {fmt!r}")
     xt = {torch.float32: X_F32, torch.float16: X_F16, torch.bfloat16: X_BF16}.get(x.dtype)
     if xt is None:
         raise ValueError(f"x must be float32, float16 or bfloat16 (got {x.dtype})")
     _dev(W, "W", torch.uint8)
     _dev(x, "x", x.dtype)
-    need = n_rows * (n_cols // 32) * BLOCK_BYTES[f]
+    need = n_rows * row_bytes(f, n_cols)
     if W.numel() * W.element_size() < need or not W.is_contiguous():
         raise ValueError(f"W must be contiguous and hold {need} bytes")
     x2, B, ldx = _rows2d(x, "x", n_cols)

@@ -1,6 +1,7 @@
-// C entry points of the block-format (Q8_0 / Q4_0 / Q4_1) matvec, MoE and
-// dequant paths: argument routing to the format's FormatOps table (the
-// kernels themselves are in qmv_blocks_impl.h, compiled once per format).
+// C entry points of the block-format (Q8_0 / Q4_0 / Q4_1 / Q4_K) matvec,
+// MoE and dequant paths: argument routing to the format's FormatOps table
+// (the kernels themselves are in qmv_blocks_impl.h, compiled once per
+// 32-weight format, and qmv_q4k.hip).
 #include "qmv_host.h"
 
 namespace qmv {
@@ -10,6 +11,7 @@ const FormatOps* format_ops(qmv_fmt fmt) {
     case QMV_Q8_0: return &ops_q8_0();
     case QMV_Q4_0: return &ops_q4_0();
     case QMV_Q4_1: return &ops_q4_1();
+    case QMV_Q4_K: return &ops_q4_k();
     default: return nullptr;
     }
 }

@@ -22,7 +22,7 @@ on the launch stream, the measured stream-read ceiling, the oracle's time
 on the host (cpu_baseline) and a one-number summary per sweep.
 
 Extra workloads: the Q8_0 1024 x 1024 matvec over 480 rotated copies (so
-every call reads HBM), Q4_0 / Q4_1 at batch 1, 2, 4, 8, the int8 requant path
+every call reads HBM), Q4_0 / Q4_1 / Q4_K at batch 1, 2, 4, 8, the int8 requant path
 on Qwen3-0.6B shapes and the MoE expert path (plain and fused) at batch
 1, 2, 4, 8.
 
@@ -58,20 +58,20 @@ TRAFFIC_RECORDS = {
     "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>": {
         "key": "kernel_c_q8_0",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "6bcfb1eff766e89f929c39687979215f0204c616a5d202918094d70e97ffa3ee", "bytes_per_launch": 83478763, "ratio": 1.0025,
+        "sha256": "a2bb88c7a3683f935a6d77a56d8caebb6dc24d4f2691437737ddd06ae31ba6c1", "bytes_per_launch": 83478763, "ratio": 1.0025,
         "workload": "8B Q8_0 decode step, batch 1"},
     "qmv_kernel<Q8_0, 1, 64, 1, 2, 8, 2, false, float, false>": {
         "key": "kernel_q8_0_o",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "6bcfb1eff766e89f929c39687979215f0204c616a5d202918094d70e97ffa3ee", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
+        "sha256": "a2bb88c7a3683f935a6d77a56d8caebb6dc24d4f2691437737ddd06ae31ba6c1", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
     "qmv_kernel_c<Q8_0, 4, 16, 2, float, 1>": {
         "key": "kernel_c16_q8_0_down",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "6bcfb1eff766e89f929c39687979215f0204c616a5d202918094d70e97ffa3ee", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
+        "sha256": "a2bb88c7a3683f935a6d77a56d8caebb6dc24d4f2691437737ddd06ae31ba6c1", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
     "i8_stream_kernel": {
         "key": "i8_stream",
         "sources": ["bandwidth_bound_block_amd/csrc/qmv_int8.hip", "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-        "sha256": "81978a7bca22558b217b0ab15b2b8605fd4d0ef30f2a174995853ac355049531", "ratio": 1.0380,
+        "sha256": "0cae04abbe99a25c07c77728d94fb5116435cb8e707e10420958edea0fdaccb3", "ratio": 1.0380,
         "workload": "Qwen3-0.6B int8 step (28 layers + lm_head), batch 1, per-matrix launches"},
 }
 
@@ -150,7 +150,8 @@ def _dense_sweep(torch, qmv, wl, fmt, batch, layers, layer_mats, head, tagbase, 
     """fuse: optional list of (fused_name, [member names]) whose rows are
     stored concatenated (same input vector), e.g. q||k||v and gate||up."""
     import numpy as np
-    cfn = {"q8_0": qmv.lib().qmv_q8_0, "q4_0": qmv.lib().qmv_q4_0, "q4_1": qmv.lib().qmv_q4_1}[fmt]
+    cfn = {"q8_0": qmv.lib().qmv_q8_0, "q4_0": qmv.lib().qmv_q4_0, "q4_1": qmv.lib().qmv_q4_1,
+           "q4_k": qmv.lib().qmv_q4_k}[fmt]
     sw = Sweep(name, batch)
     dev = "cuda:0"
     t0 = time.time()
@@ -745,7 +746,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--sweeps", default="all",
-                    help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,int8,moe, or of "
+                    help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,q4_k,int8,moe, or of "
                          "FMT@B / FMT@Bf / FMT@1g (one 8B sweep of format FMT at batch B, f: row-fused layout, "
                          "1g: batch 1 with one launch per dependency level)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing")
@@ -820,7 +821,7 @@ def main():
                                           f"timed once, x32, + lm_head); per column at batch B: B times this")
 
     names = [] if args.sweeps == "none" else (
-        ["c1", "q8_0", "q4_0", "q4_1", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
+        ["c1", "q8_0", "q4_0", "q4_1", "q4_k", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
         if "@" in nm:
@@ -865,6 +866,13 @@ def main():
                              (8, True)):
                 s = build_llama(torch, qmv, wl, nm, B, fused=fused)
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+                del s
+                torch.cuda.empty_cache()
+        elif nm == "q4_k":
+            o = oracle_for(nm, lambda: dense_oracle(nm))
+            for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
+                s = build_llama(torch, qmv, wl, nm, B, fused=fused)
+                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph), o if B == 1 else None)
                 del s
                 torch.cuda.empty_cache()
         elif nm == "int8":

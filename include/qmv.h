@@ -74,7 +74,7 @@ extern "C" {
 
 #define QMV_ABI_VERSION 1
 
-typedef enum { QMV_Q8_0 = 0, QMV_Q4_0 = 1, QMV_Q4_1 = 2 } qmv_fmt;
+typedef enum { QMV_Q8_0 = 0, QMV_Q4_0 = 1, QMV_Q4_1 = 2, QMV_Q4_K = 3 } qmv_fmt;
 
 enum {
     QMV_OK = 0,
@@ -111,6 +111,31 @@ int32_t qmv_q4_0(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
                  float* y, int64_t ldy, void* stream);
 int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
+                 const float* x, int64_t ldx, int32_t batch,
+                 float* y, int64_t ldy, void* stream);
+
+/*
+ * Q4_K float matvec, y[b][i] = sum_j DEQ(W)[i][j] * x[b][j] ([NST] Sec.
+ * "The Unified Quant Core" names Q4_K among the core's formats; its layout
+ * is not on the pages and is read here as the ggml-compatible one):
+ * 256-weight super-blocks of 144 bytes, fp16 d and dmin, eight 6-bit
+ * sub-block scales sc_s and minimums mn_s packed in 12 bytes, 128 bytes of
+ * 4-bit codes; w_{32s+i} = d*sc_s*c - dmin*mn_s (the byte and bit positions
+ * are stated with the kernel, qmv_q4k.hip).
+ *   W       n_rows rows of n_cols/256 super-blocks; 16-byte aligned.
+ *   n_cols  >= 256 and a multiple of 256; at most 36352 (one activation row
+ *           staged in LDS, as for the FMA kernels above).
+ *   x, batch, y as qmv_q8_0.
+ * Each weight is dequantized on its own in fp32 (exact scale products, one
+ * rounding), so the accuracy bound holds on every input.  Deterministic; a
+ * column's result is the same bitwise at every batch width.
+ * Errors: QMV_EINVAL (as qmv_q8_0, with multiples of 256), QMV_EALIGN (W
+ * not 16-byte aligned, x or y not 4-byte aligned), QMV_EHIP.
+ * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q4_K (matvec on
+ * QMV_PATH_AUTO or QMV_PATH_FMA; QMV_PATH_MFMA gives QMV_EUNSUPPORTED); the
+ * MoE entry points and qmv_chain do not (QMV_EUNSUPPORTED).
+ */
+int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
                  float* y, int64_t ldy, void* stream);
 
@@ -375,7 +400,8 @@ int32_t qmv_chain_noalloc(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_
 /*
  * Dequantize a whole matrix to fp32: out[i][j] = DEQ(W)[i][j], exactly (every
  * Q8_0/Q4_0 value and every Q4_1 value d*c + m whose bits span <= 24 is
- * representable in fp32; otherwise it is rounded to nearest even).  A test
+ * representable in fp32; otherwise it is rounded to nearest even; a Q4_K
+ * value d*sc*c - dmin*mn is its exact value rounded once).  A test
  * and inspection aid ([NST] Sec. "The Unified Quant Core": the per-format
  * block decoder maps a stored block to its values).
  *   out  fp32 [n_rows][n_cols]; 4-byte aligned.

@@ -203,6 +203,64 @@ def test_roundtrip_q4_1(oracle_lib):
     assert np.all(np.abs(blk - deq) <= bound[..., None] * (1 + 1e-9) + 1e-300)
 
 
+def _q4k_affine(o, Wq, N, K):
+    """Per sub-block (a, b) with DEQ = a c - b, probed through the oracle:
+    the same super-blocks with every code 0 give -b, with every code 1 give
+    a - b."""
+    ns = K // 256
+    sb = Wq.reshape(N, ns, 144)
+    z = sb.copy()
+    z[..., 16:] = 0x00
+    one = sb.copy()
+    one[..., 16:] = 0x11
+    d0 = o.dequant("q4_k", z.reshape(N, -1), N, K).reshape(N, ns, 8, 32)[..., 0]
+    d1 = o.dequant("q4_k", one.reshape(N, -1), N, K).reshape(N, ns, 8, 32)[..., 0]
+    return d1 - d0, -d0
+
+
+def test_roundtrip_q4_k(oracle_lib):
+    """Encoder round trip: every weight within half a code step of its
+    sub-block's grid {a c - b}, plus the distance by which it lies outside
+    the grid's ends; Gaussian rows keep an rms error below a tenth of the
+    weights' spread; the special rows (all-zero, constant, scale underflow)
+    decode as expected."""
+    g = np.random.default_rng(4321)
+    N, K = 24, 512
+    W = g.standard_normal((N, K)) * 0.02
+    W[0, :256] = 0.0                        # all-zero super-block
+    W[1, :32] = 3.0                         # constant positive sub-block
+    W[2, 256:] = g.standard_normal(256) * 1e-9   # scales underflow to fp16 zero
+    W[3, :256] = -np.abs(W[3, :256])        # all non-positive
+    W[4, 256:] = np.abs(W[4, 256:])         # all non-negative: minimums 0
+    W = W.astype(np.float32)
+    Wq = wl.encode_q4_k(W)
+    assert Wq.shape == (N, K // 256 * 144)
+    deq = oracle_lib.dequant("q4_k", Wq, N, K).reshape(N, K // 256, 8, 32)
+    a, b = _q4k_affine(oracle_lib, Wq, N, K)
+    w = W.astype(np.float64).reshape(N, K // 256, 8, 32)
+    lo, hi = -b, 15 * a - b
+    outside = np.maximum(0, np.maximum(w - hi[..., None], lo[..., None] - w))
+    assert np.all(np.abs(w - deq) <= a[..., None] / 2 * (1 + 1e-9) + outside + 1e-300)
+    assert np.all(deq[0, 0] == 0) and np.all(deq[2, 1] == 0)
+    assert np.all(b[4, 1] == 0)
+    gauss = np.ones(N, dtype=bool)
+    gauss[:5] = False
+    rms = np.sqrt(np.mean((w[gauss] - deq[gauss]) ** 2))
+    assert rms < 0.1 * 0.02, rms
+
+
+def test_zero_heavy_q4_k_is_exact_zero(oracle_lib):
+    """The zero-heavy Q4_K rows decode to exactly 0 off the sparse columns
+    (d sc k - dmin sc k with dmin = d) and carry the activations' 1e3 / 1e-3
+    split."""
+    N, K = 12, 1024
+    Wq, x = wl.zero_heavy("q4_k", "t/pins/zh", N, K, B=2)
+    deq = oracle_lib.dequant("q4_k", Wq, N, K)
+    small = (np.arange(K) % 16) == 15
+    assert np.all(deq[:, ~small] == 0) and np.count_nonzero(deq[:, small]) > 0
+    assert np.all(np.abs(x[:, small]) < 0.1) and np.median(np.abs(x[:, ~small])) > 100
+
+
 # ------------------------------------------------------------------ exact brute force
 def _random_blocks(g, fmt, N, K):
     """Random stored bytes with finite, varied scales (random codes)."""
@@ -254,6 +312,68 @@ def test_matvec_exact_rational(oracle_lib, fmt, K):
             err = abs(Fraction(y[b, i]) - exact)
             assert err <= Fraction(K) * Fraction(2) ** -52 * sabs, (fmt, i, b)
             assert abs(Fraction(S[b, i]) - sabs) <= Fraction(K) * Fraction(2) ** -52 * sabs
+
+
+def _random_super_blocks(g, N, K):
+    """Random Q4_K bytes with finite fp16 d and dmin (subnormals included)."""
+    raw = g.integers(0, 256, size=(N, K // 256, 144), dtype=np.uint8)
+    for off in (0, 2):
+        h = (g.integers(0, 2, size=(N, K // 256)) << 15) | (g.integers(0, 31, size=(N, K // 256)) << 10) | \
+            g.integers(0, 1024, size=(N, K // 256))
+        raw[..., off] = h & 0xFF
+        raw[..., off + 1] = h >> 8
+    return raw.reshape(N, -1)
+
+
+def _exact_dequant_q4k(sb):
+    """Exact rational DEQ of one Q4_K super-block, from the layout reading:
+    the 6-bit fields are read bit by bit out of the 96-bit field area."""
+    sb = [int(v) for v in sb]
+
+    def f16(lo, hi):
+        return Fraction(float(np.array([lo | (hi << 8)], dtype=np.uint16).view(np.float16)[0]))
+
+    d, dmin = f16(sb[0], sb[1]), f16(sb[2], sb[3])
+    fb = sb[4:16]
+
+    def bits(byte, lo, n):
+        return (fb[byte] >> lo) & ((1 << n) - 1)
+
+    out = []
+    for s in range(8):
+        if s < 4:
+            sc, mn = bits(s, 0, 6), bits(s + 4, 0, 6)
+        else:
+            sc = bits(s + 4, 0, 4) | (bits(s - 4, 6, 2) << 4)
+            mn = bits(s + 4, 4, 4) | (bits(s, 6, 2) << 4)
+        for i in range(32):
+            q = sb[16 + 32 * (s // 2) + i]
+            c = (q >> 4) if s % 2 else (q & 15)
+            out.append(d * sc * c - dmin * mn)
+    return out
+
+
+@pytest.mark.parametrize("K", [256, 512])
+def test_matvec_exact_rational_q4k(oracle_lib, K):
+    """Random super-blocks: the oracle's double sums are within K ulps
+    (relative to sum |w x|) of the exact rational matvec, and its DEQ
+    rounds the exact weight once at most."""
+    g = np.random.default_rng(99 + K)
+    N, B = 3, 2
+    Wq = _random_super_blocks(g, N, K)
+    x = (g.standard_normal((B, K)) * np.exp(g.uniform(-8, 8, size=(B, K)))).astype(np.float32)
+    y, S = oracle_lib.matvec("q4_k", Wq, N, K, x)
+    deq = oracle_lib.dequant("q4_k", Wq, N, K)
+    rows = Wq.reshape(N, K // 256, 144)
+    for i in range(N):
+        w = sum((_exact_dequant_q4k(rows[i, k]) for k in range(K // 256)), [])
+        for j in range(K):
+            assert deq[i, j] == float(w[j]), (i, j)      # float() rounds to nearest
+        for b in range(B):
+            exact = sum(wi * Fraction(float(xi)) for wi, xi in zip(w, x[b]))
+            sabs = sum(abs(wi * Fraction(float(xi))) for wi, xi in zip(w, x[b]))
+            err = abs(Fraction(y[b, i]) - exact)
+            assert err <= Fraction(K + 1) * Fraction(2) ** -52 * sabs, (i, b)
 
 
 @pytest.mark.parametrize("fmt", FMTS)

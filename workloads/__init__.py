@@ -14,6 +14,13 @@ and encodes them into the stored block formats, as the input recipe says:
                                           c = clamp(round((w - m) / d), 0, 15)
   "round" is round-half-away-from-zero against the stored fp16 scale; the
   fp16 conversion is numpy's IEEE round-to-nearest-even.
+    Q4_K  per 256-weight super-block of eight 32-weight sub-blocks s:
+          lo_s = min(0, min w), step_s = (max w - lo_s) / 15;
+          d = fp16(max_s step_s / 63), dmin = fp16(max_s (-lo_s) / 63),
+          sc_s = clamp(round(step_s / d), 0, 63),
+          mn_s = clamp(round(-lo_s / dmin), 0, 63),
+          c = clamp(round((w + dmin mn_s) / (d sc_s)), 0, 15)
+          (a zero scale gives zero fields).
 * activations x ~ N(0, 1) float32;
 * int8 weights / activations uniform in [-127, 127]; per-row requant
   multipliers uniform in [2^30, 2^31 - 1] and shifts uniform in [0, 20];
@@ -26,11 +33,15 @@ and encodes them into the stored block formats, as the input recipe says:
   with activations of magnitude ~1e3 on the zero weights and ~1e-3 on the
   others, so that sum_j |w_j x_j| is tiny next to sum_j |x_j|.  Q8_0 codes
   0, Q4_0 codes 8, Q4_1 codes k with d*k + m = 0 exactly (d with few
-  significant bits and m = -d*k, both exact in fp16).
+  significant bits and m = -d*k, both exact in fp16), Q4_K codes k_s with
+  dmin = d and mn_s = sc_s k_s (d sc_s k_s - dmin mn_s = 0 exactly).
 
 Byte layouts (ggml-compatible, little-endian): Q8_0 = [d:fp16][q:int8 x32];
 Q4_0 = [d:fp16][qs:16 bytes], element j<16 in the low nibble of qs[j] and
-element j+16 in its high nibble; Q4_1 = [d:fp16][m:fp16][qs:16 bytes].
+element j+16 in its high nibble; Q4_1 = [d:fp16][m:fp16][qs:16 bytes];
+Q4_K = [d:fp16][dmin:fp16][b:12 bytes of 6-bit sc_s, mn_s][q:128 bytes],
+sub-block 2p in the low nibbles of q[32p..32p+31] and 2p+1 in their high
+nibbles (the packing of b is the one the oracle's reading states).
 
 Seeds: numpy PCG64 seeded with the first 8 bytes (little-endian) of
 SHA-256("qmv/<tag>").
@@ -39,7 +50,18 @@ import hashlib
 
 import numpy as np
 
-BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20}
+BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20}   # per 32 weights
+SUPER_BLOCK = {"q4_k": (256, 144)}                    # (weights, bytes)
+
+
+def row_bytes(fmt, K):
+    """Stored bytes of one row of K weights."""
+    if fmt in SUPER_BLOCK:
+        w, b = SUPER_BLOCK[fmt]
+        assert K % w == 0, (fmt, K)
+        return K // w * b
+    assert K % 32 == 0, (fmt, K)
+    return K // 32 * BLOCK_BYTES[fmt]
 
 
 def seed_for(tag: str) -> int:
@@ -158,7 +180,46 @@ def encode_q4_1(Wf):
     return out.reshape(N, -1)
 
 
-ENCODERS = {"q8_0": encode_q8_0, "q4_0": encode_q4_0, "q4_1": encode_q4_1}
+def _pack_q4k(d16, dmin16, sc, mn, c):
+    """Fields -> uint8 [..., 144]: d16, dmin16 [...] fp16; sc, mn [..., 8]
+    in 0..63; c [..., 256] codes 0..15 in weight order."""
+    sc = sc.astype(np.uint8)
+    mn = mn.astype(np.uint8)
+    b = np.empty(sc.shape[:-1] + (12,), dtype=np.uint8)
+    b[..., 0:4] = (sc[..., 0:4] & 63) | ((sc[..., 4:8] >> 4) << 6)
+    b[..., 4:8] = (mn[..., 0:4] & 63) | ((mn[..., 4:8] >> 4) << 6)
+    b[..., 8:12] = (sc[..., 4:8] & 15) | ((mn[..., 4:8] & 15) << 4)
+    cs = c.astype(np.uint8).reshape(c.shape[:-1] + (4, 2, 32))   # [pair][lo/hi][i]
+    q = (cs[..., 0, :] | (cs[..., 1, :] << 4)).reshape(c.shape[:-1] + (128,))
+    lead = d16.shape
+    return np.concatenate([d16.view(np.uint8).reshape(lead + (2,)), dmin16.view(np.uint8).reshape(lead + (2,)),
+                           b, q], axis=-1)
+
+
+def encode_q4_k(Wf):
+    """float [N, K] -> uint8 [N, K/256*144] (super-blocks of 6-bit
+    sub-block scales and minimums)."""
+    Wf = np.asarray(Wf)
+    N, K = Wf.shape
+    assert K % 256 == 0
+    ns = K // 256
+    sub = Wf.reshape(N, ns, 8, 32).astype(np.float64)
+    lo = np.minimum(sub.min(axis=-1), 0.0)
+    step = (sub.max(axis=-1) - lo) / 15.0
+    d16 = _f16(step.max(axis=-1) / 63.0)
+    dmin16 = _f16((-lo).max(axis=-1) / 63.0)
+    d = d16.astype(np.float64)[..., None]
+    dmin = dmin16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where(d != 0, np.clip(_round_half_away(step / d), 0, 63), 0)
+        mn = np.where(dmin != 0, np.clip(_round_half_away(-lo / dmin), 0, 63), 0)
+        ds = (d * sc)[..., None]
+        dm = (dmin * mn)[..., None]
+        c = np.where(ds != 0, np.clip(_round_half_away((sub + dm) / ds), 0, 15), 0)
+    return _pack_q4k(d16, dmin16, sc, mn, c.reshape(N, ns, 256)).reshape(N, ns * 144)
+
+
+ENCODERS = {"q8_0": encode_q8_0, "q4_0": encode_q4_0, "q4_1": encode_q4_1, "q4_k": encode_q4_k}
 
 
 def quant_weights(fmt, tag, N, K, std=0.02, chunk_rows=8192):
@@ -167,7 +228,7 @@ def quant_weights(fmt, tag, N, K, std=0.02, chunk_rows=8192):
     The draw is one PCG64 stream, so the bytes do not depend on chunk_rows."""
     enc = ENCODERS[fmt]
     g = rng(tag)
-    out = np.empty((N, K // 32 * BLOCK_BYTES[fmt]), dtype=np.uint8)
+    out = np.empty((N, row_bytes(fmt, K)), dtype=np.uint8)
     for r0 in range(0, N, chunk_rows):
         r1 = min(N, r0 + chunk_rows)
         w = g.standard_normal((r1 - r0, K), dtype=np.float32) * np.float32(std)
@@ -198,18 +259,28 @@ MOE_HIDDEN, MOE_FFN, MOE_EXPERTS, MOE_TOPK, MOE_LAYERS = 2048, 768, 128, 8, 48
 
 
 def block_bytes(fmt, N, K):
-    return N * (K // 32) * BLOCK_BYTES[fmt]
+    return N * row_bytes(fmt, K)
 
 
 def zero_heavy(fmt, tag, N, K, B=1, every=16):
-    """Stored bytes [N][K/32 * block bytes] and activations [B][K] float32
-    of the zero-heavy kind (module docstring): column j carries nonzero
-    codes only when j % every == every - 1 (the "small" columns)."""
+    """Stored bytes [N][row bytes] and activations [B][K] float32 of the
+    zero-heavy kind (module docstring): column j carries nonzero codes only
+    when j % every == every - 1 (the "small" columns)."""
     g = rng(tag)
     nb = K // 32
     small = (np.arange(K) % every) == every - 1
     x = g.standard_normal((B, K)).astype(np.float32)
     x *= np.where(small, np.float32(1e-3), np.float32(1e3))
+    if fmt == "q4_k":
+        ns = K // 256
+        e = g.integers(-10, 3, size=(N, ns))
+        d16 = np.ldexp(1.0 + g.integers(0, 8, size=(N, ns)) / 8.0, e).astype(np.float16)   # <= 4 bits
+        sc = g.integers(1, 5, size=(N, ns, 8))
+        k = np.minimum(g.integers(0, 16, size=(N, ns, 8)), 63 // sc)
+        codes = np.repeat(k, 32, axis=2).reshape(N, K)
+        codes[:, small] = g.integers(0, 16, size=(N, int(small.sum())))
+        out = _pack_q4k(d16, d16, sc, sc * k, codes.reshape(N, ns, 256))
+        return out.reshape(N, ns * 144), x
     e = g.integers(-10, 3, size=(N, nb))
     frac = g.integers(0, 8, size=(N, nb))
     mag = np.ldexp(1.0 + frac / 8.0, e)                     # <= 4 significant bits
