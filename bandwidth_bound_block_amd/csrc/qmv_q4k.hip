@@ -41,14 +41,74 @@ struct Q4KGroup {
 __device__ __forceinline__ u32x4 ld16_aligned(const uint8_t* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // The 32 codes of one Q4_K sub-block as a dot_multi format: element 4 i + k
-// is the low nibble of byte k of c[i]; the factor of code c is fma(d, c, m)
-// with d = d sc and m = -dmin mn (the weight itself).
+// is byte k of c[i], the code already isolated in its byte (as c, or as
+// 16 c in the high half); the factor is fma(d, byte, m), the weight itself,
+// with d = d sc (or d sc / 16) and m = -dmin mn.
 struct Q4KSub {};
 template <>
 __device__ __forceinline__ void chunk_codes<Q4KSub>(const uint32_t (&c)[8], int i, float d, float m, float (&q)[4]) {
-    const uint32_t v = c[i] & 0x0f0f0f0fu;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) q[k] = __builtin_fmaf(d, ubyte(v, k), m);
+    for (int k = 0; k < 4; ++k) q[k] = __builtin_fmaf(d, ubyte(c[i], k), m);
+}
+
+// Staged activations: x[b][64 g + e] at xs[b][g][e] with groups padded to
+// 68 floats, so the 16-byte reads of lanes on consecutive groups start 4
+// banks apart and a wave's read is free of bank conflicts (with 32-weight
+// blocks of 36 floats, lanes two blocks apart would collide two ways).
+constexpr int kQ4KXPad = 68;
+
+// Stages w of the B columns xcol[b][0..K) into LDS in that layout; loads in
+// batches of 4 per thread before any is stored.  vec: every column aligned
+// for 4-element loads.  Ends with a barrier.
+template <int B, int NT, class XT>
+__device__ __forceinline__ void q4k_stage_x(const XT* const (&xcol)[B], int K, float* xs, bool vec) {
+    const int G = K >> 6;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float* dst = xs + b * G * kQ4KXPad;
+        const XT* src = xcol[b];
+        if (vec) {
+            const int K4 = K >> 2;
+            auto put = [&](int c, const float4& v) {
+                const int e = 4 * c;
+                *reinterpret_cast<float4*>(dst + (e >> 6) * kQ4KXPad + (e & 63)) = v;
+            };
+            for (int c0 = tid; c0 < K4; c0 += 4 * NT) {
+                const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
+                const float4 v0 = XIn<XT>::load4(src + 4 * c0);
+                const float4 v1 = XIn<XT>::load4(src + 4 * min(c1, K4 - 1));
+                const float4 v2 = XIn<XT>::load4(src + 4 * min(c2, K4 - 1));
+                const float4 v3 = XIn<XT>::load4(src + 4 * min(c3, K4 - 1));
+                put(c0, v0);
+                if (c1 < K4) put(c1, v1);
+                if (c2 < K4) put(c2, v2);
+                if (c3 < K4) put(c3, v3);
+            }
+        } else {
+            auto put = [&](int e, float v) { dst[(e >> 6) * kQ4KXPad + (e & 63)] = v; };
+            for (int e0 = tid; e0 < K; e0 += 4 * NT) {
+                const int e1 = e0 + NT, e2 = e0 + 2 * NT, e3 = e0 + 3 * NT;
+                const float v0 = XIn<XT>::load1(src + e0);
+                const float v1 = XIn<XT>::load1(src + min(e1, K - 1));
+                const float v2 = XIn<XT>::load1(src + min(e2, K - 1));
+                const float v3 = XIn<XT>::load1(src + min(e3, K - 1));
+                put(e0, v0);
+                if (e1 < K) put(e1, v1);
+                if (e2 < K) put(e2, v2);
+                if (e3 < K) put(e3, v3);
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Hides a value's bits from the optimizer: a masked word then converts with
+// one byte-select convert per element instead of a bit-field extract and a
+// convert.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
 }
 
 // The 6-bit scale and minimum of sub-block s (0..7); h.y, h.z, h.w hold
@@ -63,20 +123,22 @@ __device__ __forceinline__ void q4k_scale_min(const u32x4& h, int s, int& sc, in
     mn = s < 4 ? mn_lo : mn_hi;
 }
 
+// A wave step covers RW = 64 / LPR rows, one per segment of LPR lanes.
+// (Two rows per lane, each staged activation read feeding both, measured
+// slower at every batch width: 123-228 VGPRs against 63-160.)
 template <int B, int LPR, int NW, class XT>
 __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
                                                        const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
                                                        int64_t ldy, int xvec) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
-    float* xs = lds;                          // [B][8 nsb][kXPad]
-    constexpr int RW = 64 / LPR;              // rows per wave step
+    float* xs = lds;                          // [B][4 nsb][kQ4KXPad]
+    constexpr int RW = 64 / LPR;              // rows per tile
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int seg = lane / LPR;
     const int li = lane % LPR;
     const int G = 4 * nsb;                    // 64-weight groups per row
     const int T = (G + LPR - 1) / LPR;        // steps per row
-    const int nb = 8 * nsb;                   // 32-weight sub-blocks per row
     const int64_t pitch = (int64_t)nsb * kQ4KBytes;
     const int64_t ntiles = (N + RW - 1) / RW;
     const int64_t wstride = (int64_t)gridDim.x * NW;
@@ -85,9 +147,10 @@ __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict_
         const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
         const int64_t row = min(tile * RW + seg, N - 1);
         const uint8_t* sb = W + row * pitch + (int64_t)(g >> 2) * kQ4KBytes;
+        const int coff = 16 + 32 * (g & 3);
         r.h = ld16_aligned(sb);
-        r.c0 = ld16_aligned(sb + 16 + 32 * (g & 3));
-        r.c1 = ld16_aligned(sb + 32 + 32 * (g & 3));
+        r.c0 = ld16_aligned(sb + coff);
+        r.c1 = ld16_aligned(sb + coff + 16);
     };
 
     float acc[B];
@@ -97,9 +160,9 @@ __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict_
         const int g = li + LPR * t;
         const bool valid = g < G;
         const int gc = valid ? g : G - 1;
+        const int part = gc & 3;
         const float d = half_bits_to_float(r.h.x);
         const float dmin = half_bits_to_float(r.h.x >> 16);
-        const int part = gc & 3;
         int sca, mna, scb, mnb;
         q4k_scale_min(r.h, 2 * part, sca, mna);
         q4k_scale_min(r.h, 2 * part + 1, scb, mnb);
@@ -114,12 +177,16 @@ __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict_
         for (int b = 0; b < B; ++b) s[b] = 0.f;
 #pragma unroll 1
         for (int h = 0; h < 2; ++h) {
-            const int sh = 4 * h;
-            const uint32_t c[1][8] = {{r.c0.x >> sh, r.c0.y >> sh, r.c0.z >> sh, r.c0.w >> sh, r.c1.x >> sh,
-                                       r.c1.y >> sh, r.c1.z >> sh, r.c1.w >> sh}};
-            const float fd[1] = {h ? db : da}, fm[1] = {h ? -mb : -ma};
+            // low nibbles as c; high nibbles in place, as 16 c, with the
+            // scale d sc / 16 (exact): the same products either way
+            const uint32_t mask = h ? 0xf0f0f0f0u : 0x0f0f0f0fu;
+            const uint32_t w8[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+            uint32_t c[1][8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) c[0][i] = opaque(w8[i] & mask);
+            const float fd[1] = {h ? db * 0.0625f : da}, fm[1] = {h ? -mb : -ma};
             float sh_dot[1][B];
-            dot_multi<Q4KSub, 1, B>(c, fd, fm, xs + (2 * gc + h) * kXPad, nb * kXPad, sh_dot, B);
+            dot_multi<Q4KSub, 1, B>(c, fd, fm, xs + gc * kQ4KXPad + 32 * h, G * kQ4KXPad, sh_dot, B);
 #pragma unroll
             for (int b = 0; b < B; ++b) s[b] += sh_dot[0][b];
         }
@@ -157,7 +224,7 @@ __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict_
         const XT* xcol[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) xcol[b] = x + b * ldx;
-        stage_x_cols<B, 64 * NW, XT>(xcol, nb, xs, B, xvec != 0);   // ends with a barrier
+        q4k_stage_x<B, 64 * NW, XT>(xcol, 256 * nsb, xs, xvec != 0);   // ends with a barrier
     }
     // Two register buffers used in turn; once the load cursor is past the
     // wave's last step, the step in hand is the last one: it is computed
@@ -207,7 +274,7 @@ template <int B, int LPR, int NW, class XT>
 int32_t q4k_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                    hipStream_t st) {
     auto kern = q4k_kernel<B, LPR, NW, XT>;
-    const size_t lds = (size_t)B * 8 * nsb * kXPad * sizeof(float);
+    const size_t lds = (size_t)B * 4 * nsb * kQ4KXPad * sizeof(float);
     size_t dyn_max = 0;
     if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv_q4_k", &dyn_max)) return e;
     if (lds > dyn_max) return fail(QMV_EINVAL, "qmv_q4_k: %zu bytes of staged activations exceed the LDS", lds);
@@ -220,16 +287,38 @@ int32_t q4k_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ld
     return check_launch("qmv_q4_k");
 }
 
-// Lanes per row: whole waves on rows of >= 64 groups (4096 columns), else
-// segments of 32 / 16 / 8 lanes so short rows leave few lanes idle.
+// Lanes per row: the widest split of 64 / 32 / 16 / 8 lanes that leaves at
+// most 1/16 of a row's lane-steps idle (wide splits keep more waves busy on
+// matrices of few rows), else the split with the fewest idle: 64 for 4096
+// columns (64 groups of 64 weights), 32 for 14336 (224 groups: 7 full
+// steps, where whole waves would leave half of the fourth step idle), 16
+// for 3072 (48 groups).
+inline int q4k_pick_lpr(int G) {
+    int best = 8;
+    int64_t best_idle = 1 << 30, best_span = 1;
+    for (const int l : {64, 32, 16, 8}) {
+        if (l > G && l != 8) continue;
+        const int64_t span = (G + l - 1) / l * l;   // lane-steps per row
+        const int64_t idle = span - G;
+        if (16 * idle <= span) return l;
+        if (idle * best_span < best_idle * span) {  // idle / span, exactly
+            best = l;
+            best_idle = idle;
+            best_span = span;
+        }
+    }
+    return best;
+}
+
 template <int B, int NW, class XT>
 int32_t q4k_launch_lpr(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                        hipStream_t st) {
-    const int G = 4 * nsb;
-    if (G >= 64) return q4k_launch<B, 64, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    if (G >= 32) return q4k_launch<B, 32, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    if (G >= 16) return q4k_launch<B, 16, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    return q4k_launch<B, 8, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    switch (q4k_pick_lpr(4 * nsb)) {
+    case 64: return q4k_launch<B, 64, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 32: return q4k_launch<B, 32, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 16: return q4k_launch<B, 16, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    default: return q4k_launch<B, 8, NW, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    }
 }
 
 template <class XT>
@@ -264,7 +353,7 @@ int32_t q4k_matvec_t(const char* name, const void* W, int64_t N, int64_t K, cons
     if (!aligned(y, 4)) return fail(QMV_EALIGN, "%s: y must be 4-byte aligned", name);
     if (!aligned(x, sizeof(XT))) return fail(QMV_EALIGN, "%s: x must be aligned to its element size", name);
     const int nsb = (int)(K / kQ4KWeights);
-    const int per_col = 8 * nsb * kXPad * (int)sizeof(float);
+    const int per_col = 4 * nsb * kQ4KXPad * (int)sizeof(float);
     if (per_col > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
     const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / per_col));

@@ -123,8 +123,8 @@ int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
  * 4-bit codes; w_{32s+i} = d*sc_s*c - dmin*mn_s (the byte and bit positions
  * are stated with the kernel, qmv_q4k.hip).
  *   W       n_rows rows of n_cols/256 super-blocks; 16-byte aligned.
- *   n_cols  >= 256 and a multiple of 256; at most 36352 (one activation row
- *           staged in LDS, as for the FMA kernels above).
+ *   n_cols  >= 256 and a multiple of 256; at most 38400 (one activation row
+ *           staged in LDS, 68 floats per 64 columns).
  *   x, batch, y as qmv_q8_0.
  * Each weight is dequantized on its own in fp32 (exact scale products, one
  * rounding), so the accuracy bound holds on every input.  Deterministic; a

@@ -88,6 +88,7 @@ def test_q4_k_argument_errors(qmv):
         ((A, 8, 256, A + 1, 256, 1, A, 8, None), EALIGN, "aligned"),
         ((A, 8, 256, A, 256, 1, A + 2, 8, None), EALIGN, "aligned"),
         ((A, 8, 64 * 1024 * 1024, A, 64 * 1024 * 1024, 1, A, 8, None), EINVAL, "LDS"),
+        ((A, 8, 38656, A, 38656, 1, A, 8, None), EINVAL, "LDS"),
     ]
     for args, code, word in cases:
         assert f(*args) == code, (args, qmv.last_error())

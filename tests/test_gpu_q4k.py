@@ -5,7 +5,7 @@ Float matvec: |y_gpu - y| <= 1e-4 * S + 1e-6 per output (S = sum_j |w_ij x_j|)
 against the fp64 dequantize-then-dot oracle, on encoded Gaussian weights,
 random super-block bytes (random codes, 6-bit fields and fp16 scales over
 their whole range) and the zero-heavy rows.  Shapes span every lane
-split of the kernel (8 / 16 / 32 / 64 lanes per row, from 2 to 224 groups
+split of the kernel (8 / 16 / 32 / 64 lanes per row, from 4 to 568 groups
 of 64 weights), rows in ragged counts against the workgroups, and the
 8B-shaped layer matrices at full size with sampled rows.  Dequantization is
 bitwise the fp32 rounding of the oracle's exact values; 16-bit activations
@@ -94,11 +94,13 @@ def test_q4k_hand_super_blocks(env, spec):
 
 
 # ------------------------------------------------------------------ shapes
-# (rows, columns): 1..4 super-blocks per row (8 / 16 lanes per row), 8 and
-# 16 (32 / 64 lanes), 56 = 14336 columns (224 groups: 3.5 steps of a wave,
-# a ragged last step), 142 = 36352 columns (the LDS limit at batch 1).
-SHAPES = [(1, 256), (7, 512), (37, 768), (130, 1024), (257, 2048), (65, 4096), (300, 4096), (5, 14336),
-          (33, 36352), (2100, 4096)]
+# (rows, columns): 1..4 super-blocks per row (8 / 16 lanes per row, 768
+# columns with a half-idle last step), 8 and 16 (32 / 64 lanes), 12 (16
+# lanes), 56 = 14336 columns (224 groups: 32 lanes, 7 steps), 142 = 36352
+# columns (64 lanes, a ragged ninth step), 150 = 38400 columns (the LDS
+# limit: one activation row per pass).
+SHAPES = [(1, 256), (7, 512), (37, 768), (130, 1024), (257, 2048), (61, 3072), (65, 4096), (300, 4096),
+          (5, 14336), (33, 36352), (3, 38400), (2100, 4096)]
 
 
 @pytest.mark.parametrize("B", [1, 2, 3, 5, 8])
