@@ -9,16 +9,18 @@ the integer semantics).
 
 Sources (the pages collected on the subject):
   * "One Native Stack for Private, Continuously-Learning AI", Sec. "The
-    Unified Quant Core" (formats Q8_0 34 B/32, Q4_0 18 B/32, Q4_K named
-    without its layout; one decoder per format) and the QLoRA Lemma
-    (y_i = sum_j DEQ(W)_ij x_j).
+    Unified Quant Core" (formats Q8_0 34 B/32, Q4_0 18 B/32, Q4_K 144 B/256
+    and Q6_K 210 B/256, the last two without their layouts; one decoder per
+    format) and the QLoRA Lemma (y_i = sum_j DEQ(W)_ij x_j).
   * "Economical Serving and the hanzo.ai Platform", Sec. 2.1 (one stream of
     the weights per token) and Sec. 2.2 (block decoder + traits record).
   * "Blue -- porting zen-nano (Qwen3-0.6B) to deterministic on-chain
     inference", "Quantization recipe" (int8 matvec, per-output-channel
     SaturatingRoundingDoublingHighMul then RoundingDivideByPOT to int8).
 
-Parity status: every function is pinned by the ``-m "not gpu"`` tests.
+Parity status: every function is pinned by the ``-m "not gpu"`` tests.  The
+Q4_K and Q6_K layouts are readings (ggml's); agreement with ggml itself is
+parity unpinned.
 """
 import ctypes
 import os
@@ -29,10 +31,10 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _SRC_PATH = os.path.join(_HERE, "qmv_oracle.c")
 
-Q8_0, Q4_0, Q4_1, Q4_K = 0, 1, 2, 3
-FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q4_k": Q4_K}
+Q8_0, Q4_0, Q4_1, Q4_K, Q6_K = 0, 1, 2, 3, 4
+FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q4_k": Q4_K, "q6_k": Q6_K}
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}      # per 32 weights
-SUPER_BLOCK = {Q4_K: (256, 144)}                   # (weights, bytes) per super-block
+SUPER_BLOCK = {Q4_K: (256, 144), Q6_K: (256, 210)}   # (weights, bytes) per super-block
 
 
 def row_bytes(fmt, K):

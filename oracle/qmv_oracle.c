@@ -24,22 +24,23 @@
  *          SaturatingRoundingDoublingHighMul(acc, mult[o]) followed by
  *          RoundingDivideByPOT(., shift[o]) to int8.
  * Where the pages leave a step open (byte layout, nibble order, Q4_1, the
- * Q4_K super-block layout, the bodies of the two gemmlowp functions, the
+ * Q4_K and Q6_K super-block layouts, the bodies of the two gemmlowp functions, the
  * int8 saturation range) this file takes the plainest reading; each such
  * place says "Reading:".
  *
  * Status: every function below is pinned by the CPU tests (hand-computed
  * blocks and super-blocks, exhaustive fp16 decode, exact-rational brute
  * force, integer closed forms and an independent big-integer mirror).  The
- * Q4_K layout itself is a reading: agreement with ggml's Q4_K files is
- * parity unpinned (no ggml file or output is available to compare with).
+ * Q4_K and Q6_K layouts themselves are readings: agreement with ggml's
+ * files is parity unpinned (no ggml file or output is available to compare
+ * with).
  */
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 #include <math.h>
 
-enum { QO_Q8_0 = 0, QO_Q4_0 = 1, QO_Q4_1 = 2, QO_Q4_K = 3 };
+enum { QO_Q8_0 = 0, QO_Q4_0 = 1, QO_Q4_1 = 2, QO_Q4_K = 3, QO_Q6_K = 4 };
 enum { QO_OK = 0, QO_EINVAL = 1, QO_ENOMEM = 2, QO_EOVERFLOW = 3 };
 
 /* IEEE 754 binary16 -> double, straight from the format definition:
@@ -156,10 +157,43 @@ void qo_dequant_superblock_q4k(const uint8_t* sb, double out[256]) {
     }
 }
 
+/* Q6_K: 256-weight super-blocks of 210 bytes, signed 6-bit codes.  [NST]
+ * Sec. "The Unified Quant Core" lists it as "signed 6b, 210B/256" without
+ * the byte layout.  Reading: the ggml-compatible layout (agreement with
+ * ggml itself is parity unpinned):
+ *   bytes 0-127    ql[0..127]  low 4 bits of the codes
+ *   bytes 128-191  qh[0..63]   high 2 bits of the codes
+ *   bytes 192-207  sc[0..15]   int8 scale of each 16-weight sub-block:
+ *                              weight e uses sc[e / 16]
+ *   bytes 208-209  d (fp16)
+ * Weight e = 128 h + 32 q + l (half h < 2, quarter q < 4, l < 32): its low
+ * 4 bits are the low nibble (q < 2) or high nibble (q >= 2) of
+ * ql[64 h + 32 (q mod 2) + l]; its high 2 bits are bits 2q, 2q+1 of
+ * qh[32 h + l]; the 6-bit code c in 0..63 gives
+ *   w_e = d * sc[e / 16] * (c - 32).
+ * The product has at most 11 + 8 + 6 significant bits: exact in double. */
+void qo_dequant_superblock_q6k(const uint8_t* sb, double out[256]) {
+    const uint8_t* ql = sb;
+    const uint8_t* qh = sb + 128;
+    const uint8_t* sc = sb + 192;
+    double d = qo_f16_to_f64(rd16(sb + 208));
+    int e;
+    for (e = 0; e < 256; ++e) {
+        int h = e / 128, q = (e % 128) / 32, l = e % 32;
+        int lbyte = ql[64 * h + 32 * (q % 2) + l];
+        int low4 = (q < 2) ? (lbyte & 0x0f) : (lbyte >> 4);
+        int high2 = (qh[32 * h + l] >> (2 * q)) & 3;
+        int c = low4 + 16 * high2;
+        int scale = (int)(int8_t)sc[e / 16];
+        out[e] = d * (double)scale * (double)(c - 32);
+    }
+}
+
 /* Bytes of one row of K weights; K must be a multiple of the format's
- * block (32, or 256 for Q4_K). */
+ * block (32, or 256 for the super-block formats). */
 int64_t qo_row_bytes(int fmt, int64_t K) {
     if (fmt == QO_Q4_K) return (K % 256) ? -1 : K / 256 * 144;
+    if (fmt == QO_Q6_K) return (K % 256) ? -1 : K / 256 * 210;
     if (qo_block_bytes(fmt) < 0 || K % 32) return -1;
     return K / 32 * qo_block_bytes(fmt);
 }
@@ -169,6 +203,10 @@ static void dequant_row(int fmt, const uint8_t* row, int64_t K, double* out) {
     int64_t b;
     if (fmt == QO_Q4_K) {
         for (b = 0; b < K / 256; ++b) qo_dequant_superblock_q4k(row + 144 * b, out + 256 * b);
+        return;
+    }
+    if (fmt == QO_Q6_K) {
+        for (b = 0; b < K / 256; ++b) qo_dequant_superblock_q6k(row + 210 * b, out + 256 * b);
         return;
     }
     for (b = 0; b < K / 32; ++b) qo_dequant_block(fmt, row + b * qo_block_bytes(fmt), out + 32 * b);

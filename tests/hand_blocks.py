@@ -58,8 +58,23 @@ def x_vec(kind):
     raise ValueError(kind)
 
 
+def _bytes_of(spec, n):
+    if isinstance(spec, list):
+        assert len(spec) == n
+        return [v & 0xFF for v in spec]
+    if spec.startswith("all:"):
+        return [int(spec[4:], 0) & 0xFF] * n
+    if spec == "k":
+        return list(range(n))
+    raise ValueError(spec)
+
+
 def super_block_bytes(spec):
-    """The 144 stored bytes of a Q4_K super-block spec."""
+    """The stored bytes of a super-block spec: 144 for Q4_K, 210 for Q6_K."""
+    if spec["fmt"] == "q6_k":
+        out = _bytes_of(spec["ql"], 128) + _bytes_of(spec["qh"], 64) + _bytes_of(spec["sc"], 16) + _u16(spec["d"])
+        assert len(out) == 210
+        return np.array(out, dtype=np.uint8)
     q = spec["q"]
     if q.startswith("all:"):
         qs = [int(q[4:], 16)] * 128

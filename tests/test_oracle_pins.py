@@ -62,16 +62,17 @@ def test_q4_nibble_order_distinguishes(oracle_lib):
 
 
 @pytest.mark.parametrize("spec", hb.load()["super_blocks"], ids=lambda s: s["id"])
-def test_hand_super_block_q4k(oracle_lib, spec):
-    """Q4_K super-blocks worked by hand (HB13-HB15): y of the oracle's
-    matvec and of its dequantizer, and HB14's per-sub-block weights and
-    6-bit fields."""
+def test_hand_super_block(oracle_lib, spec):
+    """Q4_K (HB13-HB15) and Q6_K (HB16-HB18) super-blocks worked by hand:
+    y of the oracle's matvec and of its dequantizer, and HB14's
+    per-sub-block weights and 6-bit fields."""
     o = oracle_lib
+    fmt = spec["fmt"]
     blk = hb.super_block_bytes(spec)
     x = hb.x_vec256(spec["x"])
-    y, S = o.matvec("q4_k", blk, 1, 256, x[None, :])
+    y, S = o.matvec(fmt, blk, 1, 256, x[None, :])
     assert y[0, 0] == float(spec["y"]), (spec["id"], y[0, 0])
-    w = o.dequant("q4_k", blk, 1, 256)[0]
+    w = o.dequant(fmt, blk, 1, 256)[0]
     assert float(np.dot(w, x.astype(np.float64))) == float(spec["y"])
     if "w" in spec:
         for s in range(8):
@@ -87,6 +88,35 @@ def test_q4k_nibble_order_distinguishes(oracle_lib):
         i = np.arange(32)
         assert np.array_equal(w[64 * p:64 * p + 32], ((32 * p + i) & 15).astype(np.float64))
         assert np.array_equal(w[64 * p + 32:64 * p + 64], ((32 * p + i) >> 4).astype(np.float64))
+
+
+def test_q6k_element_order(oracle_lib):
+    """HB17 (ql[k] = k, qh[k] = k, d = 1, scales 1) element by element:
+    w_e = c_e - 32 with c_e worked by hand from the layout reading."""
+    spec = [s for s in hb.load()["super_blocks"] if s["id"] == "HB17"][0]
+    w = oracle_lib.dequant("q6_k", hb.super_block_bytes(spec), 1, 256)[0]
+    cases = {
+        0: 0,            # h0 q0 l0: low nibble of ql[0] = 0, bits 0-1 of qh[0] = 0
+        37: 5 + 16,      # h0 q1 l5: low nibble of ql[37] = 5, bits 2-3 of qh[5] = 1
+        81: 1 + 16,      # h0 q2 l17: high nibble of ql[17] = 1, bits 4-5 of qh[17] = 1
+        127: 3 + 0,      # h0 q3 l31: high nibble of ql[63] = 3, bits 6-7 of qh[31] = 0
+        131: 3 + 48,     # h1 q0 l3: low nibble of ql[67] = 3, bits 0-1 of qh[35] = 3
+        178: 2 + 0,      # h1 q1 l18: low nibble of ql[114] = 2, bits 2-3 of qh[50] = 0
+        255: 7 + 0,      # h1 q3 l31: high nibble of ql[127] = 7, bits 6-7 of qh[63] = 0
+    }
+    for e, c in cases.items():
+        assert w[e] == c - 32, (e, w[e], c)
+
+
+def test_q6k_scale_per_16_weights(oracle_lib):
+    """HB18 (d = -0.5, every code 63): weight e uses the signed scale
+    sc[e / 16]; the sub-block boundaries 15 | 16 and 127 | 128 change it."""
+    spec = [s for s in hb.load()["super_blocks"] if s["id"] == "HB18"][0]
+    w = oracle_lib.dequant("q6_k", hb.super_block_bytes(spec), 1, 256)[0]
+    sc = spec["sc"]
+    for s_ in range(16):
+        assert np.all(w[16 * s_:16 * s_ + 16] == -0.5 * sc[s_] * 31), s_
+    assert w[15] == 1984.0 and w[16] == -1968.5 and w[127] == -124.0 and w[128] == 139.5
 
 
 def test_q4k_rows_and_one_hot(oracle_lib):
@@ -249,6 +279,45 @@ def test_roundtrip_q4_k(oracle_lib):
     assert rms < 0.1 * 0.02, rms
 
 
+def test_roundtrip_q6_k(oracle_lib):
+    """Q6_K encoder round trip: every weight within half a code step of its
+    sub-block's grid d sc (c - 32) (no clipping: the extreme maps to +-31
+    up to the rounding of sc and d); Gaussian rows keep an rms error below
+    a twentieth of the weights' spread; all-zero and underflowing
+    super-blocks decode to zero."""
+    g = np.random.default_rng(4322)
+    N, K = 24, 512
+    W = g.standard_normal((N, K)) * 0.02
+    W[0, :256] = 0.0
+    W[1, 256:] = g.standard_normal(256) * 1e-12
+    W[2, :16] = 5.0                        # constant sub-block beside small ones
+    W = W.astype(np.float32)
+    Wq = wl.encode_q6_k(W)
+    assert Wq.shape == (N, K // 256 * 210)
+    deq = oracle_lib.dequant("q6_k", Wq, N, K).reshape(N, K // 256, 16, 16)
+    # the step of each sub-block, probed through the oracle: every code 33
+    # (signed 1) gives d * sc
+    probe = Wq.reshape(N, K // 256, 210).copy()
+    probe[..., 0:128] = 0x11
+    probe[..., 128:192] = 0xAA
+    step = oracle_lib.dequant("q6_k", probe.reshape(N, -1), N, K).reshape(N, K // 256, 16, 16)[..., 0]
+    w = W.astype(np.float64).reshape(N, K // 256, 16, 16)
+    lo, hi = -32 * step, 31 * step
+    outside = np.maximum(0, np.maximum(w - hi[..., None], lo[..., None] - w))
+    assert np.all(np.abs(w - deq) <= step[..., None] / 2 * (1 + 1e-9) + outside + 1e-300)
+    assert np.all(deq[0, 0] == 0) and np.all(deq[1, 1] == 0)
+    rms = np.sqrt(np.mean((w[3:] - deq[3:]) ** 2))
+    assert rms < 0.05 * 0.02, rms
+
+
+def test_zero_heavy_q6_k_is_exact_zero(oracle_lib):
+    N, K = 12, 1024
+    Wq, x = wl.zero_heavy("q6_k", "t/pins/zh6", N, K, B=2)
+    deq = oracle_lib.dequant("q6_k", Wq, N, K)
+    small = (np.arange(K) % 16) == 15
+    assert np.all(deq[:, ~small] == 0) and np.count_nonzero(deq[:, small]) > 0
+
+
 def test_zero_heavy_q4_k_is_exact_zero(oracle_lib):
     """The zero-heavy Q4_K rows decode to exactly 0 off the sparse columns
     (d sc k - dmin sc k with dmin = d) and carry the activations' 1e3 / 1e-3
@@ -351,6 +420,58 @@ def _exact_dequant_q4k(sb):
             c = (q >> 4) if s % 2 else (q & 15)
             out.append(d * sc * c - dmin * mn)
     return out
+
+
+def _random_super_blocks_q6k(g, N, K):
+    """Random Q6_K bytes with a finite fp16 d (subnormals included)."""
+    raw = g.integers(0, 256, size=(N, K // 256, 210), dtype=np.uint8)
+    h = (g.integers(0, 2, size=(N, K // 256)) << 15) | (g.integers(0, 31, size=(N, K // 256)) << 10) | \
+        g.integers(0, 1024, size=(N, K // 256))
+    raw[..., 208] = h & 0xFF
+    raw[..., 209] = h >> 8
+    return raw.reshape(N, -1)
+
+
+def _exact_dequant_q6k(sb):
+    """Exact rational DEQ of one Q6_K super-block, from the layout reading:
+    the 6-bit codes reassembled as a bit string (4 low bits from the ql
+    area, 2 high bits from the qh area)."""
+    sb = [int(v) for v in sb]
+    d = Fraction(float(np.array([sb[208] | (sb[209] << 8)], dtype=np.uint16).view(np.float16)[0]))
+    out = []
+    for e in range(256):
+        half, rem = divmod(e, 128)
+        quarter, l = divmod(rem, 32)
+        byte = sb[64 * half + 32 * (quarter % 2) + l]
+        nib = (byte >> 4) if quarter >= 2 else (byte & 15)
+        top = (sb[128 + 32 * half + l] >> (2 * quarter)) & 3
+        scale = sb[192 + e // 16]
+        scale = scale - 256 if scale >= 128 else scale
+        out.append(d * scale * ((top << 4 | nib) - 32))
+    return out
+
+
+@pytest.mark.parametrize("K", [256, 512])
+def test_matvec_exact_rational_q6k(oracle_lib, K):
+    """Random Q6_K super-blocks: the oracle's DEQ is exact, and its double
+    sums are within (K+1) ulps (relative to sum |w x|) of the exact
+    rational matvec."""
+    g = np.random.default_rng(311 + K)
+    N, B = 3, 2
+    Wq = _random_super_blocks_q6k(g, N, K)
+    x = (g.standard_normal((B, K)) * np.exp(g.uniform(-8, 8, size=(B, K)))).astype(np.float32)
+    y, S = oracle_lib.matvec("q6_k", Wq, N, K, x)
+    deq = oracle_lib.dequant("q6_k", Wq, N, K)
+    rows = Wq.reshape(N, K // 256, 210)
+    for i in range(N):
+        w = sum((_exact_dequant_q6k(rows[i, k]) for k in range(K // 256)), [])
+        for j in range(K):
+            assert deq[i, j] == w[j], (i, j)      # exact in double
+        for b in range(B):
+            exact = sum(wi * Fraction(float(xi)) for wi, xi in zip(w, x[b]))
+            sabs = sum(abs(wi * Fraction(float(xi))) for wi, xi in zip(w, x[b]))
+            err = abs(Fraction(y[b, i]) - exact)
+            assert err <= Fraction(K + 1) * Fraction(2) ** -52 * sabs, (i, b)
 
 
 @pytest.mark.parametrize("K", [256, 512])

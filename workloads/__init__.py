@@ -21,6 +21,11 @@ and encodes them into the stored block formats, as the input recipe says:
           mn_s = clamp(round(-lo_s / dmin), 0, 63),
           c = clamp(round((w + dmin mn_s) / (d sc_s)), 0, 15)
           (a zero scale gives zero fields).
+    Q6_K  per 256-weight super-block of sixteen 16-weight sub-blocks s:
+          t_s = max|w| / 31, d = fp16(max_s t_s / 127),
+          sc_s = clamp(round(t_s / d), 0, 127),
+          c = clamp(round(w / (d sc_s)), -32, 31) + 32 (a zero scale gives
+          c = 32, the code of 0).
 * activations x ~ N(0, 1) float32;
 * int8 weights / activations uniform in [-127, 127]; per-row requant
   multipliers uniform in [2^30, 2^31 - 1] and shifts uniform in [0, 20];
@@ -34,14 +39,18 @@ and encodes them into the stored block formats, as the input recipe says:
   others, so that sum_j |w_j x_j| is tiny next to sum_j |x_j|.  Q8_0 codes
   0, Q4_0 codes 8, Q4_1 codes k with d*k + m = 0 exactly (d with few
   significant bits and m = -d*k, both exact in fp16), Q4_K codes k_s with
-  dmin = d and mn_s = sc_s k_s (d sc_s k_s - dmin mn_s = 0 exactly).
+  dmin = d and mn_s = sc_s k_s (d sc_s k_s - dmin mn_s = 0 exactly), Q6_K
+  code 32 (signed code 0).
 
 Byte layouts (ggml-compatible, little-endian): Q8_0 = [d:fp16][q:int8 x32];
 Q4_0 = [d:fp16][qs:16 bytes], element j<16 in the low nibble of qs[j] and
 element j+16 in its high nibble; Q4_1 = [d:fp16][m:fp16][qs:16 bytes];
 Q4_K = [d:fp16][dmin:fp16][b:12 bytes of 6-bit sc_s, mn_s][q:128 bytes],
 sub-block 2p in the low nibbles of q[32p..32p+31] and 2p+1 in their high
-nibbles (the packing of b is the one the oracle's reading states).
+nibbles (the packing of b is the one the oracle's reading states);
+Q6_K = [ql:128 bytes][qh:64 bytes][sc:16 x int8][d:fp16], code e = 128h +
+32q + l with its low 4 bits in ql[64h + 32(q mod 2) + l] (low nibble for
+q < 2, high for q >= 2) and its high 2 bits at bits 2q of qh[32h + l].
 
 Seeds: numpy PCG64 seeded with the first 8 bytes (little-endian) of
 SHA-256("qmv/<tag>").
@@ -51,7 +60,7 @@ import hashlib
 import numpy as np
 
 BLOCK_BYTES = {"q8_0": 34, "q4_0": 18, "q4_1": 20}   # per 32 weights
-SUPER_BLOCK = {"q4_k": (256, 144)}                    # (weights, bytes)
+SUPER_BLOCK = {"q4_k": (256, 144), "q6_k": (256, 210)}   # (weights, bytes)
 
 
 def row_bytes(fmt, K):
@@ -219,7 +228,40 @@ def encode_q4_k(Wf):
     return _pack_q4k(d16, dmin16, sc, mn, c.reshape(N, ns, 256)).reshape(N, ns * 144)
 
 
-ENCODERS = {"q8_0": encode_q8_0, "q4_0": encode_q4_0, "q4_1": encode_q4_1, "q4_k": encode_q4_k}
+def _pack_q6k(d16, sc, c):
+    """Fields -> uint8 [..., 210]: d16 [...] fp16; sc [..., 16] int8
+    values; c [..., 256] codes 0..63 in weight order."""
+    lead = d16.shape
+    c = c.astype(np.uint8).reshape(lead + (2, 4, 32))          # [half][quarter][l]
+    low, high = c & 15, c >> 4
+    ql = np.concatenate([low[..., 0, :] | (low[..., 2, :] << 4), low[..., 1, :] | (low[..., 3, :] << 4)],
+                        axis=-1).reshape(lead + (128,))
+    qh = (high[..., 0, :] | (high[..., 1, :] << 2) | (high[..., 2, :] << 4) | (high[..., 3, :] << 6)).reshape(
+        lead + (64,))
+    return np.concatenate([ql, qh, sc.astype(np.int8).view(np.uint8), d16.view(np.uint8).reshape(lead + (2,))],
+                          axis=-1)
+
+
+def encode_q6_k(Wf):
+    """float [N, K] -> uint8 [N, K/256*210] (signed 6-bit codes, int8
+    scales per 16 weights)."""
+    Wf = np.asarray(Wf)
+    N, K = Wf.shape
+    assert K % 256 == 0
+    ns = K // 256
+    sub = Wf.reshape(N, ns, 16, 16).astype(np.float64)
+    t = np.abs(sub).max(axis=-1) / 31.0
+    d16 = _f16(t.max(axis=-1) / 127.0)
+    d = d16.astype(np.float64)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        sc = np.where(d != 0, np.clip(_round_half_away(t / d), 0, 127), 0)
+        ds = (d * sc)[..., None]
+        q = np.where(ds != 0, np.clip(_round_half_away(sub / ds), -32, 31), 0)
+    return _pack_q6k(d16, sc, (q + 32).reshape(N, ns, 256)).reshape(N, ns * 210)
+
+
+ENCODERS = {"q8_0": encode_q8_0, "q4_0": encode_q4_0, "q4_1": encode_q4_1, "q4_k": encode_q4_k,
+            "q6_k": encode_q6_k}
 
 
 def quant_weights(fmt, tag, N, K, std=0.02, chunk_rows=8192):
@@ -271,6 +313,14 @@ def zero_heavy(fmt, tag, N, K, B=1, every=16):
     small = (np.arange(K) % every) == every - 1
     x = g.standard_normal((B, K)).astype(np.float32)
     x *= np.where(small, np.float32(1e-3), np.float32(1e3))
+    if fmt == "q6_k":
+        ns = K // 256
+        e = g.integers(-10, 3, size=(N, ns))
+        d16 = np.ldexp(1.0 + g.integers(0, 8, size=(N, ns)) / 8.0, e).astype(np.float16)
+        sc = g.integers(-128, 128, size=(N, ns, 16))
+        codes = np.full((N, K), 32, dtype=np.int64)
+        codes[:, small] = g.integers(0, 64, size=(N, int(small.sum())))
+        return _pack_q6k(d16, sc, codes.reshape(N, ns, 256)).reshape(N, ns * 210), x
     if fmt == "q4_k":
         ns = K // 256
         e = g.integers(-10, 3, size=(N, ns))
