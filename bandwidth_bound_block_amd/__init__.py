@@ -11,6 +11,7 @@ library has not been built.
 Entry points (same names as the C ABI):
   qmv_q8_0 / qmv_q4_0 / qmv_q4_1   float block-quantized matvec, batch 1..8
   qmv_q4_k                         the same for Q4_K super-blocks (256 weights, 144 bytes)
+  qmv_q6_k                         the same for Q6_K super-blocks (256 weights, 210 bytes)
   qmv_matvec_path                  the same with the kernel family chosen
                                    (PATH_AUTO / PATH_FMA / PATH_MFMA)
   qmv_matvec_xt                    the same with fp32, fp16 or bf16 activations
@@ -29,19 +30,19 @@ Entry points (same names as the C ABI):
 import ctypes
 import os
 
-__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
+__all__ = ["QmvError", "qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k", "qmv_q6_k", "qmv_matvec_path", "qmv_matvec_xt", "PATH_AUTO",
            "PATH_FMA", "PATH_MFMA", "X_F32", "X_F16", "X_BF16", "qmv_i8_requant", "qmv_i8_requant_lut",
            "qmv_moe", "qmv_moe_xt", "qmv_moe_swiglu", "qmv_moe_swiglu_xt", "qmv_moe_combine",
            "qmv_dequant", "qmv_stream_read", "qmv_chain", "qmv_chain_noalloc", "ChainStage", "CHAIN_WORKSPACE_BYTES", "abi_version", "last_error",
-           "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "Q4_K", "FORMATS", "BLOCK_BYTES", "row_bytes"]
+           "library_path", "lib", "Q8_0", "Q4_0", "Q4_1", "Q4_K", "Q6_K", "FORMATS", "BLOCK_BYTES", "row_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libqmv.so")
 
-Q8_0, Q4_0, Q4_1, Q4_K = 0, 1, 2, 3
-FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q4_k": Q4_K}
+Q8_0, Q4_0, Q4_1, Q4_K, Q6_K = 0, 1, 2, 3, 4
+FORMATS = {"q8_0": Q8_0, "q4_0": Q4_0, "q4_1": Q4_1, "q4_k": Q4_K, "q6_k": Q6_K}
 BLOCK_BYTES = {Q8_0: 34, Q4_0: 18, Q4_1: 20}      # per 32 weights
-SUPER_BLOCK = {Q4_K: (256, 144)}                   # (weights, bytes) per super-block
+SUPER_BLOCK = {Q4_K: (256, 144), Q6_K: (256, 210)}   # (weights, bytes) per super-block
 
 
 def row_bytes(fmt, n_cols):
@@ -80,7 +81,7 @@ def _open():
                           "(hipcc --offload-arch=gfx950) first")
     L = ctypes.CDLL(_LIB_PATH)
     P, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
-    for name in ("qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k"):
+    for name in ("qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k", "qmv_q6_k"):
         f = getattr(L, name)
         f.argtypes = [P, i64, i64, P, i64, i32, P, i64, P]
         f.restype = i32
@@ -211,10 +212,16 @@ def qmv_q4_k(W, n_rows, n_cols, x, y=None, stream=None):
     return _matvec(_lib.qmv_q4_k, Q4_K, W, n_rows, n_cols, x, y, stream)
 
 
+def qmv_q6_k(W, n_rows, n_cols, x, y=None, stream=None):
+    """y[b] = DEQ_Q6_K(W) @ x[b]; x float32 [K] or [B, K] (B <= 8), K a
+    multiple of 256."""
+    return _matvec(_lib.qmv_q6_k, Q6_K, W, n_rows, n_cols, x, y, stream)
+
+
 def qmv_matvec_path(fmt, W, n_rows, n_cols, x, path, y=None, stream=None):
-    """As qmv_q8_0/q4_0/q4_1/q4_k for format fmt (Q8_0, Q4_0, Q4_1, Q4_K or
-    its name) with the kernel family `path` (PATH_AUTO, PATH_FMA or
-    PATH_MFMA)."""
+    """As qmv_q8_0/q4_0/q4_1/q4_k/q6_k for format fmt (Q8_0, Q4_0, Q4_1,
+    Q4_K, Q6_K or its name) with the kernel family `path` (PATH_AUTO,
+    PATH_FMA or PATH_MFMA)."""
     f = FORMATS.get(fmt, fmt)
     if f not in FORMATS.values():
         raise ValueError(f"unknown format {fmt!r}")

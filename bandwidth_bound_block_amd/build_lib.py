@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libqmv.so")
-SOURCES = ["qmv_host.cpp", "qmv_blocks.hip", "qmv_fmt_q8_0.hip", "qmv_fmt_q4_0.hip", "qmv_fmt_q4_1.hip", "qmv_q4k.hip", "qmv_int8.hip", "qmv_chain.hip", "qmv_decode.hip", "qmv_mma.hip", "qmv_stream.hip"]
+SOURCES = ["qmv_host.cpp", "qmv_blocks.hip", "qmv_fmt_q8_0.hip", "qmv_fmt_q4_0.hip", "qmv_fmt_q4_1.hip", "qmv_q4k.hip", "qmv_q6k.hip", "qmv_int8.hip", "qmv_chain.hip", "qmv_decode.hip", "qmv_mma.hip", "qmv_stream.hip"]
 ARCH = "gfx950"
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 anywhere in the device code.

@@ -1,7 +1,7 @@
-// C entry points of the block-format (Q8_0 / Q4_0 / Q4_1 / Q4_K) matvec,
-// MoE and dequant paths: argument routing to the format's FormatOps table
-// (the kernels themselves are in qmv_blocks_impl.h, compiled once per
-// 32-weight format, and qmv_q4k.hip).
+// C entry points of the block-format (Q8_0 / Q4_0 / Q4_1 / Q4_K / Q6_K)
+// matvec, MoE and dequant paths: argument routing to the format's FormatOps
+// table (the kernels themselves are in qmv_blocks_impl.h, compiled once per
+// 32-weight format, qmv_q4k.hip and qmv_q6k.hip).
 #include "qmv_host.h"
 
 namespace qmv {
@@ -12,6 +12,7 @@ const FormatOps* format_ops(qmv_fmt fmt) {
     case QMV_Q4_0: return &ops_q4_0();
     case QMV_Q4_1: return &ops_q4_1();
     case QMV_Q4_K: return &ops_q4_k();
+    case QMV_Q6_K: return &ops_q6_k();
     default: return nullptr;
     }
 }

@@ -74,6 +74,7 @@ const FormatOps& ops_q8_0();
 const FormatOps& ops_q4_0();
 const FormatOps& ops_q4_1();
 const FormatOps& ops_q4_k();   // matvec and dequant only (qmv_q4k.hip)
+const FormatOps& ops_q6_k();   // matvec and dequant only (qmv_q6k.hip)
 // The table of fmt, or nullptr for an unknown format.
 const FormatOps* format_ops(qmv_fmt fmt);
 

@@ -1,0 +1,438 @@
+// Q6_K: 256-weight super-blocks of 210 bytes, batch 1..8 matvec and
+// dequantization, for gfx950.
+//
+// Format ("One Native Stack for Private, Continuously-Learning AI", Sec.
+// "The Unified Quant Core" lists Q6_K as signed 6-bit, 210 bytes per 256
+// weights, without its layout; the layout here is a reading, the
+// ggml-compatible one): bytes 0-127 ql (the codes' low 4 bits), 128-191 qh
+// (their high 2 bits), 192-207 sc[0..15] (int8, one per 16 weights), 208-209
+// d (fp16).  Weight e = 128 h + 32 q + l (h < 2, q < 4, l < 32) has its low
+// 4 bits in the low (q < 2) or high (q >= 2) nibble of ql[64 h + 32 (q & 1)
+// + l] and its high 2 bits at bits 2q, 2q + 1 of qh[32 h + l];
+//   w_e = d sc[e / 16] (c - 32).
+//
+// Mapping: a lane owns the 64 weights of one half h of a super-block with
+// l in [16 lh, 16 lh + 16), all four quarters: 16 bytes of ql for quarters
+// 0 and 2, 16 for quarters 1 and 3, 16 of qh, four scales and d.  A
+// super-block starts 2 (mod 4) bytes into W on every other index, so each
+// 16-byte piece is read as 4-byte-aligned words and re-aligned with
+// v_alignbyte; every load stays inside the matrix.  A code is rebuilt in
+// place as the signed byte 4 (c - 32) (its 4 low bits moved to bits 2-5,
+// its 2 high bits to bits 6-7 with the top bit flipped), so one
+// sign-extending convert per weight gives it; each 16-weight sum is scaled
+// by d sc / 4 (exact: 11 + 8 significant bits) and no offset is folded out
+// of a sum.  Activations are staged in LDS as fp32 in the lanes' order (68
+// floats per lane's 64 weights: conflict-free 16-byte reads).  Segments of
+// LPR lanes reduce in a fixed order: deterministic, and a column's sums are
+// the same at every batch width.
+#include <algorithm>
+
+#include "qmv_block_decode.h"
+
+namespace qmv {
+namespace {
+
+constexpr int kQ6KBytes = 210;    // per super-block
+constexpr int kQ6KWeights = 256;
+constexpr int kQ6KXPad = 68;      // staged floats per lane group of 64 weights
+
+// The stored bytes a lane needs for one step, as loaded (4-byte aligned
+// words; sh = 2 when the super-block starts 2 bytes past a word).
+struct Q6KRaw {
+    u32x4 a; uint32_t a4;   // ql bytes 64h + 16lh .. +16 (quarters 0, 2)
+    u32x4 b; uint32_t b4;   // ql bytes 64h + 32 + 16lh .. +16 (quarters 1, 3)
+    u32x4 c; uint32_t c4;   // qh bytes 32h + 16lh .. +16
+    u32x4 t; uint32_t u;    // scales sc[0..15] (and 2 bytes before when sh = 2), sc[14..15]
+    uint32_t dh;            // d (fp16 bits)
+    uint32_t sh;            // 0, or 2 when the super-block starts 2 bytes past a word
+};
+
+__device__ __forceinline__ void q6k_fetch(const uint8_t* sb, int hl, Q6KRaw& r) {
+    const int sh = (int)(reinterpret_cast<uintptr_t>(sb) & 2);
+    const uint8_t* p = sb - sh;                       // 4-byte aligned
+    const int pa = 64 * (hl >> 1) + 16 * (hl & 1);
+    const int pc = 128 + 32 * (hl >> 1) + 16 * (hl & 1);
+    r.a = ld16(p + pa);
+    r.a4 = ld4(p + pa + 16);
+    r.b = ld16(p + pa + 32);
+    r.b4 = ld4(p + pa + 48);
+    r.c = ld16(p + pc);
+    r.c4 = ld4(p + pc + 16);
+    r.t = ld16(p + 192);
+    r.u = ld2(sb + 206);
+    r.dh = ld2(sb + 208);
+    r.sh = (uint32_t)sh;
+}
+
+// Rebuilds the lane's 16-byte pieces at their true alignment.
+__device__ __forceinline__ void realign(const u32x4& v, uint32_t e, uint32_t sh, uint32_t (&o)[4]) {
+    const uint32_t w[5] = {v.x, v.y, v.z, v.w, e};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], sh);
+}
+
+// Four codes of quarter q as signed bytes 4 (c - 32): lo holds their 4 low
+// bits at bits 0-3 (q < 2) or 4-7 (q >= 2) of each byte, hf the qh word
+// with the top bit of every 2-bit field flipped.  4 operations per word for
+// a constant q, 6 for a run-time one.
+__device__ __forceinline__ uint32_t q6k_bytes(uint32_t lo, uint32_t hf, int q) {
+    const uint32_t l = q < 2 ? (lo << 2) : (lo >> 2);          // low bits to bits 2-5
+    const uint32_t h = (hf << (6 - 2 * q)) & 0xc0c0c0c0u;     // field q to bits 6-7
+    return (l & 0x3c3c3c3cu) | h;
+}
+
+// Staged activations: the 64 x values of lane group g = 4 sb + 2 h + lh
+// (elements 256 sb + 128 h + 32 q + 16 lh + i) at xs[g * 68 + 16 q + i], so
+// a lane reads its quarter's 16 values contiguously and lanes on
+// consecutive groups start 4 banks apart.  Loads in batches of 4 per thread
+// before any is stored; vec: every column aligned for 4-element loads.
+// Ends with a barrier.
+template <int B, int NT, class XT>
+__device__ __forceinline__ void q6k_stage_x(const XT* const (&xcol)[B], int K, float* xs, bool vec) {
+    const int G = K >> 6;
+    const int tid = threadIdx.x;
+    auto slot = [](int e) {
+        const int g = ((e >> 8) << 2) | (((e >> 7) & 1) << 1) | ((e >> 4) & 1);
+        return g * kQ6KXPad + 16 * ((e >> 5) & 3) + (e & 15);
+    };
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float* dst = xs + b * G * kQ6KXPad;
+        const XT* src = xcol[b];
+        if (vec) {
+            const int K4 = K >> 2;
+            auto put = [&](int c, const float4& v) { *reinterpret_cast<float4*>(dst + slot(4 * c)) = v; };
+            for (int c0 = tid; c0 < K4; c0 += 4 * NT) {
+                const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
+                const float4 v0 = XIn<XT>::load4(src + 4 * c0);
+                const float4 v1 = XIn<XT>::load4(src + 4 * min(c1, K4 - 1));
+                const float4 v2 = XIn<XT>::load4(src + 4 * min(c2, K4 - 1));
+                const float4 v3 = XIn<XT>::load4(src + 4 * min(c3, K4 - 1));
+                put(c0, v0);
+                if (c1 < K4) put(c1, v1);
+                if (c2 < K4) put(c2, v2);
+                if (c3 < K4) put(c3, v3);
+            }
+        } else {
+            for (int e0 = tid; e0 < K; e0 += 4 * NT) {
+                const int e1 = e0 + NT, e2 = e0 + 2 * NT, e3 = e0 + 3 * NT;
+                const float v0 = XIn<XT>::load1(src + e0);
+                const float v1 = XIn<XT>::load1(src + min(e1, K - 1));
+                const float v2 = XIn<XT>::load1(src + min(e2, K - 1));
+                const float v3 = XIn<XT>::load1(src + min(e3, K - 1));
+                dst[slot(e0)] = v0;
+                if (e1 < K) dst[slot(e1)] = v1;
+                if (e2 < K) dst[slot(e2)] = v2;
+                if (e3 < K) dst[slot(e3)] = v3;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// A wave step covers RW = 64 / LPR rows, one per segment of LPR lanes; lane
+// li of a segment takes lane group li + LPR t of its row in step t.
+template <int B, int LPR, int NW, class XT>
+__global__ __launch_bounds__(64 * NW) void q6k_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
+                                                       const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
+                                                       int64_t ldy, int xvec) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xs = lds;                          // [B][4 nsb][kQ6KXPad]
+    constexpr int RW = 64 / LPR;              // rows per tile
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = lane / LPR;
+    const int li = lane % LPR;
+    const int G = 4 * nsb;                    // lane groups (64 weights) per row
+    const int T = (G + LPR - 1) / LPR;        // steps per row
+    const int64_t pitch = (int64_t)nsb * kQ6KBytes;
+    const int64_t ntiles = (N + RW - 1) / RW;
+    const int64_t wstride = (int64_t)gridDim.x * NW;
+
+    auto load_step = [&](int64_t tile, int t, Q6KRaw& r) {
+        const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
+        const int64_t row = min(tile * RW + seg, N - 1);
+        q6k_fetch(W + row * pitch + (int64_t)(g >> 2) * kQ6KBytes, g & 3, r);
+    };
+
+    float acc[B];
+#pragma unroll
+    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    auto compute_step = [&](int64_t tile, int t, const Q6KRaw& r) {
+        const int g = li + LPR * t;
+        const bool valid = g < G;
+        const int gc = valid ? g : G - 1;
+        const bool h = (gc & 2) != 0;          // half of the super-block
+        const int lh = gc & 1;                 // l in [16 lh, 16 lh + 16)
+        uint32_t A[4], Bq[4], C[4], S[4];
+        realign(r.a, r.a4, r.sh, A);
+        realign(r.b, r.b4, r.sh, Bq);
+        realign(r.c, r.c4, r.sh, C);
+        realign(r.t, r.u, r.sh, S);
+        // the lane's quarter q uses sc[8 h + 2 q + lh]; d sc / 4 is exact
+        const float d4 = half_bits_to_float(r.dh) * 0.25f;
+        const uint32_t s01 = h ? S[2] : S[0], s23 = h ? S[3] : S[1];
+        uint32_t hf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) hf[k] = C[k] ^ 0xaaaaaaaau;   // top bit of each 2-bit field flipped
+        const float* xg = xs + gc * kQ6KXPad;
+        const int cs = G * kQ6KXPad;           // column stride in LDS
+        float st[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) st[b] = 0.f;
+        // quarter q: 16 weights, one scale; st += (d sc / 4) * sum 4 (c - 32) x
+        auto quarter = [&](int q) {
+            const float scale = d4 * (float)(int8_t)((q < 2 ? s01 : s23) >> (8 * lh + 16 * (q & 1)));
+            float s[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) s[b] = 0.f;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t v = q6k_bytes((q & 1) ? Bq[k] : A[k], hf[k], q);
+                const float c0 = sbyte(v, 0), c1 = sbyte(v, 1), c2 = sbyte(v, 2), c3 = sbyte(v, 3);
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float4 xv = *reinterpret_cast<const float4*>(xg + b * cs + 16 * q + 4 * k);
+                    s[b] = __builtin_fmaf(c0, xv.x, s[b]);
+                    s[b] = __builtin_fmaf(c1, xv.y, s[b]);
+                    s[b] = __builtin_fmaf(c2, xv.z, s[b]);
+                    s[b] = __builtin_fmaf(c3, xv.w, s[b]);
+                }
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b) st[b] = __builtin_fmaf(scale, s[b], st[b]);
+        };
+        // One column: the quarters unrolled (constant shifts and selects).
+        // More columns: a loop that is not unrolled, so the quarters share
+        // registers (unrolled, the scheduler interleaves them: 180 VGPRs at
+        // batch 2, spills from batch 4).
+        if constexpr (B == 1) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) quarter(q);
+        } else {
+#pragma unroll 1
+            for (int q = 0; q < 4; ++q) quarter(q);
+        }
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[b] = valid ? acc[b] + st[b] : acc[b];
+        if (t == T - 1) {
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const float tot = segment_sum<LPR>(acc[b]);
+                const int64_t row = tile * RW + seg;
+                if (li == 0 && row < N) y[b * ldy + row] = tot;
+                acc[b] = 0.f;
+            }
+        }
+    };
+    auto advance = [&](int64_t& tile, int& t) {
+        if (++t == T) {
+            t = 0;
+            tile += wstride;
+        }
+    };
+
+    int64_t ltile = (int64_t)blockIdx.x * NW + wave;   // next step to load
+    int lt = 0;
+    int64_t ctile = ltile;                             // next step to compute
+    int ct = 0;
+    Q6KRaw buf[2];
+    auto load_next = [&](Q6KRaw& r) {
+        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
+        if (ltile < ntiles) advance(ltile, lt);
+    };
+    // the first weight loads go out before the staging
+    load_next(buf[0]);
+    {
+        const XT* xcol[B];
+#pragma unroll
+        for (int b = 0; b < B; ++b) xcol[b] = x + b * ldx;
+        q6k_stage_x<B, 64 * NW, XT>(xcol, 256 * nsb, xs, xvec != 0);   // ends with a barrier
+    }
+    // Two register buffers used in turn; once the load cursor is past the
+    // wave's last step, the step in hand is the last one: it is computed
+    // after the loop and nothing more is loaded.
+    if (ctile < ntiles) {
+        while (ltile < ntiles) {
+            load_next(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[0]);
+            advance(ctile, ct);
+            if (ltile >= ntiles) {
+                buf[0] = buf[1];
+                break;
+            }
+            load_next(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[1]);
+            advance(ctile, ct);
+        }
+        compute_step(ctile, ct, buf[0]);
+    }
+}
+
+// One thread per 16-weight sub-block: out = (d sc / 4) * 4 (c - 32), the
+// weight the matvec uses (exact).
+__global__ __launch_bounds__(kThreads) void q6k_dequant_kernel(const uint8_t* __restrict__ W, int64_t nsub,
+                                                               float* __restrict__ out) {
+    const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (u >= nsub) return;
+    const uint8_t* sb = W + (u >> 4) * kQ6KBytes;
+    const int s = (int)(u & 15);               // sub-block: weights 16 s .. 16 s + 15
+    const int h = s >> 3, q = (s >> 1) & 3, lh = s & 1;
+    const float scale = half_bits_to_float(sb[208] | (sb[209] << 8)) * 0.25f * (float)(int8_t)sb[192 + s];
+    const uint8_t* ql = sb + 64 * h + 32 * (q & 1) + 16 * lh;
+    const uint8_t* qh = sb + 128 + 32 * h + 16 * lh;
+    float* o = out + u * 16;
+    for (int i = 0; i < 16; ++i) {
+        const int lo = q < 2 ? (ql[i] & 15) : (ql[i] >> 4);
+        const int c = lo | (((qh[i] >> (2 * q)) & 3) << 4);
+        o[i] = scale * (float)(4 * (c - 32));
+    }
+}
+
+template <int B, int LPR, int NW, class XT>
+int32_t q6k_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
+                   hipStream_t st) {
+    auto kern = q6k_kernel<B, LPR, NW, XT>;
+    const size_t lds = (size_t)B * 4 * nsb * kQ6KXPad * sizeof(float);
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv_q6_k", &dyn_max)) return e;
+    if (lds > dyn_max) return fail(QMV_EINVAL, "qmv_q6_k: %zu bytes of staged activations exceed the LDS", lds);
+    constexpr int rows_per_wg = NW * (64 / LPR);
+    const int64_t tiles = (N + rows_per_wg - 1) / rows_per_wg;
+    const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
+    const int xvec = (aligned(x, XIn<XT>::kVecAlign) && ldx % 4 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nsb, x, ldx, y, ldy, xvec);
+    return check_launch("qmv_q6_k");
+}
+
+// Lanes per row: the widest split of 64 / 32 / 16 / 8 lanes that leaves at
+// most 1/16 of a row's lane-steps idle, else the split with the fewest idle
+// (the same rule as for Q4_K: groups of 64 weights per lane).
+inline int q6k_pick_lpr(int G) {
+    int best = 8;
+    int64_t best_idle = 1 << 30, best_span = 1;
+    for (const int l : {64, 32, 16, 8}) {
+        if (l > G && l != 8) continue;
+        const int64_t span = (G + l - 1) / l * l;
+        const int64_t idle = span - G;
+        if (16 * idle <= span) return l;
+        if (idle * best_span < best_idle * span) {
+            best = l;
+            best_idle = idle;
+            best_span = span;
+        }
+    }
+    return best;
+}
+
+template <int B, class XT>
+int32_t q6k_launch_lpr(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
+                       hipStream_t st) {
+    switch (q6k_pick_lpr(4 * nsb)) {
+    case 64: return q6k_launch<B, 64, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 32: return q6k_launch<B, 32, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 16: return q6k_launch<B, 16, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    default: return q6k_launch<B, 8, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    }
+}
+
+template <class XT>
+int32_t q6k_batch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, int B, float* y, int64_t ldy,
+                  hipStream_t st) {
+    switch (B) {
+    case 1: return q6k_launch_lpr<1, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 2: return q6k_launch_lpr<2, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 3: return q6k_launch_lpr<3, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 4: return q6k_launch_lpr<4, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 5: return q6k_launch_lpr<5, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 6: return q6k_launch_lpr<6, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 7: return q6k_launch_lpr<7, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    default: return q6k_launch_lpr<8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    }
+}
+
+template <class XT>
+int32_t q6k_matvec_t(const char* name, const void* W, int64_t N, int64_t K, const XT* x, int64_t ldx, int32_t batch,
+                     float* y, int64_t ldy, void* stream) {
+    if (!W || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
+    if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
+    if (K < kQ6KWeights || K % kQ6KWeights)
+        return fail(QMV_EINVAL, "%s: n_cols must be a positive multiple of 256 for Q6_K (got %lld)", name,
+                    (long long)K);
+    if (batch < 1 || batch > 8) return fail(QMV_EINVAL, "%s: batch must be in 1..8 (got %d)", name, batch);
+    if (ldx < K) return fail(QMV_EINVAL, "%s: ldx (%lld) < n_cols (%lld)", name, (long long)ldx, (long long)K);
+    if (ldy < N) return fail(QMV_EINVAL, "%s: ldy (%lld) < n_rows (%lld)", name, (long long)ldy, (long long)N);
+    if (K / kQ6KWeights > (1 << 24) || N > ((int64_t)1 << 40) / (K / kQ6KWeights))
+        return fail(QMV_EINVAL, "%s: matrix too large (%lld x %lld)", name, (long long)N, (long long)K);
+    if (!aligned(W, 4)) return fail(QMV_EALIGN, "%s: W must be 4-byte aligned for Q6_K", name);
+    if (!aligned(y, 4)) return fail(QMV_EALIGN, "%s: y must be 4-byte aligned", name);
+    if (!aligned(x, sizeof(XT))) return fail(QMV_EALIGN, "%s: x must be aligned to its element size", name);
+    const int nsb = (int)(K / kQ6KWeights);
+    const int per_col = 4 * nsb * kQ6KXPad * (int)sizeof(float);
+    if (per_col > kLdsMax)
+        return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
+    const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / per_col));
+    for (int b0 = 0; b0 < batch; b0 += per_pass) {
+        const int bw = std::min(per_pass, batch - b0);
+        const int32_t rc = q6k_batch<XT>(static_cast<const uint8_t*>(W), N, nsb, x + b0 * ldx, ldx, bw,
+                                         y + b0 * ldy, ldy, as_stream(stream));
+        if (rc != QMV_OK) return rc;
+    }
+    return ok();
+}
+
+int32_t q6k_matvec(const char* name, const void* W, int64_t N, int64_t K, const void* x, int32_t x_type, int64_t ldx,
+                   int32_t batch, float* y, int64_t ldy, void* stream, int32_t path) {
+    if (path == QMV_PATH_MFMA)
+        return fail(QMV_EUNSUPPORTED, "%s: Q6_K has no matrix-core kernel (use QMV_PATH_AUTO or QMV_PATH_FMA)", name);
+    switch (x_type) {
+    case QMV_X_F32: return q6k_matvec_t(name, W, N, K, static_cast<const float*>(x), ldx, batch, y, ldy, stream);
+    case QMV_X_F16: return q6k_matvec_t(name, W, N, K, static_cast<const _Float16*>(x), ldx, batch, y, ldy, stream);
+    case QMV_X_BF16: return q6k_matvec_t(name, W, N, K, static_cast<const __bf16*>(x), ldx, batch, y, ldy, stream);
+    default: return fail(QMV_EINVAL, "%s: unknown x_type %d", name, (int)x_type);
+    }
+}
+
+int32_t q6k_dequant(const void* W, int64_t N, int64_t K, float* out, void* stream) {
+    const char* name = "qmv_dequant";
+    if (!W || !out) return fail(QMV_EINVAL, "%s: null pointer", name);
+    if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
+    if (K < kQ6KWeights || K % kQ6KWeights)
+        return fail(QMV_EINVAL, "%s: n_cols must be a positive multiple of 256 for Q6_K (got %lld)", name,
+                    (long long)K);
+    if (N > ((int64_t)1 << 40) / K) return fail(QMV_EINVAL, "%s: matrix too large", name);
+    if (!aligned(out, 4)) return fail(QMV_EALIGN, "%s: out must be 4-byte aligned", name);
+    const int64_t nsub = N * (K / 16);
+    const int64_t grid = (nsub + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(q6k_dequant_kernel, dim3((unsigned)grid), dim3(kThreads), 0, as_stream(stream),
+                       static_cast<const uint8_t*>(W), nsub, out);
+    return check_launch(name);
+}
+
+int32_t q6k_no_moe(const char* name, bool, const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, int32_t,
+                   int32_t, const void*, int32_t, int64_t, int64_t, float*, void*) {
+    return fail(QMV_EUNSUPPORTED, "%s: Q6_K experts are not supported", name);
+}
+int32_t q6k_no_combine(const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, const float*, int32_t, int32_t,
+                       const float*, int64_t, int64_t, float*, void*) {
+    return fail(QMV_EUNSUPPORTED, "qmv_moe_combine: Q6_K experts are not supported");
+}
+bool q6k_no_group(const RowSegs&, int, const float*, hipStream_t, bool, int32_t*) { return false; }
+
+}  // namespace
+
+const FormatOps& ops_q6_k() {
+    static const FormatOps ops = {q6k_matvec, q6k_dequant, q6k_no_moe, q6k_no_combine, q6k_no_group};
+    return ops;
+}
+
+}  // namespace qmv
+
+extern "C" int32_t qmv_q6_k(const void* W, int64_t n_rows, int64_t n_cols, const float* x, int64_t ldx, int32_t batch,
+                            float* y, int64_t ldy, void* stream) {
+    return qmv::ops_q6_k().matvec("qmv_q6_k", W, n_rows, n_cols, x, QMV_X_F32, ldx, batch, y, ldy, stream,
+                                  QMV_PATH_AUTO);
+}

@@ -22,7 +22,7 @@ on the launch stream, the measured stream-read ceiling, the oracle's time
 on the host (cpu_baseline) and a one-number summary per sweep.
 
 Extra workloads: the Q8_0 1024 x 1024 matvec over 480 rotated copies (so
-every call reads HBM), Q4_0 / Q4_1 / Q4_K at batch 1, 2, 4, 8, the int8 requant path
+every call reads HBM), Q4_0 / Q4_1 / Q4_K / Q6_K at batch 1, 2, 4, 8, the int8 requant path
 on Qwen3-0.6B shapes and the MoE expert path (plain and fused) at batch
 1, 2, 4, 8.
 
@@ -151,7 +151,7 @@ def _dense_sweep(torch, qmv, wl, fmt, batch, layers, layer_mats, head, tagbase, 
     stored concatenated (same input vector), e.g. q||k||v and gate||up."""
     import numpy as np
     cfn = {"q8_0": qmv.lib().qmv_q8_0, "q4_0": qmv.lib().qmv_q4_0, "q4_1": qmv.lib().qmv_q4_1,
-           "q4_k": qmv.lib().qmv_q4_k}[fmt]
+           "q4_k": qmv.lib().qmv_q4_k, "q6_k": qmv.lib().qmv_q6_k}[fmt]
     sw = Sweep(name, batch)
     dev = "cuda:0"
     t0 = time.time()
@@ -746,7 +746,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--sweeps", default="all",
-                    help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,q4_k,int8,moe, or of "
+                    help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,q4_k,q6_k,int8,moe, or of "
                          "FMT@B / FMT@Bf / FMT@1g (one 8B sweep of format FMT at batch B, f: row-fused layout, "
                          "1g: batch 1 with one launch per dependency level)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing")
@@ -821,7 +821,8 @@ def main():
                                           f"timed once, x32, + lm_head); per column at batch B: B times this")
 
     names = [] if args.sweeps == "none" else (
-        ["c1", "q8_0", "q4_0", "q4_1", "q4_k", "int8", "moe"] if args.sweeps == "all" else args.sweeps.split(","))
+        ["c1", "q8_0", "q4_0", "q4_1", "q4_k", "q6_k", "int8", "moe"] if args.sweeps == "all"
+        else args.sweeps.split(","))
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
         if "@" in nm:
@@ -868,7 +869,7 @@ def main():
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
                 del s
                 torch.cuda.empty_cache()
-        elif nm == "q4_k":
+        elif nm in ("q4_k", "q6_k"):
             o = oracle_for(nm, lambda: dense_oracle(nm))
             for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
                 s = build_llama(torch, qmv, wl, nm, B, fused=fused)

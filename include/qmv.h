@@ -74,7 +74,7 @@ extern "C" {
 
 #define QMV_ABI_VERSION 1
 
-typedef enum { QMV_Q8_0 = 0, QMV_Q4_0 = 1, QMV_Q4_1 = 2, QMV_Q4_K = 3 } qmv_fmt;
+typedef enum { QMV_Q8_0 = 0, QMV_Q4_0 = 1, QMV_Q4_1 = 2, QMV_Q4_K = 3, QMV_Q6_K = 4 } qmv_fmt;
 
 enum {
     QMV_OK = 0,
@@ -136,6 +136,31 @@ int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
  * MoE entry points and qmv_chain do not (QMV_EUNSUPPORTED).
  */
 int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
+                 const float* x, int64_t ldx, int32_t batch,
+                 float* y, int64_t ldy, void* stream);
+
+/*
+ * Q6_K float matvec, y[b][i] = sum_j DEQ(W)[i][j] * x[b][j] ([NST] Sec.
+ * "The Unified Quant Core" lists Q6_K as signed 6-bit, 210 bytes per 256
+ * weights; the byte layout is not on the pages and is read here as the
+ * ggml-compatible one): 256-weight super-blocks of 210 bytes, 128 bytes of
+ * low 4 code bits, 64 of high 2 bits, 16 int8 scales (one per 16 weights),
+ * fp16 d; w_e = d*sc[e/16]*(c-32) (bit positions stated with the kernel,
+ * qmv_q6k.hip).
+ *   W       n_rows rows of n_cols/256 super-blocks; 4-byte aligned.
+ *   n_cols  >= 256 and a multiple of 256; at most 38400 (one activation row
+ *           staged in LDS, 68 floats per 64 columns).
+ *   x, batch, y as qmv_q8_0.
+ * Codes are exact signed integers and each 16-weight sum is scaled by the
+ * exact d*sc, so the accuracy bound holds on every input.  Deterministic; a
+ * column's result is the same bitwise at every batch width.
+ * Errors: QMV_EINVAL (as qmv_q8_0, with multiples of 256), QMV_EALIGN (W,
+ * x or y not 4-byte aligned), QMV_EHIP.
+ * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q6_K (matvec on
+ * QMV_PATH_AUTO or QMV_PATH_FMA; QMV_PATH_MFMA gives QMV_EUNSUPPORTED); the
+ * MoE entry points and qmv_chain do not (QMV_EUNSUPPORTED).
+ */
+int32_t qmv_q6_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
                  float* y, int64_t ldy, void* stream);
 
@@ -401,7 +426,8 @@ int32_t qmv_chain_noalloc(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_
  * Dequantize a whole matrix to fp32: out[i][j] = DEQ(W)[i][j], exactly (every
  * Q8_0/Q4_0 value and every Q4_1 value d*c + m whose bits span <= 24 is
  * representable in fp32; otherwise it is rounded to nearest even; a Q4_K
- * value d*sc*c - dmin*mn is its exact value rounded once).  A test
+ * value d*sc*c - dmin*mn is its exact value rounded once; a Q6_K value
+ * d*sc*(c-32) is exact).  A test
  * and inspection aid ([NST] Sec. "The Unified Quant Core": the per-format
  * block decoder maps a stored block to its values).
  *   out  fp32 [n_rows][n_cols]; 4-byte aligned.

@@ -28,7 +28,7 @@ def qmv():
 
 def test_every_declared_symbol_is_exported(qmv):
     names = declared_functions()
-    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k", "qmv_matvec_path", "qmv_matvec_xt", "qmv_i8_requant",
+    assert {"qmv_q8_0", "qmv_q4_0", "qmv_q4_1", "qmv_q4_k", "qmv_q6_k", "qmv_matvec_path", "qmv_matvec_xt", "qmv_i8_requant",
             "qmv_i8_requant_lut", "qmv_moe", "qmv_moe_xt", "qmv_moe_swiglu", "qmv_moe_swiglu_xt", "qmv_moe_combine",
             "qmv_dequant",
             "qmv_chain", "qmv_last_error", "qmv_abi_version"} <= set(names)
@@ -105,6 +105,37 @@ def test_q4_k_argument_errors(qmv):
     assert L.qmv_moe_combine(qmv.Q4_K, A, 144, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert L.qmv_chain(qmv.Q4_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED and "not supported" in qmv.last_error()
     assert L.qmv_chain_noalloc(qmv.Q4_K, A, 1, None) == EUNSUPPORTED
+
+
+def test_q6_k_argument_errors(qmv):
+    """Q6_K: columns in multiples of 256, W 4-byte aligned; no MFMA path;
+    MoE and chain entry points refuse the format."""
+    f = qmv.lib().qmv_q6_k
+    cases = [
+        ((0, 8, 256, A, 256, 1, A, 8, None), EINVAL, "null"),
+        ((A, 0, 256, A, 256, 1, A, 8, None), EINVAL, "n_rows"),
+        ((A, 8, 224, A, 224, 1, A, 8, None), EINVAL, "multiple of 256"),
+        ((A, 8, 0, A, 256, 1, A, 8, None), EINVAL, "multiple of 256"),
+        ((A, 8, 256, A, 256, 9, A, 8, None), EINVAL, "batch"),
+        ((A, 8, 256, A, 255, 1, A, 8, None), EINVAL, "ldx"),
+        ((A, 8, 256, A, 256, 1, A, 7, None), EINVAL, "ldy"),
+        ((A + 2, 8, 256, A, 256, 1, A, 8, None), EALIGN, "4-byte"),
+        ((A, 8, 256, A + 1, 256, 1, A, 8, None), EALIGN, "aligned"),
+        ((A, 8, 256, A, 256, 1, A + 2, 8, None), EALIGN, "aligned"),
+        ((A, 8, 38656, A, 38656, 1, A, 8, None), EINVAL, "LDS"),
+    ]
+    for args, code, word in cases:
+        assert f(*args) == code, (args, qmv.last_error())
+        assert word in qmv.last_error(), qmv.last_error()
+    L = qmv.lib()
+    assert L.qmv_matvec_path(qmv.Q6_K, A, 8, 256, A, 256, 1, A, 8, qmv.PATH_MFMA, None) == EUNSUPPORTED
+    assert L.qmv_dequant(qmv.Q6_K, A, 8, 288, A, None) == EINVAL and "256" in qmv.last_error()
+    assert L.qmv_moe(qmv.Q6_K, A, 210, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
+    assert "Q6_K" in qmv.last_error()
+    assert L.qmv_moe_combine(qmv.Q6_K, A, 210, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
+    assert L.qmv_chain(qmv.Q6_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED
+    assert L.qmv_chain_noalloc(qmv.Q6_K, A, 1, None) == EUNSUPPORTED
+    assert L.qmv_dequant(5, A, 8, 256, A, None) == EUNSUPPORTED
 
 
 def test_matvec_path_argument_errors(qmv):
