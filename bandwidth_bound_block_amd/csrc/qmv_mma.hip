@@ -167,6 +167,58 @@ template <> struct Mma<Q4_1> {
     }
 };
 
+// Q4_K super-blocks (144 bytes per 256 weights: 18 bytes per 32-weight
+// sub-block on average, so a step of 8 blocks is one super-block and the row
+// pitch is nb * 18).  The 16-byte header holds d, dmin and the 6-bit
+// scale and minimum of each sub-block J; its weights are D c - M with
+// D = d sc_J and M = dmin mn_J (both exact in fp32), codes in the low (J
+// even) or high (J odd) nibbles of bytes 16 + 32 (J / 2) .. +32.  As for
+// Q4_1, the operand carries c - k about the code k nearest the zero of
+// D c - M (k = clamp(rint(M / D), 0, 15)), and mu = D k - M (rounded once,
+// |mu| <= |w_e| wherever c_e != k, and mu = w_e where c_e = k) multiplies
+// the block sum of x.  Rows of mostly zero weights (M = D k) give mu = 0.
+struct Q4KSuper {
+    static constexpr int kBytes = 18;       // per 32 weights, on average
+};
+template <> struct Mma<Q4KSuper> {
+    static constexpr bool kSums = true;
+    static constexpr float kOutScale = 1.f;
+    __device__ static constexpr int x0(int g) { return 8 * g; }
+    __device__ static constexpr int x1(int g) { return 8 * g + 4; }
+    template <int J>
+    __device__ static void operand(const uint8_t* row, int g, uint32_t (&b)[4], float& d, float& m) {
+        const uint32_t h0 = lds4(row), h1 = lds4(row + 4), h2 = lds4(row + 8), h3 = lds4(row + 12);
+        // b[i] is byte i % 4 of h1 (i < 4), h2 (i < 8), h3
+        constexpr int t = 8 * (J & 3);
+        int sc, mn;
+        if constexpr (J < 4) {
+            sc = (int)((h1 >> t) & 63);
+            mn = (int)((h2 >> t) & 63);
+        } else {
+            sc = (int)(((h3 >> t) & 15) | (((h1 >> (t + 6)) & 3) << 4));
+            mn = (int)(((h3 >> (t + 4)) & 15) | (((h2 >> (t + 6)) & 3) << 4));
+        }
+        const float D = half_bits_to_float(h0) * (float)sc;
+        const float M = half_bits_to_float(h0 >> 16) * (float)mn;
+        // fmax/fmin return the number for a NaN operand (D = M = 0): k = 0
+        const float k = __builtin_fminf(__builtin_fmaxf(__builtin_rintf(M * __builtin_amdgcn_rcpf(D)), 0.f), 15.f);
+        d = D;
+        m = __builtin_fmaf(D, k, -M);
+        const uint8_t* q = row + 16 + 32 * (J >> 1) + 8 * g;
+        const uint32_t w0 = lds4(q), w1 = lds4(q + 4);
+        const uint32_t c0 = opaque((J & 1) ? ((w0 >> 4) & 0x0f0f0f0fu) : (w0 & 0x0f0f0f0fu));
+        const uint32_t c1 = opaque((J & 1) ? ((w1 >> 4) & 0x0f0f0f0fu) : (w1 & 0x0f0f0f0fu));
+        b[0] = pack_bf16(ubyte(c0, 0) - k, ubyte(c0, 1) - k);
+        b[1] = pack_bf16(ubyte(c0, 2) - k, ubyte(c0, 3) - k);
+        b[2] = pack_bf16(ubyte(c1, 0) - k, ubyte(c1, 1) - k);
+        b[3] = pack_bf16(ubyte(c1, 2) - k, ubyte(c1, 3) - k);
+    }
+    // D * sum_e (c_e - k) x_e + mu * sum_e x_e
+    __device__ static float term(float acc, float d, float mu, float dot, float sx) {
+        return __builtin_fmaf(mu, sx, __builtin_fmaf(d, dot, acc));
+    }
+};
+
 // A wave step: 16 rows x SB blocks, read as whole 16-byte chunks.
 template <class F, int SB>
 struct MmaStep {
@@ -447,9 +499,16 @@ bool launch_mma(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, i
 
 // Measured on the 8B decode shapes (4096..128256 rows, 4096 and 14336
 // columns, cache-cold): the matrix-core kernel is faster from batch 3 on
-// for every format, and at batch 2 for Q4_0 (at batch 2 the FMA kernels
-// still win most Q8_0 and Q4_1 shapes).
-bool use_mfma(qmv_fmt fmt, int64_t, int, int B) { return B >= 3 || (B == 2 && fmt == QMV_Q4_0); }
+// for the 32-weight block formats, and at batch 2 for Q4_0 (at batch 2 the
+// FMA kernels still win most Q8_0 and Q4_1 shapes).  Q4_K's FMA kernel
+// holds out longer (its matrix-core operand decodes two 6-bit fields and a
+// pivot per sub-block): 14336 x 4096 at batch 3 / 4 / 8 17.9 / 19.5 / 38.2 us
+// against 21.0 / 22.5 / 22.8, 4096 x 14336 27.8 / 31.4 / 61.3 against
+// 24.0 / 24.7 / 31.0, 128256 x 4096 at batch 2 111 against 106.
+bool use_mfma(qmv_fmt fmt, int64_t N, int nb, int B) {
+    if (fmt == QMV_Q4_K) return B >= 5 || (B >= 3 && nb >= 256) || (B >= 2 && N >= 65536);
+    return B >= 3 || (B == 2 && fmt == QMV_Q4_0);
+}
 
 namespace {
 // 16 waves per workgroup pay off on many tiles at batch 3..4 (the staged
@@ -485,14 +544,15 @@ bool launch_mma_x(const uint8_t* W, int64_t N, int nb, const void* x, int32_t x_
 
 bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const void* x, int32_t x_type, int64_t ldx,
                       int B, float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
-    const int64_t pitch = (int64_t)nb * (fmt == QMV_Q8_0 ? 34 : (fmt == QMV_Q4_0 ? 18 : 20));
+    const int64_t pitch = (int64_t)nb * (fmt == QMV_Q8_0 ? 34 : (fmt == QMV_Q4_1 ? 20 : 18));   // Q4_0, Q4_K: 18
     if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || pitch >= (1 << 24) || !aligned(W, 16) || ldx % 4) return false;
     switch (fmt) {
     case QMV_Q8_0: return launch_mma_x<Q8_0>(W, N, nb, x, x_type, ldx, B, y, ldy, st, variant, rc);
     case QMV_Q4_0: return launch_mma_x<Q4_0>(W, N, nb, x, x_type, ldx, B, y, ldy, st, variant, rc);
     case QMV_Q4_1: return launch_mma_x<Q4_1>(W, N, nb, x, x_type, ldx, B, y, ldy, st, variant, rc);
+    case QMV_Q4_K: return launch_mma_x<Q4KSuper>(W, N, nb, x, x_type, ldx, B, y, ldy, st, variant, rc);
+    default: return false;
     }
-    return false;
 }
 
 }  // namespace qmv

@@ -337,8 +337,8 @@ int32_t q4k_batch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx
 }
 
 template <class XT>
-int32_t q4k_matvec_t(const char* name, const void* W, int64_t N, int64_t K, const XT* x, int64_t ldx, int32_t batch,
-                     float* y, int64_t ldy, void* stream) {
+int32_t q4k_matvec_t(const char* name, const void* W, int64_t N, int64_t K, const XT* x, int32_t x_type, int64_t ldx,
+                     int32_t batch, float* y, int64_t ldy, void* stream, int32_t path) {
     if (!W || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
     if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
     if (K < kQ4KWeights || K % kQ4KWeights)
@@ -353,6 +353,18 @@ int32_t q4k_matvec_t(const char* name, const void* W, int64_t N, int64_t K, cons
     if (!aligned(y, 4)) return fail(QMV_EALIGN, "%s: y must be 4-byte aligned", name);
     if (!aligned(x, sizeof(XT))) return fail(QMV_EALIGN, "%s: x must be aligned to its element size", name);
     const int nsb = (int)(K / kQ4KWeights);
+    // Batch 3..8 on the matrix cores (codes about a pivot per sub-block and
+    // block sums of x, as for Q4_1), where the shape allows.
+    if (path == QMV_PATH_MFMA || (path == QMV_PATH_AUTO && use_mfma(QMV_Q4_K, N, 8 * nsb, batch))) {
+        int32_t rc = QMV_OK;
+        if (batch_matvec_mma(QMV_Q4_K, static_cast<const uint8_t*>(W), N, 8 * nsb, x, x_type, ldx, batch, y, ldy,
+                             as_stream(stream), 0, &rc))
+            return rc == QMV_OK ? ok() : rc;
+        if (path == QMV_PATH_MFMA)
+            return fail(QMV_EUNSUPPORTED,
+                        "%s: the matrix-core path needs batch 2..8, x aligned to 4 elements (16 bytes for fp32) and "
+                        "ldx a multiple of 4", name);
+    }
     const int per_col = 4 * nsb * kQ4KXPad * (int)sizeof(float);
     if (per_col > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
@@ -368,12 +380,13 @@ int32_t q4k_matvec_t(const char* name, const void* W, int64_t N, int64_t K, cons
 
 int32_t q4k_matvec(const char* name, const void* W, int64_t N, int64_t K, const void* x, int32_t x_type, int64_t ldx,
                    int32_t batch, float* y, int64_t ldy, void* stream, int32_t path) {
-    if (path == QMV_PATH_MFMA)
-        return fail(QMV_EUNSUPPORTED, "%s: Q4_K has no matrix-core kernel (use QMV_PATH_AUTO or QMV_PATH_FMA)", name);
     switch (x_type) {
-    case QMV_X_F32: return q4k_matvec_t(name, W, N, K, static_cast<const float*>(x), ldx, batch, y, ldy, stream);
-    case QMV_X_F16: return q4k_matvec_t(name, W, N, K, static_cast<const _Float16*>(x), ldx, batch, y, ldy, stream);
-    case QMV_X_BF16: return q4k_matvec_t(name, W, N, K, static_cast<const __bf16*>(x), ldx, batch, y, ldy, stream);
+    case QMV_X_F32:
+        return q4k_matvec_t(name, W, N, K, static_cast<const float*>(x), x_type, ldx, batch, y, ldy, stream, path);
+    case QMV_X_F16:
+        return q4k_matvec_t(name, W, N, K, static_cast<const _Float16*>(x), x_type, ldx, batch, y, ldy, stream, path);
+    case QMV_X_BF16:
+        return q4k_matvec_t(name, W, N, K, static_cast<const __bf16*>(x), x_type, ldx, batch, y, ldy, stream, path);
     default: return fail(QMV_EINVAL, "%s: unknown x_type %d", name, (int)x_type);
     }
 }
