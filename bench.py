@@ -58,20 +58,20 @@ TRAFFIC_RECORDS = {
     "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>": {
         "key": "kernel_c_q8_0",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "a2bb88c7a3683f935a6d77a56d8caebb6dc24d4f2691437737ddd06ae31ba6c1", "bytes_per_launch": 83478763, "ratio": 1.0025,
+        "sha256": "2801ae488bf56afe936da42516ab62ffc13681b9faaa1377318c454da6e6ca73", "bytes_per_launch": 83478763, "ratio": 1.0025,
         "workload": "8B Q8_0 decode step, batch 1"},
     "qmv_kernel<Q8_0, 1, 64, 1, 2, 8, 2, false, float, false>": {
         "key": "kernel_q8_0_o",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "a2bb88c7a3683f935a6d77a56d8caebb6dc24d4f2691437737ddd06ae31ba6c1", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
+        "sha256": "2801ae488bf56afe936da42516ab62ffc13681b9faaa1377318c454da6e6ca73", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
     "qmv_kernel_c<Q8_0, 4, 16, 2, float, 1>": {
         "key": "kernel_c16_q8_0_down",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "a2bb88c7a3683f935a6d77a56d8caebb6dc24d4f2691437737ddd06ae31ba6c1", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
+        "sha256": "2801ae488bf56afe936da42516ab62ffc13681b9faaa1377318c454da6e6ca73", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
     "i8_stream_kernel": {
         "key": "i8_stream",
         "sources": ["bandwidth_bound_block_amd/csrc/qmv_int8.hip", "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-        "sha256": "0cae04abbe99a25c07c77728d94fb5116435cb8e707e10420958edea0fdaccb3", "ratio": 1.0380,
+        "sha256": "76bd0f16be16a608b8ba7f81f445083e00e986515c81f1401419b1e8673cbb30", "ratio": 1.0380,
         "workload": "Qwen3-0.6B int8 step (28 layers + lm_head), batch 1, per-matrix launches"},
 }
 
