@@ -25,16 +25,12 @@
 // floats per lane's 64 weights: conflict-free 16-byte reads).  Segments of
 // LPR lanes reduce in a fixed order: deterministic, and a column's sums are
 // the same at every batch width.
-#include <algorithm>
-
-#include "qmv_block_decode.h"
+#include "qmv_superblock.h"
 
 namespace qmv {
 namespace {
 
 constexpr int kQ6KBytes = 210;    // per super-block
-constexpr int kQ6KWeights = 256;
-constexpr int kQ6KXPad = 68;      // staged floats per lane group of 64 weights
 
 // The stored bytes a lane needs for one step, as loaded (4-byte aligned
 // words; sh = 2 when the super-block starts 2 bytes past a word).
@@ -82,52 +78,12 @@ __device__ __forceinline__ uint32_t q6k_bytes(uint32_t lo, uint32_t hf, int q) {
 }
 
 // Staged activations: the 64 x values of lane group g = 4 sb + 2 h + lh
-// (elements 256 sb + 128 h + 32 q + 16 lh + i) at xs[g * 68 + 16 q + i], so
-// a lane reads its quarter's 16 values contiguously and lanes on
-// consecutive groups start 4 banks apart.  Loads in batches of 4 per thread
-// before any is stored; vec: every column aligned for 4-element loads.
-// Ends with a barrier.
-template <int B, int NT, class XT>
-__device__ __forceinline__ void q6k_stage_x(const XT* const (&xcol)[B], int K, float* xs, bool vec) {
-    const int G = K >> 6;
-    const int tid = threadIdx.x;
-    auto slot = [](int e) {
-        const int g = ((e >> 8) << 2) | (((e >> 7) & 1) << 1) | ((e >> 4) & 1);
-        return g * kQ6KXPad + 16 * ((e >> 5) & 3) + (e & 15);
-    };
-#pragma unroll
-    for (int b = 0; b < B; ++b) {
-        float* dst = xs + b * G * kQ6KXPad;
-        const XT* src = xcol[b];
-        if (vec) {
-            const int K4 = K >> 2;
-            auto put = [&](int c, const float4& v) { *reinterpret_cast<float4*>(dst + slot(4 * c)) = v; };
-            for (int c0 = tid; c0 < K4; c0 += 4 * NT) {
-                const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
-                const float4 v0 = XIn<XT>::load4(src + 4 * c0);
-                const float4 v1 = XIn<XT>::load4(src + 4 * min(c1, K4 - 1));
-                const float4 v2 = XIn<XT>::load4(src + 4 * min(c2, K4 - 1));
-                const float4 v3 = XIn<XT>::load4(src + 4 * min(c3, K4 - 1));
-                put(c0, v0);
-                if (c1 < K4) put(c1, v1);
-                if (c2 < K4) put(c2, v2);
-                if (c3 < K4) put(c3, v3);
-            }
-        } else {
-            for (int e0 = tid; e0 < K; e0 += 4 * NT) {
-                const int e1 = e0 + NT, e2 = e0 + 2 * NT, e3 = e0 + 3 * NT;
-                const float v0 = XIn<XT>::load1(src + e0);
-                const float v1 = XIn<XT>::load1(src + min(e1, K - 1));
-                const float v2 = XIn<XT>::load1(src + min(e2, K - 1));
-                const float v3 = XIn<XT>::load1(src + min(e3, K - 1));
-                dst[slot(e0)] = v0;
-                if (e1 < K) dst[slot(e1)] = v1;
-                if (e2 < K) dst[slot(e2)] = v2;
-                if (e3 < K) dst[slot(e3)] = v3;
-            }
-        }
-    }
-    __syncthreads();
+// (elements 256 sb + 128 h + 32 q + 16 lh + i) at xs[g * kSbXPad + 16 q +
+// i], so a lane reads its quarter's 16 values contiguously and lanes on
+// consecutive groups start 4 banks apart.
+__device__ __forceinline__ int q6k_slot(int e) {
+    const int g = ((e >> 8) << 2) | (((e >> 7) & 1) << 1) | ((e >> 4) & 1);
+    return g * kSbXPad + 16 * ((e >> 5) & 3) + (e & 15);
 }
 
 // A wave step covers RW = 64 / LPR rows, one per segment of LPR lanes; lane
@@ -137,7 +93,7 @@ __global__ __launch_bounds__(64 * NW) void q6k_kernel(const uint8_t* __restrict_
                                                        const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
                                                        int64_t ldy, int xvec) {
     extern __shared__ __attribute__((aligned(16))) float lds[];
-    float* xs = lds;                          // [B][4 nsb][kQ6KXPad]
+    float* xs = lds;                          // [B][4 nsb][kSbXPad], in q6k_slot order
     constexpr int RW = 64 / LPR;              // rows per tile
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -175,8 +131,8 @@ __global__ __launch_bounds__(64 * NW) void q6k_kernel(const uint8_t* __restrict_
         uint32_t hf[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) hf[k] = C[k] ^ 0xaaaaaaaau;   // top bit of each 2-bit field flipped
-        const float* xg = xs + gc * kQ6KXPad;
-        const int cs = G * kQ6KXPad;           // column stride in LDS
+        const float* xg = xs + gc * kSbXPad;
+        const int cs = G * kSbXPad;            // column stride in LDS
         float st[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) st[b] = 0.f;
@@ -247,7 +203,7 @@ __global__ __launch_bounds__(64 * NW) void q6k_kernel(const uint8_t* __restrict_
         const XT* xcol[B];
 #pragma unroll
         for (int b = 0; b < B; ++b) xcol[b] = x + b * ldx;
-        q6k_stage_x<B, 64 * NW, XT>(xcol, 256 * nsb, xs, xvec != 0);   // ends with a barrier
+        sb_stage_x<B, 64 * NW, XT>(xcol, kSbWeights * nsb, xs, xvec != 0, q6k_slot);   // ends with a barrier
     }
     // Two register buffers used in turn; once the load cursor is past the
     // wave's last step, the step in hand is the last one: it is computed
@@ -291,143 +247,20 @@ __global__ __launch_bounds__(kThreads) void q6k_dequant_kernel(const uint8_t* __
     }
 }
 
-template <int B, int LPR, int NW, class XT>
-int32_t q6k_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
-                   hipStream_t st) {
-    auto kern = q6k_kernel<B, LPR, NW, XT>;
-    const size_t lds = (size_t)B * 4 * nsb * kQ6KXPad * sizeof(float);
-    size_t dyn_max = 0;
-    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv_q6_k", &dyn_max)) return e;
-    if (lds > dyn_max) return fail(QMV_EINVAL, "qmv_q6_k: %zu bytes of staged activations exceed the LDS", lds);
-    constexpr int rows_per_wg = NW * (64 / LPR);
-    const int64_t tiles = (N + rows_per_wg - 1) / rows_per_wg;
-    const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds));
-    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
-    const int xvec = (aligned(x, XIn<XT>::kVecAlign) && ldx % 4 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nsb, x, ldx, y, ldy, xvec);
-    return check_launch("qmv_q6_k");
-}
-
-// Lanes per row: the widest split of 64 / 32 / 16 / 8 lanes that leaves at
-// most 1/16 of a row's lane-steps idle, else the split with the fewest idle
-// (the same rule as for Q4_K: groups of 64 weights per lane).
-inline int q6k_pick_lpr(int G) {
-    int best = 8;
-    int64_t best_idle = 1 << 30, best_span = 1;
-    for (const int l : {64, 32, 16, 8}) {
-        if (l > G && l != 8) continue;
-        const int64_t span = (G + l - 1) / l * l;
-        const int64_t idle = span - G;
-        if (16 * idle <= span) return l;
-        if (idle * best_span < best_idle * span) {
-            best = l;
-            best_idle = idle;
-            best_span = span;
-        }
-    }
-    return best;
-}
-
-template <int B, class XT>
-int32_t q6k_launch_lpr(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
-                       hipStream_t st) {
-    switch (q6k_pick_lpr(4 * nsb)) {
-    case 64: return q6k_launch<B, 64, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 32: return q6k_launch<B, 32, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 16: return q6k_launch<B, 16, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    default: return q6k_launch<B, 8, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    }
-}
-
-template <class XT>
-int32_t q6k_batch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, int B, float* y, int64_t ldy,
-                  hipStream_t st) {
-    switch (B) {
-    case 1: return q6k_launch_lpr<1, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 2: return q6k_launch_lpr<2, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 3: return q6k_launch_lpr<3, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 4: return q6k_launch_lpr<4, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 5: return q6k_launch_lpr<5, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 6: return q6k_launch_lpr<6, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 7: return q6k_launch_lpr<7, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    default: return q6k_launch_lpr<8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    }
-}
-
-template <class XT>
-int32_t q6k_matvec_t(const char* name, const void* W, int64_t N, int64_t K, const XT* x, int64_t ldx, int32_t batch,
-                     float* y, int64_t ldy, void* stream) {
-    if (!W || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
-    if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
-    if (K < kQ6KWeights || K % kQ6KWeights)
-        return fail(QMV_EINVAL, "%s: n_cols must be a positive multiple of 256 for Q6_K (got %lld)", name,
-                    (long long)K);
-    if (batch < 1 || batch > 8) return fail(QMV_EINVAL, "%s: batch must be in 1..8 (got %d)", name, batch);
-    if (ldx < K) return fail(QMV_EINVAL, "%s: ldx (%lld) < n_cols (%lld)", name, (long long)ldx, (long long)K);
-    if (ldy < N) return fail(QMV_EINVAL, "%s: ldy (%lld) < n_rows (%lld)", name, (long long)ldy, (long long)N);
-    if (K / kQ6KWeights > (1 << 24) || N > ((int64_t)1 << 40) / (K / kQ6KWeights))
-        return fail(QMV_EINVAL, "%s: matrix too large (%lld x %lld)", name, (long long)N, (long long)K);
-    if (!aligned(W, 4)) return fail(QMV_EALIGN, "%s: W must be 4-byte aligned for Q6_K", name);
-    if (!aligned(y, 4)) return fail(QMV_EALIGN, "%s: y must be 4-byte aligned", name);
-    if (!aligned(x, sizeof(XT))) return fail(QMV_EALIGN, "%s: x must be aligned to its element size", name);
-    const int nsb = (int)(K / kQ6KWeights);
-    const int per_col = 4 * nsb * kQ6KXPad * (int)sizeof(float);
-    if (per_col > kLdsMax)
-        return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
-    const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / per_col));
-    for (int b0 = 0; b0 < batch; b0 += per_pass) {
-        const int bw = std::min(per_pass, batch - b0);
-        const int32_t rc = q6k_batch<XT>(static_cast<const uint8_t*>(W), N, nsb, x + b0 * ldx, ldx, bw,
-                                         y + b0 * ldy, ldy, as_stream(stream));
-        if (rc != QMV_OK) return rc;
-    }
-    return ok();
-}
-
-int32_t q6k_matvec(const char* name, const void* W, int64_t N, int64_t K, const void* x, int32_t x_type, int64_t ldx,
-                   int32_t batch, float* y, int64_t ldy, void* stream, int32_t path) {
-    if (path == QMV_PATH_MFMA)
-        return fail(QMV_EUNSUPPORTED, "%s: Q6_K has no matrix-core kernel (use QMV_PATH_AUTO or QMV_PATH_FMA)", name);
-    switch (x_type) {
-    case QMV_X_F32: return q6k_matvec_t(name, W, N, K, static_cast<const float*>(x), ldx, batch, y, ldy, stream);
-    case QMV_X_F16: return q6k_matvec_t(name, W, N, K, static_cast<const _Float16*>(x), ldx, batch, y, ldy, stream);
-    case QMV_X_BF16: return q6k_matvec_t(name, W, N, K, static_cast<const __bf16*>(x), ldx, batch, y, ldy, stream);
-    default: return fail(QMV_EINVAL, "%s: unknown x_type %d", name, (int)x_type);
-    }
-}
-
-int32_t q6k_dequant(const void* W, int64_t N, int64_t K, float* out, void* stream) {
-    const char* name = "qmv_dequant";
-    if (!W || !out) return fail(QMV_EINVAL, "%s: null pointer", name);
-    if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
-    if (K < kQ6KWeights || K % kQ6KWeights)
-        return fail(QMV_EINVAL, "%s: n_cols must be a positive multiple of 256 for Q6_K (got %lld)", name,
-                    (long long)K);
-    if (N > ((int64_t)1 << 40) / K) return fail(QMV_EINVAL, "%s: matrix too large", name);
-    if (!aligned(out, 4)) return fail(QMV_EALIGN, "%s: out must be 4-byte aligned", name);
-    const int64_t nsub = N * (K / 16);
-    const int64_t grid = (nsub + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(q6k_dequant_kernel, dim3((unsigned)grid), dim3(kThreads), 0, as_stream(stream),
-                       static_cast<const uint8_t*>(W), nsub, out);
-    return check_launch(name);
-}
-
-int32_t q6k_no_moe(const char* name, bool, const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, int32_t,
-                   int32_t, const void*, int32_t, int64_t, int64_t, float*, void*) {
-    return fail(QMV_EUNSUPPORTED, "%s: Q6_K experts are not supported", name);
-}
-int32_t q6k_no_combine(const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, const float*, int32_t, int32_t,
-                       const float*, int64_t, int64_t, float*, void*) {
-    return fail(QMV_EUNSUPPORTED, "qmv_moe_combine: Q6_K experts are not supported");
-}
-bool q6k_no_group(const RowSegs&, int, const float*, hipStream_t, bool, int32_t*) { return false; }
+struct Q6KFormat {
+    static constexpr const char* kLabel = "Q6_K";
+    static constexpr const char* kEntry = "qmv_q6_k";
+    static constexpr int kWAlign = 4;          // 4-byte-aligned loads, re-aligned in registers
+    static constexpr bool kMfma = false;
+    static constexpr int kDequantWeights = 16;
+    template <int B, int LPR, int NW, class XT>
+    static auto kernel() { return q6k_kernel<B, LPR, NW, XT>; }
+    static auto dequant_kernel() { return q6k_dequant_kernel; }
+};
 
 }  // namespace
 
-const FormatOps& ops_q6_k() {
-    static const FormatOps ops = {q6k_matvec, q6k_dequant, q6k_no_moe, q6k_no_combine, q6k_no_group};
-    return ops;
-}
+const FormatOps& ops_q6_k() { return sb_format_ops<Q6KFormat>(); }
 
 }  // namespace qmv
 

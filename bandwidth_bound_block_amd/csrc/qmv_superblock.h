@@ -1,0 +1,254 @@
+// Pieces shared by the super-block formats (256 weights per super-block,
+// one lane per 64-weight group of a row): activation staging into LDS, the
+// lanes-per-row rule, and the host side of a matvec (argument checks,
+// column passes, launch shape, the matrix-core hand-off) and of the
+// dequantizer.  A format supplies a traits struct Fmt:
+//   kFmt            its qmv_fmt (for the matrix-core hand-off, when kMfma)
+//   kLabel          "Q4_K", "Q6_K" (error messages)
+//   kEntry          the C entry point's name (launch error messages)
+//   kWAlign         alignment W needs, in bytes
+//   kMfma           whether batch 2..8 may go to the matrix-core kernel
+//   kDequantWeights weights per thread of its dequant kernel
+//   template <int B, int LPR, int NW, class XT> static auto kernel()
+//                   the matvec kernel: (W, N, nsb, x, ldx, y, ldy, xvec),
+//                   with LDS for B activation rows at kSbXPad floats per
+//                   64 weights
+//   static auto dequant_kernel()   (W, n_units, out), one unit per thread
+#pragma once
+
+#include <algorithm>
+
+#include "qmv_block_decode.h"
+
+namespace qmv {
+namespace {
+
+constexpr int kSbWeights = 256;   // per super-block
+constexpr int kSbXPad = 68;       // staged floats per 64-weight lane group: 16-byte reads of
+                                  // lanes on consecutive groups start 4 banks apart
+
+// Hides a value's bits from the optimizer: a masked word then converts with
+// one byte-select convert per element instead of a bit-field extract and a
+// convert.
+__device__ __forceinline__ uint32_t opaque_bits(uint32_t v) {
+    asm("" : "+v"(v));
+    return v;
+}
+
+// Stages the B columns xcol[b][0..K) into LDS as fp32 (16-bit inputs
+// widened exactly), element e of column b at xs[b * (K / 64) * kSbXPad +
+// slot(e)]; slot maps 4-aligned runs of 4 elements to 16-byte-aligned runs.
+// Loads in batches of 4 per thread before any is stored; vec: every column
+// aligned for 4-element loads.  Ends with a barrier.
+template <int B, int NT, class XT, class Slot>
+__device__ __forceinline__ void sb_stage_x(const XT* const (&xcol)[B], int K, float* xs, bool vec, Slot slot) {
+    const int G = K >> 6;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int b = 0; b < B; ++b) {
+        float* dst = xs + b * G * kSbXPad;
+        const XT* src = xcol[b];
+        if (vec) {
+            const int K4 = K >> 2;
+            auto put = [&](int c, const float4& v) { *reinterpret_cast<float4*>(dst + slot(4 * c)) = v; };
+            for (int c0 = tid; c0 < K4; c0 += 4 * NT) {
+                const int c1 = c0 + NT, c2 = c0 + 2 * NT, c3 = c0 + 3 * NT;
+                const float4 v0 = XIn<XT>::load4(src + 4 * c0);
+                const float4 v1 = XIn<XT>::load4(src + 4 * min(c1, K4 - 1));
+                const float4 v2 = XIn<XT>::load4(src + 4 * min(c2, K4 - 1));
+                const float4 v3 = XIn<XT>::load4(src + 4 * min(c3, K4 - 1));
+                put(c0, v0);
+                if (c1 < K4) put(c1, v1);
+                if (c2 < K4) put(c2, v2);
+                if (c3 < K4) put(c3, v3);
+            }
+        } else {
+            for (int e0 = tid; e0 < K; e0 += 4 * NT) {
+                const int e1 = e0 + NT, e2 = e0 + 2 * NT, e3 = e0 + 3 * NT;
+                const float v0 = XIn<XT>::load1(src + e0);
+                const float v1 = XIn<XT>::load1(src + min(e1, K - 1));
+                const float v2 = XIn<XT>::load1(src + min(e2, K - 1));
+                const float v3 = XIn<XT>::load1(src + min(e3, K - 1));
+                dst[slot(e0)] = v0;
+                if (e1 < K) dst[slot(e1)] = v1;
+                if (e2 < K) dst[slot(e2)] = v2;
+                if (e3 < K) dst[slot(e3)] = v3;
+            }
+        }
+    }
+    __syncthreads();
+}
+
+// Lanes per row: the widest split of 64 / 32 / 16 / 8 lanes that leaves at
+// most 1/16 of a row's lane-steps idle (wide splits keep more waves busy on
+// matrices of few rows), else the split with the fewest idle: 64 for 4096
+// columns (64 groups of 64 weights), 32 for 14336 (224 groups: 7 full
+// steps, where whole waves would leave half of the fourth step idle), 16
+// for 3072 (48 groups).
+inline int sb_pick_lpr(int G) {
+    int best = 8;
+    int64_t best_idle = 1 << 30, best_span = 1;
+    for (const int l : {64, 32, 16, 8}) {
+        if (l > G && l != 8) continue;
+        const int64_t span = (G + l - 1) / l * l;   // lane-steps per row
+        const int64_t idle = span - G;
+        if (16 * idle <= span) return l;
+        if (idle * best_span < best_idle * span) {  // idle / span, exactly
+            best = l;
+            best_idle = idle;
+            best_span = span;
+        }
+    }
+    return best;
+}
+
+template <class Fmt, int B, int LPR, int NW, class XT>
+int32_t sb_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
+                  hipStream_t st) {
+    auto kern = Fmt::template kernel<B, LPR, NW, XT>();
+    const size_t lds = (size_t)B * 4 * nsb * kSbXPad * sizeof(float);
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, Fmt::kEntry, &dyn_max)) return e;
+    if (lds > dyn_max) return fail(QMV_EINVAL, "%s: %zu bytes of staged activations exceed the LDS", Fmt::kEntry, lds);
+    constexpr int rows_per_wg = NW * (64 / LPR);
+    const int64_t tiles = (N + rows_per_wg - 1) / rows_per_wg;
+    const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
+    const int xvec = (aligned(x, XIn<XT>::kVecAlign) && ldx % 4 == 0) ? 1 : 0;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nsb, x, ldx, y, ldy, xvec);
+    return check_launch(Fmt::kEntry);
+}
+
+// 8 waves per workgroup at every batch width (a workgroup of 16 would cap
+// the registers at 128, and batch 6..8 need more).
+template <class Fmt, int B, class XT>
+int32_t sb_launch_lpr(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
+                      hipStream_t st) {
+    switch (sb_pick_lpr(4 * nsb)) {
+    case 64: return sb_launch<Fmt, B, 64, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 32: return sb_launch<Fmt, B, 32, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 16: return sb_launch<Fmt, B, 16, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    default: return sb_launch<Fmt, B, 8, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    }
+}
+
+template <class Fmt, class XT>
+int32_t sb_batch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, int B, float* y, int64_t ldy,
+                 hipStream_t st) {
+    switch (B) {
+    case 1: return sb_launch_lpr<Fmt, 1, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 2: return sb_launch_lpr<Fmt, 2, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 3: return sb_launch_lpr<Fmt, 3, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 4: return sb_launch_lpr<Fmt, 4, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 5: return sb_launch_lpr<Fmt, 5, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 6: return sb_launch_lpr<Fmt, 6, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 7: return sb_launch_lpr<Fmt, 7, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    default: return sb_launch_lpr<Fmt, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    }
+}
+
+template <class Fmt, class XT>
+int32_t sb_matvec_t(const char* name, const void* W, int64_t N, int64_t K, const XT* x, int32_t x_type, int64_t ldx,
+                    int32_t batch, float* y, int64_t ldy, void* stream, int32_t path) {
+    if (!W || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
+    if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
+    if (K < kSbWeights || K % kSbWeights)
+        return fail(QMV_EINVAL, "%s: n_cols must be a positive multiple of 256 for %s (got %lld)", name, Fmt::kLabel,
+                    (long long)K);
+    if (batch < 1 || batch > 8) return fail(QMV_EINVAL, "%s: batch must be in 1..8 (got %d)", name, batch);
+    if (ldx < K) return fail(QMV_EINVAL, "%s: ldx (%lld) < n_cols (%lld)", name, (long long)ldx, (long long)K);
+    if (ldy < N) return fail(QMV_EINVAL, "%s: ldy (%lld) < n_rows (%lld)", name, (long long)ldy, (long long)N);
+    if (K / kSbWeights > (1 << 24) || N > ((int64_t)1 << 40) / (K / kSbWeights))
+        return fail(QMV_EINVAL, "%s: matrix too large (%lld x %lld)", name, (long long)N, (long long)K);
+    if (!aligned(W, Fmt::kWAlign))
+        return fail(QMV_EALIGN, "%s: W must be %d-byte aligned for %s", name, Fmt::kWAlign, Fmt::kLabel);
+    if (!aligned(y, 4)) return fail(QMV_EALIGN, "%s: y must be 4-byte aligned", name);
+    if (!aligned(x, sizeof(XT))) return fail(QMV_EALIGN, "%s: x must be aligned to its element size", name);
+    const int nsb = (int)(K / kSbWeights);
+    if constexpr (Fmt::kMfma) {
+        if (path == QMV_PATH_MFMA || (path == QMV_PATH_AUTO && use_mfma(Fmt::kFmt, N, 8 * nsb, batch))) {
+            int32_t rc = QMV_OK;
+            if (batch_matvec_mma(Fmt::kFmt, static_cast<const uint8_t*>(W), N, 8 * nsb, x, x_type, ldx, batch, y,
+                                 ldy, as_stream(stream), 0, &rc))
+                return rc == QMV_OK ? ok() : rc;
+            if (path == QMV_PATH_MFMA)
+                return fail(QMV_EUNSUPPORTED,
+                            "%s: the matrix-core path needs batch 2..8, x aligned to 4 elements (16 bytes for fp32) "
+                            "and ldx a multiple of 4", name);
+        }
+    } else {
+        if (path == QMV_PATH_MFMA)
+            return fail(QMV_EUNSUPPORTED, "%s: %s has no matrix-core kernel (use QMV_PATH_AUTO or QMV_PATH_FMA)", name,
+                        Fmt::kLabel);
+    }
+    // One activation row per column must fit the LDS; wider batches than
+    // fit go in column passes (each re-reads W).
+    const int per_col = 4 * nsb * kSbXPad * (int)sizeof(float);
+    if (per_col > kLdsMax)
+        return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
+    const int per_pass = std::max(1, std::min<int>(batch, kLdsMax / per_col));
+    for (int b0 = 0; b0 < batch; b0 += per_pass) {
+        const int bw = std::min(per_pass, batch - b0);
+        const int32_t rc = sb_batch<Fmt, XT>(static_cast<const uint8_t*>(W), N, nsb, x + b0 * ldx, ldx, bw,
+                                             y + b0 * ldy, ldy, as_stream(stream));
+        if (rc != QMV_OK) return rc;
+    }
+    return ok();
+}
+
+template <class Fmt>
+int32_t sb_matvec(const char* name, const void* W, int64_t N, int64_t K, const void* x, int32_t x_type, int64_t ldx,
+                  int32_t batch, float* y, int64_t ldy, void* stream, int32_t path) {
+    switch (x_type) {
+    case QMV_X_F32:
+        return sb_matvec_t<Fmt>(name, W, N, K, static_cast<const float*>(x), x_type, ldx, batch, y, ldy, stream, path);
+    case QMV_X_F16:
+        return sb_matvec_t<Fmt>(name, W, N, K, static_cast<const _Float16*>(x), x_type, ldx, batch, y, ldy, stream,
+                                path);
+    case QMV_X_BF16:
+        return sb_matvec_t<Fmt>(name, W, N, K, static_cast<const __bf16*>(x), x_type, ldx, batch, y, ldy, stream,
+                                path);
+    default: return fail(QMV_EINVAL, "%s: unknown x_type %d", name, (int)x_type);
+    }
+}
+
+template <class Fmt>
+int32_t sb_dequant(const void* W, int64_t N, int64_t K, float* out, void* stream) {
+    const char* name = "qmv_dequant";
+    if (!W || !out) return fail(QMV_EINVAL, "%s: null pointer", name);
+    if (N < 1) return fail(QMV_EINVAL, "%s: n_rows must be >= 1 (got %lld)", name, (long long)N);
+    if (K < kSbWeights || K % kSbWeights)
+        return fail(QMV_EINVAL, "%s: n_cols must be a positive multiple of 256 for %s (got %lld)", name, Fmt::kLabel,
+                    (long long)K);
+    if (N > ((int64_t)1 << 40) / K) return fail(QMV_EINVAL, "%s: matrix too large", name);
+    if (!aligned(W, Fmt::kWAlign))
+        return fail(QMV_EALIGN, "%s: W must be %d-byte aligned for %s", name, Fmt::kWAlign, Fmt::kLabel);
+    if (!aligned(out, 4)) return fail(QMV_EALIGN, "%s: out must be 4-byte aligned", name);
+    const int64_t units = N * (K / Fmt::kDequantWeights);
+    const int64_t grid = (units + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(Fmt::dequant_kernel(), dim3((unsigned)grid), dim3(kThreads), 0, as_stream(stream),
+                       static_cast<const uint8_t*>(W), units, out);
+    return check_launch(name);
+}
+
+// The MoE, combine and chain-group slots of a super-block format's table.
+template <class Fmt>
+int32_t sb_no_moe(const char* name, bool, const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, int32_t,
+                  int32_t, const void*, int32_t, int64_t, int64_t, float*, void*) {
+    return fail(QMV_EUNSUPPORTED, "%s: %s experts are not supported", name, Fmt::kLabel);
+}
+template <class Fmt>
+int32_t sb_no_combine(const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, const float*, int32_t, int32_t,
+                      const float*, int64_t, int64_t, float*, void*) {
+    return fail(QMV_EUNSUPPORTED, "qmv_moe_combine: %s experts are not supported", Fmt::kLabel);
+}
+inline bool sb_no_group(const RowSegs&, int, const float*, hipStream_t, bool, int32_t*) { return false; }
+
+template <class Fmt>
+const FormatOps& sb_format_ops() {
+    static const FormatOps ops = {sb_matvec<Fmt>, sb_dequant<Fmt>, sb_no_moe<Fmt>, sb_no_combine<Fmt>, sb_no_group};
+    return ops;
+}
+
+}  // namespace
+}  // namespace qmv
