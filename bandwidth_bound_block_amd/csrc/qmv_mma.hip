@@ -495,18 +495,259 @@ bool launch_mma(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx, i
     return true;
 }
 
+// Q6_K on the matrix cores.  Its weights are d sc (c - 32) with an int8
+// scale per 16 weights, so a 32-wide MFMA step spans two scales: the scale
+// goes into the B operand.  p = 4 (c - 32) sc is an integer of at most 15
+// bits (exact in fp32) and splits exactly into two bf16 pieces, hi =
+// RN_bf16(p) and lo = p - hi (at most 7 significant bits); both pieces are
+// multiplied into one accumulator per super-block, and d / 4 (exact) scales
+// its sum.  No operand is rounded, so the bound is that of the split
+// activations, as for the other formats.  The weights go straight to
+// registers: 210-byte super-blocks start 2 bytes past a word at every other
+// index, so each 8-byte piece is read as 4-byte-aligned words (16 bytes
+// from 0 or 2 bytes before it, inside the super-block or the one before)
+// and re-aligned with v_alignbyte.  A wave step is one super-block of 16
+// rows: lane (g, r) takes row r and, of each 32-weight chunk j = 4 h + q,
+// the codes 8g..8g+7 (low 4 bits from ql[64 h + 32 (q & 1) + 8 g ..], high
+// 2 bits from qh[32 h + 8 g ..]).
+struct Q6KSuper {};
+template <> struct Mma<Q6KSuper> {
+    static constexpr bool kSums = false;
+    __device__ static constexpr int x0(int g) { return 8 * g; }
+    __device__ static constexpr int x1(int g) { return 8 * g + 4; }
+};
+
+struct Q6KLane {
+    u32x4 ql[4];        // [2 h + (q & 1)]: ql bytes 64 h + 32 (q & 1) + 8 g - sh .. +16
+    u32x4 qh[2];        // [h]: qh bytes 32 h + 8 g - sh .. +16
+    u32x4 t;            // bytes 192 - sh .. +16 (the scales)
+    uint32_t u, dh, sh; // sc[14..15], d, 0 or 2
+};
+
+__device__ __forceinline__ void q6k_lane_fetch(const uint8_t* sb, int g, Q6KLane& r) {
+    const int sh = (int)(reinterpret_cast<uintptr_t>(sb) & 2);
+    const uint8_t* p = sb - sh;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) r.ql[k] = ld16(p + 64 * (k >> 1) + 32 * (k & 1) + 8 * g);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) r.qh[h] = ld16(p + 128 + 32 * h + 8 * g);
+    r.t = ld16(p + 192);
+    r.u = ld2(sb + 206);
+    r.dh = ld2(sb + 208);
+    r.sh = (uint32_t)sh;
+}
+
+// 4 (c - 32) for four codes of quarter q as signed bytes: lo holds their 4
+// low bits at bits 0-3 (q < 2) or 4-7, hf the qh word with the top bit of
+// every 2-bit field flipped.
+__device__ __forceinline__ uint32_t q6k_code_bytes(uint32_t lo, uint32_t hf, int q) {
+    const uint32_t l = q < 2 ? (lo << 2) : (lo >> 2);
+    const uint32_t h = (hf << (6 - 2 * q)) & 0xc0c0c0c0u;
+    return (l & 0x3c3c3c3cu) | h;
+}
+
+template <int NW, class XT>
+__global__ __launch_bounds__(64 * NW) void q6k_mma_kernel(const uint8_t* __restrict__ W, int N, int nsb,
+                                                          const XT* __restrict__ x, int64_t ldx, int B,
+                                                          float* __restrict__ y, int64_t ldy, int KP, int KC) {
+    constexpr int kSlot = 16 * 20 * 4;                  // a wave's 16 x 16 partial sums (rows of 20)
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int TPI = NW / KP, ts = wave / KP, kp = wave % KP;
+    const int nb = 8 * nsb;                             // 32-weight blocks per row
+    const int tiles = (N + 15) >> 4;
+    const int ngroups = (tiles + TPI - 1) / TPI;
+    const int CS = KC / 8;                              // super-blocks per chunk (a multiple of KP)
+    const int nchunks = (nsb + CS - 1) / CS;
+    const int ipg = nsb / KP;                           // items per wave per tile group
+    const int ipc = CS / KP;                            // items per wave per full chunk
+    const int kcp = KC | 1;
+    const int64_t pitch = (int64_t)nsb * 210;
+
+    uint8_t* xs = lds;                                  // [4 * 2B][kcp] x 16 B
+    uint8_t* slots = xs + 128 * B * kcp;
+    uint8_t* slot = slots + wave * kSlot;
+
+    const int g = lane >> 4, r = lane & 15;
+    const uint8_t* a_base = xs + (g * 2 * B + r % (2 * B)) * kcp * 16;
+    const int my_groups = (ngroups - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+    const int total = my_groups > 0 ? my_groups * ipg : 0;
+
+    // Loads item n (past the last one: the last one again, so every pipeline
+    // slot loads unconditionally); rows past the end re-read the last row.
+    auto load = [&](int n, Q6KLane& buf) __attribute__((always_inline)) {
+        n = min(n, total - 1);
+        const int it = blockIdx.x + (n / ipg) * gridDim.x;
+        const int s = kp + KP * (n % ipg);
+        const int row = min(16 * (it * TPI + ts) + r, N - 1);
+        q6k_lane_fetch(W + (int64_t)row * pitch + (int64_t)s * 210, g, buf);
+    };
+
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    auto item = [&](int n, const Q6KLane& w) __attribute__((always_inline)) {
+        const int nig = n % ipg;
+        const int c = nig / ipc;
+        if (nig % ipc == 0 && (nchunks > 1 || n == 0)) {
+            const int b0 = c * KC;
+            __syncthreads();
+            stage_pieces<Q6KSuper, 64 * NW, XT>(x, ldx, B, b0, min(KC, nb - b0), kcp, xs, nullptr);
+            __syncthreads();
+        }
+        const int cb = (kp + KP * nig) * 8 - c * KC;   // first block of the super-block in the chunk
+        uint32_t L[4][2], H[2][2], S[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            L[k][0] = __builtin_amdgcn_alignbyte(w.ql[k].y, w.ql[k].x, w.sh);
+            L[k][1] = __builtin_amdgcn_alignbyte(w.ql[k].z, w.ql[k].y, w.sh);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            H[h][0] = __builtin_amdgcn_alignbyte(w.qh[h].y, w.qh[h].x, w.sh) ^ 0xaaaaaaaau;
+            H[h][1] = __builtin_amdgcn_alignbyte(w.qh[h].z, w.qh[h].y, w.sh) ^ 0xaaaaaaaau;
+        }
+        {
+            const uint32_t t5[5] = {w.t.x, w.t.y, w.t.z, w.t.w, w.u};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[i] = __builtin_amdgcn_alignbyte(t5[i + 1], t5[i], w.sh);
+        }
+        const int sb_sh = 8 * (g >> 1);
+        f32x4 dsum = {0.f, 0.f, 0.f, 0.f};
+        static_for(std::make_integer_sequence<int, 8>{}, [&](auto jc) __attribute__((always_inline)) {
+            constexpr int J = decltype(jc)::value, h = J >> 2, q = J & 3;
+            // scale sc[2 J + g / 2]
+            const float sc = (float)(int8_t)(S[J >> 1] >> (16 * (J & 1) + sb_sh));
+            const uint32_t v[2] = {q6k_code_bytes(L[2 * h + (q & 1)][0], H[h][0], q),
+                                   q6k_code_bytes(L[2 * h + (q & 1)][1], H[h][1], q)};
+            uint32_t bh[4], bl[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const float p0 = sbyte(v[k >> 1], 2 * (k & 1)) * sc;       // exact: <= 15 bits
+                const float p1 = sbyte(v[k >> 1], 2 * (k & 1) + 1) * sc;
+                bh[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0, p1}, bf16x2));
+                const float h0 = __builtin_bit_cast(float, bh[k] << 16);
+                const float h1 = __builtin_bit_cast(float, bh[k] & 0xffff0000u);
+                bl[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{p0 - h0, p1 - h1}, bf16x2));
+            }
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(a_base + (cb + J) * 16);
+            dsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bh), dsum, 0, 0, 0);
+            dsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf16x8, bl), dsum, 0, 0, 0);
+        });
+        const float d4 = half_bits_to_float(w.dh) * 0.25f;   // exact
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(d4, dsum[i], acc[i]);
+        if (nig == ipg - 1) {
+            // tile group done: partials of every wave through the slots
+            const int it = blockIdx.x + (n / ipg) * gridDim.x;
+            __syncthreads();
+            *reinterpret_cast<f32x4*>(slot + (r * 20 + 4 * g) * 4) = f32x4{acc[0], acc[1], acc[2], acc[3]};
+            __syncthreads();
+            const int outs = TPI * 16 * B;
+            for (int t = tid; t < outs; t += 64 * NW) {
+                const int tsl = t / (16 * B), rem = t % (16 * B), b = rem >> 4, rr = rem & 15;
+                const int row = 16 * (it * TPI + tsl) + rr;
+                float v = 0.f;
+                for (int q = 0; q < KP; ++q) {
+                    const float* pw = reinterpret_cast<const float*>(slots + (tsl * KP + q) * kSlot) + rr * 20;
+                    v += pw[b];
+                    v += pw[B + b];
+                }
+                if (row < N) y[b * ldy + row] = v;
+            }
+            __syncthreads();
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = 0.f;
+        }
+    };
+
+    // Two register buffers: the next item's loads are in flight while an
+    // item is computed.
+    if (total == 0) return;
+    Q6KLane buf[2];
+    load(0, buf[0]);
+    for (int n = 0; n < total; n += 2) {
+        load(n + 1, buf[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        item(n, buf[0]);
+        if (n + 1 >= total) break;
+        load(n + 2, buf[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        item(n + 1, buf[1]);
+    }
+}
+
+template <int NW, class XT>
+bool launch_q6k_mma(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, int B, float* y, int64_t ldy,
+                    hipStream_t st, int kp_force, int32_t* rc) {
+    constexpr int kSlot = 16 * 20 * 4;
+    const size_t fixed = (size_t)NW * kSlot;
+    const size_t per_blk = 128 * (size_t)B;             // staged pieces per 32-weight block
+    if (fixed + 9 * per_blk > (size_t)kLdsMax) return false;
+    const int64_t tiles = (N + 15) / 16;
+    const int cus = device_cu_count();
+    int KP = 1;
+    if (kp_force > 0) {
+        KP = kp_force;
+        if (NW % KP || nsb % KP) return false;
+    } else {
+        while (KP < NW && nsb % (2 * KP) == 0 && (tiles + NW / KP - 1) / (NW / KP) < cus) KP *= 2;
+    }
+    // super-blocks per chunk: a multiple of KP
+    int cs_max = 0;
+    for (;; KP /= 2) {
+        cs_max = (int)((kLdsMax - fixed) / per_blk - 1) / 8 / KP * KP;
+        if (cs_max >= KP) break;
+        if (KP == 1) return false;
+    }
+    const int nchunks = (nsb + cs_max - 1) / cs_max;
+    const int cs = ((nsb + nchunks - 1) / nchunks + KP - 1) / KP * KP;
+    const int KC = cs * 8;
+    const size_t lds = fixed + (size_t)(KC | 1) * per_blk;
+
+    auto kern = q6k_mma_kernel<NW, XT>;
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv", &dyn_max)) {
+        *rc = e;
+        return true;
+    }
+    if (lds > dyn_max) {
+        *rc = fail(QMV_EINVAL, "qmv: %zu bytes of staged activations exceed the LDS", lds);
+        return true;
+    }
+    const int64_t ngroups = (tiles + NW / KP - 1) / (NW / KP);
+    const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(ngroups, (int64_t)cus * per_cu));
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, (int)N, nsb, x, ldx, B, y, ldy, KP, KC);
+    *rc = check_launch("qmv");
+    return true;
+}
+
+template <class XT>
+bool launch_q6k_mma_auto(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, int B, float* y,
+                         int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
+    if (!aligned(x, XIn<XT>::kVecAlign)) return false;
+    const int nw = (variant >> 8) == 16 ? 16 : 8;
+    const int kp = variant & 0xff;
+    return nw == 16 ? launch_q6k_mma<16, XT>(W, N, nsb, x, ldx, B, y, ldy, st, kp, rc)
+                    : launch_q6k_mma<8, XT>(W, N, nsb, x, ldx, B, y, ldy, st, kp, rc);
+}
+
 }  // namespace
 
 // Measured on the 8B decode shapes (4096..128256 rows, 4096 and 14336
 // columns, cache-cold): the matrix-core kernel is faster from batch 3 on
 // for the 32-weight block formats, and at batch 2 for Q4_0 (at batch 2 the
-// FMA kernels still win most Q8_0 and Q4_1 shapes).  Q4_K's FMA kernel
-// holds out longer (its matrix-core operand decodes two 6-bit fields and a
-// pivot per sub-block): 14336 x 4096 at batch 3 / 4 / 8 17.9 / 19.5 / 38.2 us
+// FMA kernels still win most Q8_0 and Q4_1 shapes).  The super-block
+// formats' FMA kernels hold out longer on 4096-column rows (their
+// matrix-core operands decode 6-bit fields and a pivot, or split scaled
+// codes in two): Q4_K 14336 x 4096 at batch 3 / 4 / 8 17.9 / 19.5 / 38.2 us
 // against 21.0 / 22.5 / 22.8, 4096 x 14336 27.8 / 31.4 / 61.3 against
-// 24.0 / 24.7 / 31.0, 128256 x 4096 at batch 2 111 against 106.
+// 24.0 / 24.7 / 31.0, 128256 x 4096 at batch 2 111 against 106; Q6_K
+// 14336 x 4096 21.2 / 23.7 / 42.5 against 27.6 / 27.0 / 28.7, 4096 x 14336
+// 32.4 / 38.5 / 71.6 against 28.5 / 29.7 / 35.3.
 bool use_mfma(qmv_fmt fmt, int64_t N, int nb, int B) {
-    if (fmt == QMV_Q4_K) return B >= 5 || (B >= 3 && nb >= 256) || (B >= 2 && N >= 65536);
+    if (fmt == QMV_Q4_K || fmt == QMV_Q6_K) return B >= 5 || (B >= 3 && nb >= 256) || (B >= 2 && N >= 65536);
     return B >= 3 || (B == 2 && fmt == QMV_Q4_0);
 }
 
@@ -544,6 +785,19 @@ bool launch_mma_x(const uint8_t* W, int64_t N, int nb, const void* x, int32_t x_
 
 bool batch_matvec_mma(qmv_fmt fmt, const uint8_t* W, int64_t N, int nb, const void* x, int32_t x_type, int64_t ldx,
                       int B, float* y, int64_t ldy, hipStream_t st, int variant, int32_t* rc) {
+    if (fmt == QMV_Q6_K) {
+        const int nsb = nb / 8;
+        if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || !aligned(W, 4) || ldx % 4) return false;
+        switch (x_type) {
+        case QMV_X_F32:
+            return launch_q6k_mma_auto(W, N, nsb, static_cast<const float*>(x), ldx, B, y, ldy, st, variant, rc);
+        case QMV_X_F16:
+            return launch_q6k_mma_auto(W, N, nsb, static_cast<const _Float16*>(x), ldx, B, y, ldy, st, variant, rc);
+        case QMV_X_BF16:
+            return launch_q6k_mma_auto(W, N, nsb, static_cast<const __bf16*>(x), ldx, B, y, ldy, st, variant, rc);
+        default: return false;
+        }
+    }
     const int64_t pitch = (int64_t)nb * (fmt == QMV_Q8_0 ? 34 : (fmt == QMV_Q4_1 ? 20 : 18));   // Q4_0, Q4_K: 18
     if (B < 2 || B > 8 || nb % 8 || N > (1 << 30) || pitch >= (1 << 24) || !aligned(W, 16) || ldx % 4) return false;
     switch (fmt) {

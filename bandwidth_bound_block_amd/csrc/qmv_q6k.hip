@@ -248,10 +248,11 @@ __global__ __launch_bounds__(kThreads) void q6k_dequant_kernel(const uint8_t* __
 }
 
 struct Q6KFormat {
+    static constexpr qmv_fmt kFmt = QMV_Q6_K;
     static constexpr const char* kLabel = "Q6_K";
     static constexpr const char* kEntry = "qmv_q6_k";
     static constexpr int kWAlign = 4;          // 4-byte-aligned loads, re-aligned in registers
-    static constexpr bool kMfma = false;
+    static constexpr bool kMfma = true;        // batch 2..8: q6k_mma_kernel
     static constexpr int kDequantWeights = 16;
     template <int B, int LPR, int NW, class XT>
     static auto kernel() { return q6k_kernel<B, LPR, NW, XT>; }

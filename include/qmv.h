@@ -156,13 +156,17 @@ int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
  *           staged in LDS, 68 floats per 64 columns).
  *   x, batch, y as qmv_q8_0.
  * Codes are exact signed integers and each 16-weight sum is scaled by the
- * exact d*sc, so the accuracy bound holds on every input.  Deterministic; a
- * column's result is the same bitwise at every batch width.
+ * exact d*sc, so the accuracy bound holds on every input.  Deterministic; on
+ * the FMA kernel a column's result is the same bitwise at every batch width.
+ * Batch 2..8 may run on the matrix cores (sc*(c-32) split exactly into two
+ * bf16 pieces; within the same bound, columns independent of the batch
+ * width among themselves); qmv_matvec_path chooses the family.
  * Errors: QMV_EINVAL (as qmv_q8_0, with multiples of 256), QMV_EALIGN (W,
  * x or y not 4-byte aligned), QMV_EHIP.
  * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q6_K (matvec on
- * QMV_PATH_AUTO or QMV_PATH_FMA; QMV_PATH_MFMA gives QMV_EUNSUPPORTED); the
- * MoE entry points and qmv_chain do not (QMV_EUNSUPPORTED).
+ * every path; QMV_PATH_MFMA needs batch 2..8, x aligned to 4 elements and
+ * ldx a multiple of 4, else QMV_EUNSUPPORTED); the MoE entry points and
+ * qmv_chain do not (QMV_EUNSUPPORTED).
  */
 int32_t qmv_q6_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,

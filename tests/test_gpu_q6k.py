@@ -12,7 +12,10 @@ of 64 weights), rows in ragged counts against the workgroups, and the
 8B-shaped layer matrices at full size with sampled rows.  Dequantization is
 bitwise the oracle's values (exact in fp32); 16-bit activations
 give bitwise the fp32 call on the widened values; a column is bitwise the
-same at every batch width and over repeated calls.
+same at every batch width and over repeated calls.  The matrix-core path is
+checked the same way: against the oracle on the shapes above, random bytes
+and zero-heavy rows, bitwise position- and width-independent columns,
+16-bit activations.
 """
 import functools
 import sys
@@ -147,6 +150,7 @@ def test_q6k_zero_heavy(env, B):
 
 
 def test_q6k_columns_equal_batch1_and_deterministic(env):
+    """The FMA kernel: every column bitwise its batch-1 result."""
     torch, qmv = env
     N, K = 1000, 4096
     W = dev(torch, wl.quant_weights("q6_k", "t/q6k/det", N, K))
@@ -155,7 +159,7 @@ def test_q6k_columns_equal_batch1_and_deterministic(env):
     for B in (2, 3, 5, 8):
         say(f"q6_k columns B={B}")
         for rep in range(2):
-            y = qmv.qmv_q6_k(W, N, K, x[:B])
+            y = qmv.qmv_matvec_path("q6_k", W, N, K, x[:B], qmv.PATH_FMA)
             torch.cuda.synchronize()
             for b in range(B):
                 assert torch.equal(y[b].view(torch.int32), ref[b].view(torch.int32)), (B, b, rep)
@@ -217,3 +221,74 @@ def test_q6k_llama8b_layer_set(env, B):
                                          np.random.default_rng(N + K).choice(N, 512, replace=False)]))
         yr, S = oracle.matvec("q6_k", W, N, K, x, rows=rows)
         assert_tol(y.cpu().numpy()[:, rows], yr, S, (name, B))
+
+
+# ------------------------------------------------------------------ matrix cores
+MMA_SHAPES = [(1, 256), (37, 768), (130, 1024), (257, 2048), (65, 4096), (300, 4096), (5, 14336), (33, 36352),
+              (2100, 4096)]
+
+
+@pytest.mark.parametrize("B", [2, 3, 5, 8])
+def test_q6k_mfma_shapes(env, B):
+    """The matrix-core path (scales folded into two exact bf16 pieces of
+    the codes) against the oracle; the automatic path too, and at batch >= 5
+    it takes the matrix cores for every shape (bitwise the same)."""
+    torch, qmv = env
+    for N, K in MMA_SHAPES:
+        say(f"q6_k mfma B={B} {N}x{K}")
+        W = wl.quant_weights("q6_k", f"t/q6k/{N}x{K}", N, K)
+        Wd = dev(torch, W)
+        x = wl.activations(f"t/q6k/mx/{K}/{B}", B, K)
+        xd = dev(torch, x)
+        y = qmv.qmv_matvec_path("q6_k", Wd, N, K, xd, qmv.PATH_MFMA)
+        ya = qmv.qmv_q6_k(Wd, N, K, xd)
+        torch.cuda.synchronize()
+        yr, S = oracle.matvec("q6_k", W, N, K, x)
+        assert_tol(y.cpu().numpy(), yr, S, (N, K, B))
+        assert_tol(ya.cpu().numpy(), yr, S, ("auto", N, K, B))
+        if B >= 5:
+            assert torch.equal(y.view(torch.int32), ya.view(torch.int32)), (N, K, B)
+
+
+def test_q6k_mfma_random_and_zero_heavy(env):
+    """Random super-block bytes (d over the whole fp16 range, int8 scales
+    and codes at their extremes) and zero-heavy rows on the matrix cores."""
+    torch, qmv = env
+    g = np.random.default_rng(29)
+    for N, K, B in [(64, 1024, 3), (300, 2048, 8), (19, 4096, 2)]:
+        say(f"q6_k mfma random bytes B={B} {N}x{K}")
+        W = random_super_blocks(2000 + K, N, K)
+        x = (g.standard_normal((B, K)) * np.exp(g.uniform(-6, 6, size=(B, K)))).astype(np.float32)
+        y = qmv.qmv_matvec_path("q6_k", dev(torch, W), N, K, dev(torch, x), qmv.PATH_MFMA)
+        torch.cuda.synchronize()
+        yr, S = oracle.matvec("q6_k", W, N, K, x)
+        assert_tol(y.cpu().numpy(), yr, S, ("random", N, K, B))
+    for N, K, B in [(700, 4096, 3), (300, 14336, 8), (9, 512, 4)]:
+        say(f"q6_k mfma zero-heavy B={B} {N}x{K}")
+        W, x = wl.zero_heavy("q6_k", f"t/q6k/mzh/{N}x{K}", N, K, B=B)
+        y = qmv.qmv_matvec_path("q6_k", dev(torch, W), N, K, dev(torch, x), qmv.PATH_MFMA)
+        torch.cuda.synchronize()
+        yr, S = oracle.matvec("q6_k", W, N, K, x)
+        assert_tol(y.cpu().numpy(), yr, S, ("zero-heavy", N, K, B))
+
+
+def test_q6k_mfma_columns_independent_and_x16(env):
+    """On the matrix cores a column gives bitwise the same result at every
+    width 2..8 and position, over repeated calls; f16/bf16 activations give
+    bitwise the fp32 call on the widened values."""
+    torch, qmv = env
+    N, K = 1000, 4096
+    Wd = dev(torch, wl.quant_weights("q6_k", "t/q6k/mdet", N, K))
+    x = dev(torch, wl.activations("t/q6k/mdet/x", 8, K))
+    full = qmv.qmv_matvec_path("q6_k", Wd, N, K, x, qmv.PATH_MFMA)
+    for B in (2, 3, 5, 8):
+        for off in (0, 8 - B):
+            y = qmv.qmv_matvec_path("q6_k", Wd, N, K, x[off:off + B], qmv.PATH_MFMA)
+            torch.cuda.synchronize()
+            assert torch.equal(y.view(torch.int32), full[off:off + B].view(torch.int32)), (B, off)
+    for kind in ("f16", "bf16"):
+        xh = x.to(torch.float16 if kind == "f16" else torch.bfloat16)
+        y16 = qmv.qmv_matvec_xt("q6_k", Wd, N, K, xh, qmv.PATH_MFMA)
+        y32 = qmv.qmv_matvec_path("q6_k", Wd, N, K, xh.float(), qmv.PATH_MFMA)
+        torch.cuda.synchronize()
+        assert torch.equal(y16.view(torch.int32), y32.view(torch.int32)), kind
