@@ -52,6 +52,8 @@ def row_bytes(fmt, n_cols):
         w, b = SUPER_BLOCK[f]
         return n_cols // w * b
     return n_cols // 32 * BLOCK_BYTES.get(f, 0)
+
+
 PATH_AUTO, PATH_FMA, PATH_MFMA = 0, 1, 2
 X_F32, X_F16, X_BF16 = 0, 1, 2
 _ERRORS = {1: "QMV_EINVAL", 2: "QMV_EALIGN", 3: "QMV_EUNSUPPORTED", 4: "QMV_EHIP"}
@@ -322,7 +324,7 @@ def _moe_args(fmt, W_experts, expert_stride_bytes, n_experts, rows, n_cols, expe
         st_tok, st_slot = T * n_cols, n_cols
     else:
         raise ValueError("x must be [B, K] or [B, top_k, K]")
-    if W_experts.numel() < (n_experts - 1) * expert_stride_bytes + rows * (n_cols // 32) * BLOCK_BYTES.get(fmt, 0):
+    if W_experts.numel() < (n_experts - 1) * expert_stride_bytes + rows * row_bytes(fmt, n_cols):
         raise ValueError("W_experts is smaller than n_experts expert matrices")
     return torch, fmt, B, T, st_tok, st_slot
 

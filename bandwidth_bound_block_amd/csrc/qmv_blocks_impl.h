@@ -37,18 +37,23 @@
 #include "qmv_block_decode.h"
 
 namespace qmv {
+#ifndef QMV_MOE_PAIRS_MAX_BATCH
+#define QMV_MOE_PAIRS_MAX_BATCH 8
+#endif
+
 namespace {
 
 // ------------------------------------------------------------------ kernels
-// Routing of the dense kernel (ROUTE = true): grid row p (blockIdx.y)
-// computes pair p of a single token's expert list, with expert ids[p]
-// (weights at ids[p] * estride), activations at p * xs_slot and outputs at
-// p * ldy.  An id outside [0, n_experts) makes that pair's outputs quiet NaN.
+// Routing of the dense kernel (ROUTE = true): grid row p = b * top_k + s
+// (blockIdx.y) computes the pair (token b, slot s), with expert ids[p]
+// (weights at ids[p] * estride), activations at b * xs_tok + s * xs_slot
+// and outputs at p * ldy.  An id outside [0, n_experts) makes that pair's
+// outputs quiet NaN.
 struct PairRoute {
     const int32_t* ids;
     int64_t estride;
-    int64_t xs_slot;
-    int32_t n_experts;
+    int64_t xs_tok, xs_slot;
+    int32_t top_k, n_experts;
 };
 
 // SiLU(g) = g / (1 + e^-g), in fp32 on the device (expf of the device
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel(const uint8_t* __restrict_
         const int e = route.ids[p];          // uniform: one scalar load
         bad = e < 0 || e >= route.n_experts;
         W += (int64_t)(bad ? 0 : e) * route.estride;
-        x += (int64_t)p * route.xs_slot;
+        x += (int64_t)(p / route.top_k) * route.xs_tok + (int64_t)(p % route.top_k) * route.xs_slot;
         y += (int64_t)p * ldy;
     }
 
@@ -1077,7 +1082,8 @@ int32_t launch_moe_bc(const uint8_t* Wx, int64_t estride, int n_experts, int64_t
 // expert ids[p] with no prologue at all.
 template <class F, int LPR, int XU, class XT, bool SW>
 int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
-                         int top_k, const XT* x, int64_t xs_slot, float* y, hipStream_t st) {
+                         int batch, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y,
+                         hipStream_t st) {
     constexpr int NW = 4;
     // Q4_x: two rows per lane, as the dense batch-1 kernel; SwiGLU: the
     // gate and up rows of an output row
@@ -1090,10 +1096,11 @@ int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int6
     if (lds > dyn_max) return fail(QMV_EINVAL, "qmv_moe: %zu bytes of staged activations exceed the LDS", lds);
     const int per_cu = resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds);
     const int64_t tiles = (N + NW * (64 / LPR) * OUT_RPL - 1) / (NW * (64 / LPR) * OUT_RPL);
-    const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu / top_k));
-    const PairRoute route{ids, estride, xs_slot, n_experts};
-    hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)top_k), dim3(64 * NW), lds, st, Wx, N, nb, x, (int64_t)nb * 32,
-                       y, N, 1, route);
+    const int pairs = batch * top_k;
+    const int64_t gx = std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu / pairs));
+    const PairRoute route{ids, estride, xs_tok, xs_slot, top_k, n_experts};
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)pairs), dim3(64 * NW), lds, st, Wx, N, nb, x,
+                       (int64_t)nb * 32, y, N, 1, route);
     return check_launch("qmv_moe");
 }
 
@@ -1102,10 +1109,13 @@ int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t
                       int batch, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
     const int K4 = nb * 8;   // 4-element chunks of one activation row; 256 threads
-    if (batch == 1 && xvec && K4 <= 4 * 256)
-        return launch_moe_pairs<F, LPR, 4, XT, SW>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
-    if (batch == 1 && xvec && K4 <= 16 * 256)
-        return launch_moe_pairs<F, LPR, 16, XT, SW>(Wx, estride, n_experts, N, nb, ids, top_k, x, xs_slot, y, st);
+    const bool pairs = batch <= QMV_MOE_PAIRS_MAX_BATCH && xvec;
+    if (pairs && K4 <= 4 * 256)
+        return launch_moe_pairs<F, LPR, 4, XT, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok,
+                                                   xs_slot, y, st);
+    if (pairs && K4 <= 16 * 256)
+        return launch_moe_pairs<F, LPR, 16, XT, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok,
+                                                    xs_slot, y, st);
     if (K4 <= 2 * 256)
         return launch_moe_bc<F, LPR, 2, SW, XT>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok, xs_slot, y,
                                                 xvec, st);

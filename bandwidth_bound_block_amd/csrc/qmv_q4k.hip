@@ -63,10 +63,12 @@ __device__ __forceinline__ void q4k_scale_min(const u32x4& h, int s, int& sc, in
 // A wave step covers RW = 64 / LPR rows, one per segment of LPR lanes.
 // (Two rows per lane, each staged activation read feeding both, measured
 // slower at every batch width: 123-228 VGPRs against 63-160.)
-template <int B, int LPR, int NW, class XT>
+template <int B, int LPR, int NW, class XT, bool ROUTE>
 __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
                                                        const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
-                                                       int64_t ldy, int xvec) {
+                                                       int64_t ldy, int xvec, const SbRoute route) {
+    bool bad = false;   // routed pair with an invalid expert id: its outputs become NaN
+    if constexpr (ROUTE) bad = sb_route(route, W, x, y, ldy);
     extern __shared__ __attribute__((aligned(16))) float lds[];
     float* xs = lds;                          // [B][4 nsb][kSbXPad], x[b][64 g + e] at [b][g][e]
     constexpr int RW = 64 / LPR;              // rows per tile
@@ -134,7 +136,7 @@ __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict_
             for (int b = 0; b < B; ++b) {
                 const float tot = segment_sum<LPR>(acc[b]);
                 const int64_t row = tile * RW + seg;
-                if (li == 0 && row < N) y[b * ldy + row] = tot;
+                if (li == 0 && row < N) y[b * ldy + row] = bad ? __builtin_nanf("") : tot;
                 acc[b] = 0.f;
             }
         }
@@ -216,8 +218,9 @@ struct Q4KFormat {
     static constexpr int kWAlign = 16;         // the kernel's aligned 16-byte loads
     static constexpr bool kMfma = true;        // batch 2..8: Mma<Q4KSuper> in the matrix-core kernel
     static constexpr int kDequantWeights = 32;
-    template <int B, int LPR, int NW, class XT>
-    static auto kernel() { return q4k_kernel<B, LPR, NW, XT>; }
+    static constexpr int kBytes = kQ4KBytes;
+    template <int B, int LPR, int NW, class XT, bool ROUTE>
+    static auto kernel() { return q4k_kernel<B, LPR, NW, XT, ROUTE>; }
     static auto dequant_kernel() { return q4k_dequant_kernel; }
 };
 

@@ -88,10 +88,12 @@ __device__ __forceinline__ int q6k_slot(int e) {
 
 // A wave step covers RW = 64 / LPR rows, one per segment of LPR lanes; lane
 // li of a segment takes lane group li + LPR t of its row in step t.
-template <int B, int LPR, int NW, class XT>
+template <int B, int LPR, int NW, class XT, bool ROUTE>
 __global__ __launch_bounds__(64 * NW) void q6k_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
                                                        const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
-                                                       int64_t ldy, int xvec) {
+                                                       int64_t ldy, int xvec, const SbRoute route) {
+    bool bad = false;   // routed pair with an invalid expert id: its outputs become NaN
+    if constexpr (ROUTE) bad = sb_route(route, W, x, y, ldy);
     extern __shared__ __attribute__((aligned(16))) float lds[];
     float* xs = lds;                          // [B][4 nsb][kSbXPad], in q6k_slot order
     constexpr int RW = 64 / LPR;              // rows per tile
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(64 * NW) void q6k_kernel(const uint8_t* __restrict_
             for (int b = 0; b < B; ++b) {
                 const float tot = segment_sum<LPR>(acc[b]);
                 const int64_t row = tile * RW + seg;
-                if (li == 0 && row < N) y[b * ldy + row] = tot;
+                if (li == 0 && row < N) y[b * ldy + row] = bad ? __builtin_nanf("") : tot;
                 acc[b] = 0.f;
             }
         }
@@ -254,8 +256,9 @@ struct Q6KFormat {
     static constexpr int kWAlign = 4;          // 4-byte-aligned loads, re-aligned in registers
     static constexpr bool kMfma = true;        // batch 2..8: q6k_mma_kernel
     static constexpr int kDequantWeights = 16;
-    template <int B, int LPR, int NW, class XT>
-    static auto kernel() { return q6k_kernel<B, LPR, NW, XT>; }
+    static constexpr int kBytes = kQ6KBytes;
+    template <int B, int LPR, int NW, class XT, bool ROUTE>
+    static auto kernel() { return q6k_kernel<B, LPR, NW, XT, ROUTE>; }
     static auto dequant_kernel() { return q6k_dequant_kernel; }
 };
 

@@ -9,10 +9,12 @@
 //   kWAlign         alignment W needs, in bytes
 //   kMfma           whether batch 2..8 may go to the matrix-core kernel
 //   kDequantWeights weights per thread of its dequant kernel
-//   template <int B, int LPR, int NW, class XT> static auto kernel()
-//                   the matvec kernel: (W, N, nsb, x, ldx, y, ldy, xvec),
-//                   with LDS for B activation rows at kSbXPad floats per
-//                   64 weights
+//   kBytes          bytes per super-block
+//   template <int B, int LPR, int NW, class XT, bool ROUTE> static auto kernel()
+//                   the matvec kernel: (W, N, nsb, x, ldx, y, ldy, xvec,
+//                   route), with LDS for B activation rows at kSbXPad floats
+//                   per 64 weights; ROUTE: grid row p computes MoE pair p
+//                   (SbRoute)
 //   static auto dequant_kernel()   (W, n_units, out), one unit per thread
 #pragma once
 
@@ -24,6 +26,30 @@ namespace qmv {
 namespace {
 
 constexpr int kSbWeights = 256;   // per super-block
+
+// MoE routing of the super-block kernels: grid row p = b * top_k + s
+// (blockIdx.y) computes y[p] = DEQ(W_e) x_{b,s} with e = ids[p], x_{b,s} at
+// x + b * xs_tok + s * xs_slot (elements) and y[p] at y + p * ldy.  An id
+// outside [0, n_experts) streams expert 0 and writes quiet NaN.
+struct SbRoute {
+    const int32_t* ids;
+    int64_t estride;              // bytes between experts
+    int64_t xs_tok, xs_slot;
+    int32_t top_k, n_experts;
+};
+
+// Applies the route of grid row blockIdx.y to the kernel's W, x and y
+// pointers; returns whether its id is bad.
+template <class PW, class PX, class PY>
+__device__ __forceinline__ bool sb_route(const SbRoute& route, PW& W, PX& x, PY& y, int64_t ldy) {
+    const int p = blockIdx.y;
+    const int e = route.ids[p];            // uniform: one scalar load
+    const bool bad = e < 0 || e >= route.n_experts;
+    W += (int64_t)(bad ? 0 : e) * route.estride;
+    x += (int64_t)(p / route.top_k) * route.xs_tok + (int64_t)(p % route.top_k) * route.xs_slot;
+    y += (int64_t)p * ldy;
+    return bad;
+}
 constexpr int kSbXPad = 68;       // staged floats per 64-weight lane group: 16-byte reads of
                                   // lanes on consecutive groups start 4 banks apart
 
@@ -102,10 +128,34 @@ inline int sb_pick_lpr(int G) {
     return best;
 }
 
+// route: MoE pairs (grid rows) or nullptr (one dense matrix).
 template <class Fmt, int B, int LPR, int NW, class XT>
 int32_t sb_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
-                  hipStream_t st) {
-    auto kern = Fmt::template kernel<B, LPR, NW, XT>();
+                  hipStream_t st, const SbRoute* route, int pairs) {
+    if (route) {
+        if constexpr (B == 1) {
+            auto kern = Fmt::template kernel<1, LPR, NW, XT, true>();
+            const size_t lds = (size_t)4 * nsb * kSbXPad * sizeof(float);
+            size_t dyn_max = 0;
+            if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, Fmt::kEntry, &dyn_max))
+                return e;
+            if (lds > dyn_max)
+                return fail(QMV_EINVAL, "%s: %zu bytes of staged activations exceed the LDS", Fmt::kEntry, lds);
+            constexpr int rows_per_wg = NW * (64 / LPR);
+            const int64_t tiles = (N + rows_per_wg - 1) / rows_per_wg;
+            const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds));
+            const int64_t slots = std::max<int64_t>(1, (int64_t)device_cu_count() * per_cu / pairs);
+            const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, slots));
+            const int xvec = (aligned(x, XIn<XT>::kVecAlign) && route->xs_tok % 4 == 0 && route->xs_slot % 4 == 0)
+                                 ? 1 : 0;
+            hipLaunchKernelGGL(kern, dim3(grid, pairs), dim3(64 * NW), lds, st, W, N, nsb, x, ldx, y, ldy, xvec,
+                               *route);
+            return check_launch(Fmt::kEntry);
+        } else {
+            return fail(QMV_EINVAL, "%s: routed launches take one column", Fmt::kEntry);
+        }
+    }
+    auto kern = Fmt::template kernel<B, LPR, NW, XT, false>();
     const size_t lds = (size_t)B * 4 * nsb * kSbXPad * sizeof(float);
     size_t dyn_max = 0;
     if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, Fmt::kEntry, &dyn_max)) return e;
@@ -115,7 +165,7 @@ int32_t sb_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx
     const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds));
     const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
     const int xvec = (aligned(x, XIn<XT>::kVecAlign) && ldx % 4 == 0) ? 1 : 0;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nsb, x, ldx, y, ldy, xvec);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, W, N, nsb, x, ldx, y, ldy, xvec, SbRoute{});
     return check_launch(Fmt::kEntry);
 }
 
@@ -123,12 +173,12 @@ int32_t sb_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx
 // the registers at 128, and batch 6..8 need more).
 template <class Fmt, int B, class XT>
 int32_t sb_launch_lpr(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
-                      hipStream_t st) {
+                      hipStream_t st, const SbRoute* route = nullptr, int pairs = 1) {
     switch (sb_pick_lpr(4 * nsb)) {
-    case 64: return sb_launch<Fmt, B, 64, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 32: return sb_launch<Fmt, B, 32, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    case 16: return sb_launch<Fmt, B, 16, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
-    default: return sb_launch<Fmt, B, 8, 8, XT>(W, N, nsb, x, ldx, y, ldy, st);
+    case 64: return sb_launch<Fmt, B, 64, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
+    case 32: return sb_launch<Fmt, B, 32, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
+    case 16: return sb_launch<Fmt, B, 16, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
+    default: return sb_launch<Fmt, B, 8, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
     }
 }
 
@@ -231,12 +281,66 @@ int32_t sb_dequant(const void* W, int64_t N, int64_t K, float* out, void* stream
     return check_launch(name);
 }
 
-// The MoE, combine and chain-group slots of a super-block format's table.
-template <class Fmt>
-int32_t sb_no_moe(const char* name, bool, const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, int32_t,
-                  int32_t, const void*, int32_t, int64_t, int64_t, float*, void*) {
-    return fail(QMV_EUNSUPPORTED, "%s: %s experts are not supported", name, Fmt::kLabel);
+// MoE experts: every (token, slot) pair is one grid row of the batch-1
+// kernel (a pair's expert is streamed for that pair; at batch 1 the pairs
+// of a token have distinct experts).  The fused SwiGLU form is not offered
+// for these formats.
+template <class Fmt, class XT>
+int32_t sb_moe_t(const char* name, const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K,
+                 const int32_t* ids, int32_t batch, int32_t top_k, const XT* x, int64_t xs_tok, int64_t xs_slot,
+                 float* y, void* stream) {
+    if (!Wx || !ids || !x || !y) return fail(QMV_EINVAL, "%s: null pointer", name);
+    if (E < 1) return fail(QMV_EINVAL, "%s: n_experts must be >= 1", name);
+    if (N < 1 || K < kSbWeights || K % kSbWeights)
+        return fail(QMV_EINVAL, "%s: bad matrix shape %lld x %lld (n_cols a multiple of 256 for %s)", name,
+                    (long long)N, (long long)K, Fmt::kLabel);
+    if (batch < 1 || batch > 8) return fail(QMV_EINVAL, "%s: batch must be in 1..8 (got %d)", name, batch);
+    if (top_k < 1 || top_k > 16) return fail(QMV_EINVAL, "%s: top_k must be in 1..16 (got %d)", name, top_k);
+    const int64_t nsb = K / kSbWeights;
+    if (nsb > (1 << 24) || N > ((int64_t)1 << 40) / nsb) return fail(QMV_EINVAL, "%s: matrix too large", name);
+    const int64_t mbytes = N * nsb * Fmt::kBytes;
+    if (estride < mbytes || estride % Fmt::kWAlign)
+        return fail(QMV_EINVAL, "%s: expert_stride_bytes (%lld) must be >= %lld and a multiple of %d", name,
+                    (long long)estride, (long long)mbytes, Fmt::kWAlign);
+    if (E > 1 && estride > ((int64_t)1 << 46) / (E - 1)) return fail(QMV_EINVAL, "%s: experts too large", name);
+    if (batch > 1 && xs_tok < K) return fail(QMV_EINVAL, "%s: x_stride_token must be >= n_cols", name);
+    if (xs_tok < 0) return fail(QMV_EINVAL, "%s: x_stride_token must be >= 0", name);
+    if (top_k > 1 && xs_slot != 0 && xs_slot < K)
+        return fail(QMV_EINVAL, "%s: x_stride_slot must be 0 or >= n_cols", name);
+    if (xs_slot < 0) return fail(QMV_EINVAL, "%s: x_stride_slot must be >= 0", name);
+    if (!aligned(Wx, Fmt::kWAlign))
+        return fail(QMV_EALIGN, "%s: W_experts must be %d-byte aligned for %s", name, Fmt::kWAlign, Fmt::kLabel);
+    if (!aligned(y, 4) || !aligned(ids, 4))
+        return fail(QMV_EALIGN, "%s: the output and expert_ids must be 4-byte aligned", name);
+    if (!aligned(x, sizeof(XT))) return fail(QMV_EALIGN, "%s: x must be aligned to its %zu-byte elements", name,
+                                             sizeof(XT));
+    if (4 * nsb * kSbXPad * (int64_t)sizeof(float) > kLdsMax)
+        return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
+    const SbRoute route{ids, estride, xs_tok, xs_slot, top_k, E};
+    return sb_launch_lpr<Fmt, 1, XT>(static_cast<const uint8_t*>(Wx), N, (int)nsb, x, K, y, N, as_stream(stream),
+                                     &route, batch * top_k);
 }
+
+template <class Fmt>
+int32_t sb_moe(const char* name, bool swiglu, const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K,
+               const int32_t* ids, int32_t batch, int32_t top_k, const void* x, int32_t x_type, int64_t xs_tok,
+               int64_t xs_slot, float* y, void* stream) {
+    if (swiglu) return fail(QMV_EUNSUPPORTED, "%s: the fused SwiGLU form is not offered for %s", name, Fmt::kLabel);
+    switch (x_type) {
+    case QMV_X_F32:
+        return sb_moe_t<Fmt>(name, Wx, estride, E, N, K, ids, batch, top_k, static_cast<const float*>(x), xs_tok,
+                             xs_slot, y, stream);
+    case QMV_X_F16:
+        return sb_moe_t<Fmt>(name, Wx, estride, E, N, K, ids, batch, top_k, static_cast<const _Float16*>(x), xs_tok,
+                             xs_slot, y, stream);
+    case QMV_X_BF16:
+        return sb_moe_t<Fmt>(name, Wx, estride, E, N, K, ids, batch, top_k, static_cast<const __bf16*>(x), xs_tok,
+                             xs_slot, y, stream);
+    default: return fail(QMV_EINVAL, "%s: unknown activation type %d", name, (int)x_type);
+    }
+}
+
+// The combine and chain-group slots of a super-block format's table.
 template <class Fmt>
 int32_t sb_no_combine(const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, const float*, int32_t, int32_t,
                       const float*, int64_t, int64_t, float*, void*) {
@@ -246,7 +350,7 @@ inline bool sb_no_group(const RowSegs&, int, const float*, hipStream_t, bool, in
 
 template <class Fmt>
 const FormatOps& sb_format_ops() {
-    static const FormatOps ops = {sb_matvec<Fmt>, sb_dequant<Fmt>, sb_no_moe<Fmt>, sb_no_combine<Fmt>, sb_no_group};
+    static const FormatOps ops = {sb_matvec<Fmt>, sb_dequant<Fmt>, sb_moe<Fmt>, sb_no_combine<Fmt>, sb_no_group};
     return ops;
 }
 

@@ -58,16 +58,16 @@ TRAFFIC_RECORDS = {
     "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>": {
         "key": "kernel_c_q8_0",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "2801ae488bf56afe936da42516ab62ffc13681b9faaa1377318c454da6e6ca73", "bytes_per_launch": 83478763, "ratio": 1.0025,
+        "sha256": "697d932f2c4e37948668b2bc3e36c9c89c988ecc4610569f59379872ae9f04d1", "bytes_per_launch": 83478763, "ratio": 1.0025,
         "workload": "8B Q8_0 decode step, batch 1"},
     "qmv_kernel<Q8_0, 1, 64, 1, 2, 8, 2, false, float, false>": {
         "key": "kernel_q8_0_o",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "2801ae488bf56afe936da42516ab62ffc13681b9faaa1377318c454da6e6ca73", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
+        "sha256": "697d932f2c4e37948668b2bc3e36c9c89c988ecc4610569f59379872ae9f04d1", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
     "qmv_kernel_c<Q8_0, 4, 16, 2, float, 1>": {
         "key": "kernel_c16_q8_0_down",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "2801ae488bf56afe936da42516ab62ffc13681b9faaa1377318c454da6e6ca73", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
+        "sha256": "697d932f2c4e37948668b2bc3e36c9c89c988ecc4610569f59379872ae9f04d1", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
     "i8_stream_kernel": {
         "key": "i8_stream",
         "sources": ["bandwidth_bound_block_amd/csrc/qmv_int8.hip", "bandwidth_bound_block_amd/csrc/qmv_host.h"],
@@ -355,26 +355,28 @@ def build_int8(torch, qmv, wl, fused=False):
     return sw
 
 
-def build_moe(torch, qmv, wl, batch):
+def build_moe(torch, qmv, wl, batch, fmt="q4_0"):
     """48 MoE layers: per layer one launch for gate||up (each expert's gate
     and up rows concatenated, 1536 x 2048) and one for down (2048 x 768, one
     input per token and slot).  Bytes count each distinct routed expert once."""
     import numpy as np
-    sw = Sweep(f"moe30b_q4_0_b{batch}", batch)
+    sw = Sweep(f"moe30b_{fmt}_b{batch}", batch)
     dev = "cuda:0"
     cfn = qmv.lib().qmv_moe
+    fcode = qmv.FORMATS[fmt]
     E, T, H, F = wl.MOE_EXPERTS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
     t0 = time.time()
-    if "moe" not in _ENC_CACHE:
-        gate = wl.quant_weights("q4_0", "moe/gate", E * F, H).reshape(E, -1)
-        up = wl.quant_weights("q4_0", "moe/up", E * F, H).reshape(E, -1)
-        _ENC_CACHE["moe"] = (np.concatenate([gate, up], axis=1).reshape(-1),
-                             wl.quant_weights("q4_0", "moe/down", E * H, F).reshape(-1))
-    gu = torch.from_numpy(_ENC_CACHE["moe"][0]).to(dev)
-    down = torch.from_numpy(_ENC_CACHE["moe"][1]).to(dev)
-    log(f"[moe] experts ready in {time.time() - t0:.1f}s")
-    gu_stride = 2 * wl.block_bytes("q4_0", F, H)
-    dn_stride = wl.block_bytes("q4_0", H, F)
+    key = f"moe_{fmt}"
+    if key not in _ENC_CACHE:
+        gate = wl.quant_weights(fmt, "moe/gate", E * F, H).reshape(E, -1)
+        up = wl.quant_weights(fmt, "moe/up", E * F, H).reshape(E, -1)
+        _ENC_CACHE[key] = (np.concatenate([gate, up], axis=1).reshape(-1),
+                           wl.quant_weights(fmt, "moe/down", E * H, F).reshape(-1))
+    gu = torch.from_numpy(_ENC_CACHE[key][0]).to(dev)
+    down = torch.from_numpy(_ENC_CACHE[key][1]).to(dev)
+    log(f"[moe {fmt}] experts ready in {time.time() - t0:.1f}s")
+    gu_stride = 2 * wl.block_bytes(fmt, F, H)
+    dn_stride = wl.block_bytes(fmt, H, F)
     uniq = []
     for layer in range(wl.MOE_LAYERS):
         ids_np = wl.moe_ids(f"moe/ids/{layer}/{batch}", batch, T, E)
@@ -387,10 +389,10 @@ def build_moe(torch, qmv, wl, batch):
         xd = torch.from_numpy(wl.activations(f"moe/x/dn/{layer}/{batch}", batch * T, F)).to(dev)
         yd = torch.empty((batch, T, H), dtype=torch.float32, device=dev)
         sw.keep += [ids, Wgu, Wdn, x, ygu, xd, yd]
-        sw.add("gate_up", cfn, (1, Wgu.data_ptr(), gu_stride, E, 2 * F, H, ids.data_ptr(), batch, T,
+        sw.add("gate_up", cfn, (fcode, Wgu.data_ptr(), gu_stride, E, 2 * F, H, ids.data_ptr(), batch, T,
                                 x.data_ptr(), H, 0, ygu.data_ptr()),
                nu * gu_stride + 4 * batch * H + 4 * batch * T * 2 * F + 4 * batch * T)
-        sw.add("down", cfn, (1, Wdn.data_ptr(), dn_stride, E, H, F, ids.data_ptr(), batch, T,
+        sw.add("down", cfn, (fcode, Wdn.data_ptr(), dn_stride, E, H, F, ids.data_ptr(), batch, T,
                              xd.data_ptr(), T * F, F, yd.data_ptr()),
                nu * dn_stride + 4 * batch * T * F + 4 * batch * T * H + 4 * batch * T)
     sw.mean_unique = float(np.mean(uniq))
@@ -748,7 +750,8 @@ def main():
     ap.add_argument("--sweeps", default="all",
                     help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,q4_k,q6_k,int8,moe, or of "
                          "FMT@B / FMT@Bf / FMT@1g (one 8B sweep of format FMT at batch B, f: row-fused layout, "
-                         "1g: batch 1 with one launch per dependency level)")
+                         "1g: batch 1 with one launch per dependency level), moe@B[:q4_k] / moeblock@B (one MoE "
+                         "sweep at batch B)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing")
     ap.add_argument("--no-headline", action="store_true",
                     help="skip the headline step (profiling runs of single sweeps); no final line is printed")
@@ -825,7 +828,19 @@ def main():
         else args.sweeps.split(","))
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
-        if "@" in nm:
+        if nm.startswith(("moe@", "moeblock@")):
+            # one MoE sweep: moe@B (Q4_0 experts, or moe@B:q4_k) / moeblock@B
+            what, spec = nm.split("@")
+            B, _, fmt = spec.partition(":")
+            if what == "moe":
+                s = build_moe(torch, qmv, wl, int(B), fmt or "q4_0")
+            else:
+                s = build_moe_block(torch, qmv, wl, int(B))
+            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph),
+                   mean_distinct_experts=_r(s.mean_unique, 2))
+            del s
+            torch.cuda.empty_cache()
+        elif "@" in nm:
             fmt, spec = nm.split("@")
             if spec == "1g":
                 s = build_llama_grouped(torch, qmv, wl, fmt)
@@ -894,6 +909,13 @@ def main():
                     record(s, r, o, mean_distinct_experts=_r(s.mean_unique, 2))
                     del s
                     torch.cuda.empty_cache()
+            # Q4_K experts (one grid row per token and slot), batch 1 and 8
+            for B in (1, 8):
+                s = build_moe(torch, qmv, wl, B, "q4_k")
+                r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+                record(s, r, mean_distinct_experts=_r(s.mean_unique, 2))
+                del s
+                torch.cuda.empty_cache()
 
     if head is None:
         return

@@ -70,8 +70,9 @@ def test_float_matvec_argument_errors(qmv, name):
 
 
 def test_q4_k_argument_errors(qmv):
-    """Q4_K: columns in multiples of 256, W 16-byte aligned; no MFMA path;
-    MoE and chain entry points refuse the format."""
+    """Q4_K: columns in multiples of 256, W 16-byte aligned; the MFMA path
+    needs batch >= 2; MoE argument checks; the fused SwiGLU, combine and
+    chain entry points refuse the format."""
     f = qmv.lib().qmv_q4_k
     cases = [
         ((0, 8, 256, A, 256, 1, A, 8, None), EINVAL, "null"),
@@ -100,16 +101,27 @@ def test_q4_k_argument_errors(qmv):
     assert "x_type" in qmv.last_error()
     assert L.qmv_dequant(qmv.Q4_K, A, 8, 288, A, None) == EINVAL and "256" in qmv.last_error()
     assert L.qmv_dequant(qmv.Q4_K, A + 4, 8, 256, A, None) == EALIGN
-    assert L.qmv_moe(qmv.Q4_K, A, 144, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
+    # MoE experts: routed per pair; argument errors only (nothing launches here)
+    assert L.qmv_moe(qmv.Q4_K, A, 144, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert "expert_stride" in qmv.last_error()
+    assert L.qmv_moe(qmv.Q4_K, A, 1152, 2, 8, 288, A, 1, 1, A, 288, 288, A, None) == EINVAL
+    assert "multiple of 256" in qmv.last_error()
+    assert L.qmv_moe(qmv.Q4_K, A, 1160, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert L.qmv_moe(qmv.Q4_K, A + 4, 1152, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EALIGN
+    assert "16-byte" in qmv.last_error()
+    assert L.qmv_moe(qmv.Q4_K, A, 1152, 2, 8, 256, A, 9, 1, A, 256, 256, A, None) == EINVAL
+    assert L.qmv_moe_swiglu(qmv.Q4_K, A, 2304, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
+    assert "SwiGLU" in qmv.last_error()
+    assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert "Q4_K" in qmv.last_error()
-    assert L.qmv_moe_combine(qmv.Q4_K, A, 144, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert L.qmv_chain(qmv.Q4_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED and "not supported" in qmv.last_error()
     assert L.qmv_chain_noalloc(qmv.Q4_K, A, 1, None) == EUNSUPPORTED
 
 
 def test_q6_k_argument_errors(qmv):
-    """Q6_K: columns in multiples of 256, W 4-byte aligned; no MFMA path;
-    MoE and chain entry points refuse the format."""
+    """Q6_K: columns in multiples of 256, W 4-byte aligned; the MFMA path
+    needs batch >= 2; MoE argument checks; the fused SwiGLU, combine and
+    chain entry points refuse the format."""
     f = qmv.lib().qmv_q6_k
     cases = [
         ((0, 8, 256, A, 256, 1, A, 8, None), EINVAL, "null"),
@@ -130,9 +142,14 @@ def test_q6_k_argument_errors(qmv):
     L = qmv.lib()
     assert L.qmv_matvec_path(qmv.Q6_K, A, 8, 256, A, 256, 1, A, 8, qmv.PATH_MFMA, None) == EUNSUPPORTED
     assert L.qmv_dequant(qmv.Q6_K, A, 8, 288, A, None) == EINVAL and "256" in qmv.last_error()
-    assert L.qmv_moe(qmv.Q6_K, A, 210, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
+    assert L.qmv_moe(qmv.Q6_K, A, 210, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert "expert_stride" in qmv.last_error()
+    assert L.qmv_moe(qmv.Q6_K, A + 2, 1680, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EALIGN
+    assert L.qmv_moe(qmv.Q6_K, A, 1680, 2, 8, 256, A, 1, 17, A, 256, 256, A, None) == EINVAL
+    assert "top_k" in qmv.last_error()
+    assert L.qmv_moe_swiglu(qmv.Q6_K, A, 3360, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
+    assert L.qmv_moe_combine(qmv.Q6_K, A, 1680, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert "Q6_K" in qmv.last_error()
-    assert L.qmv_moe_combine(qmv.Q6_K, A, 210, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert L.qmv_chain(qmv.Q6_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED
     assert L.qmv_chain_noalloc(qmv.Q6_K, A, 1, None) == EUNSUPPORTED
     assert L.qmv_dequant(5, A, 8, 256, A, None) == EUNSUPPORTED
