@@ -37,10 +37,6 @@
 #include "qmv_block_decode.h"
 
 namespace qmv {
-#ifndef QMV_MOE_PAIRS_MAX_BATCH
-#define QMV_MOE_PAIRS_MAX_BATCH 8
-#endif
-
 namespace {
 
 // ------------------------------------------------------------------ kernels
@@ -1054,8 +1050,10 @@ int32_t launch_moe(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N,
     return check_launch("qmv_moe");
 }
 
-// Member columns per pass.  One token routes to an expert once, so batch 1
-// needs one column.  At batches 2..8 a routed expert of 128 has 1.0 to 1.3
+// The grouping kernel runs where the per-pair route cannot stage its
+// activations (rows of more than 16384 columns, or activations that are not
+// 16-byte aligned).  Member columns per pass: one token routes to an expert
+// once, so batch 1 needs one column.  At batches 2..8 a routed expert of 128 has 1.0 to 1.3
 // members on average.  Measured on the 30B-A3B expert shapes (cache-cold):
 // one column per pass, three steps in flight and a grid sized for the
 // expected distinct experts win where the rows are long (2048 columns) or
@@ -1077,9 +1075,12 @@ int32_t launch_moe_bc(const uint8_t* Wx, int64_t estride, int n_experts, int64_t
                                                 xvec, batch == 1, st);
 }
 
-// Batch 1: the pairs of one token need no grouping (a duplicated id only
-// streams that expert twice), so grid row p runs the dense kernel on
-// expert ids[p] with no prologue at all.
+// Every batch 1..8: pair p = token * top_k + slot is grid row p of the
+// dense kernel on expert ids[p], with no prologue and no grouping.  An
+// expert routed from several tokens (or twice by one) is streamed once per
+// pair; the later streams find it mostly in L2 or the MALL, and the grid is
+// the dense kernel's full persistent grid instead of a few steps per
+// workgroup after a grouping prologue.
 template <class F, int LPR, int XU, class XT, bool SW>
 int32_t launch_moe_pairs(const uint8_t* Wx, int64_t estride, int n_experts, int64_t N, int nb, const int32_t* ids,
                          int batch, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y,
@@ -1109,7 +1110,9 @@ int32_t launch_moe_xu(const uint8_t* Wx, int64_t estride, int n_experts, int64_t
                       int batch, int top_k, const XT* x, int64_t xs_tok, int64_t xs_slot, float* y, int xvec,
                       hipStream_t st) {
     const int K4 = nb * 8;   // 4-element chunks of one activation row; 256 threads
-    const bool pairs = batch <= QMV_MOE_PAIRS_MAX_BATCH && xvec;
+    // the per-pair route wherever the activations stage straight-line;
+    // the grouping kernel otherwise
+    const bool pairs = xvec != 0;
     if (pairs && K4 <= 4 * 256)
         return launch_moe_pairs<F, LPR, 4, XT, SW>(Wx, estride, n_experts, N, nb, ids, batch, top_k, x, xs_tok,
                                                    xs_slot, y, st);

@@ -136,8 +136,9 @@ int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
  * width among themselves); qmv_matvec_path chooses the family.
  * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q4_K (matvec on
  * every path; QMV_PATH_MFMA needs batch 2..8, x aligned to 4 elements and
- * ldx a multiple of 4, else QMV_EUNSUPPORTED); the MoE entry points and
- * qmv_chain do not (QMV_EUNSUPPORTED).
+ * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do qmv_moe and
+ * qmv_moe_xt; qmv_moe_swiglu, qmv_moe_combine and qmv_chain do not
+ * (QMV_EUNSUPPORTED).
  */
 int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
@@ -165,8 +166,9 @@ int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
  * x or y not 4-byte aligned), QMV_EHIP.
  * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q6_K (matvec on
  * every path; QMV_PATH_MFMA needs batch 2..8, x aligned to 4 elements and
- * ldx a multiple of 4, else QMV_EUNSUPPORTED); the MoE entry points and
- * qmv_chain do not (QMV_EUNSUPPORTED).
+ * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do qmv_moe and
+ * qmv_moe_xt; qmv_moe_swiglu, qmv_moe_combine and qmv_chain do not
+ * (QMV_EUNSUPPORTED).
  */
 int32_t qmv_q6_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
@@ -254,8 +256,8 @@ int32_t qmv_i8_requant_lut(const int8_t* W, int64_t n_rows, int64_t n_cols,
                            int8_t* y, int64_t ldy, void* stream);
 
 /*
- * Grouped mixture-of-experts expert matvec ([NST] Sec. "The Unified Quant
- * Core": each routed expert goes through the same decode matvec core).
+ * Mixture-of-experts expert matvec ([NST] Sec. "The Unified Quant Core":
+ * each routed expert goes through the same decode matvec core).
  * For token b < batch and slot s < top_k, with e = expert_ids[b*top_k + s]:
  *   y[(b*top_k + s)*n_rows + i] = sum_j DEQ(W_e)[i][j] * x_{b,s}[j]
  * where W_e = (const uint8_t*)W_experts + e*expert_stride_bytes is an
@@ -263,13 +265,21 @@ int32_t qmv_i8_requant_lut(const int8_t* W, int64_t n_rows, int64_t n_cols,
  * x_{b,s} = x + b*x_stride_token + s*x_stride_slot (elements).  Gate/up
  * projections pass x_stride_slot = 0 (one input per token); the down
  * projection passes x_stride_slot = n_cols (one input per token and slot).
- * Each expert that appears in expert_ids is streamed from memory once per
- * call and applied to every (token, slot) routed to it.
- *   fmt                 QMV_Q8_0, QMV_Q4_0 or QMV_Q4_1.
- *   n_cols              a multiple of 32, at most 35488 (one activation row,
- *                       144 bytes per 32 columns, plus 4 KB of routing
- *                       tables fit the 160 KB LDS of a workgroup).
- *   expert_stride_bytes >= the bytes of one expert matrix; a multiple of 4.
+ * Each (token, slot) pair is computed as its own matvec (the same sums as a
+ * single-expert call, bitwise); an expert routed from several tokens is
+ * read from HBM about once and from the GPU's caches for its other pairs.
+ * Activations that cannot be staged straight-line (rows of more than 16384
+ * columns, or x or its strides not 16-byte aligned) go through a kernel
+ * that groups each expert's pairs instead; the results are the same.
+ *   fmt                 QMV_Q8_0, QMV_Q4_0, QMV_Q4_1, QMV_Q4_K or QMV_Q6_K.
+ *   n_cols              Q8_0 / Q4_0 / Q4_1: a multiple of 32, at most 35488
+ *                       (one activation row, 144 bytes per 32 columns, plus
+ *                       4 KB of routing tables fit the 160 KB LDS of a
+ *                       workgroup).  Q4_K / Q6_K: a multiple of 256, at most
+ *                       38400 (1088 bytes of staged row per 256 columns).
+ *   expert_stride_bytes >= the bytes of one expert matrix; a multiple of 4
+ *                       (of 16 for Q4_K, whose experts are read in 16-byte
+ *                       pieces, with W_experts 16-byte aligned).
  *   n_experts           >= 1.
  *   expert_ids          int32 [batch][top_k], device memory.  An id outside
  *                       [0, n_experts) cannot be reported synchronously: the
@@ -312,11 +322,11 @@ int32_t qmv_moe_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_byt
  *   g = sum_j DEQ(W_e)[i][j] * x_{b,s}[j],  u = sum_j DEQ(W_e)[n_ff + i][j] * x_{b,s}[j],
  *   h[(b*top_k + s)*n_ff + i] = SiLU(g) * u,   SiLU(g) = g / (1 + e^-g),
  * with g and u the sums qmv_moe produces for those rows (bitwise), and
- * SiLU and the product in fp32.  Every routed expert is streamed once per
- * call.  Arguments as qmv_moe, with expert_stride_bytes >= the bytes of
+ * SiLU and the product in fp32.  Experts are read as in qmv_moe.
+ * Arguments as qmv_moe, with expert_stride_bytes >= the bytes of
  * 2*n_ff rows; h is fp32 [batch][top_k][n_ff], 4-byte aligned.  Invalid
  * ids give quiet NaN rows, as in qmv_moe.
- * Errors: as qmv_moe.
+ * Errors: as qmv_moe; QMV_EUNSUPPORTED for QMV_Q4_K and QMV_Q6_K.
  */
 int32_t qmv_moe_swiglu(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                        int32_t n_experts, int64_t n_ff, int64_t n_cols,
@@ -350,7 +360,7 @@ int32_t qmv_moe_swiglu_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_str
  * Other arguments as qmv_moe.  A token with an invalid id gets quiet NaN
  * for all its n_rows outputs.
  * Errors: as qmv_moe; QMV_EINVAL for null weights, QMV_EALIGN for
- * misaligned weights.
+ * misaligned weights, QMV_EUNSUPPORTED for QMV_Q4_K and QMV_Q6_K.
  */
 int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                         int32_t n_experts, int64_t n_rows, int64_t n_cols,

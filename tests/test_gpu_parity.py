@@ -603,10 +603,10 @@ def test_moe_routing_edge_cases(env, case):
 @pytest.mark.parametrize("case", ["dup_invalid", "long_rows", "unaligned_slots"])
 def test_moe_batch1_paths(env, case):
     """One token: its pairs run as separate grid rows of the dense kernel
-    (no grouping; a duplicated id streams that expert twice), or, when the
-    activations cannot be staged straight-line (rows of > 16384 columns, or
-    slot strides that break 16-byte alignment), through the grouping
-    kernel.  Either way each valid pair equals the single-expert dense call
+    (no grouping; a duplicated id streams that expert twice, the second time
+    mostly from cache), or, when the activations cannot be staged
+    straight-line (rows of > 16384 columns, or slot strides that break
+    16-byte alignment), through the grouping kernel.  Either way each valid pair equals the single-expert dense call
     bitwise, invalid ids give NaN, and the result is within the bound."""
     torch, qmv = env
     fmt = "q4_1"
@@ -1063,10 +1063,11 @@ def test_moe_combine_edges(env, fmt, case):
 @pytest.mark.parametrize("kind", ["f16", "bf16"])
 def test_moe_x16_equals_widened_fp32(env, fmt, kind):
     """qmv_moe_xt and qmv_moe_swiglu_xt with 16-bit activations equal, bitwise,
-    qmv_moe / qmv_moe_swiglu on the exactly widened activations: batch 1
-    (per-pair route) and 2..8 (grouping kernel), per-token and per-slot
-    inputs, duplicated ids, rows needing the looping stager, and x at a
-    2-byte offset; within the bound of the oracle on the widened values."""
+    qmv_moe / qmv_moe_swiglu on the exactly widened activations: the
+    per-pair route (aligned activations of <= 16384 columns, any batch) and
+    the grouping kernel (longer rows, x at a 2-byte offset), per-token and
+    per-slot inputs, duplicated ids; within the bound of the oracle on the
+    widened values."""
     torch, qmv = env
     E = 6
     cases = [("b1_tok", 1, 256, 2048, [[4, 1, 4, 0]], False, 0),
