@@ -60,11 +60,46 @@ __device__ __forceinline__ void q4k_scale_min(const u32x4& h, int s, int& sc, in
     mn = s < 4 ? mn_lo : mn_hi;
 }
 
+// The scales and minimums of sub-blocks 2 part and 2 part + 1 together:
+// the two sub-blocks' bytes are spread into the low bytes of a word's two
+// 16-bit halves, so one shift and mask decode both.  The selectors and the
+// mask depend only on part, which is fixed per lane (a lane's groups are
+// li + LPR t with LPR a multiple of 4).  For part < 2 the fields are the
+// low six bits of b[s] (scale) and b[s+4] (minimum); for part >= 2 the low
+// four bits come from b[s+4] (scale: its low nibble, minimum: its high
+// nibble) and the top two from bits 6, 7 of b[s-4] and b[s].
+struct Q4KPairSel {
+    uint32_t sel;    // bytes o, o+1 of the first operand (part >= 2) or of the second
+    uint32_t selp;   // bytes o, o+1 of the second operand (part >= 2), else zeros
+    uint32_t ma;     // mask of the low field: 6 bits (part < 2) or 4
+};
+__device__ __forceinline__ Q4KPairSel q4k_pair_sel(int part) {
+    const uint32_t o = 2 * (part & 1);
+    const bool hi = part >= 2;
+    const uint32_t b0 = (hi ? 4u : 0u) + o;
+    Q4KPairSel ps;
+    ps.sel = b0 | (0x0cu << 8) | ((b0 + 1) << 16) | (0x0cu << 24);   // 0x0c selects a zero byte
+    ps.selp = hi ? (o | (0x0cu << 8) | ((o + 1) << 16) | (0x0cu << 24)) : 0x0c0c0c0cu;
+    ps.ma = hi ? 0x000f000fu : 0x003f003fu;
+    return ps;
+}
+// sc2, mn2: the scales and minimums of the two sub-blocks in bytes 0 and 2.
+__device__ __forceinline__ void q4k_pair_scales(const u32x4& h, const Q4KPairSel& ps, uint32_t& sc2, uint32_t& mn2) {
+    // h.y = b[0..3], h.z = b[4..7], h.w = b[8..11]; byte k of h.w >> 4
+    // holds the high nibble of b[8+k] in its low four bits
+    const uint32_t a_sc = __builtin_amdgcn_perm(h.w, h.y, ps.sel);
+    const uint32_t a_mn = __builtin_amdgcn_perm(h.w >> 4, h.z, ps.sel);
+    const uint32_t yp = __builtin_amdgcn_perm(0u, h.y, ps.selp);
+    const uint32_t zp = __builtin_amdgcn_perm(0u, h.z, ps.selp);
+    sc2 = (a_sc & ps.ma) | ((yp >> 2) & 0x00300030u);
+    mn2 = (a_mn & ps.ma) | ((zp >> 2) & 0x00300030u);
+}
+
 // A wave step covers RW = 64 / LPR rows, one per segment of LPR lanes.
 // (Two rows per lane, each staged activation read feeding both, measured
 // slower at every batch width: 123-228 VGPRs against 63-160.)
 template <int B, int LPR, int NW, class XT, bool ROUTE>
-__global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(B == 1 ? 8 : 1))) void q4k_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
                                                        const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
                                                        int64_t ldy, int xvec, const SbRoute route) {
     bool bad = false;   // routed pair with an invalid expert id: its outputs become NaN
@@ -82,32 +117,39 @@ __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict_
     const int64_t ntiles = (N + RW - 1) / RW;
     const int64_t wstride = (int64_t)gridDim.x * NW;
 
+    // A step's loads: the tile's first row as a wave-uniform base and 32-bit
+    // lane offsets from it (a tile spans RW rows of at most 150 super-blocks).
     auto load_step = [&](int64_t tile, int t, Q4KGroup& r) {
         const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
-        const int64_t row = min(tile * RW + seg, N - 1);
-        const uint8_t* sb = W + row * pitch + (int64_t)(g >> 2) * kQ4KBytes;
-        const int coff = 16 + 32 * (g & 3);
-        r.h = ld16_aligned(sb);
-        r.c0 = ld16_aligned(sb + coff);
-        r.c1 = ld16_aligned(sb + coff + 16);
+        const int64_t r0 = tile * RW;                            // tile < ntiles: r0 < N
+        const uint8_t* base = W + r0 * pitch;
+        const int64_t rem = N - 1 - r0;
+        const int lim = __builtin_amdgcn_readfirstlane(rem < RW - 1 ? (int)rem : RW - 1);
+        const int lr = min(seg, lim);                            // rows past the end: the last row
+        const uint32_t off = __umul24((uint32_t)lr, (uint32_t)pitch) + (uint32_t)(g >> 2) * kQ4KBytes;
+        const uint32_t coff = off + 16 + 32 * (g & 3);
+        r.h = ld16_aligned(base + off);
+        r.c0 = ld16_aligned(base + coff);
+        r.c1 = ld16_aligned(base + coff + 16);
     };
 
     float acc[B];
 #pragma unroll
     for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    // part = g & 3 for every group g of the lane (on a clamped step past the
+    // row's end the result is discarded)
+    const Q4KPairSel ps = q4k_pair_sel(li & 3);
     auto compute_step = [&](int64_t tile, int t, const Q4KGroup& r) {
         const int g = li + LPR * t;
         const bool valid = g < G;
         const int gc = valid ? g : G - 1;
-        const int part = gc & 3;
         const float d = half_bits_to_float(r.h.x);
         const float dmin = half_bits_to_float(r.h.x >> 16);
-        int sca, mna, scb, mnb;
-        q4k_scale_min(r.h, 2 * part, sca, mna);
-        q4k_scale_min(r.h, 2 * part + 1, scb, mnb);
-        // exact: 11 + 6 significant bits each
-        const float da = d * (float)sca, ma = dmin * (float)mna;
-        const float db = d * (float)scb, mb = dmin * (float)mnb;
+        uint32_t sc2, mn2;
+        q4k_pair_scales(r.h, ps, sc2, mn2);
+        // exact: 11 + 6 significant bits each (and d sc / 16 exact too)
+        const float da = d * ubyte(sc2, 0), ma = dmin * ubyte(mn2, 0);
+        const float db16 = (d * 0.0625f) * ubyte(sc2, 2), mb = dmin * ubyte(mn2, 2);
         // Sub-block 2 part (the low nibbles of the 32 code bytes), then
         // 2 part + 1 (the high nibbles): a loop that is not unrolled, so the
         // two halves share registers.
@@ -123,7 +165,7 @@ __global__ __launch_bounds__(64 * NW) void q4k_kernel(const uint8_t* __restrict_
             uint32_t c[1][8];
 #pragma unroll
             for (int i = 0; i < 8; ++i) c[0][i] = opaque_bits(w8[i] & mask);
-            const float fd[1] = {h ? db * 0.0625f : da}, fm[1] = {h ? -mb : -ma};
+            const float fd[1] = {h ? db16 : da}, fm[1] = {h ? -mb : -ma};
             float sh_dot[1][B];
             dot_multi<Q4KSub, 1, B>(c, fd, fm, xs + gc * kSbXPad + 32 * h, G * kSbXPad, sh_dot, B);
 #pragma unroll
