@@ -985,7 +985,11 @@ int32_t matvec(const char* name, const void* W, int64_t N, int64_t K, const XT* 
     int32_t rc = check_common(name, W, N, K, x, ldx, batch, y, ldy, (int)sizeof(XT));
     if (rc != QMV_OK) return rc;
     const int nb = (int)(K / 32);
-    if (path == QMV_PATH_MFMA || (path == QMV_PATH_AUTO && use_mfma(fmt_of<F>(), N, nb, batch))) {
+    // one activation row staged whole by the FMA kernels must fit in LDS;
+    // beyond that the automatic choice takes the matrix cores where they apply
+    const bool fma_fits = (int64_t)nb * kXPad * (int64_t)sizeof(float) <= kLdsMax;
+    if (path == QMV_PATH_MFMA ||
+        (path == QMV_PATH_AUTO && (use_mfma(fmt_of<F>(), N, nb, batch) || (!fma_fits && batch >= 2)))) {
         if (batch_matvec_mma(fmt_of<F>(), static_cast<const uint8_t*>(W), N, nb, x, xtype_of<XT>(), ldx, batch, y,
                              ldy, as_stream(stream), 0, &rc))
             return rc == QMV_OK ? ok() : rc;

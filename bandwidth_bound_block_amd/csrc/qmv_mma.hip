@@ -735,10 +735,19 @@ bool launch_q6k_mma_auto(const uint8_t* W, int64_t N, int nsb, const XT* x, int6
 
 }  // namespace
 
-// Measured on the 8B decode shapes (4096..128256 rows, 4096 and 14336
-// columns, cache-cold): the matrix-core kernel is faster from batch 3 on
-// for the 32-weight block formats, and at batch 2 for Q4_0 (at batch 2 the
-// FMA kernels still win most Q8_0 and Q4_1 shapes).  The super-block
+// Measured on the 8B decode shapes.  32-weight block formats, GPU time per
+// launch from graph replays over cache-cold copies: the FMA kernels win at
+// batch 2 except on the 128256-row lm_head (Q4_0 k / o / qkv / gate_up /
+// down 4.5 / 6.1 / 7.5 / 23.3 / 15.8 us against 7.1 / 7.6 / 10.3 / 25.4 /
+// 15.8), and at batch 3..4 on the 1024-row k and v, where every workgroup
+// of the matrix-core kernel stages the whole activation block for a few
+// row tiles (Q4_0 batch 3 5.4 against 7.6 us); from batch 5 and on larger
+// matrices the matrix cores win or tie (batch 8 k 9.7 against 10.9, gate_up
+// 26.4 against 53.2; Q8_0 and Q4_1 alike).  Whole steps (graph replays,
+// same box, alternated twice) against the matrix cores from batch 2 (Q4_0)
+// or 3: batch 2 +7% (Q4_0), batch 3 +5% (Q4_0) and +6% (Q4_1), batch 4 +4%
+// (Q4_0, Q8_0), the row-fused steps unchanged; the FMA kernels on the
+// 4096-row q and o as well lost 0.6-6% at batch 3..4.  The super-block
 // formats' FMA kernels hold out longer on 4096-column rows (their
 // matrix-core operands decode 6-bit fields and a pivot, or split scaled
 // codes in two): Q4_K 14336 x 4096 at batch 3 / 4 / 8 17.9 / 19.5 / 38.2 us
@@ -748,7 +757,10 @@ bool launch_q6k_mma_auto(const uint8_t* W, int64_t N, int nsb, const XT* x, int6
 // 32.4 / 38.5 / 71.6 against 28.5 / 29.7 / 35.3.
 bool use_mfma(qmv_fmt fmt, int64_t N, int nb, int B) {
     if (fmt == QMV_Q4_K || fmt == QMV_Q6_K) return B >= 5 || (B >= 3 && nb >= 256) || (B >= 2 && N >= 65536);
-    return B >= 3 || (B == 2 && fmt == QMV_Q4_0);
+    if (N >= 65536) return B >= 2;
+    if (B == 2) return false;
+    if (B <= 4) return N > 1024 || nb >= 256;
+    return true;
 }
 
 namespace {

@@ -26,7 +26,11 @@
  *     a column bitwise the same result as a batch-1 call on it alone; the
  *     matrix-core kernel (batch 2..8, see qmv_matvec_path) gives a column
  *     bitwise the same result at every batch width 2..8 and position, and
- *     agrees with the batch-1 result within the accuracy contract.
+ *     agrees with the batch-1 result within the accuracy contract.  Which
+ *     family runs is chosen per shape and batch from measurements (for
+ *     the 32-weight formats: the FMA kernels at batch 2 and on rows of up
+ *     to 1024 at batch 3..4, the matrix cores from 65536 rows, on longer
+ *     matrices at batch 3..4 and from batch 5).
  *   - Float results are fp32, accumulated in fp32; they agree with the exact
  *     dequantize-then-dot within |err| <= 1e-4 * sum_j |w_ij x_j| + 1e-6 per
  *     output (the accuracy contract the tests enforce), for every stored
@@ -90,12 +94,12 @@ enum {
  *   W       packed blocks of the format named by the function, n_rows rows of
  *           n_cols/32 blocks; 4-byte aligned.
  *   n_rows  >= 1.
- *   n_cols  >= 32 and a multiple of 32; at most 36384 where the FMA kernels
- *           run (batch 1, and batch 2 for Q8_0 / Q4_1): they stage one
- *           activation row in LDS, 144 bytes per 32 columns, within the
- *           160 KB of a workgroup.  The matrix-core kernel (batch >= 3, and
- *           Q4_0 at batch 2, n_cols a multiple of 256) stages it in chunks
- *           and has no such limit.
+ *   n_cols  >= 32 and a multiple of 32; at most 36384 at batch 1: the FMA
+ *           kernels stage one activation row in LDS, 144 bytes per 32
+ *           columns, within the 160 KB of a workgroup.  At batch 2..8 longer
+ *           rows go to the matrix-core kernel, which stages them in chunks
+ *           (n_cols a multiple of 256, and the alignments qmv_matvec_path
+ *           lists); otherwise QMV_EINVAL.
  *   x       fp32 [batch][ldx], ldx >= n_cols; 4-byte aligned.
  *   batch   1..8.
  *   y       fp32 [batch][ldy], ldy >= n_rows; 4-byte aligned.

@@ -241,6 +241,29 @@ def test_mfma_path_small_shapes(env, fmt, B):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_auto_path_rows_beyond_fma_staging(env, fmt):
+    """36608 columns: one activation row does not fit the FMA kernels' LDS
+    staging (at most 36384), so batch 1 is refused, and at batch 2..8 the
+    automatic choice takes the matrix cores (bitwise the forced path, within
+    the bound of the oracle) whatever the shape rule prefers."""
+    torch, qmv = env
+    N, K = 40, 36608
+    W = wl.quant_weights(fmt, f"t/long/{N}x{K}", N, K)
+    Wd = dev(torch, W)
+    with pytest.raises(qmv.QmvError):
+        qmv.qmv_matvec_path(fmt, Wd, N, K, dev(torch, wl.activations("t/long/x1", 1, K)), qmv.PATH_AUTO)
+    for B in (2, 3, 8):
+        say(f"long rows {fmt} B={B}")
+        x = wl.activations(f"t/long/x/{B}", B, K)
+        xd = dev(torch, x)
+        ya = mfma_matvec(env, fmt, Wd, N, K, xd, qmv.PATH_AUTO)
+        ym = mfma_matvec(env, fmt, Wd, N, K, xd, qmv.PATH_MFMA)
+        assert torch.equal(ya.view(torch.int32), ym.view(torch.int32)), (fmt, B)
+        yr, S = oracle.matvec(fmt, W, N, K, x)
+        assert_tol(ya.cpu().numpy(), yr, S, (fmt, B))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_mfma_path_random_bytes_and_scales(env, fmt):
     """Arbitrary codes and finite fp16 scales (subnormal to 65504), and
     activations over many binades: the split into two bf16 pieces keeps the
