@@ -748,15 +748,24 @@ bool launch_q6k_mma_auto(const uint8_t* W, int64_t N, int nsb, const XT* x, int6
 // or 3: batch 2 +7% (Q4_0), batch 3 +5% (Q4_0) and +6% (Q4_1), batch 4 +4%
 // (Q4_0, Q8_0), the row-fused steps unchanged; the FMA kernels on the
 // 4096-row q and o as well lost 0.6-6% at batch 3..4.  The super-block
-// formats' FMA kernels hold out longer on 4096-column rows (their
-// matrix-core operands decode 6-bit fields and a pivot, or split scaled
-// codes in two): Q4_K 14336 x 4096 at batch 3 / 4 / 8 17.9 / 19.5 / 38.2 us
-// against 21.0 / 22.5 / 22.8, 4096 x 14336 27.8 / 31.4 / 61.3 against
-// 24.0 / 24.7 / 31.0, 128256 x 4096 at batch 2 111 against 106; Q6_K
-// 14336 x 4096 21.2 / 23.7 / 42.5 against 27.6 / 27.0 / 28.7, 4096 x 14336
-// 32.4 / 38.5 / 71.6 against 28.5 / 29.7 / 35.3.
+// formats' FMA kernels hold out longer (their matrix-core operands decode
+// 6-bit fields and a pivot, or split scaled codes in two); per shape from
+// graph replays, Q4_K / Q6_K: k (1024 rows) on the FMA kernels at every
+// batch (batch 8 10.8 / 10.6 us against 11.1 / 12.5), 4096..6144 rows up
+// to batch 5, 14336 and 28672 rows up to batch 3 (Q4_K) or 4 (Q6_K; Q4_K
+// gate_up at batch 3 / 4 30.6 / 35.8 against 32.7 / 33.6), and
+// 14336-column rows at batch 2 only (Q6_K down at batch 2 / 3 19.6 / 32.0
+// against 28.2 / 27.9).  Whole steps against the earlier rule (matrix cores from batch
+// 5, on long rows from batch 3): Q4_K batch 4 +3%, row-fused +8%, batch 5
+// +1%; Q6_K batch 5 / 8 +3% / +2.5%; the rest unchanged.
 bool use_mfma(qmv_fmt fmt, int64_t N, int nb, int B) {
-    if (fmt == QMV_Q4_K || fmt == QMV_Q6_K) return B >= 5 || (B >= 3 && nb >= 256) || (B >= 2 && N >= 65536);
+    if (fmt == QMV_Q4_K || fmt == QMV_Q6_K) {
+        if (N >= 65536) return B >= 2;
+        if (nb >= 256) return B >= 3;
+        if (N <= 1024) return false;
+        if (N <= 6144) return B >= 6;
+        return B >= (fmt == QMV_Q4_K ? 4 : 5);
+    }
     if (N >= 65536) return B >= 2;
     if (B == 2) return false;
     if (B <= 4) return N > 1024 || nb >= 256;
