@@ -245,6 +245,10 @@ __device__ __forceinline__ void load_block(const uint8_t* W, int64_t g, float& d
 __device__ __forceinline__ float sbyte(uint32_t w, int k) {
     return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(w >> (8 * k))));
 }
+// SiLU(g) = g / (1 + e^-g), in fp32 on the device (expf of the device
+// library); g = -inf or +inf give -0 and +inf, NaN stays NaN.
+__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
+
 __device__ __forceinline__ float ubyte(uint32_t w, int k) {
     return static_cast<float>((w >> (8 * k)) & 0xffu);
 }

@@ -52,10 +52,6 @@ struct PairRoute {
     int32_t top_k, n_experts;
 };
 
-// SiLU(g) = g / (1 + e^-g), in fp32 on the device (expf of the device
-// library); g = -inf or +inf give -0 and +inf, NaN stays NaN.
-__device__ __forceinline__ float silu(float g) { return g / (1.f + expf(-g)); }
-
 // Dense matvec.  A persistent grid (as many workgroups as fit on the GPU at
 // once); wave w of the grid takes row tiles w, w + waves, ... .  A tile is
 // G*RPL rows (G row segments of LPR lanes, RPL rows per lane) and is worked

@@ -97,11 +97,17 @@ __device__ __forceinline__ void q4k_pair_scales(const u32x4& h, const Q4KPairSel
 
 // A wave step covers RW = 64 / LPR rows, one per segment of LPR lanes.
 // (Two rows per lane, each staged activation read feeding both, measured
-// slower at every batch width: 123-228 VGPRs against 63-160.)
-template <int B, int LPR, int NW, class XT, bool ROUTE>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(B == 1 ? 8 : 1))) void q4k_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
-                                                       const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
-                                                       int64_t ldy, int xvec, const SbRoute route) {
+// slower at every batch width: 123-228 VGPRs against 63-160.)  SW (routed,
+// one column): every expert holds 2N rows, gate rows then up rows, and the
+// segment of output row i streams gate row i and up row N + i in the same
+// lanes and steps (two rows per lane, each row's sums as in the one-row
+// form), then writes SiLU(gate) * up.
+template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(B == 1 && !SW ? 8 : 1))) void q4k_kernel(
+    const uint8_t* __restrict__ W, int64_t N, int nsb, const XT* __restrict__ x, int64_t ldx, float* __restrict__ y,
+    int64_t ldy, int xvec, const SbRoute route) {
+    static_assert(!SW || (ROUTE && B == 1), "the fused SwiGLU form is routed, one column");
+    constexpr int NR = SW ? 2 : 1;            // rows per lane
     bool bad = false;   // routed pair with an invalid expert id: its outputs become NaN
     if constexpr (ROUTE) bad = sb_route(route, W, x, y, ldy);
     extern __shared__ __attribute__((aligned(16))) float lds[];
@@ -119,67 +125,101 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(B == 1 
 
     // A step's loads: the tile's first row as a wave-uniform base and 32-bit
     // lane offsets from it (a tile spans RW rows of at most 150 super-blocks).
-    auto load_step = [&](int64_t tile, int t, Q4KGroup& r) {
+    struct Step {
+        Q4KGroup r[NR];                       // [1]: the up row N + i (SW)
+    };
+    auto load_step = [&](int64_t tile, int t, Step& st) {
         const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
         const int64_t r0 = tile * RW;                            // tile < ntiles: r0 < N
-        const uint8_t* base = W + r0 * pitch;
         const int64_t rem = N - 1 - r0;
         const int lim = __builtin_amdgcn_readfirstlane(rem < RW - 1 ? (int)rem : RW - 1);
         const int lr = min(seg, lim);                            // rows past the end: the last row
         const uint32_t off = __umul24((uint32_t)lr, (uint32_t)pitch) + (uint32_t)(g >> 2) * kQ4KBytes;
         const uint32_t coff = off + 16 + 32 * (g & 3);
-        r.h = ld16_aligned(base + off);
-        r.c0 = ld16_aligned(base + coff);
-        r.c1 = ld16_aligned(base + coff + 16);
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const uint8_t* base = W + (r0 + k * N) * pitch;
+            st.r[k].h = ld16_aligned(base + off);
+            st.r[k].c0 = ld16_aligned(base + coff);
+            st.r[k].c1 = ld16_aligned(base + coff + 16);
+        }
     };
 
-    float acc[B];
+    float acc[NR][B];
 #pragma unroll
-    for (int b = 0; b < B; ++b) acc[b] = 0.f;
+    for (int k = 0; k < NR; ++k)
+#pragma unroll
+        for (int b = 0; b < B; ++b) acc[k][b] = 0.f;
     // part = g & 3 for every group g of the lane (on a clamped step past the
     // row's end the result is discarded)
     const Q4KPairSel ps = q4k_pair_sel(li & 3);
-    auto compute_step = [&](int64_t tile, int t, const Q4KGroup& r) {
+    auto compute_step = [&](int64_t tile, int t, const Step& st) {
         const int g = li + LPR * t;
         const bool valid = g < G;
         const int gc = valid ? g : G - 1;
-        const float d = half_bits_to_float(r.h.x);
-        const float dmin = half_bits_to_float(r.h.x >> 16);
-        uint32_t sc2, mn2;
-        q4k_pair_scales(r.h, ps, sc2, mn2);
-        // exact: 11 + 6 significant bits each (and d sc / 16 exact too)
-        const float da = d * ubyte(sc2, 0), ma = dmin * ubyte(mn2, 0);
-        const float db16 = (d * 0.0625f) * ubyte(sc2, 2), mb = dmin * ubyte(mn2, 2);
+        float da[NR], ma[NR], db16[NR], mb[NR];
+#pragma unroll
+        for (int k = 0; k < NR; ++k) {
+            const u32x4& h = st.r[k].h;
+            const float d = half_bits_to_float(h.x);
+            const float dmin = half_bits_to_float(h.x >> 16);
+            uint32_t sc2, mn2;
+            q4k_pair_scales(h, ps, sc2, mn2);
+            // exact: 11 + 6 significant bits each (and d sc / 16 exact too)
+            da[k] = d * ubyte(sc2, 0);
+            ma[k] = dmin * ubyte(mn2, 0);
+            db16[k] = (d * 0.0625f) * ubyte(sc2, 2);
+            mb[k] = dmin * ubyte(mn2, 2);
+        }
         // Sub-block 2 part (the low nibbles of the 32 code bytes), then
         // 2 part + 1 (the high nibbles): a loop that is not unrolled, so the
         // two halves share registers.
-        float s[B];
+        float s[NR][B];
 #pragma unroll
-        for (int b = 0; b < B; ++b) s[b] = 0.f;
+        for (int k = 0; k < NR; ++k)
+#pragma unroll
+            for (int b = 0; b < B; ++b) s[k][b] = 0.f;
 #pragma unroll 1
         for (int h = 0; h < 2; ++h) {
             // low nibbles as c; high nibbles in place, as 16 c, with the
             // scale d sc / 16 (exact): the same products either way
             const uint32_t mask = h ? 0xf0f0f0f0u : 0x0f0f0f0fu;
-            const uint32_t w8[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
-            uint32_t c[1][8];
+            uint32_t c[NR][8];
+            float fd[NR], fm[NR];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) c[0][i] = opaque_bits(w8[i] & mask);
-            const float fd[1] = {h ? db16 : da}, fm[1] = {h ? -mb : -ma};
-            float sh_dot[1][B];
-            dot_multi<Q4KSub, 1, B>(c, fd, fm, xs + gc * kSbXPad + 32 * h, G * kSbXPad, sh_dot, B);
+            for (int k = 0; k < NR; ++k) {
+                const Q4KGroup& r = st.r[k];
+                const uint32_t w8[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
 #pragma unroll
-            for (int b = 0; b < B; ++b) s[b] += sh_dot[0][b];
+                for (int i = 0; i < 8; ++i) c[k][i] = opaque_bits(w8[i] & mask);
+                fd[k] = h ? db16[k] : da[k];
+                fm[k] = h ? -mb[k] : -ma[k];
+            }
+            float sh_dot[NR][B];
+            dot_multi<Q4KSub, NR, B>(c, fd, fm, xs + gc * kSbXPad + 32 * h, G * kSbXPad, sh_dot, B);
+#pragma unroll
+            for (int k = 0; k < NR; ++k)
+#pragma unroll
+                for (int b = 0; b < B; ++b) s[k][b] += sh_dot[k][b];
         }
 #pragma unroll
-        for (int b = 0; b < B; ++b) acc[b] = valid ? acc[b] + s[b] : acc[b];
-        if (t == T - 1) {
+        for (int k = 0; k < NR; ++k)
 #pragma unroll
-            for (int b = 0; b < B; ++b) {
-                const float tot = segment_sum<LPR>(acc[b]);
-                const int64_t row = tile * RW + seg;
-                if (li == 0 && row < N) y[b * ldy + row] = bad ? __builtin_nanf("") : tot;
-                acc[b] = 0.f;
+            for (int b = 0; b < B; ++b) acc[k][b] = valid ? acc[k][b] + s[k][b] : acc[k][b];
+        if (t == T - 1) {
+            const int64_t row = tile * RW + seg;
+            if constexpr (SW) {
+                const float gs = segment_sum<LPR>(acc[0][0]);
+                const float us = segment_sum<LPR>(acc[1][0]);
+                if (li == 0 && row < N) y[row] = bad ? __builtin_nanf("") : silu(gs) * us;
+                acc[0][0] = acc[1][0] = 0.f;
+            } else {
+#pragma unroll
+                for (int b = 0; b < B; ++b) {
+                    const float tot = segment_sum<LPR>(acc[0][b]);
+                    if (li == 0 && row < N) y[b * ldy + row] = bad ? __builtin_nanf("") : tot;
+                    acc[0][b] = 0.f;
+                }
             }
         }
     };
@@ -194,8 +234,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(B == 1 
     int lt = 0;
     int64_t ctile = ltile;                             // next step to compute
     int ct = 0;
-    Q4KGroup buf[2];
-    auto load_next = [&](Q4KGroup& r) {
+    Step buf[2];
+    auto load_next = [&](Step& r) {
         load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
         if (ltile < ntiles) advance(ltile, lt);
     };
@@ -259,10 +299,11 @@ struct Q4KFormat {
     static constexpr const char* kEntry = "qmv_q4_k";
     static constexpr int kWAlign = 16;         // the kernel's aligned 16-byte loads
     static constexpr bool kMfma = true;        // batch 2..8: Mma<Q4KSuper> in the matrix-core kernel
+    static constexpr bool kSwiglu = true;      // MoE gate||up with SiLU(gate) * up fused (routed kernel)
     static constexpr int kDequantWeights = 32;
     static constexpr int kBytes = kQ4KBytes;
-    template <int B, int LPR, int NW, class XT, bool ROUTE>
-    static auto kernel() { return q4k_kernel<B, LPR, NW, XT, ROUTE>; }
+    template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>
+    static auto kernel() { return q4k_kernel<B, LPR, NW, XT, ROUTE, SW>; }
     static auto dequant_kernel() { return q4k_dequant_kernel; }
 };
 

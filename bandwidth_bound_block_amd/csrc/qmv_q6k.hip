@@ -255,10 +255,14 @@ struct Q6KFormat {
     static constexpr const char* kEntry = "qmv_q6_k";
     static constexpr int kWAlign = 4;          // 4-byte-aligned loads, re-aligned in registers
     static constexpr bool kMfma = true;        // batch 2..8: q6k_mma_kernel
+    static constexpr bool kSwiglu = false;
     static constexpr int kDequantWeights = 16;
     static constexpr int kBytes = kQ6KBytes;
-    template <int B, int LPR, int NW, class XT, bool ROUTE>
-    static auto kernel() { return q6k_kernel<B, LPR, NW, XT, ROUTE>; }
+    template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>
+    static auto kernel() {
+        static_assert(!SW, "no fused SwiGLU form for Q6_K");
+        return q6k_kernel<B, LPR, NW, XT, ROUTE>;
+    }
     static auto dequant_kernel() { return q6k_dequant_kernel; }
 };
 

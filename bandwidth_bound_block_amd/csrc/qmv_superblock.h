@@ -128,13 +128,14 @@ inline int sb_pick_lpr(int G) {
     return best;
 }
 
-// route: MoE pairs (grid rows) or nullptr (one dense matrix).
-template <class Fmt, int B, int LPR, int NW, class XT>
+// route: MoE pairs (grid rows) or nullptr (one dense matrix).  SW (routed
+// only): N output rows of SiLU(gate) * up from experts of 2N rows.
+template <class Fmt, int B, int LPR, int NW, class XT, bool SW = false>
 int32_t sb_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                   hipStream_t st, const SbRoute* route, int pairs) {
     if (route) {
         if constexpr (B == 1) {
-            auto kern = Fmt::template kernel<1, LPR, NW, XT, true>();
+            auto kern = Fmt::template kernel<1, LPR, NW, XT, true, SW>();
             const size_t lds = (size_t)4 * nsb * kSbXPad * sizeof(float);
             size_t dyn_max = 0;
             if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, Fmt::kEntry, &dyn_max))
@@ -171,14 +172,14 @@ int32_t sb_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx
 
 // 8 waves per workgroup at every batch width (a workgroup of 16 would cap
 // the registers at 128, and batch 6..8 need more).
-template <class Fmt, int B, class XT>
+template <class Fmt, int B, class XT, bool SW = false>
 int32_t sb_launch_lpr(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx, float* y, int64_t ldy,
                       hipStream_t st, const SbRoute* route = nullptr, int pairs = 1) {
     switch (sb_pick_lpr(4 * nsb)) {
-    case 64: return sb_launch<Fmt, B, 64, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
-    case 32: return sb_launch<Fmt, B, 32, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
-    case 16: return sb_launch<Fmt, B, 16, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
-    default: return sb_launch<Fmt, B, 8, 8, XT>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
+    case 64: return sb_launch<Fmt, B, 64, 8, XT, SW>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
+    case 32: return sb_launch<Fmt, B, 32, 8, XT, SW>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
+    case 16: return sb_launch<Fmt, B, 16, 8, XT, SW>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
+    default: return sb_launch<Fmt, B, 8, 8, XT, SW>(W, N, nsb, x, ldx, y, ldy, st, route, pairs);
     }
 }
 
@@ -282,10 +283,11 @@ int32_t sb_dequant(const void* W, int64_t N, int64_t K, float* out, void* stream
 }
 
 // MoE experts: every (token, slot) pair is one grid row of the batch-1
-// kernel (a pair's expert is streamed for that pair; at batch 1 the pairs
-// of a token have distinct experts).  The fused SwiGLU form is not offered
-// for these formats.
-template <class Fmt, class XT>
+// kernel (a pair's expert is streamed for that pair; an expert shared by
+// several pairs is read from HBM about once, its other reads hitting the
+// caches).  SW: the fused SwiGLU form, N output rows per pair from experts
+// of 2N rows (formats whose kernel has it).
+template <class Fmt, class XT, bool SW = false>
 int32_t sb_moe_t(const char* name, const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K,
                  const int32_t* ids, int32_t batch, int32_t top_k, const XT* x, int64_t xs_tok, int64_t xs_slot,
                  float* y, void* stream) {
@@ -297,8 +299,10 @@ int32_t sb_moe_t(const char* name, const void* Wx, int64_t estride, int32_t E, i
     if (batch < 1 || batch > 8) return fail(QMV_EINVAL, "%s: batch must be in 1..8 (got %d)", name, batch);
     if (top_k < 1 || top_k > 16) return fail(QMV_EINVAL, "%s: top_k must be in 1..16 (got %d)", name, top_k);
     const int64_t nsb = K / kSbWeights;
-    if (nsb > (1 << 24) || N > ((int64_t)1 << 40) / nsb) return fail(QMV_EINVAL, "%s: matrix too large", name);
-    const int64_t mbytes = N * nsb * Fmt::kBytes;
+    if (SW && N > ((int64_t)1 << 39)) return fail(QMV_EINVAL, "%s: n_ff too large", name);
+    const int64_t rows = SW ? 2 * N : N;      // rows of one expert matrix
+    if (nsb > (1 << 24) || rows > ((int64_t)1 << 40) / nsb) return fail(QMV_EINVAL, "%s: matrix too large", name);
+    const int64_t mbytes = rows * nsb * Fmt::kBytes;
     if (estride < mbytes || estride % Fmt::kWAlign)
         return fail(QMV_EINVAL, "%s: expert_stride_bytes (%lld) must be >= %lld and a multiple of %d", name,
                     (long long)estride, (long long)mbytes, Fmt::kWAlign);
@@ -317,27 +321,39 @@ int32_t sb_moe_t(const char* name, const void* Wx, int64_t estride, int32_t E, i
     if (4 * nsb * kSbXPad * (int64_t)sizeof(float) > kLdsMax)
         return fail(QMV_EINVAL, "%s: n_cols %lld too large for one activation row in LDS", name, (long long)K);
     const SbRoute route{ids, estride, xs_tok, xs_slot, top_k, E};
-    return sb_launch_lpr<Fmt, 1, XT>(static_cast<const uint8_t*>(Wx), N, (int)nsb, x, K, y, N, as_stream(stream),
-                                     &route, batch * top_k);
+    return sb_launch_lpr<Fmt, 1, XT, SW>(static_cast<const uint8_t*>(Wx), N, (int)nsb, x, K, y, N,
+                                         as_stream(stream), &route, batch * top_k);
+}
+
+template <class Fmt, bool SW>
+int32_t sb_moe_x(const char* name, const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K,
+                 const int32_t* ids, int32_t batch, int32_t top_k, const void* x, int32_t x_type, int64_t xs_tok,
+                 int64_t xs_slot, float* y, void* stream) {
+    switch (x_type) {
+    case QMV_X_F32:
+        return sb_moe_t<Fmt, float, SW>(name, Wx, estride, E, N, K, ids, batch, top_k, static_cast<const float*>(x),
+                                        xs_tok, xs_slot, y, stream);
+    case QMV_X_F16:
+        return sb_moe_t<Fmt, _Float16, SW>(name, Wx, estride, E, N, K, ids, batch, top_k,
+                                           static_cast<const _Float16*>(x), xs_tok, xs_slot, y, stream);
+    case QMV_X_BF16:
+        return sb_moe_t<Fmt, __bf16, SW>(name, Wx, estride, E, N, K, ids, batch, top_k,
+                                         static_cast<const __bf16*>(x), xs_tok, xs_slot, y, stream);
+    default: return fail(QMV_EINVAL, "%s: unknown activation type %d", name, (int)x_type);
+    }
 }
 
 template <class Fmt>
 int32_t sb_moe(const char* name, bool swiglu, const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K,
                const int32_t* ids, int32_t batch, int32_t top_k, const void* x, int32_t x_type, int64_t xs_tok,
                int64_t xs_slot, float* y, void* stream) {
-    if (swiglu) return fail(QMV_EUNSUPPORTED, "%s: the fused SwiGLU form is not offered for %s", name, Fmt::kLabel);
-    switch (x_type) {
-    case QMV_X_F32:
-        return sb_moe_t<Fmt>(name, Wx, estride, E, N, K, ids, batch, top_k, static_cast<const float*>(x), xs_tok,
-                             xs_slot, y, stream);
-    case QMV_X_F16:
-        return sb_moe_t<Fmt>(name, Wx, estride, E, N, K, ids, batch, top_k, static_cast<const _Float16*>(x), xs_tok,
-                             xs_slot, y, stream);
-    case QMV_X_BF16:
-        return sb_moe_t<Fmt>(name, Wx, estride, E, N, K, ids, batch, top_k, static_cast<const __bf16*>(x), xs_tok,
-                             xs_slot, y, stream);
-    default: return fail(QMV_EINVAL, "%s: unknown activation type %d", name, (int)x_type);
+    if (swiglu) {
+        if constexpr (Fmt::kSwiglu)
+            return sb_moe_x<Fmt, true>(name, Wx, estride, E, N, K, ids, batch, top_k, x, x_type, xs_tok, xs_slot, y,
+                                       stream);
+        return fail(QMV_EUNSUPPORTED, "%s: the fused SwiGLU form is not offered for %s", name, Fmt::kLabel);
     }
+    return sb_moe_x<Fmt, false>(name, Wx, estride, E, N, K, ids, batch, top_k, x, x_type, xs_tok, xs_slot, y, stream);
 }
 
 // The combine and chain-group slots of a super-block format's table.

@@ -58,16 +58,16 @@ TRAFFIC_RECORDS = {
     "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>": {
         "key": "kernel_c_q8_0",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "ef98cca793e8ef6e0658d49f8a98a77928cb29f877d09980fb477f24e8c97311", "bytes_per_launch": 83478763, "ratio": 1.0025,
+        "sha256": "6b37feb96e956bbc9921650c451db57fc05200d9393cf6b559336c6381b5f14c", "bytes_per_launch": 83478763, "ratio": 1.0025,
         "workload": "8B Q8_0 decode step, batch 1"},
     "qmv_kernel<Q8_0, 1, 64, 1, 2, 8, 2, false, float, false>": {
         "key": "kernel_q8_0_o",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "ef98cca793e8ef6e0658d49f8a98a77928cb29f877d09980fb477f24e8c97311", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
+        "sha256": "6b37feb96e956bbc9921650c451db57fc05200d9393cf6b559336c6381b5f14c", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
     "qmv_kernel_c<Q8_0, 4, 16, 2, float, 1>": {
         "key": "kernel_c16_q8_0_down",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "ef98cca793e8ef6e0658d49f8a98a77928cb29f877d09980fb477f24e8c97311", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
+        "sha256": "6b37feb96e956bbc9921650c451db57fc05200d9393cf6b559336c6381b5f14c", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
     "i8_stream_kernel": {
         "key": "i8_stream",
         "sources": ["bandwidth_bound_block_amd/csrc/qmv_int8.hip", "bandwidth_bound_block_amd/csrc/qmv_host.h"],

@@ -140,9 +140,9 @@ int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
  * width among themselves); qmv_matvec_path chooses the family.
  * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q4_K (matvec on
  * every path; QMV_PATH_MFMA needs batch 2..8, x aligned to 4 elements and
- * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do qmv_moe and
- * qmv_moe_xt; qmv_moe_swiglu, qmv_moe_combine and qmv_chain do not
- * (QMV_EUNSUPPORTED).
+ * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do qmv_moe,
+ * qmv_moe_xt, qmv_moe_swiglu and qmv_moe_swiglu_xt; qmv_moe_combine and
+ * qmv_chain do not (QMV_EUNSUPPORTED).
  */
 int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
@@ -330,7 +330,9 @@ int32_t qmv_moe_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_byt
  * Arguments as qmv_moe, with expert_stride_bytes >= the bytes of
  * 2*n_ff rows; h is fp32 [batch][top_k][n_ff], 4-byte aligned.  Invalid
  * ids give quiet NaN rows, as in qmv_moe.
- * Errors: as qmv_moe; QMV_EUNSUPPORTED for QMV_Q4_K and QMV_Q6_K.
+ * QMV_Q4_K experts run it in the routed Q4_K kernel (gate row i and up row
+ * n_ff + i of a pair in the same lanes and steps).
+ * Errors: as qmv_moe; QMV_EUNSUPPORTED for QMV_Q6_K.
  */
 int32_t qmv_moe_swiglu(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                        int32_t n_experts, int64_t n_ff, int64_t n_cols,

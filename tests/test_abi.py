@@ -110,8 +110,12 @@ def test_q4_k_argument_errors(qmv):
     assert L.qmv_moe(qmv.Q4_K, A + 4, 1152, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EALIGN
     assert "16-byte" in qmv.last_error()
     assert L.qmv_moe(qmv.Q4_K, A, 1152, 2, 8, 256, A, 9, 1, A, 256, 256, A, None) == EINVAL
-    assert L.qmv_moe_swiglu(qmv.Q4_K, A, 2304, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
-    assert "SwiGLU" in qmv.last_error()
+    # the fused SwiGLU form: experts of 2 n_ff rows
+    assert L.qmv_moe_swiglu(qmv.Q4_K, A, 2288, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert "expert_stride" in qmv.last_error() and "2304" in qmv.last_error()
+    assert L.qmv_moe_swiglu(qmv.Q4_K, A + 4, 2304, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EALIGN
+    assert L.qmv_moe_swiglu(qmv.Q4_K, A, 2304, 2, 8, 256, A, 9, 1, A, 256, 256, A, None) == EINVAL
+    assert L.qmv_moe_swiglu(qmv.Q4_K, A, 2304, 2, 8, 288, A, 1, 1, A, 288, 288, A, None) == EINVAL
     assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert "Q4_K" in qmv.last_error()
     assert L.qmv_chain(qmv.Q4_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED and "not supported" in qmv.last_error()

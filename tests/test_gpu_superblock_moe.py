@@ -140,3 +140,89 @@ def test_superblock_moe_x16_and_zero_heavy(env, fmt):
     yr, S = oracle.moe(fmt, Wz, stride, E, N, K, ids, xz)
     y = run(env, fmt, Wz, stride, N, K, ids, xz)
     assert_tol(y, yr, S, (fmt, "zero-heavy"))
+
+
+# ------------------------------------------------------------------ fused SwiGLU (Q4_K)
+def swiglu_bound(h, g, u, Sg, Su):
+    """|h_gpu - h| for h = SiLU(g) u from fp32 g, u within the matvec bound
+    (tg, tu): |SiLU'| <= 1.1, so |dh| <= 1.1 tg (|u| + tu) + (|SiLU(g)| +
+    1.1 tg) tu, plus the fp32 epilogue (a few ulps of h)."""
+    tg, tu = 1e-4 * Sg + 1e-6, 1e-4 * Su + 1e-6
+    sg = np.abs(g / (1.0 + np.exp(-g)))
+    return 1.1 * tg * (np.abs(u) + tu) + (sg + 1.1 * tg) * tu + 2.0 ** -20 * np.abs(h) + 1e-30
+
+
+@pytest.mark.parametrize("B", [1, 2, 8])
+def test_q4k_moe_swiglu_30b_shapes(env, B):
+    """Q4_K experts of gate||up 1536 x 2048 (gate rows, then up rows), top-8
+    per token: h against the oracle within the propagated bound on sampled
+    rows, and the gate and up sums those of qmv_moe on the same experts (h
+    == SiLU(g) u up to the epilogue's rounding)."""
+    torch, qmv = env
+    H, F = wl.MOE_HIDDEN, wl.MOE_FFN
+    Wall = experts("q4_k", "gate_up", 2 * F, H)
+    stride = wl.block_bytes("q4_k", 2 * F, H)
+    ids = wl.moe_ids(f"t/sbmoe/sw/ids/{B}", B, T, E)
+    x = wl.activations(f"t/sbmoe/sw/x/{B}", B, H)
+    say(f"q4_k moe swiglu B={B}")
+    Wd, idd, xd = dev(torch, Wall), dev(torch, ids), dev(torch, x)
+    h = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, H, idd, xd)
+    y = qmv.qmv_moe("q4_k", Wd, stride, E, 2 * F, H, idd, xd)
+    torch.cuda.synchronize()
+    h, y = h.cpu().numpy(), y.cpu().numpy().astype(np.float64)
+    rows = np.sort(np.random.default_rng(B).choice(F, size=96, replace=False))
+    hr, g, u, Sg, Su = oracle.moe_swiglu("q4_k", Wall, stride, E, F, H, ids, x, rows=rows)
+    err = np.abs(h[:, :, rows].astype(np.float64) - hr)
+    bound = swiglu_bound(hr, g, u, Sg, Su)
+    assert np.all(err <= bound), float((err / bound).max())
+    g32, u32 = y[:, :, :F], y[:, :, F:]
+    href = g32 / (1.0 + np.exp(-g32)) * u32
+    assert np.all(np.abs(h - href) <= 2.0 ** -21 * np.abs(href) + 1e-37)
+
+
+def test_q4k_moe_swiglu_edges(env):
+    """Padded strides, duplicate and invalid ids (quiet NaN rows, the others
+    within the bound), per-slot inputs, 16-bit activations (bitwise the fp32
+    call on the widened values), a ragged row count; Q6_K refuses the fused
+    form."""
+    torch, qmv = env
+    F, K = 300, 1024
+    per = wl.block_bytes("q4_k", 2 * F, K)
+    stride = per + 512
+    Wm = wl.quant_weights("q4_k", "t/sbmoe/swedge", E * 2 * F, K).reshape(E, per)
+    Wall = np.zeros((E, stride), dtype=np.uint8)
+    Wall[:, :per] = Wm
+    Wall = Wall.reshape(-1)
+    ids = np.array([[0, 1, 2, 3, 4, 5, 6, 7], [31, 31, 5, 5, 0, 9, -1, 30], [3, 1, 4, 1, 5, 9, 2, E]],
+                   dtype=np.int32)
+    B = ids.shape[0]
+    x = wl.activations("t/sbmoe/swedge/x", B, K)
+    Wd, idd = dev(torch, Wall), dev(torch, ids)
+    say("q4_k moe swiglu edges")
+    h = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, K, idd, dev(torch, x))
+    torch.cuda.synchronize()
+    h = h.cpu().numpy()
+    valid = (ids >= 0) & (ids < E)
+    assert np.all(np.isnan(h[~valid])) and not np.any(np.isnan(h[valid]))
+    hr, g, u, Sg, Su = oracle.moe_swiglu("q4_k", Wall, stride, E, F, K, np.where(valid, ids, 0).astype(np.int32), x)
+    err = np.abs(h[valid].astype(np.float64) - hr[valid])
+    assert np.all(err <= swiglu_bound(hr[valid], g[valid], u[valid], Sg[valid], Su[valid]))
+    for kind, tt in [("f16", torch.float16), ("bf16", torch.bfloat16)]:
+        xh = dev(torch, x).to(tt)
+        h16 = qmv.qmv_moe_swiglu_xt("q4_k", Wd, stride, E, F, K, idd, xh)
+        h32 = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, K, idd, xh.float())
+        torch.cuda.synchronize()
+        assert torch.equal(h16.view(torch.int32), h32.view(torch.int32)), kind
+    # one input per token and slot
+    xs = wl.activations("t/sbmoe/swedge/xs", B * T, K).reshape(B, T, K)
+    hs = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, K, idd, dev(torch, xs))
+    torch.cuda.synchronize()
+    hs = hs.cpu().numpy()
+    hr, g, u, Sg, Su = oracle.moe_swiglu("q4_k", Wall, stride, E, F, K, np.where(valid, ids, 0).astype(np.int32),
+                                         None, x_slots=xs)
+    err = np.abs(hs[valid].astype(np.float64) - hr[valid])
+    assert np.all(err <= swiglu_bound(hr[valid], g[valid], u[valid], Sg[valid], Su[valid]))
+    W6 = dev(torch, wl.quant_weights("q6_k", "t/sbmoe/sw6", 2 * 2 * 8, 256).reshape(-1))
+    with pytest.raises(qmv.QmvError):
+        qmv.qmv_moe_swiglu("q6_k", W6, wl.block_bytes("q6_k", 16, 256), 2, 8, 256,
+                           dev(torch, np.zeros((1, 1), dtype=np.int32)), dev(torch, np.zeros((1, 256), np.float32)))
