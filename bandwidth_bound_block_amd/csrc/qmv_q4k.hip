@@ -271,6 +271,159 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(B == 1 
     }
 }
 
+// One 64-weight group's sum for one column, in q4k_kernel's order (the two
+// halves in turn through dot_multi): bitwise that kernel's step sum.
+__device__ __forceinline__ float q4k_group_sum(const Q4KGroup& r, const Q4KPairSel& ps, const float* xg) {
+    const float d = half_bits_to_float(r.h.x);
+    const float dmin = half_bits_to_float(r.h.x >> 16);
+    uint32_t sc2, mn2;
+    q4k_pair_scales(r.h, ps, sc2, mn2);
+    const float da = d * ubyte(sc2, 0), ma = dmin * ubyte(mn2, 0);
+    const float db16 = (d * 0.0625f) * ubyte(sc2, 2), mb = dmin * ubyte(mn2, 2);
+    float s = 0.f;
+#pragma unroll 1
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t mask = h ? 0xf0f0f0f0u : 0x0f0f0f0fu;
+        const uint32_t w8[8] = {r.c0.x, r.c0.y, r.c0.z, r.c0.w, r.c1.x, r.c1.y, r.c1.z, r.c1.w};
+        uint32_t c[1][8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) c[0][i] = opaque_bits(w8[i] & mask);
+        const float fd[1] = {h ? db16 : da}, fm[1] = {h ? -mb : -ma};
+        float sh[1][1];
+        dot_multi<Q4KSub, 1, 1>(c, fd, fm, xg + 32 * h, 0, sh, 1);
+        s += sh[0][0];
+    }
+    return s;
+}
+
+// MoE down projection with the router-weighted combine, token-major:
+// workgroup (bx, b) computes rows [r0, r1) of out[b] = sum_s w[b][s] *
+// DEQ(W_{e_s}) x_{b,s} over the top_k slots of token b.  The slots'
+// activation vectors are staged together (SC at a time when they do not all
+// fit the LDS).  The work is the units (slot, tile of RW rows); wave w takes
+// units w, w + NW, ... with a two-deep load pipeline across them, and each
+// unit's row sums (q4k_kernel's, with the same lanes per row: bitwise the
+// qmv_moe outputs) go to LDS.  Then one thread per row adds them in slot
+// order, fma(w_s, y_s, acc) from s = 0 up.  An expert routed from several
+// tokens is read once per token (no atomics, no workspace).
+template <int LPR, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(5))) void q4k_combine_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
+                                                               int n_experts, int64_t N, int nsb,
+                                                               const int32_t* __restrict__ ids,
+                                                               const float* __restrict__ wts, int top_k,
+                                                               const float* __restrict__ x, int64_t xs_tok,
+                                                               int64_t xs_slot, float* __restrict__ out, int xvec,
+                                                               int SC, int rows_wg) {
+    __shared__ const uint8_t* s_base[kSbMaxSlots];
+    __shared__ float s_w[kSbMaxSlots];
+    __shared__ int s_bad;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int RW = 64 / LPR;              // rows per tile
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int seg = lane / LPR;
+    const int li = lane % LPR;
+    const int G = 4 * nsb;                    // 64-weight groups per row
+    const int T = (G + LPR - 1) / LPR;        // steps per row
+    const int64_t pitch = (int64_t)nsb * kQ4KBytes;
+    const int b = blockIdx.y;
+    const int64_t ntiles = (N + RW - 1) / RW;
+    const int per_wg = rows_wg / RW;
+    const int64_t tb = (int64_t)blockIdx.x * per_wg;
+    const int64_t te = min(ntiles, tb + per_wg);
+    if (tb >= te) return;                     // the whole workgroup: no barrier is skipped by part of it
+    const int wtiles = (int)(te - tb);
+    const int per_col = G * kSbXPad;          // floats of one staged slot vector
+    float* xs = lds;                          // [SC][G][kSbXPad]
+    float* ybuf = lds + SC * per_col;         // [top_k][rows_wg]: row sums per slot
+    const int64_t r0 = tb * RW;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    if (tid < top_k) {
+        const int e = ids[b * top_k + tid];
+        const bool eb = e < 0 || e >= n_experts;
+        if (eb) s_bad = 1;
+        s_base[tid] = Wx + (int64_t)(eb ? 0 : e) * estride;
+        s_w[tid] = wts[b * top_k + tid];
+    }
+    __syncthreads();                          // s_base, s_w, s_bad
+    const Q4KPairSel ps = q4k_pair_sel(li & 3);
+    for (int s0 = 0; s0 < top_k; s0 += SC) {
+        const int sc = min(SC, top_k - s0);
+        const int units = sc * wtiles;
+        const int my_units = wave < units ? (units - wave + NW - 1) / NW : 0;
+        const int nsteps = my_units * T;
+        // the chunk's slot vectors (every wave is done with the previous
+        // chunk's: its units all ended before this barrier)
+        __syncthreads();
+        for (int k = 0; k < sc; ++k) {
+            const float* xcol[1] = {x + (int64_t)b * xs_tok + (int64_t)(s0 + k) * xs_slot};
+            // groups of 64 in order, each padded to kSbXPad floats; ends with a barrier
+            sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs + k * per_col, xvec != 0,
+                                          [](int e) { return (e >> 6) * kSbXPad + (e & 63); });
+        }
+        if (nsteps == 0) continue;
+        // step n of this wave: unit q = wave + NW (n / T), group step t = n % T
+        auto load = [&](int n, Q4KGroup& r) {
+            const int q = wave + NW * (n / T);
+            const int t = n % T;
+            const int slot = q / wtiles;
+            const int64_t tile = tb + (q - slot * wtiles);
+            const int g = min(li + LPR * t, G - 1);             // clamp: stays in bounds
+            const int64_t rt = tile * RW;                        // tile < ntiles: rt < N
+            const int64_t rem = N - 1 - rt;
+            const int lr = min(seg, rem < RW - 1 ? (int)rem : RW - 1);   // rows past the end: the last row
+            const uint8_t* base = s_base[s0 + slot] + rt * pitch;
+            const uint32_t off = __umul24((uint32_t)lr, (uint32_t)pitch) + (uint32_t)(g >> 2) * kQ4KBytes;
+            const uint32_t coff = off + 16 + 32 * (g & 3);
+            r.h = ld16_aligned(base + off);
+            r.c0 = ld16_aligned(base + coff);
+            r.c1 = ld16_aligned(base + coff + 16);
+        };
+        float acc = 0.f;
+        auto compute = [&](int n, const Q4KGroup& r) {
+            const int q = wave + NW * (n / T);
+            const int t = n % T;
+            const int slot = q / wtiles;
+            const int64_t tile = tb + (q - slot * wtiles);
+            const int g = li + LPR * t;
+            const bool valid = g < G;
+            const int gc = valid ? g : G - 1;
+            const float s = q4k_group_sum(r, ps, xs + slot * per_col + gc * kSbXPad);
+            acc = valid ? acc + s : acc;
+            if (t == T - 1) {
+                const float tot = segment_sum<LPR>(acc);
+                const int64_t row = tile * RW + seg;
+                if (li == 0 && row < N) ybuf[(s0 + slot) * rows_wg + (row - r0)] = tot;
+                acc = 0.f;
+            }
+        };
+        // two register buffers used in turn (nsteps is wave-uniform)
+        Q4KGroup buf0, buf1;
+        load(0, buf0);
+        for (int n = 0;;) {
+            if (n + 1 < nsteps) load(n + 1, buf1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(n, buf0);
+            if (++n == nsteps) break;
+            if (n + 1 < nsteps) load(n + 1, buf0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(n, buf1);
+            if (++n == nsteps) break;
+        }
+    }
+    __syncthreads();
+    const float qnan = __builtin_nanf("");
+    const int64_t r1 = min(te * RW, N);
+    for (int64_t row = r0 + tid; row < r1; row += 64 * NW) {
+        const float* yr = ybuf + (row - r0);
+        float v = s_w[0] * yr[0];
+        for (int s = 1; s < top_k; ++s) v = __builtin_fmaf(s_w[s], yr[s * rows_wg], v);
+        out[(int64_t)b * N + row] = s_bad ? qnan : v;
+    }
+}
+
 // One thread per 32-weight sub-block: out = fma(d sc, c, -dmin mn), the
 // same value the matvec uses for each weight.
 __global__ __launch_bounds__(kThreads) void q4k_dequant_kernel(const uint8_t* __restrict__ W, int64_t nsub,
@@ -300,6 +453,9 @@ struct Q4KFormat {
     static constexpr int kWAlign = 16;         // the kernel's aligned 16-byte loads
     static constexpr bool kMfma = true;        // batch 2..8: Mma<Q4KSuper> in the matrix-core kernel
     static constexpr bool kSwiglu = true;      // MoE gate||up with SiLU(gate) * up fused (routed kernel)
+    static constexpr bool kCombine = true;     // MoE down with the weighted combine fused
+    template <int LPR, int NW>
+    static auto combine_kernel() { return q4k_combine_kernel<LPR, NW>; }
     static constexpr int kDequantWeights = 32;
     static constexpr int kBytes = kQ4KBytes;
     template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>

@@ -26,6 +26,8 @@ namespace qmv {
 namespace {
 
 constexpr int kSbWeights = 256;   // per super-block
+constexpr int kSbMaxSlots = 16;   // top_k of the MoE entry points
+constexpr int kSbCombineRows = 1024;   // rows per workgroup of a combine launch, at most
 
 // MoE routing of the super-block kernels: grid row p = b * top_k + s
 // (blockIdx.y) computes y[p] = DEQ(W_e) x_{b,s} with e = ids[p], x_{b,s} at
@@ -356,17 +358,95 @@ int32_t sb_moe(const char* name, bool swiglu, const void* Wx, int64_t estride, i
     return sb_moe_x<Fmt, false>(name, Wx, estride, E, N, K, ids, batch, top_k, x, x_type, xs_tok, xs_slot, y, stream);
 }
 
-// The combine and chain-group slots of a super-block format's table.
-template <class Fmt>
-int32_t sb_no_combine(const void*, int64_t, int32_t, int64_t, int64_t, const int32_t*, const float*, int32_t, int32_t,
-                      const float*, int64_t, int64_t, float*, void*) {
-    return fail(QMV_EUNSUPPORTED, "qmv_moe_combine: %s experts are not supported", Fmt::kLabel);
+// MoE down with the router-weighted combine (formats whose table has a
+// combine kernel): grid (row ranges, tokens), ranges x tokens filling the
+// GPU once, a range holding at most kSbCombineRows rows; 8 waves per
+// workgroup at batch 1..2 (about one row tile per workgroup: one wave per
+// (slot, tile) unit of a token's 8 slots), else 4.
+template <class Fmt, int LPR, int NW>
+int32_t sb_combine_launch(const uint8_t* Wx, int64_t estride, int E, int64_t N, int nsb, const int32_t* ids,
+                          const float* wts, int batch, int top_k, const float* x, int64_t xs_tok, int64_t xs_slot,
+                          float* out, int xvec, hipStream_t st) {
+    const char* name = "qmv_moe_combine";
+    constexpr int RW = 64 / LPR;
+    auto kern = Fmt::template combine_kernel<LPR, NW>();
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, name, &dyn_max)) return e;
+    const size_t per_col = (size_t)4 * nsb * kSbXPad * sizeof(float);
+    const size_t sums_max = (size_t)top_k * (kSbCombineRows + RW) * sizeof(float);
+    if (per_col + sums_max > dyn_max)
+        return fail(QMV_EINVAL, "%s: n_cols %d too large for one activation row in LDS", name, nsb * kSbWeights);
+    const int SC = (int)std::min<size_t>((size_t)top_k, (dyn_max - sums_max) / per_col);
+    const int64_t ntiles = (N + RW - 1) / RW;
+    const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW,
+                                                SC * per_col + (size_t)top_k * NW * RW * sizeof(float)));
+    const int64_t min_ranges = (ntiles * RW + kSbCombineRows - 1) / kSbCombineRows;
+    const int64_t gx = std::max<int64_t>(
+        min_ranges, std::min<int64_t>(ntiles, std::max<int64_t>(1, (int64_t)device_cu_count() * per_cu / batch)));
+    const int64_t per_wg = (ntiles + gx - 1) / gx;
+    const int rows_wg = (int)(per_wg * RW);
+    const size_t lds = SC * per_col + (size_t)top_k * rows_wg * sizeof(float);
+    hipLaunchKernelGGL(kern, dim3((unsigned)gx, (unsigned)batch), dim3(64 * NW), lds, st, Wx, estride, E, N, nsb,
+                       ids, wts, top_k, x, xs_tok, xs_slot, out, xvec, SC, rows_wg);
+    return check_launch(name);
 }
+
+template <class Fmt>
+int32_t sb_combine(const void* Wx, int64_t estride, int32_t E, int64_t N, int64_t K, const int32_t* ids,
+                   const float* wts, int32_t batch, int32_t top_k, const float* x, int64_t xs_tok, int64_t xs_slot,
+                   float* out, void* stream) {
+    const char* name = "qmv_moe_combine";
+    if constexpr (!Fmt::kCombine) {
+        return fail(QMV_EUNSUPPORTED, "%s: %s experts are not supported", name, Fmt::kLabel);
+    } else {
+        if (!Wx || !ids || !wts || !x || !out) return fail(QMV_EINVAL, "%s: null pointer", name);
+        if (E < 1) return fail(QMV_EINVAL, "%s: n_experts must be >= 1", name);
+        if (N < 1 || K < kSbWeights || K % kSbWeights)
+            return fail(QMV_EINVAL, "%s: bad matrix shape %lld x %lld (n_cols a multiple of 256 for %s)", name,
+                        (long long)N, (long long)K, Fmt::kLabel);
+        if (batch < 1 || batch > 8) return fail(QMV_EINVAL, "%s: batch must be in 1..8 (got %d)", name, batch);
+        if (top_k < 1 || top_k > kSbMaxSlots)
+            return fail(QMV_EINVAL, "%s: top_k must be in 1..16 (got %d)", name, top_k);
+        const int64_t nsb = K / kSbWeights;
+        if (nsb > (1 << 24) || N > ((int64_t)1 << 40) / nsb) return fail(QMV_EINVAL, "%s: matrix too large", name);
+        const int64_t mbytes = N * nsb * Fmt::kBytes;
+        if (estride < mbytes || estride % Fmt::kWAlign)
+            return fail(QMV_EINVAL, "%s: expert_stride_bytes (%lld) must be >= %lld and a multiple of %d", name,
+                        (long long)estride, (long long)mbytes, Fmt::kWAlign);
+        if (E > 1 && estride > ((int64_t)1 << 46) / (E - 1)) return fail(QMV_EINVAL, "%s: experts too large", name);
+        if (batch > 1 && xs_tok < K) return fail(QMV_EINVAL, "%s: x_stride_token must be >= n_cols", name);
+        if (xs_tok < 0) return fail(QMV_EINVAL, "%s: x_stride_token must be >= 0", name);
+        if (top_k > 1 && xs_slot != 0 && xs_slot < K)
+            return fail(QMV_EINVAL, "%s: x_stride_slot must be 0 or >= n_cols", name);
+        if (xs_slot < 0) return fail(QMV_EINVAL, "%s: x_stride_slot must be >= 0", name);
+        if (!aligned(Wx, Fmt::kWAlign))
+            return fail(QMV_EALIGN, "%s: W_experts must be %d-byte aligned for %s", name, Fmt::kWAlign, Fmt::kLabel);
+        if (!aligned(out, 4) || !aligned(ids, 4) || !aligned(wts, 4) || !aligned(x, 4))
+            return fail(QMV_EALIGN, "%s: x, out, expert_ids and weights must be 4-byte aligned", name);
+        const int xvec = (aligned(x, 16) && xs_tok % 4 == 0 && xs_slot % 4 == 0) ? 1 : 0;
+        const uint8_t* W8 = static_cast<const uint8_t*>(Wx);
+        hipStream_t st = as_stream(stream);
+        auto go = [&](auto lpr) {
+            constexpr int L = decltype(lpr)::value;
+            return batch <= 2 ? sb_combine_launch<Fmt, L, 8>(W8, estride, E, N, (int)nsb, ids, wts, batch, top_k, x,
+                                                             xs_tok, xs_slot, out, xvec, st)
+                              : sb_combine_launch<Fmt, L, 4>(W8, estride, E, N, (int)nsb, ids, wts, batch, top_k, x,
+                                                             xs_tok, xs_slot, out, xvec, st);
+        };
+        switch (sb_pick_lpr(4 * nsb)) {
+        case 64: return go(std::integral_constant<int, 64>{});
+        case 32: return go(std::integral_constant<int, 32>{});
+        case 16: return go(std::integral_constant<int, 16>{});
+        default: return go(std::integral_constant<int, 8>{});
+        }
+    }
+}
+// The chain-group slot of a super-block format's table.
 inline bool sb_no_group(const RowSegs&, int, const float*, hipStream_t, bool, int32_t*) { return false; }
 
 template <class Fmt>
 const FormatOps& sb_format_ops() {
-    static const FormatOps ops = {sb_matvec<Fmt>, sb_dequant<Fmt>, sb_moe<Fmt>, sb_no_combine<Fmt>, sb_no_group};
+    static const FormatOps ops = {sb_matvec<Fmt>, sb_dequant<Fmt>, sb_moe<Fmt>, sb_combine<Fmt>, sb_no_group};
     return ops;
 }
 

@@ -24,7 +24,7 @@ on the host (cpu_baseline) and a one-number summary per sweep.
 Extra workloads: the Q8_0 1024 x 1024 matvec over 480 rotated copies (so
 every call reads HBM), Q4_0 / Q4_1 / Q4_K / Q6_K at batch 1, 2, 4, 8, the int8 requant path
 on Qwen3-0.6B shapes and the MoE expert path (plain and fused) at batch
-1, 2, 4, 8, with Q4_K experts at batch 1 and 8.
+1, 2, 4, 8, with Q4_K experts (plain and fused) at batch 1 and 8.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--sweeps all|none|a,b] [--detail FILE]
 """
@@ -399,7 +399,7 @@ def build_moe(torch, qmv, wl, batch, fmt="q4_0"):
     return sw
 
 
-def build_moe_block(torch, qmv, wl, batch):
+def build_moe_block(torch, qmv, wl, batch, fmt="q4_0"):
     """48 MoE blocks with the steps around the expert matvecs fused: per
     layer qmv_moe_swiglu over gate||up (h = SiLU(gate x) * (up x), 768 per
     slot) and qmv_moe_combine over down (out = sum_s w_s * down_s h_s),
@@ -407,18 +407,20 @@ def build_moe_block(torch, qmv, wl, batch):
     routed expert once (the method's bytes); the combine kernel reads an
     expert once per token routed to it."""
     import numpy as np
-    sw = Sweep(f"moe30b_block_q4_0_b{batch}", batch)
+    sw = Sweep(f"moe30b_block_{fmt}_b{batch}", batch)
     dev = "cuda:0"
+    fcode = qmv.FORMATS[fmt]
     E, T, H, F = wl.MOE_EXPERTS, wl.MOE_TOPK, wl.MOE_HIDDEN, wl.MOE_FFN
-    if "moe" not in _ENC_CACHE:
-        gate = wl.quant_weights("q4_0", "moe/gate", E * F, H).reshape(E, -1)
-        up = wl.quant_weights("q4_0", "moe/up", E * F, H).reshape(E, -1)
-        _ENC_CACHE["moe"] = (np.concatenate([gate, up], axis=1).reshape(-1),
-                             wl.quant_weights("q4_0", "moe/down", E * H, F).reshape(-1))
-    gu = torch.from_numpy(_ENC_CACHE["moe"][0]).to(dev)
-    down = torch.from_numpy(_ENC_CACHE["moe"][1]).to(dev)
-    gu_stride = 2 * wl.block_bytes("q4_0", F, H)
-    dn_stride = wl.block_bytes("q4_0", H, F)
+    key = f"moe_{fmt}"
+    if key not in _ENC_CACHE:
+        gate = wl.quant_weights(fmt, "moe/gate", E * F, H).reshape(E, -1)
+        up = wl.quant_weights(fmt, "moe/up", E * F, H).reshape(E, -1)
+        _ENC_CACHE[key] = (np.concatenate([gate, up], axis=1).reshape(-1),
+                           wl.quant_weights(fmt, "moe/down", E * H, F).reshape(-1))
+    gu = torch.from_numpy(_ENC_CACHE[key][0]).to(dev)
+    down = torch.from_numpy(_ENC_CACHE[key][1]).to(dev)
+    gu_stride = 2 * wl.block_bytes(fmt, F, H)
+    dn_stride = wl.block_bytes(fmt, H, F)
     uniq = []
     for layer in range(wl.MOE_LAYERS):
         ids_np = wl.moe_ids(f"moe/ids/{layer}/{batch}", batch, T, E)
@@ -432,10 +434,10 @@ def build_moe_block(torch, qmv, wl, batch):
         out = torch.empty((batch, H), dtype=torch.float32, device=dev)
         sw.keep += [ids, w, Wgu, Wdn, x, h, out]
         sw.add("swiglu", qmv.lib().qmv_moe_swiglu,
-               (1, Wgu.data_ptr(), gu_stride, E, F, H, ids.data_ptr(), batch, T, x.data_ptr(), H, 0, h.data_ptr()),
+               (fcode, Wgu.data_ptr(), gu_stride, E, F, H, ids.data_ptr(), batch, T, x.data_ptr(), H, 0, h.data_ptr()),
                nu * gu_stride + 4 * batch * H + 4 * batch * T * F + 4 * batch * T)
         sw.add("combine", qmv.lib().qmv_moe_combine,
-               (1, Wdn.data_ptr(), dn_stride, E, H, F, ids.data_ptr(), w.data_ptr(), batch, T, h.data_ptr(), T * F, F,
+               (fcode, Wdn.data_ptr(), dn_stride, E, H, F, ids.data_ptr(), w.data_ptr(), batch, T, h.data_ptr(), T * F, F,
                 out.data_ptr()),
                nu * dn_stride + 4 * batch * T * F + 4 * batch * H + 8 * batch * T)
     sw.mean_unique = float(np.mean(uniq))
@@ -750,7 +752,7 @@ def main():
     ap.add_argument("--sweeps", default="all",
                     help="extra workloads: all, none, or a comma list of c1,q8_0,q4_0,q4_1,q4_k,q6_k,int8,moe, or of "
                          "FMT@B / FMT@Bf / FMT@1g (one 8B sweep of format FMT at batch B, f: row-fused layout, "
-                         "1g: batch 1 with one launch per dependency level), moe@B[:q4_k] / moeblock@B (one MoE "
+                         "1g: batch 1 with one launch per dependency level), moe@B[:q4_k] / moeblock@B[:q4_k] (one MoE "
                          "sweep at batch B)")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip every oracle timing")
     ap.add_argument("--no-headline", action="store_true",
@@ -829,13 +831,13 @@ def main():
     ksteps = max(5, min(args.steps, 20))
     for nm in names:
         if nm.startswith(("moe@", "moeblock@")):
-            # one MoE sweep: moe@B (Q4_0 experts, or moe@B:q4_k) / moeblock@B
+            # one MoE sweep: moe@B / moeblock@B (Q4_0 experts, or moe@B:q4_k / moeblock@B:q4_k)
             what, spec = nm.split("@")
             B, _, fmt = spec.partition(":")
             if what == "moe":
                 s = build_moe(torch, qmv, wl, int(B), fmt or "q4_0")
             else:
-                s = build_moe_block(torch, qmv, wl, int(B))
+                s = build_moe_block(torch, qmv, wl, int(B), fmt or "q4_0")
             record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph),
                    mean_distinct_experts=_r(s.mean_unique, 2))
             del s
@@ -909,13 +911,15 @@ def main():
                     record(s, r, o, mean_distinct_experts=_r(s.mean_unique, 2))
                     del s
                     torch.cuda.empty_cache()
-            # Q4_K experts (one grid row per token and slot), batch 1 and 8
+            # Q4_K experts (one grid row per token and slot), plain and the
+            # fused block, batch 1 and 8
             for B in (1, 8):
-                s = build_moe(torch, qmv, wl, B, "q4_k")
-                r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
-                record(s, r, mean_distinct_experts=_r(s.mean_unique, 2))
-                del s
-                torch.cuda.empty_cache()
+                for build in (build_moe, build_moe_block):
+                    s = build(torch, qmv, wl, B, "q4_k")
+                    r = time_sweep(torch, s, ksteps, args.warmup, not args.no_graph)
+                    record(s, r, mean_distinct_experts=_r(s.mean_unique, 2))
+                    del s
+                    torch.cuda.empty_cache()
 
     if head is None:
         return

@@ -116,8 +116,12 @@ def test_q4_k_argument_errors(qmv):
     assert L.qmv_moe_swiglu(qmv.Q4_K, A + 4, 2304, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EALIGN
     assert L.qmv_moe_swiglu(qmv.Q4_K, A, 2304, 2, 8, 256, A, 9, 1, A, 256, 256, A, None) == EINVAL
     assert L.qmv_moe_swiglu(qmv.Q4_K, A, 2304, 2, 8, 288, A, 1, 1, A, 288, 288, A, None) == EINVAL
-    assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
-    assert "Q4_K" in qmv.last_error()
+    # the fused combine: argument errors only (nothing launches here)
+    assert L.qmv_moe_combine(qmv.Q4_K, A, 1136, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert "expert_stride" in qmv.last_error()
+    assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, A + 2, 1, 1, A, 256, 256, A, None) == EALIGN
+    assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, None, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, A, 1, 17, A, 256, 256, A, None) == EINVAL
     assert L.qmv_chain(qmv.Q4_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED and "not supported" in qmv.last_error()
     assert L.qmv_chain_noalloc(qmv.Q4_K, A, 1, None) == EUNSUPPORTED
 

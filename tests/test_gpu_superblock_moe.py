@@ -226,3 +226,101 @@ def test_q4k_moe_swiglu_edges(env):
     with pytest.raises(qmv.QmvError):
         qmv.qmv_moe_swiglu("q6_k", W6, wl.block_bytes("q6_k", 16, 256), 2, 8, 256,
                            dev(torch, np.zeros((1, 1), dtype=np.int32)), dev(torch, np.zeros((1, 256), np.float32)))
+
+
+# ------------------------------------------------------------------ fused combine (Q4_K)
+def combine_bound(S, w):
+    """The combine's bound: the weighted matvec bounds plus the fp32
+    multiply-add chain over at most 16 slots."""
+    return (1e-4 + 16 * 2.0 ** -24) * S + 1e-6 * np.abs(w).sum(axis=1, keepdims=True) + 1e-30
+
+
+def combine(env, fmt, Wall, stride, N, K, ids, w, x, n_experts=E):
+    torch, qmv = env
+    out = qmv.qmv_moe_combine(fmt, dev(torch, Wall), stride, n_experts, N, K, dev(torch, ids), dev(torch, w),
+                              dev(torch, x))
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+@pytest.mark.parametrize("B", [1, 2, 8])
+def test_q4k_moe_combine_30b_shapes(env, B):
+    """Q4_K down experts 2048 x 768 (3 super-blocks per row), one input per
+    (token, slot), router weights summing to 1: against the oracle, and
+    against the weighted sum of qmv_moe's per-slot outputs."""
+    H, F = wl.MOE_HIDDEN, wl.MOE_FFN
+    Wall = experts("q4_k", "down", H, F)
+    stride = wl.block_bytes("q4_k", H, F)
+    ids = wl.moe_ids(f"t/sbmoe/cb/ids/{B}", B, T, E)
+    w = wl.router_weights(f"t/sbmoe/cb/w/{B}", B, T)
+    x = wl.activations(f"t/sbmoe/cb/x/{B}", B * T, F).reshape(B, T, F)
+    say(f"q4_k moe combine B={B}")
+    out = combine(env, "q4_k", Wall, stride, H, F, ids, w, x)
+    ref, S = oracle.moe_combine("q4_k", Wall, stride, E, H, F, ids, w, x_slots=x)
+    err = np.abs(out.astype(np.float64) - ref)
+    assert np.all(err <= combine_bound(S, w)), float((err / combine_bound(S, w)).max())
+    y = run(env, "q4_k", Wall, stride, H, F, ids, x).astype(np.float64)
+    mix = np.einsum("bs,bsn->bn", w.astype(np.float64), y)
+    assert np.all(np.abs(out - mix) <= T * 2.0 ** -24 * np.einsum("bs,bsn->bn", np.abs(w), np.abs(y)) + 1e-37)
+
+
+@pytest.mark.parametrize("case", ["one_hot_dup", "invalid", "chunked_slots", "token_inputs"])
+def test_q4k_moe_combine_edges(env, case):
+    """Six experts.  One-hot weights (out equals one slot's qmv_moe output
+    bitwise) with duplicated ids and a padded stride, an invalid id (the
+    token's row becomes NaN), top_k 16 on rows of 16384 columns (one slot
+    vector staged at a time), one input per token; Q6_K refuses the fused
+    form."""
+    torch, qmv = env
+    E6 = 6
+    if case == "one_hot_dup":
+        N, K, ids = 300, 1024, np.array([[2, 5, 2], [0, 0, 1]], dtype=np.int32)
+    elif case == "invalid":
+        N, K, ids = 96, 512, np.array([[1, 3], [7, 2], [4, 4]], dtype=np.int32)
+    elif case == "chunked_slots":
+        N, K, ids = 300, 16384, np.array([[i % E6 for i in range(16)]], dtype=np.int32)
+    else:
+        N, K, ids = 128, 2048, np.array([[5, 1, 0, 3], [2, 2, 4, 1]], dtype=np.int32)
+    B, Tk = ids.shape
+    per = wl.block_bytes("q4_k", N, K)
+    stride = per + (256 if case == "one_hot_dup" else 0)
+    Wm = wl.quant_weights("q4_k", f"t/sbmoe/cb/{case}", E6 * N, K).reshape(E6, per)
+    Wall = np.zeros((E6, stride), dtype=np.uint8)
+    Wall[:, :per] = Wm
+    Wall = Wall.reshape(-1)
+    w = wl.router_weights(f"t/sbmoe/cb/w/{case}", B, Tk)
+    say(f"q4_k moe combine edge {case}")
+    if case == "token_inputs":
+        x = wl.activations(f"t/sbmoe/cb/x/{case}", B, K)
+        out = combine(env, "q4_k", Wall, stride, N, K, ids, w, x, E6)
+        ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids, w, x_tokens=x)
+    else:
+        x = wl.activations(f"t/sbmoe/cb/x/{case}", B * Tk, K).reshape(B, Tk, K)
+        if case == "one_hot_dup":
+            w = np.zeros((B, Tk), dtype=np.float32)
+            w[0, 2] = 1.0
+            w[1, 1] = 1.0
+        out = combine(env, "q4_k", Wall, stride, N, K, ids, w, x, E6)
+        if case == "invalid":
+            valid = np.all((ids >= 0) & (ids < E6), axis=1)
+            assert np.all(np.isnan(out[~valid])) and not np.any(np.isnan(out[valid]))
+            ids_ok = np.where((ids >= 0) & (ids < E6), ids, 0).astype(np.int32)
+            ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids_ok, w, x_slots=x)
+            out, ref, S, w = out[valid], ref[valid], S[valid], w[valid]
+        elif case == "chunked_slots":
+            ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids, w, x_slots=x)
+        else:
+            ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids, w, x_slots=x)
+            y = qmv.qmv_moe("q4_k", dev(torch, Wall), stride, E6, N, K, dev(torch, ids), dev(torch, x))
+            torch.cuda.synchronize()
+            y = y.cpu().numpy()
+            assert np.array_equal(out[0].view(np.uint32), y[0, 2].view(np.uint32))
+            assert np.array_equal(out[1].view(np.uint32), y[1, 1].view(np.uint32))
+    err = np.abs(out.astype(np.float64) - ref)
+    assert np.all(err <= combine_bound(S, w)), (case, float((err / combine_bound(S, w)).max()))
+    if case == "token_inputs":
+        W6 = dev(torch, wl.quant_weights("q6_k", "t/sbmoe/cb6", 2 * 8, 256).reshape(-1))
+        with pytest.raises(qmv.QmvError):
+            qmv.qmv_moe_combine("q6_k", W6, wl.block_bytes("q6_k", 8, 256), 2, 8, 256,
+                                dev(torch, np.zeros((1, 1), dtype=np.int32)), dev(torch, np.ones((1, 1), np.float32)),
+                                dev(torch, np.zeros((1, 256), np.float32)))
