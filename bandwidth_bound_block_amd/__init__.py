@@ -461,9 +461,9 @@ def chain_stages(stages, fmt=None):
     arr = (ChainStage * len(stages))()
     for i, (W, n_rows, n_cols, x, y, wait) in enumerate(stages):
         _dev(W, "W", torch.uint8)
-        bb = BLOCK_BYTES.get(_fmt(fmt)) if fmt is not None else None   # unknown fmt: the library rejects it
-        if bb is not None:
-            need = n_rows * (n_cols // 32) * bb
+        rb = row_bytes(_fmt(fmt), n_cols) if fmt is not None else 0   # unknown fmt: the library rejects it
+        if rb:
+            need = n_rows * rb
             if W.numel() < need or not W.is_contiguous():
                 raise ValueError(f"stage {i}: W must be contiguous and hold {need} bytes")
         _dev(x, "x", torch.float32)
@@ -475,7 +475,9 @@ def chain_stages(stages, fmt=None):
 
 
 def qmv_chain(fmt, stages, workspace, stream=None):
-    """Runs batch-1 matvec stages in one persistent launch (see qmv.h).
+    """Runs batch-1 matvec stages in one call (see qmv.h): one persistent
+    launch for the 32-weight formats, stage groups as launches of their own
+    for Q4_K and Q6_K.
 
     stages: list of (W, n_rows, n_cols, x, y, wait) with GPU tensors, or a
     ctypes array from chain_stages().  workspace: uint8 GPU tensor of at

@@ -468,15 +468,27 @@ extern "C" int32_t qmv_chain(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t
     case QMV_Q8_0: return qmv::chain<qmv::Q8_0>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
     case QMV_Q4_0: return qmv::chain<qmv::Q4_0>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
     case QMV_Q4_1: return qmv::chain<qmv::Q4_1>(fmt, stages, n_stages, workspace, workspace_bytes, stream);
-    default: return qmv::fail(QMV_EUNSUPPORTED, "qmv_chain: format %d is not supported (Q8_0, Q4_0, Q4_1)", (int)fmt);
+    default: {
+        const qmv::FormatOps* ops = qmv::format_ops(fmt);
+        if (!ops || !ops->chain) return qmv::fail(QMV_EUNSUPPORTED, "qmv_chain: unknown format %d", (int)fmt);
+        if (!workspace) return qmv::fail(QMV_EINVAL, "qmv_chain: null pointer");
+        if (workspace_bytes < QMV_CHAIN_WORKSPACE_BYTES)
+            return qmv::fail(QMV_EINVAL, "qmv_chain: workspace of %zu bytes < %d", workspace_bytes,
+                             QMV_CHAIN_WORKSPACE_BYTES);
+        return ops->chain("qmv_chain", stages, n_stages, stream);
+    }
     }
 }
 
 extern "C" int32_t qmv_chain_noalloc(qmv_fmt fmt, const qmv_chain_stage* stages, int32_t n_stages, void* stream) {
     const char* name = "qmv_chain_noalloc";
     void* ws = nullptr;
-    if (fmt != QMV_Q8_0 && fmt != QMV_Q4_0 && fmt != QMV_Q4_1)
-        return qmv::fail(QMV_EUNSUPPORTED, "%s: format %d is not supported (Q8_0, Q4_0, Q4_1)", name, (int)fmt);
+    if (fmt != QMV_Q8_0 && fmt != QMV_Q4_0 && fmt != QMV_Q4_1) {
+        // no barrier words: the stages run as separate launches
+        const qmv::FormatOps* ops = qmv::format_ops(fmt);
+        if (!ops || !ops->chain) return qmv::fail(QMV_EUNSUPPORTED, "%s: unknown format %d", name, (int)fmt);
+        return ops->chain(name, stages, n_stages, stream);
+    }
     if (!stages) return qmv::fail(QMV_EINVAL, "%s: null pointer", name);
     if (n_stages < 1) return qmv::fail(QMV_EINVAL, "%s: n_stages must be >= 1", name);
     if (const int32_t rc = qmv::scratch_address(&ws)) return rc;

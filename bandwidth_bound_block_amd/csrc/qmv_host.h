@@ -69,12 +69,15 @@ struct FormatOps {
                            const float* wts, int32_t batch, int32_t top_k, const float* x, int64_t xs_tok,
                            int64_t xs_slot, float* out, void* stream);
     bool (*group_contig)(const RowSegs& segs, int nb, const float* x, hipStream_t st, bool force, int32_t* rc);
+    // qmv_chain for formats without the persistent chain kernels (nullptr
+    // for the others): stage groups and stages as separate launches
+    int32_t (*chain)(const char* name, const qmv_chain_stage* stages, int32_t n_stages, void* stream);
 };
 const FormatOps& ops_q8_0();
 const FormatOps& ops_q4_0();
 const FormatOps& ops_q4_1();
-const FormatOps& ops_q4_k();   // matvec and dequant only (qmv_q4k.hip)
-const FormatOps& ops_q6_k();   // matvec and dequant only (qmv_q6k.hip)
+const FormatOps& ops_q4_k();   // qmv_q4k.hip
+const FormatOps& ops_q6_k();   // qmv_q6k.hip
 // The table of fmt, or nullptr for an unknown format.
 const FormatOps* format_ops(qmv_fmt fmt);
 

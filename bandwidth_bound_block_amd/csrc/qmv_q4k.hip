@@ -424,6 +424,115 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(5))) vo
     }
 }
 
+// Up to kMaxSegs Q4_K matrices of one width that read one x (decode's q,
+// k and v) as one batch-1 launch over their concatenated rows: a lane's row
+// picks its matrix from the cumulative row counts; each row's sum is
+// q4k_kernel's (the same lanes per row and step arithmetic), so every
+// output is bitwise the batch-1 entry point's.
+template <int LPR, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(5))) void q4k_group_kernel(
+    const RowSegs segs, int nsb, const float* __restrict__ x, int xvec) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xs = lds;                          // [4 nsb][kSbXPad]
+    constexpr int RW = 64 / LPR;              // rows per tile
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = lane / LPR;
+    const int li = lane % LPR;
+    const int G = 4 * nsb;
+    const int T = (G + LPR - 1) / LPR;
+    const int64_t pitch = (int64_t)nsb * kQ4KBytes;
+    const int64_t rows = segs.end[segs.n - 1];
+    const int64_t ntiles = (rows + RW - 1) / RW;
+    const int64_t wstride = (int64_t)gridDim.x * NW;
+    // the matrix of a row (constant indices only: the table stays in registers)
+    auto locate = [&](int64_t row, const uint8_t*& Wm, float*& ym, int64_t& start) {
+        Wm = segs.W[0];
+        ym = segs.y[0];
+        start = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxSegs; ++i) {
+            const bool in = i < segs.n && row >= segs.end[i - 1];
+            Wm = in ? segs.W[i] : Wm;
+            ym = in ? segs.y[i] : ym;
+            start = in ? segs.end[i - 1] : start;
+        }
+    };
+    auto load_step = [&](int64_t tile, int t, Q4KGroup& r) {
+        const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
+        const int64_t row = min(tile * RW + seg, rows - 1);     // rows past the end: the last row
+        const uint8_t* Wm;
+        float* ym;
+        int64_t start;
+        locate(row, Wm, ym, start);
+        const uint8_t* sb = Wm + (row - start) * pitch + (int64_t)(g >> 2) * kQ4KBytes;
+        const int coff = 16 + 32 * (g & 3);
+        r.h = ld16_aligned(sb);
+        r.c0 = ld16_aligned(sb + coff);
+        r.c1 = ld16_aligned(sb + coff + 16);
+    };
+    const Q4KPairSel ps = q4k_pair_sel(li & 3);
+    float acc = 0.f;
+    auto compute_step = [&](int64_t tile, int t, const Q4KGroup& r) {
+        const int g = li + LPR * t;
+        const bool valid = g < G;
+        const int gc = valid ? g : G - 1;
+        const float s = q4k_group_sum(r, ps, xs + gc * kSbXPad);
+        acc = valid ? acc + s : acc;
+        if (t == T - 1) {
+            const float tot = segment_sum<LPR>(acc);
+            const int64_t row = tile * RW + seg;
+            if (li == 0 && row < rows) {
+                const uint8_t* Wm;
+                float* ym;
+                int64_t start;
+                locate(row, Wm, ym, start);
+                ym[row - start] = tot;
+            }
+            acc = 0.f;
+        }
+    };
+    auto advance = [&](int64_t& tile, int& t) {
+        if (++t == T) {
+            t = 0;
+            tile += wstride;
+        }
+    };
+    int64_t ltile = (int64_t)blockIdx.x * NW + wave;   // next step to load
+    int lt = 0;
+    int64_t ctile = ltile;                             // next step to compute
+    int ct = 0;
+    Q4KGroup buf[2];
+    auto load_next = [&](Q4KGroup& r) {
+        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
+        if (ltile < ntiles) advance(ltile, lt);
+    };
+    load_next(buf[0]);
+    {
+        const float* xcol[1] = {x};
+        // groups of 64 in order, each padded to kSbXPad floats; ends with a barrier
+        sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs, xvec != 0,
+                                      [](int e) { return (e >> 6) * kSbXPad + (e & 63); });
+    }
+    if (ctile < ntiles) {
+        while (ltile < ntiles) {
+            load_next(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[0]);
+            advance(ctile, ct);
+            if (ltile >= ntiles) {
+                buf[0] = buf[1];
+                break;
+            }
+            load_next(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[1]);
+            advance(ctile, ct);
+        }
+        compute_step(ctile, ct, buf[0]);
+    }
+}
+
 // One thread per 32-weight sub-block: out = fma(d sc, c, -dmin mn), the
 // same value the matvec uses for each weight.
 __global__ __launch_bounds__(kThreads) void q4k_dequant_kernel(const uint8_t* __restrict__ W, int64_t nsub,
@@ -456,6 +565,9 @@ struct Q4KFormat {
     static constexpr bool kCombine = true;     // MoE down with the weighted combine fused
     template <int LPR, int NW>
     static auto combine_kernel() { return q4k_combine_kernel<LPR, NW>; }
+    static constexpr bool kGroup = true;       // qmv_chain: shared-input stages as one launch
+    template <int LPR, int NW>
+    static auto group_kernel() { return q4k_group_kernel<LPR, NW>; }
     static constexpr int kDequantWeights = 32;
     static constexpr int kBytes = kQ4KBytes;
     template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>

@@ -257,6 +257,7 @@ struct Q6KFormat {
     static constexpr bool kMfma = true;        // batch 2..8: q6k_mma_kernel
     static constexpr bool kSwiglu = false;
     static constexpr bool kCombine = false;
+    static constexpr bool kGroup = false;
     static constexpr int kDequantWeights = 16;
     static constexpr int kBytes = kQ6KBytes;
     template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>

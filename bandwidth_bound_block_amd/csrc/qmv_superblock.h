@@ -441,12 +441,100 @@ int32_t sb_combine(const void* Wx, int64_t estride, int32_t E, int64_t N, int64_
         }
     }
 }
-// The chain-group slot of a super-block format's table.
+// The chain-group slot of a super-block format's table (qmv_chain of these
+// formats groups through sb_chain below).
 inline bool sb_no_group(const RowSegs&, int, const float*, hipStream_t, bool, int32_t*) { return false; }
+
+// Stages sharing one x as one launch over their concatenated rows
+// (formats with a group kernel).
+template <class Fmt, int LPR>
+int32_t sb_group_launch(const RowSegs& segs, int nsb, const float* x, hipStream_t st) {
+    constexpr int NW = 8;
+    constexpr int RW = 64 / LPR;
+    auto kern = Fmt::template group_kernel<LPR, NW>();
+    const size_t lds = (size_t)4 * nsb * kSbXPad * sizeof(float);
+    size_t dyn_max = 0;
+    if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, "qmv_chain", &dyn_max)) return e;
+    if (lds > dyn_max) return fail(QMV_EINVAL, "qmv_chain: %zu bytes of staged activations exceed the LDS", lds);
+    const int64_t rows = segs.end[segs.n - 1];
+    const int64_t tiles = (rows + NW * RW - 1) / (NW * RW);
+    const int per_cu = std::max(1, resident_wgs(reinterpret_cast<const void*>(kern), 64 * NW, lds));
+    const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(tiles, (int64_t)device_cu_count() * per_cu));
+    const int xvec = aligned(x, 16) ? 1 : 0;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(64 * NW), lds, st, segs, nsb, x, xvec);
+    return check_launch("qmv_chain");
+}
+
+// qmv_chain for a super-block format: stages in order, each run of up to
+// kMaxSegs stages that read one x with one width and do not wait as one
+// launch over their concatenated rows (formats with a group kernel), every
+// other stage as the batch-1 entry point's launch.  Stream order stands in
+// for the stage barriers, so no workspace is used; each output is bitwise
+// the batch-1 entry point's.
+template <class Fmt>
+int32_t sb_chain(const char* name, const qmv_chain_stage* stages, int32_t n_stages, void* stream) {
+    if (!stages) return fail(QMV_EINVAL, "%s: null pointer", name);
+    if (n_stages < 1) return fail(QMV_EINVAL, "%s: n_stages must be >= 1", name);
+    for (int s = 0; s < n_stages; ++s) {
+        const qmv_chain_stage& q = stages[s];
+        if (!q.W || !q.x || !q.y) return fail(QMV_EINVAL, "%s: stage %d: null pointer", name, s);
+        if (q.n_rows < 1 || q.n_rows > (1 << 30))
+            return fail(QMV_EINVAL, "%s: stage %d: n_rows must be in 1..2^30", name, s);
+        if (q.n_cols < kSbWeights || q.n_cols % kSbWeights || 4 * (q.n_cols / kSbWeights) * kSbXPad * 4 > kLdsMax)
+            return fail(QMV_EINVAL, "%s: stage %d: n_cols must be a multiple of 256 in 256..38400 for %s", name, s,
+                        Fmt::kLabel);
+        if (!aligned(q.W, Fmt::kWAlign))
+            return fail(QMV_EALIGN, "%s: stage %d: W must be %d-byte aligned for %s", name, s, Fmt::kWAlign,
+                        Fmt::kLabel);
+        if (!aligned(q.x, 4) || !aligned(q.y, 4))
+            return fail(QMV_EALIGN, "%s: stage %d: x and y must be 4-byte aligned", name, s);
+    }
+    hipStream_t st = as_stream(stream);
+    for (int i = 0; i < n_stages;) {
+        const qmv_chain_stage& q = stages[i];
+        const int nsb = (int)(q.n_cols / kSbWeights);
+        int j = i + 1;
+        while (j < n_stages && j - i < kMaxSegs && !stages[j].wait && stages[j].x == q.x &&
+               stages[j].n_cols == q.n_cols)
+            ++j;
+        int32_t rc = QMV_OK;
+        if constexpr (Fmt::kGroup) {
+            if (j - i > 1) {
+                RowSegs segs = {};
+                segs.n = j - i;
+                int64_t rows = 0;
+                for (int k = i; k < j; ++k) {
+                    segs.W[k - i] = static_cast<const uint8_t*>(stages[k].W);
+                    segs.y[k - i] = stages[k].y;
+                    rows += stages[k].n_rows;
+                    segs.end[k - i] = rows;
+                }
+                switch (sb_pick_lpr(4 * nsb)) {
+                case 64: rc = sb_group_launch<Fmt, 64>(segs, nsb, q.x, st); break;
+                case 32: rc = sb_group_launch<Fmt, 32>(segs, nsb, q.x, st); break;
+                case 16: rc = sb_group_launch<Fmt, 16>(segs, nsb, q.x, st); break;
+                default: rc = sb_group_launch<Fmt, 8>(segs, nsb, q.x, st); break;
+                }
+                if (rc != QMV_OK) return rc;
+                i = j;
+                continue;
+            }
+        }
+        for (int k = i; k < j; ++k) {
+            const qmv_chain_stage& r = stages[k];
+            rc = sb_launch_lpr<Fmt, 1, float>(static_cast<const uint8_t*>(r.W), r.n_rows, nsb, r.x, r.n_cols, r.y,
+                                              r.n_rows, st);
+            if (rc != QMV_OK) return rc;
+        }
+        i = j;
+    }
+    return ok();
+}
 
 template <class Fmt>
 const FormatOps& sb_format_ops() {
-    static const FormatOps ops = {sb_matvec<Fmt>, sb_dequant<Fmt>, sb_moe<Fmt>, sb_combine<Fmt>, sb_no_group};
+    static const FormatOps ops = {sb_matvec<Fmt>, sb_dequant<Fmt>, sb_moe<Fmt>, sb_combine<Fmt>, sb_no_group,
+                                  sb_chain<Fmt>};
     return ops;
 }
 

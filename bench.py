@@ -58,20 +58,20 @@ TRAFFIC_RECORDS = {
     "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>": {
         "key": "kernel_c_q8_0",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "6b37feb96e956bbc9921650c451db57fc05200d9393cf6b559336c6381b5f14c", "bytes_per_launch": 83478763, "ratio": 1.0025,
+        "sha256": "753ac41d427d22e3ceab8faacdccddbd371d9e4d6550d301a66ca2f12e5a7e5d", "bytes_per_launch": 83478763, "ratio": 1.0025,
         "workload": "8B Q8_0 decode step, batch 1"},
     "qmv_kernel<Q8_0, 1, 64, 1, 2, 8, 2, false, float, false>": {
         "key": "kernel_q8_0_o",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "6b37feb96e956bbc9921650c451db57fc05200d9393cf6b559336c6381b5f14c", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
+        "sha256": "753ac41d427d22e3ceab8faacdccddbd371d9e4d6550d301a66ca2f12e5a7e5d", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
     "qmv_kernel_c<Q8_0, 4, 16, 2, float, 1>": {
         "key": "kernel_c16_q8_0_down",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "6b37feb96e956bbc9921650c451db57fc05200d9393cf6b559336c6381b5f14c", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
+        "sha256": "753ac41d427d22e3ceab8faacdccddbd371d9e4d6550d301a66ca2f12e5a7e5d", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
     "i8_stream_kernel": {
         "key": "i8_stream",
         "sources": ["bandwidth_bound_block_amd/csrc/qmv_int8.hip", "bandwidth_bound_block_amd/csrc/qmv_host.h"],
-        "sha256": "76bd0f16be16a608b8ba7f81f445083e00e986515c81f1401419b1e8673cbb30", "ratio": 1.0380,
+        "sha256": "e1adefc3766601d9ed03a988e2885af680da6d56e109ad0b2654c87a37676d21", "ratio": 1.0380,
         "workload": "Qwen3-0.6B int8 step (28 layers + lm_head), batch 1, per-matrix launches"},
 }
 
@@ -888,6 +888,12 @@ def main():
                 torch.cuda.empty_cache()
         elif nm in ("q4_k", "q6_k"):
             o = oracle_for(nm, lambda: dense_oracle(nm))
+            if nm == "q4_k":
+                # one launch per dependency level (qmv_chain groups q, k, v and gate, up)
+                s = build_llama_grouped(torch, qmv, wl, nm)
+                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+                del s
+                torch.cuda.empty_cache()
             for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
                 s = build_llama(torch, qmv, wl, nm, B, fused=fused)
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph), o if B == 1 else None)

@@ -142,7 +142,7 @@ int32_t qmv_q4_1(const void* W, int64_t n_rows, int64_t n_cols,
  * every path; QMV_PATH_MFMA needs batch 2..8, x aligned to 4 elements and
  * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do the MoE entry
  * points (qmv_moe, qmv_moe_xt, qmv_moe_swiglu, qmv_moe_swiglu_xt,
- * qmv_moe_combine); qmv_chain does not (QMV_EUNSUPPORTED).
+ * qmv_moe_combine) and qmv_chain / qmv_chain_noalloc.
  */
 int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
@@ -170,9 +170,9 @@ int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
  * x or y not 4-byte aligned), QMV_EHIP.
  * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q6_K (matvec on
  * every path; QMV_PATH_MFMA needs batch 2..8, x aligned to 4 elements and
- * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do qmv_moe and
- * qmv_moe_xt; qmv_moe_swiglu, qmv_moe_combine and qmv_chain do not
- * (QMV_EUNSUPPORTED).
+ * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do qmv_moe,
+ * qmv_moe_xt, qmv_chain and qmv_chain_noalloc; qmv_moe_swiglu and
+ * qmv_moe_combine do not (QMV_EUNSUPPORTED).
  */
 int32_t qmv_q6_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
@@ -403,6 +403,13 @@ int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_strid
  *     entry points, which accumulate across windows before reducing);
  *   - otherwise one persistent launch of per-stage cursors, each output
  *     bitwise the batch-1 entry point's when n_cols >= 2048.
+ *   QMV_Q4_K and QMV_Q6_K stages (n_cols a multiple of 256 up to 38400, W
+ *   aligned as for qmv_q4_k / qmv_q6_k) run as launches of their own in
+ *   stage order, the stream order standing in for the barriers (the
+ *   workspace is checked but not used): for Q4_K each run of up to 4 stages
+ *   that read one x with one n_cols and do not wait is one launch over
+ *   their concatenated rows; every other stage is the batch-1 entry
+ *   point's launch.  Each output is bitwise the batch-1 entry point's.
  *   stages        host array of n_stages entries (copied into the launch).
  *   n_rows        1..2^30;  n_cols a multiple of 32 in 32..35424.
  *   W, x, y       device pointers, 4-byte aligned, as for qmv_q8_0.

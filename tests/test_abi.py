@@ -122,8 +122,21 @@ def test_q4_k_argument_errors(qmv):
     assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, A + 2, 1, 1, A, 256, 256, A, None) == EALIGN
     assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, None, 1, 1, A, 256, 256, A, None) == EINVAL
     assert L.qmv_moe_combine(qmv.Q4_K, A, 1152, 2, 8, 256, A, A, 1, 17, A, 256, 256, A, None) == EINVAL
-    assert L.qmv_chain(qmv.Q4_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED and "not supported" in qmv.last_error()
-    assert L.qmv_chain_noalloc(qmv.Q4_K, A, 1, None) == EUNSUPPORTED
+    # chains: stage checks before any launch (stages live in host memory)
+    for fmt, wal in ((qmv.Q4_K, 16), (qmv.Q6_K, 4)):
+        arr = (qmv.ChainStage * 2)()
+        arr[0] = qmv.ChainStage(A, A, A, 8, 256, 0, 0)
+        arr[1] = qmv.ChainStage(A, A, A, 8, 288, 0, 0)
+        ap = ctypes.cast(arr, ctypes.c_void_p)
+        assert L.qmv_chain(fmt, ap, 2, A, 1 << 20, None) == EINVAL and "multiple of 256" in qmv.last_error()
+        assert L.qmv_chain_noalloc(fmt, ap, 2, None) == EINVAL
+        arr[1] = qmv.ChainStage(A + wal // 2, A, A, 8, 256, 0, 0)
+        assert L.qmv_chain(fmt, ap, 2, A, 1 << 20, None) == EALIGN
+        arr[1] = qmv.ChainStage(A, A, A, 0, 256, 0, 0)
+        assert L.qmv_chain_noalloc(fmt, ap, 2, None) == EINVAL and "n_rows" in qmv.last_error()
+        assert L.qmv_chain(fmt, ap, 0, A, 1 << 20, None) == EINVAL
+        assert L.qmv_chain(fmt, ap, 2, A, 1024, None) == EINVAL and "workspace" in qmv.last_error()
+        assert L.qmv_chain_noalloc(fmt, None, 1, None) == EINVAL
 
 
 def test_q6_k_argument_errors(qmv):
@@ -158,8 +171,6 @@ def test_q6_k_argument_errors(qmv):
     assert L.qmv_moe_swiglu(qmv.Q6_K, A, 3360, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert L.qmv_moe_combine(qmv.Q6_K, A, 1680, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
     assert "Q6_K" in qmv.last_error()
-    assert L.qmv_chain(qmv.Q6_K, A, 1, A, 1 << 20, None) == EUNSUPPORTED
-    assert L.qmv_chain_noalloc(qmv.Q6_K, A, 1, None) == EUNSUPPORTED
     assert L.qmv_dequant(5, A, 8, 256, A, None) == EUNSUPPORTED
 
 
