@@ -229,6 +229,140 @@ __global__ __launch_bounds__(64 * NW) void q6k_kernel(const uint8_t* __restrict_
     }
 }
 
+// One lane group's sum (64 weights) for one column, in q6k_kernel's order
+// at batch 1 (quarters 0..3, each 16-weight sum scaled by d sc / 4 into a
+// running fma): bitwise that kernel's step sum.
+__device__ __forceinline__ float q6k_group_sum(const Q6KRaw& r, int gc, const float* xg) {
+    const bool h = (gc & 2) != 0;
+    const int lh = gc & 1;
+    uint32_t A[4], Bq[4], C[4], S[4];
+    realign(r.a, r.a4, r.sh, A);
+    realign(r.b, r.b4, r.sh, Bq);
+    realign(r.c, r.c4, r.sh, C);
+    realign(r.t, r.u, r.sh, S);
+    const float d4 = half_bits_to_float(r.dh) * 0.25f;
+    const uint32_t s01 = h ? S[2] : S[0], s23 = h ? S[3] : S[1];
+    uint32_t hf[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) hf[k] = C[k] ^ 0xaaaaaaaau;
+    float st = 0.f;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const float scale = d4 * (float)(int8_t)((q < 2 ? s01 : s23) >> (8 * lh + 16 * (q & 1)));
+        float sq = 0.f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint32_t v = q6k_bytes((q & 1) ? Bq[k] : A[k], hf[k], q);
+            const float4 xv = *reinterpret_cast<const float4*>(xg + 16 * q + 4 * k);
+            sq = __builtin_fmaf(sbyte(v, 0), xv.x, sq);
+            sq = __builtin_fmaf(sbyte(v, 1), xv.y, sq);
+            sq = __builtin_fmaf(sbyte(v, 2), xv.z, sq);
+            sq = __builtin_fmaf(sbyte(v, 3), xv.w, sq);
+        }
+        st = __builtin_fmaf(scale, sq, st);
+    }
+    return st;
+}
+
+// Up to kMaxSegs Q6_K matrices of one width that read one x, as one batch-1
+// launch over their concatenated rows (as q4k_group_kernel): each output is
+// bitwise the batch-1 entry point's.
+template <int LPR, int NW>
+__global__ __launch_bounds__(64 * NW) void q6k_group_kernel(const RowSegs segs, int nsb, const float* __restrict__ x,
+                                                             int xvec) {
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xs = lds;                          // [4 nsb][kSbXPad], in q6k_slot order
+    constexpr int RW = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = lane / LPR;
+    const int li = lane % LPR;
+    const int G = 4 * nsb;
+    const int T = (G + LPR - 1) / LPR;
+    const int64_t pitch = (int64_t)nsb * kQ6KBytes;
+    const int64_t rows = segs.end[segs.n - 1];
+    const int64_t ntiles = (rows + RW - 1) / RW;
+    const int64_t wstride = (int64_t)gridDim.x * NW;
+    auto locate = [&](int64_t row, const uint8_t*& Wm, float*& ym, int64_t& start) {
+        Wm = segs.W[0];
+        ym = segs.y[0];
+        start = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxSegs; ++i) {
+            const bool in = i < segs.n && row >= segs.end[i - 1];
+            Wm = in ? segs.W[i] : Wm;
+            ym = in ? segs.y[i] : ym;
+            start = in ? segs.end[i - 1] : start;
+        }
+    };
+    auto load_step = [&](int64_t tile, int t, Q6KRaw& r) {
+        const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
+        const int64_t row = min(tile * RW + seg, rows - 1);     // rows past the end: the last row
+        const uint8_t* Wm;
+        float* ym;
+        int64_t start;
+        locate(row, Wm, ym, start);
+        q6k_fetch(Wm + (row - start) * pitch + (int64_t)(g >> 2) * kQ6KBytes, g & 3, r);
+    };
+    float acc = 0.f;
+    auto compute_step = [&](int64_t tile, int t, const Q6KRaw& r) {
+        const int g = li + LPR * t;
+        const bool valid = g < G;
+        const int gc = valid ? g : G - 1;
+        const float s = q6k_group_sum(r, gc, xs + gc * kSbXPad);
+        acc = valid ? acc + s : acc;
+        if (t == T - 1) {
+            const float tot = segment_sum<LPR>(acc);
+            const int64_t row = tile * RW + seg;
+            if (li == 0 && row < rows) {
+                const uint8_t* Wm;
+                float* ym;
+                int64_t start;
+                locate(row, Wm, ym, start);
+                ym[row - start] = tot;
+            }
+            acc = 0.f;
+        }
+    };
+    auto advance = [&](int64_t& tile, int& t) {
+        if (++t == T) {
+            t = 0;
+            tile += wstride;
+        }
+    };
+    int64_t ltile = (int64_t)blockIdx.x * NW + wave;
+    int lt = 0;
+    int64_t ctile = ltile;
+    int ct = 0;
+    Q6KRaw buf[2];
+    auto load_next = [&](Q6KRaw& r) {
+        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
+        if (ltile < ntiles) advance(ltile, lt);
+    };
+    load_next(buf[0]);
+    {
+        const float* xcol[1] = {x};
+        sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs, xvec != 0, q6k_slot);   // ends with a barrier
+    }
+    if (ctile < ntiles) {
+        while (ltile < ntiles) {
+            load_next(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[0]);
+            advance(ctile, ct);
+            if (ltile >= ntiles) {
+                buf[0] = buf[1];
+                break;
+            }
+            load_next(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[1]);
+            advance(ctile, ct);
+        }
+        compute_step(ctile, ct, buf[0]);
+    }
+}
+
 // One thread per 16-weight sub-block: out = (d sc / 4) * 4 (c - 32), the
 // weight the matvec uses (exact).
 __global__ __launch_bounds__(kThreads) void q6k_dequant_kernel(const uint8_t* __restrict__ W, int64_t nsub,
@@ -257,7 +391,9 @@ struct Q6KFormat {
     static constexpr bool kMfma = true;        // batch 2..8: q6k_mma_kernel
     static constexpr bool kSwiglu = false;
     static constexpr bool kCombine = false;
-    static constexpr bool kGroup = false;
+    static constexpr bool kGroup = true;       // qmv_chain: shared-input stages as one launch
+    template <int LPR, int NW>
+    static auto group_kernel() { return q6k_group_kernel<LPR, NW>; }
     static constexpr int kDequantWeights = 16;
     static constexpr int kBytes = kQ6KBytes;
     template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>

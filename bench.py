@@ -888,12 +888,11 @@ def main():
                 torch.cuda.empty_cache()
         elif nm in ("q4_k", "q6_k"):
             o = oracle_for(nm, lambda: dense_oracle(nm))
-            if nm == "q4_k":
-                # one launch per dependency level (qmv_chain groups q, k, v and gate, up)
-                s = build_llama_grouped(torch, qmv, wl, nm)
-                record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
-                del s
-                torch.cuda.empty_cache()
+            # one launch per dependency level (qmv_chain groups q, k, v and gate, up)
+            s = build_llama_grouped(torch, qmv, wl, nm)
+            record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph))
+            del s
+            torch.cuda.empty_cache()
             for B, fused in ((1, False), (1, True), (2, False), (4, False), (8, False)):
                 s = build_llama(torch, qmv, wl, nm, B, fused=fused)
                 record(s, time_sweep(torch, s, ksteps, args.warmup, not args.no_graph), o if B == 1 else None)

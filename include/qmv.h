@@ -406,10 +406,10 @@ int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_strid
  *   QMV_Q4_K and QMV_Q6_K stages (n_cols a multiple of 256 up to 38400, W
  *   aligned as for qmv_q4_k / qmv_q6_k) run as launches of their own in
  *   stage order, the stream order standing in for the barriers (the
- *   workspace is checked but not used): for Q4_K each run of up to 4 stages
- *   that read one x with one n_cols and do not wait is one launch over
- *   their concatenated rows; every other stage is the batch-1 entry
- *   point's launch.  Each output is bitwise the batch-1 entry point's.
+ *   workspace is checked but not used): each run of up to 4 stages that
+ *   read one x with one n_cols and do not wait is one launch over their
+ *   concatenated rows; every other stage is the batch-1 entry point's
+ *   launch.  Each output is bitwise the batch-1 entry point's.
  *   stages        host array of n_stages entries (copied into the launch).
  *   n_rows        1..2^30;  n_cols a multiple of 32 in 32..35424.
  *   W, x, y       device pointers, 4-byte aligned, as for qmv_q8_0.

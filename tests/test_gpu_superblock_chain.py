@@ -1,7 +1,7 @@
 """qmv_chain and qmv_chain_noalloc with Q4_K and Q6_K stages through the C
 ABI on an MI355X.  These formats run a chain's stages as launches of their
-own (stream order in place of the stage barriers); Q4_K runs each run of
-up to 4 stages that read one x with one width as one launch over their
+own (stream order in place of the stage barriers), each run of up to 4
+stages that read one x with one width as one launch over their
 concatenated rows.  Every output is bitwise the batch-1 entry point's on
 the same stage, and within the bound of the oracle.
 """
