@@ -296,242 +296,24 @@ __device__ __forceinline__ float q4k_group_sum(const Q4KGroup& r, const Q4KPairS
     return s;
 }
 
-// MoE down projection with the router-weighted combine, token-major:
-// workgroup (bx, b) computes rows [r0, r1) of out[b] = sum_s w[b][s] *
-// DEQ(W_{e_s}) x_{b,s} over the top_k slots of token b.  The slots'
-// activation vectors are staged together (SC at a time when they do not all
-// fit the LDS).  The work is the units (slot, tile of RW rows); wave w takes
-// units w, w + NW, ... with a two-deep load pipeline across them, and each
-// unit's row sums (q4k_kernel's, with the same lanes per row: bitwise the
-// qmv_moe outputs) go to LDS.  Then one thread per row adds them in slot
-// order, fma(w_s, y_s, acc) from s = 0 up.  An expert routed from several
-// tokens is read once per token (no atomics, no workspace).
-template <int LPR, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(5))) void q4k_combine_kernel(const uint8_t* __restrict__ Wx, int64_t estride,
-                                                               int n_experts, int64_t N, int nsb,
-                                                               const int32_t* __restrict__ ids,
-                                                               const float* __restrict__ wts, int top_k,
-                                                               const float* __restrict__ x, int64_t xs_tok,
-                                                               int64_t xs_slot, float* __restrict__ out, int xvec,
-                                                               int SC, int rows_wg) {
-    __shared__ const uint8_t* s_base[kSbMaxSlots];
-    __shared__ float s_w[kSbMaxSlots];
-    __shared__ int s_bad;
-    extern __shared__ __attribute__((aligned(16))) float lds[];
-    constexpr int RW = 64 / LPR;              // rows per tile
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int seg = lane / LPR;
-    const int li = lane % LPR;
-    const int G = 4 * nsb;                    // 64-weight groups per row
-    const int T = (G + LPR - 1) / LPR;        // steps per row
-    const int64_t pitch = (int64_t)nsb * kQ4KBytes;
-    const int b = blockIdx.y;
-    const int64_t ntiles = (N + RW - 1) / RW;
-    const int per_wg = rows_wg / RW;
-    const int64_t tb = (int64_t)blockIdx.x * per_wg;
-    const int64_t te = min(ntiles, tb + per_wg);
-    if (tb >= te) return;                     // the whole workgroup: no barrier is skipped by part of it
-    const int wtiles = (int)(te - tb);
-    const int per_col = G * kSbXPad;          // floats of one staged slot vector
-    float* xs = lds;                          // [SC][G][kSbXPad]
-    float* ybuf = lds + SC * per_col;         // [top_k][rows_wg]: row sums per slot
-    const int64_t r0 = tb * RW;
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-    if (tid < top_k) {
-        const int e = ids[b * top_k + tid];
-        const bool eb = e < 0 || e >= n_experts;
-        if (eb) s_bad = 1;
-        s_base[tid] = Wx + (int64_t)(eb ? 0 : e) * estride;
-        s_w[tid] = wts[b * top_k + tid];
-    }
-    __syncthreads();                          // s_base, s_w, s_bad
-    const Q4KPairSel ps = q4k_pair_sel(li & 3);
-    for (int s0 = 0; s0 < top_k; s0 += SC) {
-        const int sc = min(SC, top_k - s0);
-        const int units = sc * wtiles;
-        const int my_units = wave < units ? (units - wave + NW - 1) / NW : 0;
-        const int nsteps = my_units * T;
-        // the chunk's slot vectors (every wave is done with the previous
-        // chunk's: its units all ended before this barrier)
-        __syncthreads();
-        for (int k = 0; k < sc; ++k) {
-            const float* xcol[1] = {x + (int64_t)b * xs_tok + (int64_t)(s0 + k) * xs_slot};
-            // groups of 64 in order, each padded to kSbXPad floats; ends with a barrier
-            sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs + k * per_col, xvec != 0,
-                                          [](int e) { return (e >> 6) * kSbXPad + (e & 63); });
-        }
-        if (nsteps == 0) continue;
-        // step n of this wave: unit q = wave + NW (n / T), group step t = n % T
-        auto load = [&](int n, Q4KGroup& r) {
-            const int q = wave + NW * (n / T);
-            const int t = n % T;
-            const int slot = q / wtiles;
-            const int64_t tile = tb + (q - slot * wtiles);
-            const int g = min(li + LPR * t, G - 1);             // clamp: stays in bounds
-            const int64_t rt = tile * RW;                        // tile < ntiles: rt < N
-            const int64_t rem = N - 1 - rt;
-            const int lr = min(seg, rem < RW - 1 ? (int)rem : RW - 1);   // rows past the end: the last row
-            const uint8_t* base = s_base[s0 + slot] + rt * pitch;
-            const uint32_t off = __umul24((uint32_t)lr, (uint32_t)pitch) + (uint32_t)(g >> 2) * kQ4KBytes;
-            const uint32_t coff = off + 16 + 32 * (g & 3);
-            r.h = ld16_aligned(base + off);
-            r.c0 = ld16_aligned(base + coff);
-            r.c1 = ld16_aligned(base + coff + 16);
-        };
-        float acc = 0.f;
-        auto compute = [&](int n, const Q4KGroup& r) {
-            const int q = wave + NW * (n / T);
-            const int t = n % T;
-            const int slot = q / wtiles;
-            const int64_t tile = tb + (q - slot * wtiles);
-            const int g = li + LPR * t;
-            const bool valid = g < G;
-            const int gc = valid ? g : G - 1;
-            const float s = q4k_group_sum(r, ps, xs + slot * per_col + gc * kSbXPad);
-            acc = valid ? acc + s : acc;
-            if (t == T - 1) {
-                const float tot = segment_sum<LPR>(acc);
-                const int64_t row = tile * RW + seg;
-                if (li == 0 && row < N) ybuf[(s0 + slot) * rows_wg + (row - r0)] = tot;
-                acc = 0.f;
-            }
-        };
-        // two register buffers used in turn (nsteps is wave-uniform)
-        Q4KGroup buf0, buf1;
-        load(0, buf0);
-        for (int n = 0;;) {
-            if (n + 1 < nsteps) load(n + 1, buf1);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(n, buf0);
-            if (++n == nsteps) break;
-            if (n + 1 < nsteps) load(n + 1, buf0);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(n, buf1);
-            if (++n == nsteps) break;
-        }
-    }
-    __syncthreads();
-    const float qnan = __builtin_nanf("");
-    const int64_t r1 = min(te * RW, N);
-    for (int64_t row = r0 + tid; row < r1; row += 64 * NW) {
-        const float* yr = ybuf + (row - r0);
-        float v = s_w[0] * yr[0];
-        for (int s = 1; s < top_k; ++s) v = __builtin_fmaf(s_w[s], yr[s * rows_wg], v);
-        out[(int64_t)b * N + row] = s_bad ? qnan : v;
-    }
-}
-
-// Up to kMaxSegs Q4_K matrices of one width that read one x (decode's q,
-// k and v) as one batch-1 launch over their concatenated rows: a lane's row
-// picks its matrix from the cumulative row counts; each row's sum is
-// q4k_kernel's (the same lanes per row and step arithmetic), so every
-// output is bitwise the batch-1 entry point's.
-template <int LPR, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(5))) void q4k_group_kernel(
-    const RowSegs segs, int nsb, const float* __restrict__ x, int xvec) {
-    extern __shared__ __attribute__((aligned(16))) float lds[];
-    float* xs = lds;                          // [4 nsb][kSbXPad]
-    constexpr int RW = 64 / LPR;              // rows per tile
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int seg = lane / LPR;
-    const int li = lane % LPR;
-    const int G = 4 * nsb;
-    const int T = (G + LPR - 1) / LPR;
-    const int64_t pitch = (int64_t)nsb * kQ4KBytes;
-    const int64_t rows = segs.end[segs.n - 1];
-    const int64_t ntiles = (rows + RW - 1) / RW;
-    const int64_t wstride = (int64_t)gridDim.x * NW;
-    // the matrix of a row (constant indices only: the table stays in registers)
-    auto locate = [&](int64_t row, const uint8_t*& Wm, float*& ym, int64_t& start) {
-        Wm = segs.W[0];
-        ym = segs.y[0];
-        start = 0;
-#pragma unroll
-        for (int i = 1; i < kMaxSegs; ++i) {
-            const bool in = i < segs.n && row >= segs.end[i - 1];
-            Wm = in ? segs.W[i] : Wm;
-            ym = in ? segs.y[i] : ym;
-            start = in ? segs.end[i - 1] : start;
-        }
-    };
-    auto load_step = [&](int64_t tile, int t, Q4KGroup& r) {
-        const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
-        const int64_t row = min(tile * RW + seg, rows - 1);     // rows past the end: the last row
-        const uint8_t* Wm;
-        float* ym;
-        int64_t start;
-        locate(row, Wm, ym, start);
-        const uint8_t* sb = Wm + (row - start) * pitch + (int64_t)(g >> 2) * kQ4KBytes;
+// The Q4_K step for the kernels over a format's step (sb_group_kernel,
+// sb_combine_kernel): a lane's group of 64 weights and its batch-1 sum.
+struct Q4KOps {
+    using Raw = Q4KGroup;
+    static constexpr int kBytes = kQ4KBytes;
+    static constexpr int kWaves = 5;          // 71-89 VGPRs, no spills
+    __device__ static void fetch(const uint8_t* row, int g, Raw& r) {
+        const uint8_t* sb = row + (int64_t)(g >> 2) * kQ4KBytes;
         const int coff = 16 + 32 * (g & 3);
         r.h = ld16_aligned(sb);
         r.c0 = ld16_aligned(sb + coff);
         r.c1 = ld16_aligned(sb + coff + 16);
-    };
-    const Q4KPairSel ps = q4k_pair_sel(li & 3);
-    float acc = 0.f;
-    auto compute_step = [&](int64_t tile, int t, const Q4KGroup& r) {
-        const int g = li + LPR * t;
-        const bool valid = g < G;
-        const int gc = valid ? g : G - 1;
-        const float s = q4k_group_sum(r, ps, xs + gc * kSbXPad);
-        acc = valid ? acc + s : acc;
-        if (t == T - 1) {
-            const float tot = segment_sum<LPR>(acc);
-            const int64_t row = tile * RW + seg;
-            if (li == 0 && row < rows) {
-                const uint8_t* Wm;
-                float* ym;
-                int64_t start;
-                locate(row, Wm, ym, start);
-                ym[row - start] = tot;
-            }
-            acc = 0.f;
-        }
-    };
-    auto advance = [&](int64_t& tile, int& t) {
-        if (++t == T) {
-            t = 0;
-            tile += wstride;
-        }
-    };
-    int64_t ltile = (int64_t)blockIdx.x * NW + wave;   // next step to load
-    int lt = 0;
-    int64_t ctile = ltile;                             // next step to compute
-    int ct = 0;
-    Q4KGroup buf[2];
-    auto load_next = [&](Q4KGroup& r) {
-        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
-        if (ltile < ntiles) advance(ltile, lt);
-    };
-    load_next(buf[0]);
-    {
-        const float* xcol[1] = {x};
-        // groups of 64 in order, each padded to kSbXPad floats; ends with a barrier
-        sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs, xvec != 0,
-                                      [](int e) { return (e >> 6) * kSbXPad + (e & 63); });
     }
-    if (ctile < ntiles) {
-        while (ltile < ntiles) {
-            load_next(buf[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_step(ctile, ct, buf[0]);
-            advance(ctile, ct);
-            if (ltile >= ntiles) {
-                buf[0] = buf[1];
-                break;
-            }
-            load_next(buf[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_step(ctile, ct, buf[1]);
-            advance(ctile, ct);
-        }
-        compute_step(ctile, ct, buf[0]);
+    __device__ static float group_sum(const Raw& r, int li, int gc, const float* xs) {
+        return q4k_group_sum(r, q4k_pair_sel(li & 3), xs + gc * kSbXPad);
     }
-}
+    __device__ static int slot(int e) { return (e >> 6) * kSbXPad + (e & 63); }
+};
 
 // One thread per 32-weight sub-block: out = fma(d sc, c, -dmin mn), the
 // same value the matvec uses for each weight.
@@ -564,10 +346,12 @@ struct Q4KFormat {
     static constexpr bool kSwiglu = true;      // MoE gate||up with SiLU(gate) * up fused (routed kernel)
     static constexpr bool kCombine = true;     // MoE down with the weighted combine fused
     template <int LPR, int NW>
-    static auto combine_kernel() { return q4k_combine_kernel<LPR, NW>; }
+    static auto combine_kernel() { return sb_combine_kernel<Q4KOps, LPR, NW>; }
     static constexpr bool kGroup = true;       // qmv_chain: shared-input stages as one launch
     template <int LPR, int NW>
-    static auto group_kernel() { return q4k_group_kernel<LPR, NW>; }
+    static auto group_kernel() { return sb_group_kernel<Q4KOps, LPR, NW>; }
+    template <int LPR, int NW, class XT>
+    static auto swiglu_kernel() { return q4k_kernel<1, LPR, NW, XT, true, true>; }
     static constexpr int kDequantWeights = 32;
     static constexpr int kBytes = kQ4KBytes;
     template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>

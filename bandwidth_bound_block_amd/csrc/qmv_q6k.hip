@@ -264,104 +264,21 @@ __device__ __forceinline__ float q6k_group_sum(const Q6KRaw& r, int gc, const fl
     return st;
 }
 
-// Up to kMaxSegs Q6_K matrices of one width that read one x, as one batch-1
-// launch over their concatenated rows (as q4k_group_kernel): each output is
-// bitwise the batch-1 entry point's.
-template <int LPR, int NW>
-__global__ __launch_bounds__(64 * NW) void q6k_group_kernel(const RowSegs segs, int nsb, const float* __restrict__ x,
-                                                             int xvec) {
-    extern __shared__ __attribute__((aligned(16))) float lds[];
-    float* xs = lds;                          // [4 nsb][kSbXPad], in q6k_slot order
-    constexpr int RW = 64 / LPR;
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int seg = lane / LPR;
-    const int li = lane % LPR;
-    const int G = 4 * nsb;
-    const int T = (G + LPR - 1) / LPR;
-    const int64_t pitch = (int64_t)nsb * kQ6KBytes;
-    const int64_t rows = segs.end[segs.n - 1];
-    const int64_t ntiles = (rows + RW - 1) / RW;
-    const int64_t wstride = (int64_t)gridDim.x * NW;
-    auto locate = [&](int64_t row, const uint8_t*& Wm, float*& ym, int64_t& start) {
-        Wm = segs.W[0];
-        ym = segs.y[0];
-        start = 0;
-#pragma unroll
-        for (int i = 1; i < kMaxSegs; ++i) {
-            const bool in = i < segs.n && row >= segs.end[i - 1];
-            Wm = in ? segs.W[i] : Wm;
-            ym = in ? segs.y[i] : ym;
-            start = in ? segs.end[i - 1] : start;
-        }
-    };
-    auto load_step = [&](int64_t tile, int t, Q6KRaw& r) {
-        const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
-        const int64_t row = min(tile * RW + seg, rows - 1);     // rows past the end: the last row
-        const uint8_t* Wm;
-        float* ym;
-        int64_t start;
-        locate(row, Wm, ym, start);
-        q6k_fetch(Wm + (row - start) * pitch + (int64_t)(g >> 2) * kQ6KBytes, g & 3, r);
-    };
-    float acc = 0.f;
-    auto compute_step = [&](int64_t tile, int t, const Q6KRaw& r) {
-        const int g = li + LPR * t;
-        const bool valid = g < G;
-        const int gc = valid ? g : G - 1;
-        const float s = q6k_group_sum(r, gc, xs + gc * kSbXPad);
-        acc = valid ? acc + s : acc;
-        if (t == T - 1) {
-            const float tot = segment_sum<LPR>(acc);
-            const int64_t row = tile * RW + seg;
-            if (li == 0 && row < rows) {
-                const uint8_t* Wm;
-                float* ym;
-                int64_t start;
-                locate(row, Wm, ym, start);
-                ym[row - start] = tot;
-            }
-            acc = 0.f;
-        }
-    };
-    auto advance = [&](int64_t& tile, int& t) {
-        if (++t == T) {
-            t = 0;
-            tile += wstride;
-        }
-    };
-    int64_t ltile = (int64_t)blockIdx.x * NW + wave;
-    int lt = 0;
-    int64_t ctile = ltile;
-    int ct = 0;
-    Q6KRaw buf[2];
-    auto load_next = [&](Q6KRaw& r) {
-        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
-        if (ltile < ntiles) advance(ltile, lt);
-    };
-    load_next(buf[0]);
-    {
-        const float* xcol[1] = {x};
-        sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs, xvec != 0, q6k_slot);   // ends with a barrier
+// The Q6_K step for the kernels over a format's step (sb_group_kernel,
+// sb_combine_kernel, sb_swiglu_kernel): a lane's 64 weights and their
+// batch-1 sum.
+struct Q6KOps {
+    using Raw = Q6KRaw;
+    static constexpr int kBytes = kQ6KBytes;
+    static constexpr int kWaves = 1;          // the compiler's choice
+    __device__ static void fetch(const uint8_t* row, int g, Raw& r) {
+        q6k_fetch(row + (int64_t)(g >> 2) * kQ6KBytes, g & 3, r);
     }
-    if (ctile < ntiles) {
-        while (ltile < ntiles) {
-            load_next(buf[1]);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_step(ctile, ct, buf[0]);
-            advance(ctile, ct);
-            if (ltile >= ntiles) {
-                buf[0] = buf[1];
-                break;
-            }
-            load_next(buf[0]);
-            __builtin_amdgcn_sched_barrier(0);
-            compute_step(ctile, ct, buf[1]);
-            advance(ctile, ct);
-        }
-        compute_step(ctile, ct, buf[0]);
+    __device__ static float group_sum(const Raw& r, int, int gc, const float* xs) {
+        return q6k_group_sum(r, gc, xs + gc * kSbXPad);
     }
-}
+    __device__ static int slot(int e) { return q6k_slot(e); }
+};
 
 // One thread per 16-weight sub-block: out = (d sc / 4) * 4 (c - 32), the
 // weight the matvec uses (exact).
@@ -389,18 +306,19 @@ struct Q6KFormat {
     static constexpr const char* kEntry = "qmv_q6_k";
     static constexpr int kWAlign = 4;          // 4-byte-aligned loads, re-aligned in registers
     static constexpr bool kMfma = true;        // batch 2..8: q6k_mma_kernel
-    static constexpr bool kSwiglu = false;
-    static constexpr bool kCombine = false;
+    static constexpr bool kSwiglu = true;      // MoE gate||up with SiLU(gate) * up fused (sb_swiglu_kernel)
+    static constexpr bool kCombine = true;     // MoE down with the weighted combine fused
+    template <int LPR, int NW>
+    static auto combine_kernel() { return sb_combine_kernel<Q6KOps, LPR, NW>; }
     static constexpr bool kGroup = true;       // qmv_chain: shared-input stages as one launch
     template <int LPR, int NW>
-    static auto group_kernel() { return q6k_group_kernel<LPR, NW>; }
+    static auto group_kernel() { return sb_group_kernel<Q6KOps, LPR, NW>; }
+    template <int LPR, int NW, class XT>
+    static auto swiglu_kernel() { return sb_swiglu_kernel<Q6KOps, LPR, NW, XT>; }
     static constexpr int kDequantWeights = 16;
     static constexpr int kBytes = kQ6KBytes;
     template <int B, int LPR, int NW, class XT, bool ROUTE, bool SW = false>
-    static auto kernel() {
-        static_assert(!SW, "no fused SwiGLU form for Q6_K");
-        return q6k_kernel<B, LPR, NW, XT, ROUTE>;
-    }
+    static auto kernel() { return q6k_kernel<B, LPR, NW, XT, ROUTE>; }
     static auto dequant_kernel() { return q6k_dequant_kernel; }
 };
 

@@ -107,6 +107,330 @@ __device__ __forceinline__ void sb_stage_x(const XT* const (&xcol)[B], int K, fl
     __syncthreads();
 }
 
+// ---------------------------------------------------------------- kernels
+// over one format's batch-1 step.  Ops (per format) provides:
+//   Raw                      the stored bytes one lane loads for one step
+//   kBytes                   bytes per super-block
+//   fetch(row, g, r)         loads group g (64 weights) of the row at `row`
+//   group_sum(r, li, gc, xs) the group's sum for one column staged at xs:
+//                            bitwise the batch-1 kernel's step sum
+//   slot(e)                  the LDS float index of activation element e
+//   kWaves                   waves per SIMD the kernels are held to (1: the
+//                            compiler's choice)
+// A lane li of a segment of LPR lanes takes group li + LPR t of its row in
+// step t and a row's sum is the segment's, as in the batch-1 kernels, so
+// these kernels' row sums are bitwise theirs.
+
+// Up to kMaxSegs matrices of one width that read one x (decode's q, k and
+// v), as one batch-1 launch over their concatenated rows: a lane's row
+// picks its matrix from the cumulative row counts (constant indices only,
+// so the table stays in registers).
+template <class Ops, int LPR, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Ops::kWaves))) void sb_group_kernel(
+    const RowSegs segs, int nsb, const float* __restrict__ x, int xvec) {
+    using Raw = typename Ops::Raw;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xs = lds;                          // [4 nsb][kSbXPad]
+    constexpr int RW = 64 / LPR;              // rows per tile
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = lane / LPR;
+    const int li = lane % LPR;
+    const int G = 4 * nsb;
+    const int T = (G + LPR - 1) / LPR;
+    const int64_t pitch = (int64_t)nsb * Ops::kBytes;
+    const int64_t rows = segs.end[segs.n - 1];
+    const int64_t ntiles = (rows + RW - 1) / RW;
+    const int64_t wstride = (int64_t)gridDim.x * NW;
+    auto locate = [&](int64_t row, const uint8_t*& Wm, float*& ym, int64_t& start) {
+        Wm = segs.W[0];
+        ym = segs.y[0];
+        start = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxSegs; ++i) {
+            const bool in = i < segs.n && row >= segs.end[i - 1];
+            Wm = in ? segs.W[i] : Wm;
+            ym = in ? segs.y[i] : ym;
+            start = in ? segs.end[i - 1] : start;
+        }
+    };
+    auto load_step = [&](int64_t tile, int t, Raw& r) {
+        const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
+        const int64_t row = min(tile * RW + seg, rows - 1);     // rows past the end: the last row
+        const uint8_t* Wm;
+        float* ym;
+        int64_t start;
+        locate(row, Wm, ym, start);
+        Ops::fetch(Wm + (row - start) * pitch, g, r);
+    };
+    float acc = 0.f;
+    auto compute_step = [&](int64_t tile, int t, const Raw& r) {
+        const int g = li + LPR * t;
+        const bool valid = g < G;
+        const int gc = valid ? g : G - 1;
+        const float s = Ops::group_sum(r, li, gc, xs);
+        acc = valid ? acc + s : acc;
+        if (t == T - 1) {
+            const float tot = segment_sum<LPR>(acc);
+            const int64_t row = tile * RW + seg;
+            if (li == 0 && row < rows) {
+                const uint8_t* Wm;
+                float* ym;
+                int64_t start;
+                locate(row, Wm, ym, start);
+                ym[row - start] = tot;
+            }
+            acc = 0.f;
+        }
+    };
+    auto advance = [&](int64_t& tile, int& t) {
+        if (++t == T) {
+            t = 0;
+            tile += wstride;
+        }
+    };
+    int64_t ltile = (int64_t)blockIdx.x * NW + wave;   // next step to load
+    int lt = 0;
+    int64_t ctile = ltile;                             // next step to compute
+    int ct = 0;
+    Raw buf[2];
+    auto load_next = [&](Raw& r) {
+        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
+        if (ltile < ntiles) advance(ltile, lt);
+    };
+    load_next(buf[0]);
+    {
+        const float* xcol[1] = {x};
+        sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs, xvec != 0, Ops::slot);   // ends with a barrier
+    }
+    // two register buffers used in turn; once the load cursor is past the
+    // wave's last step, the step in hand is computed after the loop
+    if (ctile < ntiles) {
+        while (ltile < ntiles) {
+            load_next(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[0]);
+            advance(ctile, ct);
+            if (ltile >= ntiles) {
+                buf[0] = buf[1];
+                break;
+            }
+            load_next(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[1]);
+            advance(ctile, ct);
+        }
+        compute_step(ctile, ct, buf[0]);
+    }
+}
+
+// MoE down projection with the router-weighted combine, token-major:
+// workgroup (bx, b) computes rows [r0, r1) of out[b] = sum_s w[b][s] *
+// DEQ(W_{e_s}) x_{b,s} over the top_k slots of token b.  The slots'
+// activation vectors are staged together (SC at a time when they do not all
+// fit the LDS).  The work is the units (slot, tile of RW rows); wave w takes
+// units w, w + NW, ... with a two-deep load pipeline across them, and each
+// unit's row sums (bitwise the qmv_moe outputs) go to LDS.  Then one thread
+// per row adds them in slot order, fma(w_s, y_s, acc) from s = 0 up.  An
+// expert routed from several tokens is read once per token (no atomics, no
+// workspace).
+template <class Ops, int LPR, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(Ops::kWaves))) void sb_combine_kernel(
+    const uint8_t* __restrict__ Wx, int64_t estride, int n_experts, int64_t N, int nsb,
+    const int32_t* __restrict__ ids, const float* __restrict__ wts, int top_k, const float* __restrict__ x,
+    int64_t xs_tok, int64_t xs_slot, float* __restrict__ out, int xvec, int SC, int rows_wg) {
+    using Raw = typename Ops::Raw;
+    __shared__ const uint8_t* s_base[kSbMaxSlots];
+    __shared__ float s_w[kSbMaxSlots];
+    __shared__ int s_bad;
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    constexpr int RW = 64 / LPR;              // rows per tile
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int seg = lane / LPR;
+    const int li = lane % LPR;
+    const int G = 4 * nsb;                    // 64-weight groups per row
+    const int T = (G + LPR - 1) / LPR;        // steps per row
+    const int64_t pitch = (int64_t)nsb * Ops::kBytes;
+    const int b = blockIdx.y;
+    const int64_t ntiles = (N + RW - 1) / RW;
+    const int per_wg = rows_wg / RW;
+    const int64_t tb = (int64_t)blockIdx.x * per_wg;
+    const int64_t te = min(ntiles, tb + per_wg);
+    if (tb >= te) return;                     // the whole workgroup: no barrier is skipped by part of it
+    const int wtiles = (int)(te - tb);
+    const int per_col = G * kSbXPad;          // floats of one staged slot vector
+    float* xs = lds;                          // [SC][G][kSbXPad]
+    float* ybuf = lds + SC * per_col;         // [top_k][rows_wg]: row sums per slot
+    const int64_t r0 = tb * RW;
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    if (tid < top_k) {
+        const int e = ids[b * top_k + tid];
+        const bool eb = e < 0 || e >= n_experts;
+        if (eb) s_bad = 1;
+        s_base[tid] = Wx + (int64_t)(eb ? 0 : e) * estride;
+        s_w[tid] = wts[b * top_k + tid];
+    }
+    __syncthreads();                          // s_base, s_w, s_bad
+    for (int s0 = 0; s0 < top_k; s0 += SC) {
+        const int sc = min(SC, top_k - s0);
+        const int units = sc * wtiles;
+        const int my_units = wave < units ? (units - wave + NW - 1) / NW : 0;
+        const int nsteps = my_units * T;
+        // the chunk's slot vectors (every wave is done with the previous
+        // chunk's: its units all ended before this barrier)
+        __syncthreads();
+        for (int k = 0; k < sc; ++k) {
+            const float* xcol[1] = {x + (int64_t)b * xs_tok + (int64_t)(s0 + k) * xs_slot};
+            sb_stage_x<1, 64 * NW, float>(xcol, kSbWeights * nsb, xs + k * per_col, xvec != 0, Ops::slot);
+        }
+        if (nsteps == 0) continue;
+        // step n of this wave: unit q = wave + NW (n / T), group step t = n % T
+        auto load = [&](int n, Raw& r) {
+            const int q = wave + NW * (n / T);
+            const int t = n % T;
+            const int slot = q / wtiles;
+            const int64_t tile = tb + (q - slot * wtiles);
+            const int g = min(li + LPR * t, G - 1);             // clamp: stays in bounds
+            const int64_t rt = tile * RW;                        // tile < ntiles: rt < N
+            const int64_t rem = N - 1 - rt;
+            const int lr = min(seg, rem < RW - 1 ? (int)rem : RW - 1);   // rows past the end: the last row
+            Ops::fetch(s_base[s0 + slot] + (rt + lr) * pitch, g, r);
+        };
+        float acc = 0.f;
+        auto compute = [&](int n, const Raw& r) {
+            const int q = wave + NW * (n / T);
+            const int t = n % T;
+            const int slot = q / wtiles;
+            const int64_t tile = tb + (q - slot * wtiles);
+            const int g = li + LPR * t;
+            const bool valid = g < G;
+            const int gc = valid ? g : G - 1;
+            const float s = Ops::group_sum(r, li, gc, xs + slot * per_col);
+            acc = valid ? acc + s : acc;
+            if (t == T - 1) {
+                const float tot = segment_sum<LPR>(acc);
+                const int64_t row = tile * RW + seg;
+                if (li == 0 && row < N) ybuf[(s0 + slot) * rows_wg + (row - r0)] = tot;
+                acc = 0.f;
+            }
+        };
+        // two register buffers used in turn (nsteps is wave-uniform)
+        Raw buf0, buf1;
+        load(0, buf0);
+        for (int n = 0;;) {
+            if (n + 1 < nsteps) load(n + 1, buf1);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(n, buf0);
+            if (++n == nsteps) break;
+            if (n + 1 < nsteps) load(n + 1, buf0);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(n, buf1);
+            if (++n == nsteps) break;
+        }
+    }
+    __syncthreads();
+    const float qnan = __builtin_nanf("");
+    const int64_t r1 = min(te * RW, N);
+    for (int64_t row = r0 + tid; row < r1; row += 64 * NW) {
+        const float* yr = ybuf + (row - r0);
+        float v = s_w[0] * yr[0];
+        for (int s = 1; s < top_k; ++s) v = __builtin_fmaf(s_w[s], yr[s * rows_wg], v);
+        out[(int64_t)b * N + row] = s_bad ? qnan : v;
+    }
+}
+
+// MoE gate||up with SwiGLU fused, one grid row per (token, slot) pair (as
+// the batch-1 kernels' routed form): every expert holds 2N rows, gate rows
+// then up rows, and the segment of output row i streams gate row i and up
+// row N + i in the same lanes and steps, then writes SiLU(gate) * up.  Each
+// row's sum is the batch-1 kernel's.
+template <class Ops, int LPR, int NW, class XT>
+__global__ __launch_bounds__(64 * NW) void sb_swiglu_kernel(const uint8_t* __restrict__ W, int64_t N, int nsb,
+                                                             const XT* __restrict__ x, int64_t ldx,
+                                                             float* __restrict__ y, int64_t ldy, int xvec,
+                                                             const SbRoute route) {
+    using Raw = typename Ops::Raw;
+    const bool bad = sb_route(route, W, x, y, ldy);
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float* xs = lds;                          // [4 nsb][kSbXPad]
+    constexpr int RW = 64 / LPR;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int seg = lane / LPR;
+    const int li = lane % LPR;
+    const int G = 4 * nsb;
+    const int T = (G + LPR - 1) / LPR;
+    const int64_t pitch = (int64_t)nsb * Ops::kBytes;
+    const int64_t ntiles = (N + RW - 1) / RW;
+    const int64_t wstride = (int64_t)gridDim.x * NW;
+    struct Pair {
+        Raw g, u;
+    };
+    auto load_step = [&](int64_t tile, int t, Pair& r) {
+        const int g = min(li + LPR * t, G - 1);                 // clamp: stays in bounds
+        const int64_t row = min(tile * RW + seg, N - 1);        // rows past the end: the last row
+        Ops::fetch(W + row * pitch, g, r.g);
+        Ops::fetch(W + (N + row) * pitch, g, r.u);
+    };
+    float acc_g = 0.f, acc_u = 0.f;
+    auto compute_step = [&](int64_t tile, int t, const Pair& r) {
+        const int g = li + LPR * t;
+        const bool valid = g < G;
+        const int gc = valid ? g : G - 1;
+        const float sg = Ops::group_sum(r.g, li, gc, xs);
+        const float su = Ops::group_sum(r.u, li, gc, xs);
+        acc_g = valid ? acc_g + sg : acc_g;
+        acc_u = valid ? acc_u + su : acc_u;
+        if (t == T - 1) {
+            const float gs = segment_sum<LPR>(acc_g);
+            const float us = segment_sum<LPR>(acc_u);
+            const int64_t row = tile * RW + seg;
+            if (li == 0 && row < N) y[row] = bad ? __builtin_nanf("") : silu(gs) * us;
+            acc_g = acc_u = 0.f;
+        }
+    };
+    auto advance = [&](int64_t& tile, int& t) {
+        if (++t == T) {
+            t = 0;
+            tile += wstride;
+        }
+    };
+    int64_t ltile = (int64_t)blockIdx.x * NW + wave;
+    int lt = 0;
+    int64_t ctile = ltile;
+    int ct = 0;
+    Pair buf[2];
+    auto load_next = [&](Pair& r) {
+        load_step(min(ltile, ntiles - 1), ltile < ntiles ? lt : 0, r);
+        if (ltile < ntiles) advance(ltile, lt);
+    };
+    load_next(buf[0]);
+    {
+        const XT* xcol[1] = {x};
+        sb_stage_x<1, 64 * NW, XT>(xcol, kSbWeights * nsb, xs, xvec != 0, Ops::slot);   // ends with a barrier
+    }
+    if (ctile < ntiles) {
+        while (ltile < ntiles) {
+            load_next(buf[1]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[0]);
+            advance(ctile, ct);
+            if (ltile >= ntiles) {
+                buf[0] = buf[1];
+                break;
+            }
+            load_next(buf[0]);
+            __builtin_amdgcn_sched_barrier(0);
+            compute_step(ctile, ct, buf[1]);
+            advance(ctile, ct);
+        }
+        compute_step(ctile, ct, buf[0]);
+    }
+}
+
 // Lanes per row: the widest split of 64 / 32 / 16 / 8 lanes that leaves at
 // most 1/16 of a row's lane-steps idle (wide splits keep more waves busy on
 // matrices of few rows), else the split with the fewest idle: 64 for 4096
@@ -137,7 +461,10 @@ int32_t sb_launch(const uint8_t* W, int64_t N, int nsb, const XT* x, int64_t ldx
                   hipStream_t st, const SbRoute* route, int pairs) {
     if (route) {
         if constexpr (B == 1) {
-            auto kern = Fmt::template kernel<1, LPR, NW, XT, true, SW>();
+            auto kern = [] {
+                if constexpr (SW) return Fmt::template swiglu_kernel<LPR, NW, XT>();
+                else return Fmt::template kernel<1, LPR, NW, XT, true>();
+            }();
             const size_t lds = (size_t)4 * nsb * kSbXPad * sizeof(float);
             size_t dyn_max = 0;
             if (const int32_t e = lds_limit(reinterpret_cast<const void*>(kern), kLdsMax, Fmt::kEntry, &dyn_max))

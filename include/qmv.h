@@ -170,9 +170,9 @@ int32_t qmv_q4_k(const void* W, int64_t n_rows, int64_t n_cols,
  * x or y not 4-byte aligned), QMV_EHIP.
  * qmv_matvec_path / qmv_matvec_xt / qmv_dequant accept QMV_Q6_K (matvec on
  * every path; QMV_PATH_MFMA needs batch 2..8, x aligned to 4 elements and
- * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do qmv_moe,
- * qmv_moe_xt, qmv_chain and qmv_chain_noalloc; qmv_moe_swiglu and
- * qmv_moe_combine do not (QMV_EUNSUPPORTED).
+ * ldx a multiple of 4, else QMV_EUNSUPPORTED), and so do the MoE entry
+ * points (qmv_moe, qmv_moe_xt, qmv_moe_swiglu, qmv_moe_swiglu_xt,
+ * qmv_moe_combine) and qmv_chain / qmv_chain_noalloc.
  */
 int32_t qmv_q6_k(const void* W, int64_t n_rows, int64_t n_cols,
                  const float* x, int64_t ldx, int32_t batch,
@@ -330,9 +330,9 @@ int32_t qmv_moe_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_byt
  * Arguments as qmv_moe, with expert_stride_bytes >= the bytes of
  * 2*n_ff rows; h is fp32 [batch][top_k][n_ff], 4-byte aligned.  Invalid
  * ids give quiet NaN rows, as in qmv_moe.
- * QMV_Q4_K experts run it in the routed Q4_K kernel (gate row i and up row
- * n_ff + i of a pair in the same lanes and steps).
- * Errors: as qmv_moe; QMV_EUNSUPPORTED for QMV_Q6_K.
+ * QMV_Q4_K and QMV_Q6_K experts run it in their super-block kernels (gate
+ * row i and up row n_ff + i of a pair in the same lanes and steps).
+ * Errors: as qmv_moe.
  */
 int32_t qmv_moe_swiglu(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                        int32_t n_experts, int64_t n_ff, int64_t n_cols,
@@ -365,12 +365,12 @@ int32_t qmv_moe_swiglu_xt(qmv_fmt fmt, const void* W_experts, int64_t expert_str
  *            workgroup (n_cols <= 28608 at top_k = 8).
  * Other arguments as qmv_moe.  A token with an invalid id gets quiet NaN
  * for all its n_rows outputs.
- * QMV_Q4_K experts run it in their own kernel (the routed Q4_K kernel's
- * row sums; one staged slot vector, 1088 bytes per 256 columns, plus
- * top_k * 4100 bytes of row sums within the LDS: n_cols <= 30720 at
- * top_k = 8, 37376 at top_k = 1).
+ * QMV_Q4_K and QMV_Q6_K experts run it in a super-block kernel (the
+ * batch-1 kernels' row sums; one staged slot vector, 1088 bytes per 256
+ * columns, plus top_k * 4100 bytes of row sums within the LDS: n_cols <=
+ * 30720 at top_k = 8, 37376 at top_k = 1).
  * Errors: as qmv_moe; QMV_EINVAL for null weights, QMV_EALIGN for
- * misaligned weights, QMV_EUNSUPPORTED for QMV_Q6_K.
+ * misaligned weights.
  */
 int32_t qmv_moe_combine(qmv_fmt fmt, const void* W_experts, int64_t expert_stride_bytes,
                         int32_t n_experts, int64_t n_rows, int64_t n_cols,

@@ -168,9 +168,12 @@ def test_q6_k_argument_errors(qmv):
     assert L.qmv_moe(qmv.Q6_K, A + 2, 1680, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EALIGN
     assert L.qmv_moe(qmv.Q6_K, A, 1680, 2, 8, 256, A, 1, 17, A, 256, 256, A, None) == EINVAL
     assert "top_k" in qmv.last_error()
-    assert L.qmv_moe_swiglu(qmv.Q6_K, A, 3360, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
-    assert L.qmv_moe_combine(qmv.Q6_K, A, 1680, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EUNSUPPORTED
-    assert "Q6_K" in qmv.last_error()
+    # the fused forms: argument errors only (nothing launches here)
+    assert L.qmv_moe_swiglu(qmv.Q6_K, A, 3356, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert "expert_stride" in qmv.last_error() and "3360" in qmv.last_error()
+    assert L.qmv_moe_swiglu(qmv.Q6_K, A + 2, 3360, 2, 8, 256, A, 1, 1, A, 256, 256, A, None) == EALIGN
+    assert L.qmv_moe_combine(qmv.Q6_K, A, 1676, 2, 8, 256, A, A, 1, 1, A, 256, 256, A, None) == EINVAL
+    assert L.qmv_moe_combine(qmv.Q6_K, A, 1680, 2, 8, 256, A, A + 2, 1, 1, A, 256, 256, A, None) == EALIGN
     assert L.qmv_dequant(5, A, 8, 256, A, None) == EUNSUPPORTED
 
 

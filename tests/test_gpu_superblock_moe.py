@@ -1,6 +1,6 @@
-"""MoE experts stored as Q4_K or Q6_K super-blocks (qmv_moe, qmv_moe_xt)
-through the C ABI on an MI355X, against the oracle's per-(token, slot)
-loop.
+"""MoE experts stored as Q4_K or Q6_K super-blocks (qmv_moe, qmv_moe_xt,
+and the fused qmv_moe_swiglu / _xt and qmv_moe_combine) through the C ABI
+on an MI355X, against the oracle's per-(token, slot) loop.
 
 Each (token, slot) pair is one grid row of the super-block kernel.  Shapes
 are the 30B-A3B-style experts (gate||up 1536 x 2048 with one input per
@@ -142,7 +142,7 @@ def test_superblock_moe_x16_and_zero_heavy(env, fmt):
     assert_tol(y, yr, S, (fmt, "zero-heavy"))
 
 
-# ------------------------------------------------------------------ fused SwiGLU (Q4_K)
+# ------------------------------------------------------------------ fused SwiGLU
 def swiglu_bound(h, g, u, Sg, Su):
     """|h_gpu - h| for h = SiLU(g) u from fp32 g, u within the matvec bound
     (tg, tu): |SiLU'| <= 1.1, so |dh| <= 1.1 tg (|u| + tu) + (|SiLU(g)| +
@@ -152,26 +152,27 @@ def swiglu_bound(h, g, u, Sg, Su):
     return 1.1 * tg * (np.abs(u) + tu) + (sg + 1.1 * tg) * tu + 2.0 ** -20 * np.abs(h) + 1e-30
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("B", [1, 2, 8])
-def test_q4k_moe_swiglu_30b_shapes(env, B):
-    """Q4_K experts of gate||up 1536 x 2048 (gate rows, then up rows), top-8
+def test_superblock_moe_swiglu_30b_shapes(env, fmt, B):
+    """Super-block experts of gate||up 1536 x 2048 (gate rows, then up rows), top-8
     per token: h against the oracle within the propagated bound on sampled
     rows, and the gate and up sums those of qmv_moe on the same experts (h
     == SiLU(g) u up to the epilogue's rounding)."""
     torch, qmv = env
     H, F = wl.MOE_HIDDEN, wl.MOE_FFN
-    Wall = experts("q4_k", "gate_up", 2 * F, H)
-    stride = wl.block_bytes("q4_k", 2 * F, H)
+    Wall = experts(fmt, "gate_up", 2 * F, H)
+    stride = wl.block_bytes(fmt, 2 * F, H)
     ids = wl.moe_ids(f"t/sbmoe/sw/ids/{B}", B, T, E)
     x = wl.activations(f"t/sbmoe/sw/x/{B}", B, H)
-    say(f"q4_k moe swiglu B={B}")
+    say(f"{fmt} moe swiglu B={B}")
     Wd, idd, xd = dev(torch, Wall), dev(torch, ids), dev(torch, x)
-    h = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, H, idd, xd)
-    y = qmv.qmv_moe("q4_k", Wd, stride, E, 2 * F, H, idd, xd)
+    h = qmv.qmv_moe_swiglu(fmt, Wd, stride, E, F, H, idd, xd)
+    y = qmv.qmv_moe(fmt, Wd, stride, E, 2 * F, H, idd, xd)
     torch.cuda.synchronize()
     h, y = h.cpu().numpy(), y.cpu().numpy().astype(np.float64)
     rows = np.sort(np.random.default_rng(B).choice(F, size=96, replace=False))
-    hr, g, u, Sg, Su = oracle.moe_swiglu("q4_k", Wall, stride, E, F, H, ids, x, rows=rows)
+    hr, g, u, Sg, Su = oracle.moe_swiglu(fmt, Wall, stride, E, F, H, ids, x, rows=rows)
     err = np.abs(h[:, :, rows].astype(np.float64) - hr)
     bound = swiglu_bound(hr, g, u, Sg, Su)
     assert np.all(err <= bound), float((err / bound).max())
@@ -180,16 +181,16 @@ def test_q4k_moe_swiglu_30b_shapes(env, B):
     assert np.all(np.abs(h - href) <= 2.0 ** -21 * np.abs(href) + 1e-37)
 
 
-def test_q4k_moe_swiglu_edges(env):
+@pytest.mark.parametrize("fmt", FMTS)
+def test_superblock_moe_swiglu_edges(env, fmt):
     """Padded strides, duplicate and invalid ids (quiet NaN rows, the others
     within the bound), per-slot inputs, 16-bit activations (bitwise the fp32
-    call on the widened values), a ragged row count; Q6_K refuses the fused
-    form."""
+    call on the widened values), a ragged row count."""
     torch, qmv = env
     F, K = 300, 1024
-    per = wl.block_bytes("q4_k", 2 * F, K)
+    per = wl.block_bytes(fmt, 2 * F, K)
     stride = per + 512
-    Wm = wl.quant_weights("q4_k", "t/sbmoe/swedge", E * 2 * F, K).reshape(E, per)
+    Wm = wl.quant_weights(fmt, "t/sbmoe/swedge", E * 2 * F, K).reshape(E, per)
     Wall = np.zeros((E, stride), dtype=np.uint8)
     Wall[:, :per] = Wm
     Wall = Wall.reshape(-1)
@@ -198,37 +199,33 @@ def test_q4k_moe_swiglu_edges(env):
     B = ids.shape[0]
     x = wl.activations("t/sbmoe/swedge/x", B, K)
     Wd, idd = dev(torch, Wall), dev(torch, ids)
-    say("q4_k moe swiglu edges")
-    h = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, K, idd, dev(torch, x))
+    say(f"{fmt} moe swiglu edges")
+    h = qmv.qmv_moe_swiglu(fmt, Wd, stride, E, F, K, idd, dev(torch, x))
     torch.cuda.synchronize()
     h = h.cpu().numpy()
     valid = (ids >= 0) & (ids < E)
     assert np.all(np.isnan(h[~valid])) and not np.any(np.isnan(h[valid]))
-    hr, g, u, Sg, Su = oracle.moe_swiglu("q4_k", Wall, stride, E, F, K, np.where(valid, ids, 0).astype(np.int32), x)
+    hr, g, u, Sg, Su = oracle.moe_swiglu(fmt, Wall, stride, E, F, K, np.where(valid, ids, 0).astype(np.int32), x)
     err = np.abs(h[valid].astype(np.float64) - hr[valid])
     assert np.all(err <= swiglu_bound(hr[valid], g[valid], u[valid], Sg[valid], Su[valid]))
     for kind, tt in [("f16", torch.float16), ("bf16", torch.bfloat16)]:
         xh = dev(torch, x).to(tt)
-        h16 = qmv.qmv_moe_swiglu_xt("q4_k", Wd, stride, E, F, K, idd, xh)
-        h32 = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, K, idd, xh.float())
+        h16 = qmv.qmv_moe_swiglu_xt(fmt, Wd, stride, E, F, K, idd, xh)
+        h32 = qmv.qmv_moe_swiglu(fmt, Wd, stride, E, F, K, idd, xh.float())
         torch.cuda.synchronize()
         assert torch.equal(h16.view(torch.int32), h32.view(torch.int32)), kind
     # one input per token and slot
     xs = wl.activations("t/sbmoe/swedge/xs", B * T, K).reshape(B, T, K)
-    hs = qmv.qmv_moe_swiglu("q4_k", Wd, stride, E, F, K, idd, dev(torch, xs))
+    hs = qmv.qmv_moe_swiglu(fmt, Wd, stride, E, F, K, idd, dev(torch, xs))
     torch.cuda.synchronize()
     hs = hs.cpu().numpy()
-    hr, g, u, Sg, Su = oracle.moe_swiglu("q4_k", Wall, stride, E, F, K, np.where(valid, ids, 0).astype(np.int32),
+    hr, g, u, Sg, Su = oracle.moe_swiglu(fmt, Wall, stride, E, F, K, np.where(valid, ids, 0).astype(np.int32),
                                          None, x_slots=xs)
     err = np.abs(hs[valid].astype(np.float64) - hr[valid])
     assert np.all(err <= swiglu_bound(hr[valid], g[valid], u[valid], Sg[valid], Su[valid]))
-    W6 = dev(torch, wl.quant_weights("q6_k", "t/sbmoe/sw6", 2 * 2 * 8, 256).reshape(-1))
-    with pytest.raises(qmv.QmvError):
-        qmv.qmv_moe_swiglu("q6_k", W6, wl.block_bytes("q6_k", 16, 256), 2, 8, 256,
-                           dev(torch, np.zeros((1, 1), dtype=np.int32)), dev(torch, np.zeros((1, 256), np.float32)))
 
 
-# ------------------------------------------------------------------ fused combine (Q4_K)
+# ------------------------------------------------------------------ fused combine
 def combine_bound(S, w):
     """The combine's bound: the weighted matvec bounds plus the fp32
     multiply-add chain over at most 16 slots."""
@@ -243,29 +240,31 @@ def combine(env, fmt, Wall, stride, N, K, ids, w, x, n_experts=E):
     return out.cpu().numpy()
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("B", [1, 2, 8])
-def test_q4k_moe_combine_30b_shapes(env, B):
-    """Q4_K down experts 2048 x 768 (3 super-blocks per row), one input per
+def test_superblock_moe_combine_30b_shapes(env, fmt, B):
+    """Super-block down experts 2048 x 768 (3 super-blocks per row), one input per
     (token, slot), router weights summing to 1: against the oracle, and
     against the weighted sum of qmv_moe's per-slot outputs."""
     H, F = wl.MOE_HIDDEN, wl.MOE_FFN
-    Wall = experts("q4_k", "down", H, F)
-    stride = wl.block_bytes("q4_k", H, F)
+    Wall = experts(fmt, "down", H, F)
+    stride = wl.block_bytes(fmt, H, F)
     ids = wl.moe_ids(f"t/sbmoe/cb/ids/{B}", B, T, E)
     w = wl.router_weights(f"t/sbmoe/cb/w/{B}", B, T)
     x = wl.activations(f"t/sbmoe/cb/x/{B}", B * T, F).reshape(B, T, F)
-    say(f"q4_k moe combine B={B}")
-    out = combine(env, "q4_k", Wall, stride, H, F, ids, w, x)
-    ref, S = oracle.moe_combine("q4_k", Wall, stride, E, H, F, ids, w, x_slots=x)
+    say(f"{fmt} moe combine B={B}")
+    out = combine(env, fmt, Wall, stride, H, F, ids, w, x)
+    ref, S = oracle.moe_combine(fmt, Wall, stride, E, H, F, ids, w, x_slots=x)
     err = np.abs(out.astype(np.float64) - ref)
     assert np.all(err <= combine_bound(S, w)), float((err / combine_bound(S, w)).max())
-    y = run(env, "q4_k", Wall, stride, H, F, ids, x).astype(np.float64)
+    y = run(env, fmt, Wall, stride, H, F, ids, x).astype(np.float64)
     mix = np.einsum("bs,bsn->bn", w.astype(np.float64), y)
     assert np.all(np.abs(out - mix) <= T * 2.0 ** -24 * np.einsum("bs,bsn->bn", np.abs(w), np.abs(y)) + 1e-37)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("case", ["one_hot_dup", "invalid", "chunked_slots", "token_inputs"])
-def test_q4k_moe_combine_edges(env, case):
+def test_superblock_moe_combine_edges(env, fmt, case):
     """Six experts.  One-hot weights (out equals one slot's qmv_moe output
     bitwise) with duplicated ids and a padded stride, an invalid id (the
     token's row becomes NaN), top_k 16 on rows of 16384 columns (one slot
@@ -282,45 +281,39 @@ def test_q4k_moe_combine_edges(env, case):
     else:
         N, K, ids = 128, 2048, np.array([[5, 1, 0, 3], [2, 2, 4, 1]], dtype=np.int32)
     B, Tk = ids.shape
-    per = wl.block_bytes("q4_k", N, K)
+    per = wl.block_bytes(fmt, N, K)
     stride = per + (256 if case == "one_hot_dup" else 0)
-    Wm = wl.quant_weights("q4_k", f"t/sbmoe/cb/{case}", E6 * N, K).reshape(E6, per)
+    Wm = wl.quant_weights(fmt, f"t/sbmoe/cb/{case}", E6 * N, K).reshape(E6, per)
     Wall = np.zeros((E6, stride), dtype=np.uint8)
     Wall[:, :per] = Wm
     Wall = Wall.reshape(-1)
     w = wl.router_weights(f"t/sbmoe/cb/w/{case}", B, Tk)
-    say(f"q4_k moe combine edge {case}")
+    say(f"{fmt} moe combine edge {case}")
     if case == "token_inputs":
         x = wl.activations(f"t/sbmoe/cb/x/{case}", B, K)
-        out = combine(env, "q4_k", Wall, stride, N, K, ids, w, x, E6)
-        ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids, w, x_tokens=x)
+        out = combine(env, fmt, Wall, stride, N, K, ids, w, x, E6)
+        ref, S = oracle.moe_combine(fmt, Wall, stride, E6, N, K, ids, w, x_tokens=x)
     else:
         x = wl.activations(f"t/sbmoe/cb/x/{case}", B * Tk, K).reshape(B, Tk, K)
         if case == "one_hot_dup":
             w = np.zeros((B, Tk), dtype=np.float32)
             w[0, 2] = 1.0
             w[1, 1] = 1.0
-        out = combine(env, "q4_k", Wall, stride, N, K, ids, w, x, E6)
+        out = combine(env, fmt, Wall, stride, N, K, ids, w, x, E6)
         if case == "invalid":
             valid = np.all((ids >= 0) & (ids < E6), axis=1)
             assert np.all(np.isnan(out[~valid])) and not np.any(np.isnan(out[valid]))
             ids_ok = np.where((ids >= 0) & (ids < E6), ids, 0).astype(np.int32)
-            ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids_ok, w, x_slots=x)
+            ref, S = oracle.moe_combine(fmt, Wall, stride, E6, N, K, ids_ok, w, x_slots=x)
             out, ref, S, w = out[valid], ref[valid], S[valid], w[valid]
         elif case == "chunked_slots":
-            ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids, w, x_slots=x)
+            ref, S = oracle.moe_combine(fmt, Wall, stride, E6, N, K, ids, w, x_slots=x)
         else:
-            ref, S = oracle.moe_combine("q4_k", Wall, stride, E6, N, K, ids, w, x_slots=x)
-            y = qmv.qmv_moe("q4_k", dev(torch, Wall), stride, E6, N, K, dev(torch, ids), dev(torch, x))
+            ref, S = oracle.moe_combine(fmt, Wall, stride, E6, N, K, ids, w, x_slots=x)
+            y = qmv.qmv_moe(fmt, dev(torch, Wall), stride, E6, N, K, dev(torch, ids), dev(torch, x))
             torch.cuda.synchronize()
             y = y.cpu().numpy()
             assert np.array_equal(out[0].view(np.uint32), y[0, 2].view(np.uint32))
             assert np.array_equal(out[1].view(np.uint32), y[1, 1].view(np.uint32))
     err = np.abs(out.astype(np.float64) - ref)
     assert np.all(err <= combine_bound(S, w)), (case, float((err / combine_bound(S, w)).max()))
-    if case == "token_inputs":
-        W6 = dev(torch, wl.quant_weights("q6_k", "t/sbmoe/cb6", 2 * 8, 256).reshape(-1))
-        with pytest.raises(qmv.QmvError):
-            qmv.qmv_moe_combine("q6_k", W6, wl.block_bytes("q6_k", 8, 256), 2, 8, 256,
-                                dev(torch, np.zeros((1, 1), dtype=np.int32)), dev(torch, np.ones((1, 1), np.float32)),
-                                dev(torch, np.zeros((1, 256), np.float32)))
