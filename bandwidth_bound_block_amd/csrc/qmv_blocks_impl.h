@@ -244,23 +244,37 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
     auto advance = [&](int& row, int& t) {
         if (++t == T) { t = 0; row += wstride32; }
     };
+    // The matrix of a (wave-uniform) row: selects over the table with
+    // constant indices only, so the table stays in scalar registers and the
+    // lookup issues no dependent loads from the argument segment.
+    auto locate = [&](int row, const uint8_t*& Wm, float*& ym, int& start) {
+        Wm = segs.W[0];
+        ym = segs.y[0];
+        start = 0;
+#pragma unroll
+        for (int i = 1; i < kMaxSegs; ++i) {
+            const bool in = i < segs.n && row >= (int)segs.end[i - 1];
+            Wm = in ? segs.W[i] : Wm;
+            ym = in ? segs.y[i] : ym;
+            start = in ? (int)segs.end[i - 1] : start;
+        }
+    };
     // The load cursor keeps a buffer descriptor over each row of its row
-    // group (wave-uniform, in scalar registers): the matrix lookup runs once
-    // per row group (rows only increase, so it starts from the last matrix
-    // found), and a step's loads are the descriptor, a scalar step offset
-    // and a per-lane constant offset.
+    // group (wave-uniform, in scalar registers), set once per row group; a
+    // step's loads are the descriptor, a scalar step offset and a per-lane
+    // constant offset.
     __amdgpu_buffer_rsrc_t lrs[RR];
-    int lseg = 0;
     int voff[C::kLoads];
     C::lane_offsets(lane, voff);
     auto set_rows = [&](int p) {
-        int i = lseg;
 #pragma unroll
         for (int k = 0; k < RR; ++k) {
             const int row = min(RR * p + k, N - 1);
-            while (i + 1 < segs.n && row >= segs.end[i]) ++i;
-            if (k == 0) lseg = i;
-            lrs[k] = raw_buffer(segs.W[i] + (int64_t)(row - (i ? (int)segs.end[i - 1] : 0)) * pitch, pitch);
+            const uint8_t* Wm;
+            float* ym;
+            int start;
+            locate(row, Wm, ym, start);
+            lrs[k] = raw_buffer(Wm + (int64_t)(row - start) * pitch, pitch);
         }
     };
     set_rows(min(lrow, NP - 1));
@@ -276,7 +290,6 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
             set_rows(min(lrow, NP - 1));
         }
     };
-    int cseg = 0;   // matrix of the compute cursor's rows (rows only increase)
     float acc[RR];
 #pragma unroll
     for (int k = 0; k < RR; ++k) acc[k] = 0.f;
@@ -300,8 +313,11 @@ __global__ __launch_bounds__(64 * NW) void qmv_kernel_c(const RowSegs segs, int 
                 const float tot = segment_sum<64>(acc[k]);
                 const int row = RR * crow + k;
                 if (row < N) {
-                    while (cseg + 1 < segs.n && row >= segs.end[cseg]) ++cseg;
-                    if (lane == 0) segs.y[cseg][row - (cseg ? segs.end[cseg - 1] : 0)] = tot;
+                    const uint8_t* Wm;
+                    float* ym;
+                    int start;
+                    locate(row, Wm, ym, start);
+                    if (lane == 0) ym[row - start] = tot;
                 }
                 acc[k] = 0.f;
             }
