@@ -58,16 +58,16 @@ TRAFFIC_RECORDS = {
     "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>": {
         "key": "kernel_c_q8_0",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "753ac41d427d22e3ceab8faacdccddbd371d9e4d6550d301a66ca2f12e5a7e5d", "bytes_per_launch": 83478763, "ratio": 1.0025,
+        "sha256": "b370225818396cd2973e4d7583f4416cb2bbcd5dd601905e7f1a46e54bd83353", "bytes_per_launch": 83479950, "ratio": 1.0025,
         "workload": "8B Q8_0 decode step, batch 1"},
     "qmv_kernel<Q8_0, 1, 64, 1, 2, 8, 2, false, float, false>": {
         "key": "kernel_q8_0_o",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "753ac41d427d22e3ceab8faacdccddbd371d9e4d6550d301a66ca2f12e5a7e5d", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
+        "sha256": "b370225818396cd2973e4d7583f4416cb2bbcd5dd601905e7f1a46e54bd83353", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
     "qmv_kernel_c<Q8_0, 4, 16, 2, float, 1>": {
         "key": "kernel_c16_q8_0_down",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "753ac41d427d22e3ceab8faacdccddbd371d9e4d6550d301a66ca2f12e5a7e5d", "ratio": 1.0080, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
+        "sha256": "b370225818396cd2973e4d7583f4416cb2bbcd5dd601905e7f1a46e54bd83353", "ratio": 1.0079, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
     "i8_stream_kernel": {
         "key": "i8_stream",
         "sources": ["bandwidth_bound_block_amd/csrc/qmv_int8.hip", "bandwidth_bound_block_amd/csrc/qmv_host.h"],
