@@ -877,9 +877,9 @@ int32_t launch_c_xu(const RowSegs& segs, int nb, const XT* x, hipStream_t st) {
 // Batch 1 with whole 64-block steps and 16-byte aligned W and x: the
 // contiguous-chunk kernel where it streams faster than per-block loads
 // (measured on the 8B decode shapes, cache-cold):
-//   Q8_0: matrices of >= 8192 rows or >= 256 blocks per row;
+//   Q8_0: matrices of >= 4096 rows or >= 256 blocks per row;
 //   Q4_0/Q4_1 (closer to the VALU bound, where the LDS copy costs more):
-//   2048..32768 rows, or >= 256 blocks per row.
+//   2049..4096 rows, > 32768 rows, or >= 256 blocks per row.
 // 16 waves per workgroup for long rows (one activation copy per CU) and
 // for Q4 matrices of <= 4096 rows, else 8; fewer if the LDS does not fit.
 template <class F, class XT = float>
@@ -892,11 +892,14 @@ bool try_launch_c(const RowSegs& segs, int nb, const XT* x, hipStream_t st, bool
     const int64_t N = segs.end[segs.n - 1];
     const bool q8 = !F::kNibbles;
     const bool long_rows = nb >= 256;
-    // Measured (8B shapes, cache-cold): Q8_0 gains from this kernel on >= 8192
-    // rows or long rows; Q4_x only on long rows (down) as a single matrix
-    // (the per-block kernel with two rows per lane is faster elsewhere),
-    // and on row groups of > 8192 rows two rows per wave step (4 waves).
-    if (!force && (q8 ? !(N >= 8192 || long_rows) : !long_rows)) return false;
+    // Measured on the 8B steps (graph replays, same box): this kernel for
+    // Q8_0 matrices of >= 4096 rows or long rows, and for Q4_x on long rows
+    // (down), on 2049..4096 rows (q, o) and on > 32768 rows (lm_head); the
+    // per-block kernel with two rows per lane is faster on the Q4_x k, v and
+    // gate / up shapes.  Q4_x row sets of > 8192 rows take two rows per wave
+    // step (4 waves).
+    if (!force && (q8 ? !(N >= 4096 || long_rows) : !(long_rows || (N > 2048 && N <= 4096) || N > 32768)))
+        return false;
     const size_t lds_x = (size_t)nb * kXPad * sizeof(float);
     if (!q8 && !long_rows && N > 8192 && lds_x + 4 * 2 * (size_t)Contig<F>::kStepBytes <= (size_t)kLdsMax) {
         *rc = launch_c_xu<F, 4, XT, 2>(segs, nb, x, st);
@@ -932,7 +935,7 @@ int32_t launch_b1(const uint8_t* W, int64_t N, int nb, const XT* x, int64_t ldx,
     const int K4 = nb * 8;
     // Q4_x: two rows per lane (measured faster on every 8B shape it takes)
     constexpr int RPL = F::kNibbles ? 2 : 1;
-    // 8 waves where x is large, and for Q8_0 (o, 4096 x 4096: 6.0 -> 5.6 us);
+    // 8 waves where x is large, and for Q8_0 (4096 x 4096: 6.0 -> 5.6 us);
     // Q4_x keeps 4 (q+k+v and lm_head were slower with 8)
     if (lds > 40 * 1024 || !F::kNibbles) {
         if (vec && K4 <= 2 * 512) return launch_lpr<F, 1, 2, 8, XT, RPL>(W, N, nb, x, ldx, y, ldy, st);

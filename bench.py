@@ -53,21 +53,17 @@ LABEL_BATCHES = 5         # per-label timing: median of 5 batches (p10/p90 = min
 _IMPL = ["bandwidth_bound_block_amd/csrc/qmv_blocks_impl.h", "bandwidth_bound_block_amd/csrc/qmv_block_decode.h",
          "bandwidth_bound_block_amd/csrc/qmv_host.h"]
 TRAFFIC_RECORDS = {
-    # the dominant kernel of the decode step, in the step's 32:32:1 mix of
-    # q+k+v, gate+up and lm_head launches: bytes per launch
+    # the dominant kernel of the decode step, in the step's 32:32:32:1 mix
+    # of q+k+v, o, gate+up and lm_head launches: bytes per launch
     "qmv_kernel_c<Q8_0, 2, 8, 2, float, 1>": {
         "key": "kernel_c_q8_0",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "b370225818396cd2973e4d7583f4416cb2bbcd5dd601905e7f1a46e54bd83353", "bytes_per_launch": 83479950, "ratio": 1.0025,
+        "sha256": "aa19641f66816f500969c8e79d12c4dff372c82fcf2ca6061f80f4bbb7c36ca8", "bytes_per_launch": 61898701, "ratio": 1.0033,
         "workload": "8B Q8_0 decode step, batch 1"},
-    "qmv_kernel<Q8_0, 1, 64, 1, 2, 8, 2, false, float, false>": {
-        "key": "kernel_q8_0_o",
-        "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "b370225818396cd2973e4d7583f4416cb2bbcd5dd601905e7f1a46e54bd83353", "ratio": 1.0109, "workload": "8B Q8_0 o (4096 x 4096), batch 1"},
     "qmv_kernel_c<Q8_0, 4, 16, 2, float, 1>": {
         "key": "kernel_c16_q8_0_down",
         "sources": _IMPL + ["bandwidth_bound_block_amd/csrc/qmv_fmt_q8_0.hip"],
-        "sha256": "b370225818396cd2973e4d7583f4416cb2bbcd5dd601905e7f1a46e54bd83353", "ratio": 1.0079, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
+        "sha256": "aa19641f66816f500969c8e79d12c4dff372c82fcf2ca6061f80f4bbb7c36ca8", "ratio": 1.0079, "workload": "8B Q8_0 down (4096 x 14336), batch 1"},
     "i8_stream_kernel": {
         "key": "i8_stream",
         "sources": ["bandwidth_bound_block_amd/csrc/qmv_int8.hip", "bandwidth_bound_block_amd/csrc/qmv_host.h"],
@@ -673,14 +669,14 @@ def final_line(head, ceiling, cpu, summary, steps, warmup):
     """The compact last stdout line: the headline step, the dominant
     kernel's roofline, the read ceiling, the oracle baseline and one
     [GB/s, tok/s] pair per extra workload (kept well under 4 KB)."""
-    # Roofline of the dominant kernel.  The q||k||v (6144 rows), gate||up
-    # (28672 rows) and lm_head (128256 rows) launches, 65 of the step's 129
-    # and ~60% of its time, run one instantiation: the contiguous-chunk
-    # kernel qmv_kernel_c<Q8_0, XU=2, 8 waves, PD=2>; down (K = 14336) runs
-    # the 16-wave one and o (4096 rows) the per-block kernel.  achieved =
+    # Roofline of the dominant kernel.  The q||k||v (6144 rows), o (4096
+    # rows), gate||up (28672 rows) and lm_head (128256 rows) launches, 97 of
+    # the step's 129 and ~70% of its time, run one instantiation: the
+    # contiguous-chunk kernel qmv_kernel_c<Q8_0, XU=2, 8 waves, PD=2>; down
+    # (K = 14336) runs the 16-wave one.  achieved =
     # that kernel's algorithmic bytes over its summed per-launch event
     # times (each launch of a label back to back on the launch stream).
-    dom = [k for k in ("qkv", "gate_up", "lm_head") if k in head["per_matrix"]]
+    dom = [k for k in ("qkv", "o", "gate_up", "lm_head") if k in head["per_matrix"]]
     pm = head["per_matrix"]
     dom_bytes = sum(pm[k]["bytes_per_launch"] * pm[k]["launches"] for k in dom)
     dom_us = sum(pm[k]["us_per_launch"] * pm[k]["launches"] for k in dom)
